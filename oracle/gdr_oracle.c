@@ -1,0 +1,200 @@
+/*
+ * fp64 CPU oracle for the gated delta rule family.  TEST INFRASTRUCTURE ONLY:
+ * only the tests, the smoke check and the benchmark's CPU-baseline leg load
+ * this library.  It shares no code, header or constant with the HIP kernels.
+ *
+ * Plain, sequential-in-time recurrences, evaluated token by token in double
+ * precision.  Every array is row-major and contiguous:
+ *   q, k            [B, T, H, Dk]
+ *   v               [B, T, H, Dv]
+ *   alpha, beta     [B, T, H]          (GDN, scalar gates)
+ *   alpha, erase    [B, T, H, Dk]      (GDN-2, key-axis gates)
+ *   write           [B, T, H, Dv]      (GDN-2, value-axis gate)
+ *   s0, s_final     [B, H, Dv, Dk]     (state S is Dv x Dk, o = S q)
+ *   o               [B, T, H, Dv]
+ * s0 == NULL means a zero initial state; s_final == NULL means "not wanted".
+ *
+ * The state is a Dv x Dk matrix: the review of Gated DeltaNet on
+ * meaningful96.github.io ("1. Problem Formulation" and "3.1 Linear Attention
+ * as Associative Memory") writes o_t = S_t q_t and the write v_t k_t^T.
+ *
+ * Row form.  Every rule here right-multiplies S by a Dk x Dk transition and
+ * adds an outer product v k^T, so row i of S (the i-th value channel) is
+ * updated from its own old value, the scalar v_i, and the shared key-side
+ * vectors.  The loops below therefore run row by row inside each token;
+ * that is the matrix product written out entry by entry, not a reordering.
+ */
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARGS 1
+#define ORACLE_ERR_NOMEM 2
+
+static void state_init(double *S, const double *s0, long Dv, long Dk) {
+    if (s0)
+        memcpy(S, s0, sizeof(double) * (size_t)(Dv * Dk));
+    else
+        memset(S, 0, sizeof(double) * (size_t)(Dv * Dk));
+}
+
+/*
+ * One token of the gated delta rule on one (sequence, head) state:
+ *
+ *   S_t = S_{t-1} . alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *   o_t = S_t q_t.
+ *
+ * This is the update of "Gated Delta Networks" (agihunt.info, both the
+ * Chinese summary and the English "Method" section) and equation of section
+ * 3.4 of the meaningful96 review; o_t = S_t q_t is from its section 1.
+ * Multiplying row s of S_{t-1} into alpha (I - beta k k^T) gives
+ * alpha s - alpha beta (s . k) k^T, to which beta v_i k^T is added.
+ */
+static void gdn_token(double *S, long Dk, long Dv, const double *q,
+                      const double *k, const double *v, double alpha,
+                      double beta, double *o) {
+    for (long i = 0; i < Dv; ++i) {
+        double *s = S + i * Dk;
+        double sk = 0.0;                     /* (S_{t-1} k_t)_i */
+        for (long j = 0; j < Dk; ++j) sk += s[j] * k[j];
+        const double c = beta * v[i] - alpha * beta * sk;
+        for (long j = 0; j < Dk; ++j) s[j] = alpha * s[j] + c * k[j];
+        double oi = 0.0;                     /* (S_t q_t)_i */
+        for (long j = 0; j < Dk; ++j) oi += s[j] * q[j];
+        o[i] = oi;
+    }
+}
+
+/* Gated delta rule forward over a whole sequence, for every (b, h). */
+int oracle_gdn_fwd(long B, long T, long H, long Dk, long Dv, const double *q,
+                   const double *k, const double *v, const double *alpha,
+                   const double *beta, const double *s0, double *o,
+                   double *s_final) {
+    if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return ORACLE_ERR_ARGS;
+    if (!q || !k || !v || !alpha || !beta || !o) return ORACLE_ERR_ARGS;
+    int err = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (long b = 0; b < B; ++b) {
+        for (long h = 0; h < H; ++h) {
+            double *S = (double *)malloc(sizeof(double) * (size_t)(Dv * Dk));
+            if (!S) {
+#pragma omp atomic write
+                err = 1;
+                continue;
+            }
+            state_init(S, s0 ? s0 + (b * H + h) * Dv * Dk : NULL, Dv, Dk);
+            for (long t = 0; t < T; ++t) {
+                const long bth = (b * T + t) * H + h;
+                gdn_token(S, Dk, Dv, q + bth * Dk, k + bth * Dk, v + bth * Dv,
+                          alpha[bth], beta[bth], o + bth * Dv);
+            }
+            if (s_final)
+                memcpy(s_final + (b * H + h) * Dv * Dk, S,
+                       sizeof(double) * (size_t)(Dv * Dk));
+            free(S);
+        }
+    }
+    return err ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}
+
+/*
+ * One decode step for N independent sequences: the same single-token update
+ * applied in place to state [N, H, Dv, Dk], with q, k [N, H, Dk],
+ * v [N, H, Dv], alpha, beta [N, H] and o [N, H, Dv].  A fixed-size state
+ * and constant memory per token is how both summaries describe decoding.
+ */
+int oracle_gdn_step(long N, long H, long Dk, long Dv, const double *q,
+                    const double *k, const double *v, const double *alpha,
+                    const double *beta, double *state, double *o) {
+    if (N < 0 || H < 0 || Dk <= 0 || Dv <= 0) return ORACLE_ERR_ARGS;
+    if (!q || !k || !v || !alpha || !beta || !state || !o)
+        return ORACLE_ERR_ARGS;
+#pragma omp parallel for schedule(static)
+    for (long nh = 0; nh < N * H; ++nh)
+        gdn_token(state + nh * Dv * Dk, Dk, Dv, q + nh * Dk, k + nh * Dk,
+                  v + nh * Dv, alpha[nh], beta[nh], o + nh * Dv);
+    return ORACLE_OK;
+}
+
+/*
+ * One token of Gated Delta Rule-2 ("Gated DeltaNet-2", agihunt.info,
+ * paragraph on the update order): decay the old state with the per-channel
+ * alpha_t on the key axis, read the old value along b_t (.) k_t, then write
+ * the residual between w_t (.) v_t and that read along k_t:
+ *
+ *   S' = S_{t-1} diag(alpha_t)
+ *   S_t = S' + (w_t (.) v_t - S' (b_t (.) k_t)) k_t^T,   o_t = S_t q_t.
+ *
+ * The equation itself is missing from the page; this is the reading its
+ * wording gives, and collapsing the gates (alpha = a 1, b = w = beta 1)
+ * returns the scalar rule above, as the page states.
+ */
+static void gdn2_token(double *S, long Dk, long Dv, const double *q,
+                       const double *k, const double *v, const double *alpha,
+                       const double *erase, const double *write, double *o) {
+    for (long i = 0; i < Dv; ++i) {
+        double *s = S + i * Dk;
+        for (long j = 0; j < Dk; ++j) s[j] *= alpha[j];      /* S' */
+        double rd = 0.0;                                     /* S'(b.k) */
+        for (long j = 0; j < Dk; ++j) rd += s[j] * (erase[j] * k[j]);
+        const double c = write[i] * v[i] - rd;
+        for (long j = 0; j < Dk; ++j) s[j] += c * k[j];
+        double oi = 0.0;
+        for (long j = 0; j < Dk; ++j) oi += s[j] * q[j];
+        o[i] = oi;
+    }
+}
+
+int oracle_gdn2_fwd(long B, long T, long H, long Dk, long Dv, const double *q,
+                    const double *k, const double *v, const double *alpha,
+                    const double *erase, const double *write,
+                    const double *s0, double *o, double *s_final) {
+    if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return ORACLE_ERR_ARGS;
+    if (!q || !k || !v || !alpha || !erase || !write || !o)
+        return ORACLE_ERR_ARGS;
+    int err = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (long b = 0; b < B; ++b) {
+        for (long h = 0; h < H; ++h) {
+            double *S = (double *)malloc(sizeof(double) * (size_t)(Dv * Dk));
+            if (!S) {
+#pragma omp atomic write
+                err = 1;
+                continue;
+            }
+            state_init(S, s0 ? s0 + (b * H + h) * Dv * Dk : NULL, Dv, Dk);
+            for (long t = 0; t < T; ++t) {
+                const long bth = (b * T + t) * H + h;
+                gdn2_token(S, Dk, Dv, q + bth * Dk, k + bth * Dk,
+                           v + bth * Dv, alpha + bth * Dk, erase + bth * Dk,
+                           write + bth * Dv, o + bth * Dv);
+            }
+            if (s_final)
+                memcpy(s_final + (b * H + h) * Dv * Dk, S,
+                       sizeof(double) * (size_t)(Dv * Dk));
+            free(S);
+        }
+    }
+    return err ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}
+
+/* Threads the oracle's parallel loops use (reported with CPU timings). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

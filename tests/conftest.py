@@ -1,0 +1,25 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line(
+        "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line(
+        "markers", "slow: full-size workloads (minutes of CPU oracle time)")
+
+
+@pytest.fixture(scope="session")
+def gdr_lib():
+    """The HIP library's Python binding (GPU tests only)."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+    import gated_delta_rule_16_amd as gdr
+    return gdr

@@ -1,0 +1,154 @@
+"""Chunkwise (UT/WY) form of the gated delta rules against the token-by-token
+oracle, in fp64 NumPy (CPU only).
+
+This pins the chunk algebra the HIP kernels evaluate — the readings of the
+undefined or garbled symbols in the chunkwise equations of section 3.7 of the
+meaningful96.github.io GDN review — before any kernel is trusted:
+
+* Gamma_rs = exp(g_r - g_s) with g the within-chunk cumulative log alpha;
+* the output mask M carries that decay and includes the diagonal;
+* left arrow X = diag(gamma) X; right arrow K = diag(gamma_C / gamma) K;
+  right arrow S = gamma_C S;  W = T diag(beta gamma) K,  U = T diag(beta) V.
+
+For Gated DeltaNet-2 (agihunt.info summary: channel decay absorbed into an
+asymmetric rank-1 erase factor, WY solve plus dense products, chunk 64) the
+decayed products A and P are formed per 16-token block with the block's
+left boundary as reference point, so every exponent on the operands is
+bounded (see ``gdn2_chunk``).
+
+Nothing here is shared with the HIP code; it is an independent derivation
+checked against the oracle at every chunk size.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle_pins import rand_gdn, rand_gdn2
+
+
+def gdn_chunk(q, k, v, a, b, s0, C):
+    """Scalar-gated chunkwise forward for one (b, h): q, k [T,Dk], v [T,Dv],
+    a, b [T]; s0 [Dv,Dk].  Returns o [T,Dv], S [Dv,Dk]."""
+    T, Dk = q.shape
+    Dv = v.shape[1]
+    S = s0.copy()
+    o = np.zeros((T, Dv))
+    for c0 in range(0, T, C):
+        sl = slice(c0, min(c0 + C, T))
+        Q, K, V, al, be = q[sl], k[sl], v[sl], a[sl], b[sl]
+        n = Q.shape[0]
+        g = np.cumsum(np.log(al))                       # g_r
+        ge = np.tril(np.ones((n, n), dtype=bool))       # r >= s
+        # Gamma_rs = exp(g_r - g_s) on r >= s; the exponent is masked before
+        # exp so the (unused) upper part cannot overflow.
+        Gam = np.exp(np.where(ge, g[:, None] - g[None, :], -np.inf))
+        gt = np.tril(np.ones((n, n), dtype=bool), -1)
+        A = np.where(gt, be[:, None] * Gam * (K @ K.T), 0.0)  # strictLower
+        Tm = np.linalg.inv(np.eye(n) + A)               # T = (I + A)^-1
+        W = Tm @ ((be * np.exp(g))[:, None] * K)   # left-arrow W
+        U = Tm @ (be[:, None] * V)                      # U^g
+        Vn = U - W @ S.T                                # U^g - W S^T
+        P = np.where(ge, (Q @ K.T) * Gam, 0.0)          # mask incl. diagonal
+        o[sl] = (np.exp(g)[:, None] * Q) @ S.T + P @ Vn
+        S = np.exp(g[-1]) * S + Vn.T @ (np.exp(g[-1] - g)[:, None] * K)
+    return o, S
+
+
+def gdn2_chunk(q, k, v, a, e, w, s0, C, sub=16):
+    """Channel-gated chunkwise forward for one (b, h).
+
+    Within a chunk, G[r] = cumsum log alpha (per channel).  The decayed
+    products A_sj = sum_c e_sc k_jc exp(G_sc - G_jc) (j < s) and
+    P_rs = sum_c q_rc k_sc exp(G_rc - G_sc) (s <= r) are formed per block of
+    ``sub`` rows: with m the position just before the block,
+    exp(G_s - G_j) = exp(G_s - G_m) exp(G_m - G_j), the first factor <= 1
+    and the second <= 1 for every earlier block; on the block's own diagonal
+    the second factor is >= 1, bounded by the block's decay range.  When that
+    range is too wide for fp32 (> 80 in natural-log units) the diagonal block
+    is formed entry by entry instead.
+    """
+    T, Dk = q.shape
+    Dv = v.shape[1]
+    S = s0.copy()
+    o = np.zeros((T, Dv))
+    for c0 in range(0, T, C):
+        sl = slice(c0, min(c0 + C, T))
+        Q, K, V, Al, E, Wg = q[sl], k[sl], v[sl], a[sl], e[sl] * k[sl], w[sl]
+        n = Q.shape[0]
+        G = np.cumsum(np.log(Al), axis=0)               # [n, Dk]
+        A = np.zeros((n, n))
+        P = np.zeros((n, n))
+        for r0 in range(0, n, sub):
+            r1 = min(r0 + sub, n)
+            Gm = G[r0 - 1] if r0 > 0 else np.zeros(Dk)
+            Et = E[r0:r1] * np.exp(G[r0:r1] - Gm)       # <= |e|
+            Qt = Q[r0:r1] * np.exp(G[r0:r1] - Gm)
+            Kt = K[:r1] * np.exp(Gm - G[:r1])            # <= |k| for j < r0
+            rng = np.max(Gm - G[r1 - 1])
+            A[r0:r1, :r1] = Et @ Kt.T
+            P[r0:r1, :r1] = Qt @ Kt.T
+            if rng > 80.0:                               # exact diagonal block
+                for s in range(r0, r1):
+                    for j in range(r0, s + 1):
+                        d = np.exp(G[s] - G[j])
+                        A[s, j] = np.sum(E[s] * K[j] * d)
+                        P[s, j] = np.sum(Q[s] * K[j] * d)
+        A = np.where(np.tril(np.ones((n, n), dtype=bool), -1), A, 0.0)
+        P = np.where(np.tril(np.ones((n, n), dtype=bool)), P, 0.0)
+        Tm = np.linalg.inv(np.eye(n) + A)
+        W2 = Tm @ (E * np.exp(G))
+        U2 = Tm @ (Wg * V)
+        Vn = U2 - W2 @ S.T
+        o[sl] = (Q * np.exp(G)) @ S.T + P @ Vn
+        S = S * np.exp(G[-1])[None, :] + Vn.T @ (K * np.exp(G[-1] - G))
+    return o, S
+
+
+@pytest.mark.parametrize("C", [1, 4, 16, 64, 200])
+def test_gdn_chunk_form(C):
+    q, k, v, a, b, S0 = rand_gdn(40, B=1, T=200, H=2, Dk=16, Dv=12)
+    o_ref, s_ref = oracle.gdn_fwd(q, k, v, a, b, S0)
+    for h in range(2):
+        o, S = gdn_chunk(q[0, :, h], k[0, :, h], v[0, :, h], a[0, :, h],
+                         b[0, :, h], S0[0, h], C)
+        np.testing.assert_allclose(o, o_ref[0, :, h], rtol=1e-11, atol=1e-11)
+        np.testing.assert_allclose(S, s_ref[0, h], rtol=1e-11, atol=1e-11)
+
+
+def test_gdn_chunk_form_strong_decay():
+    """Workload-like decay (alpha ~ exp(-softplus(N + 2))): the product of
+    alphas over a 64-chunk underflows, exp of differences does not."""
+    q, k, v, a, b, S0 = rand_gdn(41, B=1, T=160, H=1, Dk=16, Dv=16)
+    g = np.random.Generator(np.random.PCG64(1))
+    a = np.exp(-np.logaddexp(0, g.standard_normal(a.shape) + 2.0))
+    a[0, 70, 0] = 1e-300                                 # near-total reset
+    o_ref, s_ref = oracle.gdn_fwd(q, k, v, a, b, S0)
+    o, S = gdn_chunk(q[0, :, 0], k[0, :, 0], v[0, :, 0], a[0, :, 0],
+                     b[0, :, 0], S0[0, 0], 64)
+    np.testing.assert_allclose(o, o_ref[0, :, 0], rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(S, s_ref[0, 0], rtol=1e-10, atol=1e-11)
+
+
+@pytest.mark.parametrize("C", [1, 4, 16, 64, 150])
+def test_gdn2_chunk_form(C):
+    q, k, v, a, e, w, S0 = rand_gdn2(42, B=1, T=150, H=2, Dk=16, Dv=12)
+    o_ref, s_ref = oracle.gdn2_fwd(q, k, v, a, e, w, S0)
+    for h in range(2):
+        o, S = gdn2_chunk(q[0, :, h], k[0, :, h], v[0, :, h], a[0, :, h],
+                          e[0, :, h], w[0, :, h], S0[0, h], C)
+        np.testing.assert_allclose(o, o_ref[0, :, h], rtol=1e-11, atol=1e-11)
+        np.testing.assert_allclose(S, s_ref[0, h], rtol=1e-11, atol=1e-11)
+
+
+def test_gdn2_chunk_form_wide_decay_range():
+    """Per-channel alphas small enough that a 16-block's decay range passes
+    the fp32 limit: the diagonal blocks take the entry-by-entry path."""
+    q, k, v, a, e, w, S0 = rand_gdn2(43, B=1, T=128, H=1, Dk=16, Dv=8)
+    g = np.random.Generator(np.random.PCG64(2))
+    a = np.exp(-np.logaddexp(0, g.standard_normal(a.shape) + 2.0))
+    a[0, 20:24, 0, 3] = 1e-12                            # range > 80
+    o_ref, s_ref = oracle.gdn2_fwd(q, k, v, a, e, w, S0)
+    o, S = gdn2_chunk(q[0, :, 0], k[0, :, 0], v[0, :, 0], a[0, :, 0],
+                      e[0, :, 0], w[0, :, 0], S0[0, 0], 64)
+    np.testing.assert_allclose(o, o_ref[0, :, 0], rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(S, s_ref[0, 0], rtol=1e-9, atol=1e-10)

@@ -1,0 +1,55 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check
+that the pins catch every one of them."""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "gdr_oracle.c")
+
+# (name, exact text in the source, replacement)
+MUTANTS = [
+    ("gdn_sign_of_erase", "beta * v[i] - alpha * beta * sk",
+     "beta * v[i] + alpha * beta * sk"),
+    ("gdn_erase_without_decay", "beta * v[i] - alpha * beta * sk",
+     "beta * v[i] - beta * sk"),
+    ("gdn_decay_dropped", "s[j] = alpha * s[j] + c * k[j]",
+     "s[j] = s[j] + c * k[j]"),
+    ("gdn_write_without_beta", "const double c = beta * v[i] - alpha",
+     "const double c = v[i] - alpha"),
+    ("gdn_read_with_query", "sk += s[j] * k[j]", "sk += s[j] * q[j]"),
+    ("gdn_output_from_key", "oi += s[j] * q[j];\n        o[i] = oi;\n    }\n}\n\n/* Gated delta rule forward",
+     "oi += s[j] * k[j];\n        o[i] = oi;\n    }\n}\n\n/* Gated delta rule forward"),
+    ("gdn_token_index_shift", "alpha[bth], beta[bth], o + bth * Dv);",
+     "alpha[bth], beta[t + 1 < T ? bth + H : bth], o + bth * Dv);"),
+    ("gdn_transposed_state_init", "memcpy(S, s0, sizeof(double) * (size_t)(Dv * Dk));",
+     "for (long i = 0; i < Dv; ++i) for (long j = 0; j < Dk; ++j) S[i * Dk + j] = (i < Dk && j < Dv) ? s0[j * Dk + i] : 0.0;"),
+    ("gdn2_erase_gate_dropped", "rd += s[j] * (erase[j] * k[j])",
+     "rd += s[j] * k[j]"),
+    ("gdn2_write_gate_dropped", "const double c = write[i] * v[i] - rd",
+     "const double c = v[i] - rd"),
+    ("gdn2_read_before_decay",
+     "for (long j = 0; j < Dk; ++j) s[j] *= alpha[j];      /* S' */\n        double rd = 0.0;                                     /* S'(b.k) */\n        for (long j = 0; j < Dk; ++j) rd += s[j] * (erase[j] * k[j]);",
+     "double rd = 0.0;\n        for (long j = 0; j < Dk; ++j) rd += s[j] * (erase[j] * k[j]);\n        for (long j = 0; j < Dk; ++j) s[j] *= alpha[j];"),
+    ("gdn2_gate_on_value_axis", "s[j] *= alpha[j];", "s[j] *= alpha[i < Dk ? i : 0];"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(old, new, 1)
+    cpath = tmp_path / "mutant.c"
+    cpath.write_text(mutated)
+    lib = oracle.build(True, str(cpath), str(tmp_path / "libmutant.so"))
+    orc = oracle.OracleLib(lib)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {name}"
