@@ -1,0 +1,179 @@
+"""Python binding of libgdr, the gfx950 gated delta rule library.
+
+Argument marshalling only: every step of every operation runs in the HIP
+kernels behind the C ABI declared in ``include/gdr.h``.  PyTorch supplies
+device memory and the current HIP stream.  There is no CPU or PyTorch
+fallback — importing this package without the built ``libgdr.so`` fails.
+
+Functions mirror the C calls:
+
+    gdr_chunk_fwd(q, k, v, alpha, beta, s0=None, ...)            -> (o, s_final)
+    gdr_recurrent_step(q, k, v, alpha, beta, state, ...)         -> o
+    gdr2_chunk_fwd(q, k, v, alpha, erase, write, s0=None, ...)   -> (o, s_final)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime libgdr.so binds to
+
+__all__ = ["gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd",
+           "GdrError", "status_string", "lib", "LIB_PATH", "GDR_F32",
+           "GDR_BF16"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "libgdr.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g;"
+        f" g.build()'` (hipcc, gfx950) first")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+GDR_F32, GDR_BF16 = 0, 1
+_I64, _P, _E = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+
+lib.gdr_chunk_fwd.argtypes = [_I64] * 5 + [_E] + [_P] * 6 + [_E, _P, _P, _P]
+lib.gdr_chunk_fwd.restype = ctypes.c_int
+lib.gdr2_chunk_fwd.argtypes = [_I64] * 5 + [_E] + [_P] * 7 + [_E, _P, _P, _P]
+lib.gdr2_chunk_fwd.restype = ctypes.c_int
+lib.gdr_recurrent_step.argtypes = [_I64] * 4 + [_E] + [_P] * 6 + [_E, _P, _P]
+lib.gdr_recurrent_step.restype = ctypes.c_int
+lib.gdr_status_string.argtypes = [ctypes.c_int]
+lib.gdr_status_string.restype = ctypes.c_char_p
+lib.gdr_version.restype = ctypes.c_int
+
+_DT = {torch.float32: GDR_F32, torch.bfloat16: GDR_BF16}
+
+
+class GdrError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn}: {status_string(code)} (status {code})")
+        self.code = code
+
+
+def status_string(code: int) -> str:
+    return lib.gdr_status_string(int(code)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(name, t, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _run(name, code):
+    if code != 0:
+        raise GdrError(name, code)
+
+
+def gdr_chunk_fwd(q, k, v, alpha, beta, s0=None, *, out_dtype=None, o=None,
+                  s_final=None, want_state=True, stream=None):
+    """Chunkwise gated delta rule forward.
+
+    q, k [B,T,H,Dk]; v [B,T,H,Dv] (fp32 or bf16, same dtype); alpha, beta
+    [B,T,H] fp32; s0 [B,H,Dv,Dk] fp32 or None.  ``out_dtype`` defaults to
+    the input dtype.  Returns (o [B,T,H,Dv], s_final [B,H,Dv,Dk] or None).
+    ``s_final`` may be passed in (it may be ``s0`` itself).
+    """
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if q.dtype not in _DT:
+        raise TypeError(f"unsupported input dtype {q.dtype}")
+    _check("q", q, q.dtype, (B, T, H, Dk))
+    _check("k", k, q.dtype, (B, T, H, Dk))
+    _check("v", v, q.dtype, (B, T, H, Dv))
+    _check("alpha", alpha, torch.float32, (B, T, H))
+    _check("beta", beta, torch.float32, (B, T, H))
+    if s0 is not None:
+        _check("s0", s0, torch.float32, (B, H, Dv, Dk))
+    odt = q.dtype if out_dtype is None else out_dtype
+    if odt not in _DT:
+        raise TypeError(f"unsupported output dtype {odt}")
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=odt, device=q.device)
+    _check("o", o, odt, (B, T, H, Dv))
+    if s_final is None and want_state:
+        s_final = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=q.device)
+    if s_final is not None:
+        _check("s_final", s_final, torch.float32, (B, H, Dv, Dk))
+    _run("gdr_chunk_fwd", lib.gdr_chunk_fwd(
+        B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v),
+        _ptr(alpha), _ptr(beta), _ptr(s0), _DT[odt], _ptr(o), _ptr(s_final),
+        _stream(stream)))
+    return o, s_final
+
+
+def gdr2_chunk_fwd(q, k, v, alpha, erase, write, s0=None, *, out_dtype=None,
+                   o=None, s_final=None, want_state=True, stream=None):
+    """Chunkwise Gated Delta Rule-2 forward.
+
+    q, k, alpha, erase [B,T,H,Dk]; v, write [B,T,H,Dv], all one dtype (fp32
+    or bf16); s0 [B,H,Dv,Dk] fp32 or None.  Returns (o, s_final).
+    """
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if q.dtype not in _DT:
+        raise TypeError(f"unsupported input dtype {q.dtype}")
+    for name, t, d in (("q", q, Dk), ("k", k, Dk), ("alpha", alpha, Dk),
+                       ("erase", erase, Dk), ("v", v, Dv), ("write", write, Dv)):
+        _check(name, t, q.dtype, (B, T, H, d))
+    if s0 is not None:
+        _check("s0", s0, torch.float32, (B, H, Dv, Dk))
+    odt = q.dtype if out_dtype is None else out_dtype
+    if odt not in _DT:
+        raise TypeError(f"unsupported output dtype {odt}")
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=odt, device=q.device)
+    _check("o", o, odt, (B, T, H, Dv))
+    if s_final is None and want_state:
+        s_final = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=q.device)
+    if s_final is not None:
+        _check("s_final", s_final, torch.float32, (B, H, Dv, Dk))
+    _run("gdr2_chunk_fwd", lib.gdr2_chunk_fwd(
+        B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v),
+        _ptr(alpha), _ptr(erase), _ptr(write), _ptr(s0), _DT[odt], _ptr(o),
+        _ptr(s_final), _stream(stream)))
+    return o, s_final
+
+
+def gdr_recurrent_step(q, k, v, alpha, beta, state, *, out_dtype=None,
+                       o=None, stream=None):
+    """One decode token: q, k [N,H,Dk]; v [N,H,Dv]; alpha, beta [N,H] fp32;
+    state [N,H,Dv,Dk] fp32, updated in place.  Returns o [N,H,Dv]."""
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if q.dtype not in _DT:
+        raise TypeError(f"unsupported input dtype {q.dtype}")
+    _check("q", q, q.dtype, (N, H, Dk))
+    _check("k", k, q.dtype, (N, H, Dk))
+    _check("v", v, q.dtype, (N, H, Dv))
+    _check("alpha", alpha, torch.float32, (N, H))
+    _check("beta", beta, torch.float32, (N, H))
+    _check("state", state, torch.float32, (N, H, Dv, Dk))
+    odt = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, H, Dv), dtype=odt, device=q.device)
+    _check("o", o, odt, (N, H, Dv))
+    _run("gdr_recurrent_step", lib.gdr_recurrent_step(
+        N, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+        _ptr(beta), _ptr(state), _DT[odt], _ptr(o), _stream(stream)))
+    return o

@@ -1,0 +1,183 @@
+// C ABI of libgdr: host-side validation and dispatch (declared in gdr.h).
+//
+// Every check runs on the host before anything is enqueued, so an error
+// status means nothing was written.  No exception leaves this file.
+#include "../../include/gdr.h"
+#include "gdr_device.h"
+#include "launch.h"
+
+namespace gdr {
+
+namespace {
+
+__global__ void state_copy_kernel(const float* __restrict__ s0, float* __restrict__ s,
+                                  int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) s[i] = s0 ? s0[i] : 0.f;
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dims_ok(int64_t dk, int64_t dv) {
+    return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
+}
+
+bool dtype_ok(gdr_dtype_t d) { return d == GDR_F32 || d == GDR_BF16; }
+
+gdr_status_t from_hip(hipError_t e) { return e == hipSuccess ? GDR_OK : GDR_ERR_DEVICE; }
+
+// Every listed pointer must be non-NULL and 16-byte aligned.
+bool ptrs_ok(std::initializer_list<const void*> ps) {
+    for (const void* p : ps)
+        if (!p || !aligned(p)) return false;
+    return true;
+}
+
+bool opt_ok(const void* p) { return !p || aligned(p); }
+
+// Largest element count of any tensor must fit the kernels' 64-bit offsets
+// and the grid must fit 2^31 - 1 workgroups.
+bool sizes_ok(int64_t a, int64_t b, int64_t c) {
+    if (a < 0 || b < 0 || c < 0) return false;
+    const double n = (double)a * (double)b * (double)c;
+    return n < 4.0e18;
+}
+
+}  // namespace
+
+hipError_t launch_state_copy(const float* s0, float* s_final, int64_t n, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st, s0,
+                       s_final, n);
+    return hipGetLastError();
+}
+
+}  // namespace gdr
+
+using namespace gdr;
+
+static gdr_status_t chunk_common(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                 gdr_dtype_t in_dt, gdr_dtype_t out_dt, ChunkArgs& a) {
+    if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0) return GDR_ERR_INVALID;
+    if (!sizes_ok(B, T, H) || !sizes_ok(B * T * H, Dk > Dv ? Dk : Dv, 1)) return GDR_ERR_INVALID;
+    if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return GDR_ERR_UNSUPPORTED;
+    if (!dims_ok(Dk, Dv)) return GDR_ERR_UNSUPPORTED;
+    if (B * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.Dk = Dk;
+    a.Dv = Dv;
+    a.in_bf16 = in_dt == GDR_BF16;
+    a.out_bf16 = out_dt == GDR_BF16;
+    return GDR_OK;
+}
+
+static gdr_status_t chunk_run(ChunkArgs& a) {
+    if (a.B == 0 || a.H == 0) return GDR_OK;
+    if (a.T == 0) {
+        if (!a.s_final || a.s_final == a.s0) return GDR_OK;
+        return from_hip(launch_state_copy(a.s0, a.s_final, a.B * a.H * a.Dv * a.Dk, a.stream));
+    }
+    hipError_t e;
+    if (!a.in_bf16)
+        e = launch_chunk_f32(a);
+    else if (a.gated2)
+        e = launch_gdr2_bf16(a);
+    else
+        e = launch_chunk_bf16(a);
+    return from_hip(e);
+}
+
+extern "C" gdr_status_t gdr_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                      int64_t Dv, gdr_dtype_t in_dt, const void* q,
+                                      const void* k, const void* v, const float* alpha,
+                                      const float* beta, const float* s0,
+                                      gdr_dtype_t out_dt, void* o, float* s_final,
+                                      hipStream_t stream) {
+    ChunkArgs a{};
+    gdr_status_t st = chunk_common(B, T, H, Dk, Dv, in_dt, out_dt, a);
+    if (st != GDR_OK) return st;
+    const bool empty = B == 0 || T == 0 || H == 0;
+    if (!empty && !ptrs_ok({q, k, v, alpha, beta, o})) return GDR_ERR_INVALID;
+    if (!opt_ok(s0) || !opt_ok(s_final)) return GDR_ERR_INVALID;
+    a.gated2 = false;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.s0 = s0;
+    a.o = o;
+    a.s_final = s_final;
+    a.stream = stream;
+    return chunk_run(a);
+}
+
+extern "C" gdr_status_t gdr2_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                       int64_t Dv, gdr_dtype_t in_dt, const void* q,
+                                       const void* k, const void* v, const void* alpha,
+                                       const void* erase, const void* write,
+                                       const float* s0, gdr_dtype_t out_dt, void* o,
+                                       float* s_final, hipStream_t stream) {
+    ChunkArgs a{};
+    gdr_status_t st = chunk_common(B, T, H, Dk, Dv, in_dt, out_dt, a);
+    if (st != GDR_OK) return st;
+    const bool empty = B == 0 || T == 0 || H == 0;
+    if (!empty && !ptrs_ok({q, k, v, alpha, erase, write, o})) return GDR_ERR_INVALID;
+    if (!opt_ok(s0) || !opt_ok(s_final)) return GDR_ERR_INVALID;
+    a.gated2 = true;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.erase = erase;
+    a.write = write;
+    a.s0 = s0;
+    a.o = o;
+    a.s_final = s_final;
+    a.stream = stream;
+    return chunk_run(a);
+}
+
+extern "C" gdr_status_t gdr_recurrent_step(int64_t N, int64_t H, int64_t Dk, int64_t Dv,
+                                           gdr_dtype_t in_dt, const void* q, const void* k,
+                                           const void* v, const float* alpha,
+                                           const float* beta, float* state,
+                                           gdr_dtype_t out_dt, void* o, hipStream_t stream) {
+    if (N < 0 || H < 0 || Dk < 0 || Dv < 0) return GDR_ERR_INVALID;
+    if (!sizes_ok(N, H, 1) || N * H > 0x7fffffffLL) return GDR_ERR_INVALID;
+    if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return GDR_ERR_UNSUPPORTED;
+    if (!dims_ok(Dk, Dv)) return GDR_ERR_UNSUPPORTED;
+    if (N == 0 || H == 0) return GDR_OK;
+    if (!ptrs_ok({q, k, v, alpha, beta, state, o})) return GDR_ERR_INVALID;
+    StepArgs a;
+    a.N = N;
+    a.H = H;
+    a.Dk = Dk;
+    a.Dv = Dv;
+    a.in_bf16 = in_dt == GDR_BF16;
+    a.out_bf16 = out_dt == GDR_BF16;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.state = state;
+    a.o = o;
+    a.stream = stream;
+    return from_hip(launch_step(a));
+}
+
+extern "C" const char* gdr_status_string(gdr_status_t s) {
+    switch (s) {
+        case GDR_OK: return "ok";
+        case GDR_ERR_INVALID: return "invalid argument (NULL or misaligned pointer, or bad size)";
+        case GDR_ERR_UNSUPPORTED: return "unsupported head dims or dtype";
+        case GDR_ERR_DEVICE: return "HIP runtime error at launch";
+    }
+    return "unknown status";
+}
+
+extern "C" int gdr_version(void) { return 100; }

@@ -1,0 +1,46 @@
+// Internal launch interface between the C ABI (gdr_api.cpp) and the kernels.
+// Arguments arrive here already validated: dims in {64, 128}, sizes > 0.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+struct StepArgs {
+    int64_t N, H, Dk, Dv;
+    bool in_bf16, out_bf16;
+    const void *q, *k, *v;
+    const float *alpha, *beta;
+    float* state;
+    void* o;
+    hipStream_t stream;
+};
+
+// One struct for both chunked rules.  For the scalar-gated rule alpha and
+// beta are fp32 [B,T,H] and erase/write are unused; for Gated Delta Rule-2
+// alpha, erase ([B,T,H,Dk]) and write ([B,T,H,Dv]) are in the input dtype
+// and beta is unused.
+struct ChunkArgs {
+    int64_t B, T, H, Dk, Dv;
+    bool in_bf16, out_bf16;
+    bool gated2;
+    const void *q, *k, *v;
+    const void *alpha, *beta, *erase, *write;
+    const float* s0;
+    void* o;
+    float* s_final;
+    hipStream_t stream;
+};
+
+hipError_t launch_step(const StepArgs& a);
+// fp32 inputs: VALU kernels, both rules.
+hipError_t launch_chunk_f32(const ChunkArgs& a);
+// bf16 inputs, scalar gates: bf16 MFMA kernel.
+hipError_t launch_chunk_bf16(const ChunkArgs& a);
+// bf16 inputs, channel gates: bf16 MFMA kernel.
+hipError_t launch_gdr2_bf16(const ChunkArgs& a);
+// Copy s0 (or zeros) into s_final for an empty sequence.
+hipError_t launch_state_copy(const float* s0, float* s_final, int64_t n, hipStream_t st);
+
+}  // namespace gdr

@@ -1,0 +1,166 @@
+/*
+ * gdr.h — C ABI of the MI355X (gfx950) gated delta rule library, libgdr.so.
+ *
+ * Three operations, each evaluated by hand-written HIP kernels:
+ *
+ *   gdr_chunk_fwd       chunkwise-parallel forward of the gated delta rule
+ *   gdr_recurrent_step  one decode token of the same rule, state in place
+ *   gdr2_chunk_fwd      chunkwise forward of Gated Delta Rule-2 (channel gates)
+ *
+ * The rule ("Gated Delta Networks", agihunt.info, "Method"; review of GDN on
+ * meaningful96.github.io, section 3.4; inputs and outputs from its
+ * section 1 "Problem Formulation"):
+ *
+ *   S_t = S_{t-1} alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *   o_t = S_t q_t,
+ *
+ * with the state S a d_v x d_k fp32 matrix per (sequence, head).  No scale
+ * is applied to q (o_t = S_t q_t exactly); q and k are expected to be
+ * L2-normalised by the caller, as the block does before the mixer
+ * (review section 3.8), but nothing here depends on it for correctness.
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; tensors
+ *     are contiguous and row-major in the layouts given per argument.  The
+ *     library keeps no allocation and no state between calls and calls no
+ *     allocator.
+ *   - Calls are asynchronous on `stream` (0 = the null stream) and return
+ *     after the kernels are enqueued.
+ *   - Arguments are validated on the host before anything is launched; on
+ *     any error nothing is written.  Status codes:
+ *       GDR_ERR_INVALID      a required pointer is NULL, a size is negative,
+ *                            or a pointer is not 16-byte aligned;
+ *       GDR_ERR_UNSUPPORTED  (Dk, Dv) not in {64, 128} x {64, 128}, or an
+ *                            unsupported dtype;
+ *       GDR_ERR_DEVICE       the HIP runtime reported a launch error.
+ *     No C++ exception crosses this interface.
+ *   - Values are not checked on the device: NaN/Inf propagate.  Decay gates
+ *     are used through their logarithm, clamped below at log(FLT_MIN), so a
+ *     gate of exactly 0 acts as a full reset without producing NaN.
+ *   - Gate ranges: alpha in (0, 1]; beta, erase, write in [0, 1].
+ *   - T, B, H, N may be 0 (nothing is launched; s_final receives s0 or zeros
+ *     when T == 0 and B*H > 0).  Any T >= 1 is accepted: the sequence is cut
+ *     into internal chunks and the last one is partial.  The chunk length is
+ *     not a parameter; results do not depend on it beyond rounding.
+ *   - s0 == NULL means a zero initial state; s_final == NULL means the final
+ *     state is not written.  s0 and s_final may be the same buffer.  q, k, v
+ *     and the gates must not overlap o or s_final.
+ *   - Thread safety: calls carry no shared mutable state and may be issued
+ *     from several host threads on different streams.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDR_OK = 0,
+    GDR_ERR_INVALID = 1,
+    GDR_ERR_UNSUPPORTED = 2,
+    GDR_ERR_DEVICE = 3
+} gdr_status_t;
+
+typedef enum {
+    GDR_F32 = 0,   /* IEEE binary32 */
+    GDR_BF16 = 1   /* bfloat16, round-to-nearest-even on every store */
+} gdr_dtype_t;
+
+/*
+ * Chunkwise forward of the gated delta rule over whole sequences.
+ *
+ * Algorithm: the chunkwise UT/WY form of the rule ("Gated Delta Networks",
+ * "Method": chunkwise algorithm via the UT transform; review section 3.7,
+ * the equations for U^g, S_[t+1] and O_[t]).  Within a chunk the scalar
+ * gates enter through Gamma_rs = exp(g_r - g_s), g the within-chunk
+ * cumulative log alpha; chunks are chained through the fp32 state.
+ *
+ *   B, T, H     batch, sequence length, heads (each >= 0)
+ *   Dk, Dv      key and value head dims, each 64 or 128
+ *   in_dt       dtype of q, k, v (GDR_F32 or GDR_BF16)
+ *   q, k        [B, T, H, Dk] in_dt
+ *   v           [B, T, H, Dv] in_dt
+ *   alpha, beta [B, T, H] fp32 (scalar gates per token and head)
+ *   s0          [B, H, Dv, Dk] fp32 or NULL (zero initial state)
+ *   out_dt      dtype of o (GDR_F32 or GDR_BF16)
+ *   o           [B, T, H, Dv] out_dt  (output, o_t = S_t q_t)
+ *   s_final     [B, H, Dv, Dk] fp32 or NULL; may alias s0
+ *
+ * Precision: fp32 inputs are computed in fp32.  bf16 inputs run on bf16
+ * matrix cores with fp32 accumulation; every product whose operand is a
+ * computed (not input) value uses a two-term bf16 split of that operand, so
+ * products carry ~16 significant bits.  Output rounding to bf16 (out_dt =
+ * GDR_BF16) adds up to half a bf16 ulp of each output.
+ */
+gdr_status_t gdr_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                           int64_t Dv, gdr_dtype_t in_dt, const void *q,
+                           const void *k, const void *v, const float *alpha,
+                           const float *beta, const float *s0,
+                           gdr_dtype_t out_dt, void *o, float *s_final,
+                           hipStream_t stream);
+
+/*
+ * One decode token for N independent sequences, the state updated in place.
+ *
+ * For each (n, h) and each row i of S (value channel i), in one pass over
+ * the old row: a_i = s_i . k, c_i = s_i . q; d_i = beta (v_i - alpha a_i);
+ * s_i <- alpha s_i + d_i k; o_i = alpha c_i + d_i (k . q).  This is the rule
+ * above for a single token with a fixed-size state (constant memory per
+ * decoded token, as both GDN summaries describe decoding).
+ *
+ *   N, H        sequences, heads (each >= 0)
+ *   Dk, Dv      64 or 128
+ *   in_dt       dtype of q, k, v
+ *   q, k        [N, H, Dk] in_dt
+ *   v           [N, H, Dv] in_dt
+ *   alpha, beta [N, H] fp32
+ *   state       [N, H, Dv, Dk] fp32, read and overwritten
+ *   out_dt      dtype of o
+ *   o           [N, H, Dv] out_dt
+ */
+gdr_status_t gdr_recurrent_step(int64_t N, int64_t H, int64_t Dk, int64_t Dv,
+                                gdr_dtype_t in_dt, const void *q,
+                                const void *k, const void *v,
+                                const float *alpha, const float *beta,
+                                float *state, gdr_dtype_t out_dt, void *o,
+                                hipStream_t stream);
+
+/*
+ * Chunkwise forward of Gated Delta Rule-2 ("Gated DeltaNet-2",
+ * agihunt.info: per token, decay the state with the per-channel alpha_t on
+ * the key axis, read the old value along b_t (.) k_t, write the residual of
+ * w_t (.) v_t against that read along k_t; in chunks, the channel decay is
+ * absorbed into an asymmetric rank-1 erase factor and solved in WY form):
+ *
+ *   S' = S_{t-1} diag(alpha_t),
+ *   S_t = S' + (w_t (.) v_t - S' (b_t (.) k_t)) k_t^T,   o_t = S_t q_t.
+ *
+ *   q, k        [B, T, H, Dk] in_dt
+ *   v           [B, T, H, Dv] in_dt
+ *   alpha       [B, T, H, Dk] in_dt, per-key-channel decay in (0, 1]
+ *   erase       [B, T, H, Dk] in_dt, b in [0, 1]
+ *   write       [B, T, H, Dv] in_dt, w in [0, 1]
+ *   s0, s_final, o, out_dt as for gdr_chunk_fwd.
+ */
+gdr_status_t gdr2_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                            int64_t Dv, gdr_dtype_t in_dt, const void *q,
+                            const void *k, const void *v, const void *alpha,
+                            const void *erase, const void *write,
+                            const float *s0, gdr_dtype_t out_dt, void *o,
+                            float *s_final, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *gdr_status_string(gdr_status_t s);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int gdr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

@@ -1,0 +1,109 @@
+"""The C ABI on the CPU: the library loads, exports every function gdr.h
+declares, and validates arguments on the host (no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+
+@pytest.fixture(scope="module")
+def gdr():
+    import gated_delta_rule_16_amd as g
+    return g
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(",
+                      src, flags=re.M)
+
+
+def test_header_declares_the_three_operations():
+    names = declared_functions()
+    for n in ("gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd",
+              "gdr_status_string", "gdr_version"):
+        assert n in names, names
+
+
+def test_every_declared_symbol_is_exported(gdr):
+    for n in declared_functions():
+        assert hasattr(gdr.lib, n), f"{n} not exported by libgdr.so"
+
+
+def test_status_strings(gdr):
+    assert gdr.status_string(0) == "ok"
+    for c in (1, 2, 3):
+        assert gdr.status_string(c) != "unknown status"
+    assert gdr.lib.gdr_version() >= 100
+
+
+A16 = 1 << 20          # a fake, 16-byte aligned "device" address
+BAD = A16 + 4          # misaligned
+
+
+def chunk(gdr, B=1, T=8, H=1, Dk=64, Dv=64, dt=1, q=A16, k=A16, v=A16,
+          a=A16, b=A16, s0=None, odt=1, o=A16, sf=None):
+    return gdr.lib.gdr_chunk_fwd(B, T, H, Dk, Dv, dt, q, k, v, a, b, s0, odt,
+                                 o, sf, None)
+
+
+def chunk2(gdr, B=1, T=8, H=1, Dk=64, Dv=64, dt=1, q=A16, k=A16, v=A16,
+           a=A16, e=A16, w=A16, s0=None, odt=1, o=A16, sf=None):
+    return gdr.lib.gdr2_chunk_fwd(B, T, H, Dk, Dv, dt, q, k, v, a, e, w, s0,
+                                  odt, o, sf, None)
+
+
+def step(gdr, N=2, H=1, Dk=64, Dv=64, dt=1, q=A16, k=A16, v=A16, a=A16,
+         b=A16, s=A16, odt=1, o=A16):
+    return gdr.lib.gdr_recurrent_step(N, H, Dk, Dv, dt, q, k, v, a, b, s, odt,
+                                      o, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1),
+    (dict(a=None), 1), (dict(b=None), 1), (dict(o=None), 1),
+    (dict(q=BAD), 1), (dict(o=BAD), 1), (dict(s0=BAD), 1), (dict(sf=BAD), 1),
+    (dict(B=-1), 1), (dict(T=-1), 1), (dict(H=-1), 1),
+    (dict(Dk=96), 2), (dict(Dv=32), 2), (dict(Dk=0), 2), (dict(dt=7), 2),
+    (dict(odt=5), 2),
+])
+def test_chunk_fwd_validation(gdr, kw, code):
+    assert chunk(gdr, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(a=None), 1), (dict(e=None), 1), (dict(w=None), 1),
+    (dict(e=BAD), 1), (dict(B=-3), 1), (dict(Dk=48), 2), (dict(dt=9), 2),
+])
+def test_gdr2_chunk_fwd_validation(gdr, kw, code):
+    assert chunk2(gdr, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(s=None), 1), (dict(s=BAD), 1), (dict(o=None), 1),
+    (dict(N=-1), 1), (dict(Dk=256), 2), (dict(Dv=100), 2), (dict(dt=3), 2),
+])
+def test_recurrent_step_validation(gdr, kw, code):
+    assert step(gdr, **kw) == code
+
+
+def test_empty_calls_launch_nothing(gdr):
+    # nothing to do: returns OK without touching the device
+    assert chunk(gdr, B=0, q=None, k=None, v=None, a=None, b=None, o=None) == 0
+    assert chunk(gdr, H=0, q=None, k=None, v=None, a=None, b=None, o=None) == 0
+    assert chunk(gdr, T=0, q=None, k=None, v=None, a=None, b=None, o=None) == 0
+    assert step(gdr, N=0, q=None, k=None, v=None, a=None, b=None, s=None,
+                o=None) == 0
+    assert chunk2(gdr, B=0, q=None) == 0
+
+
+def test_binding_rejects_cpu_tensors(gdr):
+    import torch
+    x = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(ValueError):
+        gdr.gdr_chunk_fwd(x, x, x, torch.zeros(1, 4, 1), torch.zeros(1, 4, 1))

@@ -1,0 +1,160 @@
+"""GPU parity: the HIP kernels against the fp64 oracle, element by element.
+
+Metric: max_i |x_hat_i - x_i| / rms(x) over the whole output (oracle.err_rms).
+Tolerances from the stated bar: 1e-3 for fp32 inputs, 2e-2 for bf16 inputs,
+on o and on the final state alike.  bf16 *outputs* are additionally allowed
+their own rounding (half a bf16 ulp per element, measured on the oracle's
+output as ``floor``): the largest outputs of these workloads reach ~14x the
+RMS, so bf16 rounding alone costs up to ~0.04 on this metric.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gdr_gen import make_config, make_decode, make_gdn, make_gdn2
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-3, "bf16": 2e-2}
+DEV = "cuda"
+
+
+def _bf16_floor(x):
+    xb = torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return oracle.err_rms(xb.double().numpy(), x)
+
+
+def _tol(in_dt, out_dt, o_ref):
+    t = TOL[in_dt]
+    if out_dt == "bf16":
+        t = t + _bf16_floor(o_ref)
+    return t
+
+
+def _gpu(x):
+    return None if x is None else x.to(DEV)
+
+
+def _odt(name):
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+# ---------------------------------------------------------------- decode ----
+
+@pytest.mark.parametrize("dims", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("dt,odt", [("f32", "f32"), ("bf16", "f32"),
+                                    ("bf16", "bf16")])
+def test_step_small(gdr_lib, dims, dt, odt):
+    Dk, Dv = dims
+    inp = make_decode(N=5, H=3, Dk=Dk, Dv=Dv, steps=4, dtype=dt, seed=7)
+    st_ref = inp.state0.double().numpy().copy()
+    st = _gpu(inp.state0.clone())
+    for s in range(4):
+        o_ref = oracle.gdn_step(inp.q[s], inp.k[s], inp.v[s], inp.alpha[s],
+                                inp.beta[s], st_ref)
+        o = gdr_lib.gdr_recurrent_step(_gpu(inp.q[s]), _gpu(inp.k[s]),
+                                       _gpu(inp.v[s]), _gpu(inp.alpha[s]),
+                                       _gpu(inp.beta[s]), st,
+                                       out_dtype=_odt(odt))
+        torch.cuda.synchronize()
+        assert oracle.err_rms(o.cpu(), o_ref) <= _tol(dt, odt, o_ref)
+        assert oracle.err_rms(st.cpu(), st_ref) <= TOL[dt]
+
+
+def test_step_decode_workload_sampled(gdr_lib):
+    """Decode workload at full size (256 sequences x 16 heads, d = 128, 64
+    steps, the launch the benchmark times); the oracle follows a sample of
+    32 sequences through all 64 steps."""
+    inp = make_config(3)
+    S = _gpu(inp.state0)
+    pick = torch.arange(0, 256, 8)
+    st_ref = inp.state0[pick].double().numpy().copy()
+    q, k, v = _gpu(inp.q), _gpu(inp.k), _gpu(inp.v)
+    a, b = _gpu(inp.alpha), _gpu(inp.beta)
+    errs = []
+    for s in range(inp.meta["steps"]):
+        o = gdr_lib.gdr_recurrent_step(q[s], k[s], v[s], a[s], b[s], S,
+                                       out_dtype=torch.float32)
+        o_ref = oracle.gdn_step(inp.q[s][pick], inp.k[s][pick],
+                                inp.v[s][pick], inp.alpha[s][pick],
+                                inp.beta[s][pick], st_ref)
+        errs.append(oracle.err_rms(o[pick.to(DEV)].cpu(), o_ref))
+    torch.cuda.synchronize()
+    assert max(errs) <= TOL["bf16"], max(errs)
+    assert oracle.err_rms(S[pick.to(DEV)].cpu(), st_ref) <= TOL["bf16"]
+
+
+# ------------------------------------------------- fp32 chunked forward ----
+
+def _run_gdn(gdr_lib, inp, odt, s_final_alias=False):
+    s0 = _gpu(inp.s0)
+    sf = s0 if (s_final_alias and s0 is not None) else None
+    o, s = gdr_lib.gdr_chunk_fwd(_gpu(inp.q), _gpu(inp.k), _gpu(inp.v),
+                                 _gpu(inp.alpha), _gpu(inp.beta), s0,
+                                 out_dtype=_odt(odt), s_final=sf)
+    torch.cuda.synchronize()
+    return o.cpu(), s.cpu()
+
+
+def _run_gdn2(gdr_lib, inp, odt):
+    o, s = gdr_lib.gdr2_chunk_fwd(_gpu(inp.q), _gpu(inp.k), _gpu(inp.v),
+                                  _gpu(inp.alpha), _gpu(inp.erase),
+                                  _gpu(inp.write), _gpu(inp.s0),
+                                  out_dtype=_odt(odt))
+    torch.cuda.synchronize()
+    return o.cpu(), s.cpu()
+
+
+def _check_gdn(gdr_lib, inp, odt, alias=False):
+    o_ref, s_ref = oracle.gdn_fwd(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
+                                  inp.s0)
+    o, s = _run_gdn(gdr_lib, inp, odt, alias)
+    eo, es = oracle.err_rms(o, o_ref), oracle.err_rms(s, s_ref)
+    assert eo <= _tol(inp.dtype, odt, o_ref), (eo, es)
+    assert es <= TOL[inp.dtype], (eo, es)
+    return eo, es
+
+
+def _check_gdn2(gdr_lib, inp, odt):
+    o_ref, s_ref = oracle.gdn2_fwd(inp.q, inp.k, inp.v, inp.alpha, inp.erase,
+                                   inp.write, inp.s0)
+    o, s = _run_gdn2(gdr_lib, inp, odt)
+    eo, es = oracle.err_rms(o, o_ref), oracle.err_rms(s, s_ref)
+    assert eo <= _tol(inp.dtype, odt, o_ref), (eo, es)
+    assert es <= TOL[inp.dtype], (eo, es)
+    return eo, es
+
+
+def test_gdn_tiny_fp32_workload(gdr_lib):
+    """The tiny fp32 workload: B1 H2 T256 d64, zero state."""
+    _check_gdn(gdr_lib, make_config(0), "f32")
+
+
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 63, 64, 65, 100, 127, 200])
+def test_gdn_fp32_ragged(gdr_lib, T):
+    inp = make_gdn(B=2, T=T, H=3, Dk=64, Dv=64, dtype="f32", seed=T,
+                   s0_std=0.5)
+    _check_gdn(gdr_lib, inp, "f32")
+
+
+@pytest.mark.parametrize("dims", [(128, 128), (128, 64), (64, 128)])
+def test_gdn_fp32_dims(gdr_lib, dims):
+    inp = make_gdn(B=1, T=150, H=2, Dk=dims[0], Dv=dims[1], dtype="f32",
+                   seed=11, s0_std=0.3)
+    _check_gdn(gdr_lib, inp, "f32")
+    _check_gdn(gdr_lib, inp, "bf16")
+
+
+def test_gdn_fp32_state_alias(gdr_lib):
+    inp = make_gdn(B=2, T=77, H=2, Dk=64, Dv=64, dtype="f32", seed=3,
+                   s0_std=0.5)
+    _check_gdn(gdr_lib, inp, "f32", alias=True)
+
+
+@pytest.mark.parametrize("T", [1, 33, 64, 129])
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128)])
+def test_gdn2_fp32(gdr_lib, T, dims):
+    inp = make_gdn2(B=1, T=T, H=2, Dk=dims[0], Dv=dims[1], dtype="f32",
+                    seed=T + dims[0], s0_std=0.5)
+    _check_gdn2(gdr_lib, inp, "f32")
