@@ -1,7 +1,466 @@
-// placeholder: bf16 MFMA kernels are added next
-#include "gdr_device.h"
+// bf16-input path of gdr_chunk_fwd: the chunkwise UT/WY form of the gated
+// delta rule on gfx950 bf16 matrix cores, one fused pass over the sequence.
+//
+// Chunk algebra (rows of the state S are value channels; within a chunk of
+// C = 64 tokens, g_r = sum_{i<=r} log alpha_i, gamma_r = e^{g_r}; this is
+// the review's section 3.7 system on meaningful96.github.io with Gamma_rs =
+// e^{g_r - g_s}, the output mask carrying that decay and its diagonal, and
+// U^g - W S^T regrouped as T R):
+//
+//   A_rs  = beta_r e^{g_r - g_s} k_r . k_s            s < r
+//   T     = (I + A)^{-1}                              (depends on keys only)
+//   R_s   = beta_s (v_s - gamma_s S k_s)              (needs the state)
+//   V_new = T R
+//   P_rs  = e^{g_r - g_s} q_r . k_s                   s <= r
+//   o_r   = gamma_r S q_r + sum_{s<=r} P_rs V_new_s
+//   S    <- gamma_C S + sum_s (e^{g_C - g_s} V_new_s) k_s^T
+//
+// Work split: one 256-thread workgroup (4 waves) per (b, h, 64 state rows);
+// rows of S evolve independently given the key side, so Dv = 128 runs as
+// two workgroups per head that both build A, T and P.  The workgroup walks
+// the chunks in order with S resident: fp32 in matrix-core accumulators
+// (as S^T tiles) and a bf16 hi/lo copy in LDS for use as an operand.  The
+// next chunk's q, k, v, alpha, beta are loaded into registers while the
+// current chunk computes.
+//
+// Per chunk (32x32x16 bf16 MFMA tiles, 4 waves):
+//   (1) K K^T and K Q^T lower tiles -> A (fp32) and P (hi/lo)     48 MFMA
+//   (2) K S^T -> R (hi/lo), Q S^T kept in registers             128 MFMA
+//   (3) T = (I + A)^{-1} by forward substitution in fp32 VALU
+//   (4) V_new = T R -> V_new and decayed V_new (hi/lo)             48 MFMA
+//   (5) o = gamma (Q S^T) + P V_new -> HBM                         48 MFMA
+//   (6) S^T = gamma_C S^T + K^T V'                                 64 MFMA
 #include "launch.h"
+#include "mfma_common.h"
+
 namespace gdr {
-hipError_t launch_chunk_bf16(const ChunkArgs&) { return hipErrorNotSupported; }
-hipError_t launch_gdr2_bf16(const ChunkArgs&) { return hipErrorNotSupported; }
+
+namespace {
+
+constexpr int CH = 64;    // tokens per chunk
+constexpr int RB = 64;    // state rows per workgroup
+constexpr int NT = 256;   // threads per workgroup
+constexpr int P72 = 72;   // pitch (elements) of 64-deep contraction-major tiles
+constexpr int PA = 68;    // pitch (floats) of the fp32 A tile
+
+struct Bf16Params {
+    int64_t T, H;
+    const bf16_t *q, *k, *v;
+    const float *alpha, *beta;
+    const float* s0;
+    void* o;
+    float* s_final;
+};
+
+template <int DK>
+struct Smem {
+    static constexpr int PK = DK + 8;  // pitch of K, Q, S rows (elements)
+    static constexpr int KB_SZ = 64 * PK * 2;
+    static constexpr int T_SZ = 2 * 64 * P72 * 2;
+    static constexpr int A_SZ = 64 * PA * 4;
+    static constexpr int N_SZ = 2 * RB * P72 * 2;
+    static constexpr int R0 = 0;                       // K tile | T hi, lo
+    static constexpr int QB = R0 + (KB_SZ > T_SZ ? KB_SZ : T_SZ);
+    static constexpr int KT = QB + KB_SZ;              // K^T [DK][P72]
+    static constexpr int VT = KT + DK * P72 * 2;       // V^T [RB][P72]
+    static constexpr int SH = VT + RB * P72 * 2;       // S hi [RB][PK]
+    static constexpr int SL = SH + RB * PK * 2;        // S lo
+    static constexpr int AN = SL + RB * PK * 2;        // A fp32 | V_new^T hi, lo
+    static constexpr int PP = AN + (A_SZ > N_SZ ? A_SZ : N_SZ);  // P hi, lo
+    static constexpr int RM = PP + 2 * 64 * P72 * 2;   // R^T hi, lo | V'^T hi, lo
+    static constexpr int GT = RM + 2 * RB * P72 * 2;   // g, beta, gamma, decay-to-end
+    static constexpr int TOTAL = GT + 4 * CH * 4;
+};
+
+template <int DK, int DV, typename TOut>
+__global__ __launch_bounds__(NT) void chunk_bf16_kernel(Bf16Params p) {
+    using M = Smem<DK>;
+    constexpr int PK = M::PK;
+    constexpr int NRB = DV / RB;
+    constexpr int KC = DK / 8;               // 16-byte pieces per key row
+    constexpr int KLD = CH * KC / NT;        // key (and query) pieces per thread
+    constexpr int VC = RB / 8;               // 16-byte pieces per value row slice
+    constexpr int VLD = CH * VC / NT;
+    constexpr int NS = DK / 64;              // S^T tiles per wave
+    static_assert(KLD * NT == CH * KC && VLD * NT == CH * VC, "load split");
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    bf16_t* Kb = reinterpret_cast<bf16_t*>(smem + M::R0);
+    bf16_t* Th = Kb;
+    bf16_t* Tl = Th + 64 * P72;
+    bf16_t* Qb = reinterpret_cast<bf16_t*>(smem + M::QB);
+    bf16_t* KT = reinterpret_cast<bf16_t*>(smem + M::KT);
+    bf16_t* VT = reinterpret_cast<bf16_t*>(smem + M::VT);
+    bf16_t* Sh = reinterpret_cast<bf16_t*>(smem + M::SH);
+    bf16_t* Sl = reinterpret_cast<bf16_t*>(smem + M::SL);
+    float* Af = reinterpret_cast<float*>(smem + M::AN);
+    bf16_t* Nh = reinterpret_cast<bf16_t*>(smem + M::AN);
+    bf16_t* Nl = Nh + RB * P72;
+    bf16_t* Ph = reinterpret_cast<bf16_t*>(smem + M::PP);
+    bf16_t* Pl = Ph + 64 * P72;
+    bf16_t* Rh = reinterpret_cast<bf16_t*>(smem + M::RM);
+    bf16_t* Rl = Rh + RB * P72;
+    bf16_t* Mh = Rh;
+    bf16_t* Ml = Rl;
+    float* g_s = reinterpret_cast<float*>(smem + M::GT);
+    float* b_s = g_s + CH;
+    float* gam_s = b_s + CH;
+    float* dec_s = gam_s + CH;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+    const int rbk = blockIdx.x % NRB;
+    const int64_t bh = blockIdx.x / NRB;
+    const int64_t H = p.H, T = p.T;
+    const int64_t h = bh % H;
+    const int64_t b = bh / H;
+    const int row0 = rbk * RB;
+    // tile of the 64 x 64 (token x state-row) products owned by this wave
+    const int tb = wave >> 1;
+    const int ib = wave & 1;
+
+    // ---- initial state: S^T tiles in accumulators, hi/lo S in LDS --------
+    f32x16 sacc[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        const int t = wave * NS + u;
+        const int dkb = t >> 1, ibs = t & 1;
+        const int i = ibs * 32 + l32;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int dk = dkb * 32 + 8 * j + 4 * hi;
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (p.s0)
+                x = *reinterpret_cast<const f32x4*>(p.s0 + ((bh * DV + row0 + i) * DK + dk));
+            sacc[u][4 * j + 0] = x.x;
+            sacc[u][4 * j + 1] = x.y;
+            sacc[u][4 * j + 2] = x.z;
+            sacc[u][4 * j + 3] = x.w;
+            st4_split(Sh + i * PK + dk, Sl + i * PK + dk, x.x, x.y, x.z, x.w);
+        }
+    }
+
+    // ---- register prefetch of one chunk -----------------------------------
+    u32x4 pk[KLD], pq[KLD], pv[VLD];
+    float pa = 1.f, pb = 0.f;
+    auto prefetch = [&](int64_t t0) {
+#pragma unroll
+        for (int m = 0; m < KLD; ++m) {
+            const int c = tid + NT * m;
+            const int row = c / KC, col = (c % KC) * 8;
+            const int64_t tok = t0 + row;
+            if (tok < T) {
+                const int64_t off = ((b * T + tok) * H + h) * DK + col;
+                pk[m] = *reinterpret_cast<const u32x4*>(p.k + off);
+                pq[m] = *reinterpret_cast<const u32x4*>(p.q + off);
+            } else {
+                pk[m] = u32x4{0u, 0u, 0u, 0u};
+                pq[m] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < VLD; ++m) {
+            const int c = tid + NT * m;
+            const int row = c / VC, col = (c % VC) * 8;
+            const int64_t tok = t0 + row;
+            if (tok < T)
+                pv[m] = *reinterpret_cast<const u32x4*>(
+                    p.v + (((b * T + tok) * H + h) * DV + row0 + col));
+            else
+                pv[m] = u32x4{0u, 0u, 0u, 0u};
+        }
+        if (tid < CH) {
+            const int64_t tok = t0 + tid;
+            pa = tok < T ? p.alpha[(b * T + tok) * H + h] : 1.f;
+            pb = tok < T ? p.beta[(b * T + tok) * H + h] : 0.f;
+        }
+    };
+
+    prefetch(0);
+    const int64_t nch = (T + CH - 1) / CH;
+    for (int64_t c = 0; c < nch; ++c) {
+        const int64_t t0 = c * CH;
+        const int n = (int)((T - t0) < CH ? (T - t0) : CH);
+        lds_barrier();
+        // ---- stage the chunk: K, Q row-major; K^T, V^T contraction-major ---
+#pragma unroll
+        for (int m = 0; m < KLD; ++m) {
+            const int cc = tid + NT * m;
+            const int row = cc / KC, col = (cc % KC) * 8;
+            *reinterpret_cast<u32x4*>(Kb + row * PK + col) = pk[m];
+            *reinterpret_cast<u32x4*>(Qb + row * PK + col) = pq[m];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                KT[(col + 2 * x) * P72 + row] = (bf16_t)(pk[m][x] & 0xffffu);
+                KT[(col + 2 * x + 1) * P72 + row] = (bf16_t)(pk[m][x] >> 16);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < VLD; ++m) {
+            const int cc = tid + NT * m;
+            const int row = cc / VC, col = (cc % VC) * 8;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                VT[(col + 2 * x) * P72 + row] = (bf16_t)(pv[m][x] & 0xffffu);
+                VT[(col + 2 * x + 1) * P72 + row] = (bf16_t)(pv[m][x] >> 16);
+            }
+        }
+        if (wave == 0) {
+            // cumulative log decay over the chunk (inclusive scan over lanes)
+            float gx = safe_log(pa);
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(gx, off, 64);
+                if (lane >= off) gx += y;
+            }
+            const float glast = __shfl(gx, 63, 64);
+            g_s[lane] = gx;
+            b_s[lane] = pb;
+            gam_s[lane] = __expf(gx);
+            dec_s[lane] = __expf(glast - gx);
+        }
+        if (c + 1 < nch) prefetch(t0 + CH);
+        lds_barrier();
+
+        // ---- (1) A and P from the lower 32x32 tiles of K K^T and K Q^T ----
+        if (wave < 3) {
+            const int sb = wave == 2 ? 1 : 0;   // tile rows: tokens s
+            const int rt = wave == 0 ? 0 : 1;   // tile cols: tokens r
+            f32x16 akk = {}, apk = {};
+#pragma unroll
+            for (int ks = 0; ks < DK / 16; ++ks) {
+                const int kk = ks * 16 + 8 * hi;
+                const bf16x8 ka = frag(Kb, PK, sb * 32 + l32, kk);
+                const bf16x8 kb = frag(Kb, PK, rt * 32 + l32, kk);
+                const bf16x8 qb = frag(Qb, PK, rt * 32 + l32, kk);
+                akk = mfma(ka, kb, akk);
+                apk = mfma(ka, qb, apk);
+            }
+            const int r = rt * 32 + l32;
+            const float gr = g_s[r], br = b_s[r];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int s0 = sb * 32 + 8 * j + 4 * hi;
+                float av[4], pv4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = s0 + e;
+                    const float d = s <= r ? __expf(fminf(gr - g_s[s], 0.f)) : 0.f;
+                    av[e] = s < r ? br * d * akk[4 * j + e] : 0.f;
+                    pv4[e] = d * apk[4 * j + e];
+                }
+                *reinterpret_cast<f32x4*>(Af + r * PA + s0) = f32x4{av[0], av[1], av[2], av[3]};
+                st4_split(Ph + r * P72 + s0, Pl + r * P72 + s0, pv4[0], pv4[1], pv4[2], pv4[3]);
+            }
+        } else {
+            // upper block (r < 32 <= s) of A and P is zero
+            for (int e = lane; e < 32 * 32; e += 64) {
+                const int r = e >> 5, s = 32 + (e & 31);
+                Af[r * PA + s] = 0.f;
+                Ph[r * P72 + s] = 0;
+                Pl[r * P72 + s] = 0;
+            }
+        }
+
+        // ---- (2) K S^T -> R;  Q S^T kept for the output --------------------
+        f32x16 qs = {};
+        {
+            f32x16 aks = {};
+#pragma unroll
+            for (int ks = 0; ks < DK / 16; ++ks) {
+                const int kk = ks * 16 + 8 * hi;
+                const bf16x8 ka = frag(Kb, PK, tb * 32 + l32, kk);
+                const bf16x8 qa = frag(Qb, PK, tb * 32 + l32, kk);
+                const bf16x8 sh = frag(Sh, PK, ib * 32 + l32, kk);
+                const bf16x8 sl = frag(Sl, PK, ib * 32 + l32, kk);
+                aks = mfma(ka, sh, aks);
+                aks = mfma(ka, sl, aks);
+                qs = mfma(qa, sh, qs);
+                qs = mfma(qa, sl, qs);
+            }
+            const int i = ib * 32 + l32;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int s0 = tb * 32 + 8 * j + 4 * hi;
+                const uint2 vv = *reinterpret_cast<const uint2*>(VT + i * P72 + s0);
+                const float v4[4] = {bf2f((bf16_t)(vv.x & 0xffffu)), bf2f((bf16_t)(vv.x >> 16)),
+                                     bf2f((bf16_t)(vv.y & 0xffffu)), bf2f((bf16_t)(vv.y >> 16))};
+                float r4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    r4[e] = b_s[s0 + e] * (v4[e] - gam_s[s0 + e] * aks[4 * j + e]);
+                st4_split(Rh + i * P72 + s0, Rl + i * P72 + s0, r4[0], r4[1], r4[2], r4[3]);
+            }
+        }
+        lds_barrier();
+
+        // ---- (3) T = (I + A)^{-1}: column j by 4 lanes, forward substitution
+        {
+            const int q4 = tid & 3;
+            const int col = wave + 4 * ((tid >> 2) & 15);
+            float tq[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) tq[u] = (4 * u + q4 == col) ? 1.f : 0.f;
+#pragma unroll
+            for (int r = 1; r < 64; ++r) {
+                float part = 0.f;
+#pragma unroll
+                for (int u = 0; u <= ((r - 1) >> 2); ++u)
+                    part += Af[r * PA + 4 * u + q4] * tq[u];
+                part += __shfl_xor(part, 1, 64);
+                part += __shfl_xor(part, 2, 64);
+                const float val = (r == col ? 1.f : 0.f) - part;
+                if (q4 == (r & 3)) tq[r >> 2] = val;
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int r = 4 * u + q4;
+                bf16_t th, tl;
+                split_bf16(tq[u], th, tl);
+                Th[r * P72 + col] = th;
+                Tl[r * P72 + col] = tl;
+            }
+        }
+        lds_barrier();
+
+        // ---- (4) V_new = T R ------------------------------------------------
+        f32x16 vn = {};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int kk = ks * 16 + 8 * hi;
+            const bf16x8 th = frag(Th, P72, tb * 32 + l32, kk);
+            const bf16x8 tl = frag(Tl, P72, tb * 32 + l32, kk);
+            const bf16x8 rh = frag(Rh, P72, ib * 32 + l32, kk);
+            const bf16x8 rl = frag(Rl, P72, ib * 32 + l32, kk);
+            vn = mfma(th, rh, vn);
+            vn = mfma(th, rl, vn);
+            vn = mfma(tl, rh, vn);
+        }
+        lds_barrier();  // R and T fully read: their space is reused below
+        {
+            const int i = ib * 32 + l32;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r0 = tb * 32 + 8 * j + 4 * hi;
+                st4_split(Nh + i * P72 + r0, Nl + i * P72 + r0, vn[4 * j], vn[4 * j + 1],
+                          vn[4 * j + 2], vn[4 * j + 3]);
+                st4_split(Mh + i * P72 + r0, Ml + i * P72 + r0, vn[4 * j] * dec_s[r0],
+                          vn[4 * j + 1] * dec_s[r0 + 1], vn[4 * j + 2] * dec_s[r0 + 2],
+                          vn[4 * j + 3] * dec_s[r0 + 3]);
+            }
+        }
+        lds_barrier();
+
+        // ---- (5) o = gamma (Q S^T) + P V_new -------------------------------
+        {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qs[4 * j + e] *= gam_s[tb * 32 + 8 * j + 4 * hi + e];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int kk = ks * 16 + 8 * hi;
+                const bf16x8 ph = frag(Ph, P72, tb * 32 + l32, kk);
+                const bf16x8 pl = frag(Pl, P72, tb * 32 + l32, kk);
+                const bf16x8 nh = frag(Nh, P72, ib * 32 + l32, kk);
+                const bf16x8 nl = frag(Nl, P72, ib * 32 + l32, kk);
+                qs = mfma(ph, nh, qs);
+                qs = mfma(ph, nl, qs);
+                qs = mfma(pl, nh, qs);
+            }
+            TOut* o = reinterpret_cast<TOut*>(p.o);
+            const int i = row0 + ib * 32 + l32;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = tb * 32 + 8 * j + 4 * hi + e;
+                    if (r < n) io<TOut>::st(o + (((b * T + t0 + r) * H + h) * DV + i), qs[4 * j + e]);
+                }
+        }
+
+        // ---- (6) S^T = gamma_C S^T + K^T V' --------------------------------
+        {
+            const float gC = __expf(g_s[CH - 1]);
+#pragma unroll
+            for (int u = 0; u < NS; ++u) {
+                const int t = wave * NS + u;
+                const int dkb = t >> 1, ibs = t & 1;
+                sacc[u] *= gC;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int kk = ks * 16 + 8 * hi;
+                    const bf16x8 ka = frag(KT, P72, dkb * 32 + l32, kk);
+                    const bf16x8 mh = frag(Mh, P72, ibs * 32 + l32, kk);
+                    const bf16x8 ml = frag(Ml, P72, ibs * 32 + l32, kk);
+                    sacc[u] = mfma(ka, mh, sacc[u]);
+                    sacc[u] = mfma(ka, ml, sacc[u]);
+                }
+                const int i = ibs * 32 + l32;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int dk = dkb * 32 + 8 * j + 4 * hi;
+                    st4_split(Sh + i * PK + dk, Sl + i * PK + dk, sacc[u][4 * j], sacc[u][4 * j + 1],
+                              sacc[u][4 * j + 2], sacc[u][4 * j + 3]);
+                }
+            }
+        }
+    }
+
+    if (p.s_final) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            const int t = wave * NS + u;
+            const int dkb = t >> 1, ibs = t & 1;
+            const int i = ibs * 32 + l32;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int dk = dkb * 32 + 8 * j + 4 * hi;
+                *reinterpret_cast<f32x4*>(p.s_final + ((bh * DV + row0 + i) * DK + dk)) =
+                    f32x4{sacc[u][4 * j], sacc[u][4 * j + 1], sacc[u][4 * j + 2], sacc[u][4 * j + 3]};
+            }
+        }
+    }
 }
+
+template <int DK, int DV, typename TOut>
+hipError_t launch_bf16_t(const ChunkArgs& a) {
+    Bf16Params p;
+    p.T = a.T;
+    p.H = a.H;
+    p.q = (const bf16_t*)a.q;
+    p.k = (const bf16_t*)a.k;
+    p.v = (const bf16_t*)a.v;
+    p.alpha = (const float*)a.alpha;
+    p.beta = (const float*)a.beta;
+    p.s0 = a.s0;
+    p.o = a.o;
+    p.s_final = a.s_final;
+    const size_t lds = Smem<DK>::TOTAL;
+    auto fn = chunk_bf16_kernel<DK, DV, TOut>;
+    hipError_t e =
+        hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const unsigned grid = (unsigned)(a.B * a.H * (DV / RB));
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(NT), lds, a.stream, p);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_bf16_d(const ChunkArgs& a) {
+    return a.out_bf16 ? launch_bf16_t<DK, DV, bf16_t>(a) : launch_bf16_t<DK, DV, float>(a);
+}
+
+}  // namespace
+
+hipError_t launch_chunk_bf16(const ChunkArgs& a) {
+    if (a.Dk == 128 && a.Dv == 128) return launch_bf16_d<128, 128>(a);
+    if (a.Dk == 128 && a.Dv == 64) return launch_bf16_d<128, 64>(a);
+    if (a.Dk == 64 && a.Dv == 128) return launch_bf16_d<64, 128>(a);
+    return launch_bf16_d<64, 64>(a);
+}
+
+}  // namespace gdr

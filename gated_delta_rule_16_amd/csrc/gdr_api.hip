@@ -35,6 +35,11 @@ bool ptrs_ok(std::initializer_list<const void*> ps) {
 
 bool opt_ok(const void* p) { return !p || aligned(p); }
 
+// Element-aligned pointer (scalar gates and outputs are accessed per element).
+bool elem_ok(const void* p, size_t bytes) {
+    return p && (reinterpret_cast<uintptr_t>(p) % bytes) == 0;
+}
+
 // Largest element count of any tensor must fit the kernels' 64-bit offsets
 // and the grid must fit 2^31 - 1 workgroups.
 bool sizes_ok(int64_t a, int64_t b, int64_t c) {
@@ -87,6 +92,7 @@ static gdr_status_t chunk_run(ChunkArgs& a) {
         e = launch_gdr2_bf16(a);
     else
         e = launch_chunk_bf16(a);
+    if (e == hipErrorNotSupported) return GDR_ERR_UNSUPPORTED;
     return from_hip(e);
 }
 
@@ -100,7 +106,9 @@ extern "C" gdr_status_t gdr_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t D
     gdr_status_t st = chunk_common(B, T, H, Dk, Dv, in_dt, out_dt, a);
     if (st != GDR_OK) return st;
     const bool empty = B == 0 || T == 0 || H == 0;
-    if (!empty && !ptrs_ok({q, k, v, alpha, beta, o})) return GDR_ERR_INVALID;
+    if (!empty && (!ptrs_ok({q, k, v}) || !elem_ok(alpha, 4) || !elem_ok(beta, 4) ||
+                   !elem_ok(o, out_dt == GDR_BF16 ? 2 : 4)))
+        return GDR_ERR_INVALID;
     if (!opt_ok(s0) || !opt_ok(s_final)) return GDR_ERR_INVALID;
     a.gated2 = false;
     a.q = q;
@@ -125,7 +133,9 @@ extern "C" gdr_status_t gdr2_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t 
     gdr_status_t st = chunk_common(B, T, H, Dk, Dv, in_dt, out_dt, a);
     if (st != GDR_OK) return st;
     const bool empty = B == 0 || T == 0 || H == 0;
-    if (!empty && !ptrs_ok({q, k, v, alpha, erase, write, o})) return GDR_ERR_INVALID;
+    if (!empty && (!ptrs_ok({q, k, v, alpha, erase, write}) ||
+                   !elem_ok(o, out_dt == GDR_BF16 ? 2 : 4)))
+        return GDR_ERR_INVALID;
     if (!opt_ok(s0) || !opt_ok(s_final)) return GDR_ERR_INVALID;
     a.gated2 = true;
     a.q = q;
@@ -151,7 +161,9 @@ extern "C" gdr_status_t gdr_recurrent_step(int64_t N, int64_t H, int64_t Dk, int
     if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return GDR_ERR_UNSUPPORTED;
     if (!dims_ok(Dk, Dv)) return GDR_ERR_UNSUPPORTED;
     if (N == 0 || H == 0) return GDR_OK;
-    if (!ptrs_ok({q, k, v, alpha, beta, state, o})) return GDR_ERR_INVALID;
+    if (!ptrs_ok({q, k, v, state}) || !elem_ok(alpha, 4) || !elem_ok(beta, 4) ||
+        !elem_ok(o, out_dt == GDR_BF16 ? 2 : 4))
+        return GDR_ERR_INVALID;
     StepArgs a;
     a.N = N;
     a.H = H;

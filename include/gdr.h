@@ -29,7 +29,10 @@
  *   - Arguments are validated on the host before anything is launched; on
  *     any error nothing is written.  Status codes:
  *       GDR_ERR_INVALID      a required pointer is NULL, a size is negative,
- *                            or a pointer is not 16-byte aligned;
+ *                            or a pointer is misaligned: q, k, v, the
+ *                            channel gates, s0, s_final and the decode
+ *                            state need 16-byte alignment; the scalar gates
+ *                            and o need element alignment;
  *       GDR_ERR_UNSUPPORTED  (Dk, Dv) not in {64, 128} x {64, 128}, or an
  *                            unsupported dtype;
  *       GDR_ERR_DEVICE       the HIP runtime reported a launch error.

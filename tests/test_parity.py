@@ -158,3 +158,54 @@ def test_gdn2_fp32(gdr_lib, T, dims):
     inp = make_gdn2(B=1, T=T, H=2, Dk=dims[0], Dv=dims[1], dtype="f32",
                     seed=T + dims[0], s0_std=0.5)
     _check_gdn2(gdr_lib, inp, "f32")
+
+
+# ------------------------------------------- bf16 chunked forward (MFMA) ----
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 128, 200, 333])
+def test_gdn_bf16_ragged(gdr_lib, T):
+    inp = make_gdn(B=2, T=T, H=2, Dk=128, Dv=128, dtype="bf16", seed=100 + T,
+                   s0_std=0.05)
+    _check_gdn(gdr_lib, inp, "f32")
+
+
+@pytest.mark.parametrize("dims", [(128, 128), (128, 64), (64, 128), (64, 64)])
+@pytest.mark.parametrize("odt", ["f32", "bf16"])
+def test_gdn_bf16_dims(gdr_lib, dims, odt):
+    inp = make_gdn(B=1, T=190, H=3, Dk=dims[0], Dv=dims[1], dtype="bf16",
+                   seed=7 + dims[0] + dims[1], s0_std=0.05)
+    _check_gdn(gdr_lib, inp, odt)
+
+
+def test_gdn_bf16_zero_state_and_alias(gdr_lib):
+    inp = make_gdn(B=2, T=150, H=2, Dk=128, Dv=128, dtype="bf16", seed=9)
+    _check_gdn(gdr_lib, inp, "f32")
+    inp = make_gdn(B=2, T=150, H=2, Dk=128, Dv=128, dtype="bf16", seed=9,
+                   s0_std=0.05)
+    _check_gdn(gdr_lib, inp, "f32", alias=True)
+
+
+def test_gdn_bf16_workload_b8_h16_t4096(gdr_lib):
+    """The 1.3B-layer workload at full size (B8 H16 T4096 d128), the launch
+    the benchmark times; the oracle checks batches 0 and 5 (32 heads)."""
+    inp = make_config(1)
+    o, s = _run_gdn(gdr_lib, inp, "f32")
+    pick = [0, 5]
+    o_ref, s_ref = oracle.gdn_fwd(inp.q[pick], inp.k[pick], inp.v[pick],
+                                  inp.alpha[pick], inp.beta[pick], None)
+    eo = oracle.err_rms(o[pick], o_ref)
+    es = oracle.err_rms(s[pick], s_ref)
+    print(f"workload B8H16T4096: err(o)={eo:.3e} err(S)={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
+
+
+@pytest.mark.parametrize("cfg", [2, "2lit"])
+def test_gdn_bf16_long_context(gdr_lib, cfg):
+    """B1 H16 T32768 d128 with a random initial state: 512 chained chunks."""
+    inp = make_config(cfg)
+    o, s = _run_gdn(gdr_lib, inp, "f32")
+    o_ref, s_ref = oracle.gdn_fwd(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
+                                  inp.s0)
+    eo, es = oracle.err_rms(o, o_ref), oracle.err_rms(s, s_ref)
+    print(f"long context {cfg}: err(o)={eo:.3e} err(S)={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
