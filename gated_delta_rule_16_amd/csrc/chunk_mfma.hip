@@ -21,15 +21,18 @@
 // the chunks in order with S resident: fp32 in matrix-core accumulators
 // (as S^T tiles) and a bf16 hi/lo copy in LDS for use as an operand.  The
 // next chunk's q, k, v, alpha, beta are loaded into registers while the
-// current chunk computes.
+// current chunk computes.  Every matrix-core phase first issues all of its
+// LDS operand reads and then its MFMAs, so reads stream behind the math.
 //
-// Per chunk (32x32x16 bf16 MFMA tiles, 4 waves):
-//   (1) K K^T and K Q^T lower tiles -> A (fp32) and P (hi/lo)     48 MFMA
-//   (2) K S^T -> R (hi/lo), Q S^T kept in registers             128 MFMA
-//   (3) T = (I + A)^{-1} by forward substitution in fp32 VALU
-//   (4) V_new = T R -> V_new and decayed V_new (hi/lo)             48 MFMA
-//   (5) o = gamma (Q S^T) + P V_new -> HBM                         48 MFMA
-//   (6) S^T = gamma_C S^T + K^T V'                                 64 MFMA
+// Per chunk (bf16 32x32x16 MFMA tiles unless noted, 4 waves):
+//   (1) K K^T and K Q^T lower tiles -> A (fp32) and P (hi/lo)      48 MFMA
+//   (2) K S^T -> R (hi/lo), Q S^T kept in registers              128 MFMA
+//   (3) T = (I + A)^{-1} in 16x16 blocks: diagonal blocks by forward
+//       substitution (4 lanes per column), then T_10, T_32, and the lower
+//       32x32 block -T_22 A_21 T_11 on fp32 16x16x4 matrix cores
+//   (4) V_new = T R -> V_new and decayed V_new (hi/lo)              36 MFMA
+//   (5) o = gamma (Q S^T) + P V_new -> HBM                          36 MFMA
+//   (6) S^T = gamma_C S^T + K^T V' (K^T read transposed from LDS)   64 MFMA
 #include "launch.h"
 #include "mfma_common.h"
 
@@ -40,8 +43,9 @@ namespace {
 constexpr int CH = 64;    // tokens per chunk
 constexpr int RB = 64;    // state rows per workgroup
 constexpr int NT = 256;   // threads per workgroup
-constexpr int P72 = 72;   // pitch (elements) of 64-deep contraction-major tiles
-constexpr int PA = 68;    // pitch (floats) of the fp32 A tile
+constexpr int P72 = 72;   // pitch (elements) of 64-wide bf16 tiles
+constexpr int PF = 68;    // pitch (floats) of 64-wide fp32 tiles
+constexpr int PX = 17;    // pitch (floats) of 16x16 solve scratch tiles
 
 struct Bf16Params {
     int64_t T, H;
@@ -55,22 +59,41 @@ struct Bf16Params {
 template <int DK>
 struct Smem {
     static constexpr int PK = DK + 8;  // pitch of K, Q, S rows (elements)
-    static constexpr int KB_SZ = 64 * PK * 2;
-    static constexpr int T_SZ = 2 * 64 * P72 * 2;
-    static constexpr int A_SZ = 64 * PA * 4;
-    static constexpr int N_SZ = 2 * RB * P72 * 2;
-    static constexpr int R0 = 0;                       // K tile | T hi, lo
-    static constexpr int QB = R0 + (KB_SZ > T_SZ ? KB_SZ : T_SZ);
-    static constexpr int KT = QB + KB_SZ;              // K^T [DK][P72]
-    static constexpr int VT = KT + DK * P72 * 2;       // V^T [RB][P72]
-    static constexpr int SH = VT + RB * P72 * 2;       // S hi [RB][PK]
-    static constexpr int SL = SH + RB * PK * 2;        // S lo
-    static constexpr int AN = SL + RB * PK * 2;        // A fp32 | V_new^T hi, lo
-    static constexpr int PP = AN + (A_SZ > N_SZ ? A_SZ : N_SZ);  // P hi, lo
-    static constexpr int RM = PP + 2 * 64 * P72 * 2;   // R^T hi, lo | V'^T hi, lo
-    static constexpr int GT = RM + 2 * RB * P72 * 2;   // g, beta, gamma, decay-to-end
+    static constexpr int KB = 0;                             // K [64][PK]
+    static constexpr int QB = KB + 64 * PK * 2;              // Q [64][PK] | T fp32 [64][PF]
+    static constexpr int QB_SZ = (64 * PK * 2) > (64 * PF * 4) ? (64 * PK * 2) : (64 * PF * 4);
+    static constexpr int VB = QB + QB_SZ;                    // V [64][P72] | solve scratch
+    static constexpr int VB_SZ = (64 * P72 * 2) > (4 * 16 * PX * 4) ? (64 * P72 * 2)
+                                                                    : (4 * 16 * PX * 4);
+    static constexpr int SH = VB + VB_SZ;                    // S hi [RB][PK]
+    static constexpr int SL = SH + RB * PK * 2;              // S lo
+    static constexpr int AN = SL + RB * PK * 2;              // A fp32 [64][PF] | V_new^T hi, lo
+    static constexpr int AN_SZ = (64 * PF * 4) > (2 * RB * P72 * 2) ? (64 * PF * 4)
+                                                                    : (2 * RB * P72 * 2);
+    static constexpr int TT = AN + AN_SZ;                    // T hi, lo [64][P72]
+    static constexpr int PP = TT + 2 * 64 * P72 * 2;         // P hi, lo [64][P72]
+    static constexpr int RM = PP + 2 * 64 * P72 * 2;         // R^T hi, lo | V'^T hi, lo
+    static constexpr int GT = RM + 2 * RB * P72 * 2;         // g, beta, gamma, decay-to-end
     static constexpr int TOTAL = GT + 4 * CH * 4;
 };
+
+// Store one fp32 16x16 tile held in the C layout of the 16x16x4 matrix core
+// (register r: row 4 (lane / 16) + r, column lane % 16) into T's fp32 copy
+// and its hi/lo bf16 copies, at block (R, C).
+__device__ __forceinline__ void store_t_block(float* Tf, bf16_t* Th, bf16_t* Tl, const f32x4& t,
+                                              int R, int C, bool keep_f32) {
+    const int lane = threadIdx.x & 63;
+    const int m = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = 16 * R + 4 * kq + r, col = 16 * C + m;
+        if (keep_f32) Tf[row * PF + col] = t[r];
+        bf16_t h, l;
+        split_bf16(t[r], h, l);
+        Th[row * P72 + col] = h;
+        Tl[row * P72 + col] = l;
+    }
+}
 
 template <int DK, int DV, typename TOut>
 __global__ __launch_bounds__(NT) void chunk_bf16_kernel(Bf16Params p) {
@@ -82,20 +105,23 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(Bf16Params p) {
     constexpr int VC = RB / 8;               // 16-byte pieces per value row slice
     constexpr int VLD = CH * VC / NT;
     constexpr int NS = DK / 64;              // S^T tiles per wave
+    constexpr int KS = DK / 16;              // k-steps over the key dim
     static_assert(KLD * NT == CH * KC && VLD * NT == CH * VC, "load split");
+    static_assert(M::TOTAL <= 160 * 1024, "LDS budget");
 
     extern __shared__ __align__(16) unsigned char smem[];
-    bf16_t* Kb = reinterpret_cast<bf16_t*>(smem + M::R0);
-    bf16_t* Th = Kb;
-    bf16_t* Tl = Th + 64 * P72;
+    bf16_t* Kb = reinterpret_cast<bf16_t*>(smem + M::KB);
     bf16_t* Qb = reinterpret_cast<bf16_t*>(smem + M::QB);
-    bf16_t* KT = reinterpret_cast<bf16_t*>(smem + M::KT);
-    bf16_t* VT = reinterpret_cast<bf16_t*>(smem + M::VT);
+    float* Tf = reinterpret_cast<float*>(smem + M::QB);
+    bf16_t* Vb = reinterpret_cast<bf16_t*>(smem + M::VB);
+    float* Xs = reinterpret_cast<float*>(smem + M::VB);
     bf16_t* Sh = reinterpret_cast<bf16_t*>(smem + M::SH);
     bf16_t* Sl = reinterpret_cast<bf16_t*>(smem + M::SL);
     float* Af = reinterpret_cast<float*>(smem + M::AN);
     bf16_t* Nh = reinterpret_cast<bf16_t*>(smem + M::AN);
     bf16_t* Nl = Nh + RB * P72;
+    bf16_t* Th = reinterpret_cast<bf16_t*>(smem + M::TT);
+    bf16_t* Tl = Th + 64 * P72;
     bf16_t* Ph = reinterpret_cast<bf16_t*>(smem + M::PP);
     bf16_t* Pl = Ph + 64 * P72;
     bf16_t* Rh = reinterpret_cast<bf16_t*>(smem + M::RM);
@@ -112,6 +138,8 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(Bf16Params p) {
     const int wave = tid >> 6;
     const int l32 = lane & 31;
     const int hi = lane >> 5;
+    const int m16 = lane & 15;
+    const int kq = lane >> 4;
     const int rbk = blockIdx.x % NRB;
     const int64_t bh = blockIdx.x / NRB;
     const int64_t H = p.H, T = p.T;
@@ -121,6 +149,14 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(Bf16Params p) {
     // tile of the 64 x 64 (token x state-row) products owned by this wave
     const int tb = wave >> 1;
     const int ib = wave & 1;
+
+    // T's upper 16x16 blocks inside its diagonal 32x32 tiles are read as
+    // zeros by (4); they are never written afterwards.
+    for (int e = tid; e < 2 * 16 * 16; e += NT) {
+        const int blk = e >> 8, r = 32 * blk + ((e >> 4) & 15), s = 32 * blk + 16 + (e & 15);
+        Th[r * P72 + s] = 0;
+        Tl[r * P72 + s] = 0;
+    }
 
     // ---- initial state: S^T tiles in accumulators, hi/lo S in LDS --------
     f32x16 sacc[NS];
@@ -144,6 +180,9 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(Bf16Params p) {
     }
 
     // ---- register prefetch of one chunk -----------------------------------
+    const bf16_t* kbase = p.k + (b * T * H + h) * DK;
+    const bf16_t* qbase = p.q + (b * T * H + h) * DK;
+    const bf16_t* vbase = p.v + (b * T * H + h) * DV + row0;
     u32x4 pk[KLD], pq[KLD], pv[VLD];
     float pa = 1.f, pb = 0.f;
     auto prefetch = [&](int64_t t0) {
@@ -153,9 +192,9 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(Bf16Params p) {
             const int row = c / KC, col = (c % KC) * 8;
             const int64_t tok = t0 + row;
             if (tok < T) {
-                const int64_t off = ((b * T + tok) * H + h) * DK + col;
-                pk[m] = *reinterpret_cast<const u32x4*>(p.k + off);
-                pq[m] = *reinterpret_cast<const u32x4*>(p.q + off);
+                const int64_t off = tok * H * DK + col;
+                pk[m] = *reinterpret_cast<const u32x4*>(kbase + off);
+                pq[m] = *reinterpret_cast<const u32x4*>(qbase + off);
             } else {
                 pk[m] = u32x4{0u, 0u, 0u, 0u};
                 pq[m] = u32x4{0u, 0u, 0u, 0u};
@@ -167,8 +206,7 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(Bf16Params p) {
             const int row = c / VC, col = (c % VC) * 8;
             const int64_t tok = t0 + row;
             if (tok < T)
-                pv[m] = *reinterpret_cast<const u32x4*>(
-                    p.v + (((b * T + tok) * H + h) * DV + row0 + col));
+                pv[m] = *reinterpret_cast<const u32x4*>(vbase + tok * H * DV + col);
             else
                 pv[m] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -185,37 +223,22 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(Bf16Params p) {
         const int64_t t0 = c * CH;
         const int n = (int)((T - t0) < CH ? (T - t0) : CH);
         lds_barrier();
-        // ---- stage the chunk: K, Q row-major; K^T, V^T contraction-major ---
+        // ---- stage the chunk (row-major; transposes come from tr reads) ----
 #pragma unroll
         for (int m = 0; m < KLD; ++m) {
             const int cc = tid + NT * m;
             const int row = cc / KC, col = (cc % KC) * 8;
             *reinterpret_cast<u32x4*>(Kb + row * PK + col) = pk[m];
             *reinterpret_cast<u32x4*>(Qb + row * PK + col) = pq[m];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                KT[(col + 2 * x) * P72 + row] = (bf16_t)(pk[m][x] & 0xffffu);
-                KT[(col + 2 * x + 1) * P72 + row] = (bf16_t)(pk[m][x] >> 16);
-            }
         }
 #pragma unroll
         for (int m = 0; m < VLD; ++m) {
             const int cc = tid + NT * m;
             const int row = cc / VC, col = (cc % VC) * 8;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                VT[(col + 2 * x) * P72 + row] = (bf16_t)(pv[m][x] & 0xffffu);
-                VT[(col + 2 * x + 1) * P72 + row] = (bf16_t)(pv[m][x] >> 16);
-            }
+            *reinterpret_cast<u32x4*>(Vb + row * P72 + col) = pv[m];
         }
         if (wave == 0) {
-            // cumulative log decay over the chunk (inclusive scan over lanes)
-            float gx = safe_log(pa);
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(gx, off, 64);
-                if (lane >= off) gx += y;
-            }
+            const float gx = wave_scan(safe_log(pa));   // cumulative log decay
             const float glast = __shfl(gx, 63, 64);
             g_s[lane] = gx;
             b_s[lane] = pb;
@@ -229,148 +252,255 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(Bf16Params p) {
         if (wave < 3) {
             const int sb = wave == 2 ? 1 : 0;   // tile rows: tokens s
             const int rt = wave == 0 ? 0 : 1;   // tile cols: tokens r
+            bf16x8 fa[KS], fk[KS], fq[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int kk = ks * 16 + 8 * hi;
+                fa[ks] = frag(Kb, PK, sb * 32 + l32, kk);
+                fk[ks] = frag(Kb, PK, rt * 32 + l32, kk);
+                fq[ks] = frag(Qb, PK, rt * 32 + l32, kk);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             f32x16 akk = {}, apk = {};
 #pragma unroll
-            for (int ks = 0; ks < DK / 16; ++ks) {
-                const int kk = ks * 16 + 8 * hi;
-                const bf16x8 ka = frag(Kb, PK, sb * 32 + l32, kk);
-                const bf16x8 kb = frag(Kb, PK, rt * 32 + l32, kk);
-                const bf16x8 qb = frag(Qb, PK, rt * 32 + l32, kk);
-                akk = mfma(ka, kb, akk);
-                apk = mfma(ka, qb, apk);
+            for (int ks = 0; ks < KS; ++ks) {
+                akk = mfma(fa[ks], fk[ks], akk);
+                apk = mfma(fa[ks], fq[ks], apk);
             }
             const int r = rt * 32 + l32;
             const float gr = g_s[r], br = b_s[r];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int s0 = sb * 32 + 8 * j + 4 * hi;
+                const f32x4 gs = *reinterpret_cast<const f32x4*>(g_s + s0);
                 float av[4], pv4[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int s = s0 + e;
-                    const float d = s <= r ? __expf(fminf(gr - g_s[s], 0.f)) : 0.f;
+                    const float d = s <= r ? __expf(fminf(gr - gs[e], 0.f)) : 0.f;
                     av[e] = s < r ? br * d * akk[4 * j + e] : 0.f;
                     pv4[e] = d * apk[4 * j + e];
                 }
-                *reinterpret_cast<f32x4*>(Af + r * PA + s0) = f32x4{av[0], av[1], av[2], av[3]};
+                *reinterpret_cast<f32x4*>(Af + r * PF + s0) = f32x4{av[0], av[1], av[2], av[3]};
                 st4_split(Ph + r * P72 + s0, Pl + r * P72 + s0, pv4[0], pv4[1], pv4[2], pv4[3]);
-            }
-        } else {
-            // upper block (r < 32 <= s) of A and P is zero
-            for (int e = lane; e < 32 * 32; e += 64) {
-                const int r = e >> 5, s = 32 + (e & 31);
-                Af[r * PA + s] = 0.f;
-                Ph[r * P72 + s] = 0;
-                Pl[r * P72 + s] = 0;
             }
         }
 
         // ---- (2) K S^T -> R;  Q S^T kept for the output --------------------
         f32x16 qs = {};
         {
+            bf16x8 fk[KS], fq[KS], fh[KS], fl[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int kk = ks * 16 + 8 * hi;
+                fk[ks] = frag(Kb, PK, tb * 32 + l32, kk);
+                fq[ks] = frag(Qb, PK, tb * 32 + l32, kk);
+                fh[ks] = frag(Sh, PK, ib * 32 + l32, kk);
+                fl[ks] = frag(Sl, PK, ib * 32 + l32, kk);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             f32x16 aks = {};
 #pragma unroll
-            for (int ks = 0; ks < DK / 16; ++ks) {
-                const int kk = ks * 16 + 8 * hi;
-                const bf16x8 ka = frag(Kb, PK, tb * 32 + l32, kk);
-                const bf16x8 qa = frag(Qb, PK, tb * 32 + l32, kk);
-                const bf16x8 sh = frag(Sh, PK, ib * 32 + l32, kk);
-                const bf16x8 sl = frag(Sl, PK, ib * 32 + l32, kk);
-                aks = mfma(ka, sh, aks);
-                aks = mfma(ka, sl, aks);
-                qs = mfma(qa, sh, qs);
-                qs = mfma(qa, sl, qs);
+            for (int ks = 0; ks < KS; ++ks) {
+                aks = mfma(fk[ks], fh[ks], aks);
+                qs = mfma(fq[ks], fh[ks], qs);
+                aks = mfma(fk[ks], fl[ks], aks);
+                qs = mfma(fq[ks], fl[ks], qs);
             }
             const int i = ib * 32 + l32;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int s0 = tb * 32 + 8 * j + 4 * hi;
-                const uint2 vv = *reinterpret_cast<const uint2*>(VT + i * P72 + s0);
-                const float v4[4] = {bf2f((bf16_t)(vv.x & 0xffffu)), bf2f((bf16_t)(vv.x >> 16)),
-                                     bf2f((bf16_t)(vv.y & 0xffffu)), bf2f((bf16_t)(vv.y >> 16))};
+                // V[s0 .. s0+3][i] via a transposed read of the row-major tile
+                const s16x4 vv = lds_tr16(Vb + (s0 + (m16 >> 2)) * P72 + ib * 32 +
+                                          16 * (kq & 1) + 4 * (m16 & 3));
+                const f32x4 bs = *reinterpret_cast<const f32x4*>(b_s + s0);
+                const f32x4 gs = *reinterpret_cast<const f32x4*>(gam_s + s0);
                 float r4[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    r4[e] = b_s[s0 + e] * (v4[e] - gam_s[s0 + e] * aks[4 * j + e]);
+                    r4[e] = bs[e] * (bf2f((bf16_t)vv[e]) - gs[e] * aks[4 * j + e]);
                 st4_split(Rh + i * P72 + s0, Rl + i * P72 + s0, r4[0], r4[1], r4[2], r4[3]);
             }
         }
         lds_barrier();
 
-        // ---- (3) T = (I + A)^{-1}: column j by 4 lanes, forward substitution
+        // ---- (3) T = (I + A)^{-1} -----------------------------------------
         {
-            const int q4 = tid & 3;
-            const int col = wave + 4 * ((tid >> 2) & 15);
-            float tq[16];
+            // Diagonal block `wave`: lane 4c + q works on column c, summing
+            // the rows s = q (mod 4): T_rc = delta_rc - sum_{s<r} A_rs T_sc.
+            const int q = lane & 3, cidx = lane >> 2, base = 16 * wave;
+            float a[16][4];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) tq[u] = (4 * u + q4 == col) ? 1.f : 0.f;
-#pragma unroll
-            for (int r = 1; r < 64; ++r) {
-                float part = 0.f;
+            for (int r = 1; r < 16; ++r)
 #pragma unroll
                 for (int u = 0; u <= ((r - 1) >> 2); ++u)
-                    part += Af[r * PA + 4 * u + q4] * tq[u];
-                part += __shfl_xor(part, 1, 64);
-                part += __shfl_xor(part, 2, 64);
-                const float val = (r == col ? 1.f : 0.f) - part;
-                if (q4 == (r & 3)) tq[r >> 2] = val;
+                    a[r][u] = Af[(base + r) * PF + base + 4 * u + q];
+            float t[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) t[u] = (4 * u + q == cidx) ? 1.f : 0.f;
+#pragma unroll
+            for (int r = 1; r < 16; ++r) {
+                float part = 0.f;
+#pragma unroll
+                for (int u = 0; u <= ((r - 1) >> 2); ++u) part += a[r][u] * t[u];
+                const float val = (r == cidx ? 1.f : 0.f) - quad_sum(part);
+                if (q == (r & 3)) t[r >> 2] = val;
             }
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int r = 4 * u + q4;
+            for (int u = 0; u < 4; ++u) {
+                const int row = base + 4 * u + q, col = base + cidx;
+                Tf[row * PF + col] = t[u];
                 bf16_t th, tl;
-                split_bf16(tq[u], th, tl);
-                Th[r * P72 + col] = th;
-                Tl[r * P72 + col] = tl;
+                split_bf16(t[u], th, tl);
+                Th[row * P72 + col] = th;
+                Tl[row * P72 + col] = tl;
             }
+        }
+        lds_barrier();
+        if (wave < 2) {
+            // T_10 = -T_11 A_10 T_00 (wave 0) and T_32 = -T_33 A_32 T_22 (wave 1)
+            const int R = 2 * wave + 1, C = 2 * wave;
+            float* X = Xs + wave * 16 * PX;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                acc = mfma_f32(Af[(16 * R + m16) * PF + 16 * C + 4 * ks + kq],
+                               Tf[(16 * C + 4 * ks + kq) * PF + 16 * C + m16], acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) X[(4 * kq + r) * PX + m16] = acc[r];
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                t = mfma_f32(Tf[(16 * R + m16) * PF + 16 * R + 4 * ks + kq],
+                             X[(4 * ks + kq) * PX + m16], t);
+            store_t_block(Tf, Th, Tl, -t, R, C, true);
+        }
+        lds_barrier();
+        // Lower 32x32 block: Y = A_21 T_11, then T_21 = -T_22 Y, one 16x16
+        // output block per wave: block row 2 + (wave >> 1), column wave & 1.
+        const int yi = 2 + (wave >> 1), yj = wave & 1;
+        {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            // T_11 block column yj has nonzero blocks in rows yj .. 1
+            for (int ks = 4 * yj; ks < 8; ++ks)
+                acc = mfma_f32(Af[(16 * yi + m16) * PF + 4 * ks + kq],
+                               Tf[(4 * ks + kq) * PF + 16 * yj + m16], acc);
+            float* Y = Xs + wave * 16 * PX;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Y[(4 * kq + r) * PX + m16] = acc[r];
+        }
+        lds_barrier();
+        {
+            f32x4 t = {0.f, 0.f, 0.f, 0.f};
+            // T_22 block row yi has nonzero blocks in columns 2 .. yi; Y's
+            // block row 2 + k (column yj) was written by wave 2 k + yj.
+            for (int ks = 0; ks < 4 * (yi - 1); ++ks) {
+                const float* Y = Xs + (2 * (ks >> 2) + yj) * 16 * PX;
+                t = mfma_f32(Tf[(16 * yi + m16) * PF + 32 + 4 * ks + kq],
+                             Y[(4 * (ks & 3) + kq) * PX + m16], t);
+            }
+            store_t_block(Tf, Th, Tl, -t, yi, yj, false);
         }
         lds_barrier();
 
         // ---- (4) V_new = T R ------------------------------------------------
         f32x16 vn = {};
+        {
+            bf16x8 th[4], tl[4], rh[4], rl[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int kk = ks * 16 + 8 * hi;
-            const bf16x8 th = frag(Th, P72, tb * 32 + l32, kk);
-            const bf16x8 tl = frag(Tl, P72, tb * 32 + l32, kk);
-            const bf16x8 rh = frag(Rh, P72, ib * 32 + l32, kk);
-            const bf16x8 rl = frag(Rl, P72, ib * 32 + l32, kk);
-            vn = mfma(th, rh, vn);
-            vn = mfma(th, rl, vn);
-            vn = mfma(tl, rh, vn);
+            for (int ks = 0; ks < 4; ++ks) {
+                if (ks < 2 || tb == 1) {   // T vanishes above its diagonal 32x32 tiles
+                    const int kk = ks * 16 + 8 * hi;
+                    th[ks] = frag(Th, P72, tb * 32 + l32, kk);
+                    tl[ks] = frag(Tl, P72, tb * 32 + l32, kk);
+                    rh[ks] = frag(Rh, P72, ib * 32 + l32, kk);
+                    rl[ks] = frag(Rl, P72, ib * 32 + l32, kk);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                if (ks < 2 || tb == 1) {
+                    vn = mfma(th[ks], rh[ks], vn);
+                    vn = mfma(th[ks], rl[ks], vn);
+                    vn = mfma(tl[ks], rh[ks], vn);
+                }
+            }
         }
-        lds_barrier();  // R and T fully read: their space is reused below
+        lds_barrier();  // R fully read (its space takes V'), A dead (takes V_new)
         {
             const int i = ib * 32 + l32;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r0 = tb * 32 + 8 * j + 4 * hi;
+                const f32x4 dd = *reinterpret_cast<const f32x4*>(dec_s + r0);
                 st4_split(Nh + i * P72 + r0, Nl + i * P72 + r0, vn[4 * j], vn[4 * j + 1],
                           vn[4 * j + 2], vn[4 * j + 3]);
-                st4_split(Mh + i * P72 + r0, Ml + i * P72 + r0, vn[4 * j] * dec_s[r0],
-                          vn[4 * j + 1] * dec_s[r0 + 1], vn[4 * j + 2] * dec_s[r0 + 2],
-                          vn[4 * j + 3] * dec_s[r0 + 3]);
+                st4_split(Mh + i * P72 + r0, Ml + i * P72 + r0, vn[4 * j] * dd[0],
+                          vn[4 * j + 1] * dd[1], vn[4 * j + 2] * dd[2], vn[4 * j + 3] * dd[3]);
             }
         }
         lds_barrier();
 
         // ---- (5) o = gamma (Q S^T) + P V_new -------------------------------
         {
+            bf16x8 ph[4], pl[4], nh[4], nl[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int ks = 0; ks < 4; ++ks) {
+                if (ks < 2 || tb == 1) {   // P vanishes above its diagonal tiles
+                    const int kk = ks * 16 + 8 * hi;
+                    ph[ks] = frag(Ph, P72, tb * 32 + l32, kk);
+                    pl[ks] = frag(Pl, P72, tb * 32 + l32, kk);
+                    nh[ks] = frag(Nh, P72, ib * 32 + l32, kk);
+                    nl[ks] = frag(Nl, P72, ib * 32 + l32, kk);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) qs[4 * j + e] *= gam_s[tb * 32 + 8 * j + 4 * hi + e];
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 gg = *reinterpret_cast<const f32x4*>(gam_s + tb * 32 + 8 * j + 4 * hi);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qs[4 * j + e] *= gg[e];
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                if (ks < 2 || tb == 1) {
+                    qs = mfma(ph[ks], nh[ks], qs);
+                    qs = mfma(ph[ks], nl[ks], qs);
+                    qs = mfma(pl[ks], nh[ks], qs);
+                }
+            }
+        }
+        // ---- (6) S^T = gamma_C S^T + K^T V' --------------------------------
+        {
+            bf16x8 ka[4], mh[NS][4], ml[NS][4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int kk = ks * 16 + 8 * hi;
-                const bf16x8 ph = frag(Ph, P72, tb * 32 + l32, kk);
-                const bf16x8 pl = frag(Pl, P72, tb * 32 + l32, kk);
-                const bf16x8 nh = frag(Nh, P72, ib * 32 + l32, kk);
-                const bf16x8 nl = frag(Nl, P72, ib * 32 + l32, kk);
-                qs = mfma(ph, nh, qs);
-                qs = mfma(ph, nl, qs);
-                qs = mfma(pl, nh, qs);
+                ka[ks] = frag_tr(Kb, PK, ks * 16, (wave * NS >> 1) * 32);
+#pragma unroll
+                for (int u = 0; u < NS; ++u) {
+                    const int ibs = (wave * NS + u) & 1;
+                    mh[u][ks] = frag(Mh, P72, ibs * 32 + l32, kk);
+                    ml[u][ks] = frag(Ml, P72, ibs * 32 + l32, kk);
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            const float gC = __expf(g_s[CH - 1]);
+#pragma unroll
+            for (int u = 0; u < NS; ++u) sacc[u] *= gC;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int u = 0; u < NS; ++u) {
+                    sacc[u] = mfma(ka[ks], mh[u][ks], sacc[u]);
+                    sacc[u] = mfma(ka[ks], ml[u][ks], sacc[u]);
+                }
+        }
+        {
             TOut* o = reinterpret_cast<TOut*>(p.o);
             const int i = row0 + ib * 32 + l32;
 #pragma unroll
@@ -380,31 +510,16 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(Bf16Params p) {
                     const int r = tb * 32 + 8 * j + 4 * hi + e;
                     if (r < n) io<TOut>::st(o + (((b * T + t0 + r) * H + h) * DV + i), qs[4 * j + e]);
                 }
-        }
-
-        // ---- (6) S^T = gamma_C S^T + K^T V' --------------------------------
-        {
-            const float gC = __expf(g_s[CH - 1]);
 #pragma unroll
             for (int u = 0; u < NS; ++u) {
                 const int t = wave * NS + u;
                 const int dkb = t >> 1, ibs = t & 1;
-                sacc[u] *= gC;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int kk = ks * 16 + 8 * hi;
-                    const bf16x8 ka = frag(KT, P72, dkb * 32 + l32, kk);
-                    const bf16x8 mh = frag(Mh, P72, ibs * 32 + l32, kk);
-                    const bf16x8 ml = frag(Ml, P72, ibs * 32 + l32, kk);
-                    sacc[u] = mfma(ka, mh, sacc[u]);
-                    sacc[u] = mfma(ka, ml, sacc[u]);
-                }
-                const int i = ibs * 32 + l32;
+                const int si = ibs * 32 + l32;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int dk = dkb * 32 + 8 * j + 4 * hi;
-                    st4_split(Sh + i * PK + dk, Sl + i * PK + dk, sacc[u][4 * j], sacc[u][4 * j + 1],
-                              sacc[u][4 * j + 2], sacc[u][4 * j + 3]);
+                    st4_split(Sh + si * PK + dk, Sl + si * PK + dk, sacc[u][4 * j],
+                              sacc[u][4 * j + 1], sacc[u][4 * j + 2], sacc[u][4 * j + 3]);
                 }
             }
         }

@@ -33,26 +33,97 @@ __device__ __forceinline__ bf16x8 frag(const bf16_t* base, int pitch, int row, i
     return *reinterpret_cast<const bf16x8*>(base + row * pitch + k);
 }
 
-__device__ __forceinline__ void split_bf16(float x, bf16_t& h, bf16_t& l) {
-    h = f2bf(x);
-    l = f2bf(x - bf2f(h));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Two fp32 -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even).
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
+    const bf16x2_t v = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, v);
 }
 
-// Store 4 consecutive values x[0..3] at p as bf16 hi/lo pairs (8 bytes each).
+// hi/lo split of two values: hi = bf16(x), lo = bf16(x - hi).
+__device__ __forceinline__ void split2(float a, float b, uint32_t& h, uint32_t& l) {
+    h = cvt_pk(a, b);
+    l = cvt_pk(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
+}
+
+__device__ __forceinline__ void split_bf16(float x, bf16_t& h, bf16_t& l) {
+    uint32_t ph, pl;
+    split2(x, 0.f, ph, pl);
+    h = (bf16_t)(ph & 0xffffu);
+    l = (bf16_t)(pl & 0xffffu);
+}
+
+// Store 4 consecutive values at ph / pl as bf16 hi/lo quads (8 bytes each).
 __device__ __forceinline__ void st4_split(bf16_t* ph, bf16_t* pl, float x0, float x1, float x2,
                                           float x3) {
-    bf16_t h0, h1, h2, h3, l0, l1, l2, l3;
-    split_bf16(x0, h0, l0);
-    split_bf16(x1, h1, l1);
-    split_bf16(x2, h2, l2);
-    split_bf16(x3, h3, l3);
     uint2 vh, vl;
-    vh.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    vh.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
-    vl.x = (uint32_t)l0 | ((uint32_t)l1 << 16);
-    vl.y = (uint32_t)l2 | ((uint32_t)l3 << 16);
+    split2(x0, x1, vh.x, vl.x);
+    split2(x2, x3, vh.y, vl.y);
     *reinterpret_cast<uint2*>(ph) = vh;
     *reinterpret_cast<uint2*>(pl) = vl;
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane 4r + c supplies the address of 4 consecutive 16-bit elements; lane i
+// of the group receives element (i & 3) of the chunk supplied by lane
+// 4r + (i >> 2), for r = 0..3.  With lane 4r + c pointing at
+// M[row0 + r][col0 + 4c] of a row-major matrix, lane i receives the column
+// M[row0 .. row0 + 3][col0 + i].
+__device__ __forceinline__ s16x4 lds_tr16(const bf16_t* p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)((__attribute__((address_space(3))) char*)(
+            (__attribute__((address_space(3))) void*)(p))));
+}
+
+// Operand fragment with the contraction running down the rows of a
+// row-major bf16 matrix M (pitch in elements): lane l receives
+// M[k0 + 8 (l / 32) + e][n0 + (l % 32)], e = 0..7 -- the layout of both MFMA
+// operands when M is stored contraction-major-transposed.
+__device__ __forceinline__ bf16x8 frag_tr(const bf16_t* M, int pitch, int k0, int n0) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, j = lane & 15;
+    const int kb = k0 + 8 * (g >> 1) + (j >> 2);
+    const int nb = n0 + 16 * (g & 1) + 4 * (j & 3);
+    const s16x4 a = lds_tr16(M + kb * pitch + nb);
+    const s16x4 b = lds_tr16(M + (kb + 4) * pitch + nb);
+    const s16x4 r8[2] = {a, b};
+    return __builtin_bit_cast(bf16x8, r8);
+}
+
+// fp32 matrix core 16x16x4: A lane l holds A[l % 16][l / 16], B lane l
+// holds B[l / 16][l % 16]; C register r holds C[4 (l / 16) + r][l % 16].
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// DPP lane moves (v_mov_b32_dpp); lanes whose source is out of range read 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over the 4 lanes of each aligned quad (quad_perm xor 1, then xor 2).
+__device__ __forceinline__ float quad_sum(float x) {
+    x += dpp_mov<0xB1>(x);
+    x += dpp_mov<0x4E>(x);
+    return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: within each row of 16
+// lanes by row_shr 1, 2, 4, 8, then across rows by row_bcast 15 and 31.
+__device__ __forceinline__ float wave_scan(float x) {
+    x += dpp_mov<0x111>(x);
+    x += dpp_mov<0x112>(x);
+    x += dpp_mov<0x114>(x);
+    x += dpp_mov<0x118>(x);
+    x += dpp_mov<0x142, 0xA>(x);
+    x += dpp_mov<0x143, 0xC>(x);
+    return x;
 }
 
 // Workgroup barrier that orders LDS only: outstanding global loads (the
