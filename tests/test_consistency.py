@@ -110,3 +110,45 @@ def test_empty_sequence_copies_state(gdr_lib):
     o, s = gdr_lib.gdr_chunk_fwd(e, e, e, a, a, s0)
     torch.cuda.synchronize()
     assert o.shape == (2, 0, 3, 64) and torch.equal(s, s0)
+
+
+def test_gdn2_collapses_to_gdn(gdr_lib):
+    """Gated Delta Rule-2 with every gate collapsed to one scalar per token
+    (alpha, b = w = beta on all channels) is the scalar gated rule: the two
+    kernels agree.  Gates are bf16-exact so both see the same values."""
+    inp = make_gdn(B=2, T=150, H=2, Dk=128, Dv=128, dtype="bf16", seed=26,
+                   s0_std=0.05)
+    a = inp.alpha.to(torch.bfloat16)
+    b = inp.beta.to(torch.bfloat16)
+    Dk, Dv = 128, 128
+    o1, s1 = gdr_lib.gdr_chunk_fwd(_g(inp.q), _g(inp.k), _g(inp.v),
+                                   _g(a.float()), _g(b.float()), _g(inp.s0),
+                                   out_dtype=torch.float32)
+    o2, s2 = gdr_lib.gdr2_chunk_fwd(
+        _g(inp.q), _g(inp.k), _g(inp.v),
+        _g(a[..., None].expand(-1, -1, -1, Dk).contiguous()),
+        _g(b[..., None].expand(-1, -1, -1, Dk).contiguous()),
+        _g(b[..., None].expand(-1, -1, -1, Dv).contiguous()), _g(inp.s0),
+        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert oracle.err_rms(o2.cpu(), o1.cpu()) <= 2e-2
+    assert oracle.err_rms(s2.cpu(), s1.cpu()) <= 2e-2
+
+
+def test_gdn2_kda_collapse(gdr_lib):
+    """b = w = beta (per token) with per-channel alpha: the KDA special case
+    against the oracle."""
+    from gdr_gen import make_gdn2
+    inp = make_gdn2(B=1, T=130, H=2, Dk=128, Dv=128, dtype="bf16", seed=27,
+                    s0_std=0.05)
+    beta = inp.erase[..., :1]
+    e = beta.expand(-1, -1, -1, 128).contiguous()
+    w = beta.expand(-1, -1, -1, 128).contiguous()
+    o, s = gdr_lib.gdr2_chunk_fwd(_g(inp.q), _g(inp.k), _g(inp.v),
+                                  _g(inp.alpha), _g(e), _g(w), _g(inp.s0),
+                                  out_dtype=torch.float32)
+    o_ref, s_ref = oracle.gdn2_fwd(inp.q, inp.k, inp.v, inp.alpha, e, w,
+                                   inp.s0)
+    torch.cuda.synchronize()
+    assert oracle.err_rms(o.cpu(), o_ref) <= 2e-2
+    assert oracle.err_rms(s.cpu(), s_ref) <= 2e-2

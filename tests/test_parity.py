@@ -209,3 +209,49 @@ def test_gdn_bf16_long_context(gdr_lib, cfg):
     eo, es = oracle.err_rms(o, o_ref), oracle.err_rms(s, s_ref)
     print(f"long context {cfg}: err(o)={eo:.3e} err(S)={es:.3e}")
     assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
+
+
+# ----------------------------------- Gated Delta Rule-2, bf16 (MFMA) ----
+
+@pytest.mark.parametrize("T", [1, 16, 17, 63, 64, 65, 130, 200])
+def test_gdn2_bf16_ragged(gdr_lib, T):
+    inp = make_gdn2(B=2, T=T, H=2, Dk=128, Dv=128, dtype="bf16", seed=300 + T,
+                    s0_std=0.05)
+    _check_gdn2(gdr_lib, inp, "f32")
+
+
+@pytest.mark.parametrize("dims", [(128, 128), (128, 64), (64, 128), (64, 64)])
+@pytest.mark.parametrize("odt", ["f32", "bf16"])
+def test_gdn2_bf16_dims(gdr_lib, dims, odt):
+    inp = make_gdn2(B=1, T=150, H=3, Dk=dims[0], Dv=dims[1], dtype="bf16",
+                    seed=31 + dims[0] + dims[1], s0_std=0.05)
+    _check_gdn2(gdr_lib, inp, odt)
+
+
+def test_gdn2_bf16_wide_decay_range(gdr_lib):
+    """Channel gates small enough that a 16-token block's decay range passes
+    the factored form's limit: that diagonal block is formed entry by
+    entry.  Also alpha = 0 (full reset of a channel)."""
+    inp = make_gdn2(B=1, T=140, H=2, Dk=128, Dv=128, dtype="bf16", seed=41,
+                    s0_std=0.05)
+    a = inp.alpha.clone()
+    a[0, 20:23, 0, 5] = 1e-12
+    a[0, 70, 1, :] = 0.0
+    a[0, 100:116, 1, 7] = 0.004
+    inp.alpha = a
+    _check_gdn2(gdr_lib, inp, "f32")
+
+
+def test_gdn2_bf16_workload_b4_h16_t4096(gdr_lib):
+    """The channel-gated workload at full size (B4 H16 T4096 d128), the
+    launch the benchmark times; the oracle checks batches 0 and 3."""
+    inp = make_config(4)
+    o, s = _run_gdn2(gdr_lib, inp, "f32")
+    pick = [0, 3]
+    o_ref, s_ref = oracle.gdn2_fwd(inp.q[pick], inp.k[pick], inp.v[pick],
+                                   inp.alpha[pick], inp.erase[pick],
+                                   inp.write[pick], None)
+    eo = oracle.err_rms(o[pick], o_ref)
+    es = oracle.err_rms(s[pick], s_ref)
+    print(f"workload B4H16T4096 GDN-2: err(o)={eo:.3e} err(S)={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
