@@ -15,11 +15,15 @@ The JSON line (stdout, last line) carries:
   decode             gdr_recurrent_step on 256 sequences x 16 heads, d=128,
                      64 consecutive steps: GB/s of state + token traffic
   gdr2               gdr2_chunk_fwd on B=4 H=16 T=4096 d=128 (bf16 gates)
-  cpu_baseline       the fp64 oracle timed on the host on a bounded sample
+  copy_reference     a plain 512 MiB device copy (achievable bandwidth)
+  cpu_baseline       the fp64 oracle timed on the host on the same workload
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -35,6 +39,81 @@ METRIC = "tokens/s chunkwise gated-delta fwd (H16,d128,T4K); % MFMA peak; decode
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+CSRC = os.path.join(ROOT, "gated_delta_rule_16_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+# kernel-name prefix in rocprofv3 output -> the bench leg it belongs to
+KERNELS = {"gdn": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, float>",
+           "gdr2": "void gdr::(anonymous namespace)::gdr2_bf16_kernel<128, 128, float>",
+           "decode": "void gdr::step_kernel<128, 128, unsigned short, float>",
+           "copy": "__amd_rocclr_copyBuffer"}
+
+
+def source_hash() -> str:
+    """Hash of every HIP source and header: counter readings are only valid
+    for the kernels they were taken on."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if f.endswith((".hip", ".h")):
+            h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def summarize(trace_dir, fetch_dir, write_dir, out_txt, command):
+    """Turn rocprofv3 CSV output (a --kernel-trace --stats run and two --pmc
+    runs, FETCH_SIZE then WRITE_SIZE) into a short text summary and the JSON
+    the benchmark reads its `traffic` figures from.  Counter KiB are scaled
+    by what the same counter reads for the plain 512 MiB device copy."""
+    stats = list(csv.DictReader(open(glob.glob(os.path.join(trace_dir, "*kernel_stats.csv"))[0])))
+    per = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = list(csv.DictReader(open(glob.glob(os.path.join(d, "*counter_collection.csv"))[0])))
+        for leg, prefix in KERNELS.items():
+            vals = [float(r["Counter_Value"]) for r in rows
+                    if r["Kernel_Name"].startswith(prefix) and r["Counter_Name"] == name]
+            if vals:
+                per.setdefault(leg, {})[name] = sum(vals) / len(vals)
+    copy_bytes_kib = 512 * 1024   # the copy reads and writes 512 MiB each
+    scale = {"FETCH_SIZE": copy_bytes_kib / per["copy"]["FETCH_SIZE"],
+             "WRITE_SIZE": copy_bytes_kib / per["copy"]["WRITE_SIZE"]}
+    traffic = {}
+    for leg, c in per.items():
+        if leg == "copy":
+            continue
+        rd = c["FETCH_SIZE"] * scale["FETCH_SIZE"] * 1024
+        wr = c["WRITE_SIZE"] * scale["WRITE_SIZE"] * 1024
+        traffic[leg] = {"read_bytes": rd, "write_bytes": wr, "bytes": rd + wr}
+    lines = [f"# rocprofv3 summary (HIP sources hash {source_hash()})", "",
+             "Command:", f"  {command}", "", "Kernel trace (--kernel-trace --stats):",
+             f"  {'kernel':60s} {'calls':>6s} {'avg us':>10s} {'min us':>10s} {'max us':>10s}"]
+    for r in stats:
+        lines.append(f"  {r['Name'][:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
+                     f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f}")
+    lines += ["", "HBM counters per dispatch (KiB as read; scale = copy's known bytes / reading):",
+              f"  FETCH_SIZE scale {scale['FETCH_SIZE']:.4f}, WRITE_SIZE scale {scale['WRITE_SIZE']:.4f}"]
+    for leg, c in per.items():
+        t = traffic.get(leg)
+        extra = "" if t is None else (f" -> read {t['read_bytes'] / 1e6:.1f} MB, write "
+                                      f"{t['write_bytes'] / 1e6:.1f} MB per launch")
+        lines.append(f"  {leg:7s} FETCH {c['FETCH_SIZE']:12.1f}  WRITE {c['WRITE_SIZE']:12.1f}{extra}")
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    json.dump({"source_hash": source_hash(), "scale": scale, "traffic": traffic,
+               "command": command}, open(TRAFFIC_FILE, "w"), indent=1)
+    print("\n".join(lines))
+
+
+def measured_traffic(leg):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernels have changed since the counters were taken."""
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != source_hash():
+        return None
+    t = d.get("traffic", {}).get(leg)
+    return None if t is None else t["bytes"]
 
 
 def time_launches(fn, warmup, steps):
@@ -135,21 +214,34 @@ def bench_gdr2(gdr, torch, warmup, steps):
     return dict(mean=mean, min=mn, median=med, B=B, T=T, H=H, bytes=bytes_launch)
 
 
-def cpu_baseline(inp):
-    """fp64 oracle on batches 0-1 of the same workload (2 x 16 heads x 4096
-    tokens), all host threads the oracle's OpenMP runtime uses."""
+def bench_copy(torch, warmup, steps, nbytes=512 << 20):
+    """A plain device-to-device copy of known size: the achievable-bandwidth
+    reference, and the kernel whose FETCH_SIZE / WRITE_SIZE counters scale
+    the counter readings of the other kernels."""
+    dev = torch.device("cuda:0")
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    y = torch.empty_like(x)
+    mean, mn, med, wall = time_launches(lambda: y.copy_(x), warmup, steps)
+    return dict(mean=mean, min=mn, bytes=2 * nbytes)
+
+
+def cpu_baseline(inp, repeats=3):
+    """The fp64 oracle on the whole workload (B8 H16 T4096 d128: it finishes
+    in about a second on the host), best of `repeats`, on every thread the
+    oracle's OpenMP runtime uses."""
     import oracle
-    sel = [0, 1]
-    q, k, v, a, b = (x[sel] for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta))
-    qq, kk, vv, aa, bb = (oracle._f64(x) for x in (q, k, v, a, b))   # conversion excluded
-    t0 = time.perf_counter()
-    oracle.gdn_fwd(qq, kk, vv, aa, bb, None)
-    dt = time.perf_counter() - t0
-    tokens = len(sel) * inp.q.shape[1]
-    return dict(value=tokens / dt, unit="tokens/s", cores=oracle.num_threads(),
+    qq, kk, vv, aa, bb = (oracle._f64(x) for x in (inp.q, inp.k, inp.v, inp.alpha,
+                                                     inp.beta))   # conversion excluded
+    best = float("inf")
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.gdn_fwd(qq, kk, vv, aa, bb, None)
+        best = min(best, time.perf_counter() - t0)
+    tokens = inp.q.shape[0] * inp.q.shape[1]
+    return dict(value=tokens / best, unit="tokens/s", cores=oracle.num_threads(),
                 kind="oracle",
-                sample=f"batches 0-1 of B8 H16 T4096 d128 ({tokens} tokens x 16 heads), "
-                       f"fp64, {dt:.2f} s")
+                sample=f"whole workload B8 H16 T4096 d128 ({tokens} tokens x 16 heads), "
+                       f"fp64 token-by-token recurrence, best of {repeats}: {best:.2f} s")
 
 
 def main():
@@ -158,13 +250,19 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
-    ap.add_argument("--only", choices=["gdn", "decode", "gdr2"], default=None,
+    ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "copy"], default=None,
                     help="time one operation only (for profiling)")
+    ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT"),
+                    help="summarize rocprofv3 CSV output into OUT and the traffic JSON, then exit")
+    ap.add_argument("--command", default="", help="the profiling command, recorded in --summarize")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(*args.summarize, command=args.command)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the path shards by batch/head with no communication; see the design notes)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this "
+              f"library runs on a single GPU (batch and head shards would need no "
+              f"communication, but no multi-GPU launcher is built)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -185,6 +283,9 @@ def main():
     if args.only in (None, "gdr2"):
         log("timing gdr2_chunk_fwd B4 H16 T4096 d128 ...")
         res["gdr2"] = bench_gdr2(gdr, torch, args.warmup, args.steps)
+    if args.only in (None, "copy"):
+        log("timing a 512 MiB device copy ...")
+        res["copy"] = bench_copy(torch, args.warmup, args.steps)
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -197,7 +298,8 @@ def main():
         out["ms_per_step"] = g["wall"] / args.steps * 1e3
         gbs = g["bytes"] / g["mean"] / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                           "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                           "traffic": measured_traffic("gdn"),
                            "kernel": "chunk_bf16_kernel<128,128,float>",
                            "algorithmic_bytes_per_launch": g["bytes"],
                            "launch_us_mean": g["mean"] * 1e6, "launch_us_min": g["min"] * 1e6}
@@ -214,7 +316,8 @@ def main():
         out["decode"] = {"workload": "gdr_recurrent_step N256 H16 d128, 64 steps",
                          "us_per_step_median": d["median"] * 1e6,
                          "us_per_step_min": d["min"] * 1e6, "GB/s": gbs,
-                         "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_step": d["bytes"]}
+                         "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_step": d["bytes"],
+                         "traffic": measured_traffic("decode")}
     if "gdr2" in res:
         r = res["gdr2"]
         if "error" in r:
@@ -224,7 +327,14 @@ def main():
             out["gdr2"] = {"workload": "gdr2_chunk_fwd B4 H16 T4096 d128 bf16, fp32 o",
                            "tokens/s": r["B"] * r["T"] / r["mean"],
                            "launch_us_mean": r["mean"] * 1e6, "GB/s": gbs,
-                           "frac_hbm": gbs / HBM_PEAK_GBS}
+                           "frac_hbm": gbs / HBM_PEAK_GBS,
+                           "algorithmic_bytes_per_launch": r["bytes"],
+                           "traffic": measured_traffic("gdr2")}
+    if "copy" in res:
+        cp = res["copy"]
+        out["copy_reference"] = {"what": "torch device-to-device copy, 512 MiB read + 512 MiB "
+                                         "written", "GB/s": cp["bytes"] / cp["mean"] / 1e9,
+                                 "frac_hbm": cp["bytes"] / cp["mean"] / 1e9 / HBM_PEAK_GBS}
     if not args.no_cpu and "gdn" in res:
         log("timing the fp64 oracle on the host ...")
         out["cpu_baseline"] = cpu_baseline(res["gdn"]["inp"])

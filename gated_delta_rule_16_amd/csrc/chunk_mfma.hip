@@ -46,7 +46,7 @@ constexpr int RB = 64;    // state rows per workgroup
 constexpr int NT = 256;   // threads per workgroup
 
 struct Bf16Params {
-    int64_t T, H;
+    int64_t T, H, BH;
     const bf16_t *q, *k, *v;
     const float *alpha, *beta;
     const float* s0;
@@ -120,8 +120,13 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(Bf16Params p) {
     const int hi = lane >> 5;
     const int m16 = lane & 15;
     const int kq = lane >> 4;
-    const int rbk = blockIdx.x % NRB;
-    const int64_t bh = blockIdx.x / NRB;
+    // Workgroups are dealt to the 8 XCDs round-robin (blockIdx.x % 8); the
+    // NRB row blocks of one head take the same XCD so that its key-side
+    // tiles are read from HBM once and then hit that XCD's L2.
+    const int64_t slot = blockIdx.x >> 3;
+    const int64_t bh = (slot / NRB) * 8 + (blockIdx.x & 7);
+    const int rbk = (int)(slot % NRB);
+    if (bh >= p.BH) return;
     const int64_t H = p.H, T = p.T;
     const int64_t h = bh % H;
     const int64_t b = bh / H;
@@ -448,6 +453,7 @@ hipError_t launch_bf16_t(const ChunkArgs& a) {
     Bf16Params p;
     p.T = a.T;
     p.H = a.H;
+    p.BH = a.B * a.H;
     p.q = (const bf16_t*)a.q;
     p.k = (const bf16_t*)a.k;
     p.v = (const bf16_t*)a.v;
@@ -461,7 +467,8 @@ hipError_t launch_bf16_t(const ChunkArgs& a) {
     hipError_t e =
         hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    const unsigned grid = (unsigned)(a.B * a.H * (DV / RB));
+    // 8 * ceil(B*H / 8) heads' worth of row blocks; surplus workgroups exit
+    const unsigned grid = (unsigned)(((a.B * a.H + 7) / 8) * 8 * (DV / RB));
     hipLaunchKernelGGL(fn, dim3(grid), dim3(NT), lds, a.stream, p);
     return hipGetLastError();
 }
