@@ -2,7 +2,7 @@
 // delta rule on gfx950 bf16 matrix cores, one fused pass over the sequence.
 //
 // Chunk algebra (rows of the state S are value channels; within a chunk of
-// C = 64 tokens, g_r = sum_{i<=r} log alpha_i, gamma_r = e^{g_r}; this is
+// C = 32 tokens, g_r = sum_{i<=r} log alpha_i, gamma_r = e^{g_r}; this is
 // the review's section 3.7 system on meaningful96.github.io with Gamma_rs =
 // e^{g_r - g_s}, the output mask carrying that decay and its diagonal, and
 // U^g - W S^T regrouped as T R):
@@ -15,35 +15,42 @@
 //   o_r   = gamma_r S q_r + sum_{s<=r} P_rs V_new_s
 //   S    <- gamma_C S + sum_s (e^{g_C - g_s} V_new_s) k_s^T
 //
-// Work split: one 256-thread workgroup (4 waves) per (b, h, 64 state rows);
-// rows of S evolve independently given the key side, so Dv = 128 runs as
-// two workgroups per head that both build A, T and P.  The workgroup walks
-// the chunks in order with S resident: fp32 in matrix-core accumulators
-// (as S^T tiles) and a bf16 hi/lo copy in LDS for use as an operand.  The
-// next chunk's q, k, v, alpha, beta are loaded into registers while the
-// current chunk computes.  Every matrix-core phase first issues all of its
-// LDS operand reads and then its MFMAs, so reads stream behind the math.
+// Everything that depends only on q, k, alpha, beta of a chunk (A, T, P and
+// the decay factors) is off the sequential path: the workgroup is split in
+// two teams that run one chunk apart.
 //
-// Per chunk (bf16 32x32x16 MFMA tiles unless noted, 4 waves):
-//   (1) K K^T and K Q^T lower tiles -> A (fp32) and P (hi/lo)      48 MFMA
-//   (2) K S^T -> R (hi/lo), Q S^T kept in registers              128 MFMA
-//   (3) T = (I + A)^{-1} in 16x16 blocks: diagonal blocks by forward
-//       substitution (4 lanes per column), then T_10, T_32, and the lower
-//       32x32 block -T_22 A_21 T_11 on fp32 16x16x4 matrix cores
-//   (4) V_new = T R -> V_new and decayed V_new (hi/lo)              36 MFMA
-//   (5) o = gamma (Q S^T) + P V_new -> HBM                          36 MFMA
-//   (6) S^T = gamma_C S^T + K^T V' (K^T read transposed from LDS)   64 MFMA
+//   team A  RB / 16 waves, wave a owns state rows 16 a .. 16 a + 15 (as S^T
+//           tiles in registers) and walks the chunks in order: K S^T and
+//           Q S^T, R, V_new = T R, o, and the state update.  Every operand
+//           it needs from another wave was written in the previous period,
+//           so it runs without barriers inside a period.
+//   team B  two waves that prepare chunk c + 1 while team A works on c:
+//           wave B0 stages K, computes the gates, A and T = (I + A)^{-1}
+//           (forward substitution on the 16x16 diagonal blocks, the
+//           off-diagonal block on fp32 matrix cores); wave B1 stages Q and
+//           V and computes P.  Their global loads run one chunk further
+//           ahead, in registers.
+//
+// A period ends with one workgroup barrier; LDS holds two sets of chunk
+// tiles (team A reads set c & 1 while team B writes the other).
+//
+// Matrix products use v_mfma_f32_16x16x32_bf16 (lane l, g = l / 16,
+// m = l % 16: A operand A[m][8 g + e], B operand B[8 g + e][m], C register
+// r = C[4 g + r][m]).  A contraction may visit its index in any order as
+// long as both operands agree; team A uses kappa(g, e) = 4 g + e for e < 4
+// and 16 + 4 g + (e - 4) otherwise, which makes a C tile pair (rows 4 g + r
+// of tiles 0 and 1) directly usable as the next product's B operand, so the
+// state, R and V_new never leave registers.  Computed operands enter as bf16
+// hi/lo pairs (see mfma_common.h).
 #include "launch.h"
 #include "mfma_common.h"
-#include "wy_solve.h"
 
 namespace gdr {
 
 namespace {
 
-constexpr int CH = 64;    // tokens per chunk
-constexpr int RB = 64;    // state rows per workgroup
-constexpr int NT = 256;   // threads per workgroup
+constexpr int CH = 32;    // tokens per chunk
+constexpr int P36 = 36;   // pitch of the 32-wide T, P (bf16) and A, T (fp32) tiles
 
 struct Bf16Params {
     int64_t T, H, BH;
@@ -54,72 +61,67 @@ struct Bf16Params {
     float* s_final;
 };
 
-template <int DK>
-struct Smem {
-    static constexpr int PK = DK + 8;  // pitch of K, Q, S rows (elements)
-    static constexpr int KB = 0;                             // K [64][PK]
-    static constexpr int QB = KB + 64 * PK * 2;              // Q [64][PK] | T fp32 [64][PF]
-    static constexpr int QB_SZ = (64 * PK * 2) > (64 * PF * 4) ? (64 * PK * 2) : (64 * PF * 4);
-    static constexpr int VB = QB + QB_SZ;                    // V [64][P72] | solve scratch
-    static constexpr int VB_SZ = (64 * P72 * 2) > (4 * 16 * PX * 4) ? (64 * P72 * 2)
-                                                                    : (4 * 16 * PX * 4);
-    static constexpr int SH = VB + VB_SZ;                    // S hi [RB][PK]
-    static constexpr int SL = SH + RB * PK * 2;              // S lo
-    static constexpr int AN = SL + RB * PK * 2;              // A fp32 [64][PF] | V_new^T hi, lo
-    static constexpr int AN_SZ = (64 * PF * 4) > (2 * RB * P72 * 2) ? (64 * PF * 4)
-                                                                    : (2 * RB * P72 * 2);
-    static constexpr int TT = AN + AN_SZ;                    // T hi, lo [64][P72]
-    static constexpr int PP = TT + 2 * 64 * P72 * 2;         // P hi, lo [64][P72]
-    static constexpr int RM = PP + 2 * 64 * P72 * 2;         // R^T hi, lo | V'^T hi, lo
-    static constexpr int GT = RM + 2 * RB * P72 * 2;         // g, beta, gamma, decay-to-end
-    static constexpr int TOTAL = GT + 4 * CH * 4;
+template <int DK, int RB>
+struct Lay {
+    static constexpr int PV = RB == 64 ? 80 : 48;   // V row pitch: 8 or 24 banks apart
+    static constexpr int K = 0;                     // K [32][DK] (swizzled)
+    static constexpr int Q = K + CH * DK * 2;       // Q [32][DK] (swizzled)
+    static constexpr int V = Q + CH * DK * 2;       // V [32][PV]
+    static constexpr int TH = V + CH * PV * 2;      // T hi, lo [32][P36]
+    static constexpr int TL = TH + CH * P36 * 2;
+    static constexpr int PH = TL + CH * P36 * 2;    // P hi, lo [32][P36]
+    static constexpr int PL = PH + CH * P36 * 2;
+    static constexpr int G = PL + CH * P36 * 2;     // g, beta, gamma, decay-to-end [4][32]
+    static constexpr int SET = G + 4 * CH * 4;
+    static constexpr int AF = 2 * SET;              // B0 private: A fp32 [32][P36]
+    static constexpr int TF = AF + CH * P36 * 4;    //             T fp32 [32][P36]
+    static constexpr int TOTAL = TF + CH * P36 * 4;
+    static_assert(SET % 16 == 0 && (CH * PV * 2) % 16 == 0, "alignment");
 };
 
-template <int DK, int DV, typename TOut>
-__global__ __launch_bounds__(NT) void chunk_bf16_kernel(Bf16Params p) {
-    using M = Smem<DK>;
-    constexpr int PK = M::PK;
+// K and Q rows are stored with their 4-element (8-byte) pieces permuted by
+// row: piece p of row r lives at p ^ f(r), f(r) = 4 (r mod 4) + (r / 4) mod 4.
+// Both read patterns (16 consecutive rows at one piece, and 4 rows x 4
+// pieces for the transposed reads) then hit 16 distinct bank pairs.
+template <int DK>
+__device__ __forceinline__ int swz(int row, int col) {
+    const int f = ((row & 3) << 2) | ((row >> 2) & 3);
+    return row * DK + ((((col >> 2) ^ f)) << 2);
+}
+
+// Orders this wave's earlier LDS writes before its later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ void split44(const f32x4& a, const f32x4& b, bf16x8& h, bf16x8& l) {
+    split8(f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}, h, l);
+}
+
+__device__ __forceinline__ void st8(bf16_t* p, const uint2& x) {
+    *reinterpret_cast<uint2*>(p) = x;
+}
+
+template <int DK, int DV, int RB, typename TOut>
+__global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Params p) {
+    using L = Lay<DK, RB>;
+    constexpr int NA = RB / 16;   // team A waves
+    constexpr int KJ = DK / 32;   // 32-deep contraction steps over the key dim
+    constexpr int NS = DK / 16;   // S^T tiles per team A wave
     constexpr int NRB = DV / RB;
-    constexpr int KC = DK / 8;               // 16-byte pieces per key row
-    constexpr int KLD = CH * KC / NT;        // key (and query) pieces per thread
-    constexpr int VC = RB / 8;               // 16-byte pieces per value row slice
-    constexpr int VLD = CH * VC / NT;
-    constexpr int NS = DK / 64;              // S^T tiles per wave
-    constexpr int KS = DK / 16;              // k-steps over the key dim
-    static_assert(KLD * NT == CH * KC && VLD * NT == CH * VC, "load split");
-    static_assert(M::TOTAL <= 160 * 1024, "LDS budget");
+    constexpr int VC = RB / 8;    // 16-byte pieces per value row slice
+    constexpr int VL = CH * VC / 64;
+    static_assert(VL * 64 == CH * VC, "value load split");
+    static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
 
     extern __shared__ __align__(16) unsigned char smem[];
-    bf16_t* Kb = reinterpret_cast<bf16_t*>(smem + M::KB);
-    bf16_t* Qb = reinterpret_cast<bf16_t*>(smem + M::QB);
-    float* Tf = reinterpret_cast<float*>(smem + M::QB);
-    bf16_t* Vb = reinterpret_cast<bf16_t*>(smem + M::VB);
-    float* Xs = reinterpret_cast<float*>(smem + M::VB);
-    bf16_t* Sh = reinterpret_cast<bf16_t*>(smem + M::SH);
-    bf16_t* Sl = reinterpret_cast<bf16_t*>(smem + M::SL);
-    float* Af = reinterpret_cast<float*>(smem + M::AN);
-    bf16_t* Nh = reinterpret_cast<bf16_t*>(smem + M::AN);
-    bf16_t* Nl = Nh + RB * P72;
-    bf16_t* Th = reinterpret_cast<bf16_t*>(smem + M::TT);
-    bf16_t* Tl = Th + 64 * P72;
-    bf16_t* Ph = reinterpret_cast<bf16_t*>(smem + M::PP);
-    bf16_t* Pl = Ph + 64 * P72;
-    bf16_t* Rh = reinterpret_cast<bf16_t*>(smem + M::RM);
-    bf16_t* Rl = Rh + RB * P72;
-    bf16_t* Mh = Rh;
-    bf16_t* Ml = Rl;
-    float* g_s = reinterpret_cast<float*>(smem + M::GT);
-    float* b_s = g_s + CH;
-    float* gam_s = b_s + CH;
-    float* dec_s = gam_s + CH;
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int l32 = lane & 31;
-    const int hi = lane >> 5;
-    const int m16 = lane & 15;
-    const int kq = lane >> 4;
+    const int g = lane >> 4;
+    const int m = lane & 15;
+
     // Workgroups are dealt to the 8 XCDs round-robin (blockIdx.x % 8); the
     // NRB row blocks of one head take the same XCD so that its key-side
     // tiles are read from HBM once and then hit that XCD's L2.
@@ -131,324 +133,408 @@ __global__ __launch_bounds__(NT) void chunk_bf16_kernel(Bf16Params p) {
     const int64_t h = bh % H;
     const int64_t b = bh / H;
     const int row0 = rbk * RB;
-    // tile of the 64 x 64 (token x state-row) products owned by this wave
-    const int tb = wave >> 1;
-    const int ib = wave & 1;
+    const int64_t nch = (T + CH - 1) / CH;
 
-    // T's upper 16x16 blocks inside its diagonal 32x32 tiles are read as
-    // zeros by (4); they are never written afterwards.
-    for (int e = tid; e < 2 * 16 * 16; e += NT) {
-        const int blk = e >> 8, r = 32 * blk + ((e >> 4) & 15), s = 32 * blk + 16 + (e & 15);
-        Th[r * P72 + s] = 0;
-        Tl[r * P72 + s] = 0;
+    auto setp = [&](int64_t c, int off) { return smem + (int)(c & 1) * L::SET + off; };
+
+    // T and P vanish above their diagonal 16x16 blocks (rows 0..15,
+    // columns 16..31); those entries are never written afterwards.
+    for (int e = tid; e < 2 * 4 * 256; e += blockDim.x) {
+        const int set = e >> 10, arr = (e >> 8) & 3, r = (e >> 4) & 15, s = 16 + (e & 15);
+        const int off = arr == 0 ? L::TH : arr == 1 ? L::TL : arr == 2 ? L::PH : L::PL;
+        reinterpret_cast<bf16_t*>(smem + set * L::SET + off)[r * P36 + s] = 0;
     }
 
-    // ---- initial state: S^T tiles in accumulators, hi/lo S in LDS --------
-    f32x16 sacc[NS];
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-        const int t = wave * NS + u;
-        const int dkb = t >> 1, ibs = t & 1;
-        const int i = ibs * 32 + l32;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int dk = dkb * 32 + 8 * j + 4 * hi;
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
-            if (p.s0)
-                x = *reinterpret_cast<const f32x4*>(p.s0 + ((bh * DV + row0 + i) * DK + dk));
-            sacc[u][4 * j + 0] = x.x;
-            sacc[u][4 * j + 1] = x.y;
-            sacc[u][4 * j + 2] = x.z;
-            sacc[u][4 * j + 3] = x.w;
-            st4_split(Sh + i * PK + dk, Sl + i * PK + dk, x.x, x.y, x.z, x.w);
-        }
-    }
-
-    // ---- register prefetch of one chunk -----------------------------------
+    const int64_t tstride = H * DK;   // elements between tokens of q, k
     const bf16_t* kbase = p.k + (b * T * H + h) * DK;
     const bf16_t* qbase = p.q + (b * T * H + h) * DK;
     const bf16_t* vbase = p.v + (b * T * H + h) * DV + row0;
-    u32x4 pk[KLD], pq[KLD], pv[VLD];
-    float pa = 1.f, pb = 0.f;
-    auto prefetch = [&](int64_t t0) {
+    const float* abase = p.alpha + b * T * H + h;
+    const float* bbase = p.beta + b * T * H + h;
+
+    if (wave < NA) {
+        // =========================== team A ================================
+        const int a = wave;
+        const int i = 16 * a + m;   // state row (within the block) of this lane
+        // sa[t][r] = S[i][16 t + 4 g + r]
+        f32x4 sa[NS];
 #pragma unroll
-        for (int m = 0; m < KLD; ++m) {
-            const int c = tid + NT * m;
-            const int row = c / KC, col = (c % KC) * 8;
-            const int64_t tok = t0 + row;
-            if (tok < T) {
-                const int64_t off = tok * H * DK + col;
-                pk[m] = *reinterpret_cast<const u32x4*>(kbase + off);
-                pq[m] = *reinterpret_cast<const u32x4*>(qbase + off);
-            } else {
-                pk[m] = u32x4{0u, 0u, 0u, 0u};
-                pq[m] = u32x4{0u, 0u, 0u, 0u};
+        for (int t = 0; t < NS; ++t) {
+            sa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (p.s0)
+                sa[t] = *reinterpret_cast<const f32x4*>(p.s0 + ((bh * DV + row0 + i) * DK + 16 * t +
+                                                                4 * g));
+        }
+        lds_barrier();   // set 0 prepared
+        TOut* obase = reinterpret_cast<TOut*>(p.o) + (b * T * H + h) * DV + row0 + i;
+        for (int64_t c = 0; c < nch; ++c) {
+            const bf16_t* Kb = reinterpret_cast<const bf16_t*>(setp(c, L::K));
+            const bf16_t* Qb = reinterpret_cast<const bf16_t*>(setp(c, L::Q));
+            const bf16_t* Vb = reinterpret_cast<const bf16_t*>(setp(c, L::V));
+            const bf16_t* Th = reinterpret_cast<const bf16_t*>(setp(c, L::TH));
+            const bf16_t* Tl = reinterpret_cast<const bf16_t*>(setp(c, L::TL));
+            const bf16_t* Ph = reinterpret_cast<const bf16_t*>(setp(c, L::PH));
+            const bf16_t* Pl = reinterpret_cast<const bf16_t*>(setp(c, L::PL));
+            const float* G = reinterpret_cast<const float*>(setp(c, L::G));
+
+            // ---- K S^T and Q S^T for the two 16-token tiles -------------
+            bf16x8 kf[2][KJ], qf[2][KJ];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int j = 0; j < KJ; ++j) {
+                    const int row = 16 * tt + m;
+                    kf[tt][j] = ld2x4(Kb + swz<DK>(row, 32 * j + 4 * g),
+                                      Kb + swz<DK>(row, 32 * j + 16 + 4 * g));
+                    qf[tt][j] = ld2x4(Qb + swz<DK>(row, 32 * j + 4 * g),
+                                      Qb + swz<DK>(row, 32 * j + 16 + 4 * g));
+                }
+            bf16x8 sh[KJ], sl[KJ];
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) split44(sa[2 * j], sa[2 * j + 1], sh[j], sl[j]);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 ks[2], qs[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                ks[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                qs[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < KJ; ++j) {
+                    ks[tt] = mfma16(kf[tt][j], sh[j], ks[tt]);
+                    qs[tt] = mfma16(qf[tt][j], sh[j], qs[tt]);
+                    ks[tt] = mfma16(kf[tt][j], sl[j], ks[tt]);
+                    qs[tt] = mfma16(qf[tt][j], sl[j], qs[tt]);
+                }
             }
-        }
+
+            // ---- R = beta (V - gamma K S^T), V_new = T R ----------------
+            f32x4 bet[2], gam[2], dec[2];
+            s16x4 vv[2];
 #pragma unroll
-        for (int m = 0; m < VLD; ++m) {
-            const int c = tid + NT * m;
-            const int row = c / VC, col = (c % VC) * 8;
-            const int64_t tok = t0 + row;
-            if (tok < T)
-                pv[m] = *reinterpret_cast<const u32x4*>(vbase + tok * H * DV + col);
-            else
-                pv[m] = u32x4{0u, 0u, 0u, 0u};
+            for (int tt = 0; tt < 2; ++tt) {
+                bet[tt] = *reinterpret_cast<const f32x4*>(G + CH + 16 * tt + 4 * g);
+                gam[tt] = *reinterpret_cast<const f32x4*>(G + 2 * CH + 16 * tt + 4 * g);
+                dec[tt] = *reinterpret_cast<const f32x4*>(G + 3 * CH + 16 * tt + 4 * g);
+                // V[16 tt + 4 g + r][i], r = 0..3, by a transposed read
+                vv[tt] = lds_tr16(Vb + (16 * tt + 4 * g + (m >> 2)) * L::PV + 16 * a + 4 * (m & 3));
+            }
+            const float gC = G[2 * CH + CH - 1];
+            bf16x8 th[2], tl[2], ph[2], pl[2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const int row = (16 * rt + m) * P36;
+                th[rt] = ld2x4(Th + row + 4 * g, Th + row + 16 + 4 * g);
+                tl[rt] = ld2x4(Tl + row + 4 * g, Tl + row + 16 + 4 * g);
+                ph[rt] = ld2x4(Ph + row + 4 * g, Ph + row + 16 + 4 * g);
+                pl[rt] = ld2x4(Pl + row + 4 * g, Pl + row + 16 + 4 * g);
+            }
+            f32x4 rr[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    rr[tt][r] = bet[tt][r] * (bf2f((bf16_t)vv[tt][r]) - gam[tt][r] * ks[tt][r]);
+            bf16x8 rh, rl;
+            split44(rr[0], rr[1], rh, rl);
+            f32x4 vn[2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                vn[rt] = mfma16(th[rt], rh, f32x4{0.f, 0.f, 0.f, 0.f});
+                vn[rt] = mfma16(th[rt], rl, vn[rt]);
+                vn[rt] = mfma16(tl[rt], rh, vn[rt]);
+            }
+
+            // ---- o = gamma Q S^T + P V_new;  S^T = gamma_C S^T + K^T V' --
+            bf16x8 nh, nl, mh, ml;
+            split44(vn[0], vn[1], nh, nl);
+            split44(vn[0] * dec[0], vn[1] * dec[1], mh, ml);
+            bf16x8 kt[NS];
+#pragma unroll
+            for (int t = 0; t < NS; ++t) {
+                // K[kappa(g, e)][16 t + m] by two transposed reads
+                const int col = 16 * t + 4 * (m & 3);
+                const s16x4 x0 = lds_tr16(Kb + swz<DK>(4 * g + (m >> 2), col));
+                const s16x4 x1 = lds_tr16(Kb + swz<DK>(16 + 4 * g + (m >> 2), col));
+                const s16x4 x2[2] = {x0, x1};
+                kt[t] = __builtin_bit_cast(bf16x8, x2);
+            }
+            f32x4 o[2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                o[rt] = qs[rt] * gam[rt];
+                o[rt] = mfma16(ph[rt], nh, o[rt]);
+                o[rt] = mfma16(ph[rt], nl, o[rt]);
+                o[rt] = mfma16(pl[rt], nh, o[rt]);
+            }
+#pragma unroll
+            for (int t = 0; t < NS; ++t) {
+                sa[t] *= gC;
+                sa[t] = mfma16(kt[t], mh, sa[t]);
+                sa[t] = mfma16(kt[t], ml, sa[t]);
+            }
+            const int64_t t0 = c * CH;
+            const int n = (int)((T - t0) < CH ? (T - t0) : CH);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tok = 16 * rt + 4 * g + r;
+                    if (tok < n) io<TOut>::st(obase + (t0 + tok) * H * DV, o[rt][r]);
+                }
+            lds_barrier();
         }
-        if (tid < CH) {
-            const int64_t tok = t0 + tid;
-            pa = tok < T ? p.alpha[(b * T + tok) * H + h] : 1.f;
-            pb = tok < T ? p.beta[(b * T + tok) * H + h] : 0.f;
+        if (p.s_final) {
+#pragma unroll
+            for (int t = 0; t < NS; ++t)
+                *reinterpret_cast<f32x4*>(p.s_final + ((bh * DV + row0 + i) * DK + 16 * t + 4 * g)) =
+                    sa[t];
+        }
+        return;
+    }
+
+    // ============================== team B =================================
+    // Global loads of chunk cn: lane (g, m) holds rows 16 tt + m, elements
+    // 32 j + 8 g .. + 7 of K (and Q) -- the natural operand layout of the
+    // 16x16x32 product; lanes 0..31 hold the gates of token `lane`.  Each
+    // wave keeps two chunks in flight (chunk x in buffer x & 1).
+    // Rows past the end of the sequence repeat its last token: they only
+    // ever meet beta = 0 (rows of A, R and V_new) or are not stored (o).
+    auto load_k = [&](int64_t cn, u32x4 (&kr)[2][KJ], const bf16_t* base) {
+        const int64_t t0 = cn * CH;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int64_t tok = min(t0 + 16 * tt + m, T - 1);
+#pragma unroll
+            for (int j = 0; j < KJ; ++j)
+                kr[tt][j] = *reinterpret_cast<const u32x4*>(base + tok * tstride + 32 * j + 8 * g);
+        }
+    };
+    // alpha (1 past the end) and beta of token `lane`
+    auto load_gate = [&](int64_t cn, float& al, float& be) {
+        const int64_t tok = cn * CH + (lane & 31);
+        const bool live = lane < CH && tok < T;
+        al = live ? abase[tok * H] : 1.f;
+        be = live ? bbase[tok * H] : 0.f;
+    };
+    // Period structure shared by both waves: prologue prepares chunk 0, then
+    // period c loads chunk c + 2 and prepares chunk c + 1.
+    auto run = [&](auto&& load, auto&& prepare, auto& f0, auto& f1) {
+        load(0, f0);
+        if (nch > 1) load(1, f1);
+        prepare(0, f0);
+        lds_barrier();
+        for (int64_t c = 0; c < nch; c += 2) {
+            if (c + 2 < nch) load(c + 2, f0);
+            if (c + 1 < nch) prepare(c + 1, f1);
+            lds_barrier();
+            if (c + 1 < nch) {
+                if (c + 3 < nch) load(c + 3, f1);
+                if (c + 2 < nch) prepare(c + 2, f0);
+                lds_barrier();
+            }
         }
     };
 
-    prefetch(0);
-    const int64_t nch = (T + CH - 1) / CH;
-    for (int64_t c = 0; c < nch; ++c) {
-        const int64_t t0 = c * CH;
-        const int n = (int)((T - t0) < CH ? (T - t0) : CH);
-        lds_barrier();
-        // ---- stage the chunk (row-major; transposes come from tr reads) ----
-#pragma unroll
-        for (int m = 0; m < KLD; ++m) {
-            const int cc = tid + NT * m;
-            const int row = cc / KC, col = (cc % KC) * 8;
-            *reinterpret_cast<u32x4*>(Kb + row * PK + col) = pk[m];
-            *reinterpret_cast<u32x4*>(Qb + row * PK + col) = pq[m];
-        }
-#pragma unroll
-        for (int m = 0; m < VLD; ++m) {
-            const int cc = tid + NT * m;
-            const int row = cc / VC, col = (cc % VC) * 8;
-            *reinterpret_cast<u32x4*>(Vb + row * P72 + col) = pv[m];
-        }
-        if (wave == 0) {
-            const float gx = wave_scan(safe_log(pa));   // cumulative log decay
-            const float glast = __shfl(gx, 63, 64);
-            g_s[lane] = gx;
-            b_s[lane] = pb;
-            gam_s[lane] = __expf(gx);
-            dec_s[lane] = __expf(glast - gx);
-        }
-        if (c + 1 < nch) prefetch(t0 + CH);
-        lds_barrier();
-
-        // ---- (1) A and P from the lower 32x32 tiles of K K^T and K Q^T ----
-        if (wave < 3) {
-            const int sb = wave == 2 ? 1 : 0;   // tile rows: tokens s
-            const int rt = wave == 0 ? 0 : 1;   // tile cols: tokens r
-            bf16x8 fa[KS], fk[KS], fq[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int kk = ks * 16 + 8 * hi;
-                fa[ks] = frag(Kb, PK, sb * 32 + l32, kk);
-                fk[ks] = frag(Kb, PK, rt * 32 + l32, kk);
-                fq[ks] = frag(Qb, PK, rt * 32 + l32, kk);
+    if (wave == NA) {
+        // ------------------------------- B0 --------------------------------
+        // K staging, gates, A, T = (I + A)^{-1}
+        struct Buf {
+            u32x4 k[2][KJ];
+            float al, be;
+        };
+        float* Af = reinterpret_cast<float*>(smem + L::AF);
+        float* Tf = reinterpret_cast<float*>(smem + L::TF);
+        auto load = [&](int64_t cn, Buf& f) {
+            load_k(cn, f.k, kbase);
+            load_gate(cn, f.al, f.be);
+        };
+        auto prepare = [&](int64_t cn, const Buf& f) {
+            bf16_t* Kb = reinterpret_cast<bf16_t*>(setp(cn, L::K));
+            bf16_t* Th = reinterpret_cast<bf16_t*>(setp(cn, L::TH));
+            bf16_t* Tl = reinterpret_cast<bf16_t*>(setp(cn, L::TL));
+            float* G = reinterpret_cast<float*>(setp(cn, L::G));
+            const float gx = wave_scan(safe_log(f.al));   // g of token `lane` (lanes < 32)
+            const float gC = __shfl(gx, CH - 1, 64);
+            if (lane < CH) {
+                G[lane] = gx;
+                G[CH + lane] = f.be;
+                G[2 * CH + lane] = __expf(gx);
+                G[3 * CH + lane] = __expf(gC - gx);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            f32x16 akk = {}, apk = {};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                akk = mfma(fa[ks], fk[ks], akk);
-                apk = mfma(fa[ks], fq[ks], apk);
-            }
-            const int r = rt * 32 + l32;
-            const float gr = g_s[r], br = b_s[r];
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int s0 = sb * 32 + 8 * j + 4 * hi;
-                const f32x4 gs = *reinterpret_cast<const f32x4*>(g_s + s0);
-                float av[4], pv4[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int s = s0 + e;
-                    const float d = s <= r ? __expf(fminf(gr - gs[e], 0.f)) : 0.f;
-                    av[e] = s < r ? br * d * akk[4 * j + e] : 0.f;
-                    pv4[e] = d * apk[4 * j + e];
+                for (int j = 0; j < KJ; ++j) {
+                    const int row = 16 * tt + m;
+                    st8(Kb + swz<DK>(row, 32 * j + 8 * g), uint2{f.k[tt][j][0], f.k[tt][j][1]});
+                    st8(Kb + swz<DK>(row, 32 * j + 8 * g + 4), uint2{f.k[tt][j][2], f.k[tt][j][3]});
                 }
-                *reinterpret_cast<f32x4*>(Af + r * PF + s0) = f32x4{av[0], av[1], av[2], av[3]};
-                st4_split(Ph + r * P72 + s0, Pl + r * P72 + s0, pv4[0], pv4[1], pv4[2], pv4[3]);
+            // Gram tiles (s-tile, r-tile) = (0,0), (0,1), (1,1):
+            // C[4 g + r][m] = k_{16 st + 4 g + r} . k_{16 rt + m}
+            f32x4 acc[3] = {};
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) {
+                const bf16x8 k0 = __builtin_bit_cast(bf16x8, f.k[0][j]);
+                const bf16x8 k1 = __builtin_bit_cast(bf16x8, f.k[1][j]);
+                acc[0] = mfma16(k0, k0, acc[0]);
+                acc[1] = mfma16(k0, k1, acc[1]);
+                acc[2] = mfma16(k1, k1, acc[2]);
             }
-        }
-
-        // ---- (2) K S^T -> R;  Q S^T kept for the output --------------------
-        f32x16 qs = {};
-        {
-            bf16x8 fk[KS], fq[KS], fh[KS], fl[KS];
+            wave_lds_sync();   // G visible to every lane
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int kk = ks * 16 + 8 * hi;
-                fk[ks] = frag(Kb, PK, tb * 32 + l32, kk);
-                fq[ks] = frag(Qb, PK, tb * 32 + l32, kk);
-                fh[ks] = frag(Sh, PK, ib * 32 + l32, kk);
-                fl[ks] = frag(Sl, PK, ib * 32 + l32, kk);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            f32x16 aks = {};
+            for (int u = 0; u < 3; ++u) {
+                const int st = u == 2 ? 1 : 0, rt = u == 0 ? 0 : 1;
+                const int rp = 16 * rt + m;
+                const float gr = G[rp], br = G[CH + rp];
+                const f32x4 gs = *reinterpret_cast<const f32x4*>(G + 16 * st + 4 * g);
+                f32x4 av;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                aks = mfma(fk[ks], fh[ks], aks);
-                qs = mfma(fq[ks], fh[ks], qs);
-                aks = mfma(fk[ks], fl[ks], aks);
-                qs = mfma(fq[ks], fl[ks], qs);
-            }
-            const int i = ib * 32 + l32;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int s0 = tb * 32 + 8 * j + 4 * hi;
-                // V[s0 .. s0+3][i] via a transposed read of the row-major tile
-                const s16x4 vv = lds_tr16(Vb + (s0 + (m16 >> 2)) * P72 + ib * 32 +
-                                          16 * (kq & 1) + 4 * (m16 & 3));
-                const f32x4 bs = *reinterpret_cast<const f32x4*>(b_s + s0);
-                const f32x4 gs = *reinterpret_cast<const f32x4*>(gam_s + s0);
-                float r4[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    r4[e] = bs[e] * (bf2f((bf16_t)vv[e]) - gs[e] * aks[4 * j + e]);
-                st4_split(Rh + i * P72 + s0, Rl + i * P72 + s0, r4[0], r4[1], r4[2], r4[3]);
-            }
-        }
-        lds_barrier();
-
-        // ---- (3) T = (I + A)^{-1} -----------------------------------------
-        solve_unit_lower_64(Af, Tf, Xs, Th, Tl);
-
-        // ---- (4) V_new = T R ------------------------------------------------
-        f32x16 vn = {};
-        {
-            bf16x8 th[4], tl[4], rh[4], rl[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                if (ks < 2 || tb == 1) {   // T vanishes above its diagonal 32x32 tiles
-                    const int kk = ks * 16 + 8 * hi;
-                    th[ks] = frag(Th, P72, tb * 32 + l32, kk);
-                    tl[ks] = frag(Tl, P72, tb * 32 + l32, kk);
-                    rh[ks] = frag(Rh, P72, ib * 32 + l32, kk);
-                    rl[ks] = frag(Rl, P72, ib * 32 + l32, kk);
+                for (int r = 0; r < 4; ++r) {
+                    const int s = 16 * st + 4 * g + r;
+                    av[r] = s < rp ? br * __expf(fminf(gr - gs[r], 0.f)) * acc[u][r] : 0.f;
                 }
+                *reinterpret_cast<f32x4*>(Af + rp * P36 + 16 * st + 4 * g) = av;
             }
-            __builtin_amdgcn_sched_barrier(0);
+            wave_lds_sync();
+            // Diagonal blocks X = (I + L)^{-1}, L = A's block `blk`: lane pair
+            // (blk, rr) builds row rr from X = I - X L, columns right to left,
+            // pushing each finished entry into the columns left of it.
+            {
+                const int blk = lane >> 5, rr = (lane >> 1) & 15, half = lane & 1;
+                const float* Lb = Af + 16 * blk * P36 + 16 * blk;
+                float acc2[16], x[16];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                if (ks < 2 || tb == 1) {
-                    vn = mfma(th[ks], rh[ks], vn);
-                    vn = mfma(th[ks], rl[ks], vn);
-                    vn = mfma(tl[ks], rh[ks], vn);
+                for (int cc = 0; cc < 16; ++cc) acc2[cc] = 0.f;
+#pragma unroll
+                for (int cp = 15; cp >= 0; --cp) {
+                    x[cp] = (rr == cp ? 1.f : 0.f) - acc2[cp];
+#pragma unroll
+                    for (int q4 = 0; q4 < (cp + 3) / 4; ++q4) {
+                        const f32x4 lr = *reinterpret_cast<const f32x4*>(Lb + cp * P36 + 4 * q4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * q4 + e < cp) acc2[4 * q4 + e] += x[cp] * lr[e];
+                    }
                 }
+                // columns 8 half .. 8 half + 7 of row 16 blk + rr
+                const int row = 16 * blk + rr, col = 16 * blk + 8 * half;
+                // (bitwise select: a conditional here becomes an indexed
+                // private array)
+                const uint32_t msk = half ? 0xffffffffu : 0u;
+                float xs[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    xs[e] = __uint_as_float((__float_as_uint(x[8 + e]) & msk) |
+                                            (__float_as_uint(x[e]) & ~msk));
+                *reinterpret_cast<f32x4*>(Tf + row * P36 + col) = f32x4{xs[0], xs[1], xs[2], xs[3]};
+                *reinterpret_cast<f32x4*>(Tf + row * P36 + col + 4) =
+                    f32x4{xs[4], xs[5], xs[6], xs[7]};
+                bf16x8 xh, xl;
+                split8(f32x8{xs[0], xs[1], xs[2], xs[3], xs[4], xs[5], xs[6], xs[7]}, xh, xl);
+                const u32x4 uh = __builtin_bit_cast(u32x4, xh), ul = __builtin_bit_cast(u32x4, xl);
+                st8(Th + row * P36 + col, uint2{uh[0], uh[1]});
+                st8(Th + row * P36 + col + 4, uint2{uh[2], uh[3]});
+                st8(Tl + row * P36 + col, uint2{ul[0], ul[1]});
+                st8(Tl + row * P36 + col + 4, uint2{ul[2], ul[3]});
             }
-        }
-        lds_barrier();  // R fully read (its space takes V'), A dead (takes V_new)
-        {
-            const int i = ib * 32 + l32;
+            wave_lds_sync();
+            // T_10 = -T_11 A_10 T_00 on fp32 16x16x4 matrix cores:
+            // Y = A_10 T_00 (C layout Y[4 g + r][m]), then -T_10^T = Y^T T_11^T
+            // with the contraction order 4 g + kk so that Y's registers are
+            // its A operand as they stand.
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r0 = tb * 32 + 8 * j + 4 * hi;
-                const f32x4 dd = *reinterpret_cast<const f32x4*>(dec_s + r0);
-                st4_split(Nh + i * P72 + r0, Nl + i * P72 + r0, vn[4 * j], vn[4 * j + 1],
-                          vn[4 * j + 2], vn[4 * j + 3]);
-                st4_split(Mh + i * P72 + r0, Ml + i * P72 + r0, vn[4 * j] * dd[0],
-                          vn[4 * j + 1] * dd[1], vn[4 * j + 2] * dd[2], vn[4 * j + 3] * dd[3]);
+            for (int kk = 0; kk < 4; ++kk)
+                y = mfma_f32(Af[(16 + m) * P36 + 4 * kk + g], Tf[(4 * kk + g) * P36 + m], y);
+            f32x4 t10 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                t10 = mfma_f32(y[kk], Tf[(16 + m) * P36 + 16 + 4 * g + kk], t10);
+            uint2 vh, vl;
+            split2(-t10[0], -t10[1], vh.x, vl.x);
+            split2(-t10[2], -t10[3], vh.y, vl.y);
+            st8(Th + (16 + m) * P36 + 4 * g, vh);
+            st8(Tl + (16 + m) * P36 + 4 * g, vl);
+        };
+        Buf f0, f1;
+        run(load, prepare, f0, f1);
+    } else {
+        // ------------------------------- B1 --------------------------------
+        // Q and V staging, P
+        struct Buf {
+            u32x4 k[2][KJ];
+            u32x4 q[2][KJ];
+            u32x4 v[VL];
+            float al, be;
+        };
+        auto load = [&](int64_t cn, Buf& f) {
+            load_k(cn, f.k, kbase);
+            load_k(cn, f.q, qbase);
+            const int64_t t0 = cn * CH;
+#pragma unroll
+            for (int u = 0; u < VL; ++u) {
+                const int pc = lane + 64 * u;
+                const int64_t tok = min(t0 + pc / VC, T - 1);
+                f.v[u] = *reinterpret_cast<const u32x4*>(vbase + tok * H * DV + 8 * (pc % VC));
             }
-        }
-        lds_barrier();
-
-        // ---- (5) o = gamma (Q S^T) + P V_new -------------------------------
-        {
-            bf16x8 ph[4], pl[4], nh[4], nl[4];
+            load_gate(cn, f.al, f.be);
+        };
+        auto prepare = [&](int64_t cn, const Buf& f) {
+            bf16_t* Qb = reinterpret_cast<bf16_t*>(setp(cn, L::Q));
+            bf16_t* Vb = reinterpret_cast<bf16_t*>(setp(cn, L::V));
+            bf16_t* Ph = reinterpret_cast<bf16_t*>(setp(cn, L::PH));
+            bf16_t* Pl = reinterpret_cast<bf16_t*>(setp(cn, L::PL));
+            const float gx = wave_scan(safe_log(f.al));
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                if (ks < 2 || tb == 1) {   // P vanishes above its diagonal tiles
-                    const int kk = ks * 16 + 8 * hi;
-                    ph[ks] = frag(Ph, P72, tb * 32 + l32, kk);
-                    pl[ks] = frag(Pl, P72, tb * 32 + l32, kk);
-                    nh[ks] = frag(Nh, P72, ib * 32 + l32, kk);
-                    nl[ks] = frag(Nl, P72, ib * 32 + l32, kk);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x4 gg = *reinterpret_cast<const f32x4*>(gam_s + tb * 32 + 8 * j + 4 * hi);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) qs[4 * j + e] *= gg[e];
-            }
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                if (ks < 2 || tb == 1) {
-                    qs = mfma(ph[ks], nh[ks], qs);
-                    qs = mfma(ph[ks], nl[ks], qs);
-                    qs = mfma(pl[ks], nh[ks], qs);
-                }
-            }
-        }
-        // ---- (6) S^T = gamma_C S^T + K^T V' --------------------------------
-        {
-            bf16x8 ka[4], mh[NS][4], ml[NS][4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int kk = ks * 16 + 8 * hi;
-                ka[ks] = frag_tr(Kb, PK, ks * 16, (wave * NS >> 1) * 32);
-#pragma unroll
-                for (int u = 0; u < NS; ++u) {
-                    const int ibs = (wave * NS + u) & 1;
-                    mh[u][ks] = frag(Mh, P72, ibs * 32 + l32, kk);
-                    ml[u][ks] = frag(Ml, P72, ibs * 32 + l32, kk);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            const float gC = __expf(g_s[CH - 1]);
-#pragma unroll
-            for (int u = 0; u < NS; ++u) sacc[u] *= gC;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int u = 0; u < NS; ++u) {
-                    sacc[u] = mfma(ka[ks], mh[u][ks], sacc[u]);
-                    sacc[u] = mfma(ka[ks], ml[u][ks], sacc[u]);
-                }
-        }
-        {
-            TOut* o = reinterpret_cast<TOut*>(p.o);
-            const int i = row0 + ib * 32 + l32;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = tb * 32 + 8 * j + 4 * hi + e;
-                    if (r < n) io<TOut>::st(o + (((b * T + t0 + r) * H + h) * DV + i), qs[4 * j + e]);
+                for (int j = 0; j < KJ; ++j) {
+                    const int row = 16 * tt + m;
+                    st8(Qb + swz<DK>(row, 32 * j + 8 * g), uint2{f.q[tt][j][0], f.q[tt][j][1]});
+                    st8(Qb + swz<DK>(row, 32 * j + 8 * g + 4), uint2{f.q[tt][j][2], f.q[tt][j][3]});
                 }
 #pragma unroll
-            for (int u = 0; u < NS; ++u) {
-                const int t = wave * NS + u;
-                const int dkb = t >> 1, ibs = t & 1;
-                const int si = ibs * 32 + l32;
+            for (int u = 0; u < VL; ++u) {
+                const int pc = lane + 64 * u;
+                *reinterpret_cast<u32x4*>(Vb + (pc / VC) * L::PV + 8 * (pc % VC)) = f.v[u];
+            }
+            // C[4 g + r][m] = k_{16 st + 4 g + r} . q_{16 rt + m}
+            f32x4 acc[3] = {};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int dk = dkb * 32 + 8 * j + 4 * hi;
-                    st4_split(Sh + si * PK + dk, Sl + si * PK + dk, sacc[u][4 * j],
-                              sacc[u][4 * j + 1], sacc[u][4 * j + 2], sacc[u][4 * j + 3]);
+            for (int j = 0; j < KJ; ++j) {
+                const bf16x8 k0 = __builtin_bit_cast(bf16x8, f.k[0][j]);
+                const bf16x8 k1 = __builtin_bit_cast(bf16x8, f.k[1][j]);
+                const bf16x8 q0 = __builtin_bit_cast(bf16x8, f.q[0][j]);
+                const bf16x8 q1 = __builtin_bit_cast(bf16x8, f.q[1][j]);
+                acc[0] = mfma16(k0, q0, acc[0]);
+                acc[1] = mfma16(k0, q1, acc[1]);
+                acc[2] = mfma16(k1, q1, acc[2]);
+            }
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                const int st = u == 2 ? 1 : 0, rt = u == 0 ? 0 : 1;
+                const int rp = 16 * rt + m;
+                const float gr = __shfl(gx, rp, 64);
+                float pv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int s = 16 * st + 4 * g + r;
+                    const float gs = __shfl(gx, s, 64);
+                    pv[r] = s <= rp ? __expf(fminf(gr - gs, 0.f)) * acc[u][r] : 0.f;
                 }
+                uint2 vh, vl;
+                split2(pv[0], pv[1], vh.x, vl.x);
+                split2(pv[2], pv[3], vh.y, vl.y);
+                st8(Ph + rp * P36 + 16 * st + 4 * g, vh);
+                st8(Pl + rp * P36 + 16 * st + 4 * g, vl);
             }
-        }
-    }
-
-    if (p.s_final) {
-#pragma unroll
-        for (int u = 0; u < NS; ++u) {
-            const int t = wave * NS + u;
-            const int dkb = t >> 1, ibs = t & 1;
-            const int i = ibs * 32 + l32;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int dk = dkb * 32 + 8 * j + 4 * hi;
-                *reinterpret_cast<f32x4*>(p.s_final + ((bh * DV + row0 + i) * DK + dk)) =
-                    f32x4{sacc[u][4 * j], sacc[u][4 * j + 1], sacc[u][4 * j + 2], sacc[u][4 * j + 3]};
-            }
-        }
+        };
+        Buf f0, f1;
+        run(load, prepare, f0, f1);
     }
 }
 
-template <int DK, int DV, typename TOut>
+template <int DK, int DV, int RB, typename TOut>
 hipError_t launch_bf16_t(const ChunkArgs& a) {
     Bf16Params p;
     p.T = a.T;
@@ -462,20 +548,25 @@ hipError_t launch_bf16_t(const ChunkArgs& a) {
     p.s0 = a.s0;
     p.o = a.o;
     p.s_final = a.s_final;
-    const size_t lds = Smem<DK>::TOTAL;
-    auto fn = chunk_bf16_kernel<DK, DV, TOut>;
+    const size_t lds = Lay<DK, RB>::TOTAL;
+    auto fn = chunk_bf16_kernel<DK, DV, RB, TOut>;
     hipError_t e =
         hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     // 8 * ceil(B*H / 8) heads' worth of row blocks; surplus workgroups exit
     const unsigned grid = (unsigned)(((a.B * a.H + 7) / 8) * 8 * (DV / RB));
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(NT), lds, a.stream, p);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * (RB / 16 + 2)), lds, a.stream, p);
     return hipGetLastError();
 }
 
 template <int DK, int DV>
 hipError_t launch_bf16_d(const ChunkArgs& a) {
-    return a.out_bf16 ? launch_bf16_t<DK, DV, bf16_t>(a) : launch_bf16_t<DK, DV, float>(a);
+    // Few heads (long single sequences): narrower row blocks so that more
+    // workgroups run side by side.
+    if (a.B * a.H * (DV / 64) < 128) {
+        return a.out_bf16 ? launch_bf16_t<DK, DV, 16, bf16_t>(a) : launch_bf16_t<DK, DV, 16, float>(a);
+    }
+    return a.out_bf16 ? launch_bf16_t<DK, DV, 64, bf16_t>(a) : launch_bf16_t<DK, DV, 64, float>(a);
 }
 
 }  // namespace

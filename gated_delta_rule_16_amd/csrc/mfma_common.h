@@ -126,6 +126,45 @@ __device__ __forceinline__ float wave_scan(float x) {
     return x;
 }
 
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// 8 consecutive fp32 from LDS (two 16-byte reads).
+__device__ __forceinline__ f32x8 ld8f(const float* p) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__device__ __forceinline__ f32x8 ld8bf(const bf16_t* p) {
+    const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+    return f32x8{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
+                 __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u),
+                 __uint_as_float(u[2] << 16), __uint_as_float(u[2] & 0xffff0000u),
+                 __uint_as_float(u[3] << 16), __uint_as_float(u[3] & 0xffff0000u)};
+}
+
+// fp32 x8 -> hi/lo bf16 operand fragments.
+__device__ __forceinline__ void split8(const f32x8& x, bf16x8& h, bf16x8& l) {
+    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+    split2(x[0], x[1], h0, l0);
+    split2(x[2], x[3], h1, l1);
+    split2(x[4], x[5], h2, l2);
+    split2(x[6], x[7], h3, l3);
+    h = __builtin_bit_cast(bf16x8, u32x4{h0, h1, h2, h3});
+    l = __builtin_bit_cast(bf16x8, u32x4{l0, l1, l2, l3});
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two 8-byte LDS reads (4 bf16 each) joined into one operand fragment.
+__device__ __forceinline__ bf16x8 ld2x4(const bf16_t* p0, const bf16_t* p1) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p0);
+    const uint2 b = *reinterpret_cast<const uint2*>(p1);
+    return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+}
+
 // Workgroup barrier that orders LDS only: outstanding global loads (the
 // next chunk's prefetch) stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {

@@ -162,7 +162,7 @@ def test_gdn2_fp32(gdr_lib, T, dims):
 
 # ------------------------------------------- bf16 chunked forward (MFMA) ----
 
-@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 128, 200, 333])
+@pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 63, 64, 65, 96, 127, 128, 200, 333])
 def test_gdn_bf16_ragged(gdr_lib, T):
     inp = make_gdn(B=2, T=T, H=2, Dk=128, Dv=128, dtype="bf16", seed=100 + T,
                    s0_std=0.05)
@@ -175,6 +175,17 @@ def test_gdn_bf16_dims(gdr_lib, dims, odt):
     inp = make_gdn(B=1, T=190, H=3, Dk=dims[0], Dv=dims[1], dtype="bf16",
                    seed=7 + dims[0] + dims[1], s0_std=0.05)
     _check_gdn(gdr_lib, inp, odt)
+
+
+@pytest.mark.parametrize("T,dims", [(33, (128, 128)), (100, (128, 128)),
+                                    (70, (64, 128)), (45, (128, 64)), (64, (64, 64))])
+def test_gdn_bf16_many_heads(gdr_lib, T, dims):
+    """Enough heads for the wide row blocks (64 state rows per workgroup) that
+    the full-size workload uses; the few-head tests above take the narrow
+    ones."""
+    inp = make_gdn(B=8, T=T, H=16, Dk=dims[0], Dv=dims[1], dtype="bf16",
+                   seed=500 + T, s0_std=0.05)
+    _check_gdn(gdr_lib, inp, "f32")
 
 
 def test_gdn_bf16_zero_state_and_alias(gdr_lib):
