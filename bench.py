@@ -44,7 +44,7 @@ def log(*a):
 CSRC = os.path.join(ROOT, "gated_delta_rule_16_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
 # kernel-name prefix in rocprofv3 output -> the bench leg it belongs to
-KERNELS = {"gdn": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, float>",
+KERNELS = {"gdn": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, 64, float>",
            "gdr2": "void gdr::(anonymous namespace)::gdr2_bf16_kernel<128, 128, float>",
            "decode": "void gdr::step_kernel<128, 128, unsigned short, float>",
            "copy": "__amd_rocclr_copyBuffer"}
@@ -300,7 +300,7 @@ def main():
         out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                            "traffic": measured_traffic("gdn"),
-                           "kernel": "chunk_bf16_kernel<128,128,float>",
+                           "kernel": "chunk_bf16_kernel<128,128,64,float>",
                            "algorithmic_bytes_per_launch": g["bytes"],
                            "launch_us_mean": g["mean"] * 1e6, "launch_us_min": g["min"] * 1e6}
         tf = g["flops"] / g["mean"] / 1e12
@@ -309,7 +309,7 @@ def main():
         out["config"] = {"workload": "gdr_chunk_fwd B8 H16 T4096 d128, bf16 q/k/v, "
                                      "fp32 alpha/beta/o/state, zero initial state",
                          "B": g["B"], "T": g["T"], "H": g["H"], "Dk": g["Dk"], "Dv": g["Dv"],
-                         "chunk": 64, "global_batch": g["B"], "seq_len": g["T"]}
+                         "chunk": 32, "global_batch": g["B"], "seq_len": g["T"]}
     if "decode" in res:
         d = res["decode"]
         gbs = d["bytes"] / d["median"] / 1e9

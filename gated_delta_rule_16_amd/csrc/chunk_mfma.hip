@@ -15,24 +15,30 @@
 //   o_r   = gamma_r S q_r + sum_{s<=r} P_rs V_new_s
 //   S    <- gamma_C S + sum_s (e^{g_C - g_s} V_new_s) k_s^T
 //
+// The state is carried as S = sigma * S_hat with one scalar sigma per chunk
+// (the running product of the chunk decays gamma_C, reset to 1 whenever it
+// would drop below 2^-40), so decaying the whole state costs nothing: sigma
+// is folded into per-token factors that multiply K S_hat^T and Q S_hat^T
+// and divide the update (each at most 2^40 by the reset rule).
+//
 // Everything that depends only on q, k, alpha, beta of a chunk (A, T, P and
-// the decay factors) is off the sequential path: the workgroup is split in
-// two teams that run one chunk apart.
+// the per-token factors) is off the sequential path.  The workgroup holds
 //
 //   team A  RB / 16 waves, wave a owns state rows 16 a .. 16 a + 15 (as S^T
 //           tiles in registers) and walks the chunks in order: K S^T and
 //           Q S^T, R, V_new = T R, o, and the state update.  Every operand
-//           it needs from another wave was written in the previous period,
-//           so it runs without barriers inside a period.
-//   team B  two waves that prepare chunk c + 1 while team A works on c:
-//           wave B0 stages K, computes the gates, A and T = (I + A)^{-1}
-//           (forward substitution on the 16x16 diagonal blocks, the
-//           off-diagonal block on fp32 matrix cores); wave B1 stages Q and
-//           V and computes P.  Their global loads run one chunk further
+//           it needs from another wave was written in an earlier period, so
+//           it runs without barriers inside a period.
+//   team B  four waves, one per SIMD beside the team A waves, running ahead:
+//           B0 stages K and computes the per-token factors and sigma, B1
+//           solves T = (I + A)^{-1}, B2 stages Q and V and computes P (all
+//           for chunk c + 1 while team A works on chunk c), and B3 computes
+//           A for chunk c + 2.  Their global loads run one chunk further
 //           ahead, in registers.
 //
-// A period ends with one workgroup barrier; LDS holds two sets of chunk
-// tiles (team A reads set c & 1 while team B writes the other).
+// A period ends with one workgroup barrier.  LDS holds two sets of chunk
+// tiles (team A reads set c & 1 while team B writes the other) and two
+// copies of A.
 //
 // Matrix products use v_mfma_f32_16x16x32_bf16 (lane l, g = l / 16,
 // m = l % 16: A operand A[m][8 g + e], B operand B[8 g + e][m], C register
@@ -49,8 +55,10 @@ namespace gdr {
 
 namespace {
 
-constexpr int CH = 32;    // tokens per chunk
-constexpr int P36 = 36;   // pitch of the 32-wide T, P (bf16) and A, T (fp32) tiles
+constexpr int CH = 32;          // tokens per chunk
+constexpr int P36 = 36;         // pitch of the 32-wide T, P (bf16) and A, T (fp32) tiles
+constexpr int NB = 4;           // team B waves
+constexpr float kSigmaMin = 9.094947e-13f;   // 2^-40
 
 struct Bf16Params {
     int64_t T, H, BH;
@@ -60,6 +68,15 @@ struct Bf16Params {
     void* o;
     float* s_final;
 };
+
+// Per-token factors for team A (token t of the chunk, sigma at chunk start):
+//   FR1 = beta_t                 multiplies v_t in R
+//   FR2 = beta_t gamma_t sigma   multiplies (K S_hat^T)_t in R
+//   FO  = gamma_t sigma          multiplies (Q S_hat^T)_t in o
+//   FV  = e^{g_C - g_t} / sigma' scales V_new_t in the update, sigma' the
+//                                next chunk's sigma (1 after a reset)
+// followed by the reset flag and the factor S_hat is multiplied by on a reset.
+enum { FR1 = 0, FR2 = CH, FO = 2 * CH, FV = 3 * CH, FRESET = 4 * CH, FMUL = 4 * CH + 1 };
 
 template <int DK, int RB>
 struct Lay {
@@ -71,10 +88,10 @@ struct Lay {
     static constexpr int TL = TH + CH * P36 * 2;
     static constexpr int PH = TL + CH * P36 * 2;    // P hi, lo [32][P36]
     static constexpr int PL = PH + CH * P36 * 2;
-    static constexpr int G = PL + CH * P36 * 2;     // g, beta, gamma, decay-to-end [4][32]
-    static constexpr int SET = G + 4 * CH * 4;
-    static constexpr int AF = 2 * SET;              // B0 private: A fp32 [32][P36]
-    static constexpr int TF = AF + CH * P36 * 4;    //             T fp32 [32][P36]
+    static constexpr int G = PL + CH * P36 * 2;     // per-token factors
+    static constexpr int SET = G + (4 * CH + 4) * 4;
+    static constexpr int AF = 2 * SET;              // A fp32 [32][P36], two copies
+    static constexpr int TF = AF + 2 * CH * P36 * 4;   // B1 private: T fp32 [32][P36]
     static constexpr int TOTAL = TF + CH * P36 * 4;
     static_assert(SET % 16 == 0 && (CH * PV * 2) % 16 == 0, "alignment");
 };
@@ -104,7 +121,7 @@ __device__ __forceinline__ void st8(bf16_t* p, const uint2& x) {
 }
 
 template <int DK, int DV, int RB, typename TOut>
-__global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Params p) {
+__global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Params p) {
     using L = Lay<DK, RB>;
     constexpr int NA = RB / 16;   // team A waves
     constexpr int KJ = DK / 32;   // 32-deep contraction steps over the key dim
@@ -136,6 +153,9 @@ __global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Para
     const int64_t nch = (T + CH - 1) / CH;
 
     auto setp = [&](int64_t c, int off) { return smem + (int)(c & 1) * L::SET + off; };
+    auto afp = [&](int64_t c) {
+        return reinterpret_cast<float*>(smem + L::AF + (int)(c & 1) * CH * P36 * 4);
+    };
 
     // T and P vanish above their diagonal 16x16 blocks (rows 0..15,
     // columns 16..31); those entries are never written afterwards.
@@ -156,7 +176,7 @@ __global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Para
         // =========================== team A ================================
         const int a = wave;
         const int i = 16 * a + m;   // state row (within the block) of this lane
-        // sa[t][r] = S[i][16 t + 4 g + r]
+        // sa[t][r] = S_hat[i][16 t + 4 g + r]
         f32x4 sa[NS];
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
@@ -165,7 +185,11 @@ __global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Para
                 sa[t] = *reinterpret_cast<const f32x4*>(p.s0 + ((bh * DV + row0 + i) * DK + 16 * t +
                                                                 4 * g));
         }
-        lds_barrier();   // set 0 prepared
+        // two periods of pipeline fill: A of chunks 0 and 1, then the rest
+        // of chunk 0
+        lds_barrier();
+        lds_barrier();
+        const int64_t ostride = H * DV;
         TOut* obase = reinterpret_cast<TOut*>(p.o) + (b * T * H + h) * DV + row0 + i;
         for (int64_t c = 0; c < nch; ++c) {
             const bf16_t* Kb = reinterpret_cast<const bf16_t*>(setp(c, L::K));
@@ -207,18 +231,20 @@ __global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Para
                 }
             }
 
-            // ---- R = beta (V - gamma K S^T), V_new = T R ----------------
-            f32x4 bet[2], gam[2], dec[2];
+            // ---- R = FR1 V - FR2 (K S_hat^T), V_new = T R ---------------
+            f32x4 fr1[2], fr2[2], fo[2], fv[2];
             s16x4 vv[2];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                bet[tt] = *reinterpret_cast<const f32x4*>(G + CH + 16 * tt + 4 * g);
-                gam[tt] = *reinterpret_cast<const f32x4*>(G + 2 * CH + 16 * tt + 4 * g);
-                dec[tt] = *reinterpret_cast<const f32x4*>(G + 3 * CH + 16 * tt + 4 * g);
+                fr1[tt] = *reinterpret_cast<const f32x4*>(G + FR1 + 16 * tt + 4 * g);
+                fr2[tt] = *reinterpret_cast<const f32x4*>(G + FR2 + 16 * tt + 4 * g);
+                fo[tt] = *reinterpret_cast<const f32x4*>(G + FO + 16 * tt + 4 * g);
+                fv[tt] = *reinterpret_cast<const f32x4*>(G + FV + 16 * tt + 4 * g);
                 // V[16 tt + 4 g + r][i], r = 0..3, by a transposed read
                 vv[tt] = lds_tr16(Vb + (16 * tt + 4 * g + (m >> 2)) * L::PV + 16 * a + 4 * (m & 3));
             }
-            const float gC = G[2 * CH + CH - 1];
+            const bool reset = __builtin_amdgcn_readfirstlane(__float_as_int(G[FRESET])) != 0;
+            const float smul = G[FMUL];
             bf16x8 th[2], tl[2], ph[2], pl[2];
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
@@ -233,7 +259,8 @@ __global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Para
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    rr[tt][r] = bet[tt][r] * (bf2f((bf16_t)vv[tt][r]) - gam[tt][r] * ks[tt][r]);
+                    rr[tt][r] = __builtin_fmaf(-fr2[tt][r], ks[tt][r],
+                                               fr1[tt][r] * bf2f((bf16_t)vv[tt][r]));
             bf16x8 rh, rl;
             split44(rr[0], rr[1], rh, rl);
             f32x4 vn[2];
@@ -244,10 +271,10 @@ __global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Para
                 vn[rt] = mfma16(tl[rt], rh, vn[rt]);
             }
 
-            // ---- o = gamma Q S^T + P V_new;  S^T = gamma_C S^T + K^T V' --
+            // ---- o = FO (Q S_hat^T) + P V_new;  S_hat^T += K^T (FV V_new) --
             bf16x8 nh, nl, mh, ml;
             split44(vn[0], vn[1], nh, nl);
-            split44(vn[0] * dec[0], vn[1] * dec[1], mh, ml);
+            split44(vn[0] * fv[0], vn[1] * fv[1], mh, ml);
             bf16x8 kt[NS];
 #pragma unroll
             for (int t = 0; t < NS; ++t) {
@@ -261,29 +288,41 @@ __global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Para
             f32x4 o[2];
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                o[rt] = qs[rt] * gam[rt];
+                o[rt] = qs[rt] * fo[rt];
                 o[rt] = mfma16(ph[rt], nh, o[rt]);
                 o[rt] = mfma16(ph[rt], nl, o[rt]);
                 o[rt] = mfma16(pl[rt], nh, o[rt]);
             }
+            if (reset) {
+#pragma unroll
+                for (int t = 0; t < NS; ++t) sa[t] *= smul;
+            }
 #pragma unroll
             for (int t = 0; t < NS; ++t) {
-                sa[t] *= gC;
                 sa[t] = mfma16(kt[t], mh, sa[t]);
                 sa[t] = mfma16(kt[t], ml, sa[t]);
             }
             const int64_t t0 = c * CH;
-            const int n = (int)((T - t0) < CH ? (T - t0) : CH);
+            TOut* oc = obase + (t0 + 4 * g) * ostride;
+            if (T - t0 >= CH) {
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+                for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tok = 16 * rt + 4 * g + r;
-                    if (tok < n) io<TOut>::st(obase + (t0 + tok) * H * DV, o[rt][r]);
-                }
+                    for (int r = 0; r < 4; ++r)
+                        io<TOut>::st(oc + (16 * rt + r) * ostride, o[rt][r]);
+            } else {
+                const int n = (int)(T - t0);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (16 * rt + 4 * g + r < n)
+                            io<TOut>::st(oc + (16 * rt + r) * ostride, o[rt][r]);
+            }
             lds_barrier();
         }
         if (p.s_final) {
+            // the last chunk always resets sigma to 1, so S_hat is S here
 #pragma unroll
             for (int t = 0; t < NS; ++t)
                 *reinterpret_cast<f32x4*>(p.s_final + ((bh * DV + row0 + i) * DK + 16 * t + 4 * g)) =
@@ -293,12 +332,12 @@ __global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Para
     }
 
     // ============================== team B =================================
+    const int bw = wave - NA;
     // Global loads of chunk cn: lane (g, m) holds rows 16 tt + m, elements
-    // 32 j + 8 g .. + 7 of K (and Q) -- the natural operand layout of the
-    // 16x16x32 product; lanes 0..31 hold the gates of token `lane`.  Each
-    // wave keeps two chunks in flight (chunk x in buffer x & 1).
-    // Rows past the end of the sequence repeat its last token: they only
-    // ever meet beta = 0 (rows of A, R and V_new) or are not stored (o).
+    // 32 j + 8 g .. + 7 of K (or Q) -- the natural operand layout of the
+    // 16x16x32 product; lanes 0..31 hold the gates of token `lane`.  Rows
+    // past the end of the sequence repeat its last token: they only ever
+    // meet beta = 0 (rows of A, R and V_new) or are not stored (o).
     auto load_k = [&](int64_t cn, u32x4 (&kr)[2][KJ], const bf16_t* base) {
         const int64_t t0 = cn * CH;
 #pragma unroll
@@ -309,58 +348,60 @@ __global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Para
                 kr[tt][j] = *reinterpret_cast<const u32x4*>(base + tok * tstride + 32 * j + 8 * g);
         }
     };
-    // alpha (1 past the end) and beta of token `lane`
+    // alpha and beta of token `lane` (clamped into the sequence; masked at
+    // use by gate_live, so that no wait follows the load)
     auto load_gate = [&](int64_t cn, float& al, float& be) {
-        const int64_t tok = cn * CH + (lane & 31);
-        const bool live = lane < CH && tok < T;
-        al = live ? abase[tok * H] : 1.f;
-        be = live ? bbase[tok * H] : 0.f;
+        const int64_t tok = min(cn * CH + (lane & 31), T - 1);
+        al = abase[tok * H];
+        be = bbase[tok * H];
     };
-    // Period structure shared by both waves: prologue prepares chunk 0, then
-    // period c loads chunk c + 2 and prepares chunk c + 1.
-    auto run = [&](auto&& load, auto&& prepare, auto& f0, auto& f1) {
-        load(0, f0);
-        if (nch > 1) load(1, f1);
-        prepare(0, f0);
-        lds_barrier();
-        for (int64_t c = 0; c < nch; c += 2) {
-            if (c + 2 < nch) load(c + 2, f0);
-            if (c + 1 < nch) prepare(c + 1, f1);
-            lds_barrier();
-            if (c + 1 < nch) {
-                if (c + 3 < nch) load(c + 3, f1);
-                if (c + 2 < nch) prepare(c + 2, f0);
-                lds_barrier();
-            }
-        }
+    // alpha = 1, beta = 0 past the end of the sequence (and on lanes 32..63)
+    auto gate_live = [&](int64_t cn) { return lane < CH && cn * CH + lane < T; };
+    // g of token `lane` (lanes < 32) for chunk cn
+    auto gate_scan = [&](int64_t cn, float al) {
+        return wave_scan(gate_live(cn) ? safe_log(al) : 0.f);
     };
 
-    if (wave == NA) {
-        // ------------------------------- B0 --------------------------------
-        // K staging, gates, A, T = (I + A)^{-1}
+    // A role prepares chunk x in period x - lead (periods run from -2 to
+    // nch - 1, each closed by the workgroup barrier).  Buffers f0, f1 carry
+    // chunks x and x + 1; the load of chunk x + 2 is issued at the start of
+    // the period that prepares x + 1.  Loads are unconditional (an index
+    // past the end repeats the last chunk) so that the wait before each
+    // prepare covers just its buffer.
+    auto run = [&](int lead, auto&& load, auto&& prepare, auto& f0, auto& f1) {
+        for (int e = 0; e < 2 - lead; ++e) lds_barrier();
+        load(0, f0);
+        load(min((int64_t)1, nch - 1), f1);
+        int64_t x = 0;
+        for (; x + 1 < nch; x += 2) {
+            prepare(x, f0);
+            lds_barrier();
+            load(min(x + 2, nch - 1), f0);
+            prepare(x + 1, f1);
+            lds_barrier();
+            load(min(x + 3, nch - 1), f1);
+        }
+        if (x < nch) {
+            prepare(x, f0);
+            lds_barrier();
+        }
+        for (int e = 0; e < lead; ++e) lds_barrier();
+    };
+
+    if (bw == 0) {
+        // --------------------- B0: K staging, factors ----------------------
         struct Buf {
             u32x4 k[2][KJ];
             float al, be;
         };
-        float* Af = reinterpret_cast<float*>(smem + L::AF);
-        float* Tf = reinterpret_cast<float*>(smem + L::TF);
+        float sigma = 1.f;   // sigma at the start of the chunk being prepared
         auto load = [&](int64_t cn, Buf& f) {
             load_k(cn, f.k, kbase);
             load_gate(cn, f.al, f.be);
         };
         auto prepare = [&](int64_t cn, const Buf& f) {
             bf16_t* Kb = reinterpret_cast<bf16_t*>(setp(cn, L::K));
-            bf16_t* Th = reinterpret_cast<bf16_t*>(setp(cn, L::TH));
-            bf16_t* Tl = reinterpret_cast<bf16_t*>(setp(cn, L::TL));
             float* G = reinterpret_cast<float*>(setp(cn, L::G));
-            const float gx = wave_scan(safe_log(f.al));   // g of token `lane` (lanes < 32)
-            const float gC = __shfl(gx, CH - 1, 64);
-            if (lane < CH) {
-                G[lane] = gx;
-                G[CH + lane] = f.be;
-                G[2 * CH + lane] = __expf(gx);
-                G[3 * CH + lane] = __expf(gC - gx);
-            }
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -369,33 +410,38 @@ __global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Para
                     st8(Kb + swz<DK>(row, 32 * j + 8 * g), uint2{f.k[tt][j][0], f.k[tt][j][1]});
                     st8(Kb + swz<DK>(row, 32 * j + 8 * g + 4), uint2{f.k[tt][j][2], f.k[tt][j][3]});
                 }
-            // Gram tiles (s-tile, r-tile) = (0,0), (0,1), (1,1):
-            // C[4 g + r][m] = k_{16 st + 4 g + r} . k_{16 rt + m}
-            f32x4 acc[3] = {};
-#pragma unroll
-            for (int j = 0; j < KJ; ++j) {
-                const bf16x8 k0 = __builtin_bit_cast(bf16x8, f.k[0][j]);
-                const bf16x8 k1 = __builtin_bit_cast(bf16x8, f.k[1][j]);
-                acc[0] = mfma16(k0, k0, acc[0]);
-                acc[1] = mfma16(k0, k1, acc[1]);
-                acc[2] = mfma16(k1, k1, acc[2]);
+            const float gx = gate_scan(cn, f.al);
+            const float gC = __shfl(gx, CH - 1, 64);
+            const float be = gate_live(cn) ? f.be : 0.f;
+            // sigma' = sigma gamma_C; a reset keeps S_hat = S from here on.
+            // The last chunk always resets so that the final S_hat is S.
+            const float s1 = sigma * __expf(gC);
+            const bool reset = s1 < kSigmaMin || cn == nch - 1;
+            const float fo = sigma * __expf(gx);
+            const float dec = __expf(gC - gx);
+            if (lane < CH) {
+                G[FR1 + lane] = be;
+                G[FR2 + lane] = be * fo;
+                G[FO + lane] = fo;
+                G[FV + lane] = reset ? dec : dec / s1;
             }
-            wave_lds_sync();   // G visible to every lane
-#pragma unroll
-            for (int u = 0; u < 3; ++u) {
-                const int st = u == 2 ? 1 : 0, rt = u == 0 ? 0 : 1;
-                const int rp = 16 * rt + m;
-                const float gr = G[rp], br = G[CH + rp];
-                const f32x4 gs = *reinterpret_cast<const f32x4*>(G + 16 * st + 4 * g);
-                f32x4 av;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int s = 16 * st + 4 * g + r;
-                    av[r] = s < rp ? br * __expf(fminf(gr - gs[r], 0.f)) * acc[u][r] : 0.f;
-                }
-                *reinterpret_cast<f32x4*>(Af + rp * P36 + 16 * st + 4 * g) = av;
+            if (lane == 0) {
+                G[FRESET] = reset ? 1.f : 0.f;
+                G[FMUL] = s1;
             }
-            wave_lds_sync();
+            sigma = reset ? 1.f : s1;
+        };
+        Buf f0, f1;
+        run(1, load, prepare, f0, f1);
+    } else if (bw == 1) {
+        // ----------------------- B1: T = (I + A)^{-1} -----------------------
+        float* Tf = reinterpret_cast<float*>(smem + L::TF);
+        struct Buf {};
+        auto load = [&](int64_t, Buf&) {};
+        auto prepare = [&](int64_t cn, const Buf&) {
+            const float* Af = afp(cn);
+            bf16_t* Th = reinterpret_cast<bf16_t*>(setp(cn, L::TH));
+            bf16_t* Tl = reinterpret_cast<bf16_t*>(setp(cn, L::TL));
             // Diagonal blocks X = (I + L)^{-1}, L = A's block `blk`: lane pair
             // (blk, rr) builds row rr from X = I - X L, columns right to left,
             // pushing each finished entry into the columns left of it.
@@ -416,10 +462,9 @@ __global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Para
                             if (4 * q4 + e < cp) acc2[4 * q4 + e] += x[cp] * lr[e];
                     }
                 }
-                // columns 8 half .. 8 half + 7 of row 16 blk + rr
+                // columns 8 half .. 8 half + 7 of row 16 blk + rr (bitwise
+                // select: a conditional here becomes an indexed private array)
                 const int row = 16 * blk + rr, col = 16 * blk + 8 * half;
-                // (bitwise select: a conditional here becomes an indexed
-                // private array)
                 const uint32_t msk = half ? 0xffffffffu : 0u;
                 float xs[8];
 #pragma unroll
@@ -457,10 +502,9 @@ __global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Para
             st8(Tl + (16 + m) * P36 + 4 * g, vl);
         };
         Buf f0, f1;
-        run(load, prepare, f0, f1);
-    } else {
-        // ------------------------------- B1 --------------------------------
-        // Q and V staging, P
+        run(1, load, prepare, f0, f1);
+    } else if (bw == 2) {
+        // ---------------------- B2: Q and V staging, P ----------------------
         struct Buf {
             u32x4 k[2][KJ];
             u32x4 q[2][KJ];
@@ -484,7 +528,6 @@ __global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Para
             bf16_t* Vb = reinterpret_cast<bf16_t*>(setp(cn, L::V));
             bf16_t* Ph = reinterpret_cast<bf16_t*>(setp(cn, L::PH));
             bf16_t* Pl = reinterpret_cast<bf16_t*>(setp(cn, L::PL));
-            const float gx = wave_scan(safe_log(f.al));
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -510,6 +553,7 @@ __global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Para
                 acc[1] = mfma16(k0, q1, acc[1]);
                 acc[2] = mfma16(k1, q1, acc[2]);
             }
+            const float gx = gate_scan(cn, f.al);
 #pragma unroll
             for (int u = 0; u < 3; ++u) {
                 const int st = u == 2 ? 1 : 0, rt = u == 0 ? 0 : 1;
@@ -530,7 +574,49 @@ __global__ __launch_bounds__(64 * (RB / 16 + 2)) void chunk_bf16_kernel(Bf16Para
             }
         };
         Buf f0, f1;
-        run(load, prepare, f0, f1);
+        run(1, load, prepare, f0, f1);
+    } else {
+        // ------------------------------ B3: A -------------------------------
+        struct Buf {
+            u32x4 k[2][KJ];
+            float al, be;
+        };
+        auto load = [&](int64_t cn, Buf& f) {
+            load_k(cn, f.k, kbase);
+            load_gate(cn, f.al, f.be);
+        };
+        auto prepare = [&](int64_t cn, const Buf& f) {
+            float* Af = afp(cn);
+            // Gram tiles (s-tile, r-tile) = (0,0), (0,1), (1,1):
+            // C[4 g + r][m] = k_{16 st + 4 g + r} . k_{16 rt + m}
+            f32x4 acc[3] = {};
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) {
+                const bf16x8 k0 = __builtin_bit_cast(bf16x8, f.k[0][j]);
+                const bf16x8 k1 = __builtin_bit_cast(bf16x8, f.k[1][j]);
+                acc[0] = mfma16(k0, k0, acc[0]);
+                acc[1] = mfma16(k0, k1, acc[1]);
+                acc[2] = mfma16(k1, k1, acc[2]);
+            }
+            const float gx = gate_scan(cn, f.al);
+            const float be = gate_live(cn) ? f.be : 0.f;
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                const int st = u == 2 ? 1 : 0, rt = u == 0 ? 0 : 1;
+                const int rp = 16 * rt + m;
+                const float gr = __shfl(gx, rp, 64), br = __shfl(be, rp, 64);
+                f32x4 av;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int s = 16 * st + 4 * g + r;
+                    const float gs = __shfl(gx, s, 64);
+                    av[r] = s < rp ? br * __expf(fminf(gr - gs, 0.f)) * acc[u][r] : 0.f;
+                }
+                *reinterpret_cast<f32x4*>(Af + rp * P36 + 16 * st + 4 * g) = av;
+            }
+        };
+        Buf f0, f1;
+        run(2, load, prepare, f0, f1);
     }
 }
 
@@ -555,7 +641,7 @@ hipError_t launch_bf16_t(const ChunkArgs& a) {
     if (e != hipSuccess) return e;
     // 8 * ceil(B*H / 8) heads' worth of row blocks; surplus workgroups exit
     const unsigned grid = (unsigned)(((a.B * a.H + 7) / 8) * 8 * (DV / RB));
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * (RB / 16 + 2)), lds, a.stream, p);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * (RB / 16 + NB)), lds, a.stream, p);
     return hipGetLastError();
 }
 
