@@ -30,15 +30,14 @@
 //           it needs from another wave was written in an earlier period, so
 //           it runs without barriers inside a period.
 //   team B  four waves, one per SIMD beside the team A waves, running ahead:
-//           B0 stages K and computes the per-token factors and sigma, B1
-//           solves T = (I + A)^{-1}, B2 stages Q and V and computes P (all
-//           for chunk c + 1 while team A works on chunk c), and B3 computes
-//           A for chunk c + 2.  Their global loads run one chunk further
-//           ahead, in registers.
+//           B3 stages K, scans the gates and computes A for chunk c + 2;
+//           for chunk c + 1, B0 computes the per-token factors and sigma, B1
+//           solves T = (I + A)^{-1}, and B2 stages Q and V and computes P.
+//           Their global loads run two chunks further ahead, in registers.
 //
 // A period ends with one workgroup barrier.  LDS holds two sets of chunk
-// tiles (team A reads set c & 1 while team B writes the other) and two
-// copies of A.
+// tiles (team A reads set c & 1 while team B writes the other), three of K
+// and the gate scan (chunk c mod 3), and two copies of A.
 //
 // Matrix products use v_mfma_f32_16x16x32_bf16 (lane l, g = l / 16,
 // m = l % 16: A operand A[m][8 g + e], B operand B[8 g + e][m], C register
@@ -56,7 +55,8 @@ namespace gdr {
 namespace {
 
 constexpr int CH = 32;          // tokens per chunk
-constexpr int P36 = 36;         // pitch of the 32-wide T, P (bf16) and A, T (fp32) tiles
+constexpr int P36 = 36;         // pitch of the 32-wide fp32 tiles (A, T)
+constexpr int P48 = 48;         // pitch of the 32-wide bf16 tiles (T, P hi/lo): 96 bytes
 constexpr int NB = 4;           // team B waves
 constexpr float kSigmaMin = 9.094947e-13f;   // 2^-40
 
@@ -81,29 +81,43 @@ enum { FR1 = 0, FR2 = CH, FO = 2 * CH, FV = 3 * CH, FRESET = 4 * CH, FMUL = 4 * 
 template <int DK, int RB>
 struct Lay {
     static constexpr int PV = RB == 64 ? 80 : 48;   // V row pitch: 8 or 24 banks apart
-    static constexpr int K = 0;                     // K [32][DK] (swizzled)
-    static constexpr int Q = K + CH * DK * 2;       // Q [32][DK] (swizzled)
+    // per set (chunk parity)
+    static constexpr int Q = 0;                     // Q [32][DK] (swizzled)
     static constexpr int V = Q + CH * DK * 2;       // V [32][PV]
-    static constexpr int TH = V + CH * PV * 2;      // T hi, lo [32][P36]
-    static constexpr int TL = TH + CH * P36 * 2;
-    static constexpr int PH = TL + CH * P36 * 2;    // P hi, lo [32][P36]
-    static constexpr int PL = PH + CH * P36 * 2;
-    static constexpr int G = PL + CH * P36 * 2;     // per-token factors
+    static constexpr int TH = V + CH * PV * 2;      // T hi, lo [32][P48] (columns kperm'd)
+    static constexpr int TL = TH + CH * P48 * 2;
+    static constexpr int PH = TL + CH * P48 * 2;    // P hi, lo [32][P48] (columns kperm'd)
+    static constexpr int PL = PH + CH * P48 * 2;
+    static constexpr int G = PL + CH * P48 * 2;     // per-token factors
     static constexpr int SET = G + (4 * CH + 4) * 4;
-    static constexpr int AF = 2 * SET;              // A fp32 [32][P36], two copies
+    // per chunk mod 3: K twice -- in operand order (swizzled) for the
+    // products over the key dim, and row-major [32][DK + 16] for the
+    // transposed reads -- and the gate scan (g, beta)
+    static constexpr int PKN = DK + 16;
+    static constexpr int KSLOT = CH * DK * 2 + CH * PKN * 2;
+    static constexpr int KR = 2 * SET;
+    static constexpr int GR = KR + 3 * KSLOT;
+    static constexpr int AF = GR + 3 * 2 * CH * 4;  // A fp32 [32][P36], two copies
     static constexpr int TF = AF + 2 * CH * P36 * 4;   // B1 private: T fp32 [32][P36]
     static constexpr int TOTAL = TF + CH * P36 * 4;
     static_assert(SET % 16 == 0 && (CH * PV * 2) % 16 == 0, "alignment");
 };
 
-// K and Q rows are stored with their 4-element (8-byte) pieces permuted by
-// row: piece p of row r lives at p ^ f(r), f(r) = 4 (r mod 4) + (r / 4) mod 4.
-// Both read patterns (16 consecutive rows at one piece, and 4 rows x 4
-// pieces for the transposed reads) then hit 16 distinct bank pairs.
+// Operand order of a contraction over 32 columns: column 16 h + 4 q + e of
+// each block of 32 (h < 2, q < 4, e < 4) is stored at 8 q + 4 h + e, so the
+// 8 values that lane group q feeds an MFMA in kappa order are one 16-byte
+// read.  K, Q (per 32 key channels), T and P (over their 32 tokens) are
+// stored this way.
+__device__ __forceinline__ int kperm(int c) {
+    return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3);
+}
+
+// Element offset of (row, stored column pc) in an operand-order K or Q
+// tile: 16-byte unit u of row r is stored at u ^ (r mod DK / 8), so the 16
+// rows one lane group reads at one unit fall on distinct banks.
 template <int DK>
-__device__ __forceinline__ int swz(int row, int col) {
-    const int f = ((row & 3) << 2) | ((row >> 2) & 3);
-    return row * DK + ((((col >> 2) ^ f)) << 2);
+__device__ __forceinline__ int kq_at(int row, int pc) {
+    return row * DK + ((((pc >> 3) ^ (row & (DK / 8 - 1)))) << 3) + (pc & 7);
 }
 
 // Orders this wave's earlier LDS writes before its later LDS reads.
@@ -156,13 +170,19 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
     auto afp = [&](int64_t c) {
         return reinterpret_cast<float*>(smem + L::AF + (int)(c & 1) * CH * P36 * 4);
     };
+    auto kring = [&](int64_t c) {
+        return reinterpret_cast<bf16_t*>(smem + L::KR + (int)(c % 3) * L::KSLOT);
+    };
+    auto gring = [&](int64_t c) {
+        return reinterpret_cast<float*>(smem + L::GR + (int)(c % 3) * 2 * CH * 4);
+    };
 
     // T and P vanish above their diagonal 16x16 blocks (rows 0..15,
     // columns 16..31); those entries are never written afterwards.
     for (int e = tid; e < 2 * 4 * 256; e += blockDim.x) {
         const int set = e >> 10, arr = (e >> 8) & 3, r = (e >> 4) & 15, s = 16 + (e & 15);
         const int off = arr == 0 ? L::TH : arr == 1 ? L::TL : arr == 2 ? L::PH : L::PL;
-        reinterpret_cast<bf16_t*>(smem + set * L::SET + off)[r * P36 + s] = 0;
+        reinterpret_cast<bf16_t*>(smem + set * L::SET + off)[r * P48 + kperm(s)] = 0;
     }
 
     const int64_t tstride = H * DK;   // elements between tokens of q, k
@@ -185,14 +205,28 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                 sa[t] = *reinterpret_cast<const f32x4*>(p.s0 + ((bh * DV + row0 + i) * DK + 16 * t +
                                                                 4 * g));
         }
+        // S_hat as hi/lo B operands (contraction index kappa over 32 key
+        // channels per step); refreshed at the end of every chunk
+        bf16x8 sh[KJ], sl[KJ];
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) split44(sa[2 * j], sa[2 * j + 1], sh[j], sl[j]);
         // two periods of pipeline fill: A of chunks 0 and 1, then the rest
         // of chunk 0
         lds_barrier();
         lds_barrier();
-        const int64_t ostride = H * DV;
-        TOut* obase = reinterpret_cast<TOut*>(p.o) + (b * T * H + h) * DV + row0 + i;
+        // o goes out through buffer stores: a per-chunk resource whose range
+        // ends after the chunk's last token (stores past it are dropped) and
+        // fixed per-lane byte offsets o[t0 + 16 rt + 4 g + r][row0 + i]
+        uint32_t ooff[2][4];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                ooff[rt][r] = (uint32_t)(((16 * rt + 4 * g + r) * (int)(H * DV) + row0 + i) *
+                                         (int)sizeof(TOut));
+        TOut* obase = reinterpret_cast<TOut*>(p.o) + (b * T * H + h) * DV;
         for (int64_t c = 0; c < nch; ++c) {
-            const bf16_t* Kb = reinterpret_cast<const bf16_t*>(setp(c, L::K));
+            const bf16_t* Kb = kring(c);
             const bf16_t* Qb = reinterpret_cast<const bf16_t*>(setp(c, L::Q));
             const bf16_t* Vb = reinterpret_cast<const bf16_t*>(setp(c, L::V));
             const bf16_t* Th = reinterpret_cast<const bf16_t*>(setp(c, L::TH));
@@ -201,59 +235,57 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
             const bf16_t* Pl = reinterpret_cast<const bf16_t*>(setp(c, L::PL));
             const float* G = reinterpret_cast<const float*>(setp(c, L::G));
 
-            // ---- K S^T and Q S^T for the two 16-token tiles -------------
+            // The state chain K S^T -> R -> V_new -> update -> next split
+            // runs first in each phase; Q S^T, o and the stores fill the
+            // matrix-core and VALU gaps around it.
+            // ---- K S_hat^T (state chain) -----------------------------------
             bf16x8 kf[2][KJ], qf[2][KJ];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int j = 0; j < KJ; ++j) {
-                    const int row = 16 * tt + m;
-                    kf[tt][j] = ld2x4(Kb + swz<DK>(row, 32 * j + 4 * g),
-                                      Kb + swz<DK>(row, 32 * j + 16 + 4 * g));
-                    qf[tt][j] = ld2x4(Qb + swz<DK>(row, 32 * j + 4 * g),
-                                      Qb + swz<DK>(row, 32 * j + 16 + 4 * g));
-                }
-            bf16x8 sh[KJ], sl[KJ];
+                for (int j = 0; j < KJ; ++j)
+                    kf[tt][j] = *reinterpret_cast<const bf16x8*>(Kb + kq_at<DK>(16 * tt + m, 32 * j + 8 * g));
 #pragma unroll
-            for (int j = 0; j < KJ; ++j) split44(sa[2 * j], sa[2 * j + 1], sh[j], sl[j]);
-            __builtin_amdgcn_sched_barrier(0);
-            f32x4 ks[2], qs[2];
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                ks[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                qs[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < KJ; ++j)
+                    qf[tt][j] = *reinterpret_cast<const bf16x8*>(Qb + kq_at<DK>(16 * tt + m, 32 * j + 8 * g));
+            f32x4 ks[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-                for (int j = 0; j < KJ; ++j) {
+            for (int j = 0; j < KJ; ++j)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
                     ks[tt] = mfma16(kf[tt][j], sh[j], ks[tt]);
-                    qs[tt] = mfma16(qf[tt][j], sh[j], qs[tt]);
                     ks[tt] = mfma16(kf[tt][j], sl[j], ks[tt]);
-                    qs[tt] = mfma16(qf[tt][j], sl[j], qs[tt]);
                 }
-            }
-
-            // ---- R = FR1 V - FR2 (K S_hat^T), V_new = T R ---------------
+            // operands of the rest of the chunk, read while the products run
             f32x4 fr1[2], fr2[2], fo[2], fv[2];
             s16x4 vv[2];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 fr1[tt] = *reinterpret_cast<const f32x4*>(G + FR1 + 16 * tt + 4 * g);
                 fr2[tt] = *reinterpret_cast<const f32x4*>(G + FR2 + 16 * tt + 4 * g);
-                fo[tt] = *reinterpret_cast<const f32x4*>(G + FO + 16 * tt + 4 * g);
-                fv[tt] = *reinterpret_cast<const f32x4*>(G + FV + 16 * tt + 4 * g);
                 // V[16 tt + 4 g + r][i], r = 0..3, by a transposed read
                 vv[tt] = lds_tr16(Vb + (16 * tt + 4 * g + (m >> 2)) * L::PV + 16 * a + 4 * (m & 3));
             }
-            const bool reset = __builtin_amdgcn_readfirstlane(__float_as_int(G[FRESET])) != 0;
-            const float smul = G[FMUL];
-            bf16x8 th[2], tl[2], ph[2], pl[2];
+            bf16x8 th[2], tl[2];
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                const int row = (16 * rt + m) * P36;
-                th[rt] = ld2x4(Th + row + 4 * g, Th + row + 16 + 4 * g);
-                tl[rt] = ld2x4(Tl + row + 4 * g, Tl + row + 16 + 4 * g);
-                ph[rt] = ld2x4(Ph + row + 4 * g, Ph + row + 16 + 4 * g);
-                pl[rt] = ld2x4(Pl + row + 4 * g, Pl + row + 16 + 4 * g);
+                const int at = (16 * rt + m) * P48 + 8 * g;
+                th[rt] = *reinterpret_cast<const bf16x8*>(Th + at);
+                tl[rt] = *reinterpret_cast<const bf16x8*>(Tl + at);
             }
+            __builtin_amdgcn_sched_barrier(0);
+
+            // ---- R = FR1 V - FR2 (K S_hat^T), beside Q S_hat^T -------------
+            f32x4 qs[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int j = 0; j < KJ; ++j)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    qs[tt] = mfma16(qf[tt][j], sh[j], qs[tt]);
+                    qs[tt] = mfma16(qf[tt][j], sl[j], qs[tt]);
+                }
             f32x4 rr[2];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
@@ -263,6 +295,14 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                                                fr1[tt][r] * bf2f((bf16_t)vv[tt][r]));
             bf16x8 rh, rl;
             split44(rr[0], rr[1], rh, rl);
+#pragma unroll
+            for (int u = 0; u < 4 * KJ; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+            }
+            __builtin_amdgcn_sched_barrier(0);
+
+            // ---- V_new = T R (state chain) ---------------------------------
             f32x4 vn[2];
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
@@ -270,21 +310,30 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                 vn[rt] = mfma16(th[rt], rl, vn[rt]);
                 vn[rt] = mfma16(tl[rt], rh, vn[rt]);
             }
-
-            // ---- o = FO (Q S_hat^T) + P V_new;  S_hat^T += K^T (FV V_new) --
-            bf16x8 nh, nl, mh, ml;
-            split44(vn[0], vn[1], nh, nl);
-            split44(vn[0] * fv[0], vn[1] * fv[1], mh, ml);
-            bf16x8 kt[NS];
+            bf16x8 ph[2], pl[2], kt[NS];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const int at = (16 * rt + m) * P48 + 8 * g;
+                ph[rt] = *reinterpret_cast<const bf16x8*>(Ph + at);
+                pl[rt] = *reinterpret_cast<const bf16x8*>(Pl + at);
+                fo[rt] = *reinterpret_cast<const f32x4*>(G + FO + 16 * rt + 4 * g);
+                fv[rt] = *reinterpret_cast<const f32x4*>(G + FV + 16 * rt + 4 * g);
+            }
 #pragma unroll
             for (int t = 0; t < NS; ++t) {
                 // K[kappa(g, e)][16 t + m] by two transposed reads
-                const int col = 16 * t + 4 * (m & 3);
-                const s16x4 x0 = lds_tr16(Kb + swz<DK>(4 * g + (m >> 2), col));
-                const s16x4 x1 = lds_tr16(Kb + swz<DK>(16 + 4 * g + (m >> 2), col));
+                const bf16_t* kn = Kb + CH * DK + (4 * g + (m >> 2)) * L::PKN + 16 * t + 4 * (m & 3);
+                const s16x4 x0 = lds_tr16(kn);
+                const s16x4 x1 = lds_tr16(kn + 16 * L::PKN);
                 const s16x4 x2[2] = {x0, x1};
                 kt[t] = __builtin_bit_cast(bf16x8, x2);
             }
+            __builtin_amdgcn_sched_barrier(0);
+
+            // ---- update operands first, then o = FO (Q S_hat^T) + P V_new --
+            bf16x8 nh, nl, mh, ml;
+            split44(vn[0] * fv[0], vn[1] * fv[1], mh, ml);
+            split44(vn[0], vn[1], nh, nl);
             f32x4 o[2];
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
@@ -293,32 +342,51 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                 o[rt] = mfma16(ph[rt], nl, o[rt]);
                 o[rt] = mfma16(pl[rt], nh, o[rt]);
             }
-            if (reset) {
+            __builtin_amdgcn_sched_barrier(0);
+
+            if (__builtin_amdgcn_readfirstlane(__float_as_int(G[FRESET])) != 0) {
+                // sigma restarts at 1: S_hat takes the chunk decay now
+                const float smul = G[FMUL];
 #pragma unroll
                 for (int t = 0; t < NS; ++t) sa[t] *= smul;
             }
+
+            // ---- S_hat^T += K^T (FV V_new), next chunk's split beside it ---
 #pragma unroll
             for (int t = 0; t < NS; ++t) {
                 sa[t] = mfma16(kt[t], mh, sa[t]);
                 sa[t] = mfma16(kt[t], ml, sa[t]);
             }
-            const int64_t t0 = c * CH;
-            TOut* oc = obase + (t0 + 4 * g) * ostride;
-            if (T - t0 >= CH) {
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) split44(sa[2 * j], sa[2 * j + 1], sh[j], sl[j]);
+            {
+                const int64_t t0 = c * CH;
+                const int n = (int)min((int64_t)CH, T - t0);
+                const __amdgpu_buffer_rsrc_t ores = __builtin_amdgcn_make_buffer_rsrc(
+                    obase + t0 * H * DV, (short)0, n * (int)(H * DV * sizeof(TOut)), 0x00020000);
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        io<TOut>::st(oc + (16 * rt + r) * ostride, o[rt][r]);
-            } else {
-                const int n = (int)(T - t0);
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (16 * rt + 4 * g + r < n)
-                            io<TOut>::st(oc + (16 * rt + r) * ostride, o[rt][r]);
+                    for (int r = 0; r < 4; ++r) {
+                        if constexpr (sizeof(TOut) == 4)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[rt][r]), ores,
+                                                                  (int)ooff[rt][r], 0, 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b16(f2bf(o[rt][r]), ores,
+                                                                  (int)ooff[rt][r], 0, 0);
+                    }
             }
+            // products of tile pairs 0, 1 first, then each pair's split
+            // beside the next pair's products, the stores before the last
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+#pragma unroll
+            for (int j = 0; j + 2 < KJ; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+            __builtin_amdgcn_sched_group_barrier(0x040, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
             lds_barrier();
         }
         if (p.s_final) {
@@ -333,86 +401,97 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
 
     // ============================== team B =================================
     const int bw = wave - NA;
-    // Global loads of chunk cn: lane (g, m) holds rows 16 tt + m, elements
-    // 32 j + 8 g .. + 7 of K (or Q) -- the natural operand layout of the
-    // 16x16x32 product; lanes 0..31 hold the gates of token `lane`.  Rows
+    // Team B shares each SIMD with a team A wave; ahead of team A's
+    // instructions it finishes its short dependent chains within the period.
+    __builtin_amdgcn_s_setprio(2);
+    // Global loads: a uniform chunk base plus a 32-bit lane offset.  Rows
     // past the end of the sequence repeat its last token: they only ever
     // meet beta = 0 (rows of A, R and V_new) or are not stored (o).
+    auto last_row = [&](int64_t cn) { return (int)min((int64_t)CH - 1, T - 1 - cn * CH); };
+    // lane (g, m) gets rows 16 tt + m, elements 32 j + 8 g .. + 7 -- the
+    // natural operand layout of the 16x16x32 product
     auto load_k = [&](int64_t cn, u32x4 (&kr)[2][KJ], const bf16_t* base) {
-        const int64_t t0 = cn * CH;
+        const int last = last_row(cn);
+        const char* cb = reinterpret_cast<const char*>(base + cn * CH * tstride);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const int64_t tok = min(t0 + 16 * tt + m, T - 1);
+            const uint32_t off = (uint32_t)(min(16 * tt + m, last) * (int)tstride + 8 * g) * 2u;
 #pragma unroll
             for (int j = 0; j < KJ; ++j)
-                kr[tt][j] = *reinterpret_cast<const u32x4*>(base + tok * tstride + 32 * j + 8 * g);
+                kr[tt][j] = *reinterpret_cast<const u32x4*>(cb + off + 64 * j);
         }
     };
-    // alpha and beta of token `lane` (clamped into the sequence; masked at
-    // use by gate_live, so that no wait follows the load)
-    auto load_gate = [&](int64_t cn, float& al, float& be) {
-        const int64_t tok = min(cn * CH + (lane & 31), T - 1);
-        al = abase[tok * H];
-        be = bbase[tok * H];
+    // stores rows 16 tt + m, elements 32 j + 8 g .. + 7 into a K or Q tile
+    auto stage_kq = [&](bf16_t* dst, const u32x4 (&kr)[2][KJ]) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) {
+                const int row = 16 * tt + m;
+                st8(dst + kq_at<DK>(row, kperm(32 * j + 8 * g)), uint2{kr[tt][j][0], kr[tt][j][1]});
+                st8(dst + kq_at<DK>(row, kperm(32 * j + 8 * g + 4)), uint2{kr[tt][j][2], kr[tt][j][3]});
+            }
     };
-    // alpha = 1, beta = 0 past the end of the sequence (and on lanes 32..63)
-    auto gate_live = [&](int64_t cn) { return lane < CH && cn * CH + lane < T; };
-    // g of token `lane` (lanes < 32) for chunk cn
-    auto gate_scan = [&](int64_t cn, float al) {
-        return wave_scan(gate_live(cn) ? safe_log(al) : 0.f);
+    // g and beta of the chunk's tokens from the gate ring: gq, bq for tokens
+    // 16 rt + m; gk for tokens 16 st + 4 g .. + 3
+    struct Gates {
+        float gq[2], bq[2];
+        f32x4 gk[2];
+    };
+    auto read_gates = [&](const float* gr) {
+        Gates z;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            z.gq[u] = gr[16 * u + m];
+            z.bq[u] = gr[CH + 16 * u + m];
+            z.gk[u] = *reinterpret_cast<const f32x4*>(gr + 16 * u + 4 * g);
+        }
+        return z;
     };
 
     // A role prepares chunk x in period x - lead (periods run from -2 to
-    // nch - 1, each closed by the workgroup barrier).  Buffers f0, f1 carry
-    // chunks x and x + 1; the load of chunk x + 2 is issued at the start of
-    // the period that prepares x + 1.  Loads are unconditional (an index
-    // past the end repeats the last chunk) so that the wait before each
-    // prepare covers just its buffer.
-    auto run = [&](int lead, auto&& load, auto&& prepare, auto& f0, auto& f1) {
+    // nch - 1, each closed by the workgroup barrier).  Loading roles keep two
+    // chunks in flight in three register buffers (chunk x in buffer x mod 3);
+    // loads are unconditional (an index past the end repeats the last chunk)
+    // so that the wait before each prepare covers just its buffer.
+    auto run = [&](int lead, auto&& load, auto&& prepare, auto& fa, auto& fb, auto& fc) {
         for (int e = 0; e < 2 - lead; ++e) lds_barrier();
-        load(0, f0);
-        load(min((int64_t)1, nch - 1), f1);
-        int64_t x = 0;
-        for (; x + 1 < nch; x += 2) {
-            prepare(x, f0);
+        load(0, fa);
+        load(min((int64_t)1, nch - 1), fb);
+        for (int64_t x = 0; x < nch; x += 3) {
+            load(min(x + 2, nch - 1), fc);
+            prepare(x, fa);
             lds_barrier();
-            load(min(x + 2, nch - 1), f0);
-            prepare(x + 1, f1);
-            lds_barrier();
-            load(min(x + 3, nch - 1), f1);
+            load(min(x + 3, nch - 1), fa);
+            if (x + 1 < nch) {
+                prepare(x + 1, fb);
+                lds_barrier();
+            }
+            load(min(x + 4, nch - 1), fb);
+            if (x + 2 < nch) {
+                prepare(x + 2, fc);
+                lds_barrier();
+            }
         }
-        if (x < nch) {
-            prepare(x, f0);
+        for (int e = 0; e < lead; ++e) lds_barrier();
+    };
+    auto run_noload = [&](int lead, auto&& prepare) {
+        for (int e = 0; e < 2 - lead; ++e) lds_barrier();
+        for (int64_t x = 0; x < nch; ++x) {
+            prepare(x);
             lds_barrier();
         }
         for (int e = 0; e < lead; ++e) lds_barrier();
     };
 
     if (bw == 0) {
-        // --------------------- B0: K staging, factors ----------------------
-        struct Buf {
-            u32x4 k[2][KJ];
-            float al, be;
-        };
+        // ------------------------ B0: per-token factors ----------------------
         float sigma = 1.f;   // sigma at the start of the chunk being prepared
-        auto load = [&](int64_t cn, Buf& f) {
-            load_k(cn, f.k, kbase);
-            load_gate(cn, f.al, f.be);
-        };
-        auto prepare = [&](int64_t cn, const Buf& f) {
-            bf16_t* Kb = reinterpret_cast<bf16_t*>(setp(cn, L::K));
+        auto prepare = [&](int64_t cn) {
+            const float* gr = gring(cn);
             float* G = reinterpret_cast<float*>(setp(cn, L::G));
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int j = 0; j < KJ; ++j) {
-                    const int row = 16 * tt + m;
-                    st8(Kb + swz<DK>(row, 32 * j + 8 * g), uint2{f.k[tt][j][0], f.k[tt][j][1]});
-                    st8(Kb + swz<DK>(row, 32 * j + 8 * g + 4), uint2{f.k[tt][j][2], f.k[tt][j][3]});
-                }
-            const float gx = gate_scan(cn, f.al);
-            const float gC = __shfl(gx, CH - 1, 64);
-            const float be = gate_live(cn) ? f.be : 0.f;
+            const float gx = gr[lane & 31], be = gr[CH + (lane & 31)];
+            const float gC = gr[CH - 1];
             // sigma' = sigma gamma_C; a reset keeps S_hat = S from here on.
             // The last chunk always resets so that the final S_hat is S.
             const float s1 = sigma * __expf(gC);
@@ -431,14 +510,11 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
             }
             sigma = reset ? 1.f : s1;
         };
-        Buf f0, f1;
-        run(1, load, prepare, f0, f1);
+        run_noload(1, prepare);
     } else if (bw == 1) {
         // ----------------------- B1: T = (I + A)^{-1} -----------------------
         float* Tf = reinterpret_cast<float*>(smem + L::TF);
-        struct Buf {};
-        auto load = [&](int64_t, Buf&) {};
-        auto prepare = [&](int64_t cn, const Buf&) {
+        auto prepare = [&](int64_t cn) {
             const float* Af = afp(cn);
             bf16_t* Th = reinterpret_cast<bf16_t*>(setp(cn, L::TH));
             bf16_t* Tl = reinterpret_cast<bf16_t*>(setp(cn, L::TL));
@@ -448,6 +524,15 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
             {
                 const int blk = lane >> 5, rr = (lane >> 1) & 15, half = lane & 1;
                 const float* Lb = Af + 16 * blk * P36 + 16 * blk;
+                // all of L's strictly lower part (row cp, columns < cp) in
+                // registers first, so the 16 dependent steps wait on nothing
+                f32x4 lrow[16][4];
+#pragma unroll
+                for (int cp = 1; cp < 16; ++cp)
+#pragma unroll
+                    for (int q4 = 0; q4 < (cp + 3) / 4; ++q4)
+                        lrow[cp][q4] = *reinterpret_cast<const f32x4*>(Lb + cp * P36 + 4 * q4);
+                __builtin_amdgcn_sched_barrier(0);
                 float acc2[16], x[16];
 #pragma unroll
                 for (int cc = 0; cc < 16; ++cc) acc2[cc] = 0.f;
@@ -455,12 +540,10 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                 for (int cp = 15; cp >= 0; --cp) {
                     x[cp] = (rr == cp ? 1.f : 0.f) - acc2[cp];
 #pragma unroll
-                    for (int q4 = 0; q4 < (cp + 3) / 4; ++q4) {
-                        const f32x4 lr = *reinterpret_cast<const f32x4*>(Lb + cp * P36 + 4 * q4);
+                    for (int q4 = 0; q4 < (cp + 3) / 4; ++q4)
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            if (4 * q4 + e < cp) acc2[4 * q4 + e] += x[cp] * lr[e];
-                    }
+                            if (4 * q4 + e < cp) acc2[4 * q4 + e] += x[cp] * lrow[cp][q4][e];
                 }
                 // columns 8 half .. 8 half + 7 of row 16 blk + rr (bitwise
                 // select: a conditional here becomes an indexed private array)
@@ -477,116 +560,127 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                 bf16x8 xh, xl;
                 split8(f32x8{xs[0], xs[1], xs[2], xs[3], xs[4], xs[5], xs[6], xs[7]}, xh, xl);
                 const u32x4 uh = __builtin_bit_cast(u32x4, xh), ul = __builtin_bit_cast(u32x4, xl);
-                st8(Th + row * P36 + col, uint2{uh[0], uh[1]});
-                st8(Th + row * P36 + col + 4, uint2{uh[2], uh[3]});
-                st8(Tl + row * P36 + col, uint2{ul[0], ul[1]});
-                st8(Tl + row * P36 + col + 4, uint2{ul[2], ul[3]});
+                st8(Th + row * P48 + kperm(col), uint2{uh[0], uh[1]});
+                st8(Th + row * P48 + kperm(col + 4), uint2{uh[2], uh[3]});
+                st8(Tl + row * P48 + kperm(col), uint2{ul[0], ul[1]});
+                st8(Tl + row * P48 + kperm(col + 4), uint2{ul[2], ul[3]});
             }
             wave_lds_sync();
             // T_10 = -T_11 A_10 T_00 on fp32 16x16x4 matrix cores:
             // Y = A_10 T_00 (C layout Y[4 g + r][m]), then -T_10^T = Y^T T_11^T
             // with the contraction order 4 g + kk so that Y's registers are
             // its A operand as they stand.
+            float ya[4], yb[4], tb[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                ya[kk] = Af[(16 + m) * P36 + 4 * kk + g];
+                yb[kk] = Tf[(4 * kk + g) * P36 + m];
+                tb[kk] = Tf[(16 + m) * P36 + 16 + 4 * g + kk];
+            }
+            __builtin_amdgcn_sched_barrier(0);
             f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                y = mfma_f32(Af[(16 + m) * P36 + 4 * kk + g], Tf[(4 * kk + g) * P36 + m], y);
+            for (int kk = 0; kk < 4; ++kk) y = mfma_f32(ya[kk], yb[kk], y);
             f32x4 t10 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                t10 = mfma_f32(y[kk], Tf[(16 + m) * P36 + 16 + 4 * g + kk], t10);
+            for (int kk = 0; kk < 4; ++kk) t10 = mfma_f32(y[kk], tb[kk], t10);
             uint2 vh, vl;
             split2(-t10[0], -t10[1], vh.x, vl.x);
             split2(-t10[2], -t10[3], vh.y, vl.y);
-            st8(Th + (16 + m) * P36 + 4 * g, vh);
-            st8(Tl + (16 + m) * P36 + 4 * g, vl);
+            st8(Th + (16 + m) * P48 + kperm(4 * g), vh);
+            st8(Tl + (16 + m) * P48 + kperm(4 * g), vl);
         };
-        Buf f0, f1;
-        run(1, load, prepare, f0, f1);
+        run_noload(1, prepare);
     } else if (bw == 2) {
         // ---------------------- B2: Q and V staging, P ----------------------
         struct Buf {
-            u32x4 k[2][KJ];
             u32x4 q[2][KJ];
             u32x4 v[VL];
-            float al, be;
         };
         auto load = [&](int64_t cn, Buf& f) {
-            load_k(cn, f.k, kbase);
             load_k(cn, f.q, qbase);
-            const int64_t t0 = cn * CH;
+            const int last = last_row(cn);
+            const char* cb = reinterpret_cast<const char*>(vbase + cn * CH * H * DV);
 #pragma unroll
             for (int u = 0; u < VL; ++u) {
                 const int pc = lane + 64 * u;
-                const int64_t tok = min(t0 + pc / VC, T - 1);
-                f.v[u] = *reinterpret_cast<const u32x4*>(vbase + tok * H * DV + 8 * (pc % VC));
+                const uint32_t off = (uint32_t)(min(pc / VC, last) * (int)(H * DV) + 8 * (pc % VC)) * 2u;
+                f.v[u] = *reinterpret_cast<const u32x4*>(cb + off);
             }
-            load_gate(cn, f.al, f.be);
         };
         auto prepare = [&](int64_t cn, const Buf& f) {
             bf16_t* Qb = reinterpret_cast<bf16_t*>(setp(cn, L::Q));
             bf16_t* Vb = reinterpret_cast<bf16_t*>(setp(cn, L::V));
             bf16_t* Ph = reinterpret_cast<bf16_t*>(setp(cn, L::PH));
             bf16_t* Pl = reinterpret_cast<bf16_t*>(setp(cn, L::PL));
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int j = 0; j < KJ; ++j) {
-                    const int row = 16 * tt + m;
-                    st8(Qb + swz<DK>(row, 32 * j + 8 * g), uint2{f.q[tt][j][0], f.q[tt][j][1]});
-                    st8(Qb + swz<DK>(row, 32 * j + 8 * g + 4), uint2{f.q[tt][j][2], f.q[tt][j][3]});
-                }
+            const bf16_t* Kb = kring(cn);
+            stage_kq(Qb, f.q);
 #pragma unroll
             for (int u = 0; u < VL; ++u) {
                 const int pc = lane + 64 * u;
                 *reinterpret_cast<u32x4*>(Vb + (pc / VC) * L::PV + 8 * (pc % VC)) = f.v[u];
             }
+            wave_lds_sync();   // this wave's Q tile, read back in operand order
             // C[4 g + r][m] = k_{16 st + 4 g + r} . q_{16 rt + m}
+            bf16x8 kf[2][KJ], qf[2][KJ];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int j = 0; j < KJ; ++j) {
+                    const int row = 16 * tt + m;
+                    kf[tt][j] = *reinterpret_cast<const bf16x8*>(Kb + kq_at<DK>(row, 32 * j + 8 * g));
+                    qf[tt][j] = *reinterpret_cast<const bf16x8*>(Qb + kq_at<DK>(row, 32 * j + 8 * g));
+                }
+            const Gates z = read_gates(gring(cn));
             f32x4 acc[3] = {};
 #pragma unroll
             for (int j = 0; j < KJ; ++j) {
-                const bf16x8 k0 = __builtin_bit_cast(bf16x8, f.k[0][j]);
-                const bf16x8 k1 = __builtin_bit_cast(bf16x8, f.k[1][j]);
-                const bf16x8 q0 = __builtin_bit_cast(bf16x8, f.q[0][j]);
-                const bf16x8 q1 = __builtin_bit_cast(bf16x8, f.q[1][j]);
-                acc[0] = mfma16(k0, q0, acc[0]);
-                acc[1] = mfma16(k0, q1, acc[1]);
-                acc[2] = mfma16(k1, q1, acc[2]);
+                acc[0] = mfma16(kf[0][j], qf[0][j], acc[0]);
+                acc[1] = mfma16(kf[0][j], qf[1][j], acc[1]);
+                acc[2] = mfma16(kf[1][j], qf[1][j], acc[2]);
             }
-            const float gx = gate_scan(cn, f.al);
 #pragma unroll
             for (int u = 0; u < 3; ++u) {
                 const int st = u == 2 ? 1 : 0, rt = u == 0 ? 0 : 1;
                 const int rp = 16 * rt + m;
-                const float gr = __shfl(gx, rp, 64);
                 float pv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int s = 16 * st + 4 * g + r;
-                    const float gs = __shfl(gx, s, 64);
-                    pv[r] = s <= rp ? __expf(fminf(gr - gs, 0.f)) * acc[u][r] : 0.f;
+                    pv[r] = s <= rp ? __expf(fminf(z.gq[rt] - z.gk[st][r], 0.f)) * acc[u][r] : 0.f;
                 }
                 uint2 vh, vl;
                 split2(pv[0], pv[1], vh.x, vl.x);
                 split2(pv[2], pv[3], vh.y, vl.y);
-                st8(Ph + rp * P36 + 16 * st + 4 * g, vh);
-                st8(Pl + rp * P36 + 16 * st + 4 * g, vl);
+                st8(Ph + rp * P48 + kperm(16 * st + 4 * g), vh);
+                st8(Pl + rp * P48 + kperm(16 * st + 4 * g), vl);
             }
         };
-        Buf f0, f1;
-        run(1, load, prepare, f0, f1);
+        Buf fa, fb, fc;
+        run(1, load, prepare, fa, fb, fc);
     } else {
-        // ------------------------------ B3: A -------------------------------
+        // --------------------- B3: K staging, gate scan, A -------------------
         struct Buf {
             u32x4 k[2][KJ];
-            float al, be;
+            float al, be;   // alpha, beta of token `lane` (lanes < 32)
         };
         auto load = [&](int64_t cn, Buf& f) {
             load_k(cn, f.k, kbase);
-            load_gate(cn, f.al, f.be);
+            const uint32_t off = (uint32_t)(min(lane & 31, last_row(cn)) * (int)H);
+            f.al = (abase + cn * CH * H)[off];
+            f.be = (bbase + cn * CH * H)[off];
         };
         auto prepare = [&](int64_t cn, const Buf& f) {
             float* Af = afp(cn);
+            float* gr = gring(cn);
+            bf16_t* Kr = kring(cn);
+            stage_kq(Kr, f.k);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int j = 0; j < KJ; ++j)
+                    *reinterpret_cast<u32x4*>(Kr + CH * DK + (16 * tt + m) * L::PKN + 32 * j + 8 * g) =
+                        f.k[tt][j];
             // Gram tiles (s-tile, r-tile) = (0,0), (0,1), (1,1):
             // C[4 g + r][m] = k_{16 st + 4 g + r} . k_{16 rt + m}
             f32x4 acc[3] = {};
@@ -598,25 +692,32 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                 acc[1] = mfma16(k0, k1, acc[1]);
                 acc[2] = mfma16(k1, k1, acc[2]);
             }
-            const float gx = gate_scan(cn, f.al);
-            const float be = gate_live(cn) ? f.be : 0.f;
+            // alpha = 1, beta = 0 past the end of the sequence (and on lanes
+            // 32..63); g = within-chunk cumulative log decay
+            const bool live = lane < CH && cn * CH + lane < T;
+            const float gx = wave_scan(live ? safe_log(f.al) : 0.f);
+            if (lane < CH) {
+                gr[lane] = gx;
+                gr[CH + lane] = live ? f.be : 0.f;
+            }
+            wave_lds_sync();
+            const Gates z = read_gates(gr);
 #pragma unroll
             for (int u = 0; u < 3; ++u) {
                 const int st = u == 2 ? 1 : 0, rt = u == 0 ? 0 : 1;
                 const int rp = 16 * rt + m;
-                const float gr = __shfl(gx, rp, 64), br = __shfl(be, rp, 64);
                 f32x4 av;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int s = 16 * st + 4 * g + r;
-                    const float gs = __shfl(gx, s, 64);
-                    av[r] = s < rp ? br * __expf(fminf(gr - gs, 0.f)) * acc[u][r] : 0.f;
+                    av[r] = s < rp ? z.bq[rt] * __expf(fminf(z.gq[rt] - z.gk[st][r], 0.f)) * acc[u][r]
+                                   : 0.f;
                 }
                 *reinterpret_cast<f32x4*>(Af + rp * P36 + 16 * st + 4 * g) = av;
             }
         };
-        Buf f0, f1;
-        run(2, load, prepare, f0, f1);
+        Buf fa, fb, fc;
+        run(2, load, prepare, fa, fb, fc);
     }
 }
 
