@@ -43,10 +43,21 @@ __device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// hi/lo split of two values: hi = bf16(x), lo = bf16(x - hi).
+// hi/lo split of two values: hi = bf16(x), lo = bf16(x - hi).  The
+// residuals x - hi come from v_dot2c_f32_bf16 on the packed hi pair,
+// dot((hi_a, hi_b), (-1, 0)) + a (and (0, -1) for b): -hi is exact and the
+// sum is x - hi, itself exact in fp32, so this matches the plain
+// subtraction bit for bit while skipping the unpacking of hi.  The two
+// constants live in SGPRs: as inline operands they are mis-encoded.
 __device__ __forceinline__ void split2(float a, float b, uint32_t& h, uint32_t& l) {
     h = cvt_pk(a, b);
-    l = cvt_pk(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
+    uint32_t ka, kb;
+    asm("s_mov_b32 %0, 0xbf80" : "=s"(ka));       // (-1, 0) as packed bf16
+    asm("s_mov_b32 %0, 0xbf800000" : "=s"(kb));   // (0, -1)
+    const bf16x2_t hp = __builtin_bit_cast(bf16x2_t, h);
+    const float ra = __builtin_amdgcn_fdot2_f32_bf16(hp, __builtin_bit_cast(bf16x2_t, ka), a, false);
+    const float rb = __builtin_amdgcn_fdot2_f32_bf16(hp, __builtin_bit_cast(bf16x2_t, kb), b, false);
+    l = cvt_pk(ra, rb);
 }
 
 __device__ __forceinline__ void split_bf16(float x, bf16_t& h, bf16_t& l) {
