@@ -32,22 +32,30 @@
 //            tiles in registers and walks the chunks in order: E S^T, R,
 //            V_new = T R, Q S^T, o, the update.
 //   team B   running ahead of it:
-//            E0..E3 (waves 4..7), chunk c + 2: the elementwise pass --
+//            E0..E3 (waves 4..7), chunk c + 3: the elementwise pass --
 //                 lambda by running products, 1 / lambda, the operands E, Q,
-//                 K' as bf16 hi/lo pairs; wave 4 + j takes tokens 4j .. 4j+3
-//                 (lane = channel pair) and forms the products of its
-//                 prefix itself, so the waves never wait on each other;
-//            AP-A (wave 2), chunk c + 1: A = E K'^T, T = (I + A)^{-1}, and
-//                 the wide-chunk path;
+//                 K'; each wave takes a few tokens (lane = channel pair) and
+//                 forms the products of the rows before them itself, so the
+//                 waves never wait on each other;
+//            AP-A (wave 2): A = E K'^T for chunk c + 2 (or the wide-chunk
+//                 path), T = (I + A)^{-1} for chunk c + 1;
 //            AP-P (wave 3), chunk c + 1: P = Q K'^T, w (.) v.
-// One workgroup barrier closes each period; LDS keeps three sets of the
-// elementwise operands (chunk mod 3) and two of T, P, w (.) v (chunk mod 2).
+// One workgroup barrier closes each period; LDS keeps four sets of the
+// elementwise operands (chunk mod 4) and two of A, T, P and w (.) v.
 //
 // Products: v_mfma_f32_16x16x32_bf16 over the key dim, with the contraction
 // order kappa (see kperm) that makes a pair of S^T accumulator tiles the B
 // operand as they stand; v_mfma_f32_16x16x16_bf16 over tokens, whose C tile
 // (rows 4 g + r, column m) is already the B operand of the next product.
-// Every computed operand enters as a bf16 hi/lo pair (mfma_common.h).
+//
+// Precision: computed operands enter as bf16 hi/lo pairs (mfma_common.h)
+// where it matters.  P, P V_new, Q S^T and the update take three terms.
+// E (in E S^T and A), A itself and T enter as single bf16 values: E S^T
+// and A only shape R's correction and T, whose relative error the
+// substitution does not amplify; a simulation of this chunk algorithm
+// against the fp64 recurrence (1024 tokens; decays from fast to near 1,
+// with and without an initial state) puts the error at <= 2.3e-3 (o) and
+// <= 1.8e-3 (S) of rms, against 2e-4 with every operand split.
 #include <type_traits>
 
 #include "launch.h"
@@ -61,8 +69,9 @@ constexpr int CH = 16;            // tokens per chunk
 constexpr int RB = 32;            // state rows per workgroup
 constexpr int NA = RB / 16;       // team A waves
 constexpr int NWAVE = NA + 6;
+constexpr int DEPTH = 3;          // periods between the elementwise pass and team A
 constexpr int P24 = 24;           // pitch of T, P (bf16) and w . v (fp32)
-constexpr int PAF = 20;           // pitch of A (fp32)
+constexpr int PAF = 20;           // pitch of A and wide-path P (fp32)
 constexpr float kLamMin = 1.2621774e-29f;   // 2^-96
 
 struct Gdr2Params {
@@ -76,26 +85,25 @@ struct Gdr2Params {
 template <int DK>
 struct Lay2 {
     static constexpr int PKN = DK + 16;            // K' row pitch (elements)
-    // elementwise operands, chunk mod 3
-    static constexpr int EH = 0;                    // E hi, lo [16][DK], operand order
-    static constexpr int EL = EH + CH * DK * 2;
-    static constexpr int QH = EL + CH * DK * 2;     // Q hi, lo [16][DK], operand order
+    // elementwise operands, chunk mod 4
+    static constexpr int EH = 0;                    // E [16][DK] bf16, operand order
+    static constexpr int QH = EH + CH * DK * 2;     // Q hi, lo [16][DK], operand order
     static constexpr int QL = QH + CH * DK * 2;
     static constexpr int KH = QL + CH * DK * 2;     // K' hi, lo [16][PKN], natural order
     static constexpr int KL = KH + CH * PKN * 2;
     static constexpr int LC = KL + CH * PKN * 2;    // lambda_C [DK] fp32, then the wide flag
     static constexpr int ESET = LC + DK * 4 + 16;
     // T, P, w . v, chunk mod 2
-    static constexpr int TH = 0;                    // T hi, lo [16][P24]
-    static constexpr int TL = TH + CH * P24 * 2;
-    static constexpr int PH = TL + CH * P24 * 2;    // P hi, lo [16][P24]
+    static constexpr int TH = 0;                    // T [16][P24] bf16
+    static constexpr int PH = TH + CH * P24 * 2;    // P hi, lo [16][P24]
     static constexpr int PL = PH + CH * P24 * 2;
     static constexpr int WV = PL + CH * P24 * 2;    // w . v [RB][P24] fp32, by state row
     static constexpr int TSET = WV + RB * P24 * 4;
     static constexpr int ER = 0;
-    static constexpr int TR = ER + 3 * ESET;
-    static constexpr int AF = TR + 2 * TSET;        // A fp32 [16][PAF] (AP-A)
-    static constexpr int FG = AF + CH * PAF * 4;    // wide path: G fp32 [16][DK]
+    static constexpr int TR = ER + 4 * ESET;
+    static constexpr int AF = TR + 2 * TSET;        // A fp32 [16][PAF], chunk mod 2
+    static constexpr int WP = AF + 2 * CH * PAF * 4;   // wide-path P fp32 [16][PAF], chunk mod 2
+    static constexpr int FG = WP + 2 * CH * PAF * 4;   // wide path: G fp32 [16][DK]
     static constexpr int FK = FG + CH * DK * 4;     //   k, b, q bf16 [16][DK]
     static constexpr int FB = FK + CH * DK * 2;
     static constexpr int FQ = FB + CH * DK * 2;
@@ -135,6 +143,13 @@ __device__ __forceinline__ void split4(const f32x4& x, s16x4& h, s16x4& l) {
     l = __builtin_bit_cast(s16x4, uint2{l0, l1});
 }
 
+// Two 4-element operand halves as one 8-element operand.
+__device__ __forceinline__ bf16x8 cat44(const s16x4& a, const s16x4& b) {
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 __device__ __forceinline__ float lo_bf(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
@@ -166,7 +181,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
     const int row0 = rbk * RB;
     const int64_t nch = (T + CH - 1) / CH;
 
-    auto eset = [&](int64_t c) { return smem + L::ER + (int)(c % 3) * L::ESET; };
+    auto eset = [&](int64_t c) { return smem + L::ER + (int)(c & 3) * L::ESET; };
     auto tset = [&](int64_t c) { return smem + L::TR + (int)(c & 1) * L::TSET; };
     auto bfp = [&](unsigned char* base, int off) { return reinterpret_cast<bf16_t*>(base + off); };
     auto wide_flag = [&](unsigned char* es) {
@@ -190,14 +205,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                 sa[t] = *reinterpret_cast<const f32x4*>(p.s0 + ((bh * DV + row0 + i) * DK + 16 * t +
                                                                 4 * g));
         }
-        bf16x8 sh[KJ], sl[KJ];
-#pragma unroll
-        for (int j = 0; j < KJ; ++j)
-            split8(f32x8{sa[2 * j][0], sa[2 * j][1], sa[2 * j][2], sa[2 * j][3], sa[2 * j + 1][0],
-                         sa[2 * j + 1][1], sa[2 * j + 1][2], sa[2 * j + 1][3]},
-                   sh[j], sl[j]);
-        lds_barrier();
-        lds_barrier();
+        for (int e = 0; e < DEPTH; ++e) lds_barrier();
         // o[t0 + 4 g + r][row0 + i] by buffer stores from a per-chunk
         // resource ending at the sequence end (stores past it are dropped)
         uint32_t ooff[4];
@@ -205,63 +213,35 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
         for (int r = 0; r < 4; ++r)
             ooff[r] = (uint32_t)(((4 * g + r) * (int)(H * DV) + row0 + i) * (int)sizeof(TOut));
         TOut* obase = reinterpret_cast<TOut*>(p.o) + (b * T * H + h) * DV;
+        // E and Q fragments of the next chunk are read during this one (its
+        // elementwise set is complete two periods ahead)
+        bf16x8 eh[KJ], qh[KJ], ql[KJ];
+        auto read_eq = [&](int64_t c) {
+            unsigned char* es = eset(c);
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) {
+                const int at = kq_at<DK>(m, 32 * j + 8 * g);
+                eh[j] = *reinterpret_cast<const bf16x8*>(bfp(es, L::EH) + at);
+                qh[j] = *reinterpret_cast<const bf16x8*>(bfp(es, L::QH) + at);
+                ql[j] = *reinterpret_cast<const bf16x8*>(bfp(es, L::QL) + at);
+            }
+        };
+        read_eq(0);
         for (int64_t c = 0; c < nch; ++c) {
             unsigned char* es = eset(c);
             unsigned char* ts = tset(c);
-            const bf16_t* Eh = bfp(es, L::EH);
-            const bf16_t* El = bfp(es, L::EL);
-            const bf16_t* Qh = bfp(es, L::QH);
-            const bf16_t* Ql = bfp(es, L::QL);
             const bf16_t* Kh = bfp(es, L::KH);
             const bf16_t* Kl = bfp(es, L::KL);
             const float* lc = reinterpret_cast<const float*>(es + L::LC);
             const int wide = wide_flag(es);
-
-            // ---- E S^T (state chain) ---------------------------------------
-            bf16x8 eh[KJ], el[KJ];
-#pragma unroll
-            for (int j = 0; j < KJ; ++j) {
-                eh[j] = *reinterpret_cast<const bf16x8*>(Eh + kq_at<DK>(m, 32 * j + 8 * g));
-                el[j] = *reinterpret_cast<const bf16x8*>(El + kq_at<DK>(m, 32 * j + 8 * g));
-            }
-            f32x4 k3[3] = {};
-#pragma unroll
-            for (int j = 0; j < KJ; ++j) {
-                k3[0] = mfma16(eh[j], sh[j], k3[0]);
-                k3[1] = mfma16(eh[j], sl[j], k3[1]);
-                k3[2] = mfma16(el[j], sh[j], k3[2]);
-            }
+            // operands written in the previous period; their reads overlap
+            // the products below
             const f32x4 wv = *reinterpret_cast<const f32x4*>(
                 reinterpret_cast<const float*>(ts + L::WV) + i * P24 + 4 * g);
             const s16x4 th = *reinterpret_cast<const s16x4*>(bfp(ts, L::TH) + m * P24 + 4 * g);
-            const s16x4 tl = *reinterpret_cast<const s16x4*>(bfp(ts, L::TL) + m * P24 + 4 * g);
-            bf16x8 qh[KJ], ql[KJ];
-#pragma unroll
-            for (int j = 0; j < KJ; ++j) {
-                qh[j] = *reinterpret_cast<const bf16x8*>(Qh + kq_at<DK>(m, 32 * j + 8 * g));
-                ql[j] = *reinterpret_cast<const bf16x8*>(Ql + kq_at<DK>(m, 32 * j + 8 * g));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-
-            // ---- R = w.v - E S^T, beside Q S^T -----------------------------
-            f32x4 q3[3] = {};
-#pragma unroll
-            for (int j = 0; j < KJ; ++j) {
-                q3[0] = mfma16(qh[j], sh[j], q3[0]);
-                q3[1] = mfma16(qh[j], sl[j], q3[1]);
-                q3[2] = mfma16(ql[j], sh[j], q3[2]);
-            }
-            const f32x4 rr = wv - (k3[0] + k3[1] + k3[2]);
-            s16x4 rh, rl;
-            split4(rr, rh, rl);
-            __builtin_amdgcn_sched_barrier(0);
-
-            // ---- V_new = T R (state chain) ---------------------------------
-            f32x4 v3[3];
-            v3[0] = mfma16k(th, rh, f32x4{0.f, 0.f, 0.f, 0.f});
-            v3[1] = mfma16k(th, rl, f32x4{0.f, 0.f, 0.f, 0.f});
-            v3[2] = mfma16k(tl, rh, f32x4{0.f, 0.f, 0.f, 0.f});
-            // K'^T[16 t + m][4 g + e] by transposed reads, lambda_C, P
+            const s16x4 ph = *reinterpret_cast<const s16x4*>(bfp(ts, L::PH) + m * P24 + 4 * g);
+            const s16x4 pl = *reinterpret_cast<const s16x4*>(bfp(ts, L::PL) + m * P24 + 4 * g);
+            // K'^T[16 t + m][4 g + e] by transposed reads; lambda_C
             s16x4 kth[NS], ktl[NS];
 #pragma unroll
             for (int t = 0; t < NS; ++t) {
@@ -272,18 +252,42 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
             f32x4 lam[NS];
 #pragma unroll
             for (int t = 0; t < NS; ++t) lam[t] = *reinterpret_cast<const f32x4*>(lc + 16 * t + 4 * g);
-            const s16x4 ph = *reinterpret_cast<const s16x4*>(bfp(ts, L::PH) + m * P24 + 4 * g);
-            const s16x4 pl = *reinterpret_cast<const s16x4*>(bfp(ts, L::PL) + m * P24 + 4 * g);
-            const f32x4 vn = v3[0] + v3[1] + v3[2];
-            s16x4 nh, nl;
-            split4(vn, nh, nl);
             __builtin_amdgcn_sched_barrier(0);
 
-            // ---- o = Q S^T + P V_new -------------------------------------
+            // ---- S as hi/lo B operands, slab by slab beside E S^T, Q S^T -----
+            f32x4 k2[2] = {}, q3[3] = {};
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) {
+                bf16x8 sh, sl;
+                split8(f32x8{sa[2 * j][0], sa[2 * j][1], sa[2 * j][2], sa[2 * j][3],
+                             sa[2 * j + 1][0], sa[2 * j + 1][1], sa[2 * j + 1][2],
+                             sa[2 * j + 1][3]},
+                       sh, sl);
+                k2[0] = mfma16(eh[j], sh, k2[0]);
+                k2[1] = mfma16(eh[j], sl, k2[1]);
+                q3[0] = mfma16(qh[j], sh, q3[0]);
+                q3[1] = mfma16(qh[j], sl, q3[1]);
+                q3[2] = mfma16(ql[j], sh, q3[2]);
+            }
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);   // this slab's split
+                __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);    // its five products
+            }
+            __builtin_amdgcn_sched_barrier(0);
+
+            // ---- R = w.v - E S^T;  V_new = [T | T] [R_hi; R_lo] ---------------
+            s16x4 rh, rl;
+            split4(wv - (k2[0] + k2[1]), rh, rl);
+            const f32x4 vn = mfma16(cat44(th, th), cat44(rh, rl), f32x4{0.f, 0.f, 0.f, 0.f});
+            s16x4 nh, nl;
+            split4(vn, nh, nl);
+            const bf16x8 nn = cat44(nh, nh);
+
+            // ---- o = Q S^T + [P_hi | P_lo] [N_hi; N_hi] + P_hi N_lo ----------
             f32x4 o = q3[0] + q3[1] + q3[2];
-            o = mfma16k(ph, nh, o);
+            o = mfma16(cat44(ph, pl), nn, o);
             o = mfma16k(ph, nl, o);
-            o = mfma16k(pl, nh, o);
 
             // ---- S^T <- (S^T + K'^T V_new) lambda_C --------------------------
             if (wide) {
@@ -292,20 +296,13 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
             }
 #pragma unroll
             for (int t = 0; t < NS; ++t) {
-                sa[t] = mfma16k(kth[t], nh, sa[t]);
+                sa[t] = mfma16(cat44(kth[t], ktl[t]), nn, sa[t]);
                 sa[t] = mfma16k(kth[t], nl, sa[t]);
-                sa[t] = mfma16k(ktl[t], nh, sa[t]);
             }
             if (!wide) {
 #pragma unroll
                 for (int t = 0; t < NS; ++t) sa[t] *= lam[t];
             }
-#pragma unroll
-            for (int j = 0; j < KJ; ++j)
-                split8(f32x8{sa[2 * j][0], sa[2 * j][1], sa[2 * j][2], sa[2 * j][3],
-                             sa[2 * j + 1][0], sa[2 * j + 1][1], sa[2 * j + 1][2],
-                             sa[2 * j + 1][3]},
-                       sh[j], sl[j]);
             {
                 const int64_t t0 = c * CH;
                 const int n = (int)min((int64_t)CH, T - t0);
@@ -320,6 +317,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                         __builtin_amdgcn_raw_buffer_store_b16(f2bf(o[r]), ores, (int)ooff[r], 0, 0);
                 }
             }
+            read_eq(c + 1);
             lds_barrier();
         }
         if (p.s_final) {
@@ -332,19 +330,19 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
     }
 
     // ============================== team B =================================
-    // Global loads: a uniform chunk base plus a 32-bit lane offset.  Rows
-    // past the end of the sequence repeat its last token and are masked in
-    // the arithmetic (alpha = 1, erase = write = 0).
+    // Global loads: a uniform row base plus a 32-bit lane offset.  Rows past
+    // the end of the sequence repeat its last token and are masked in the
+    // arithmetic (alpha = 1, erase = write = 0).
     auto last_row = [&](int64_t cn) { return (int)min((int64_t)CH - 1, T - 1 - cn * CH); };
     auto n_live = [&](int64_t cn) { return (int)min((int64_t)CH, T - cn * CH); };
 
-    // A role prepares chunk x in period x - lead (periods run from -2 to
+    // A role prepares chunk x in period x - lead (periods run from -DEPTH to
     // nch - 1, each closed by the workgroup barrier).  Loading roles keep two
     // chunks in flight in three register buffers; loads are unconditional
     // (an index past the end repeats the last chunk) so that the wait before
     // each prepare covers just its buffer.
     auto run = [&](int lead, auto&& load, auto&& prepare, auto& fa, auto& fb, auto& fc) {
-        for (int e = 0; e < 2 - lead; ++e) lds_barrier();
+        for (int e = 0; e < DEPTH - lead; ++e) lds_barrier();
         load(0, fa);
         load(min((int64_t)1, nch - 1), fb);
         for (int64_t x = 0; x < nch; x += 3) {
@@ -364,41 +362,14 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
         }
         for (int e = 0; e < lead; ++e) lds_barrier();
     };
-    auto run_noload = [&](int lead, auto&& prepare) {
-        for (int e = 0; e < 2 - lead; ++e) lds_barrier();
-        for (int64_t x = 0; x < nch; ++x) {
-            prepare(x);
-            lds_barrier();
-        }
-        for (int e = 0; e < lead; ++e) lds_barrier();
-    };
     const int cp = lane % (DK / 2);   // channel pair of the lane in the key-side passes
 
-    // C[4 g + r][m] = sum_c X[m][c] K'[4 g + r][c] for X = E or Q (operand
-    // order): lane (g, m) gets row m, columns 4 g .. 4 g + 3 of X K'^T.
-    auto xk_product = [&](const bf16_t* Xh, const bf16_t* Xl, const bf16_t* Kh, const bf16_t* Kl) {
-        f32x4 acc[3] = {};
-#pragma unroll
-        for (int j = 0; j < KJ; ++j) {
-            const bf16x8 xh = *reinterpret_cast<const bf16x8*>(Xh + kq_at<DK>(m, 32 * j + 8 * g));
-            const bf16x8 xl = *reinterpret_cast<const bf16x8*>(Xl + kq_at<DK>(m, 32 * j + 8 * g));
-            const int at = m * L::PKN + 32 * j + 4 * g;
-            const bf16x8 kh = ld2x4(Kh + at, Kh + at + 16);
-            const bf16x8 kl = ld2x4(Kl + at, Kl + at + 16);
-            acc[0] = mfma16(kh, xh, acc[0]);
-            acc[1] = mfma16(kh, xl, acc[1]);
-            acc[2] = mfma16(kl, xh, acc[2]);
-        }
-        return acc[0] + acc[1] + acc[2];
-    };
-
     if (wave == NA) {
-        // ------------------- AP-A: A, T = (I + A)^{-1} -----------------------
-        float* Af = reinterpret_cast<float*>(smem + L::AF);
+        // ------------- AP-A: A for chunk p + 2, T for chunk p + 1 -------------
         // Wide chunk: A and P entry by entry from the log decays G (within
         // the chunk, per channel), and the update operand
         // k (.) lambda_C / lambda = k (.) e^{G_C - G} in place of K'.
-        auto wide_chunk = [&](int64_t cn, unsigned char* es, unsigned char* ts) {
+        auto wide_chunk = [&](int64_t cn, unsigned char* es, float* Af, float* Wp) {
             float* Gf = reinterpret_cast<float*>(smem + L::FG);
             bf16_t* Fk = bfp(smem, L::FK);
             bf16_t* Fb = bfp(smem, L::FB);
@@ -436,8 +407,6 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                 *reinterpret_cast<uint32_t*>(Kl + t * L::PKN + 2 * cp) = xl;
             }
             wave_lds_sync();
-            bf16_t* Ph = bfp(ts, L::PH);
-            bf16_t* Pl = bfp(ts, L::PL);
             // all 256 (r, s) pairs: s <= r are formed, the rest are zero
             for (int e = lane; e < CH * CH; e += 64) {
                 const int r = e >> 4, s = e & 15;
@@ -451,67 +420,76 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                     }
                 }
                 Af[r * PAF + s] = s < r ? av : 0.f;
-                bf16_t xh, xl;
-                split_bf16(pv, xh, xl);
-                Ph[r * P24 + s] = xh;
-                Pl[r * P24 + s] = xl;
+                Wp[r * PAF + s] = pv;
             }
         };
-        auto prepare = [&](int64_t cn) {
-            unsigned char* es = eset(cn);
-            unsigned char* ts = tset(cn);
-            if (wide_flag(es)) {
-                wide_chunk(cn, es, ts);
-            } else {
-                // C[4 g + r][m] = A[m][4 g + r]; kept for 4 g + r < m
-                const f32x4 acc = xk_product(bfp(es, L::EH), bfp(es, L::EL), bfp(es, L::KH),
-                                             bfp(es, L::KL));
-                f32x4 av;
+        const int rr = (lane >> 1) & 15, half = lane & 1;
+        for (int64_t pp = -DEPTH; pp < nch; ++pp) {
+            const int64_t x2 = pp + 2, x1 = pp + 1;
+            if (x2 >= 0 && x2 < nch) {
+                unsigned char* es = eset(x2);
+                float* Af = reinterpret_cast<float*>(smem + L::AF + (int)(x2 & 1) * CH * PAF * 4);
+                if (wide_flag(es)) {
+                    float* Wp = reinterpret_cast<float*>(smem + L::WP + (int)(x2 & 1) * CH * PAF * 4);
+                    wide_chunk(x2, es, Af, Wp);
+                } else {
+                    // C[4 g + r][m] = sum_c E[m][c] K'[4 g + r][c] = A[m][4 g + r];
+                    // kept for 4 g + r < m
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) av[r] = 4 * g + r < m ? acc[r] : 0.f;
-                *reinterpret_cast<f32x4*>(Af + m * PAF + 4 * g) = av;
+                    for (int j = 0; j < KJ; ++j) {
+                        const bf16x8 xh = *reinterpret_cast<const bf16x8*>(
+                            bfp(es, L::EH) + kq_at<DK>(m, 32 * j + 8 * g));
+                        const int at = m * L::PKN + 32 * j + 4 * g;
+                        const bf16x8 kh = ld2x4(bfp(es, L::KH) + at, bfp(es, L::KH) + at + 16);
+                        acc = mfma16(kh, xh, acc);
+                    }
+                    f32x4 av;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) av[r] = 4 * g + r < m ? acc[r] : 0.f;
+                    *reinterpret_cast<f32x4*>(Af + m * PAF + 4 * g) = av;
+                }
             }
-            wave_lds_sync();
-            // X = (I + A)^{-1}: lane pair (rr, half) builds row rr from
-            // X = I - X A, columns right to left, pushing each finished entry
-            // into the columns left of it; A's strictly lower part is read
-            // into registers first so the 16 dependent steps wait on nothing.
-            const int rr = (lane >> 1) & 15, half = lane & 1;
-            f32x4 lrow[CH][4];
+            if (x1 >= 0 && x1 < nch) {
+                // X = (I + A)^{-1}: lane pair (rr, half) builds row rr from
+                // X = I - X A, columns right to left, pushing each finished
+                // entry into the columns left of it; A's strictly lower part
+                // is read into registers first so the 16 dependent steps wait
+                // on nothing.
+                const float* Af = reinterpret_cast<const float*>(smem + L::AF + (int)(x1 & 1) * CH * PAF * 4);
+                f32x4 lrow[CH][4];
 #pragma unroll
-            for (int q = 1; q < CH; ++q)
+                for (int q = 1; q < CH; ++q)
 #pragma unroll
-                for (int q4 = 0; q4 < (q + 3) / 4; ++q4)
-                    lrow[q][q4] = *reinterpret_cast<const f32x4*>(Af + q * PAF + 4 * q4);
-            __builtin_amdgcn_sched_barrier(0);
-            float acc2[CH], x[CH];
+                    for (int q4 = 0; q4 < (q + 3) / 4; ++q4)
+                        lrow[q][q4] = *reinterpret_cast<const f32x4*>(Af + q * PAF + 4 * q4);
+                float acc2[CH], x[CH];
 #pragma unroll
-            for (int cc = 0; cc < CH; ++cc) acc2[cc] = 0.f;
+                for (int cc = 0; cc < CH; ++cc) acc2[cc] = 0.f;
 #pragma unroll
-            for (int q = CH - 1; q >= 0; --q) {
-                x[q] = (rr == q ? 1.f : 0.f) - acc2[q];
+                for (int q = CH - 1; q >= 0; --q) {
+                    x[q] = (rr == q ? 1.f : 0.f) - acc2[q];
 #pragma unroll
-                for (int q4 = 0; q4 < (q + 3) / 4; ++q4)
+                    for (int q4 = 0; q4 < (q + 3) / 4; ++q4)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * q4 + e < q) acc2[4 * q4 + e] += x[q] * lrow[q][q4][e];
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * q4 + e < q) acc2[4 * q4 + e] += x[q] * lrow[q][q4][e];
+                }
+                // columns 8 half .. 8 half + 7 of row rr (bitwise select: a
+                // conditional here becomes an indexed private array)
+                const uint32_t msk = half ? 0xffffffffu : 0u;
+                float xs[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    xs[e] = __uint_as_float((__float_as_uint(x[8 + e]) & msk) |
+                                            (__float_as_uint(x[e]) & ~msk));
+                const u32x4 xh = u32x4{cvt_pk(xs[0], xs[1]), cvt_pk(xs[2], xs[3]),
+                                       cvt_pk(xs[4], xs[5]), cvt_pk(xs[6], xs[7])};
+                if (lane < 32)
+                    *reinterpret_cast<u32x4*>(bfp(tset(x1), L::TH) + rr * P24 + 8 * half) = xh;
             }
-            // columns 8 half .. 8 half + 7 of row rr (bitwise select: a
-            // conditional here becomes an indexed private array)
-            const uint32_t msk = half ? 0xffffffffu : 0u;
-            float xs[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                xs[e] = __uint_as_float((__float_as_uint(x[8 + e]) & msk) |
-                                        (__float_as_uint(x[e]) & ~msk));
-            bf16x8 xh, xl;
-            split8(f32x8{xs[0], xs[1], xs[2], xs[3], xs[4], xs[5], xs[6], xs[7]}, xh, xl);
-            if (lane < 32) {
-                *reinterpret_cast<bf16x8*>(bfp(ts, L::TH) + rr * P24 + 8 * half) = xh;
-                *reinterpret_cast<bf16x8*>(bfp(ts, L::TL) + rr * P24 + 8 * half) = xl;
-            }
-        };
-        run_noload(1, prepare);
+            lds_barrier();
+        }
     } else if (wave == NA + 1) {
         // ------------------------ AP-P: P, w . v ----------------------------
         // lane: token t = lane / 4, state rows 8 (lane % 4) .. + 7
@@ -529,18 +507,34 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
         auto prepare = [&](int64_t cn, const Buf& f) {
             unsigned char* es = eset(cn);
             unsigned char* ts = tset(cn);
+            f32x4 pv;
             if (!wide_flag(es)) {
-                // C[4 g + r][m] = P[m][4 g + r]; kept for 4 g + r <= m
-                const f32x4 acc = xk_product(bfp(es, L::QH), bfp(es, L::QL), bfp(es, L::KH),
-                                             bfp(es, L::KL));
-                f32x4 pv;
+                // C[4 g + r][m] = sum_c Q[m][c] K'[4 g + r][c] = P[m][4 g + r];
+                // kept for 4 g + r <= m
+                f32x4 acc[3] = {};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) pv[r] = 4 * g + r <= m ? acc[r] : 0.f;
-                s16x4 xh, xl;
-                split4(pv, xh, xl);
-                *reinterpret_cast<s16x4*>(bfp(ts, L::PH) + m * P24 + 4 * g) = xh;
-                *reinterpret_cast<s16x4*>(bfp(ts, L::PL) + m * P24 + 4 * g) = xl;
+                for (int j = 0; j < KJ; ++j) {
+                    const int aq = kq_at<DK>(m, 32 * j + 8 * g);
+                    const bf16x8 xh = *reinterpret_cast<const bf16x8*>(bfp(es, L::QH) + aq);
+                    const bf16x8 xl = *reinterpret_cast<const bf16x8*>(bfp(es, L::QL) + aq);
+                    const int at = m * L::PKN + 32 * j + 4 * g;
+                    const bf16x8 kh = ld2x4(bfp(es, L::KH) + at, bfp(es, L::KH) + at + 16);
+                    const bf16x8 kl = ld2x4(bfp(es, L::KL) + at, bfp(es, L::KL) + at + 16);
+                    acc[0] = mfma16(kh, xh, acc[0]);
+                    acc[1] = mfma16(kh, xl, acc[1]);
+                    acc[2] = mfma16(kl, xh, acc[2]);
+                }
+                const f32x4 s = acc[0] + acc[1] + acc[2];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pv[r] = 4 * g + r <= m ? s[r] : 0.f;
+            } else {
+                const float* Wp = reinterpret_cast<const float*>(smem + L::WP + (int)(cn & 1) * CH * PAF * 4);
+                pv = *reinterpret_cast<const f32x4*>(Wp + m * PAF + 4 * g);
             }
+            s16x4 xh, xl;
+            split4(pv, xh, xl);
+            *reinterpret_cast<s16x4*>(bfp(ts, L::PH) + m * P24 + 4 * g) = xh;
+            *reinterpret_cast<s16x4*>(bfp(ts, L::PL) + m * P24 + 4 * g) = xl;
             const bool live = wt < n_live(cn);
             float* wv = reinterpret_cast<float*>(ts + L::WV);
 #pragma unroll
@@ -552,61 +546,66 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
         Buf fa, fb, fc;
         run(1, load, prepare, fa, fb, fc);
     } else {
-        // ------------- E0..E3: lambda, 1 / lambda, E, Q, K' (hi/lo) ----------
+        // ------------- E0..E3: lambda, 1 / lambda, E, Q, K' -------------------
         const int ej = wave - NA - 2;
-        auto erole = [&](auto jc) {
-            constexpr int J = decltype(jc)::value;
-            constexpr int NPRE = 4 * J;    // rows before this wave's tokens
+        auto erole = [&](auto t0c, auto ntc) {
+            constexpr int T0 = decltype(t0c)::value;   // first token of this wave
+            constexpr int NT = decltype(ntc)::value;   // tokens of this wave
             struct Buf {
-                uint32_t a[NPRE + 4];
-                uint32_t k[4], b[4], q[4];
+                uint32_t a[T0 + NT];
+                uint32_t k[NT], b[NT], q[NT];
             };
+            // buffer loads: a per-chunk resource whose range ends at the
+            // sequence end (rows past it read as 0), and per-row lane
+            // offsets computed once
+            int roff[T0 + NT];
+#pragma unroll
+            for (int t = 0; t < T0 + NT; ++t) roff[t] = t * (int)tstride * 2 + 4 * cp;
             auto load = [&](int64_t cn, Buf& f) {
-                const int last = last_row(cn);
                 const int64_t cb = kofs + cn * CH * tstride;
-                const bf16_t* ab = p.alpha + cb;
-                const bf16_t* kb = p.k + cb;
-                const bf16_t* bb = p.erase + cb;
-                const bf16_t* qb = p.q + cb;
+                const int nbytes = n_live(cn) * (int)tstride * 2;
+                const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(p.alpha + cb), (short)0, nbytes, 0x00020000);
+                const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(p.k + cb), (short)0, nbytes, 0x00020000);
+                const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(p.erase + cb), (short)0, nbytes, 0x00020000);
+                const auto rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(p.q + cb), (short)0, nbytes, 0x00020000);
 #pragma unroll
-                for (int t = 0; t < NPRE + 4; ++t) {
-                    const uint32_t off = (uint32_t)(min(t, last) * (int)tstride + 2 * cp);
-                    f.a[t] = *reinterpret_cast<const uint32_t*>(ab + off);
-                }
+                for (int t = 0; t < T0 + NT; ++t)
+                    f.a[t] = __builtin_amdgcn_raw_buffer_load_b32(ra, roff[t], 0, 0);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const uint32_t off = (uint32_t)(min(NPRE + u, last) * (int)tstride + 2 * cp);
-                    f.k[u] = *reinterpret_cast<const uint32_t*>(kb + off);
-                    f.b[u] = *reinterpret_cast<const uint32_t*>(bb + off);
-                    f.q[u] = *reinterpret_cast<const uint32_t*>(qb + off);
+                for (int u = 0; u < NT; ++u) {
+                    f.k[u] = __builtin_amdgcn_raw_buffer_load_b32(rk, roff[T0 + u], 0, 0);
+                    f.b[u] = __builtin_amdgcn_raw_buffer_load_b32(rb, roff[T0 + u], 0, 0);
+                    f.q[u] = __builtin_amdgcn_raw_buffer_load_b32(rq, roff[T0 + u], 0, 0);
                 }
             };
             const int pc = kperm(2 * cp);
-            auto prepare = [&](int64_t cn, const Buf& f) {
+            auto body = [&](int64_t cn, const Buf& f, int n, auto maskc) {
+                constexpr bool MASK = decltype(maskc)::value;
                 unsigned char* es = eset(cn);
-                const int n = n_live(cn);
+                auto live = [&](int t) { return !MASK || t < n; };
                 float l0 = 1.f, l1 = 1.f;
 #pragma unroll
-                for (int t = 0; t < NPRE; ++t) {
-                    const bool live = t < n;
-                    l0 *= live ? lo_bf(f.a[t]) : 1.f;
-                    l1 *= live ? hi_bf(f.a[t]) : 1.f;
+                for (int t = 0; t < T0; ++t) {
+                    if (live(t)) {
+                        l0 *= lo_bf(f.a[t]);
+                        l1 *= hi_bf(f.a[t]);
+                    }
                 }
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int t = NPRE + u;
-                    const bool live = t < n;
-                    l0 *= live ? lo_bf(f.a[t]) : 1.f;
-                    l1 *= live ? hi_bf(f.a[t]) : 1.f;
+                for (int u = 0; u < NT; ++u) {
+                    const int t = T0 + u;
+                    const bool lv = live(t);
+                    if (lv) {
+                        l0 *= lo_bf(f.a[t]);
+                        l1 *= hi_bf(f.a[t]);
+                    }
                     const float r0 = __builtin_amdgcn_rcpf(l0), r1 = __builtin_amdgcn_rcpf(l1);
                     const float k0 = lo_bf(f.k[u]), k1 = hi_bf(f.k[u]);
-                    const float e0 = live ? lo_bf(f.b[u]) * k0 : 0.f;
-                    const float e1 = live ? hi_bf(f.b[u]) * k1 : 0.f;
-                    uint32_t xh, xl;
+                    const float e0 = lv ? lo_bf(f.b[u]) * k0 : 0.f;
+                    const float e1 = lv ? hi_bf(f.b[u]) * k1 : 0.f;
                     const int ot = kq_at<DK>(t, pc);
-                    split2(e0 * l0, e1 * l1, xh, xl);
-                    *reinterpret_cast<uint32_t*>(bfp(es, L::EH) + ot) = xh;
-                    *reinterpret_cast<uint32_t*>(bfp(es, L::EL) + ot) = xl;
+                    *reinterpret_cast<uint32_t*>(bfp(es, L::EH) + ot) = cvt_pk(e0 * l0, e1 * l1);
+                    uint32_t xh, xl;
                     split2(lo_bf(f.q[u]) * l0, hi_bf(f.q[u]) * l1, xh, xl);
                     *reinterpret_cast<uint32_t*>(bfp(es, L::QH) + ot) = xh;
                     *reinterpret_cast<uint32_t*>(bfp(es, L::QL) + ot) = xl;
@@ -614,7 +613,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                     *reinterpret_cast<uint32_t*>(bfp(es, L::KH) + t * L::PKN + 2 * cp) = xh;
                     *reinterpret_cast<uint32_t*>(bfp(es, L::KL) + t * L::PKN + 2 * cp) = xl;
                 }
-                if constexpr (J == 3) {
+                if constexpr (T0 + NT == CH) {
                     float* lc = reinterpret_cast<float*>(es + L::LC);
                     *reinterpret_cast<float2*>(lc + 2 * cp) = float2{l0, l1};
                     const bool w = !(l0 >= kLamMin && l1 >= kLamMin);
@@ -622,13 +621,20 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                     if (lane == 0) *reinterpret_cast<int*>(lc + DK) = any != 0 ? 1 : 0;
                 }
             };
+            auto prepare = [&](int64_t cn, const Buf& f) {
+                const int n = n_live(cn);
+                if (n == CH)
+                    body(cn, f, n, std::false_type{});
+                else
+                    body(cn, f, n, std::true_type{});
+            };
             Buf fa, fb, fc;
-            run(2, load, prepare, fa, fb, fc);
+            run(DEPTH, load, prepare, fa, fb, fc);
         };
-        if (ej == 0) erole(std::integral_constant<int, 0>{});
-        else if (ej == 1) erole(std::integral_constant<int, 1>{});
-        else if (ej == 2) erole(std::integral_constant<int, 2>{});
-        else erole(std::integral_constant<int, 3>{});
+        if (ej == 0) erole(std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{});
+        else if (ej == 1) erole(std::integral_constant<int, 4>{}, std::integral_constant<int, 4>{});
+        else if (ej == 2) erole(std::integral_constant<int, 8>{}, std::integral_constant<int, 4>{});
+        else erole(std::integral_constant<int, 12>{}, std::integral_constant<int, 4>{});
     }
 }
 
