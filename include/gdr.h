@@ -37,10 +37,12 @@
  *                            unsupported dtype;
  *       GDR_ERR_DEVICE       the HIP runtime reported a launch error.
  *     No C++ exception crosses this interface.
- *   - Values are not checked on the device: NaN/Inf propagate.  Decay gates
- *     are used through their logarithm, clamped below at log(FLT_MIN), so a
- *     gate of exactly 0 acts as a full reset without producing NaN.
- *   - Gate ranges: alpha in (0, 1]; beta, erase, write in [0, 1].
+ *   - Values are not checked on the device: NaN/Inf propagate.  A decay gate
+ *     of exactly 0 acts as a full reset without producing NaN (gates are
+ *     clamped to FLT_MIN wherever a logarithm is taken).
+ *   - Gate ranges: alpha in (0, 1]; write in [0, 1]; beta and erase in
+ *     [0, 2] -- above 1 the per-token transition has a negative eigenvalue
+ *     along k, down to the reflection I - 2 k k^T at 2.
  *   - T, B, H, N may be 0 (nothing is launched; s_final receives s0 or zeros
  *     when T == 0 and B*H > 0).  Any T >= 1 is accepted: the sequence is cut
  *     into internal chunks and the last one is partial.  The chunk length is
@@ -145,7 +147,7 @@ gdr_status_t gdr_recurrent_step(int64_t N, int64_t H, int64_t Dk, int64_t Dv,
  *   q, k        [B, T, H, Dk] in_dt
  *   v           [B, T, H, Dv] in_dt
  *   alpha       [B, T, H, Dk] in_dt, per-key-channel decay in (0, 1]
- *   erase       [B, T, H, Dk] in_dt, b in [0, 1]
+ *   erase       [B, T, H, Dk] in_dt, b in [0, 2]
  *   write       [B, T, H, Dv] in_dt, w in [0, 1]
  *   s0, s_final, o, out_dt as for gdr_chunk_fwd.
  */

@@ -415,6 +415,53 @@ def pin_gdn2_erase_axis(orc):
         np.testing.assert_allclose(sf[0, 0], ref, rtol=0, atol=1e-15)
 
 
+def pin_gdn2_householder(orc):
+    """Negative eigenvalue range: per-channel alpha = 1, erase b = 2 on every
+    channel, w = 0 and unit keys make each step S <- S (I - 2 k k^T), a
+    reflection.  The Frobenius norm of S is kept at every step, and the same
+    key twice in a row gives back the state it started from."""
+    g = _rng(25)
+    T, Dk, Dv = 12, 6, 5
+    k = _unit(g.standard_normal((1, T, 1, Dk)))
+    k[0, 7] = k[0, 6]                                    # tokens 6 and 7 repeat
+    q = g.standard_normal((1, T, 1, Dk))
+    v = g.standard_normal((1, T, 1, Dv))
+    S0 = g.standard_normal((1, 1, Dv, Dk))
+    ones, twos = np.ones((1, T, 1, Dk)), np.full((1, T, 1, Dk), 2.0)
+    n0 = np.linalg.norm(S0[0, 0])
+    states = []
+    for t in range(T):
+        _, st = orc.gdn2_fwd(q[:, :t + 1], k[:, :t + 1], v[:, :t + 1], ones[:, :t + 1],
+                             twos[:, :t + 1], np.zeros((1, t + 1, 1, Dv)), S0)
+        states.append(st[0, 0])
+        assert abs(np.linalg.norm(st[0, 0]) - n0) <= 1e-12 * n0, t
+    np.testing.assert_allclose(states[7], states[5], rtol=0, atol=1e-12)
+
+
+def pin_gdn_negative_beta(orc):
+    """Scalar rule with beta = 2, alpha = 1, v = 0 and unit keys: each step is
+    the reflection S (I - 2 k k^T), so |S|_F is kept and a repeated key undoes
+    itself; with v != 0 the step adds 2 v k^T after the reflection."""
+    g = _rng(26)
+    T, Dk, Dv = 10, 6, 4
+    k = _unit(g.standard_normal((1, T, 1, Dk)))
+    k[0, 4] = k[0, 3]
+    q = g.standard_normal((1, T, 1, Dk))
+    S0 = g.standard_normal((1, 1, Dv, Dk))
+    a, b = np.ones((1, T, 1)), np.full((1, T, 1), 2.0)
+    n0 = np.linalg.norm(S0[0, 0])
+    _, s3 = orc.gdn_fwd(q[:, :3], k[:, :3], np.zeros((1, 3, 1, Dv)), a[:, :3], b[:, :3], S0)
+    _, s5 = orc.gdn_fwd(q[:, :5], k[:, :5], np.zeros((1, 5, 1, Dv)), a[:, :5], b[:, :5], S0)
+    _, sT = orc.gdn_fwd(q, k, np.zeros((1, T, 1, Dv)), a, b, S0)
+    assert abs(np.linalg.norm(sT[0, 0]) - n0) <= 1e-12 * n0
+    np.testing.assert_allclose(s5[0, 0], s3[0, 0], rtol=0, atol=1e-12)
+    v = g.standard_normal((1, 1, 1, Dv))
+    _, s1 = orc.gdn_fwd(q[:, :1], k[:, :1], v, a[:, :1], b[:, :1], S0)
+    kk = k[0, 0, 0]
+    ref = S0[0, 0] @ (np.eye(Dk) - 2 * np.outer(kk, kk)) + 2 * np.outer(v[0, 0, 0], kk)
+    np.testing.assert_allclose(s1[0, 0], ref, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [
     pin_golden_gdn, pin_golden_step, pin_golden_gdn2,
     pin_exact_matrix_form_gdn, pin_exact_matrix_form_gdn2,
@@ -422,5 +469,5 @@ ALL_PINS = [
     pin_d_orthonormal_retrieval, pin_e_gdn2_collapse, pin_f_first_token,
     pin_g_read_only, pin_h_split, pin_h_step_chain, pin_i_sgd,
     pin_j_contraction, pin_k_kda, pin_gdn2_pure_decay, pin_gdn2_write_only,
-    pin_gdn2_erase_axis,
+    pin_gdn2_erase_axis, pin_gdn2_householder, pin_gdn_negative_beta,
 ]

@@ -253,6 +253,33 @@ def test_gdn2_bf16_wide_decay_range(gdr_lib):
     _check_gdn2(gdr_lib, inp, "f32")
 
 
+# Negative eigenvalues: erase / beta up to 2 makes the per-token transition
+# I - 2 k k^T (a reflection) at the top of the range, so (I + A) loses its
+# diagonal dominance; these check that T = (I + A)^{-1} stays accurate.
+
+@pytest.mark.parametrize("regime", ["fast_decay", "long_memory"])
+def test_gdn2_bf16_negative_eigenvalue_erase(gdr_lib, regime):
+    kw = dict(alpha_shift=2.0) if regime == "fast_decay" else dict(alpha_shift=-4.0, s0_std=0.05)
+    inp = make_gdn2(B=1, T=300, H=2, Dk=128, Dv=128, dtype="bf16", seed=61, **kw)
+    inp.erase = (inp.erase.float() * 2.0).to(torch.bfloat16)
+    _check_gdn2(gdr_lib, inp, "f32")
+
+
+def test_gdn2_fp32_negative_eigenvalue_erase(gdr_lib):
+    inp = make_gdn2(B=1, T=130, H=2, Dk=64, Dv=128, dtype="f32", seed=62,
+                    alpha_shift=-4.0, s0_std=0.5)
+    inp.erase = inp.erase * 2.0
+    _check_gdn2(gdr_lib, inp, "f32")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_gdn_negative_eigenvalue_beta(gdr_lib, dt):
+    inp = make_gdn(B=2, T=200, H=2, Dk=128, Dv=128, dtype=dt, seed=63,
+                   alpha_shift=-4.0, s0_std=0.05)
+    inp.beta = inp.beta * 2.0
+    _check_gdn(gdr_lib, inp, "f32")
+
+
 def test_gdn2_bf16_workload_b4_h16_t4096(gdr_lib):
     """The channel-gated workload at full size (B4 H16 T4096 d128), the
     launch the benchmark times; the oracle checks batches 0 and 3."""
