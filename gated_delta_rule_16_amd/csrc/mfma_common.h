@@ -178,10 +178,19 @@ __device__ __forceinline__ bf16x8 ld2x4(const bf16_t* p0, const bf16_t* p1) {
 
 // Workgroup barrier that orders LDS only: outstanding global loads (the
 // next chunk's prefetch) stay in flight across it.
+//
+// The scalar branch after it is never taken (no launch has 2^32 - 1
+// workgroups; if one did, it would only run a no-op).  It ends the basic
+// block at the barrier, so the compiler lays each loop out with its code on
+// its own side of the barriers instead of rotating part of one period's
+// work past them; measured on the scalar-gate chunk kernel (B8 H16 T4096,
+// interleaved launches) that is ~11% faster, and neutral to slightly faster
+// on the channel-gate one.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    if (blockIdx.x == 0xffffffffu) asm volatile("s_nop 0" ::: "memory");
 }
 
 }  // namespace gdr
