@@ -60,7 +60,7 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def summarize(trace_dir, fetch_dir, write_dir, out_txt, command):
+def summarize(trace_dir, fetch_dir, write_dir, out_txt, command, timed=20):
     """Turn rocprofv3 CSV output (a --kernel-trace --stats run and two --pmc
     runs, FETCH_SIZE then WRITE_SIZE) into a short text summary and the JSON
     the benchmark reads its `traffic` figures from.  Counter KiB are scaled
@@ -90,6 +90,20 @@ def summarize(trace_dir, fetch_dir, write_dir, out_txt, command):
     for r in stats:
         lines.append(f"  {r['Name'][:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
                      f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f}")
+    # the same trace, per bench leg: the timed launches only (the last
+    # `timed` dispatches of each kernel; the warm-up launches before them
+    # include the clock ramp after idle)
+    trace = list(csv.DictReader(open(glob.glob(os.path.join(trace_dir, "*kernel_trace.csv"))[0])))
+    lines += ["", f"Timed launches (the last {timed} dispatches of each kernel in the trace, as the "
+              "bench times them):", f"  {'leg':8s} {'kernel':44s} {'n':>4s} {'avg us':>10s} {'min us':>10s}"]
+    for leg, prefix in KERNELS.items():
+        d = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in trace
+                   if r["Kernel_Name"].startswith(prefix))
+        if not d:
+            continue
+        dur = [(e - b) / 1e3 for b, e in d[-timed:]]
+        lines.append(f"  {leg:8s} {prefix[:44]:44s} {len(dur):4d} {sum(dur) / len(dur):10.1f} "
+                     f"{min(dur):10.1f}")
     lines += ["", "HBM counters per dispatch (KiB as read; scale = copy's known bytes / reading):",
               f"  FETCH_SIZE scale {scale['FETCH_SIZE']:.4f}, WRITE_SIZE scale {scale['WRITE_SIZE']:.4f}"]
     for leg, c in per.items():
@@ -248,7 +262,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "copy"], default=None,
                     help="time one operation only (for profiling)")
