@@ -34,7 +34,7 @@
 //   team B   running ahead of it:
 //            E0..E3 (waves 4..7), chunk c + 3: the elementwise pass --
 //                 lambda by running products, 1 / lambda, the operands E, Q,
-//                 K'; each wave takes a few tokens (lane = channel pair) and
+//                 K'; each wave takes 3 to 5 tokens (lane = channel pair) and
 //                 forms the products of the rows before them itself, so the
 //                 waves never wait on each other;
 //            AP-A (wave 2): A = E K'^T for chunk c + 2 (or the wide-chunk
@@ -631,10 +631,13 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
             Buf fa, fb, fc;
             run(DEPTH, load, prepare, fa, fb, fc);
         };
-        if (ej == 0) erole(std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{});
-        else if (ej == 1) erole(std::integral_constant<int, 4>{}, std::integral_constant<int, 4>{});
-        else if (ej == 2) erole(std::integral_constant<int, 8>{}, std::integral_constant<int, 4>{});
-        else erole(std::integral_constant<int, 12>{}, std::integral_constant<int, 4>{});
+        // tokens per wave 3, 3, 5, 5: waves 4 and 5 share their SIMDs with
+        // team A, waves 6 and 7 with the lighter AP waves (measured best of
+        // the splits tried: 4/4/4/4, 3/3/5/5, 3/4/5/4, 3/4/4/5, 2/2/6/6, 3/3/4/6, 2/3/5/6)
+        if (ej == 0) erole(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
+        else if (ej == 1) erole(std::integral_constant<int, 3>{}, std::integral_constant<int, 3>{});
+        else if (ej == 2) erole(std::integral_constant<int, 6>{}, std::integral_constant<int, 5>{});
+        else erole(std::integral_constant<int, 11>{}, std::integral_constant<int, 5>{});
     }
 }
 
