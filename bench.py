@@ -15,6 +15,9 @@ The JSON line (stdout, last line) carries:
   decode             gdr_recurrent_step on 256 sequences x 16 heads, d=128,
                      64 consecutive steps: GB/s of state + token traffic
   gdr2               gdr2_chunk_fwd on B=4 H=16 T=4096 d=128 (bf16 gates)
+  long_context       gdr_chunk_fwd on B=1 H=16 T=32768 d=128 with an initial
+                     state (16 sequential chains; tokens/s, HBM and MFMA
+                     fractions)
   copy_reference     a plain 512 MiB device copy (achievable bandwidth)
   cpu_baseline       the fp64 oracle timed on the host on the same workload
 """
@@ -177,6 +180,31 @@ def bench_gdn(gdr, torch, warmup, steps):
                 Dv=Dv, bytes=bytes_launch, flops=flops_launch)
 
 
+def bench_longctx(gdr, torch, warmup, steps):
+    """The long-context workload: B1 H16 T32768 d128 with an initial state
+    (16 sequential chains of 1024 chunks; few heads, so narrow row blocks)."""
+    from gdr_gen import make_config
+    inp = make_config(2)
+    B, T, H, Dk = inp.q.shape
+    Dv = inp.v.shape[-1]
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
+    a, b = inp.alpha.to(dev), inp.beta.to(dev)
+    s0 = inp.s0.to(dev)
+    o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+    sf = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+
+    def fn():
+        gdr.gdr_chunk_fwd(q, k, v, a, b, s0, out_dtype=torch.float32, o=o, s_final=sf)
+
+    mean, mn, med, wall = time_launches(fn, warmup, steps)
+    th = B * T * H
+    bytes_launch = th * (2 * (Dk + Dk + Dv) + 8 + 4 * Dv) + 2 * 4 * B * H * Dv * Dk
+    C = 64
+    flops_launch = th * 2 * (3 * Dk * Dv + 5 * C * (Dk + Dv) // 2)
+    return dict(mean=mean, min=mn, B=B, T=T, H=H, bytes=bytes_launch, flops=flops_launch)
+
+
 def bench_decode(gdr, torch, warmup):
     from gdr_gen import make_config
     inp = make_config(3)
@@ -264,7 +292,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
-    ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "copy"], default=None,
+    ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "longctx", "copy"], default=None,
                     help="time one operation only (for profiling)")
     ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarize rocprofv3 CSV output into OUT and the traffic JSON, then exit")
@@ -297,6 +325,9 @@ def main():
     if args.only in (None, "gdr2"):
         log("timing gdr2_chunk_fwd B4 H16 T4096 d128 ...")
         res["gdr2"] = bench_gdr2(gdr, torch, args.warmup, args.steps)
+    if args.only in (None, "longctx"):
+        log("timing gdr_chunk_fwd B1 H16 T32768 d128 (long context) ...")
+        res["longctx"] = bench_longctx(gdr, torch, min(args.warmup, 10), min(args.steps, 10))
     if args.only in (None, "copy"):
         log("timing a 512 MiB device copy ...")
         res["copy"] = bench_copy(torch, args.warmup, args.steps)
@@ -344,6 +375,15 @@ def main():
                            "frac_hbm": gbs / HBM_PEAK_GBS,
                            "algorithmic_bytes_per_launch": r["bytes"],
                            "traffic": measured_traffic("gdr2")}
+    if "longctx" in res:
+        r = res["longctx"]
+        gbs = r["bytes"] / r["mean"] / 1e9
+        out["long_context"] = {
+            "workload": "gdr_chunk_fwd B1 H16 T32768 d128 bf16, fp32 alpha/beta/o, initial state",
+            "tokens/s": r["B"] * r["T"] / r["mean"], "launch_us_mean": r["mean"] * 1e6,
+            "launch_us_min": r["min"] * 1e6, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+            "mfma_frac": r["flops"] / r["mean"] / 1e12 / BF16_PEAK_TFLOPS,
+            "algorithmic_bytes_per_launch": r["bytes"]}
     if "copy" in res:
         cp = res["copy"]
         out["copy_reference"] = {"what": "torch device-to-device copy, 512 MiB read + 512 MiB "
