@@ -18,6 +18,10 @@ The JSON line (stdout, last line) carries:
   long_context       gdr_chunk_fwd on B=1 H=16 T=32768 d=128 with an initial
                      state (16 sequential chains; tokens/s, HBM and MFMA
                      fractions)
+  l2norm             the fused L2 normalisation of q, k (GDR_L2NORM_QK) on
+                     the GDN and GDN-2 workloads with raw q, k: launch time
+                     fused, plain (no normalisation), and a separate
+                     normalise pass in PyTorch followed by the plain call
   copy_reference     a plain 512 MiB device copy (achievable bandwidth)
   cpu_baseline       the fp64 oracle timed on the host on the same workload
 """
@@ -256,6 +260,48 @@ def bench_gdr2(gdr, torch, warmup, steps):
     return dict(mean=mean, min=mn, median=med, B=B, T=T, H=H, bytes=bytes_launch)
 
 
+def bench_l2norm(gdr, torch, warmup, steps):
+    """Fused q, k normalisation against the plain call and against a
+    separate normalise pass (fp32 sum of squares in PyTorch, bf16 result)
+    followed by the plain call, on the GDN (B8 H16 T4096) and GDN-2 (B4 H16
+    T4096) workloads with raw q, k."""
+    from gdr_gen import make_gdn, make_gdn2
+    dev = torch.device("cuda:0")
+    eps = 1e-6
+
+    def norm_pass(x):
+        xf = x.float()
+        return (xf * torch.rsqrt((xf * xf).sum(-1, keepdim=True) + eps)).to(x.dtype)
+
+    res = {}
+    inp = make_gdn(B=8, T=4096, H=16, Dk=128, Dv=128, dtype="bf16", seed=1001, raw_qk=True)
+    q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
+    a, b = inp.alpha.to(dev), inp.beta.to(dev)
+    o = torch.empty((8, 4096, 16, 128), dtype=torch.float32, device=dev)
+    sf = torch.empty((8, 16, 128, 128), dtype=torch.float32, device=dev)
+    fused = lambda: gdr.gdr_chunk_fwd(q, k, v, a, b, None, out_dtype=torch.float32, o=o,
+                                      s_final=sf, l2norm_qk=True)
+    plain = lambda: gdr.gdr_chunk_fwd(q, k, v, a, b, None, out_dtype=torch.float32, o=o,
+                                      s_final=sf)
+    sep = lambda: gdr.gdr_chunk_fwd(norm_pass(q), norm_pass(k), v, a, b, None,
+                                    out_dtype=torch.float32, o=o, s_final=sf)
+    res["gdn"] = {n: time_launches(f, warmup, steps)[0] * 1e6
+                  for n, f in (("fused_us", fused), ("plain_us", plain), ("separate_pass_us", sep))}
+    del q, k, v, a, b, o, sf, inp
+    inp = make_gdn2(B=4, T=4096, H=16, Dk=128, Dv=128, dtype="bf16", seed=1004, raw_qk=True)
+    args = [x.to(dev) for x in (inp.q, inp.k, inp.v, inp.alpha, inp.erase, inp.write)]
+    o = torch.empty((4, 4096, 16, 128), dtype=torch.float32, device=dev)
+    sf = torch.empty((4, 16, 128, 128), dtype=torch.float32, device=dev)
+    fused = lambda: gdr.gdr2_chunk_fwd(*args, None, out_dtype=torch.float32, o=o, s_final=sf,
+                                       l2norm_qk=True)
+    plain = lambda: gdr.gdr2_chunk_fwd(*args, None, out_dtype=torch.float32, o=o, s_final=sf)
+    sep = lambda: gdr.gdr2_chunk_fwd(norm_pass(args[0]), norm_pass(args[1]), *args[2:], None,
+                                     out_dtype=torch.float32, o=o, s_final=sf)
+    res["gdr2"] = {n: time_launches(f, warmup, steps)[0] * 1e6
+                   for n, f in (("fused_us", fused), ("plain_us", plain), ("separate_pass_us", sep))}
+    return res
+
+
 def bench_copy(torch, warmup, steps, nbytes=512 << 20):
     """A plain device-to-device copy of known size: the achievable-bandwidth
     reference, and the kernel whose FETCH_SIZE / WRITE_SIZE counters scale
@@ -292,7 +338,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
-    ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "longctx", "copy"], default=None,
+    ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "longctx", "l2norm", "copy"],
+                    default=None,
                     help="time one operation only (for profiling)")
     ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarize rocprofv3 CSV output into OUT and the traffic JSON, then exit")
@@ -328,6 +375,9 @@ def main():
     if args.only in (None, "longctx"):
         log("timing gdr_chunk_fwd B1 H16 T32768 d128 (long context) ...")
         res["longctx"] = bench_longctx(gdr, torch, min(args.warmup, 10), min(args.steps, 10))
+    if args.only in (None, "l2norm"):
+        log("timing the fused q, k normalisation (GDN and GDN-2 workloads) ...")
+        res["l2norm"] = bench_l2norm(gdr, torch, min(args.warmup, 10), min(args.steps, 20))
     if args.only in (None, "copy"):
         log("timing a 512 MiB device copy ...")
         res["copy"] = bench_copy(torch, args.warmup, args.steps)
@@ -384,6 +434,11 @@ def main():
             "launch_us_min": r["min"] * 1e6, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
             "mfma_frac": r["flops"] / r["mean"] / 1e12 / BF16_PEAK_TFLOPS,
             "algorithmic_bytes_per_launch": r["bytes"]}
+    if "l2norm" in res:
+        out["l2norm"] = {"what": "launch us with raw q, k: fused GDR_L2NORM_QK, plain call "
+                                 "(no normalisation), separate PyTorch normalise pass + plain call",
+                         "gdn B8 H16 T4096": res["l2norm"]["gdn"],
+                         "gdr2 B4 H16 T4096": res["l2norm"]["gdr2"]}
     if "copy" in res:
         cp = res["copy"]
         out["copy_reference"] = {"what": "torch device-to-device copy, 512 MiB read + 512 MiB "

@@ -10,6 +10,9 @@ Functions mirror the C calls:
     gdr_chunk_fwd(q, k, v, alpha, beta, s0=None, ...)            -> (o, s_final)
     gdr_recurrent_step(q, k, v, alpha, beta, state, ...)         -> o
     gdr2_chunk_fwd(q, k, v, alpha, erase, write, s0=None, ...)   -> (o, s_final)
+
+``l2norm_qk=True`` calls the ``_ex`` variant of the same C function with
+GDR_L2NORM_QK: q and k are L2-normalised on load inside the kernels.
 """
 from __future__ import annotations
 
@@ -20,7 +23,7 @@ import torch  # loads the HIP runtime libgdr.so binds to
 
 __all__ = ["gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd",
            "GdrError", "status_string", "lib", "LIB_PATH", "GDR_F32",
-           "GDR_BF16"]
+           "GDR_BF16", "GDR_L2NORM_QK"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "libgdr.so")
@@ -33,7 +36,8 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 GDR_F32, GDR_BF16 = 0, 1
-_I64, _P, _E = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+GDR_L2NORM_QK = 1
+_I64, _P, _E, _U = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32
 
 lib.gdr_chunk_fwd.argtypes = [_I64] * 5 + [_E] + [_P] * 6 + [_E, _P, _P, _P]
 lib.gdr_chunk_fwd.restype = ctypes.c_int
@@ -41,6 +45,12 @@ lib.gdr2_chunk_fwd.argtypes = [_I64] * 5 + [_E] + [_P] * 7 + [_E, _P, _P, _P]
 lib.gdr2_chunk_fwd.restype = ctypes.c_int
 lib.gdr_recurrent_step.argtypes = [_I64] * 4 + [_E] + [_P] * 6 + [_E, _P, _P]
 lib.gdr_recurrent_step.restype = ctypes.c_int
+lib.gdr_chunk_fwd_ex.argtypes = [_I64] * 5 + [_E] + [_P] * 6 + [_E, _P, _P, _U, _P]
+lib.gdr_chunk_fwd_ex.restype = ctypes.c_int
+lib.gdr2_chunk_fwd_ex.argtypes = [_I64] * 5 + [_E] + [_P] * 7 + [_E, _P, _P, _U, _P]
+lib.gdr2_chunk_fwd_ex.restype = ctypes.c_int
+lib.gdr_recurrent_step_ex.argtypes = [_I64] * 4 + [_E] + [_P] * 6 + [_E, _P, _U, _P]
+lib.gdr_recurrent_step_ex.restype = ctypes.c_int
 lib.gdr_status_string.argtypes = [ctypes.c_int]
 lib.gdr_status_string.restype = ctypes.c_char_p
 lib.gdr_version.restype = ctypes.c_int
@@ -86,7 +96,7 @@ def _run(name, code):
 
 
 def gdr_chunk_fwd(q, k, v, alpha, beta, s0=None, *, out_dtype=None, o=None,
-                  s_final=None, want_state=True, stream=None):
+                  s_final=None, want_state=True, l2norm_qk=False, stream=None):
     """Chunkwise gated delta rule forward.
 
     q, k [B,T,H,Dk]; v [B,T,H,Dv] (fp32 or bf16, same dtype); alpha, beta
@@ -115,15 +125,18 @@ def gdr_chunk_fwd(q, k, v, alpha, beta, s0=None, *, out_dtype=None, o=None,
         s_final = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=q.device)
     if s_final is not None:
         _check("s_final", s_final, torch.float32, (B, H, Dv, Dk))
-    _run("gdr_chunk_fwd", lib.gdr_chunk_fwd(
-        B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v),
-        _ptr(alpha), _ptr(beta), _ptr(s0), _DT[odt], _ptr(o), _ptr(s_final),
-        _stream(stream)))
+    args = (B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v),
+            _ptr(alpha), _ptr(beta), _ptr(s0), _DT[odt], _ptr(o), _ptr(s_final))
+    if l2norm_qk:
+        _run("gdr_chunk_fwd_ex", lib.gdr_chunk_fwd_ex(*args, GDR_L2NORM_QK, _stream(stream)))
+    else:
+        _run("gdr_chunk_fwd", lib.gdr_chunk_fwd(*args, _stream(stream)))
     return o, s_final
 
 
 def gdr2_chunk_fwd(q, k, v, alpha, erase, write, s0=None, *, out_dtype=None,
-                   o=None, s_final=None, want_state=True, stream=None):
+                   o=None, s_final=None, want_state=True, l2norm_qk=False,
+                   stream=None):
     """Chunkwise Gated Delta Rule-2 forward.
 
     q, k, alpha, erase [B,T,H,Dk]; v, write [B,T,H,Dv], all one dtype (fp32
@@ -148,15 +161,18 @@ def gdr2_chunk_fwd(q, k, v, alpha, erase, write, s0=None, *, out_dtype=None,
         s_final = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=q.device)
     if s_final is not None:
         _check("s_final", s_final, torch.float32, (B, H, Dv, Dk))
-    _run("gdr2_chunk_fwd", lib.gdr2_chunk_fwd(
-        B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v),
-        _ptr(alpha), _ptr(erase), _ptr(write), _ptr(s0), _DT[odt], _ptr(o),
-        _ptr(s_final), _stream(stream)))
+    args = (B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v),
+            _ptr(alpha), _ptr(erase), _ptr(write), _ptr(s0), _DT[odt], _ptr(o),
+            _ptr(s_final))
+    if l2norm_qk:
+        _run("gdr2_chunk_fwd_ex", lib.gdr2_chunk_fwd_ex(*args, GDR_L2NORM_QK, _stream(stream)))
+    else:
+        _run("gdr2_chunk_fwd", lib.gdr2_chunk_fwd(*args, _stream(stream)))
     return o, s_final
 
 
 def gdr_recurrent_step(q, k, v, alpha, beta, state, *, out_dtype=None,
-                       o=None, stream=None):
+                       o=None, l2norm_qk=False, stream=None):
     """One decode token: q, k [N,H,Dk]; v [N,H,Dv]; alpha, beta [N,H] fp32;
     state [N,H,Dv,Dk] fp32, updated in place.  Returns o [N,H,Dv]."""
     N, H, Dk = q.shape
@@ -173,7 +189,11 @@ def gdr_recurrent_step(q, k, v, alpha, beta, state, *, out_dtype=None,
     if o is None:
         o = torch.empty((N, H, Dv), dtype=odt, device=q.device)
     _check("o", o, odt, (N, H, Dv))
-    _run("gdr_recurrent_step", lib.gdr_recurrent_step(
-        N, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-        _ptr(beta), _ptr(state), _DT[odt], _ptr(o), _stream(stream)))
+    args = (N, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+            _ptr(beta), _ptr(state), _DT[odt], _ptr(o))
+    if l2norm_qk:
+        _run("gdr_recurrent_step_ex", lib.gdr_recurrent_step_ex(
+            *args, GDR_L2NORM_QK, _stream(stream)))
+    else:
+        _run("gdr_recurrent_step", lib.gdr_recurrent_step(*args, _stream(stream)))
     return o

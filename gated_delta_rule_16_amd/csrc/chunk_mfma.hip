@@ -35,6 +35,14 @@
 //           solves T = (I + A)^{-1}, and B2 stages Q and V and computes P.
 //           Their global loads run two chunks further ahead, in registers.
 //
+// With GDR_L2NORM_QK (template flag NORM) q and k stay exact bf16 operands:
+// k_hat = rho k and q_hat = pi q enter as per-token factors on fp32 results.
+// rho_t = 1 / sqrt(|k_t|^2 + eps) comes from the diagonal of B3's Gram
+// tiles and multiplies A's rows and columns, FR2, FV and P's columns; pi_t
+// from the diagonal of B2's Q Q^T tiles multiplies P's rows and, through
+// the factor set, (Q S_hat^T)_t in o.  Both sums are exact bf16 products
+// accumulated in fp32 on the matrix cores.
+//
 // A period ends with one workgroup barrier.  LDS holds two sets of chunk
 // tiles (team A reads set c & 1 while team B writes the other), three of K
 // and the gate scan (chunk c mod 3), and two copies of A.
@@ -47,6 +55,8 @@
 // of tiles 0 and 1) directly usable as the next product's B operand, so the
 // state, R and V_new never leave registers.  Computed operands enter as bf16
 // hi/lo pairs (see mfma_common.h).
+#include <type_traits>
+
 #include "launch.h"
 #include "mfma_common.h"
 
@@ -76,9 +86,11 @@ struct Bf16Params {
 //   FV  = e^{g_C - g_t} / sigma' scales V_new_t in the update, sigma' the
 //                                next chunk's sigma (1 after a reset)
 // followed by the reset flag and the factor S_hat is multiplied by on a reset.
-enum { FR1 = 0, FR2 = CH, FO = 2 * CH, FV = 3 * CH, FRESET = 4 * CH, FMUL = 4 * CH + 1 };
+// With NORM, FPI = pi_t (1 / |q_t|) follows, written by B2.
+enum { FR1 = 0, FR2 = CH, FO = 2 * CH, FV = 3 * CH, FRESET = 4 * CH, FMUL = 4 * CH + 1,
+       FPI = 4 * CH + 4 };
 
-template <int DK, int RB>
+template <int DK, int RB, bool NORM>
 struct Lay {
     static constexpr int PV = RB == 64 ? 80 : 48;   // V row pitch: 8 or 24 banks apart
     // per set (chunk parity)
@@ -89,15 +101,16 @@ struct Lay {
     static constexpr int PH = TL + CH * P48 * 2;    // P hi, lo [32][P48] (columns kperm'd)
     static constexpr int PL = PH + CH * P48 * 2;
     static constexpr int G = PL + CH * P48 * 2;     // per-token factors
-    static constexpr int SET = G + (4 * CH + 4) * 4;
+    static constexpr int SET = G + (NORM ? 5 * CH + 4 : 4 * CH + 4) * 4;
     // per chunk mod 3: K twice -- in operand order (swizzled) for the
     // products over the key dim, and row-major [32][DK + 16] for the
-    // transposed reads -- and the gate scan (g, beta)
+    // transposed reads -- and the gate scan (g, beta, with NORM rho)
     static constexpr int PKN = DK + 16;
+    static constexpr int GRS = (NORM ? 3 : 2) * CH * 4;
     static constexpr int KSLOT = CH * DK * 2 + CH * PKN * 2;
     static constexpr int KR = 2 * SET;
     static constexpr int GR = KR + 3 * KSLOT;
-    static constexpr int AF = GR + 3 * 2 * CH * 4;  // A fp32 [32][P36], two copies
+    static constexpr int AF = GR + 3 * GRS;         // A fp32 [32][P36], two copies
     static constexpr int TF = AF + 2 * CH * P36 * 4;   // B1 private: T fp32 [32][P36]
     static constexpr int TOTAL = TF + CH * P36 * 4;
     static_assert(SET % 16 == 0 && (CH * PV * 2) % 16 == 0, "alignment");
@@ -134,9 +147,9 @@ __device__ __forceinline__ void st8(bf16_t* p, const uint2& x) {
     *reinterpret_cast<uint2*>(p) = x;
 }
 
-template <int DK, int DV, int RB, typename TOut>
+template <int DK, int DV, int RB, typename TOut, bool NORM>
 __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Params p) {
-    using L = Lay<DK, RB>;
+    using L = Lay<DK, RB, NORM>;
     constexpr int NA = RB / 16;   // team A waves
     constexpr int KJ = DK / 32;   // 32-deep contraction steps over the key dim
     constexpr int NS = DK / 16;   // S^T tiles per team A wave
@@ -174,7 +187,7 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
         return reinterpret_cast<bf16_t*>(smem + L::KR + (int)(c % 3) * L::KSLOT);
     };
     auto gring = [&](int64_t c) {
-        return reinterpret_cast<float*>(smem + L::GR + (int)(c % 3) * 2 * CH * 4);
+        return reinterpret_cast<float*>(smem + L::GR + (int)(c % 3) * L::GRS);
     };
 
     // T and P vanish above their diagonal 16x16 blocks (rows 0..15,
@@ -317,6 +330,7 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                 ph[rt] = *reinterpret_cast<const bf16x8*>(Ph + at);
                 pl[rt] = *reinterpret_cast<const bf16x8*>(Pl + at);
                 fo[rt] = *reinterpret_cast<const f32x4*>(G + FO + 16 * rt + 4 * g);
+                if constexpr (NORM) fo[rt] *= *reinterpret_cast<const f32x4*>(G + FPI + 16 * rt + 4 * g);
                 fv[rt] = *reinterpret_cast<const f32x4*>(G + FV + 16 * rt + 4 * g);
             }
 #pragma unroll
@@ -433,18 +447,26 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
             }
     };
     // g and beta of the chunk's tokens from the gate ring: gq, bq for tokens
-    // 16 rt + m; gk for tokens 16 st + 4 g .. + 3
+    // 16 rt + m; gk for tokens 16 st + 4 g .. + 3; with NORM rho of the
+    // same tokens in rq and rk (1 otherwise)
     struct Gates {
-        float gq[2], bq[2];
-        f32x4 gk[2];
+        float gq[2], bq[2], rq[2];
+        f32x4 gk[2], rk[2];
     };
-    auto read_gates = [&](const float* gr) {
+    auto read_gates = [&](const float* gr, auto rhoc) {
+        constexpr bool RHO = decltype(rhoc)::value;
         Gates z;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             z.gq[u] = gr[16 * u + m];
             z.bq[u] = gr[CH + 16 * u + m];
             z.gk[u] = *reinterpret_cast<const f32x4*>(gr + 16 * u + 4 * g);
+            z.rq[u] = 1.f;
+            z.rk[u] = f32x4{1.f, 1.f, 1.f, 1.f};
+            if constexpr (RHO) {
+                z.rq[u] = gr[2 * CH + 16 * u + m];
+                z.rk[u] = *reinterpret_cast<const f32x4*>(gr + 2 * CH + 16 * u + 4 * g);
+            }
         }
         return z;
     };
@@ -491,6 +513,7 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
             const float* gr = gring(cn);
             float* G = reinterpret_cast<float*>(setp(cn, L::G));
             const float gx = gr[lane & 31], be = gr[CH + (lane & 31)];
+            const float rho = NORM ? gr[2 * CH + (lane & 31)] : 1.f;
             const float gC = gr[CH - 1];
             // sigma' = sigma gamma_C; a reset keeps S_hat = S from here on.
             // The last chunk always resets so that the final S_hat is S.
@@ -500,9 +523,9 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
             const float dec = __expf(gC - gx);
             if (lane < CH) {
                 G[FR1 + lane] = be;
-                G[FR2 + lane] = be * fo;
+                G[FR2 + lane] = be * fo * rho;
                 G[FO + lane] = fo;
-                G[FV + lane] = reset ? dec : dec / s1;
+                G[FV + lane] = (reset ? dec : dec / s1) * rho;
             }
             if (lane == 0) {
                 G[FRESET] = reset ? 1.f : 0.f;
@@ -631,13 +654,38 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                     kf[tt][j] = *reinterpret_cast<const bf16x8*>(Kb + kq_at<DK>(row, 32 * j + 8 * g));
                     qf[tt][j] = *reinterpret_cast<const bf16x8*>(Qb + kq_at<DK>(row, 32 * j + 8 * g));
                 }
-            const Gates z = read_gates(gring(cn));
-            f32x4 acc[3] = {};
+            const float* grc = gring(cn);
+            const Gates z = read_gates(grc, std::false_type{});
+            f32x4 acc[3] = {}, qq[2] = {};
 #pragma unroll
             for (int j = 0; j < KJ; ++j) {
                 acc[0] = mfma16(kf[0][j], qf[0][j], acc[0]);
                 acc[1] = mfma16(kf[0][j], qf[1][j], acc[1]);
                 acc[2] = mfma16(kf[1][j], qf[1][j], acc[2]);
+                if constexpr (NORM) {
+                    // diagonal tiles of Q Q^T: |q|^2 of the chunk's rows
+                    qq[0] = mfma16(qf[0][j], qf[0][j], qq[0]);
+                    qq[1] = mfma16(qf[1][j], qf[1][j], qq[1]);
+                }
+            }
+            // pi of rows 16 rt + m: |q_{16 rt + m}|^2 sits in register
+            // m - 4 g of the diagonal tile on the lane with g = m / 4; one
+            // bpermute hands it to the row's other lane groups
+            float pq[2] = {1.f, 1.f};
+            if constexpr (NORM) {
+                const int dr = m & 3;
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    float d = qq[tt][0];
+#pragma unroll
+                    for (int r = 1; r < 4; ++r) d = dr == r ? qq[tt][r] : d;
+                    pq[tt] = l2_inv(__shfl(d, 16 * (m >> 2) + m, 64));
+                }
+                if (g == 0) {
+                    float* G = reinterpret_cast<float*>(setp(cn, L::G));
+                    G[FPI + m] = pq[0];
+                    G[FPI + 16 + m] = pq[1];
+                }
             }
 #pragma unroll
             for (int u = 0; u < 3; ++u) {
@@ -648,6 +696,7 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                 for (int r = 0; r < 4; ++r) {
                     const int s = 16 * st + 4 * g + r;
                     pv[r] = s <= rp ? __expf(fminf(z.gq[rt] - z.gk[st][r], 0.f)) * acc[u][r] : 0.f;
+                    if constexpr (NORM) pv[r] *= pq[rt] * grc[2 * CH + s];
                 }
                 uint2 vh, vl;
                 split2(pv[0], pv[1], vh.x, vl.x);
@@ -700,8 +749,23 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                 gr[lane] = gx;
                 gr[CH + lane] = live ? f.be : 0.f;
             }
+            if constexpr (NORM) {
+                // |k_m|^2 and |k_{16 + m}|^2 sit in register m - 4 g of the
+                // diagonal tiles on the lanes with g = m / 4
+                const int dr = m & 3;
+                float d0 = acc[0][0], d1 = acc[2][0];
+#pragma unroll
+                for (int r = 1; r < 4; ++r) {
+                    d0 = dr == r ? acc[0][r] : d0;
+                    d1 = dr == r ? acc[2][r] : d1;
+                }
+                if ((m >> 2) == g) {
+                    gr[2 * CH + m] = l2_inv(d0);
+                    gr[2 * CH + 16 + m] = l2_inv(d1);
+                }
+            }
             wave_lds_sync();
-            const Gates z = read_gates(gr);
+            const Gates z = read_gates(gr, std::bool_constant<NORM>{});
 #pragma unroll
             for (int u = 0; u < 3; ++u) {
                 const int st = u == 2 ? 1 : 0, rt = u == 0 ? 0 : 1;
@@ -712,6 +776,7 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                     const int s = 16 * st + 4 * g + r;
                     av[r] = s < rp ? z.bq[rt] * __expf(fminf(z.gq[rt] - z.gk[st][r], 0.f)) * acc[u][r]
                                    : 0.f;
+                    if constexpr (NORM) av[r] *= z.rq[rt] * z.rk[st][r];
                 }
                 *reinterpret_cast<f32x4*>(Af + rp * P36 + 16 * st + 4 * g) = av;
             }
@@ -721,8 +786,8 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
     }
 }
 
-template <int DK, int DV, int RB, typename TOut>
-hipError_t launch_bf16_t(const ChunkArgs& a) {
+template <int DK, int DV, int RB, typename TOut, bool NORM>
+hipError_t launch_bf16_n(const ChunkArgs& a) {
     Bf16Params p;
     p.T = a.T;
     p.H = a.H;
@@ -735,8 +800,8 @@ hipError_t launch_bf16_t(const ChunkArgs& a) {
     p.s0 = a.s0;
     p.o = a.o;
     p.s_final = a.s_final;
-    const size_t lds = Lay<DK, RB>::TOTAL;
-    auto fn = chunk_bf16_kernel<DK, DV, RB, TOut>;
+    const size_t lds = Lay<DK, RB, NORM>::TOTAL;
+    auto fn = chunk_bf16_kernel<DK, DV, RB, TOut, NORM>;
     hipError_t e =
         hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -744,6 +809,12 @@ hipError_t launch_bf16_t(const ChunkArgs& a) {
     const unsigned grid = (unsigned)(((a.B * a.H + 7) / 8) * 8 * (DV / RB));
     hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * (RB / 16 + NB)), lds, a.stream, p);
     return hipGetLastError();
+}
+
+template <int DK, int DV, int RB, typename TOut>
+hipError_t launch_bf16_t(const ChunkArgs& a) {
+    return a.l2norm ? launch_bf16_n<DK, DV, RB, TOut, true>(a)
+                    : launch_bf16_n<DK, DV, RB, TOut, false>(a);
 }
 
 template <int DK, int DV>

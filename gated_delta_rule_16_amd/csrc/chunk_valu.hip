@@ -45,6 +45,7 @@ struct F32Params {
     const float* s0;
     void* o;
     float* s_final;
+    bool l2norm;
 };
 
 template <int DK>
@@ -140,6 +141,30 @@ __global__ __launch_bounds__(NT) void chunk_f32_kernel(F32Params p) {
             be[r] = r < n ? p.beta[off] : 0.f;
         }
         __syncthreads();
+        // ---- GDR_L2NORM_QK: unit-norm q and k rows (and e = b k with k) --
+        //      eight lanes per row; rows past n stay zero.  Only the rows'
+        //      own lanes touch them, and the next reads follow the barrier
+        //      after the decay scan.
+        if (p.l2norm) {
+            static_assert(NT == 8 * C, "eight lanes per row");
+            const int r = tid >> 3, part = tid & 7;
+            float sk = 0.f, sq = 0.f;
+            for (int j = part; j < DK; j += 8) {
+                sk += Ks[r * L::PK + j] * Ks[r * L::PK + j];
+                sq += Qs[r * L::PK + j] * Qs[r * L::PK + j];
+            }
+#pragma unroll
+            for (int msk = 1; msk < 8; msk <<= 1) {
+                sk += __shfl_xor(sk, msk, 64);
+                sq += __shfl_xor(sq, msk, 64);
+            }
+            const float rk = l2_inv(sk), rq = l2_inv(sq);
+            for (int j = part; j < DK; j += 8) {
+                Ks[r * L::PK + j] *= rk;
+                Qs[r * L::PK + j] *= rq;
+                if (G2) Es[r * L::PK + j] *= rk;
+            }
+        }
         // ---- cumulative log decay ----------------------------------------
         if (G2) {
             if (tid < DK) {
@@ -289,6 +314,7 @@ hipError_t launch_f32_t(const ChunkArgs& a) {
     p.s0 = a.s0;
     p.o = a.o;
     p.s_final = a.s_final;
+    p.l2norm = a.l2norm;
     const size_t lds = sizeof(float) * Lds<DK>::TOTAL;
     auto fn = chunk_f32_kernel<DK, DV, G2, TOut>;
     hipError_t e = hipFuncSetAttribute((const void*)fn,

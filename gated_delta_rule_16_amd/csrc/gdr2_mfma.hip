@@ -40,6 +40,11 @@
 //            AP-A (wave 2): A = E K'^T for chunk c + 2 (or the wide-chunk
 //                 path), T = (I + A)^{-1} for chunk c + 1;
 //            AP-P (wave 3), chunk c + 1: P = Q K'^T, w (.) v.
+// With GDR_L2NORM_QK (template flag NORM) the E waves also sum k_t^2 and
+// q_t^2 over the channels (fp32 per lane, then across the wave) and fold
+// rho_t = 1 / |k_t| into E and K', pi_t = 1 / |q_t| into Q, before those are
+// rounded; rho and pi go to the elementwise set for the wide-chunk path,
+// which reads the raw inputs.
 // One workgroup barrier closes each period; LDS keeps four sets of the
 // elementwise operands (chunk mod 4) and two of A, T, P and w (.) v.
 //
@@ -82,7 +87,7 @@ struct Gdr2Params {
     float* s_final;
 };
 
-template <int DK>
+template <int DK, bool NORM>
 struct Lay2 {
     static constexpr int PKN = DK + 16;            // K' row pitch (elements)
     // elementwise operands, chunk mod 4
@@ -92,7 +97,8 @@ struct Lay2 {
     static constexpr int KH = QL + CH * DK * 2;     // K' hi, lo [16][PKN], natural order
     static constexpr int KL = KH + CH * PKN * 2;
     static constexpr int LC = KL + CH * PKN * 2;    // lambda_C [DK] fp32, then the wide flag
-    static constexpr int ESET = LC + DK * 4 + 16;
+    static constexpr int NR = LC + DK * 4 + 16;     // NORM: rho [16], pi [16] fp32
+    static constexpr int ESET = NR + (NORM ? 2 * CH * 4 : 0);
     // T, P, w . v, chunk mod 2
     static constexpr int TH = 0;                    // T [16][P24] bf16
     static constexpr int PH = TH + CH * P24 * 2;    // P hi, lo [16][P24]
@@ -153,9 +159,24 @@ __device__ __forceinline__ bf16x8 cat44(const s16x4& a, const s16x4& b) {
 __device__ __forceinline__ float lo_bf(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-template <int DK, int DV, typename TOut>
+// Sum over the key channels of one token when lane l holds channel pair
+// l mod (DK / 2): the 16 lanes of each row by DPP (quad swaps, then the
+// half-row and row mirrors), then across rows; at DK = 64 lanes 32..63
+// repeat lanes 0..31 and the last step is skipped.  Every lane gets the sum.
+template <int DK>
+__device__ __forceinline__ float key_sum(float x) {
+    x += dpp_mov<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    x += dpp_mov<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    x += dpp_mov<0x141>(x);   // row_half_mirror
+    x += dpp_mov<0x140>(x);   // row_mirror
+    x += __shfl_xor(x, 16, 64);
+    if constexpr (DK == 128) x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+template <int DK, int DV, typename TOut, bool NORM>
 __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
-    using L = Lay2<DK>;
+    using L = Lay2<DK, NORM>;
     constexpr int KJ = DK / 32;   // 32-deep contraction steps over the key dim
     constexpr int NS = DK / 16;   // S^T tiles per team A wave
     constexpr int NRB = DV / RB;
@@ -400,9 +421,14 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
             bf16_t* Kl = bfp(es, L::KL);
 #pragma unroll
             for (int t = 0; t < CH; ++t) {
+                float k0 = lo_bf(kk[t]), k1 = hi_bf(kk[t]);
+                if constexpr (NORM) {
+                    const float rho = reinterpret_cast<const float*>(es + L::NR)[t];
+                    k0 *= rho;
+                    k1 *= rho;
+                }
                 uint32_t xh, xl;
-                split2(lo_bf(kk[t]) * __expf(g0[CH - 1] - g0[t]),
-                       hi_bf(kk[t]) * __expf(g1[CH - 1] - g1[t]), xh, xl);
+                split2(k0 * __expf(g0[CH - 1] - g0[t]), k1 * __expf(g1[CH - 1] - g1[t]), xh, xl);
                 *reinterpret_cast<uint32_t*>(Kh + t * L::PKN + 2 * cp) = xh;
                 *reinterpret_cast<uint32_t*>(Kl + t * L::PKN + 2 * cp) = xl;
             }
@@ -418,6 +444,11 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                         pv += bf2f(Fq[r * DK + c]) * ks;
                         av += bf2f(Fb[r * DK + c]) * bf2f(Fk[r * DK + c]) * ks;
                     }
+                }
+                if constexpr (NORM) {
+                    const float* nr = reinterpret_cast<const float*>(es + L::NR);
+                    av *= nr[r] * nr[s];
+                    pv *= nr[CH + r] * nr[s];
                 }
                 Af[r * PAF + s] = s < r ? av : 0.f;
                 Wp[r * PAF + s] = pv;
@@ -591,6 +622,35 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                         l1 *= hi_bf(f.a[t]);
                     }
                 }
+                // rho, pi of this wave's tokens (rows past the end read 0)
+                float rho[NT], pin[NT];
+#pragma unroll
+                for (int u = 0; u < NT; ++u) {
+                    rho[u] = 1.f;
+                    pin[u] = 1.f;
+                }
+                if constexpr (NORM) {
+#pragma unroll
+                    for (int u = 0; u < NT; ++u) {
+                        const float k0 = lo_bf(f.k[u]), k1 = hi_bf(f.k[u]);
+                        const float q0 = lo_bf(f.q[u]), q1 = hi_bf(f.q[u]);
+                        rho[u] = key_sum<DK>(__builtin_fmaf(k1, k1, k0 * k0));
+                        pin[u] = key_sum<DK>(__builtin_fmaf(q1, q1, q0 * q0));
+                    }
+#pragma unroll
+                    for (int u = 0; u < NT; ++u) {
+                        rho[u] = l2_inv(rho[u]);
+                        pin[u] = l2_inv(pin[u]);
+                    }
+                    if (lane == 0) {
+                        float* nr = reinterpret_cast<float*>(es + L::NR);
+#pragma unroll
+                        for (int u = 0; u < NT; ++u) {
+                            nr[T0 + u] = rho[u];
+                            nr[CH + T0 + u] = pin[u];
+                        }
+                    }
+                }
 #pragma unroll
                 for (int u = 0; u < NT; ++u) {
                     const int t = T0 + u;
@@ -600,13 +660,20 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                         l1 *= hi_bf(f.a[t]);
                     }
                     const float r0 = __builtin_amdgcn_rcpf(l0), r1 = __builtin_amdgcn_rcpf(l1);
-                    const float k0 = lo_bf(f.k[u]), k1 = hi_bf(f.k[u]);
+                    float k0 = lo_bf(f.k[u]), k1 = hi_bf(f.k[u]);
+                    if constexpr (NORM) {
+                        k0 *= rho[u];
+                        k1 *= rho[u];
+                    }
                     const float e0 = lv ? lo_bf(f.b[u]) * k0 : 0.f;
                     const float e1 = lv ? hi_bf(f.b[u]) * k1 : 0.f;
                     const int ot = kq_at<DK>(t, pc);
                     *reinterpret_cast<uint32_t*>(bfp(es, L::EH) + ot) = cvt_pk(e0 * l0, e1 * l1);
                     uint32_t xh, xl;
-                    split2(lo_bf(f.q[u]) * l0, hi_bf(f.q[u]) * l1, xh, xl);
+                    if constexpr (NORM)
+                        split2(lo_bf(f.q[u]) * pin[u] * l0, hi_bf(f.q[u]) * pin[u] * l1, xh, xl);
+                    else
+                        split2(lo_bf(f.q[u]) * l0, hi_bf(f.q[u]) * l1, xh, xl);
                     *reinterpret_cast<uint32_t*>(bfp(es, L::QH) + ot) = xh;
                     *reinterpret_cast<uint32_t*>(bfp(es, L::QL) + ot) = xl;
                     split2(k0 * r0, k1 * r1, xh, xl);
@@ -641,8 +708,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
     }
 }
 
-template <int DK, int DV, typename TOut>
-hipError_t launch_t(const ChunkArgs& a) {
+template <int DK, int DV, typename TOut, bool NORM>
+hipError_t launch_n(const ChunkArgs& a) {
     Gdr2Params p;
     p.T = a.T;
     p.H = a.H;
@@ -656,8 +723,8 @@ hipError_t launch_t(const ChunkArgs& a) {
     p.s0 = a.s0;
     p.o = a.o;
     p.s_final = a.s_final;
-    const size_t lds = Lay2<DK>::TOTAL;
-    auto fn = gdr2_bf16_kernel<DK, DV, TOut>;
+    const size_t lds = Lay2<DK, NORM>::TOTAL;
+    auto fn = gdr2_bf16_kernel<DK, DV, TOut, NORM>;
     hipError_t e =
         hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -665,6 +732,11 @@ hipError_t launch_t(const ChunkArgs& a) {
     const unsigned grid = (unsigned)(((a.B * a.H + 7) / 8) * 8 * (DV / RB));
     hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * NWAVE), lds, a.stream, p);
     return hipGetLastError();
+}
+
+template <int DK, int DV, typename TOut>
+hipError_t launch_t(const ChunkArgs& a) {
+    return a.l2norm ? launch_n<DK, DV, TOut, true>(a) : launch_n<DK, DV, TOut, false>(a);
 }
 
 template <int DK, int DV>

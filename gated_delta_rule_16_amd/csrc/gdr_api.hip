@@ -24,6 +24,8 @@ bool dims_ok(int64_t dk, int64_t dv) {
 
 bool dtype_ok(gdr_dtype_t d) { return d == GDR_F32 || d == GDR_BF16; }
 
+bool flags_ok(uint32_t f) { return (f & ~GDR_L2NORM_QK) == 0; }
+
 gdr_status_t from_hip(hipError_t e) { return e == hipSuccess ? GDR_OK : GDR_ERR_DEVICE; }
 
 // Every listed pointer must be non-NULL and 16-byte aligned.
@@ -96,12 +98,13 @@ static gdr_status_t chunk_run(ChunkArgs& a) {
     return from_hip(e);
 }
 
-extern "C" gdr_status_t gdr_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
-                                      int64_t Dv, gdr_dtype_t in_dt, const void* q,
-                                      const void* k, const void* v, const float* alpha,
-                                      const float* beta, const float* s0,
-                                      gdr_dtype_t out_dt, void* o, float* s_final,
-                                      hipStream_t stream) {
+extern "C" gdr_status_t gdr_chunk_fwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                         int64_t Dv, gdr_dtype_t in_dt, const void* q,
+                                         const void* k, const void* v, const float* alpha,
+                                         const float* beta, const float* s0,
+                                         gdr_dtype_t out_dt, void* o, float* s_final,
+                                         uint32_t flags, hipStream_t stream) {
+    if (!flags_ok(flags)) return GDR_ERR_UNSUPPORTED;
     ChunkArgs a{};
     gdr_status_t st = chunk_common(B, T, H, Dk, Dv, in_dt, out_dt, a);
     if (st != GDR_OK) return st;
@@ -111,6 +114,7 @@ extern "C" gdr_status_t gdr_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t D
         return GDR_ERR_INVALID;
     if (!opt_ok(s0) || !opt_ok(s_final)) return GDR_ERR_INVALID;
     a.gated2 = false;
+    a.l2norm = (flags & GDR_L2NORM_QK) != 0;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -123,12 +127,23 @@ extern "C" gdr_status_t gdr_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t D
     return chunk_run(a);
 }
 
-extern "C" gdr_status_t gdr2_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
-                                       int64_t Dv, gdr_dtype_t in_dt, const void* q,
-                                       const void* k, const void* v, const void* alpha,
-                                       const void* erase, const void* write,
-                                       const float* s0, gdr_dtype_t out_dt, void* o,
-                                       float* s_final, hipStream_t stream) {
+extern "C" gdr_status_t gdr_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                      int64_t Dv, gdr_dtype_t in_dt, const void* q,
+                                      const void* k, const void* v, const float* alpha,
+                                      const float* beta, const float* s0,
+                                      gdr_dtype_t out_dt, void* o, float* s_final,
+                                      hipStream_t stream) {
+    return gdr_chunk_fwd_ex(B, T, H, Dk, Dv, in_dt, q, k, v, alpha, beta, s0, out_dt, o,
+                            s_final, 0u, stream);
+}
+
+extern "C" gdr_status_t gdr2_chunk_fwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                          int64_t Dv, gdr_dtype_t in_dt, const void* q,
+                                          const void* k, const void* v, const void* alpha,
+                                          const void* erase, const void* write,
+                                          const float* s0, gdr_dtype_t out_dt, void* o,
+                                          float* s_final, uint32_t flags, hipStream_t stream) {
+    if (!flags_ok(flags)) return GDR_ERR_UNSUPPORTED;
     ChunkArgs a{};
     gdr_status_t st = chunk_common(B, T, H, Dk, Dv, in_dt, out_dt, a);
     if (st != GDR_OK) return st;
@@ -138,6 +153,7 @@ extern "C" gdr_status_t gdr2_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t 
         return GDR_ERR_INVALID;
     if (!opt_ok(s0) || !opt_ok(s_final)) return GDR_ERR_INVALID;
     a.gated2 = true;
+    a.l2norm = (flags & GDR_L2NORM_QK) != 0;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -151,11 +167,23 @@ extern "C" gdr_status_t gdr2_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t 
     return chunk_run(a);
 }
 
-extern "C" gdr_status_t gdr_recurrent_step(int64_t N, int64_t H, int64_t Dk, int64_t Dv,
-                                           gdr_dtype_t in_dt, const void* q, const void* k,
-                                           const void* v, const float* alpha,
-                                           const float* beta, float* state,
-                                           gdr_dtype_t out_dt, void* o, hipStream_t stream) {
+extern "C" gdr_status_t gdr2_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                       int64_t Dv, gdr_dtype_t in_dt, const void* q,
+                                       const void* k, const void* v, const void* alpha,
+                                       const void* erase, const void* write,
+                                       const float* s0, gdr_dtype_t out_dt, void* o,
+                                       float* s_final, hipStream_t stream) {
+    return gdr2_chunk_fwd_ex(B, T, H, Dk, Dv, in_dt, q, k, v, alpha, erase, write, s0, out_dt,
+                             o, s_final, 0u, stream);
+}
+
+extern "C" gdr_status_t gdr_recurrent_step_ex(int64_t N, int64_t H, int64_t Dk, int64_t Dv,
+                                              gdr_dtype_t in_dt, const void* q, const void* k,
+                                              const void* v, const float* alpha,
+                                              const float* beta, float* state,
+                                              gdr_dtype_t out_dt, void* o, uint32_t flags,
+                                              hipStream_t stream) {
+    if (!flags_ok(flags)) return GDR_ERR_UNSUPPORTED;
     if (N < 0 || H < 0 || Dk < 0 || Dv < 0) return GDR_ERR_INVALID;
     if (!sizes_ok(N, H, 1) || N * H > 0x7fffffffLL) return GDR_ERR_INVALID;
     if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return GDR_ERR_UNSUPPORTED;
@@ -171,6 +199,7 @@ extern "C" gdr_status_t gdr_recurrent_step(int64_t N, int64_t H, int64_t Dk, int
     a.Dv = Dv;
     a.in_bf16 = in_dt == GDR_BF16;
     a.out_bf16 = out_dt == GDR_BF16;
+    a.l2norm = (flags & GDR_L2NORM_QK) != 0;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -182,14 +211,23 @@ extern "C" gdr_status_t gdr_recurrent_step(int64_t N, int64_t H, int64_t Dk, int
     return from_hip(launch_step(a));
 }
 
+extern "C" gdr_status_t gdr_recurrent_step(int64_t N, int64_t H, int64_t Dk, int64_t Dv,
+                                           gdr_dtype_t in_dt, const void* q, const void* k,
+                                           const void* v, const float* alpha,
+                                           const float* beta, float* state,
+                                           gdr_dtype_t out_dt, void* o, hipStream_t stream) {
+    return gdr_recurrent_step_ex(N, H, Dk, Dv, in_dt, q, k, v, alpha, beta, state, out_dt, o,
+                                 0u, stream);
+}
+
 extern "C" const char* gdr_status_string(gdr_status_t s) {
     switch (s) {
         case GDR_OK: return "ok";
         case GDR_ERR_INVALID: return "invalid argument (NULL or misaligned pointer, or bad size)";
-        case GDR_ERR_UNSUPPORTED: return "unsupported head dims or dtype";
+        case GDR_ERR_UNSUPPORTED: return "unsupported head dims, dtype or flags";
         case GDR_ERR_DEVICE: return "HIP runtime error at launch";
     }
     return "unknown status";
 }
 
-extern "C" int gdr_version(void) { return 100; }
+extern "C" int gdr_version(void) { return 200; }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/gdr.h"
+
 namespace gdr {
 
 typedef uint16_t bf16_t;  // bfloat16 storage (upper half of an fp32)
@@ -45,5 +47,9 @@ template <> struct io<bf16_t> {
 __device__ __forceinline__ float safe_log(float a) {
     return fmaxf(logf(fmaxf(a, 1.17549435e-38f)), kLogFltMin);
 }
+
+// Scale that L2-normalises a q or k row with sum of squares ss
+// (GDR_L2NORM_QK): x_hat = x / sqrt(ss + eps).
+__device__ __forceinline__ float l2_inv(float ss) { return rsqrtf(ss + GDR_L2NORM_EPS); }
 
 }  // namespace gdr

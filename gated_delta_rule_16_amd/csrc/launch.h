@@ -10,6 +10,7 @@ namespace gdr {
 struct StepArgs {
     int64_t N, H, Dk, Dv;
     bool in_bf16, out_bf16;
+    bool l2norm;            // normalise q, k on load (GDR_L2NORM_QK)
     const void *q, *k, *v;
     const float *alpha, *beta;
     float* state;
@@ -25,6 +26,7 @@ struct ChunkArgs {
     int64_t B, T, H, Dk, Dv;
     bool in_bf16, out_bf16;
     bool gated2;
+    bool l2norm;            // normalise q, k on load (GDR_L2NORM_QK)
     const void *q, *k, *v;
     const void *alpha, *beta, *erase, *write;
     const float* s0;

@@ -21,7 +21,9 @@
 //   * the two row dot products are reduced across the Dk/4 lanes of a row
 //     with xor shuffles that never leave the row's lane group;
 //   * state traffic uses non-temporal loads and stores: every byte is
-//     touched exactly once per call.
+//     touched exactly once per call;
+//   * with GDR_L2NORM_QK, q and k are scaled by 1 / norm after the load;
+//     their sums of squares take the same in-row reduction as the dots.
 #include "gdr_device.h"
 #include "launch.h"
 
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(256) void step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, float* __restrict__ state,
-    TOut* __restrict__ o) {
+    TOut* __restrict__ o, bool l2norm) {
     constexpr int LPR = DK / 4;               // lanes per row
     constexpr int RPP = 64 / LPR;             // rows per wave access
     constexpr int ROWS_W = DV / 4;            // rows per wave
@@ -74,6 +76,17 @@ __global__ __launch_bounds__(256) void step_kernel(
     for (int p = 0; p < PASSES; ++p)
         vv[p] = io<TIn>::ld(v + head * DV + row0 + p * RPP);
 
+    if (l2norm) {
+        const float rk = l2_inv(row_sum<LPR>(kk[0] * kk[0] + kk[1] * kk[1] +
+                                             kk[2] * kk[2] + kk[3] * kk[3]));
+        const float rq = l2_inv(row_sum<LPR>(qq[0] * qq[0] + qq[1] * qq[1] +
+                                             qq[2] * qq[2] + qq[3] * qq[3]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            kk[j] *= rk;
+            qq[j] *= rq;
+        }
+    }
     const float kq = row_sum<LPR>(kk[0] * qq[0] + kk[1] * qq[1] +
                                   kk[2] * qq[2] + kk[3] * qq[3]);
 
@@ -99,7 +112,7 @@ template <int DK, int DV, typename TIn, typename TOut>
 static hipError_t launch_step_t(const StepArgs& a) {
     hipLaunchKernelGGL((step_kernel<DK, DV, TIn, TOut>), dim3((unsigned)(a.N * a.H)),
                        dim3(256), 0, a.stream, (const TIn*)a.q, (const TIn*)a.k,
-                       (const TIn*)a.v, a.alpha, a.beta, a.state, (TOut*)a.o);
+                       (const TIn*)a.v, a.alpha, a.beta, a.state, (TOut*)a.o, a.l2norm);
     return hipGetLastError();
 }
 

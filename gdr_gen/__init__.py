@@ -13,7 +13,11 @@ meaningful96.github.io GDN review, section 4.2, for head dim 128):
 * ``numpy.random.Generator(PCG64(seed))``; draws in a fixed order
   q, k, v, gate noise(s), initial state.
 * q, k ~ N(0, 1) then L2-normalised per (token, head) in fp64 (the block's
-  L2 step, review section 3.8); v ~ N(0, 1).
+  L2 step, review section 3.8); v ~ N(0, 1).  With ``raw_qk=True`` (inputs
+  for the kernels' own L2 normalisation) q and k are instead left as drawn
+  and each (token, head) row is scaled by exp(U(log 0.05, log 20)); those
+  scales are drawn after everything else, so the other tensors keep their
+  values.
 * GDN scalar gates: alpha = exp(-softplus(x + shift)) with x ~ N(0, 1),
   beta = sigmoid(N(0, 1)).  GDN-2 gates: per-channel alpha of the same form,
   erase b and write w = sigmoid(N(0, 1)).
@@ -50,6 +54,16 @@ def _unit_rows(x: np.ndarray) -> np.ndarray:
     # L2-normalise the last axis in fp64.  N(0,1) vectors of dim >= 8 are
     # never near zero, so no epsilon is added.
     return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+
+
+def _qk(g: np.random.Generator, q: np.ndarray, k: np.ndarray, raw: bool):
+    # called after every other draw of a generator
+    if not raw:
+        return _unit_rows(q), _unit_rows(k)
+    lo, hi = np.log(0.05), np.log(20.0)
+    sq = np.exp(g.uniform(lo, hi, q.shape[:-1] + (1,)))
+    sk = np.exp(g.uniform(lo, hi, k.shape[:-1] + (1,)))
+    return q * sq, k * sk
 
 
 def _softplus(x: np.ndarray) -> np.ndarray:
@@ -108,31 +122,35 @@ class DecodeInputs:
 
 def make_gdn(B: int, T: int, H: int, Dk: int, Dv: int, dtype: str = "bf16",
              seed: int = 0, alpha_shift: float = 2.0,
-             s0_std: Optional[float] = None, name: str = "") -> GdnInputs:
+             s0_std: Optional[float] = None, name: str = "",
+             raw_qk: bool = False) -> GdnInputs:
     """Scalar-gated inputs; alpha = exp(-softplus(N(0,1) + alpha_shift))."""
     g = _rng(seed)
-    q = _unit_rows(g.standard_normal((B, T, H, Dk)))
-    k = _unit_rows(g.standard_normal((B, T, H, Dk)))
+    q = g.standard_normal((B, T, H, Dk))
+    k = g.standard_normal((B, T, H, Dk))
     v = g.standard_normal((B, T, H, Dv))
     a = np.exp(-_softplus(g.standard_normal((B, T, H)) + alpha_shift))
     b = _sigmoid(g.standard_normal((B, T, H)))
     s0 = None
     if s0_std is not None:
         s0 = _cast(s0_std * g.standard_normal((B, H, Dv, Dk)), "f32")
+    q, k = _qk(g, q, k, raw_qk)
     return GdnInputs(_cast(q, dtype), _cast(k, dtype), _cast(v, dtype),
                      _cast(a, "f32"), _cast(b, "f32"), s0, dtype, name,
                      dict(B=B, T=T, H=H, Dk=Dk, Dv=Dv, seed=seed,
-                          alpha_shift=alpha_shift, s0_std=s0_std))
+                          alpha_shift=alpha_shift, s0_std=s0_std,
+                          raw_qk=raw_qk))
 
 
 def make_gdn2(B: int, T: int, H: int, Dk: int, Dv: int, dtype: str = "bf16",
               seed: int = 0, alpha_shift: float = 2.0,
-              s0_std: Optional[float] = None, name: str = "") -> Gdn2Inputs:
+              s0_std: Optional[float] = None, name: str = "",
+              raw_qk: bool = False) -> Gdn2Inputs:
     """Channel-gated inputs; per-channel alpha = exp(-softplus(N + shift)),
     erase and write = sigmoid(N(0,1))."""
     g = _rng(seed)
-    q = _unit_rows(g.standard_normal((B, T, H, Dk)))
-    k = _unit_rows(g.standard_normal((B, T, H, Dk)))
+    q = g.standard_normal((B, T, H, Dk))
+    k = g.standard_normal((B, T, H, Dk))
     v = g.standard_normal((B, T, H, Dv))
     a = np.exp(-_softplus(g.standard_normal((B, T, H, Dk)) + alpha_shift))
     e = _sigmoid(g.standard_normal((B, T, H, Dk)))
@@ -140,28 +158,33 @@ def make_gdn2(B: int, T: int, H: int, Dk: int, Dv: int, dtype: str = "bf16",
     s0 = None
     if s0_std is not None:
         s0 = _cast(s0_std * g.standard_normal((B, H, Dv, Dk)), "f32")
+    q, k = _qk(g, q, k, raw_qk)
     return Gdn2Inputs(_cast(q, dtype), _cast(k, dtype), _cast(v, dtype),
                       _cast(a, dtype), _cast(e, dtype), _cast(w, dtype), s0,
                       dtype, name,
                       dict(B=B, T=T, H=H, Dk=Dk, Dv=Dv, seed=seed,
-                           alpha_shift=alpha_shift, s0_std=s0_std))
+                           alpha_shift=alpha_shift, s0_std=s0_std,
+                           raw_qk=raw_qk))
 
 
 def make_decode(N: int, H: int, Dk: int, Dv: int, steps: int,
                 dtype: str = "bf16", seed: int = 0, alpha_shift: float = 2.0,
-                state_std: float = 0.02, name: str = "") -> DecodeInputs:
+                state_std: float = 0.02, name: str = "",
+                raw_qk: bool = False) -> DecodeInputs:
     """Decode inputs: a random fp32 state and ``steps`` fresh tokens."""
     g = _rng(seed)
-    q = _unit_rows(g.standard_normal((steps, N, H, Dk)))
-    k = _unit_rows(g.standard_normal((steps, N, H, Dk)))
+    q = g.standard_normal((steps, N, H, Dk))
+    k = g.standard_normal((steps, N, H, Dk))
     v = g.standard_normal((steps, N, H, Dv))
     a = np.exp(-_softplus(g.standard_normal((steps, N, H)) + alpha_shift))
     b = _sigmoid(g.standard_normal((steps, N, H)))
     s = _cast(state_std * g.standard_normal((N, H, Dv, Dk)), "f32")
+    q, k = _qk(g, q, k, raw_qk)
     return DecodeInputs(s, _cast(q, dtype), _cast(k, dtype), _cast(v, dtype),
                         _cast(a, "f32"), _cast(b, "f32"), dtype, name,
                         dict(N=N, H=H, Dk=Dk, Dv=Dv, steps=steps, seed=seed,
-                             alpha_shift=alpha_shift, state_std=state_std))
+                             alpha_shift=alpha_shift, state_std=state_std,
+                             raw_qk=raw_qk))
 
 
 # The five workloads.  Seed = 1000 + index.  The long-context workload draws

@@ -15,9 +15,10 @@
  *   o_t = S_t q_t,
  *
  * with the state S a d_v x d_k fp32 matrix per (sequence, head).  No scale
- * is applied to q (o_t = S_t q_t exactly); q and k are expected to be
- * L2-normalised by the caller, as the block does before the mixer
- * (review section 3.8), but nothing here depends on it for correctness.
+ * is applied to q (o_t = S_t q_t exactly).  The block L2-normalises q and
+ * k before the mixer (review section 3.8): the plain calls take them as
+ * given (nothing here depends on the normalisation for correctness), and
+ * the _ex variants at the end of this header can apply it on load.
  *
  * Conventions shared by every call
  *   - Every tensor pointer is a DEVICE pointer owned by the caller; tensors
@@ -33,8 +34,8 @@
  *                            channel gates, s0, s_final and the decode
  *                            state need 16-byte alignment; the scalar gates
  *                            and o need element alignment;
- *       GDR_ERR_UNSUPPORTED  (Dk, Dv) not in {64, 128} x {64, 128}, or an
- *                            unsupported dtype;
+ *       GDR_ERR_UNSUPPORTED  (Dk, Dv) not in {64, 128} x {64, 128}, an
+ *                            unsupported dtype, or an unknown flag bit;
  *       GDR_ERR_DEVICE       the HIP runtime reported a launch error.
  *     No C++ exception crosses this interface.
  *   - Values are not checked on the device: NaN/Inf propagate.  A decay gate
@@ -157,6 +158,58 @@ gdr_status_t gdr2_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
                             const void *erase, const void *write,
                             const float *s0, gdr_dtype_t out_dt, void *o,
                             float *s_final, hipStream_t stream);
+
+/*
+ * Fused prologue: the _ex variants below take the same arguments as the
+ * three calls above plus a `flags` word, an OR of
+ *
+ *   GDR_L2NORM_QK  normalise q_t and k_t to unit L2 norm per token and head
+ *                  as they are loaded, the step the Gated DeltaNet block
+ *                  applies to q and k right before the rule (review on
+ *                  meaningful96.github.io, section 3.8, the q and k paths of
+ *                  the block; the Gated DeltaNet-2 page keeps that block
+ *                  design):
+ *
+ *                    x_hat = x / sqrt(sum_c x_c^2 + GDR_L2NORM_EPS)
+ *
+ *                  over the Dk channels, the sum taken in fp32 over the
+ *                  input values.  The rule then runs on q_hat, k_hat
+ *                  exactly as documented above (for Gated Delta Rule-2 the
+ *                  erase direction becomes b (.) k_hat).  q and k in memory
+ *                  are not modified.
+ *
+ * flags == 0 is the plain call.  A set bit not listed here returns
+ * GDR_ERR_UNSUPPORTED and launches nothing.  Precision and every other
+ * convention are those of the plain call; on the bf16 paths q_hat and k_hat
+ * are never rounded back to bf16: the 1 / norm factors are applied to fp32
+ * intermediate results or to operands that are split into hi/lo pairs.
+ */
+#define GDR_L2NORM_QK 1u
+#define GDR_L2NORM_EPS 1e-6f
+
+gdr_status_t gdr_chunk_fwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                              int64_t Dv, gdr_dtype_t in_dt, const void *q,
+                              const void *k, const void *v,
+                              const float *alpha, const float *beta,
+                              const float *s0, gdr_dtype_t out_dt, void *o,
+                              float *s_final, uint32_t flags,
+                              hipStream_t stream);
+
+gdr_status_t gdr_recurrent_step_ex(int64_t N, int64_t H, int64_t Dk,
+                                   int64_t Dv, gdr_dtype_t in_dt,
+                                   const void *q, const void *k,
+                                   const void *v, const float *alpha,
+                                   const float *beta, float *state,
+                                   gdr_dtype_t out_dt, void *o,
+                                   uint32_t flags, hipStream_t stream);
+
+gdr_status_t gdr2_chunk_fwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                               int64_t Dv, gdr_dtype_t in_dt, const void *q,
+                               const void *k, const void *v,
+                               const void *alpha, const void *erase,
+                               const void *write, const float *s0,
+                               gdr_dtype_t out_dt, void *o, float *s_final,
+                               uint32_t flags, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *gdr_status_string(gdr_status_t s);

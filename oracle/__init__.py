@@ -19,6 +19,8 @@ gdn_step(q, k, v, alpha, beta, state) -> o   (state updated in place)
 gdn2_fwd(q, k, v, alpha, erase, write, s0=None) -> (o, s_final)
     Gated Delta Rule-2: decay S by diag(alpha_t), read along erase (.) k,
     write (write (.) v - read) along k.
+l2norm(x, eps=1e-6) -> x / sqrt(sum over the last axis of x^2 + eps)
+    The block's L2 normalisation of q and k, applied before either rule.
 
 Parity pins: every function is pinned by tests/test_oracle.py against
 closed forms, invariants, exact rational worked examples
@@ -37,7 +39,7 @@ _SRC = os.path.join(_HERE, "gdr_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 __all__ = ["build", "OracleLib", "default", "gdn_fwd", "gdn_step",
-           "gdn2_fwd", "num_threads", "set_num_threads", "err_rms"]
+           "gdn2_fwd", "l2norm", "num_threads", "set_num_threads", "err_rms"]
 
 
 def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
@@ -45,7 +47,7 @@ def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
     if force or not os.path.exists(out):
         tmp = out + ".tmp"
         subprocess.check_call(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared",
-                               "-std=c11", "-Wall", "-o", tmp, src])
+                               "-std=c11", "-Wall", "-o", tmp, src, "-lm"])
         os.replace(tmp, out)
     return out
 
@@ -75,6 +77,8 @@ class OracleLib:
         lib.oracle_gdn_step.restype = ctypes.c_int
         lib.oracle_gdn2_fwd.argtypes = [L] * 5 + [P] * 9
         lib.oracle_gdn2_fwd.restype = ctypes.c_int
+        lib.oracle_l2norm_rows.argtypes = [L, L, P, ctypes.c_double, P]
+        lib.oracle_l2norm_rows.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         self.lib = lib
@@ -145,6 +149,18 @@ class OracleLib:
             raise RuntimeError(f"oracle_gdn2_fwd failed ({rc})")
         return o, sf
 
+    def l2norm(self, x, eps=1e-6):
+        """Rows of x (last axis) scaled to unit L2 norm,
+        x / sqrt(sum x^2 + eps) (``oracle_l2norm_rows``).  float64."""
+        x = _f64(x)
+        d = x.shape[-1] if x.ndim else 1
+        n = x.size // d if d else 0
+        out = np.empty_like(x)
+        rc = self.lib.oracle_l2norm_rows(n, d, _p(x), float(eps), _p(out))
+        if rc:
+            raise RuntimeError(f"oracle_l2norm_rows failed ({rc})")
+        return out
+
 
 _default = None
 
@@ -185,6 +201,13 @@ def gdn2_fwd(*a, **kw):
 
 
 gdn2_fwd.__doc__ = OracleLib.gdn2_fwd.__doc__
+
+
+def l2norm(*a, **kw):
+    return default().l2norm(*a, **kw)
+
+
+l2norm.__doc__ = OracleLib.l2norm.__doc__
 
 
 def err_rms(x_hat, x) -> float:

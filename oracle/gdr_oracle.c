@@ -26,6 +26,7 @@
  */
 #include <stddef.h>
 #include <stdlib.h>
+#include <math.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -180,6 +181,29 @@ int oracle_gdn2_fwd(long B, long T, long H, long Dk, long Dv, const double *q,
         }
     }
     return err ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}
+
+/*
+ * L2 normalisation of the rows of x [n, d] into out [n, d]:
+ *
+ *   out_r = x_r / sqrt(sum_c x_rc^2 + eps).
+ *
+ * The Gated DeltaNet block ends the q and k paths with an L2 normalisation
+ * before the rule (review on meaningful96.github.io, section 3.8, the block
+ * diagram of q and k; the Gated DeltaNet-2 page keeps that block design).
+ * The pages give no guard for a zero row: eps inside the square root is the
+ * reading taken here (the library fixes eps = 1e-6).
+ */
+int oracle_l2norm_rows(long n, long d, const double *x, double eps, double *out) {
+    if (n < 0 || d < 0 || !(eps >= 0.0)) return 1;
+    for (long r = 0; r < n; ++r) {
+        const double *xr = x + r * d;
+        double ss = 0.0;
+        for (long c = 0; c < d; ++c) ss += xr[c] * xr[c];
+        const double inv = 1.0 / sqrt(ss + eps);
+        for (long c = 0; c < d; ++c) out[r * d + c] = xr[c] * inv;
+    }
+    return 0;
 }
 
 /* Threads the oracle's parallel loops use (reported with CPU timings). */

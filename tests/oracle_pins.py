@@ -462,6 +462,40 @@ def pin_gdn_negative_beta(orc):
     np.testing.assert_allclose(s1[0, 0], ref, rtol=0, atol=1e-12)
 
 
+# --- the block's L2 normalisation of q and k --------------------------------
+def pin_l2norm_worked(orc):
+    """Worked rows with eps = 0: (3, 4) -> (0.6, 0.8); (1, 1, 1, 1) ->
+    (0.5, 0.5, 0.5, 0.5); (0, -2, 0) -> (0, -1, 0).  A zero row stays zero
+    under eps > 0."""
+    x = np.array([[3.0, 4.0, 0.0, 0.0], [1.0, 1.0, 1.0, 1.0], [0.0, -2.0, 0.0, 0.0]])
+    ref = np.array([[0.6, 0.8, 0.0, 0.0], [0.5, 0.5, 0.5, 0.5], [0.0, -1.0, 0.0, 0.0]])
+    np.testing.assert_allclose(orc.l2norm(x, eps=0.0), ref, rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(orc.l2norm(np.zeros((2, 5)), eps=1e-6), np.zeros((2, 5)))
+
+
+def pin_l2norm_eps(orc):
+    """eps sits inside the square root: a row of norm r becomes norm
+    r / sqrt(r^2 + eps).  At r^2 = eps that is 1 / sqrt(2)."""
+    for r in (1e-3, 0.37, 5.0):
+        x = np.array([[r, 0.0, 0.0]])
+        out = orc.l2norm(x, eps=1e-6)
+        np.testing.assert_allclose(out[0, 0], r / np.sqrt(r * r + 1e-6), rtol=1e-15)
+    np.testing.assert_allclose(orc.l2norm(np.array([[0.0, 1e-3]]), eps=1e-6)[0, 1],
+                               1.0 / np.sqrt(2.0), rtol=1e-14)
+
+
+def pin_l2norm_rows(orc):
+    """Each row (last axis) on its own: with eps = 0 every row of a random
+    [3, 4, 7] array of mixed scales has norm 1 and points along its input
+    (out * |x| = x)."""
+    g = _rng(27)
+    x = g.standard_normal((3, 4, 7)) * g.uniform(0.01, 100.0, (3, 4, 1))
+    out = orc.l2norm(x, eps=0.0)
+    nrm = np.linalg.norm(x, axis=-1, keepdims=True)
+    np.testing.assert_allclose(np.linalg.norm(out, axis=-1), 1.0, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(out * nrm, x, rtol=1e-13, atol=0)
+
+
 ALL_PINS = [
     pin_golden_gdn, pin_golden_step, pin_golden_gdn2,
     pin_exact_matrix_form_gdn, pin_exact_matrix_form_gdn2,
@@ -470,4 +504,5 @@ ALL_PINS = [
     pin_g_read_only, pin_h_split, pin_h_step_chain, pin_i_sgd,
     pin_j_contraction, pin_k_kda, pin_gdn2_pure_decay, pin_gdn2_write_only,
     pin_gdn2_erase_axis, pin_gdn2_householder, pin_gdn_negative_beta,
+    pin_l2norm_worked, pin_l2norm_eps, pin_l2norm_rows,
 ]

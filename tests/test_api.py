@@ -26,6 +26,7 @@ def declared_functions():
 def test_header_declares_the_three_operations():
     names = declared_functions()
     for n in ("gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd",
+              "gdr_chunk_fwd_ex", "gdr_recurrent_step_ex", "gdr2_chunk_fwd_ex",
               "gdr_status_string", "gdr_version"):
         assert n in names, names
 
@@ -39,7 +40,7 @@ def test_status_strings(gdr):
     assert gdr.status_string(0) == "ok"
     for c in (1, 2, 3):
         assert gdr.status_string(c) != "unknown status"
-    assert gdr.lib.gdr_version() >= 100
+    assert gdr.lib.gdr_version() >= 200
 
 
 A16 = 1 << 20          # a fake, 16-byte aligned "device" address
@@ -114,3 +115,29 @@ def test_binding_rejects_cpu_tensors(gdr):
     x = torch.zeros(1, 4, 1, 64)
     with pytest.raises(ValueError):
         gdr.gdr_chunk_fwd(x, x, x, torch.zeros(1, 4, 1), torch.zeros(1, 4, 1))
+
+
+def test_ex_variants_check_flags(gdr):
+    """Unknown flag bits are rejected before anything else is looked at; the
+    known bit goes through the same argument checks as the plain call."""
+    L = gdr.lib
+    for bad in (2, 4, 0x80000000, 0xffffffff):
+        assert L.gdr_chunk_fwd_ex(1, 8, 1, 64, 64, 1, A16, A16, A16, A16, A16, None, 1,
+                                  A16, None, bad, None) == 2
+        assert L.gdr2_chunk_fwd_ex(1, 8, 1, 64, 64, 1, A16, A16, A16, A16, A16, A16, None,
+                                   1, A16, None, bad, None) == 2
+        assert L.gdr_recurrent_step_ex(2, 1, 64, 64, 1, A16, A16, A16, A16, A16, A16, 1,
+                                       A16, bad, None) == 2
+    f = gdr.GDR_L2NORM_QK
+    # validation failures (no launch): NULL q, misaligned v, bad head dim
+    assert L.gdr_chunk_fwd_ex(1, 8, 1, 64, 64, 1, None, A16, A16, A16, A16, None, 1,
+                              A16, None, f, None) == 1
+    assert L.gdr2_chunk_fwd_ex(1, 8, 1, 64, 64, 1, A16, A16, BAD, A16, A16, A16, None,
+                               1, A16, None, f, None) == 1
+    assert L.gdr_recurrent_step_ex(2, 1, 96, 64, 1, A16, A16, A16, A16, A16, A16, 1,
+                                   A16, f, None) == 2
+    # empty calls return OK with the flag set
+    assert L.gdr_chunk_fwd_ex(0, 8, 1, 64, 64, 1, None, None, None, None, None, None, 1,
+                              None, None, f, None) == 0
+    assert L.gdr_recurrent_step_ex(0, 1, 64, 64, 1, None, None, None, None, None, None,
+                                   1, None, f, None) == 0

@@ -34,6 +34,11 @@ MUTANTS = [
      "for (long j = 0; j < Dk; ++j) s[j] *= alpha[j];      /* S' */\n        double rd = 0.0;                                     /* S'(b.k) */\n        for (long j = 0; j < Dk; ++j) rd += s[j] * (erase[j] * k[j]);",
      "double rd = 0.0;\n        for (long j = 0; j < Dk; ++j) rd += s[j] * (erase[j] * k[j]);\n        for (long j = 0; j < Dk; ++j) s[j] *= alpha[j];"),
     ("gdn2_gate_on_value_axis", "s[j] *= alpha[j];", "s[j] *= alpha[i < Dk ? i : 0];"),
+    ("l2norm_sum_not_squared", "ss += xr[c] * xr[c]", "ss += fabs(xr[c])"),
+    ("l2norm_eps_outside_root", "1.0 / sqrt(ss + eps)", "1.0 / (sqrt(ss) + eps)"),
+    ("l2norm_row_shift", "const double *xr = x + r * d;",
+     "const double *xr = x + (r + 1 < n ? r + 1 : r) * d;"),
+    ("l2norm_sign_lost", "out[r * d + c] = xr[c] * inv", "out[r * d + c] = fabs(xr[c]) * inv"),
 ]
 
 
