@@ -260,11 +260,37 @@ def bench_gdr2(gdr, torch, warmup, steps):
     return dict(mean=mean, min=mn, median=med, B=B, T=T, H=H, bytes=bytes_launch)
 
 
+def time_interleaved(fns, warmup, rounds):
+    """Median and min per-call time (us) of each callable in `fns` (a dict),
+    the calls interleaved round-robin (rotating the order each round) after
+    `warmup` calls of each, so that all of them see the same clocks."""
+    import torch
+    names = list(fns)
+    for _ in range(warmup):
+        for n in names:
+            fns[n]()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t = {n: [] for n in names}
+    for r in range(rounds):
+        for n in names[r % len(names):] + names[:r % len(names)]:
+            ev[0].record()
+            fns[n]()
+            ev[1].record()
+            torch.cuda.synchronize()
+            t[n].append(ev[0].elapsed_time(ev[1]) * 1e3)
+    out = {}
+    for n in names:
+        x = sorted(t[n])
+        out[n] = {"median": x[len(x) // 2], "min": x[0]}
+    return out
+
+
 def bench_l2norm(gdr, torch, warmup, steps):
     """Fused q, k normalisation against the plain call and against a
     separate normalise pass (fp32 sum of squares in PyTorch, bf16 result)
     followed by the plain call, on the GDN (B8 H16 T4096) and GDN-2 (B4 H16
-    T4096) workloads with raw q, k."""
+    T4096) workloads with raw q, k; the three are timed interleaved."""
     from gdr_gen import make_gdn, make_gdn2
     dev = torch.device("cuda:0")
     eps = 1e-6
@@ -285,8 +311,8 @@ def bench_l2norm(gdr, torch, warmup, steps):
                                       s_final=sf)
     sep = lambda: gdr.gdr_chunk_fwd(norm_pass(q), norm_pass(k), v, a, b, None,
                                     out_dtype=torch.float32, o=o, s_final=sf)
-    res["gdn"] = {n: time_launches(f, warmup, steps)[0] * 1e6
-                  for n, f in (("fused_us", fused), ("plain_us", plain), ("separate_pass_us", sep))}
+    t = time_interleaved({"fused": fused, "plain": plain, "separate_pass": sep}, warmup, steps)
+    res["gdn"] = {f"{n}_us_median": v["median"] for n, v in t.items()}
     del q, k, v, a, b, o, sf, inp
     inp = make_gdn2(B=4, T=4096, H=16, Dk=128, Dv=128, dtype="bf16", seed=1004, raw_qk=True)
     args = [x.to(dev) for x in (inp.q, inp.k, inp.v, inp.alpha, inp.erase, inp.write)]
@@ -297,8 +323,8 @@ def bench_l2norm(gdr, torch, warmup, steps):
     plain = lambda: gdr.gdr2_chunk_fwd(*args, None, out_dtype=torch.float32, o=o, s_final=sf)
     sep = lambda: gdr.gdr2_chunk_fwd(norm_pass(args[0]), norm_pass(args[1]), *args[2:], None,
                                      out_dtype=torch.float32, o=o, s_final=sf)
-    res["gdr2"] = {n: time_launches(f, warmup, steps)[0] * 1e6
-                   for n, f in (("fused_us", fused), ("plain_us", plain), ("separate_pass_us", sep))}
+    t = time_interleaved({"fused": fused, "plain": plain, "separate_pass": sep}, warmup, steps)
+    res["gdr2"] = {f"{n}_us_median": v["median"] for n, v in t.items()}
     return res
 
 
@@ -377,7 +403,7 @@ def main():
         res["longctx"] = bench_longctx(gdr, torch, min(args.warmup, 10), min(args.steps, 10))
     if args.only in (None, "l2norm"):
         log("timing the fused q, k normalisation (GDN and GDN-2 workloads) ...")
-        res["l2norm"] = bench_l2norm(gdr, torch, min(args.warmup, 10), min(args.steps, 20))
+        res["l2norm"] = bench_l2norm(gdr, torch, args.warmup, min(args.steps, 30))
     if args.only in (None, "copy"):
         log("timing a 512 MiB device copy ...")
         res["copy"] = bench_copy(torch, args.warmup, args.steps)

@@ -40,18 +40,30 @@
 //            AP-A (wave 2): A = E K'^T for chunk c + 2 (or the wide-chunk
 //                 path), T = (I + A)^{-1} for chunk c + 1;
 //            AP-P (wave 3), chunk c + 1: P = Q K'^T, w (.) v.
-// With GDR_L2NORM_QK (template flag NORM) the E waves also sum k_t^2 and
-// q_t^2 over the channels (fp32 per lane, then across the wave) and fold
-// rho_t = 1 / |k_t| into E and K', pi_t = 1 / |q_t| into Q, before those are
-// rounded; rho and pi go to the elementwise set for the wide-chunk path,
-// which reads the raw inputs.
+// With GDR_L2NORM_QK (template flag NORM), rho_t = 1 / |k_t| and
+// pi_t = 1 / |q_t| enter as per-token scalars only; E, Q and K' stay those
+// of the raw q, k.  Carrying V~ = diag(rho) V_new in place of V_new (a
+// similarity transform of the solve) puts every rho on a row:
+//   A~_sj = rho_s^2 A_sj,   T~ = (I + A~)^{-1} = diag(rho) T diag(rho)^{-1},
+//   R~_s  = rho_s (w (.) v)_s - rho_s^2 (S E^T)_s,   V~ = T~ R~,
+//   P~_rs = pi_r P_rs,   o_r = pi_r (Q S^T)_r + sum_s P~_rs V~_s,
+//   S    <- (S + K'^T V~) diag(lambda_C)
+// (A, P, E, K' those of the raw q, k; the rho_j of A's columns and P's
+// columns cancel against V~).  The E waves write per-lane partial sums of
+// k^2 and q^2; AP-A reduces them when it forms A and stores rho^2, pi and
+// rho with the chunk's elementwise set.
 // One workgroup barrier closes each period; LDS keeps four sets of the
 // elementwise operands (chunk mod 4) and two of A, T, P and w (.) v.
 //
-// Products: v_mfma_f32_16x16x32_bf16 over the key dim, with the contraction
-// order kappa (see kperm) that makes a pair of S^T accumulator tiles the B
-// operand as they stand; v_mfma_f32_16x16x16_bf16 over tokens, whose C tile
-// (rows 4 g + r, column m) is already the B operand of the next product.
+// Products: v_mfma_f32_16x16x32_bf16 throughout.  Over the key dim with the
+// contraction order kappa (see kperm) that makes a pair of S^T accumulator
+// tiles the B operand as they stand; over the 16 tokens with two 16-deep
+// halves side by side (hi and lo terms, see cat44), the C tile (rows
+// 4 g + r, column m) of one product being the B operand of the next.  A
+// 16-deep leftover term takes the 32-deep instruction with a zero half
+// rather than v_mfma_f32_16x16x16_bf16: an accumulator chained from one
+// instruction into the other has been read before it was written (stale
+// first registers) when the compiler left four wait states between them.
 //
 // Precision: computed operands enter as bf16 hi/lo pairs (mfma_common.h)
 // where it matters.  P, P V_new, Q S^T and the update take three terms.
@@ -97,8 +109,8 @@ struct Lay2 {
     static constexpr int KH = QL + CH * DK * 2;     // K' hi, lo [16][PKN], natural order
     static constexpr int KL = KH + CH * PKN * 2;
     static constexpr int LC = KL + CH * PKN * 2;    // lambda_C [DK] fp32, then the wide flag
-    static constexpr int NR = LC + DK * 4 + 16;     // NORM: rho [16], pi [16] fp32
-    static constexpr int ESET = NR + (NORM ? 2 * CH * 4 : 0);
+    static constexpr int NR = LC + DK * 4 + 16;     // NORM: rho^2, pi, rho [16] fp32 each
+    static constexpr int ESET = NR + (NORM ? 3 * CH * 4 : 0);
     // T, P, w . v, chunk mod 2
     static constexpr int TH = 0;                    // T [16][P24] bf16
     static constexpr int PH = TH + CH * P24 * 2;    // P hi, lo [16][P24]
@@ -113,7 +125,10 @@ struct Lay2 {
     static constexpr int FK = FG + CH * DK * 4;     //   k, b, q bf16 [16][DK]
     static constexpr int FB = FK + CH * DK * 2;
     static constexpr int FQ = FB + CH * DK * 2;
-    static constexpr int TOTAL = FQ + CH * DK * 2;
+    // NORM: per-lane partial sums (k^2, q^2) [16 tokens][64 lanes] fp32 x2,
+    // chunk mod 2, 16-byte units swizzled by token (see ps_at)
+    static constexpr int PS = FQ + CH * DK * 2;
+    static constexpr int TOTAL = PS + (NORM ? 2 * CH * 64 * 8 : 0);
     static_assert(ESET % 16 == 0 && TSET % 16 == 0 && KH % 16 == 0 && KL % 16 == 0, "alignment");
 };
 
@@ -137,10 +152,6 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
-__device__ __forceinline__ f32x4 mfma16k(const s16x4& a, const s16x4& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ void split4(const f32x4& x, s16x4& h, s16x4& l) {
     uint32_t h0, h1, l0, l1;
     split2(x[0], x[1], h0, l0);
@@ -159,19 +170,14 @@ __device__ __forceinline__ bf16x8 cat44(const s16x4& a, const s16x4& b) {
 __device__ __forceinline__ float lo_bf(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// Sum over the key channels of one token when lane l holds channel pair
-// l mod (DK / 2): the 16 lanes of each row by DPP (quad swaps, then the
-// half-row and row mirrors), then across rows; at DK = 64 lanes 32..63
-// repeat lanes 0..31 and the last step is skipped.  Every lane gets the sum.
-template <int DK>
-__device__ __forceinline__ float key_sum(float x) {
-    x += dpp_mov<0xB1>(x);    // quad_perm [1, 0, 3, 2]
-    x += dpp_mov<0x4E>(x);    // quad_perm [2, 3, 0, 1]
-    x += dpp_mov<0x141>(x);   // row_half_mirror
-    x += dpp_mov<0x140>(x);   // row_mirror
-    x += __shfl_xor(x, 16, 64);
-    if constexpr (DK == 128) x += __shfl_xor(x, 32, 64);
-    return x;
+// NORM factors of a chunk in its elementwise set: rho^2, pi, rho by token.
+enum { NR_RHO2 = 0, NR_PI = CH, NR_RHO = 2 * CH };
+
+// Float offset of lane l's (k^2, q^2) partial pair for token t: 16-byte unit
+// l / 2 of the token's row, XOR-swizzled by 4 (t mod 4) so that the reducing
+// lanes (4 tokens x 4 unit phases per 16 lanes) read distinct banks.
+__device__ __forceinline__ int ps_at(int t, int l) {
+    return t * 128 + 4 * ((l >> 1) ^ (4 * (t & 3))) + 2 * (l & 1);
 }
 
 template <int DK, int DV, typename TOut, bool NORM>
@@ -254,6 +260,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
             const bf16_t* Kh = bfp(es, L::KH);
             const bf16_t* Kl = bfp(es, L::KL);
             const float* lc = reinterpret_cast<const float*>(es + L::LC);
+            const float* nrc = reinterpret_cast<const float*>(es + L::NR);
             const int wide = wide_flag(es);
             // operands written in the previous period; their reads overlap
             // the products below
@@ -298,17 +305,25 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
             __builtin_amdgcn_sched_barrier(0);
 
             // ---- R = w.v - E S^T;  V_new = [T | T] [R_hi; R_lo] ---------------
+            //      (NORM: R~ = rho w.v - rho^2 E S^T, w.v already scaled)
             s16x4 rh, rl;
-            split4(wv - (k2[0] + k2[1]), rh, rl);
+            if constexpr (NORM)
+                split4(wv - *reinterpret_cast<const f32x4*>(nrc + NR_RHO2 + 4 * g) * (k2[0] + k2[1]),
+                       rh, rl);
+            else
+                split4(wv - (k2[0] + k2[1]), rh, rl);
             const f32x4 vn = mfma16(cat44(th, th), cat44(rh, rl), f32x4{0.f, 0.f, 0.f, 0.f});
             s16x4 nh, nl;
             split4(vn, nh, nl);
             const bf16x8 nn = cat44(nh, nh);
+            const bf16x8 nz = cat44(nl, s16x4{0, 0, 0, 0});
 
-            // ---- o = Q S^T + [P_hi | P_lo] [N_hi; N_hi] + P_hi N_lo ----------
+            // ---- o = Q S^T + [P_hi | P_lo] [N_hi; N_hi] + [P_hi | P_lo] [N_lo; 0]
             f32x4 o = q3[0] + q3[1] + q3[2];
-            o = mfma16(cat44(ph, pl), nn, o);
-            o = mfma16k(ph, nl, o);
+            if constexpr (NORM) o *= *reinterpret_cast<const f32x4*>(nrc + NR_PI + 4 * g);
+            const bf16x8 pp = cat44(ph, pl);
+            o = mfma16(pp, nn, o);
+            o = mfma16(pp, nz, o);
 
             // ---- S^T <- (S^T + K'^T V_new) lambda_C --------------------------
             if (wide) {
@@ -317,8 +332,9 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
             }
 #pragma unroll
             for (int t = 0; t < NS; ++t) {
-                sa[t] = mfma16(cat44(kth[t], ktl[t]), nn, sa[t]);
-                sa[t] = mfma16k(kth[t], nl, sa[t]);
+                const bf16x8 kk = cat44(kth[t], ktl[t]);
+                sa[t] = mfma16(kk, nn, sa[t]);
+                sa[t] = mfma16(kk, nz, sa[t]);
             }
             if (!wide) {
 #pragma unroll
@@ -421,14 +437,9 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
             bf16_t* Kl = bfp(es, L::KL);
 #pragma unroll
             for (int t = 0; t < CH; ++t) {
-                float k0 = lo_bf(kk[t]), k1 = hi_bf(kk[t]);
-                if constexpr (NORM) {
-                    const float rho = reinterpret_cast<const float*>(es + L::NR)[t];
-                    k0 *= rho;
-                    k1 *= rho;
-                }
                 uint32_t xh, xl;
-                split2(k0 * __expf(g0[CH - 1] - g0[t]), k1 * __expf(g1[CH - 1] - g1[t]), xh, xl);
+                split2(lo_bf(kk[t]) * __expf(g0[CH - 1] - g0[t]),
+                       hi_bf(kk[t]) * __expf(g1[CH - 1] - g1[t]), xh, xl);
                 *reinterpret_cast<uint32_t*>(Kh + t * L::PKN + 2 * cp) = xh;
                 *reinterpret_cast<uint32_t*>(Kl + t * L::PKN + 2 * cp) = xl;
             }
@@ -447,8 +458,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                 }
                 if constexpr (NORM) {
                     const float* nr = reinterpret_cast<const float*>(es + L::NR);
-                    av *= nr[r] * nr[s];
-                    pv *= nr[CH + r] * nr[s];
+                    av *= nr[NR_RHO2 + r];
+                    pv *= nr[NR_PI + r];
                 }
                 Af[r * PAF + s] = s < r ? av : 0.f;
                 Wp[r * PAF + s] = pv;
@@ -460,6 +471,34 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
             if (x2 >= 0 && x2 < nch) {
                 unsigned char* es = eset(x2);
                 float* Af = reinterpret_cast<float*>(smem + L::AF + (int)(x2 & 1) * CH * PAF * 4);
+                float rho2m = 1.f;
+                if constexpr (NORM) {
+                    // lane (t, u) = (lane / 4, lane % 4) sums units u, u + 4,
+                    // ... of token t's partials; the quad then holds |k_t|^2
+                    // and |q_t|^2 (at DK = 64 lanes 32..63 wrote nothing)
+                    const float* ps = reinterpret_cast<const float*>(smem + L::PS) +
+                                      (int)(x2 & 1) * CH * 128;
+                    const int t = lane >> 2, u = lane & 3;
+                    float sk = 0.f, sq = 0.f;
+#pragma unroll
+                    for (int e = 0; e < DK / 16; ++e) {
+                        const f32x4 x = *reinterpret_cast<const f32x4*>(
+                            ps + t * 128 + 4 * ((4 * e + u) ^ (4 * (t & 3))));
+                        sk += x[0] + x[2];
+                        sq += x[1] + x[3];
+                    }
+                    sk = quad_sum(sk);
+                    sq = quad_sum(sq);
+                    const float rho = l2_inv(sk);
+                    float* nr = reinterpret_cast<float*>(es + L::NR);
+                    if (u == 0) {
+                        nr[NR_RHO2 + t] = rho * rho;
+                        nr[NR_PI + t] = l2_inv(sq);
+                        nr[NR_RHO + t] = rho;
+                    }
+                    wave_lds_sync();
+                    rho2m = nr[NR_RHO2 + m];
+                }
                 if (wide_flag(es)) {
                     float* Wp = reinterpret_cast<float*>(smem + L::WP + (int)(x2 & 1) * CH * PAF * 4);
                     wide_chunk(x2, es, Af, Wp);
@@ -478,6 +517,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                     f32x4 av;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) av[r] = 4 * g + r < m ? acc[r] : 0.f;
+                    if constexpr (NORM) av *= rho2m;
                     *reinterpret_cast<f32x4*>(Af + m * PAF + 4 * g) = av;
                 }
             }
@@ -558,6 +598,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                 const f32x4 s = acc[0] + acc[1] + acc[2];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) pv[r] = 4 * g + r <= m ? s[r] : 0.f;
+                // NORM: P~ = pi_r P (the wide path's P already carries it)
+                if constexpr (NORM) pv *= reinterpret_cast<const float*>(es + L::NR)[NR_PI + m];
             } else {
                 const float* Wp = reinterpret_cast<const float*>(smem + L::WP + (int)(cn & 1) * CH * PAF * 4);
                 pv = *reinterpret_cast<const f32x4*>(Wp + m * PAF + 4 * g);
@@ -568,10 +610,17 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
             *reinterpret_cast<s16x4*>(bfp(ts, L::PL) + m * P24 + 4 * g) = xl;
             const bool live = wt < n_live(cn);
             float* wv = reinterpret_cast<float*>(ts + L::WV);
+            // NORM: rho_t w.v, the first term of R~
+            const float rw = NORM ? reinterpret_cast<const float*>(es + L::NR)[NR_RHO + wt] : 1.f;
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                wv[(wr + 2 * x) * P24 + wt] = live ? lo_bf(f.w[x]) * lo_bf(f.v[x]) : 0.f;
-                wv[(wr + 2 * x + 1) * P24 + wt] = live ? hi_bf(f.w[x]) * hi_bf(f.v[x]) : 0.f;
+                if constexpr (NORM) {
+                    wv[(wr + 2 * x) * P24 + wt] = live ? lo_bf(f.w[x]) * lo_bf(f.v[x]) * rw : 0.f;
+                    wv[(wr + 2 * x + 1) * P24 + wt] = live ? hi_bf(f.w[x]) * hi_bf(f.v[x]) * rw : 0.f;
+                } else {
+                    wv[(wr + 2 * x) * P24 + wt] = live ? lo_bf(f.w[x]) * lo_bf(f.v[x]) : 0.f;
+                    wv[(wr + 2 * x + 1) * P24 + wt] = live ? hi_bf(f.w[x]) * hi_bf(f.v[x]) : 0.f;
+                }
             }
         };
         Buf fa, fb, fc;
@@ -622,33 +671,17 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                         l1 *= hi_bf(f.a[t]);
                     }
                 }
-                // rho, pi of this wave's tokens (rows past the end read 0)
-                float rho[NT], pin[NT];
-#pragma unroll
-                for (int u = 0; u < NT; ++u) {
-                    rho[u] = 1.f;
-                    pin[u] = 1.f;
-                }
                 if constexpr (NORM) {
+                    // partial sums of k^2 and q^2 over this lane's channel
+                    // pair (rows past the end read 0)
+                    float* ps = reinterpret_cast<float*>(smem + L::PS) + (int)(cn & 1) * CH * 128;
 #pragma unroll
                     for (int u = 0; u < NT; ++u) {
                         const float k0 = lo_bf(f.k[u]), k1 = hi_bf(f.k[u]);
                         const float q0 = lo_bf(f.q[u]), q1 = hi_bf(f.q[u]);
-                        rho[u] = key_sum<DK>(__builtin_fmaf(k1, k1, k0 * k0));
-                        pin[u] = key_sum<DK>(__builtin_fmaf(q1, q1, q0 * q0));
-                    }
-#pragma unroll
-                    for (int u = 0; u < NT; ++u) {
-                        rho[u] = l2_inv(rho[u]);
-                        pin[u] = l2_inv(pin[u]);
-                    }
-                    if (lane == 0) {
-                        float* nr = reinterpret_cast<float*>(es + L::NR);
-#pragma unroll
-                        for (int u = 0; u < NT; ++u) {
-                            nr[T0 + u] = rho[u];
-                            nr[CH + T0 + u] = pin[u];
-                        }
+                        if (DK == 128 || lane < 32)
+                            *reinterpret_cast<float2*>(ps + ps_at(T0 + u, lane)) =
+                                float2{__builtin_fmaf(k1, k1, k0 * k0), __builtin_fmaf(q1, q1, q0 * q0)};
                     }
                 }
 #pragma unroll
@@ -660,20 +693,13 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                         l1 *= hi_bf(f.a[t]);
                     }
                     const float r0 = __builtin_amdgcn_rcpf(l0), r1 = __builtin_amdgcn_rcpf(l1);
-                    float k0 = lo_bf(f.k[u]), k1 = hi_bf(f.k[u]);
-                    if constexpr (NORM) {
-                        k0 *= rho[u];
-                        k1 *= rho[u];
-                    }
+                    const float k0 = lo_bf(f.k[u]), k1 = hi_bf(f.k[u]);
                     const float e0 = lv ? lo_bf(f.b[u]) * k0 : 0.f;
                     const float e1 = lv ? hi_bf(f.b[u]) * k1 : 0.f;
                     const int ot = kq_at<DK>(t, pc);
                     *reinterpret_cast<uint32_t*>(bfp(es, L::EH) + ot) = cvt_pk(e0 * l0, e1 * l1);
                     uint32_t xh, xl;
-                    if constexpr (NORM)
-                        split2(lo_bf(f.q[u]) * pin[u] * l0, hi_bf(f.q[u]) * pin[u] * l1, xh, xl);
-                    else
-                        split2(lo_bf(f.q[u]) * l0, hi_bf(f.q[u]) * l1, xh, xl);
+                    split2(lo_bf(f.q[u]) * l0, hi_bf(f.q[u]) * l1, xh, xl);
                     *reinterpret_cast<uint32_t*>(bfp(es, L::QH) + ot) = xh;
                     *reinterpret_cast<uint32_t*>(bfp(es, L::QL) + ot) = xl;
                     split2(k0 * r0, k1 * r1, xh, xl);
