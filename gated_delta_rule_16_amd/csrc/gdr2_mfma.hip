@@ -471,35 +471,45 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
             if (x2 >= 0 && x2 < nch) {
                 unsigned char* es = eset(x2);
                 float* Af = reinterpret_cast<float*>(smem + L::AF + (int)(x2 & 1) * CH * PAF * 4);
-                float rho2m = 1.f;
+                // NORM: lane (t, u) = (lane / 4, lane % 4) loads units u, u + 4,
+                // ... of token t's partial sums first, so that the loads
+                // overlap A's own reads and products
+                f32x4 psv[NORM ? DK / 16 : 1];
                 if constexpr (NORM) {
-                    // lane (t, u) = (lane / 4, lane % 4) sums units u, u + 4,
-                    // ... of token t's partials; the quad then holds |k_t|^2
-                    // and |q_t|^2 (at DK = 64 lanes 32..63 wrote nothing)
                     const float* ps = reinterpret_cast<const float*>(smem + L::PS) +
                                       (int)(x2 & 1) * CH * 128;
                     const int t = lane >> 2, u = lane & 3;
+#pragma unroll
+                    for (int e = 0; e < DK / 16; ++e)
+                        psv[e] = *reinterpret_cast<const f32x4*>(
+                            ps + t * 128 + 4 * ((4 * e + u) ^ (4 * (t & 3))));
+                }
+                // |k_t|^2, |q_t|^2 summed over the quad; rho^2, pi, rho of
+                // token t stored with the chunk's set; returns rho_t^2
+                auto reduce_norm = [&]() {
                     float sk = 0.f, sq = 0.f;
 #pragma unroll
-                    for (int e = 0; e < DK / 16; ++e) {
-                        const f32x4 x = *reinterpret_cast<const f32x4*>(
-                            ps + t * 128 + 4 * ((4 * e + u) ^ (4 * (t & 3))));
-                        sk += x[0] + x[2];
-                        sq += x[1] + x[3];
+                    for (int e = 0; e < (NORM ? DK / 16 : 0); ++e) {
+                        sk += psv[e][0] + psv[e][2];
+                        sq += psv[e][1] + psv[e][3];
                     }
                     sk = quad_sum(sk);
                     sq = quad_sum(sq);
                     const float rho = l2_inv(sk);
-                    float* nr = reinterpret_cast<float*>(es + L::NR);
-                    if (u == 0) {
+                    const int t = lane >> 2;
+                    if ((lane & 3) == 0) {
+                        float* nr = reinterpret_cast<float*>(es + L::NR);
                         nr[NR_RHO2 + t] = rho * rho;
                         nr[NR_PI + t] = l2_inv(sq);
                         nr[NR_RHO + t] = rho;
                     }
-                    wave_lds_sync();
-                    rho2m = nr[NR_RHO2 + m];
-                }
+                    return rho * rho;
+                };
                 if (wide_flag(es)) {
+                    if constexpr (NORM) {
+                        reduce_norm();
+                        wave_lds_sync();   // the entry-by-entry path reads them back
+                    }
                     float* Wp = reinterpret_cast<float*>(smem + L::WP + (int)(x2 & 1) * CH * PAF * 4);
                     wide_chunk(x2, es, Af, Wp);
                 } else {
@@ -517,7 +527,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                     f32x4 av;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) av[r] = 4 * g + r < m ? acc[r] : 0.f;
-                    if constexpr (NORM) av *= rho2m;
+                    // NORM: row m of A~ takes rho_m^2, held by lane 4 m
+                    if constexpr (NORM) av *= __shfl(reduce_norm(), 4 * m, 64);
                     *reinterpret_cast<f32x4*>(Af + m * PAF + 4 * g) = av;
                 }
             }
