@@ -22,6 +22,8 @@ The JSON line (stdout, last line) carries:
                      the GDN and GDN-2 workloads with raw q, k: launch time
                      fused, plain (no normalisation), and a separate
                      normalise pass in PyTorch followed by the plain call
+  output_gate        gdr_output_gate (RMSNorm x SiLU gate) on the B8 T4096 H16
+                     d128 output: fp32 o, bf16 gate, bf16 y; GB/s of HBM
   copy_reference     a plain 512 MiB device copy (achievable bandwidth)
   cpu_baseline       the fp64 oracle timed on the host on the same workload
 """
@@ -51,9 +53,11 @@ def log(*a):
 CSRC = os.path.join(ROOT, "gated_delta_rule_16_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
 # kernel-name prefix in rocprofv3 output -> the bench leg it belongs to
-KERNELS = {"gdn": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, 64, float>",
-           "gdr2": "void gdr::(anonymous namespace)::gdr2_bf16_kernel<128, 128, float>",
+KERNELS = {"gdn": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, 64, float, false>",
+           "gdr2": "void gdr::(anonymous namespace)::gdr2_bf16_kernel<128, 128, float, false>",
            "decode": "void gdr::step_kernel<128, 128, unsigned short, float>",
+           "gate": "void gdr::(anonymous namespace)::output_gate_kernel<128, float, unsigned short, "
+                   "unsigned short>",
            "copy": "__amd_rocclr_copyBuffer"}
 
 
@@ -328,6 +332,18 @@ def bench_l2norm(gdr, torch, warmup, steps):
     return res
 
 
+def bench_gate(gdr, torch, warmup, steps):
+    from gdr_gen import make_gate
+    inp = make_gate(8 * 4096, 16, 128, "f32", "bf16", seed=450)
+    dev = torch.device("cuda:0")
+    o, g, w = inp.o.to(dev), inp.g.to(dev), inp.w.to(dev)
+    y = torch.empty(o.shape, dtype=torch.bfloat16, device=dev)
+    mean, mn, med, wall = time_launches(
+        lambda: gdr.gdr_output_gate(o, g, w, 1e-6, y=y), warmup, steps)
+    n = o.numel()
+    return dict(mean=mean, min=mn, bytes=n * (4 + 2 + 2) + 4 * 128)
+
+
 def bench_copy(torch, warmup, steps, nbytes=512 << 20):
     """A plain device-to-device copy of known size: the achievable-bandwidth
     reference, and the kernel whose FETCH_SIZE / WRITE_SIZE counters scale
@@ -364,7 +380,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
-    ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "longctx", "l2norm", "copy"],
+    ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "longctx", "l2norm", "gate", "copy"],
                     default=None,
                     help="time one operation only (for profiling)")
     ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT"),
@@ -404,6 +420,9 @@ def main():
     if args.only in (None, "l2norm"):
         log("timing the fused q, k normalisation (GDN and GDN-2 workloads) ...")
         res["l2norm"] = bench_l2norm(gdr, torch, args.warmup, min(args.steps, 30))
+    if args.only in (None, "gate"):
+        log("timing gdr_output_gate B8 T4096 H16 d128 ...")
+        res["gate"] = bench_gate(gdr, torch, args.warmup, args.steps)
     if args.only in (None, "copy"):
         log("timing a 512 MiB device copy ...")
         res["copy"] = bench_copy(torch, args.warmup, args.steps)
@@ -421,7 +440,7 @@ def main():
         out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                            "traffic": measured_traffic("gdn"),
-                           "kernel": "chunk_bf16_kernel<128,128,64,float>",
+                           "kernel": "chunk_bf16_kernel<128,128,64,float,false>",
                            "algorithmic_bytes_per_launch": g["bytes"],
                            "launch_us_mean": g["mean"] * 1e6, "launch_us_min": g["min"] * 1e6}
         tf = g["flops"] / g["mean"] / 1e12
@@ -465,6 +484,14 @@ def main():
                                  "(no normalisation), separate PyTorch normalise pass + plain call",
                          "gdn B8 H16 T4096": res["l2norm"]["gdn"],
                          "gdr2 B4 H16 T4096": res["l2norm"]["gdr2"]}
+    if "gate" in res:
+        r = res["gate"]
+        gbs = r["bytes"] / r["mean"] / 1e9
+        out["output_gate"] = {"workload": "gdr_output_gate B8 T4096 H16 d128: fp32 o, bf16 gate, "
+                                          "fp32 weight, bf16 y",
+                              "launch_us_mean": r["mean"] * 1e6, "GB/s": gbs,
+                              "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_launch": r["bytes"],
+                              "traffic": measured_traffic("gate")}
     if "copy" in res:
         cp = res["copy"]
         out["copy_reference"] = {"what": "torch device-to-device copy, 512 MiB read + 512 MiB "

@@ -10,6 +10,7 @@ Functions mirror the C calls:
     gdr_chunk_fwd(q, k, v, alpha, beta, s0=None, ...)            -> (o, s_final)
     gdr_recurrent_step(q, k, v, alpha, beta, state, ...)         -> o
     gdr2_chunk_fwd(q, k, v, alpha, erase, write, s0=None, ...)   -> (o, s_final)
+    gdr_output_gate(o, g, w=None, eps=1e-6, ...)                -> y
 
 ``l2norm_qk=True`` calls the ``_ex`` variant of the same C function with
 GDR_L2NORM_QK: q and k are L2-normalised on load inside the kernels.
@@ -21,7 +22,7 @@ import os
 
 import torch  # loads the HIP runtime libgdr.so binds to
 
-__all__ = ["gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd",
+__all__ = ["gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd", "gdr_output_gate",
            "GdrError", "status_string", "lib", "LIB_PATH", "GDR_F32",
            "GDR_BF16", "GDR_L2NORM_QK"]
 
@@ -51,6 +52,8 @@ lib.gdr2_chunk_fwd_ex.argtypes = [_I64] * 5 + [_E] + [_P] * 7 + [_E, _P, _P, _U,
 lib.gdr2_chunk_fwd_ex.restype = ctypes.c_int
 lib.gdr_recurrent_step_ex.argtypes = [_I64] * 4 + [_E] + [_P] * 6 + [_E, _P, _U, _P]
 lib.gdr_recurrent_step_ex.restype = ctypes.c_int
+lib.gdr_output_gate.argtypes = [_I64] * 3 + [_E, _P, _E, _P, _P, ctypes.c_float, _E, _P, _P]
+lib.gdr_output_gate.restype = ctypes.c_int
 lib.gdr_status_string.argtypes = [ctypes.c_int]
 lib.gdr_status_string.restype = ctypes.c_char_p
 lib.gdr_version.restype = ctypes.c_int
@@ -197,3 +200,34 @@ def gdr_recurrent_step(q, k, v, alpha, beta, state, *, out_dtype=None,
     else:
         _run("gdr_recurrent_step", lib.gdr_recurrent_step(*args, _stream(stream)))
     return o
+
+
+def gdr_output_gate(o, g, w=None, eps=1e-6, *, out_dtype=None, y=None, stream=None):
+    """The block's output gate: y = o / sqrt(mean(o^2) + eps) * w * SiLU(g)
+    over the last axis (Dv = 64 or 128).  o, g [..., H, Dv] (fp32 or bf16,
+    each its own dtype); w [Dv] fp32 or None.  ``y`` may be ``o`` itself
+    (same dtype) for an in-place gate.  Returns y."""
+    if o.dim() < 2:
+        raise ValueError("o must be [..., H, Dv]")
+    H, Dv = o.shape[-2], o.shape[-1]
+    N = o.numel() // (H * Dv) if H * Dv else 0
+    for name, t in (("o", o), ("g", g)):
+        if t.dtype not in _DT:
+            raise TypeError(f"unsupported {name} dtype {t.dtype}")
+    _check("o", o, o.dtype, tuple(o.shape))
+    _check("g", g, g.dtype, tuple(o.shape))
+    if w is not None:
+        _check("w", w, torch.float32, (Dv,))
+    if out_dtype is None:
+        odt = o.dtype if y is None else y.dtype
+    else:
+        odt = out_dtype
+    if odt not in _DT:
+        raise TypeError(f"unsupported output dtype {odt}")
+    if y is None:
+        y = torch.empty(o.shape, dtype=odt, device=o.device)
+    _check("y", y, odt, tuple(o.shape))
+    _run("gdr_output_gate", lib.gdr_output_gate(
+        N, H, Dv, _DT[o.dtype], _ptr(o), _DT[g.dtype], _ptr(g), _ptr(w), float(eps),
+        _DT[odt], _ptr(y), _stream(stream)))
+    return y

@@ -220,6 +220,33 @@ extern "C" gdr_status_t gdr_recurrent_step(int64_t N, int64_t H, int64_t Dk, int
                                  0u, stream);
 }
 
+extern "C" gdr_status_t gdr_output_gate(int64_t N, int64_t H, int64_t Dv, gdr_dtype_t o_dt,
+                                        const void* o, gdr_dtype_t g_dt, const void* g,
+                                        const float* w, float eps, gdr_dtype_t out_dt, void* y,
+                                        hipStream_t stream) {
+    if (N < 0 || H < 0 || Dv < 0) return GDR_ERR_INVALID;
+    if (!sizes_ok(N, H, Dv)) return GDR_ERR_INVALID;
+    if (!dtype_ok(o_dt) || !dtype_ok(g_dt) || !dtype_ok(out_dt)) return GDR_ERR_UNSUPPORTED;
+    if (Dv != 64 && Dv != 128) return GDR_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f) || eps > 3.0e38f) return GDR_ERR_INVALID;
+    if (N == 0 || H == 0) return GDR_OK;
+    if (!ptrs_ok({o, g, y}) || !opt_ok(w)) return GDR_ERR_INVALID;
+    GateArgs a;
+    a.N = N;
+    a.H = H;
+    a.Dv = Dv;
+    a.o_bf16 = o_dt == GDR_BF16;
+    a.g_bf16 = g_dt == GDR_BF16;
+    a.out_bf16 = out_dt == GDR_BF16;
+    a.o = o;
+    a.g = g;
+    a.w = w;
+    a.eps = eps;
+    a.y = y;
+    a.stream = stream;
+    return from_hip(launch_output_gate(a));
+}
+
 extern "C" const char* gdr_status_string(gdr_status_t s) {
     switch (s) {
         case GDR_OK: return "ok";

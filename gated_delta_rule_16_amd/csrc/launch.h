@@ -35,7 +35,19 @@ struct ChunkArgs {
     hipStream_t stream;
 };
 
+// Output gate: o, g [N, H, Dv]; w [Dv] fp32 or NULL.
+struct GateArgs {
+    int64_t N, H, Dv;
+    bool o_bf16, g_bf16, out_bf16;
+    const void *o, *g;
+    const float* w;
+    float eps;
+    void* y;
+    hipStream_t stream;
+};
+
 hipError_t launch_step(const StepArgs& a);
+hipError_t launch_output_gate(const GateArgs& a);
 // fp32 inputs: VALU kernels, both rules.
 hipError_t launch_chunk_f32(const ChunkArgs& a);
 // bf16 inputs, scalar gates: bf16 MFMA kernel.

@@ -35,7 +35,7 @@ import torch
 
 __all__ = [
     "GdnInputs", "Gdn2Inputs", "DecodeInputs",
-    "make_gdn", "make_gdn2", "make_decode", "make_config", "CONFIGS",
+    "make_gdn", "make_gdn2", "make_decode", "make_config", "CONFIGS", "make_gate",
 ]
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -185,6 +185,29 @@ def make_decode(N: int, H: int, Dk: int, Dv: int, steps: int,
                         dict(N=N, H=H, Dk=Dk, Dv=Dv, steps=steps, seed=seed,
                              alpha_shift=alpha_shift, state_std=state_std,
                              raw_qk=raw_qk))
+
+
+@dataclass
+class GateInputs:
+    o: torch.Tensor
+    g: torch.Tensor
+    w: Optional[torch.Tensor]
+    meta: dict = field(default_factory=dict)
+
+
+def make_gate(N: int, H: int, Dv: int, o_dtype: str = "f32", g_dtype: str = "bf16",
+              seed: int = 0, weight: bool = True) -> GateInputs:
+    """Inputs of the output gate: o ~ N(0, 1) with each (token, head) row
+    scaled by exp(U(log 0.01, log 10)) (outputs of the rule span decades),
+    the gate pre-activation g ~ N(0, 2^2), the norm weight w ~ U(0.5, 1.5)."""
+    g_ = _rng(seed)
+    o = g_.standard_normal((N, H, Dv)) * np.exp(g_.uniform(np.log(0.01), np.log(10.0), (N, H, 1)))
+    gt = 2.0 * g_.standard_normal((N, H, Dv))
+    w = g_.uniform(0.5, 1.5, Dv) if weight else None
+    return GateInputs(_cast(o, o_dtype), _cast(gt, g_dtype),
+                      None if w is None else _cast(w, "f32"),
+                      dict(N=N, H=H, Dv=Dv, o_dtype=o_dtype, g_dtype=g_dtype, seed=seed,
+                           weight=weight))
 
 
 # The five workloads.  Seed = 1000 + index.  The long-context workload draws

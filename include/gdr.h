@@ -7,6 +7,9 @@
  *   gdr_recurrent_step  one decode token of the same rule, state in place
  *   gdr2_chunk_fwd      chunkwise forward of Gated Delta Rule-2 (channel gates)
  *
+ * plus their _ex variants (q, k L2-normalised on load) and the block's
+ * output gate on their result (gdr_output_gate).
+ *
  * The rule ("Gated Delta Networks", agihunt.info, "Method"; review of GDN on
  * meaningful96.github.io, section 3.4; inputs and outputs from its
  * section 1 "Problem Formulation"):
@@ -210,6 +213,33 @@ gdr_status_t gdr2_chunk_fwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                const void *write, const float *s0,
                                gdr_dtype_t out_dt, void *o, float *s_final,
                                uint32_t flags, hipStream_t stream);
+
+/*
+ * Output gate of the block, applied to the rule's output o per token and
+ * head over the Dv channels ("Gated DeltaNet-2", agihunt.info: the
+ * recurrent output passes an RMSNorm and a SiLU output gate; GDN review on
+ * meaningful96.github.io, section 3.8: normalisation and gating before the
+ * output projection):
+ *
+ *   y = o / sqrt(mean_c o_c^2 + eps) * w * g * sigmoid(g)
+ *
+ *   N, H        tokens (B * T), heads (each >= 0)
+ *   Dv          64 or 128
+ *   o_dt, o     [N, H, Dv] (the output of the calls above)
+ *   g_dt, g     [N, H, Dv], the gate branch's pre-activation
+ *   w           [Dv] fp32, the norm's per-channel weight, or NULL (ones)
+ *   eps         >= 0, added to the mean square inside the root
+ *   out_dt, y   [N, H, Dv]; y may be o itself when out_dt == o_dt
+ *
+ * One pass over HBM (o, g in, y out).  It is a call of its own and not a
+ * store-side epilogue of the chunk calls because those split a head's Dv
+ * channels over workgroups.  o, g and y need 16-byte alignment, w too when
+ * given.  Arithmetic in fp32; a bf16 y is rounded to nearest even.
+ */
+gdr_status_t gdr_output_gate(int64_t N, int64_t H, int64_t Dv, gdr_dtype_t o_dt,
+                             const void *o, gdr_dtype_t g_dt, const void *g,
+                             const float *w, float eps, gdr_dtype_t out_dt,
+                             void *y, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *gdr_status_string(gdr_status_t s);

@@ -21,6 +21,9 @@ gdn2_fwd(q, k, v, alpha, erase, write, s0=None) -> (o, s_final)
     write (write (.) v - read) along k.
 l2norm(x, eps=1e-6) -> x / sqrt(sum over the last axis of x^2 + eps)
     The block's L2 normalisation of q and k, applied before either rule.
+rmsnorm_gate(o, g, w=None, eps=1e-6) -> y
+    The block's output gate: RMSNorm of o over its last axis (weight w),
+    times SiLU(g).
 
 Parity pins: every function is pinned by tests/test_oracle.py against
 closed forms, invariants, exact rational worked examples
@@ -39,7 +42,7 @@ _SRC = os.path.join(_HERE, "gdr_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 __all__ = ["build", "OracleLib", "default", "gdn_fwd", "gdn_step",
-           "gdn2_fwd", "l2norm", "num_threads", "set_num_threads", "err_rms"]
+           "gdn2_fwd", "l2norm", "rmsnorm_gate", "num_threads", "set_num_threads", "err_rms"]
 
 
 def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
@@ -79,6 +82,8 @@ class OracleLib:
         lib.oracle_gdn2_fwd.restype = ctypes.c_int
         lib.oracle_l2norm_rows.argtypes = [L, L, P, ctypes.c_double, P]
         lib.oracle_l2norm_rows.restype = ctypes.c_int
+        lib.oracle_rmsnorm_gate_rows.argtypes = [L, L, P, P, P, ctypes.c_double, P]
+        lib.oracle_rmsnorm_gate_rows.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         self.lib = lib
@@ -161,6 +166,21 @@ class OracleLib:
             raise RuntimeError(f"oracle_l2norm_rows failed ({rc})")
         return out
 
+    def rmsnorm_gate(self, o, g, w=None, eps=1e-6):
+        """Output gate on rows of the last axis (``oracle_rmsnorm_gate_rows``):
+        o / sqrt(mean(o^2) + eps) * w * g * sigmoid(g); w of the last axis'
+        length or None (ones).  float64."""
+        o, g, w = _f64(o), _f64(g), _f64(w)
+        assert o.shape == g.shape and o.ndim >= 1
+        d = o.shape[-1]
+        assert w is None or w.shape == (d,)
+        y = np.empty_like(o)
+        rc = self.lib.oracle_rmsnorm_gate_rows(o.size // d, d, _p(o), _p(g), _p(w),
+                                               float(eps), _p(y))
+        if rc:
+            raise RuntimeError(f"oracle_rmsnorm_gate_rows failed ({rc})")
+        return y
+
 
 _default = None
 
@@ -208,6 +228,13 @@ def l2norm(*a, **kw):
 
 
 l2norm.__doc__ = OracleLib.l2norm.__doc__
+
+
+def rmsnorm_gate(*a, **kw):
+    return default().rmsnorm_gate(*a, **kw)
+
+
+rmsnorm_gate.__doc__ = OracleLib.rmsnorm_gate.__doc__
 
 
 def err_rms(x_hat, x) -> float:

@@ -206,6 +206,35 @@ int oracle_l2norm_rows(long n, long d, const double *x, double eps, double *out)
     return 0;
 }
 
+/*
+ * Output gate of the block on each row of d values (one token and head):
+ *
+ *   y_i = o_i / sqrt(mean_j o_j^2 + eps) * w_i * g_i * sigmoid(g_i),
+ *
+ * an RMS normalisation of the recurrent output followed by a SiLU output
+ * gate (the Gated DeltaNet-2 page: the recurrent output passes an RMSNorm
+ * and a SiLU output gate; review on meaningful96.github.io, section 3.8:
+ * normalisation and gating on the output before the output projection).
+ * w (d values, shared by every row) is the norm's per-channel weight, NULL
+ * meaning all ones; g is the gate branch's pre-activation.  The mean runs
+ * over the d channels of the row.
+ */
+int oracle_rmsnorm_gate_rows(long n, long d, const double *o, const double *g,
+                             const double *w, double eps, double *y) {
+    if (n < 0 || d <= 0 || !(eps >= 0.0)) return 1;
+    for (long r = 0; r < n; ++r) {
+        const double *orow = o + r * d, *grow = g + r * d;
+        double ss = 0.0;
+        for (long c = 0; c < d; ++c) ss += orow[c] * orow[c];
+        const double inv = 1.0 / sqrt(ss / (double)d + eps);
+        for (long c = 0; c < d; ++c) {
+            const double gate = grow[c] / (1.0 + exp(-grow[c]));
+            y[r * d + c] = orow[c] * inv * (w ? w[c] : 1.0) * gate;
+        }
+    }
+    return 0;
+}
+
 /* Threads the oracle's parallel loops use (reported with CPU timings). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

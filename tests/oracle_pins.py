@@ -496,6 +496,55 @@ def pin_l2norm_rows(orc):
     np.testing.assert_allclose(out * nrm, x, rtol=1e-13, atol=0)
 
 
+# --- the block's output gate -------------------------------------------------
+def _silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def pin_gate_worked(orc):
+    """Worked row, eps = 0, w = 1: o = (3, 4) has mean square 12.5, so the
+    normalised row is (3, 4) / sqrt(12.5); g = (0, 30) gates it by
+    SiLU(0) = 0 and SiLU(30) = 30 / (1 + e^-30).  A gate of ln 3 gives
+    SiLU = ln 3 * 3/4 exactly in closed form."""
+    y = orc.rmsnorm_gate(np.array([[3.0, 4.0]]), np.array([[0.0, 30.0]]), eps=0.0)
+    ref = np.array([[0.0, 4.0 / np.sqrt(12.5) * 30.0 / (1.0 + np.exp(-30.0))]])
+    np.testing.assert_allclose(y, ref, rtol=1e-15, atol=0)
+    y = orc.rmsnorm_gate(np.array([[2.0, 2.0, 2.0]]), np.full((1, 3), np.log(3.0)), eps=0.0)
+    np.testing.assert_allclose(y, np.full((1, 3), np.log(3.0) * 0.75), rtol=1e-15)
+
+
+def pin_gate_rms_and_eps(orc):
+    """With a gate that makes SiLU = 1 and w = 1, every row comes out with
+    mean square r^2 / (r^2 + eps) for an input of mean square r^2 (eps inside
+    the root, mean over the row, rows independent)."""
+    g0 = 1.2784645427610738                     # SiLU(g0) = 1
+    assert abs(_silu(g0) - 1.0) < 1e-15
+    rng = _rng(28)
+    o = rng.standard_normal((5, 7)) * rng.uniform(0.001, 10.0, (5, 1))
+    for eps in (0.0, 1e-6, 1e-2):
+        y = orc.rmsnorm_gate(o, np.full_like(o, g0), eps=eps)
+        r2 = np.mean(o * o, axis=-1)
+        np.testing.assert_allclose(np.mean(y * y, axis=-1), r2 / (r2 + eps), rtol=1e-13)
+        np.testing.assert_allclose(y * np.sqrt(r2 + eps)[:, None], o, rtol=1e-13)
+
+
+def pin_gate_weight_axis(orc):
+    """The weight scales channels (the last axis), the same for every row;
+    the gate acts elementwise."""
+    rng = _rng(29)
+    o = rng.standard_normal((4, 6))
+    g = rng.standard_normal((4, 6))
+    w = rng.uniform(0.5, 2.0, 6)
+    y1 = orc.rmsnorm_gate(o, g, None, eps=1e-6)
+    y2 = orc.rmsnorm_gate(o, g, w, eps=1e-6)
+    np.testing.assert_allclose(y2, y1 * w[None, :], rtol=1e-14)
+    g2 = g.copy(); g2[1, 3] = -g2[1, 3]
+    y3 = orc.rmsnorm_gate(o, g2, w, eps=1e-6)
+    mask = np.ones_like(o, dtype=bool); mask[1, 3] = False
+    np.testing.assert_array_equal(y3[mask], y2[mask])
+    np.testing.assert_allclose(y3[1, 3] / y2[1, 3], _silu(g2[1, 3]) / _silu(g[1, 3]), rtol=1e-13)
+
+
 ALL_PINS = [
     pin_golden_gdn, pin_golden_step, pin_golden_gdn2,
     pin_exact_matrix_form_gdn, pin_exact_matrix_form_gdn2,
@@ -505,4 +554,5 @@ ALL_PINS = [
     pin_j_contraction, pin_k_kda, pin_gdn2_pure_decay, pin_gdn2_write_only,
     pin_gdn2_erase_axis, pin_gdn2_householder, pin_gdn_negative_beta,
     pin_l2norm_worked, pin_l2norm_eps, pin_l2norm_rows,
+    pin_gate_worked, pin_gate_rms_and_eps, pin_gate_weight_axis,
 ]

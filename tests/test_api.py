@@ -27,6 +27,7 @@ def test_header_declares_the_three_operations():
     names = declared_functions()
     for n in ("gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd",
               "gdr_chunk_fwd_ex", "gdr_recurrent_step_ex", "gdr2_chunk_fwd_ex",
+              "gdr_output_gate",
               "gdr_status_string", "gdr_version"):
         assert n in names, names
 
@@ -141,3 +142,22 @@ def test_ex_variants_check_flags(gdr):
                               None, None, f, None) == 0
     assert L.gdr_recurrent_step_ex(0, 1, 64, 64, 1, None, None, None, None, None, None,
                                    1, None, f, None) == 0
+
+
+def gate(gdr, N=4, H=2, Dv=128, odt_in=1, o=A16, gdt=1, g=A16, w=None, eps=1e-6, odt=1, y=A16):
+    return gdr.lib.gdr_output_gate(N, H, Dv, odt_in, o, gdt, g, w, eps, odt, y, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=None), 1), (dict(g=None), 1), (dict(y=None), 1), (dict(o=BAD), 1),
+    (dict(g=BAD), 1), (dict(y=BAD), 1), (dict(w=BAD), 1), (dict(N=-1), 1), (dict(H=-1), 1),
+    (dict(eps=-1.0), 1), (dict(eps=float("nan")), 1), (dict(eps=float("inf")), 1),
+    (dict(Dv=96), 2), (dict(Dv=32), 2), (dict(odt_in=3), 2), (dict(gdt=9), 2), (dict(odt=4), 2),
+])
+def test_output_gate_validation(gdr, kw, code):
+    assert gate(gdr, **kw) == code
+
+
+def test_output_gate_empty(gdr):
+    assert gate(gdr, N=0, o=None, g=None, y=None) == 0
+    assert gate(gdr, H=0, o=None, g=None, y=None) == 0

@@ -39,6 +39,11 @@ MUTANTS = [
     ("l2norm_row_shift", "const double *xr = x + r * d;",
      "const double *xr = x + (r + 1 < n ? r + 1 : r) * d;"),
     ("l2norm_sign_lost", "out[r * d + c] = xr[c] * inv", "out[r * d + c] = fabs(xr[c]) * inv"),
+    ("gate_sum_not_mean", "sqrt(ss / (double)d + eps)", "sqrt(ss + eps)"),
+    ("gate_eps_outside_root", "sqrt(ss / (double)d + eps)", "(sqrt(ss / (double)d) + eps)"),
+    ("gate_sigmoid_not_silu", "const double gate = grow[c] / (1.0 + exp(-grow[c]));",
+     "const double gate = 1.0 / (1.0 + exp(-grow[c]));"),
+    ("gate_weight_by_row", "(w ? w[c] : 1.0)", "(w ? w[r < d ? r : 0] : 1.0)"),
 ]
 
 
