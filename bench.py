@@ -383,6 +383,9 @@ def main():
     ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "longctx", "l2norm", "gate", "copy"],
                     default=None,
                     help="time one operation only (for profiling)")
+    ap.add_argument("--skip", default="",
+                    help="comma-separated legs not to run (the profiled command skips l2norm, "
+                         "whose plain calls reuse the headline kernels)")
     ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarize rocprofv3 CSV output into OUT and the traffic JSON, then exit")
     ap.add_argument("--command", default="", help="the profiling command, recorded in --summarize")
@@ -402,28 +405,33 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
 
+    skip = set(x for x in args.skip.split(",") if x)
+
+    def want(leg):
+        return args.only in (None, leg) and leg not in skip
+
     res = {}
-    if args.only in (None, "gdn"):
+    if want("gdn"):
         log("timing gdr_chunk_fwd B8 H16 T4096 d128 ...")
         res["gdn"] = bench_gdn(gdr, torch, args.warmup, args.steps)
         log(f"  mean {res['gdn']['mean'] * 1e6:.1f} us")
-    if args.only in (None, "decode"):
+    if want("decode"):
         log("timing gdr_recurrent_step N256 H16 d128 x 64 steps ...")
         res["decode"] = bench_decode(gdr, torch, args.warmup)
         log(f"  median {res['decode']['median'] * 1e6:.1f} us/step")
-    if args.only in (None, "gdr2"):
+    if want("gdr2"):
         log("timing gdr2_chunk_fwd B4 H16 T4096 d128 ...")
         res["gdr2"] = bench_gdr2(gdr, torch, args.warmup, args.steps)
-    if args.only in (None, "longctx"):
+    if want("longctx"):
         log("timing gdr_chunk_fwd B1 H16 T32768 d128 (long context) ...")
         res["longctx"] = bench_longctx(gdr, torch, min(args.warmup, 10), min(args.steps, 10))
-    if args.only in (None, "l2norm"):
+    if want("l2norm"):
         log("timing the fused q, k normalisation (GDN and GDN-2 workloads) ...")
         res["l2norm"] = bench_l2norm(gdr, torch, args.warmup, min(args.steps, 30))
-    if args.only in (None, "gate"):
+    if want("gate"):
         log("timing gdr_output_gate B8 T4096 H16 d128 ...")
         res["gate"] = bench_gate(gdr, torch, args.warmup, args.steps)
-    if args.only in (None, "copy"):
+    if want("copy"):
         log("timing a 512 MiB device copy ...")
         res["copy"] = bench_copy(torch, args.warmup, args.steps)
 
