@@ -21,6 +21,8 @@ gdn2_fwd(q, k, v, alpha, erase, write, s0=None) -> (o, s_final)
     write (write (.) v - read) along k.
 l2norm(x, eps=1e-6) -> x / sqrt(sum over the last axis of x^2 + eps)
     The block's L2 normalisation of q and k, applied before either rule.
+gdn_bwd(q, k, v, alpha, beta, s0, dout, ds_final=None)
+    -> (dq, dk, dv, dalpha, dbeta, ds0), the reverse mode of gdn_fwd.
 rmsnorm_gate(o, g, w=None, eps=1e-6) -> y
     The block's output gate: RMSNorm of o over its last axis (weight w),
     times SiLU(g).
@@ -42,7 +44,7 @@ _SRC = os.path.join(_HERE, "gdr_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 __all__ = ["build", "OracleLib", "default", "gdn_fwd", "gdn_step",
-           "gdn2_fwd", "l2norm", "rmsnorm_gate", "num_threads", "set_num_threads", "err_rms"]
+           "gdn2_fwd", "gdn_bwd", "l2norm", "rmsnorm_gate", "num_threads", "set_num_threads", "err_rms"]
 
 
 def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
@@ -80,6 +82,8 @@ class OracleLib:
         lib.oracle_gdn_step.restype = ctypes.c_int
         lib.oracle_gdn2_fwd.argtypes = [L] * 5 + [P] * 9
         lib.oracle_gdn2_fwd.restype = ctypes.c_int
+        lib.oracle_gdn_bwd.argtypes = [L] * 5 + [P] * 14
+        lib.oracle_gdn_bwd.restype = ctypes.c_int
         lib.oracle_l2norm_rows.argtypes = [L, L, P, ctypes.c_double, P]
         lib.oracle_l2norm_rows.restype = ctypes.c_int
         lib.oracle_rmsnorm_gate_rows.argtypes = [L, L, P, P, P, ctypes.c_double, P]
@@ -154,6 +158,30 @@ class OracleLib:
             raise RuntimeError(f"oracle_gdn2_fwd failed ({rc})")
         return o, sf
 
+    def gdn_bwd(self, q, k, v, alpha, beta, s0, dout, ds_final=None):
+        """Reverse mode of the gated delta rule (``oracle_gdn_bwd``): the
+        gradients of sum(o * dout) + sum(S_T * ds_final) with respect to q,
+        k, v, alpha, beta and s0.  Returns float64 (dq, dk, dv, dalpha,
+        dbeta, ds0); s0 None means a zero initial state (ds0 still
+        returned)."""
+        q, k, v, a, b, s0, do, dsf = map(_f64, (q, k, v, alpha, beta, s0, dout, ds_final))
+        B, T, H, Dk = q.shape
+        Dv = v.shape[-1]
+        assert k.shape == q.shape and v.shape == (B, T, H, Dv) and do.shape == v.shape
+        assert a.shape == (B, T, H) and b.shape == (B, T, H)
+        assert s0 is None or s0.shape == (B, H, Dv, Dk)
+        assert dsf is None or dsf.shape == (B, H, Dv, Dk)
+        dq, dk = np.empty_like(q), np.empty_like(k)
+        dv = np.empty_like(v)
+        da, db = np.empty_like(a), np.empty_like(b)
+        ds0 = np.empty((B, H, Dv, Dk))
+        rc = self.lib.oracle_gdn_bwd(B, T, H, Dk, Dv, _p(q), _p(k), _p(v), _p(a), _p(b),
+                                     _p(s0), _p(do), _p(dsf), _p(dq), _p(dk), _p(dv),
+                                     _p(da), _p(db), _p(ds0))
+        if rc:
+            raise RuntimeError(f"oracle_gdn_bwd failed ({rc})")
+        return dq, dk, dv, da, db, ds0
+
     def l2norm(self, x, eps=1e-6):
         """Rows of x (last axis) scaled to unit L2 norm,
         x / sqrt(sum x^2 + eps) (``oracle_l2norm_rows``).  float64."""
@@ -221,6 +249,13 @@ def gdn2_fwd(*a, **kw):
 
 
 gdn2_fwd.__doc__ = OracleLib.gdn2_fwd.__doc__
+
+
+def gdn_bwd(*a, **kw):
+    return default().gdn_bwd(*a, **kw)
+
+
+gdn_bwd.__doc__ = OracleLib.gdn_bwd.__doc__
 
 
 def l2norm(*a, **kw):

@@ -103,6 +103,143 @@ int oracle_gdn_fwd(long B, long T, long H, long Dk, long Dv, const double *q,
 }
 
 /*
+ * Reverse mode of the gated delta rule (the derivative of oracle_gdn_fwd,
+ * written out token by token by the chain rule).  The pages describe the
+ * method's throughput as a training workload, and the GDN-2 summary notes
+ * that a chunked backward must carry the gates inside its dot products;
+ * this is the plain definition such a backward must reproduce.
+ *
+ * Per token, with u = S_{t-1} k, c = beta v - alpha beta u, the forward is
+ * S_t = alpha S_{t-1} + c k^T and o_t = S_t q.  Given G = dL/dS_t (the
+ * gradient carried back from later tokens, dL/dS_T at the end) and do_t:
+ *
+ *   G    += do_t q^T            dq_t  = S_t^T do_t
+ *   dc    = G k                 dk_t  = G^T c + S_{t-1}^T du,  du = -alpha beta dc
+ *   dv_t  = beta dc             dbeta = dc . (v - alpha u)
+ *   dalpha = <G, S_{t-1}>_F - beta (dc . u)
+ *   G    <- alpha G + du k^T    (dL/dS_{t-1});  dS_0 = G at the start.
+ *
+ * dout [B,T,H,Dv]; ds_final [B,H,Dv,Dk] or NULL (zero); outputs dq, dk
+ * [B,T,H,Dk], dv [B,T,H,Dv], dalpha, dbeta [B,T,H], ds0 [B,H,Dv,Dk] or NULL.
+ * States are kept every SEG tokens and recomputed inside each segment.
+ */
+#define ORACLE_BWD_SEG 64
+static void gdn_step_state(double *S, const double *Sprev, long Dk, long Dv,
+                           const double *k, const double *v, double alpha,
+                           double beta) {
+    for (long i = 0; i < Dv; ++i) {
+        const double *sp = Sprev + i * Dk;
+        double *s = S + i * Dk;
+        double u = 0.0;
+        for (long j = 0; j < Dk; ++j) u += sp[j] * k[j];
+        const double c = beta * v[i] - alpha * beta * u;
+        for (long j = 0; j < Dk; ++j) s[j] = alpha * sp[j] + c * k[j];
+    }
+}
+
+int oracle_gdn_bwd(long B, long T, long H, long Dk, long Dv, const double *q,
+                   const double *k, const double *v, const double *alpha,
+                   const double *beta, const double *s0, const double *dout,
+                   const double *ds_final, double *dq, double *dk, double *dv,
+                   double *dalpha, double *dbeta, double *ds0) {
+    if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return ORACLE_ERR_ARGS;
+    if (!q || !k || !v || !alpha || !beta || !dout || !dq || !dk || !dv || !dalpha || !dbeta)
+        return ORACLE_ERR_ARGS;
+    const long SEG = ORACLE_BWD_SEG;
+    const long nseg = (T + SEG - 1) / SEG;
+    int err = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (long b = 0; b < B; ++b) {
+        for (long h = 0; h < H; ++h) {
+            const size_t SS = (size_t)(Dv * Dk);
+            /* segment-start states, the states inside one segment, G, work */
+            double *ck = (double *)malloc(sizeof(double) * SS * (size_t)(nseg + 1));
+            double *st = (double *)malloc(sizeof(double) * SS * (size_t)(SEG + 1));
+            double *G = (double *)malloc(sizeof(double) * SS);
+            double *cv = (double *)malloc(sizeof(double) * (size_t)Dv);
+            double *uv = (double *)malloc(sizeof(double) * (size_t)Dv);
+            double *dcv = (double *)malloc(sizeof(double) * (size_t)Dv);
+            if (!ck || !st || !G || !cv || !uv || !dcv) {
+#pragma omp atomic write
+                err = 1;
+                free(ck); free(st); free(G); free(cv); free(uv); free(dcv);
+                continue;
+            }
+            state_init(ck, s0 ? s0 + (b * H + h) * SS : NULL, Dv, Dk);
+            for (long sg = 0; sg < nseg; ++sg) {
+                memcpy(st, ck + sg * SS, sizeof(double) * SS);
+                const long t1 = (sg + 1) * SEG < T ? (sg + 1) * SEG : T;
+                for (long t = sg * SEG; t < t1; ++t) {
+                    const long bth = (b * T + t) * H + h;
+                    gdn_step_state(st, st, Dk, Dv, k + bth * Dk, v + bth * Dv, alpha[bth], beta[bth]);
+                }
+                memcpy(ck + (sg + 1) * SS, st, sizeof(double) * SS);
+            }
+            if (ds_final)
+                memcpy(G, ds_final + (b * H + h) * SS, sizeof(double) * SS);
+            else
+                memset(G, 0, sizeof(double) * SS);
+            for (long sg = nseg - 1; sg >= 0; --sg) {
+                const long t0 = sg * SEG;
+                const long t1 = t0 + SEG < T ? t0 + SEG : T;
+                /* st[j] = S_{t0 + j}, j = 0 .. t1 - t0 */
+                memcpy(st, ck + sg * SS, sizeof(double) * SS);
+                for (long t = t0; t < t1; ++t) {
+                    const long bth = (b * T + t) * H + h;
+                    gdn_step_state(st + (t - t0 + 1) * SS, st + (t - t0) * SS, Dk, Dv,
+                                   k + bth * Dk, v + bth * Dv, alpha[bth], beta[bth]);
+                }
+                for (long t = t1 - 1; t >= t0; --t) {
+                    const long bth = (b * T + t) * H + h;
+                    const double *Sp = st + (t - t0) * SS;       /* S_{t-1} */
+                    const double *Sn = st + (t - t0 + 1) * SS;   /* S_t */
+                    const double *qt = q + bth * Dk, *kt = k + bth * Dk, *vt = v + bth * Dv;
+                    const double *dot = dout + bth * Dv;
+                    const double a = alpha[bth], be = beta[bth];
+                    double *dqt = dq + bth * Dk, *dkt = dk + bth * Dk, *dvt = dv + bth * Dv;
+                    for (long i = 0; i < Dv; ++i)
+                        for (long j = 0; j < Dk; ++j) G[i * Dk + j] += dot[i] * qt[j];
+                    for (long j = 0; j < Dk; ++j) {
+                        double x = 0.0;
+                        for (long i = 0; i < Dv; ++i) x += Sn[i * Dk + j] * dot[i];
+                        dqt[j] = x;
+                    }
+                    double dbt = 0.0, dat = 0.0;
+                    for (long i = 0; i < Dv; ++i) {
+                        double u = 0.0, dc = 0.0, gs = 0.0;
+                        for (long j = 0; j < Dk; ++j) {
+                            u += Sp[i * Dk + j] * kt[j];
+                            dc += G[i * Dk + j] * kt[j];
+                            gs += G[i * Dk + j] * Sp[i * Dk + j];
+                        }
+                        uv[i] = u;
+                        cv[i] = be * vt[i] - a * be * u;
+                        dcv[i] = dc;
+                        dvt[i] = be * dc;
+                        dbt += dc * (vt[i] - a * u);
+                        dat += gs - be * dc * u;
+                    }
+                    dbeta[bth] = dbt;
+                    dalpha[bth] = dat;
+                    for (long j = 0; j < Dk; ++j) {
+                        double x = 0.0;
+                        for (long i = 0; i < Dv; ++i)
+                            x += G[i * Dk + j] * cv[i] - a * be * dcv[i] * Sp[i * Dk + j];
+                        dkt[j] = x;
+                    }
+                    for (long i = 0; i < Dv; ++i)
+                        for (long j = 0; j < Dk; ++j)
+                            G[i * Dk + j] = a * G[i * Dk + j] - a * be * dcv[i] * kt[j];
+                }
+            }
+            if (ds0) memcpy(ds0 + (b * H + h) * SS, G, sizeof(double) * SS);
+            free(ck); free(st); free(G); free(cv); free(uv); free(dcv);
+        }
+    }
+    return err ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}
+
+/*
  * One decode step for N independent sequences: the same single-token update
  * applied in place to state [N, H, Dv, Dk], with q, k [N, H, Dk],
  * v [N, H, Dv], alpha, beta [N, H] and o [N, H, Dv].  A fixed-size state

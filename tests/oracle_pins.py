@@ -462,6 +462,82 @@ def pin_gdn_negative_beta(orc):
     np.testing.assert_allclose(s1[0, 0], ref, rtol=0, atol=1e-12)
 
 
+# --- reverse mode of the scalar-gate rule ------------------------------------
+def _gdn_loss(orc, q, k, v, a, b, S0, do, dsf):
+    o, sf = orc.gdn_fwd(q, k, v, a, b, S0)
+    return float(np.sum(o * do) + np.sum(sf * dsf))
+
+
+def pin_bwd_finite_differences(orc):
+    """Every gradient of L = sum(o * dout) + sum(S_T * dS_T) against central
+    differences of the forward oracle, element by element on a tiny case
+    (T = 6, H = 2, d_k = 4, d_v = 3, with S_0); step 1e-5, so the error is
+    ~1e-10 of the gradient scale."""
+    q, k, v, a, b, S0 = rand_gdn(30, B=1, T=6, H=2, Dk=4, Dv=3)
+    g = _rng(31)
+    do = g.standard_normal((1, 6, 2, 3))
+    dsf = g.standard_normal((1, 2, 3, 4))
+    grads = orc.gdn_bwd(q, k, v, a, b, S0, do, dsf)
+    args = [q, k, v, a, b, S0]
+    h = 1e-5
+    for idx, x in enumerate(args):
+        num = np.zeros_like(x)
+        for pos in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += h
+            xm[pos] -= h
+            ap, am = list(args), list(args)
+            ap[idx], am[idx] = xp, xm
+            num[pos] = (_gdn_loss(orc, *ap, do, dsf) - _gdn_loss(orc, *am, do, dsf)) / (2 * h)
+        scale = max(1.0, np.abs(num).max())
+        assert np.abs(grads[idx] - num).max() <= 1e-7 * scale, (idx, np.abs(grads[idx] - num).max())
+
+
+def pin_bwd_directional(orc):
+    """Directional derivatives along random directions on a case that crosses
+    the oracle's 64-token recompute segments (T = 150) and has no S_T
+    gradient and no S_0."""
+    q, k, v, a, b, _ = rand_gdn(32, B=2, T=150, H=1, Dk=5, Dv=4, s0=False)
+    g = _rng(33)
+    do = g.standard_normal(v.shape)
+    zs = np.zeros((2, 1, 4, 5))
+    dq, dk, dv, da, db, ds0 = orc.gdn_bwd(q, k, v, a, b, None, do, None)
+    S0 = np.zeros((2, 1, 4, 5))
+    for d in range(3):
+        dirs = [g.standard_normal(x.shape) for x in (q, k, v, a, b, S0)]
+        h = 1e-5
+        xp = [x + h * e for x, e in zip((q, k, v, a, b, S0), dirs)]
+        xm = [x - h * e for x, e in zip((q, k, v, a, b, S0), dirs)]
+        num = (_gdn_loss(orc, *xp, do, zs) - _gdn_loss(orc, *xm, do, zs)) / (2 * h)
+        ana = sum(float(np.sum(gr * e)) for gr, e in zip((dq, dk, dv, da, db, ds0), dirs))
+        assert abs(num - ana) <= 1e-7 * max(1.0, abs(ana)), (d, num, ana)
+
+
+def pin_bwd_autograd_matrix_form(orc):
+    """The gradients equal autograd's through the literal matrix form
+    S_t = alpha S_{t-1} (I - beta k k^T) + beta v k^T, o_t = S_t q_t in
+    torch fp64 (a different formulation from the oracle's row loops)."""
+    q, k, v, a, b, S0 = rand_gdn(34, B=1, T=20, H=2, Dk=6, Dv=5)
+    g = _rng(35)
+    do = g.standard_normal(v.shape)
+    dsf = g.standard_normal(S0.shape)
+    t = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v, a, b, S0)]
+    tq, tk, tv, ta, tb, tS = t
+    loss = 0.0
+    for h in range(2):
+        S = tS[0, h]
+        for s in range(20):
+            kk = tk[0, s, h]
+            S = ta[0, s, h] * S @ (torch.eye(6, dtype=torch.float64) - tb[0, s, h] * torch.outer(kk, kk)) \
+                + tb[0, s, h] * torch.outer(tv[0, s, h], kk)
+            loss = loss + (S @ tq[0, s, h] * torch.tensor(do[0, s, h])).sum()
+        loss = loss + (S * torch.tensor(dsf[0, h])).sum()
+    loss.backward()
+    grads = orc.gdn_bwd(q, k, v, a, b, S0, do, dsf)
+    for x, gr in zip(t, grads):
+        np.testing.assert_allclose(gr, x.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
 # --- the block's L2 normalisation of q and k --------------------------------
 def pin_l2norm_worked(orc):
     """Worked rows with eps = 0: (3, 4) -> (0.6, 0.8); (1, 1, 1, 1) ->
@@ -555,4 +631,5 @@ ALL_PINS = [
     pin_gdn2_erase_axis, pin_gdn2_householder, pin_gdn_negative_beta,
     pin_l2norm_worked, pin_l2norm_eps, pin_l2norm_rows,
     pin_gate_worked, pin_gate_rms_and_eps, pin_gate_weight_axis,
+    pin_bwd_finite_differences, pin_bwd_directional, pin_bwd_autograd_matrix_form,
 ]

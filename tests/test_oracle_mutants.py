@@ -44,6 +44,14 @@ MUTANTS = [
     ("gate_sigmoid_not_silu", "const double gate = grow[c] / (1.0 + exp(-grow[c]));",
      "const double gate = 1.0 / (1.0 + exp(-grow[c]));"),
     ("gate_weight_by_row", "(w ? w[c] : 1.0)", "(w ? w[r < d ? r : 0] : 1.0)"),
+    ("bwd_dalpha_missing_read_term", "dat += gs - be * dc * u;", "dat += gs;"),
+    ("bwd_dk_missing_read_path", "x += G[i * Dk + j] * cv[i] - a * be * dcv[i] * Sp[i * Dk + j];",
+     "x += G[i * Dk + j] * cv[i];"),
+    ("bwd_carry_without_decay", "G[i * Dk + j] = a * G[i * Dk + j] - a * be * dcv[i] * kt[j];",
+     "G[i * Dk + j] = G[i * Dk + j] - a * be * dcv[i] * kt[j];"),
+    ("bwd_dq_from_old_state", "x += Sn[i * Dk + j] * dot[i];", "x += Sp[i * Dk + j] * dot[i];"),
+    ("bwd_segment_off_by_one", "memcpy(st, ck + sg * SS, sizeof(double) * SS);\n                for (long t = t0; t < t1; ++t) {",
+     "memcpy(st, ck + (sg > 0 ? sg - 1 : 0) * SS, sizeof(double) * SS);\n                for (long t = t0; t < t1; ++t) {"),
 ]
 
 
