@@ -46,7 +46,20 @@ struct GateArgs {
     hipStream_t stream;
 };
 
+// Backward of the scalar-gate rule; gradients fp32, workspace from the caller.
+struct BwdArgs {
+    int64_t B, T, H, Dk, Dv;
+    bool in_bf16, dout_bf16;
+    const void *q, *k, *v, *dout;
+    const float *alpha, *beta, *s0, *ds_final;
+    float *dq, *dk, *dv, *dalpha, *dbeta, *ds0;
+    void* workspace;
+    hipStream_t stream;
+};
+
 hipError_t launch_step(const StepArgs& a);
+hipError_t launch_chunk_bwd(const BwdArgs& a);
+size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv);
 hipError_t launch_output_gate(const GateArgs& a);
 // fp32 inputs: VALU kernels, both rules.
 hipError_t launch_chunk_f32(const ChunkArgs& a);

@@ -7,8 +7,9 @@
  *   gdr_recurrent_step  one decode token of the same rule, state in place
  *   gdr2_chunk_fwd      chunkwise forward of Gated Delta Rule-2 (channel gates)
  *
- * plus their _ex variants (q, k L2-normalised on load) and the block's
- * output gate on their result (gdr_output_gate).
+ * plus their _ex variants (q, k L2-normalised on load), the block's
+ * output gate on their result (gdr_output_gate) and the reverse mode of
+ * the chunkwise forward (gdr_chunk_bwd).
  *
  * The rule ("Gated Delta Networks", agihunt.info, "Method"; review of GDN on
  * meaningful96.github.io, section 3.4; inputs and outputs from its
@@ -240,6 +241,49 @@ gdr_status_t gdr_output_gate(int64_t N, int64_t H, int64_t Dv, gdr_dtype_t o_dt,
                              const void *o, gdr_dtype_t g_dt, const void *g,
                              const float *w, float eps, gdr_dtype_t out_dt,
                              void *y, hipStream_t stream);
+
+/*
+ * Reverse mode of gdr_chunk_fwd (the scalar-gate rule): the gradients of a
+ * loss L through o and the final state, given dL/do and dL/dS_T.  It is the
+ * chain rule through the chunkwise form of the rule ("Gated Delta
+ * Networks", agihunt.info, "Method"; GDN review on meaningful96.github.io,
+ * section 3.7), evaluated chunk by chunk in fp32: the pages' throughput
+ * figures are for training, and the GDN-2 summary notes that a chunked
+ * backward carries the gates inside its dot products.
+ *
+ *   q, k, v, alpha, beta, s0, in_dt  the forward's inputs, as for gdr_chunk_fwd
+ *   dout_dt, dout  [B, T, H, Dv] dL/do (GDR_F32 or GDR_BF16)
+ *   ds_final       [B, H, Dv, Dk] fp32 dL/dS_T, or NULL (zero)
+ *   dq, dk         [B, T, H, Dk] fp32 (written)
+ *   dv             [B, T, H, Dv] fp32 (written)
+ *   dalpha, dbeta  [B, T, H] fp32 (written).  dalpha is dL/d(log alpha)
+ *                  divided by alpha, alpha clamped to FLT_MIN as in the
+ *                  forward's logarithm
+ *   ds0            [B, H, Dv, Dk] fp32 dL/dS_0, or NULL (not written)
+ *   workspace      device memory of at least
+ *                  gdr_chunk_bwd_workspace_size(B, T, H, Dk, Dv) bytes,
+ *                  16-byte aligned, owned by the caller; its contents on
+ *                  entry do not matter and on return are unspecified.
+ *                  It holds the chunk-start states (B H ceil(T/32) Dv Dk
+ *                  floats) and per-row-block partial sums.  A smaller
+ *                  workspace_bytes is GDR_ERR_INVALID.
+ *
+ * Calls on one workspace must not overlap.  T == 0 copies ds_final (or
+ * zeros) into ds0.  Alignment: as for gdr_chunk_fwd, plus dq, dk, dv,
+ * dout and the workspace 16 bytes, dalpha and dbeta 4 bytes.
+ */
+size_t gdr_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H,
+                                    int64_t Dk, int64_t Dv);
+
+gdr_status_t gdr_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                           int64_t Dv, gdr_dtype_t in_dt, const void *q,
+                           const void *k, const void *v, const float *alpha,
+                           const float *beta, const float *s0,
+                           gdr_dtype_t dout_dt, const void *dout,
+                           const float *ds_final, float *dq, float *dk,
+                           float *dv, float *dalpha, float *dbeta, float *ds0,
+                           void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *gdr_status_string(gdr_status_t s);

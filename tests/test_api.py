@@ -27,7 +27,7 @@ def test_header_declares_the_three_operations():
     names = declared_functions()
     for n in ("gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd",
               "gdr_chunk_fwd_ex", "gdr_recurrent_step_ex", "gdr2_chunk_fwd_ex",
-              "gdr_output_gate",
+              "gdr_output_gate", "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size",
               "gdr_status_string", "gdr_version"):
         assert n in names, names
 
@@ -161,3 +161,36 @@ def test_output_gate_validation(gdr, kw, code):
 def test_output_gate_empty(gdr):
     assert gate(gdr, N=0, o=None, g=None, y=None) == 0
     assert gate(gdr, H=0, o=None, g=None, y=None) == 0
+
+
+def bwd(gdr, B=1, T=8, H=1, Dk=64, Dv=64, dt=1, q=A16, k=A16, v=A16, a=A16, b=A16, s0=None,
+        ddt=1, do=A16, dsf=None, dq=A16, dk=A16, dv=A16, da=A16, db=A16, ds0=None, ws=A16,
+        wsb=None):
+    if wsb is None:
+        wsb = gdr.gdr_chunk_bwd_workspace_size(B, T, H, Dk, Dv)
+    return gdr.lib.gdr_chunk_bwd(B, T, H, Dk, Dv, dt, q, k, v, a, b, s0, ddt, do, dsf, dq, dk, dv,
+                                 da, db, ds0, ws, wsb, None)
+
+
+def test_bwd_workspace_size(gdr):
+    """Chunk-start states (B H ceil(T/32) Dv Dk floats) plus partials for
+    Dv/32 row blocks (2 Dk + 2 floats per token-head each)."""
+    assert gdr.gdr_chunk_bwd_workspace_size(2, 100, 3, 128, 64) == \
+        4 * (2 * 3 * 4 * 64 * 128 + 2 * 2 * 600 * 128 + 2 * 2 * 600)
+    assert gdr.gdr_chunk_bwd_workspace_size(1, 8, 1, 96, 64) == 0
+    assert gdr.gdr_chunk_bwd_workspace_size(-1, 8, 1, 64, 64) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(do=None), 1), (dict(dq=None), 1), (dict(dv=None), 1),
+    (dict(da=None), 1), (dict(ws=None), 1), (dict(ws=BAD), 1), (dict(dk=BAD), 1),
+    (dict(s0=BAD), 1), (dict(dsf=BAD), 1), (dict(ds0=BAD), 1), (dict(wsb=100), 1),
+    (dict(T=-1), 1), (dict(Dk=96), 2), (dict(ddt=5), 2), (dict(dt=9), 2),
+])
+def test_bwd_validation(gdr, kw, code):
+    assert bwd(gdr, **kw) == code
+
+
+def test_bwd_empty(gdr):
+    assert bwd(gdr, B=0, q=None, k=None, v=None, a=None, b=None, do=None, dq=None, dk=None,
+               dv=None, da=None, db=None, ws=None, wsb=0) == 0

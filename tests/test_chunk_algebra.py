@@ -152,3 +152,111 @@ def test_gdn2_chunk_form_wide_decay_range():
                       e[0, :, 0], w[0, :, 0], S0[0, 0], 64)
     np.testing.assert_allclose(o, o_ref[0, :, 0], rtol=1e-9, atol=1e-10)
     np.testing.assert_allclose(S, s_ref[0, 0], rtol=1e-9, atol=1e-10)
+
+
+def gdn_chunk_bwd(q, k, v, a, b, s0, dO, dSf, C):
+    """Chunkwise reverse mode of the scalar-gated rule for one (b, h): the
+    algebra the backward kernels evaluate.  Per chunk (n tokens, g the
+    within-chunk cumulative log alpha, gamma = e^g, D_r = e^{g_C - g_r}):
+
+      forward  A = diag(beta) (K K^T o Gamma) strict,  T = (I + A)^{-1},
+               W = diag(beta gamma) K,  R = diag(beta) V - W S^T,  U = T R,
+               P = (Q K^T o Gamma) incl. diagonal,
+               O = diag(gamma) Q S^T + P U,  S' = gamma_C S + U^T diag(D) K
+      reverse  dU = P^T dO + diag(D) K G^T,  dR = T^T dU,
+               dP = dO U^T (masked),  dT = dU R^T,  dA = -T^T dT T^T (strict),
+               dS = gamma_C G + dO^T diag(gamma) Q - dR^T W,  dV = diag(beta) dR,
+               dW = -dR S,  dQ = diag(gamma) dO S + (dP o Gamma) K,
+               dK = diag(D) U G + (dP o Gamma)^T Q + diag(beta gamma) dW
+                    + diag(beta) dA~ K + (diag(beta) dA~)^T K   (dA~ = dA o Gamma),
+               dbeta, dg from every place beta, gamma, Gamma, D, gamma_C enter,
+               dlog alpha = reverse cumulative sum of dg inside the chunk,
+    with G = dL/dS' carried from the next chunk.  Returns
+    (dq, dk, dv, dalpha, dbeta, ds0)."""
+    T, Dk = q.shape
+    Dv = v.shape[1]
+    chunks = [slice(c0, min(c0 + C, T)) for c0 in range(0, T, C)]
+    S = s0.copy()
+    starts = []
+    for sl in chunks:                                   # forward: chunk-start states
+        starts.append(S.copy())
+        _, S = gdn_chunk(q[sl], k[sl], v[sl], a[sl], b[sl], S, C)
+    G = dSf.copy()
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dla, db = np.zeros_like(a), np.zeros_like(b)
+    for sl, S in zip(reversed(chunks), reversed(starts)):
+        Q, K, V, al, be, dOc = q[sl], k[sl], v[sl], a[sl], b[sl], dO[sl]
+        n = Q.shape[0]
+        g = np.cumsum(np.log(al))
+        gam, gC = np.exp(g), np.exp(g[-1])
+        D = np.exp(g[-1] - g)
+        ge = np.tril(np.ones((n, n), dtype=bool))
+        gt = np.tril(np.ones((n, n), dtype=bool), -1)
+        Gam = np.exp(np.where(ge, g[:, None] - g[None, :], -np.inf))
+        KK = K @ K.T
+        A = np.where(gt, be[:, None] * Gam * KK, 0.0)
+        Tm = np.linalg.inv(np.eye(n) + A)
+        W = (be * gam)[:, None] * K
+        R = be[:, None] * V - W @ S.T
+        U = Tm @ R
+        P = np.where(ge, (Q @ K.T) * Gam, 0.0)
+        QS = Q @ S.T
+        UG = U @ G                                       # n x Dk
+        dU = P.T @ dOc + D[:, None] * (K @ G.T)
+        dR = Tm.T @ dU
+        dP = np.where(ge, dOc @ U.T, 0.0)
+        dT = dU @ R.T
+        dA = np.where(gt, -(Tm.T @ dT @ Tm.T), 0.0)
+        dW = -dR @ S
+        dPG = dP * Gam
+        dAG = dA * Gam
+        dq[sl] = gam[:, None] * (dOc @ S) + dPG @ K
+        dk[sl] = (D[:, None] * UG + dPG.T @ Q + (be * gam)[:, None] * dW
+                  + be[:, None] * (dAG @ K) + (be[:, None] * dAG).T @ K)
+        dv[sl] = be[:, None] * dR
+        wk = np.sum(dW * K, axis=1)
+        db[sl] = np.sum(V * dR, axis=1) + gam * wk + np.sum(dAG * KK, axis=1)
+        dgam = np.sum(dOc * QS, axis=1) + be * wk
+        dD = np.sum(K * UG, axis=1)
+        PP, AA = dP * P, dA * A
+        dg = gam * dgam + PP.sum(1) - PP.sum(0) + AA.sum(1) - AA.sum(0) - D * dD
+        dg[-1] += np.sum(D * dD) + gC * np.sum(S * G)
+        dla[sl] = np.cumsum(dg[::-1])[::-1]
+        G = gC * G + dOc.T @ (gam[:, None] * Q) - dR.T @ W
+    return dq, dk, dv, dla / a, db, G
+
+
+@pytest.mark.parametrize("C", [1, 4, 16, 32, 64])
+def test_gdn_chunk_bwd_matches_oracle(C):
+    q, k, v, a, b, S0 = rand_gdn(36, B=1, T=77, H=2, Dk=6, Dv=5)
+    g = np.random.Generator(np.random.PCG64(37))
+    do = g.standard_normal(v.shape)
+    dsf = g.standard_normal(S0.shape)
+    ref = oracle.gdn_bwd(q, k, v, a, b, S0, do, dsf)
+    for h in range(2):
+        got = gdn_chunk_bwd(q[0, :, h], k[0, :, h], v[0, :, h], a[0, :, h], b[0, :, h],
+                            S0[0, h], do[0, :, h], dsf[0, h], C)
+        want = [ref[0][0, :, h], ref[1][0, :, h], ref[2][0, :, h], ref[3][0, :, h],
+                ref[4][0, :, h], ref[5][0, h]]
+        for name, x, y in zip(("dq", "dk", "dv", "dalpha", "dbeta", "ds0"), got, want):
+            np.testing.assert_allclose(x, y, rtol=1e-9, atol=1e-10 * max(1.0, np.abs(y).max()),
+                                       err_msg=f"{name} C={C} h={h}")
+
+
+def test_gdn_chunk_bwd_small_gates():
+    """Gates near zero (alpha down to 1e-6) keep the chunk backward finite and
+    equal to the oracle's."""
+    q, k, v, a, b, S0 = rand_gdn(38, B=1, T=40, H=1, Dk=4, Dv=3)
+    a = a.copy()
+    a[0, 5, 0] = 1e-6
+    a[0, 20:23, 0] = 1e-3
+    g = np.random.Generator(np.random.PCG64(39))
+    do = g.standard_normal(v.shape)
+    dsf = g.standard_normal(S0.shape)
+    ref = oracle.gdn_bwd(q, k, v, a, b, S0, do, dsf)
+    got = gdn_chunk_bwd(q[0, :, 0], k[0, :, 0], v[0, :, 0], a[0, :, 0], b[0, :, 0], S0[0, 0],
+                        do[0, :, 0], dsf[0, 0], 16)
+    want = [ref[0][0, :, 0], ref[1][0, :, 0], ref[2][0, :, 0], ref[3][0, :, 0], ref[4][0, :, 0],
+            ref[5][0, 0]]
+    for x, y in zip(got, want):
+        np.testing.assert_allclose(x, y, rtol=1e-8, atol=1e-9 * max(1.0, np.abs(y).max()))
