@@ -24,6 +24,9 @@ The JSON line (stdout, last line) carries:
                      normalise pass in PyTorch followed by the plain call
   output_gate        gdr_output_gate (RMSNorm x SiLU gate) on the B8 T4096 H16
                      d128 output: fp32 o, bf16 gate, bf16 y; GB/s of HBM
+  backward           gdr_chunk_bwd on the B8 H16 T4096 d128 workload (bf16 inputs
+                     and dL/do, fp32 gradients): launch time and fp32 vector-ALU
+                     fraction of its algorithmic flops
   copy_reference     a plain 512 MiB device copy (achievable bandwidth)
   cpu_baseline       the fp64 oracle timed on the host on the same workload
 """
@@ -43,6 +46,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector ALU, TFLOP/s
 METRIC = "tokens/s chunkwise gated-delta fwd (H16,d128,T4K); % MFMA peak; decode GB/s"
 
 
@@ -344,6 +348,31 @@ def bench_gate(gdr, torch, warmup, steps):
     return dict(mean=mean, min=mn, bytes=n * (4 + 2 + 2) + 4 * 128)
 
 
+def bench_bwd(gdr, torch, warmup, steps):
+    """gdr_chunk_bwd on B8 H16 T4096 d128 (bf16 q/k/v and dL/do, dL/dS_T
+    given, zero S_0).  Algorithmic flops per token-head, chunk C = 32:
+    2 x (10 dk dv + 7 C dk + 5.5 C dv) -- ten state-sized products (the
+    forward's K S^T and state update, Q S^T, K S^T, K G^T, dO S, dR S, U G,
+    the two terms of the G update), the key-side Gram and P / A terms, and
+    the n x n-by-rows products."""
+    from gdr_gen import make_gdn
+    inp = make_gdn(B=8, T=4096, H=16, Dk=128, Dv=128, dtype="bf16", seed=1001)
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
+    a, b = inp.alpha.to(dev), inp.beta.to(dev)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    do = torch.randn(v.shape, generator=g).to(torch.bfloat16).to(dev)
+    dsf = (0.1 * torch.randn((8, 16, 128, 128), generator=g)).to(dev)
+    ws = torch.empty(gdr.gdr_chunk_bwd_workspace_size(8, 4096, 16, 128, 128), dtype=torch.uint8,
+                     device=dev)
+    mean, mn, med, wall = time_launches(
+        lambda: gdr.gdr_chunk_bwd(q, k, v, a, b, None, do, dsf, workspace=ws), warmup, steps)
+    th = 8 * 4096 * 16
+    C, d = 32, 128
+    flops = th * 2 * (10 * d * d + 7 * C * d + 5.5 * C * d)
+    return dict(mean=mean, min=mn, flops=flops, tokens=8 * 4096, ws=ws.numel())
+
+
 def bench_copy(torch, warmup, steps, nbytes=512 << 20):
     """A plain device-to-device copy of known size: the achievable-bandwidth
     reference, and the kernel whose FETCH_SIZE / WRITE_SIZE counters scale
@@ -380,7 +409,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
-    ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "longctx", "l2norm", "gate", "copy"],
+    ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "longctx", "l2norm", "gate", "bwd",
+                                       "copy"],
                     default=None,
                     help="time one operation only (for profiling)")
     ap.add_argument("--skip", default="",
@@ -431,6 +461,9 @@ def main():
     if want("gate"):
         log("timing gdr_output_gate B8 T4096 H16 d128 ...")
         res["gate"] = bench_gate(gdr, torch, args.warmup, args.steps)
+    if want("bwd"):
+        log("timing gdr_chunk_bwd B8 H16 T4096 d128 ...")
+        res["bwd"] = bench_bwd(gdr, torch, min(args.warmup, 5), min(args.steps, 10))
     if want("copy"):
         log("timing a 512 MiB device copy ...")
         res["copy"] = bench_copy(torch, args.warmup, args.steps)
@@ -500,6 +533,15 @@ def main():
                               "launch_us_mean": r["mean"] * 1e6, "GB/s": gbs,
                               "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_launch": r["bytes"],
                               "traffic": measured_traffic("gate")}
+    if "bwd" in res:
+        r = res["bwd"]
+        tf = r["flops"] / r["mean"] / 1e12
+        out["backward"] = {"workload": "gdr_chunk_bwd B8 H16 T4096 d128, bf16 inputs and dL/do, "
+                                       "fp32 gradients",
+                           "launch_us_mean": r["mean"] * 1e6, "tokens/s": r["tokens"] / r["mean"],
+                           "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_PEAK_TFLOPS,
+                                        "unit": "TFLOP/s", "frac": tf / FP32_PEAK_TFLOPS},
+                           "flops_per_launch": r["flops"], "workspace_bytes": r["ws"]}
     if "copy" in res:
         cp = res["copy"]
         out["copy_reference"] = {"what": "torch device-to-device copy, 512 MiB read + 512 MiB "

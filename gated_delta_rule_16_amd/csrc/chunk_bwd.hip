@@ -56,7 +56,7 @@ struct BwdParams {
 
 template <int DK>
 struct BL {
-    static constexpr int PK = DK + 1;
+    static constexpr int PK = DK + 4;            // 16-byte rows for vector reads
     static constexpr int PC = BC + 1;
     static constexpr int PR = BR + 1;
     static constexpr int K = 0;                  // [BC][PK]
@@ -80,12 +80,59 @@ struct BL {
     static constexpr int U = R + BC * PR;
     static constexpr int DU = U + BC * PR;
     static constexpr int DR = DU + BC * PR;
-    static constexpr int GG = DR + BC * PR;      // [BC] g
+    static constexpr int GM = DR + BC * PR;      // [BC][PC] Gamma_rs = e^{min(g_r - g_s, 0)}
+    static constexpr int GG = GM + BC * PC;      // [BC] g
     static constexpr int BE = GG + BC;           // [BC] beta
-    static constexpr int RED = BE + BC;          // [BC][8] row reductions
+    static constexpr int GA = BE + BC;           // [BC] gamma = e^g
+    static constexpr int DD = GA + BC;           // [BC] D = e^{g_C - g}
+    static constexpr int RED = DD + BC;          // [BC][8] row reductions
     static constexpr int MISC = RED + BC * 8;    // [8]
     static constexpr int TOTAL = MISC + 8;
+    static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget");
+    static_assert(PK % 4 == 0 && Q % 4 == 0 && S % 4 == 0 && G % 4 == 0, "16-byte rows");
 };
+
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// c[x][y] = sum_k A[r0 + x][k] B[c0 + y][k] over N (a multiple of 4) for row-
+// major A, B with 16-byte-aligned rows: a 2 x 2 register tile, 16-byte reads
+// along the contraction.
+template <int N>
+__device__ __forceinline__ void dot22(const float* A, int pa, int r0, const float* B, int pb,
+                                      int c0, float (&c)[2][2]) {
+    c[0][0] = c[0][1] = c[1][0] = c[1][1] = 0.f;
+#pragma unroll 4
+    for (int k = 0; k < N; k += 4) {
+        const f32x4 a0 = ld4(A + r0 * pa + k), a1 = ld4(A + (r0 + 1) * pa + k);
+        const f32x4 b0 = ld4(B + c0 * pb + k), b1 = ld4(B + (c0 + 1) * pb + k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            c[0][0] += a0[e] * b0[e];
+            c[0][1] += a0[e] * b1[e];
+            c[1][0] += a1[e] * b0[e];
+            c[1][1] += a1[e] * b1[e];
+        }
+    }
+}
+
+// acc[x][y] += sum_k a(x, k) B[k][c0 + y], k < KN, y < NC (4 or 8): a 2 x NC
+// register tile, the right operand read as 16-byte vectors.
+template <int KN, int NC, typename FA>
+__device__ __forceinline__ void mm2n(float (&acc)[2][NC], FA a, const float* B, int pb, int c0) {
+#pragma unroll 4
+    for (int k = 0; k < KN; ++k) {
+        const float a0 = a(0, k), a1 = a(1, k);
+#pragma unroll
+        for (int h = 0; h < NC / 4; ++h) {
+            const f32x4 b = ld4(B + k * pb + c0 + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[0][4 * h + e] += a0 * b[e];
+                acc[1][4 * h + e] += a1 * b[e];
+            }
+        }
+    }
+}
 
 template <typename T>
 __device__ __forceinline__ float ldf(const void* p, int64_t i) {
@@ -96,7 +143,7 @@ template <int DK, int DV, typename TIn, typename TD>
 __global__ __launch_bounds__(BNT) void chunk_bwd_kernel(BwdParams p) {
     using L = BL<DK>;
     constexpr int NRB = DV / BR;
-    extern __shared__ float sm[];
+    extern __shared__ __align__(16) float sm[];
     float* Ks = sm + L::K;
     float* Qs = sm + L::Q;
     float* Ss = sm + L::S;
@@ -120,6 +167,9 @@ __global__ __launch_bounds__(BNT) void chunk_bwd_kernel(BwdParams p) {
     float* dRs = sm + L::DR;
     float* gs = sm + L::GG;
     float* bes = sm + L::BE;
+    float* gms = sm + L::GM;
+    float* gas = sm + L::GA;
+    float* dds = sm + L::DD;
     float* red = sm + L::RED;
     float* misc = sm + L::MISC;
 
@@ -176,36 +226,51 @@ __global__ __launch_bounds__(BNT) void chunk_bwd_kernel(BwdParams p) {
             }
         }
     };
-    auto Gam = [&](int r, int s) { return __expf(fminf(gs[r] - gs[s], 0.f)); };
+    // the chunk's decay tables (after load_chunk and a barrier)
+    auto tables = [&]() {
+        for (int e = tid; e < BC * BC; e += BNT) {
+            const int r = e / BC, c = e % BC;
+            gms[r * L::PC + c] = __expf(fminf(gs[r] - gs[c], 0.f));
+        }
+        if (tid < BC) {
+            gas[tid] = __expf(gs[tid]);
+            dds[tid] = __expf(gs[BC - 1] - gs[tid]);
+        }
+    };
+    auto Gam = [&](int r, int c) { return gms[r * L::PC + c]; };
 
     // KK (and QK) = K K^T (Q K^T) over the key dim
+    // 32 x 32 products over the key dim: thread = 2 x 2 tile (rows r0, r0 + 1;
+    // columns c0, c0 + 1)
+    const int r0 = 2 * (tid >> 4), c0 = 2 * (tid & 15);
+    auto put22 = [&](float* D, int pd, const float (&c)[2][2]) {
+        D[r0 * pd + c0] = c[0][0];
+        D[r0 * pd + c0 + 1] = c[0][1];
+        D[(r0 + 1) * pd + c0] = c[1][0];
+        D[(r0 + 1) * pd + c0 + 1] = c[1][1];
+    };
     auto gram = [&](bool with_q) {
-        for (int e = tid; e < BC * BC; e += BNT) {
-            const int r = e / BC, s = e % BC;
-            float kk = 0.f, qk = 0.f;
-            for (int j = 0; j < DK; ++j) {
-                const float ks = Ks[s * L::PK + j];
-                kk += Ks[r * L::PK + j] * ks;
-                if (with_q) qk += Qs[r * L::PK + j] * ks;
-            }
-            KKs[r * L::PC + s] = kk;
-            if (with_q) QKs[r * L::PC + s] = qk;
+        float c[2][2];
+        dot22<DK>(Ks, L::PK, r0, Ks, L::PK, c0, c);
+        put22(KKs, L::PC, c);
+        if (with_q) {
+            dot22<DK>(Qs, L::PK, r0, Ks, L::PK, c0, c);
+            put22(QKs, L::PC, c);
         }
     };
     // X S^T for X = K (and Q): [BC][rows]
     auto xs = [&](bool with_q) {
-        for (int e = tid; e < BC * BR; e += BNT) {
-            const int r = e / BR, i = e % BR;
-            float ks = 0.f, qs = 0.f;
-            for (int j = 0; j < DK; ++j) {
-                const float sv = Ss[i * L::PK + j];
-                ks += Ks[r * L::PK + j] * sv;
-                if (with_q) qs += Qs[r * L::PK + j] * sv;
-            }
-            KSs[r * L::PR + i] = ks;
-            if (with_q) QSs[r * L::PR + i] = qs;
+        float c[2][2];
+        dot22<DK>(Ks, L::PK, r0, Ss, L::PK, c0, c);
+        put22(KSs, L::PR, c);
+        if (with_q) {
+            dot22<DK>(Qs, L::PK, r0, Ss, L::PK, c0, c);
+            put22(QSs, L::PR, c);
         }
     };
+    // [rows] x DK tiles: thread = rows 2 (tid / 16), +1; columns NC (tid % 16) .. + NC - 1
+    constexpr int NC = DK / 16;
+    const int i0 = 2 * (tid >> 4), j0 = NC * (tid & 15);
     // A (strict lower), R = beta V - beta gamma K S^T
     auto form_a_r = [&]() {
         for (int e = tid; e < BC * BC; e += BNT) {
@@ -214,7 +279,7 @@ __global__ __launch_bounds__(BNT) void chunk_bwd_kernel(BwdParams p) {
         }
         for (int e = tid; e < BC * BR; e += BNT) {
             const int r = e / BR, i = e % BR;
-            Rs[r * L::PR + i] = bes[r] * (Vs[r * L::PR + i] - __expf(gs[r]) * KSs[r * L::PR + i]);
+            Rs[r * L::PR + i] = bes[r] * (Vs[r * L::PR + i] - gas[r] * KSs[r * L::PR + i]);
         }
     };
 
@@ -233,28 +298,41 @@ __global__ __launch_bounds__(BNT) void chunk_bwd_kernel(BwdParams p) {
         }
         load_chunk(t0, n, false);
         __syncthreads();
+        tables();
         gram(false);
         xs(false);
         __syncthreads();
         form_a_r();
         __syncthreads();
-        // (I + A) U = R by forward substitution, one thread per state row
+        // (I + A) U = R by forward substitution, one thread per state row,
+        // the row's column of U in registers
         if (tid < BR) {
             const int i = tid;
+            float u[BC];
+#pragma unroll
             for (int r = 0; r < BC; ++r) {
                 float x = Rs[r * L::PR + i];
-                for (int s = 0; s < r; ++s) x -= As[r * L::PC + s] * Us[s * L::PR + i];
+#pragma unroll
+                for (int c = 0; c < r; ++c) x -= As[r * L::PC + c] * u[c];
+                u[r] = x;
                 Us[r * L::PR + i] = x;
             }
         }
         __syncthreads();
         // S <- gamma_C S + U^T diag(D) K
-        const float gC = gs[BC - 1];
-        for (int e = tid; e < BR * DK; e += BNT) {
-            const int i = e / DK, j = e % DK;
-            float x = __expf(gC) * Ss[i * L::PK + j];
-            for (int r = 0; r < BC; ++r) x += Us[r * L::PR + i] * __expf(gC - gs[r]) * Ks[r * L::PK + j];
-            Ss[i * L::PK + j] = x;
+        const float gCe = __expf(gs[BC - 1]);
+        {
+            float acc[2][NC];
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int y = 0; y < NC; ++y) acc[x][y] = gCe * Ss[(i0 + x) * L::PK + j0 + y];
+            mm2n<BC, NC>(acc, [&](int x, int r) { return dds[r] * Us[r * L::PR + i0 + x]; }, Ks, L::PK, j0);
+            // each thread rewrites only the S entries it read
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int y = 0; y < NC; ++y) Ss[(i0 + x) * L::PK + j0 + y] = acc[x][y];
         }
     }
 
@@ -278,14 +356,14 @@ __global__ __launch_bounds__(BNT) void chunk_bwd_kernel(BwdParams p) {
         }
         load_chunk(t0, n, true);
         __syncthreads();
+        tables();
         gram(true);
         xs(true);
         // K G^T [BC][rows]
-        for (int e = tid; e < BC * BR; e += BNT) {
-            const int r = e / BR, i = e % BR;
-            float x = 0.f;
-            for (int j = 0; j < DK; ++j) x += Ks[r * L::PK + j] * Gs[i * L::PK + j];
-            KGs[r * L::PR + i] = x;
+        {
+            float c[2][2];
+            dot22<DK>(Ks, L::PK, r0, Gs, L::PK, c0, c);
+            put22(KGs, L::PR, c);
         }
         __syncthreads();
         form_a_r();
@@ -294,22 +372,26 @@ __global__ __launch_bounds__(BNT) void chunk_bwd_kernel(BwdParams p) {
             Ps[r * L::PC + s] = s <= r ? Gam(r, s) * QKs[r * L::PC + s] : 0.f;
         }
         __syncthreads();
-        // T = (I + A)^{-1}, one thread per column s: T_rs = -sum_{s<=m<r} A_rm T_ms
+        // T = (I + A)^{-1}, one thread per column c: T_rc = -sum_{c<=m<r} A_rm T_mc,
+        // the column in registers (entries above the diagonal are zero)
         if (tid < BC) {
-            const int s = tid;
+            const int c = tid;
+            float tc[BC];
+#pragma unroll
             for (int r = 0; r < BC; ++r) {
-                float x = r == s ? 1.f : 0.f;
-                if (r > s)
-                    for (int m = s; m < r; ++m) x -= As[r * L::PC + m] * Ts[m * L::PC + s];
-                Ts[r * L::PC + s] = x;
+                float x = r == c ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < r; ++m) x -= As[r * L::PC + m] * tc[m];
+                tc[r] = r < c ? 0.f : x;
+                Ts[r * L::PC + c] = tc[r];
             }
         }
         __syncthreads();
         // U = T R;  dU = P^T dO + diag(D) K G^T
-        const float gC = gs[BC - 1];
+        const float gCe = __expf(gs[BC - 1]);
         for (int e = tid; e < BC * BR; e += BNT) {
             const int r = e / BR, i = e % BR;
-            float u = 0.f, du = __expf(gC - gs[r]) * KGs[r * L::PR + i];
+            float u = 0.f, du = dds[r] * KGs[r * L::PR + i];
             for (int s = 0; s <= r; ++s) u += Ts[r * L::PC + s] * Rs[s * L::PR + i];
             for (int s = r; s < BC; ++s) du += Ps[s * L::PC + r] * dOs[s * L::PR + i];
             Us[r * L::PR + i] = u;
@@ -359,45 +441,70 @@ __global__ __launch_bounds__(BNT) void chunk_bwd_kernel(BwdParams p) {
         }
         __syncthreads();
         float* dAf = dTs;   // dA from here on
-        // ---- dQ, dK partials per element (r, j); row sums of dW.K and K.UG
-        //      eight lanes per token row r, 16 columns each
+        // M1 = dP o Gamma, its transpose, and M3 = B + B^T with B = diag(beta)
+        // (dA o Gamma), into tiles that are free by now (K G^T, Q K^T, K S^T)
+        float* M1 = KGs;
+        float* M1T = QKs;
+        float* M3 = KSs;
+        for (int e = tid; e < BC * BC; e += BNT) {
+            const int r = e / BC, c = e % BC;
+            const float m1 = dPs[r * L::PC + c] * Gam(r, c);
+            M1[r * L::PC + c] = m1;
+            M1T[c * L::PC + r] = m1;
+            M3[r * L::PC + c] = bes[r] * dAf[r * L::PC + c] * Gam(r, c) +
+                                bes[c] * dAf[c * L::PC + r] * Gam(c, r);
+        }
+        __syncthreads();
+        // ---- dQ, dK partials on 2 x 8 tiles (token rows r, r + 1; key
+        //      columns j0 .. j0 + 7); row sums of dW.K and K.(U G)
         {
-            const int r = tid >> 3, part = tid & 7;
-            const float be = bes[r], gr = __expf(gs[r]), Dr = __expf(gC - gs[r]);
-            float wk = 0.f, kug = 0.f;
-            for (int jj = 0; jj < DK / 8; ++jj) {
-                const int j = part + 8 * jj;
-                float dos = 0.f, dw = 0.f, ug = 0.f;
-                for (int i = 0; i < BR; ++i) {
-                    const float sij = Ss[i * L::PK + j];
-                    dos += dOs[r * L::PR + i] * sij;
-                    dw -= dRs[r * L::PR + i] * sij;
-                    ug += Us[r * L::PR + i] * Gs[i * L::PK + j];
-                }
-                float dq = gr * dos, dk = Dr * ug + be * gr * dw;
-                for (int s = 0; s < BC; ++s) {
-                    const float ks = Ks[s * L::PK + j];
-                    dq += dPs[r * L::PC + s] * Gam(r, s) * ks;                       // (dP o Gam) K
-                    dk += dPs[s * L::PC + r] * Gam(s, r) * Qs[s * L::PK + j];        // (dP o Gam)^T Q
-                    dk += be * dAf[r * L::PC + s] * Gam(r, s) * ks;                  // diag(beta) dA~ K
-                    dk += bes[s] * dAf[s * L::PC + r] * Gam(s, r) * ks;              // (diag(beta) dA~)^T K
-                }
-                if (r < n) {
-                    pqb[tok(t0 + r) * DK + j] = dq;
-                    pkb[tok(t0 + r) * DK + j] = dk;
-                }
-                const float kj = Ks[r * L::PK + j];
-                wk += dw * kj;
-                kug += kj * ug;
-            }
+            const int ra = i0;   // token rows of this thread's tile
+            float aq[2][NC] = {}, ak[2][NC] = {}, dw[2][NC] = {};
+            mm2n<BR, NC>(aq, [&](int x, int i) { return dOs[(ra + x) * L::PR + i]; }, Ss, L::PK, j0);
+            mm2n<BR, NC>(ak, [&](int x, int i) { return Us[(ra + x) * L::PR + i]; }, Gs, L::PK, j0);
+            mm2n<BR, NC>(dw, [&](int x, int i) { return -dRs[(ra + x) * L::PR + i]; }, Ss, L::PK, j0);
+            float wk[2] = {0.f, 0.f}, kug[2] = {0.f, 0.f};
 #pragma unroll
-            for (int m = 1; m < 8; m <<= 1) {
-                wk += __shfl_xor(wk, m, 64);
-                kug += __shfl_xor(kug, m, 64);
+            for (int x = 0; x < 2; ++x) {
+                const int r = ra + x;
+                const float gr = gas[r], Dr = dds[r], bg = bes[r] * gr;
+#pragma unroll
+                for (int y = 0; y < NC; ++y) {
+                    const float kj = Ks[r * L::PK + j0 + y];
+                    kug[x] += kj * ak[x][y];
+                    wk[x] += kj * dw[x][y];
+                    aq[x][y] *= gr;
+                    ak[x][y] = Dr * ak[x][y] + bg * dw[x][y];
+                }
             }
-            if (part == 0) {
-                red[r * 8 + 0] = wk;
-                red[r * 8 + 1] = kug;
+            mm2n<BC, NC>(aq, [&](int x, int c) { return M1[(ra + x) * L::PC + c]; }, Ks, L::PK, j0);
+            mm2n<BC, NC>(ak, [&](int x, int c) { return M1T[(ra + x) * L::PC + c]; }, Qs, L::PK, j0);
+            mm2n<BC, NC>(ak, [&](int x, int c) { return M3[(ra + x) * L::PC + c]; }, Ks, L::PK, j0);
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int r = ra + x;
+                if (r < n) {
+                    float* qd = pqb + tok(t0 + r) * DK + j0;
+                    float* kd = pkb + tok(t0 + r) * DK + j0;
+#pragma unroll
+                    for (int h = 0; h < NC / 4; ++h) {
+                        *reinterpret_cast<f32x4*>(qd + 4 * h) =
+                            f32x4{aq[x][4 * h], aq[x][4 * h + 1], aq[x][4 * h + 2], aq[x][4 * h + 3]};
+                        *reinterpret_cast<f32x4*>(kd + 4 * h) =
+                            f32x4{ak[x][4 * h], ak[x][4 * h + 1], ak[x][4 * h + 2], ak[x][4 * h + 3]};
+                    }
+                }
+#pragma unroll
+                for (int m = 1; m < 16; m <<= 1) {
+                    wk[x] += __shfl_xor(wk[x], m, 64);
+                    kug[x] += __shfl_xor(kug[x], m, 64);
+                }
+            }
+            if ((tid & 15) == 0) {
+                red[ra * 8 + 0] = wk[0];
+                red[ra * 8 + 1] = kug[0];
+                red[(ra + 1) * 8 + 0] = wk[1];
+                red[(ra + 1) * 8 + 1] = kug[1];
             }
         }
         // sum over the rows of S o G (for gamma_C)
@@ -415,7 +522,7 @@ __global__ __launch_bounds__(BNT) void chunk_bwd_kernel(BwdParams p) {
         // ---- dbeta, dg per token (one thread per token row)
         if (tid < BC) {
             const int r = tid;
-            const float be = bes[r], gr = __expf(gs[r]), Dr = __expf(gC - gs[r]);
+            const float be = bes[r], gr = gas[r], Dr = dds[r];
             const float wk = red[r * 8 + 0], dD = red[r * 8 + 1];
             float vdr = 0.f, dos = 0.f;
             for (int i = 0; i < BR; ++i) {
@@ -441,7 +548,7 @@ __global__ __launch_bounds__(BNT) void chunk_bwd_kernel(BwdParams p) {
             float sdd = 0.f;
             for (int r = 0; r < BC; ++r) sdd += red[r * 8 + 2];
             const float sg = misc[0] + misc[1] + misc[2] + misc[3];
-            red[(n - 1) * 8 + 4] += sdd + __expf(gC) * sg;
+            red[(n - 1) * 8 + 4] += sdd + gCe * sg;
         }
         __syncthreads();
         if (tid < n) {
@@ -449,15 +556,20 @@ __global__ __launch_bounds__(BNT) void chunk_bwd_kernel(BwdParams p) {
             pgb[tok(t0 + tid)] = red[tid * 8 + 4];
         }
         // ---- G <- gamma_C G + dO^T diag(gamma) Q - dR^T diag(beta gamma) K
-        for (int e = tid; e < BR * DK; e += BNT) {
-            const int i = e / DK, j = e % DK;
-            float x = __expf(gC) * Gs[i * L::PK + j];
-            for (int r = 0; r < BC; ++r) {
-                const float gr = __expf(gs[r]);
-                x += gr * (dOs[r * L::PR + i] * Qs[r * L::PK + j] -
-                           bes[r] * dRs[r * L::PR + i] * Ks[r * L::PK + j]);
-            }
-            Gs[i * L::PK + j] = x;
+        {
+            float acc[2][NC];
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int y = 0; y < NC; ++y) acc[x][y] = gCe * Gs[(i0 + x) * L::PK + j0 + y];
+            mm2n<BC, NC>(acc, [&](int x, int r) { return gas[r] * dOs[r * L::PR + i0 + x]; }, Qs, L::PK, j0);
+            mm2n<BC, NC>(acc, [&](int x, int r) { return -bes[r] * gas[r] * dRs[r * L::PR + i0 + x]; },
+                     Ks, L::PK, j0);
+            // each thread rewrites only the G entries it read
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int y = 0; y < NC; ++y) Gs[(i0 + x) * L::PK + j0 + y] = acc[x][y];
         }
     }
     __syncthreads();
