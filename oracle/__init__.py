@@ -23,6 +23,8 @@ l2norm(x, eps=1e-6) -> x / sqrt(sum over the last axis of x^2 + eps)
     The block's L2 normalisation of q and k, applied before either rule.
 gdn_bwd(q, k, v, alpha, beta, s0, dout, ds_final=None)
     -> (dq, dk, dv, dalpha, dbeta, ds0), the reverse mode of gdn_fwd.
+gdn2_bwd(q, k, v, alpha, erase, write, s0, dout, ds_final=None)
+    -> (dq, dk, dv, dalpha, derase, dwrite, ds0), the reverse mode of gdn2_fwd.
 rmsnorm_gate(o, g, w=None, eps=1e-6) -> y
     The block's output gate: RMSNorm of o over its last axis (weight w),
     times SiLU(g).
@@ -44,7 +46,7 @@ _SRC = os.path.join(_HERE, "gdr_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 __all__ = ["build", "OracleLib", "default", "gdn_fwd", "gdn_step",
-           "gdn2_fwd", "gdn_bwd", "l2norm", "rmsnorm_gate", "num_threads", "set_num_threads", "err_rms"]
+           "gdn2_fwd", "gdn_bwd", "gdn2_bwd", "l2norm", "rmsnorm_gate", "num_threads", "set_num_threads", "err_rms"]
 
 
 def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
@@ -84,6 +86,8 @@ class OracleLib:
         lib.oracle_gdn2_fwd.restype = ctypes.c_int
         lib.oracle_gdn_bwd.argtypes = [L] * 5 + [P] * 14
         lib.oracle_gdn_bwd.restype = ctypes.c_int
+        lib.oracle_gdn2_bwd.argtypes = [L] * 5 + [P] * 16
+        lib.oracle_gdn2_bwd.restype = ctypes.c_int
         lib.oracle_l2norm_rows.argtypes = [L, L, P, ctypes.c_double, P]
         lib.oracle_l2norm_rows.restype = ctypes.c_int
         lib.oracle_rmsnorm_gate_rows.argtypes = [L, L, P, P, P, ctypes.c_double, P]
@@ -182,6 +186,26 @@ class OracleLib:
             raise RuntimeError(f"oracle_gdn_bwd failed ({rc})")
         return dq, dk, dv, da, db, ds0
 
+    def gdn2_bwd(self, q, k, v, alpha, erase, write, s0, dout, ds_final=None):
+        """Reverse mode of Gated Delta Rule-2 (``oracle_gdn2_bwd``): gradients of
+        sum(o * dout) + sum(S_T * ds_final).  Returns float64 (dq, dk, dv,
+        dalpha, derase, dwrite, ds0)."""
+        q, k, v, a, e, w, s0, do, dsf = map(_f64, (q, k, v, alpha, erase, write, s0, dout,
+                                                   ds_final))
+        B, T, H, Dk = q.shape
+        Dv = v.shape[-1]
+        assert k.shape == q.shape and a.shape == q.shape and e.shape == q.shape
+        assert v.shape == (B, T, H, Dv) and w.shape == v.shape and do.shape == v.shape
+        assert s0 is None or s0.shape == (B, H, Dv, Dk)
+        assert dsf is None or dsf.shape == (B, H, Dv, Dk)
+        out = [np.empty_like(q), np.empty_like(k), np.empty_like(v), np.empty_like(a),
+               np.empty_like(e), np.empty_like(w), np.empty((B, H, Dv, Dk))]
+        rc = self.lib.oracle_gdn2_bwd(B, T, H, Dk, Dv, _p(q), _p(k), _p(v), _p(a), _p(e), _p(w),
+                                      _p(s0), _p(do), _p(dsf), *[_p(x) for x in out])
+        if rc:
+            raise RuntimeError(f"oracle_gdn2_bwd failed ({rc})")
+        return tuple(out)
+
     def l2norm(self, x, eps=1e-6):
         """Rows of x (last axis) scaled to unit L2 norm,
         x / sqrt(sum x^2 + eps) (``oracle_l2norm_rows``).  float64."""
@@ -256,6 +280,13 @@ def gdn_bwd(*a, **kw):
 
 
 gdn_bwd.__doc__ = OracleLib.gdn_bwd.__doc__
+
+
+def gdn2_bwd(*a, **kw):
+    return default().gdn2_bwd(*a, **kw)
+
+
+gdn2_bwd.__doc__ = OracleLib.gdn2_bwd.__doc__
 
 
 def l2norm(*a, **kw):

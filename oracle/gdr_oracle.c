@@ -372,6 +372,147 @@ int oracle_rmsnorm_gate_rows(long n, long d, const double *o, const double *g,
     return 0;
 }
 
+/*
+ * Reverse mode of Gated Delta Rule-2 (the derivative of oracle_gdn2_fwd,
+ * token by token by the chain rule; the GDN-2 summary notes that its
+ * chunked backward must carry the gates inside the dot products).  Per
+ * token and value row i, with S' = S_{t-1} diag(alpha), e = b (.) k,
+ * u_i = s'_i . e, c_i = w_i v_i - u_i, s_i <- s'_i + c_i k, o_i = s_i . q.
+ * Given G = dL/dS_t and do_t:
+ *
+ *   g_i += do_i q           dq   = sum_i do_i s_i (new state)
+ *   dc_i = g_i . k          dk   = sum_i c_i g_i + b (.) de
+ *   dw_i = dc_i v_i         dv_i = dc_i w_i
+ *   ds'_i = g_i - dc_i e    de   = -sum_i dc_i s'_i,  db = k (.) de
+ *   dalpha = sum_i ds'_i (.) s_i (old state)
+ *   G <- ds' diag(alpha)    (dL/dS_{t-1})
+ *
+ * Layouts as oracle_gdn2_fwd; dalpha, derase [B,T,H,Dk], dwrite
+ * [B,T,H,Dv].  States are kept every SEG tokens and recomputed.
+ */
+static void gdn2_step_state(double *S, const double *Sprev, long Dk, long Dv,
+                            const double *k, const double *v, const double *alpha,
+                            const double *erase, const double *write) {
+    for (long i = 0; i < Dv; ++i) {
+        const double *sp = Sprev + i * Dk;
+        double *s = S + i * Dk;
+        double u = 0.0;
+        for (long j = 0; j < Dk; ++j) u += sp[j] * alpha[j] * erase[j] * k[j];
+        const double c = write[i] * v[i] - u;
+        for (long j = 0; j < Dk; ++j) s[j] = sp[j] * alpha[j] + c * k[j];
+    }
+}
+
+int oracle_gdn2_bwd(long B, long T, long H, long Dk, long Dv, const double *q,
+                    const double *k, const double *v, const double *alpha,
+                    const double *erase, const double *write, const double *s0,
+                    const double *dout, const double *ds_final, double *dq, double *dk,
+                    double *dv, double *dalpha, double *derase, double *dwrite,
+                    double *ds0) {
+    if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return ORACLE_ERR_ARGS;
+    if (!q || !k || !v || !alpha || !erase || !write || !dout || !dq || !dk || !dv || !dalpha ||
+        !derase || !dwrite)
+        return ORACLE_ERR_ARGS;
+    const long SEG = ORACLE_BWD_SEG;
+    const long nseg = (T + SEG - 1) / SEG;
+    int err = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (long b = 0; b < B; ++b) {
+        for (long h = 0; h < H; ++h) {
+            const size_t SS = (size_t)(Dv * Dk);
+            double *ck = (double *)malloc(sizeof(double) * SS * (size_t)(nseg + 1));
+            double *st = (double *)malloc(sizeof(double) * SS * (size_t)(SEG + 1));
+            double *G = (double *)malloc(sizeof(double) * SS);
+            double *cv = (double *)malloc(sizeof(double) * (size_t)Dv);
+            double *dcv = (double *)malloc(sizeof(double) * (size_t)Dv);
+            double *ev = (double *)malloc(sizeof(double) * (size_t)Dk);
+            double *dev = (double *)malloc(sizeof(double) * (size_t)Dk);
+            if (!ck || !st || !G || !cv || !dcv || !ev || !dev) {
+#pragma omp atomic write
+                err = 1;
+                free(ck); free(st); free(G); free(cv); free(dcv); free(ev); free(dev);
+                continue;
+            }
+            state_init(ck, s0 ? s0 + (b * H + h) * SS : NULL, Dv, Dk);
+            for (long sg = 0; sg < nseg; ++sg) {
+                memcpy(st, ck + sg * SS, sizeof(double) * SS);
+                const long t1 = (sg + 1) * SEG < T ? (sg + 1) * SEG : T;
+                for (long t = sg * SEG; t < t1; ++t) {
+                    const long bth = (b * T + t) * H + h;
+                    gdn2_step_state(st, st, Dk, Dv, k + bth * Dk, v + bth * Dv, alpha + bth * Dk,
+                                    erase + bth * Dk, write + bth * Dv);
+                }
+                memcpy(ck + (sg + 1) * SS, st, sizeof(double) * SS);
+            }
+            if (ds_final)
+                memcpy(G, ds_final + (b * H + h) * SS, sizeof(double) * SS);
+            else
+                memset(G, 0, sizeof(double) * SS);
+            for (long sg = nseg - 1; sg >= 0; --sg) {
+                const long t0 = sg * SEG;
+                const long t1 = t0 + SEG < T ? t0 + SEG : T;
+                memcpy(st, ck + sg * SS, sizeof(double) * SS);
+                for (long t = t0; t < t1; ++t) {
+                    const long bth = (b * T + t) * H + h;
+                    gdn2_step_state(st + (t - t0 + 1) * SS, st + (t - t0) * SS, Dk, Dv,
+                                    k + bth * Dk, v + bth * Dv, alpha + bth * Dk,
+                                    erase + bth * Dk, write + bth * Dv);
+                }
+                for (long t = t1 - 1; t >= t0; --t) {
+                    const long bth = (b * T + t) * H + h;
+                    const double *Sp = st + (t - t0) * SS;       /* S_{t-1} */
+                    const double *Sn = st + (t - t0 + 1) * SS;   /* S_t */
+                    const double *qt = q + bth * Dk, *kt = k + bth * Dk, *vt = v + bth * Dv;
+                    const double *at = alpha + bth * Dk, *bt = erase + bth * Dk, *wt = write + bth * Dv;
+                    const double *dot = dout + bth * Dv;
+                    double *dqt = dq + bth * Dk, *dkt = dk + bth * Dk, *dvt = dv + bth * Dv;
+                    double *dat = dalpha + bth * Dk, *dbt = derase + bth * Dk, *dwt = dwrite + bth * Dv;
+                    for (long j = 0; j < Dk; ++j) {
+                        ev[j] = bt[j] * kt[j];
+                        dev[j] = 0.0;
+                        dat[j] = 0.0;
+                        dkt[j] = 0.0;
+                    }
+                    for (long i = 0; i < Dv; ++i)
+                        for (long j = 0; j < Dk; ++j) G[i * Dk + j] += dot[i] * qt[j];
+                    for (long j = 0; j < Dk; ++j) {
+                        double x = 0.0;
+                        for (long i = 0; i < Dv; ++i) x += Sn[i * Dk + j] * dot[i];
+                        dqt[j] = x;
+                    }
+                    for (long i = 0; i < Dv; ++i) {
+                        double u = 0.0, dc = 0.0;
+                        for (long j = 0; j < Dk; ++j) {
+                            u += Sp[i * Dk + j] * at[j] * ev[j];
+                            dc += G[i * Dk + j] * kt[j];
+                        }
+                        cv[i] = wt[i] * vt[i] - u;
+                        dcv[i] = dc;
+                        dwt[i] = dc * vt[i];
+                        dvt[i] = dc * wt[i];
+                    }
+                    for (long i = 0; i < Dv; ++i)
+                        for (long j = 0; j < Dk; ++j) {
+                            const double sprime = Sp[i * Dk + j] * at[j];
+                            const double dsp = G[i * Dk + j] - dcv[i] * ev[j];
+                            dkt[j] += cv[i] * G[i * Dk + j];
+                            dev[j] -= dcv[i] * sprime;
+                            dat[j] += dsp * Sp[i * Dk + j];
+                            G[i * Dk + j] = dsp * at[j];
+                        }
+                    for (long j = 0; j < Dk; ++j) {
+                        dbt[j] = dev[j] * kt[j];
+                        dkt[j] += dev[j] * bt[j];
+                    }
+                }
+            }
+            if (ds0) memcpy(ds0 + (b * H + h) * SS, G, sizeof(double) * SS);
+            free(ck); free(st); free(G); free(cv); free(dcv); free(ev); free(dev);
+        }
+    }
+    return err ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}
+
 /* Threads the oracle's parallel loops use (reported with CPU timings). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

@@ -538,6 +538,59 @@ def pin_bwd_autograd_matrix_form(orc):
         np.testing.assert_allclose(gr, x.grad.numpy(), rtol=1e-10, atol=1e-12)
 
 
+# --- reverse mode of Gated Delta Rule-2 -------------------------------------
+def _gdn2_loss(orc, q, k, v, a, e, w, S0, do, dsf):
+    o, sf = orc.gdn2_fwd(q, k, v, a, e, w, S0)
+    return float(np.sum(o * do) + np.sum(sf * dsf))
+
+
+def pin_bwd2_finite_differences(orc):
+    """Every GDN-2 gradient against central differences of the forward
+    oracle, element by element (T = 5, H = 1, d_k = 4, d_v = 3, with S_0 and
+    dS_T)."""
+    q, k, v, a, e, w, S0 = rand_gdn2(40, B=1, T=5, H=1, Dk=4, Dv=3)
+    g = _rng(41)
+    do = g.standard_normal(v.shape)
+    dsf = g.standard_normal(S0.shape)
+    grads = orc.gdn2_bwd(q, k, v, a, e, w, S0, do, dsf)
+    args = [q, k, v, a, e, w, S0]
+    h = 1e-5
+    for idx, x in enumerate(args):
+        num = np.zeros_like(x)
+        for pos in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += h
+            xm[pos] -= h
+            ap, am = list(args), list(args)
+            ap[idx], am[idx] = xp, xm
+            num[pos] = (_gdn2_loss(orc, *ap, do, dsf) - _gdn2_loss(orc, *am, do, dsf)) / (2 * h)
+        scale = max(1.0, np.abs(num).max())
+        assert np.abs(grads[idx] - num).max() <= 1e-7 * scale, (idx, np.abs(grads[idx] - num).max())
+
+
+def pin_bwd2_autograd_matrix_form(orc):
+    """GDN-2 gradients equal autograd's through the literal matrix form
+    S' = S diag(alpha), S_t = S' + (w (.) v - S'(b (.) k)) k^T, o = S_t q in
+    torch fp64, on a case that crosses the oracle's 64-token segments."""
+    q, k, v, a, e, w, S0 = rand_gdn2(42, B=1, T=70, H=1, Dk=5, Dv=4)
+    g = _rng(43)
+    do = g.standard_normal(v.shape)
+    dsf = g.standard_normal(S0.shape)
+    t = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v, a, e, w, S0)]
+    tq, tk, tv, ta, te, tw, tS = t
+    S = tS[0, 0]
+    loss = 0.0
+    for s in range(70):
+        Sp = S @ torch.diag(ta[0, s, 0])
+        S = Sp + torch.outer(tw[0, s, 0] * tv[0, s, 0] - Sp @ (te[0, s, 0] * tk[0, s, 0]), tk[0, s, 0])
+        loss = loss + (S @ tq[0, s, 0] * torch.tensor(do[0, s, 0])).sum()
+    loss = loss + (S * torch.tensor(dsf[0, 0])).sum()
+    loss.backward()
+    grads = orc.gdn2_bwd(q, k, v, a, e, w, S0, do, dsf)
+    for x, gr in zip(t, grads):
+        np.testing.assert_allclose(gr, x.grad.numpy(), rtol=1e-9, atol=1e-11)
+
+
 # --- the block's L2 normalisation of q and k --------------------------------
 def pin_l2norm_worked(orc):
     """Worked rows with eps = 0: (3, 4) -> (0.6, 0.8); (1, 1, 1, 1) ->
@@ -632,4 +685,5 @@ ALL_PINS = [
     pin_l2norm_worked, pin_l2norm_eps, pin_l2norm_rows,
     pin_gate_worked, pin_gate_rms_and_eps, pin_gate_weight_axis,
     pin_bwd_finite_differences, pin_bwd_directional, pin_bwd_autograd_matrix_form,
+    pin_bwd2_finite_differences, pin_bwd2_autograd_matrix_form,
 ]

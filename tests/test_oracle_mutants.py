@@ -50,6 +50,10 @@ MUTANTS = [
     ("bwd_carry_without_decay", "G[i * Dk + j] = a * G[i * Dk + j] - a * be * dcv[i] * kt[j];",
      "G[i * Dk + j] = G[i * Dk + j] - a * be * dcv[i] * kt[j];"),
     ("bwd_dq_from_old_state", "x += Sn[i * Dk + j] * dot[i];", "x += Sp[i * Dk + j] * dot[i];"),
+    ("bwd2_dalpha_from_new_state", "dat[j] += dsp * Sp[i * Dk + j];", "dat[j] += dsp * Sn[i * Dk + j];"),
+    ("bwd2_erase_grad_sign", "dev[j] -= dcv[i] * sprime;", "dev[j] += dcv[i] * sprime;"),
+    ("bwd2_carry_without_decay", "G[i * Dk + j] = dsp * at[j];", "G[i * Dk + j] = dsp;"),
+    ("bwd2_write_grad_uses_w", "dwt[i] = dc * vt[i];", "dwt[i] = dc * wt[i];"),
     ("bwd_segment_off_by_one", "memcpy(st, ck + sg * SS, sizeof(double) * SS);\n                for (long t = t0; t < t1; ++t) {",
      "memcpy(st, ck + (sg > 0 ? sg - 1 : 0) * SS, sizeof(double) * SS);\n                for (long t = t0; t < t1; ++t) {"),
 ]
