@@ -36,6 +36,7 @@
 // the chunk's A, T, R, U and P from the stored state.
 #include "gdr_device.h"
 #include "launch.h"
+#include "vtile.h"
 
 namespace gdr {
 
@@ -91,53 +92,6 @@ struct BL {
     static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget");
     static_assert(PK % 4 == 0 && Q % 4 == 0 && S % 4 == 0 && G % 4 == 0, "16-byte rows");
 };
-
-__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-
-// c[x][y] = sum_k A[r0 + x][k] B[c0 + y][k] over N (a multiple of 4) for row-
-// major A, B with 16-byte-aligned rows: a 2 x 2 register tile, 16-byte reads
-// along the contraction.
-template <int N>
-__device__ __forceinline__ void dot22(const float* A, int pa, int r0, const float* B, int pb,
-                                      int c0, float (&c)[2][2]) {
-    c[0][0] = c[0][1] = c[1][0] = c[1][1] = 0.f;
-#pragma unroll 4
-    for (int k = 0; k < N; k += 4) {
-        const f32x4 a0 = ld4(A + r0 * pa + k), a1 = ld4(A + (r0 + 1) * pa + k);
-        const f32x4 b0 = ld4(B + c0 * pb + k), b1 = ld4(B + (c0 + 1) * pb + k);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            c[0][0] += a0[e] * b0[e];
-            c[0][1] += a0[e] * b1[e];
-            c[1][0] += a1[e] * b0[e];
-            c[1][1] += a1[e] * b1[e];
-        }
-    }
-}
-
-// acc[x][y] += sum_k a(x, k) B[k][c0 + y], k < KN, y < NC (4 or 8): a 2 x NC
-// register tile, the right operand read as 16-byte vectors.
-template <int KN, int NC, typename FA>
-__device__ __forceinline__ void mm2n(float (&acc)[2][NC], FA a, const float* B, int pb, int c0) {
-#pragma unroll 4
-    for (int k = 0; k < KN; ++k) {
-        const float a0 = a(0, k), a1 = a(1, k);
-#pragma unroll
-        for (int h = 0; h < NC / 4; ++h) {
-            const f32x4 b = ld4(B + k * pb + c0 + 4 * h);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[0][4 * h + e] += a0 * b[e];
-                acc[1][4 * h + e] += a1 * b[e];
-            }
-        }
-    }
-}
-
-template <typename T>
-__device__ __forceinline__ float ldf(const void* p, int64_t i) {
-    return io<T>::ld(reinterpret_cast<const T*>(p) + i);
-}
 
 template <int DK, int DV, typename TIn, typename TD>
 __global__ __launch_bounds__(BNT) void chunk_bwd_kernel(BwdParams p) {

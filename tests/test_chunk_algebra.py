@@ -260,3 +260,91 @@ def test_gdn_chunk_bwd_small_gates():
             ref[5][0, 0]]
     for x, y in zip(got, want):
         np.testing.assert_allclose(x, y, rtol=1e-8, atol=1e-9 * max(1.0, np.abs(y).max()))
+
+
+def gdn2_chunk_bwd(q, k, v, a, e, w, s0, dO, dSf, C):
+    """Chunkwise reverse mode of Gated Delta Rule-2 for one (b, h).  Per chunk
+    (G the within-chunk cumulative log alpha per channel, E = b (.) k,
+    Gamma_rsc = e^{G_rc - G_sc}, E~ = E (.) e^G, Q~ = Q (.) e^G,
+    K~ = K (.) e^{G_C - G}, lambda_C = e^{G_C}):
+
+      forward  A_rs = sum_c E_rc K_sc Gamma_rsc (s < r),
+               P_rs = sum_c Q_rc K_sc Gamma_rsc (s <= r),  T = (I + A)^{-1},
+               R = w (.) v - E~ S^T,  U = T R,  O = Q~ S^T + P U,
+               S' = S diag(lambda_C) + U^T K~
+      reverse  dU = P^T dO + K~ G^T,  dR = T^T dU,  dP = dO U^T (masked),
+               dA = -T^T (dU R^T) T^T (strict),  dw = dR (.) v,  dv = dR (.) w,
+               dE~ = -dR S,  dQ~ = dO S,  dK~ = U G,
+               dS = G diag(lambda_C) + dO^T Q~ - dR^T E~,
+               and the A, P, E~, Q~, K~, lambda_C terms into dE, dQ, dK, dG
+               (the decay inside the dot products: a per-channel dG),
+               db = dE (.) K,  dK += dE (.) b,
+               dlog alpha = reverse cumulative sum of dG inside the chunk.
+    Returns (dq, dk, dv, dalpha, derase, dwrite, ds0)."""
+    T, Dk = q.shape
+    chunks = [slice(c0, min(c0 + C, T)) for c0 in range(0, T, C)]
+    S = s0.copy()
+    starts = []
+    for sl in chunks:
+        starts.append(S.copy())
+        _, S = gdn2_chunk(q[sl], k[sl], v[sl], a[sl], e[sl], w[sl], S, C)
+    Gr = dSf.copy()
+    out = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros_like(a),
+           np.zeros_like(e), np.zeros_like(w)]
+    for sl, S in zip(reversed(chunks), reversed(starts)):
+        Q, K, V, Al, B_, W_ = q[sl], k[sl], v[sl], a[sl], e[sl], w[sl]
+        dOc = dO[sl]
+        n = Q.shape[0]
+        E = B_ * K
+        G = np.cumsum(np.log(Al), axis=0)
+        Gam = np.exp(np.minimum(G[:, None, :] - G[None, :, :], 0.0))    # [r, s, c]
+        lt = np.tril(np.ones((n, n)), -1)
+        le = np.tril(np.ones((n, n)))
+        A = np.einsum('rc,sc,rsc->rs', E, K, Gam) * lt
+        P = np.einsum('rc,sc,rsc->rs', Q, K, Gam) * le
+        Tm = np.linalg.inv(np.eye(n) + A)
+        eG = np.exp(G)
+        Et, Qt, Kt = E * eG, Q * eG, K * np.exp(G[-1] - G)
+        lC = np.exp(G[-1])
+        R = W_ * V - Et @ S.T
+        U = Tm @ R
+        dU = P.T @ dOc + Kt @ Gr.T
+        dR = Tm.T @ dU
+        dP = (dOc @ U.T) * le
+        dA = -(Tm.T @ (dU @ R.T) @ Tm.T) * lt
+        dEt, dQt, dKt = -dR @ S, dOc @ S, U @ Gr
+        dlC = np.sum(Gr * S, axis=0)
+        dE = np.einsum('rs,sc,rsc->rc', dA, K, Gam) + dEt * eG
+        dQ = np.einsum('rs,sc,rsc->rc', dP, K, Gam) + dQt * eG
+        dK = (np.einsum('rs,rc,rsc->sc', dA, E, Gam) + np.einsum('rs,rc,rsc->sc', dP, Q, Gam)
+              + dKt * np.exp(G[-1] - G))
+        tA = np.einsum('rs,rc,sc,rsc->rsc', dA, E, K, Gam)
+        tP = np.einsum('rs,rc,sc,rsc->rsc', dP, Q, K, Gam)
+        dG = (tA.sum(1) - tA.sum(0) + tP.sum(1) - tP.sum(0) + dEt * Et + dQt * Qt
+              - dKt * Kt)
+        dG[-1] += np.sum(dKt * Kt, axis=0) + dlC * lC
+        out[0][sl] = dQ
+        out[1][sl] = dK + dE * B_
+        out[2][sl] = dR * W_
+        out[3][sl] = np.cumsum(dG[::-1], axis=0)[::-1] / Al
+        out[4][sl] = dE * K
+        out[5][sl] = dR * V
+        Gr = Gr * lC[None, :] + dOc.T @ Qt - dR.T @ Et
+    return tuple(out) + (Gr,)
+
+
+@pytest.mark.parametrize("C", [1, 4, 16, 32])
+def test_gdn2_chunk_bwd_matches_oracle(C):
+    q, k, v, a, e, w, S0 = rand_gdn2(44, B=1, T=45, H=2, Dk=6, Dv=5)
+    g = np.random.Generator(np.random.PCG64(45))
+    do = g.standard_normal(v.shape)
+    dsf = g.standard_normal(S0.shape)
+    ref = oracle.gdn2_bwd(q, k, v, a, e, w, S0, do, dsf)
+    names = ("dq", "dk", "dv", "dalpha", "derase", "dwrite", "ds0")
+    for h in range(2):
+        got = gdn2_chunk_bwd(q[0, :, h], k[0, :, h], v[0, :, h], a[0, :, h], e[0, :, h],
+                             w[0, :, h], S0[0, h], do[0, :, h], dsf[0, h], C)
+        want = [x[0, :, h] for x in ref[:6]] + [ref[6][0, h]]
+        for name, x, y in zip(names, got, want):
+            np.testing.assert_allclose(x, y, rtol=1e-9, atol=1e-10 * max(1.0, np.abs(y).max()),
+                                       err_msg=f"{name} C={C} h={h}")
