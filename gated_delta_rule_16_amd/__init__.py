@@ -13,6 +13,8 @@ Functions mirror the C calls:
     gdr_output_gate(o, g, w=None, eps=1e-6, ...)                -> y
     gdr_chunk_bwd(q, k, v, alpha, beta, s0, dout, ds_final=None)
         -> (dq, dk, dv, dalpha, dbeta, ds0)
+    gdr2_chunk_bwd(q, k, v, alpha, erase, write, s0, dout, ds_final=None)
+        -> (dq, dk, dv, dalpha, derase, dwrite, ds0)
 
 ``l2norm_qk=True`` calls the ``_ex`` variant of the same C function with
 GDR_L2NORM_QK: q and k are L2-normalised on load inside the kernels.
@@ -26,6 +28,7 @@ import torch  # loads the HIP runtime libgdr.so binds to
 
 __all__ = ["gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd", "gdr_output_gate",
            "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size",
+           "gdr2_chunk_bwd", "gdr2_chunk_bwd_workspace_size",
            "GdrError", "status_string", "lib", "LIB_PATH", "GDR_F32",
            "GDR_BF16", "GDR_L2NORM_QK"]
 
@@ -62,6 +65,11 @@ lib.gdr_chunk_bwd_workspace_size.restype = ctypes.c_size_t
 lib.gdr_chunk_bwd.argtypes = ([_I64] * 5 + [_E] + [_P] * 6 + [_E, _P, _P] + [_P] * 6 +
                               [_P, ctypes.c_size_t, _P])
 lib.gdr_chunk_bwd.restype = ctypes.c_int
+lib.gdr2_chunk_bwd_workspace_size.argtypes = [_I64] * 5
+lib.gdr2_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+lib.gdr2_chunk_bwd.argtypes = ([_I64] * 5 + [_E] + [_P] * 7 + [_E, _P, _P] + [_P] * 7 +
+                               [_P, ctypes.c_size_t, _P])
+lib.gdr2_chunk_bwd.restype = ctypes.c_int
 lib.gdr_status_string.argtypes = [ctypes.c_int]
 lib.gdr_status_string.restype = ctypes.c_char_p
 lib.gdr_version.restype = ctypes.c_int
@@ -283,3 +291,47 @@ def gdr_chunk_bwd(q, k, v, alpha, beta, s0, dout, ds_final=None, *, workspace=No
         _ptr(s0), _DT[dout.dtype], _ptr(dout), _ptr(ds_final), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(da), _ptr(db), _ptr(ds0), _ptr(workspace), workspace.numel(), _stream(stream)))
     return dq, dk, dv, da, db, ds0
+
+
+def gdr2_chunk_bwd_workspace_size(B, T, H, Dk, Dv) -> int:
+    """Bytes of device workspace gdr2_chunk_bwd needs for these sizes."""
+    return int(lib.gdr2_chunk_bwd_workspace_size(B, T, H, Dk, Dv))
+
+
+def gdr2_chunk_bwd(q, k, v, alpha, erase, write, s0, dout, ds_final=None, *, workspace=None,
+                   want_ds0=True, stream=None):
+    """Reverse mode of gdr2_chunk_fwd: returns fp32 (dq, dk, dv, dalpha,
+    derase, dwrite, ds0) for dL/do = ``dout`` [B,T,H,Dv] (fp32 or bf16) and
+    dL/dS_T = ``ds_final`` [B,H,Dv,Dk] fp32 or None.  Inputs as for
+    gdr2_chunk_fwd.  ``workspace`` is a uint8 GPU tensor of at least
+    gdr2_chunk_bwd_workspace_size(...) bytes, allocated here when None."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if q.dtype not in _DT or dout.dtype not in _DT:
+        raise TypeError("q and dout must be float32 or bfloat16")
+    for name, x, d in (("q", q, Dk), ("k", k, Dk), ("v", v, Dv), ("alpha", alpha, Dk),
+                       ("erase", erase, Dk), ("write", write, Dv)):
+        _check(name, x, q.dtype, (B, T, H, d))
+    _check("dout", dout, dout.dtype, (B, T, H, Dv))
+    if s0 is not None:
+        _check("s0", s0, torch.float32, (B, H, Dv, Dk))
+    if ds_final is not None:
+        _check("ds_final", ds_final, torch.float32, (B, H, Dv, Dk))
+    need = gdr2_chunk_bwd_workspace_size(B, T, H, Dk, Dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check("workspace", workspace, torch.uint8)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((B, T, H, Dk), **f32)
+    dk = torch.empty((B, T, H, Dk), **f32)
+    dv = torch.empty((B, T, H, Dv), **f32)
+    da = torch.empty((B, T, H, Dk), **f32)
+    de = torch.empty((B, T, H, Dk), **f32)
+    dw = torch.empty((B, T, H, Dv), **f32)
+    ds0 = torch.empty((B, H, Dv, Dk), **f32) if want_ds0 else None
+    _run("gdr2_chunk_bwd", lib.gdr2_chunk_bwd(
+        B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase),
+        _ptr(write), _ptr(s0), _DT[dout.dtype], _ptr(dout), _ptr(ds_final), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(da), _ptr(de), _ptr(dw), _ptr(ds0), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return dq, dk, dv, da, de, dw, ds0

@@ -304,6 +304,65 @@ extern "C" gdr_status_t gdr_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t D
     return from_hip(launch_chunk_bwd(a));
 }
 
+extern "C" size_t gdr2_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                                int64_t Dv) {
+    if (B < 0 || T < 0 || H < 0 || !dims_ok(Dk, Dv)) return 0;
+    if (!sizes_ok(B, T, H) || !sizes_ok(B * T * H, Dk > Dv ? Dk : Dv, 1)) return 0;
+    return bwd2_workspace_bytes(B, T, H, Dk, Dv);
+}
+
+extern "C" gdr_status_t gdr2_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                       gdr_dtype_t in_dt, const void* q, const void* k,
+                                       const void* v, const void* alpha, const void* erase,
+                                       const void* write, const float* s0, gdr_dtype_t dout_dt,
+                                       const void* dout, const float* ds_final, float* dq,
+                                       float* dk, float* dv, float* dalpha, float* derase,
+                                       float* dwrite, float* ds0, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0) return GDR_ERR_INVALID;
+    if (!sizes_ok(B, T, H) || !sizes_ok(B * T * H, Dk > Dv ? Dk : Dv, 1)) return GDR_ERR_INVALID;
+    if (!dtype_ok(in_dt) || !dtype_ok(dout_dt)) return GDR_ERR_UNSUPPORTED;
+    if (!dims_ok(Dk, Dv)) return GDR_ERR_UNSUPPORTED;
+    if (B * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
+    if (!opt_ok(s0) || !opt_ok(ds_final) || !opt_ok(ds0)) return GDR_ERR_INVALID;
+    if (B == 0 || H == 0) return GDR_OK;
+    if (T == 0) {
+        if (!ds0) return GDR_OK;
+        return from_hip(launch_state_copy(ds_final, ds0, B * H * Dv * Dk, stream));
+    }
+    if (!ptrs_ok({q, k, v, alpha, erase, write, dout, dq, dk, dv, dalpha, derase, dwrite,
+                  workspace}))
+        return GDR_ERR_INVALID;
+    if (workspace_bytes < bwd2_workspace_bytes(B, T, H, Dk, Dv)) return GDR_ERR_INVALID;
+    Bwd2Args a;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.Dk = Dk;
+    a.Dv = Dv;
+    a.in_bf16 = in_dt == GDR_BF16;
+    a.dout_bf16 = dout_dt == GDR_BF16;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.erase = erase;
+    a.write = write;
+    a.dout = dout;
+    a.s0 = s0;
+    a.ds_final = ds_final;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dalpha = dalpha;
+    a.derase = derase;
+    a.dwrite = dwrite;
+    a.ds0 = ds0;
+    a.workspace = workspace;
+    a.stream = stream;
+    return from_hip(launch_chunk2_bwd(a));
+}
+
 extern "C" const char* gdr_status_string(gdr_status_t s) {
     switch (s) {
         case GDR_OK: return "ok";
@@ -314,4 +373,4 @@ extern "C" const char* gdr_status_string(gdr_status_t s) {
     return "unknown status";
 }
 
-extern "C" int gdr_version(void) { return 200; }
+extern "C" int gdr_version(void) { return 300; }

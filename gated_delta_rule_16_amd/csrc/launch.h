@@ -57,9 +57,23 @@ struct BwdArgs {
     hipStream_t stream;
 };
 
+// Backward of Gated Delta Rule-2: alpha, erase [B,T,H,Dk] and write [B,T,H,Dv]
+// in the input dtype; gradients fp32 with the inputs' shapes.
+struct Bwd2Args {
+    int64_t B, T, H, Dk, Dv;
+    bool in_bf16, dout_bf16;
+    const void *q, *k, *v, *alpha, *erase, *write, *dout;
+    const float *s0, *ds_final;
+    float *dq, *dk, *dv, *dalpha, *derase, *dwrite, *ds0;
+    void* workspace;
+    hipStream_t stream;
+};
+
 hipError_t launch_step(const StepArgs& a);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
 size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv);
+hipError_t launch_chunk2_bwd(const Bwd2Args& a);
+size_t bwd2_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv);
 hipError_t launch_output_gate(const GateArgs& a);
 // fp32 inputs: VALU kernels, both rules.
 hipError_t launch_chunk_f32(const ChunkArgs& a);

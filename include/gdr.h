@@ -8,8 +8,8 @@
  *   gdr2_chunk_fwd      chunkwise forward of Gated Delta Rule-2 (channel gates)
  *
  * plus their _ex variants (q, k L2-normalised on load), the block's
- * output gate on their result (gdr_output_gate) and the reverse mode of
- * the chunkwise forward (gdr_chunk_bwd).
+ * output gate on their result (gdr_output_gate) and the reverse modes of
+ * the two chunkwise forwards (gdr_chunk_bwd, gdr2_chunk_bwd).
  *
  * The rule ("Gated Delta Networks", agihunt.info, "Method"; review of GDN on
  * meaningful96.github.io, section 3.4; inputs and outputs from its
@@ -284,6 +284,51 @@ gdr_status_t gdr_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
                            float *dv, float *dalpha, float *dbeta, float *ds0,
                            void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/*
+ * Reverse mode of gdr2_chunk_fwd (Gated Delta Rule-2): the gradients of a
+ * loss L through o and the final state, given dL/do and dL/dS_T, by the
+ * chain rule through the chunkwise form ("Gated DeltaNet-2", agihunt.info:
+ * the chunked WY form with the channel decay absorbed into the erase
+ * factor; the summary's remark that the backward keeps the gates inside
+ * its dot products).  Chunks of 16 tokens, fp32 throughout.
+ *
+ *   q, k, v, alpha, erase, write, s0, in_dt  the forward's inputs, as for
+ *                  gdr2_chunk_fwd
+ *   dout_dt, dout  [B, T, H, Dv] dL/do (GDR_F32 or GDR_BF16)
+ *   ds_final       [B, H, Dv, Dk] fp32 dL/dS_T, or NULL (zero)
+ *   dq, dk         [B, T, H, Dk] fp32 (written)
+ *   dv             [B, T, H, Dv] fp32 (written)
+ *   dalpha         [B, T, H, Dk] fp32 (written): dL/d(log alpha) divided
+ *                  by alpha, alpha clamped to FLT_MIN as in the forward
+ *   derase         [B, T, H, Dk] fp32 dL/db (written)
+ *   dwrite         [B, T, H, Dv] fp32 dL/dw (written)
+ *   ds0            [B, H, Dv, Dk] fp32 dL/dS_0, or NULL (not written)
+ *   workspace      device memory of at least
+ *                  gdr2_chunk_bwd_workspace_size(B, T, H, Dk, Dv) bytes,
+ *                  16-byte aligned, owned by the caller, contents on entry
+ *                  irrelevant and on return unspecified: the chunk-start
+ *                  states (B H ceil(T/16) Dv Dk floats) and per-row-block
+ *                  partial sums.  A smaller workspace_bytes is
+ *                  GDR_ERR_INVALID.
+ *
+ * Calls on one workspace must not overlap.  T == 0 copies ds_final (or
+ * zeros) into ds0.  Every tensor argument needs 16-byte alignment.
+ * gdr2_chunk_bwd_workspace_size returns 0 for arguments the call rejects.
+ */
+size_t gdr2_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H,
+                                     int64_t Dk, int64_t Dv);
+
+gdr_status_t gdr2_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                            int64_t Dv, gdr_dtype_t in_dt, const void *q,
+                            const void *k, const void *v, const void *alpha,
+                            const void *erase, const void *write,
+                            const float *s0, gdr_dtype_t dout_dt,
+                            const void *dout, const float *ds_final,
+                            float *dq, float *dk, float *dv, float *dalpha,
+                            float *derase, float *dwrite, float *ds0,
+                            void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *gdr_status_string(gdr_status_t s);

@@ -28,6 +28,7 @@ def test_header_declares_the_three_operations():
     for n in ("gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd",
               "gdr_chunk_fwd_ex", "gdr_recurrent_step_ex", "gdr2_chunk_fwd_ex",
               "gdr_output_gate", "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size",
+              "gdr2_chunk_bwd", "gdr2_chunk_bwd_workspace_size",
               "gdr_status_string", "gdr_version"):
         assert n in names, names
 
@@ -194,3 +195,37 @@ def test_bwd_validation(gdr, kw, code):
 def test_bwd_empty(gdr):
     assert bwd(gdr, B=0, q=None, k=None, v=None, a=None, b=None, do=None, dq=None, dk=None,
                dv=None, da=None, db=None, ws=None, wsb=0) == 0
+
+
+def bwd2(gdr, B=1, T=8, H=1, Dk=64, Dv=64, dt=1, q=A16, k=A16, v=A16, a=A16, e=A16, w=A16,
+         s0=None, ddt=1, do=A16, dsf=None, dq=A16, dk=A16, dv=A16, da=A16, de=A16, dw=A16,
+         ds0=None, ws=A16, wsb=None):
+    if wsb is None:
+        wsb = gdr.gdr2_chunk_bwd_workspace_size(B, T, H, Dk, Dv)
+    return gdr.lib.gdr2_chunk_bwd(B, T, H, Dk, Dv, dt, q, k, v, a, e, w, s0, ddt, do, dsf, dq, dk,
+                                  dv, da, de, dw, ds0, ws, wsb, None)
+
+
+def test_bwd2_workspace_size(gdr):
+    """Chunk-start states (B H ceil(T/16) Dv Dk floats) plus dq, dk, derase
+    and dG partials for Dv/32 row blocks (4 Dk floats per token-head each)."""
+    assert gdr.gdr2_chunk_bwd_workspace_size(2, 100, 3, 128, 64) == \
+        4 * (2 * 3 * 7 * 64 * 128 + 4 * 2 * 600 * 128)
+    assert gdr.gdr2_chunk_bwd_workspace_size(1, 8, 1, 64, 96) == 0
+    assert gdr.gdr2_chunk_bwd_workspace_size(1, -8, 1, 64, 64) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(a=None), 1), (dict(e=None), 1), (dict(w=BAD), 1),
+    (dict(do=None), 1), (dict(dq=None), 1), (dict(da=BAD), 1), (dict(de=None), 1),
+    (dict(dw=None), 1), (dict(ws=None), 1), (dict(ws=BAD), 1), (dict(s0=BAD), 1),
+    (dict(dsf=BAD), 1), (dict(ds0=BAD), 1), (dict(wsb=100), 1), (dict(H=-1), 1),
+    (dict(Dk=32), 2), (dict(ddt=5), 2), (dict(dt=9), 2),
+])
+def test_bwd2_validation(gdr, kw, code):
+    assert bwd2(gdr, **kw) == code
+
+
+def test_bwd2_empty(gdr):
+    assert bwd2(gdr, H=0, q=None, k=None, v=None, a=None, e=None, w=None, do=None, dq=None,
+                dk=None, dv=None, da=None, de=None, dw=None, ws=None, wsb=0) == 0
