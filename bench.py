@@ -27,6 +27,8 @@ The JSON line (stdout, last line) carries:
   backward           gdr_chunk_bwd on the B8 H16 T4096 d128 workload (bf16 inputs
                      and dL/do, fp32 gradients): launch time and fp32 vector-ALU
                      fraction of its algorithmic flops
+  backward2          gdr2_chunk_bwd on the B4 H16 T4096 d128 GDN-2 workload, as
+                     for backward
   copy_reference     a plain 512 MiB device copy (achievable bandwidth)
   cpu_baseline       the fp64 oracle timed on the host on the same workload
 """
@@ -373,6 +375,31 @@ def bench_bwd(gdr, torch, warmup, steps):
     return dict(mean=mean, min=mn, flops=flops, tokens=8 * 4096, ws=ws.numel())
 
 
+def bench_bwd2(gdr, torch, warmup, steps):
+    """gdr2_chunk_bwd on B4 H16 T4096 d128 (bf16 inputs and dL/do, dL/dS_T
+    given, zero S_0).  Algorithmic flops per token-head, chunk C = 16:
+    2 x (9 dk dv + 3 C dk + 3 C dv) -- nine state-sized products (the
+    forward's E~ S^T and state update, E~ S^T again, K~ G^T, dR S, dO S,
+    U G, the two terms of the G update), the decayed A and P entries and
+    their four reverse sums, and the n x n-by-rows products; the exp of
+    the decay tables is not counted."""
+    from gdr_gen import make_gdn2
+    inp = make_gdn2(B=4, T=4096, H=16, Dk=128, Dv=128, dtype="bf16", seed=1004)
+    dev = torch.device("cuda:0")
+    xs = [x.to(dev) for x in (inp.q, inp.k, inp.v, inp.alpha, inp.erase, inp.write)]
+    g = torch.Generator(device="cpu").manual_seed(8)
+    do = torch.randn(xs[2].shape, generator=g).to(torch.bfloat16).to(dev)
+    dsf = (0.1 * torch.randn((4, 16, 128, 128), generator=g)).to(dev)
+    ws = torch.empty(gdr.gdr2_chunk_bwd_workspace_size(4, 4096, 16, 128, 128), dtype=torch.uint8,
+                     device=dev)
+    mean, mn, med, wall = time_launches(
+        lambda: gdr.gdr2_chunk_bwd(*xs, None, do, dsf, workspace=ws), warmup, steps)
+    th = 4 * 4096 * 16
+    C, d = 16, 128
+    flops = th * 2 * (9 * d * d + 3 * C * d + 3 * C * d)
+    return dict(mean=mean, min=mn, flops=flops, tokens=4 * 4096, ws=ws.numel())
+
+
 def bench_copy(torch, warmup, steps, nbytes=512 << 20):
     """A plain device-to-device copy of known size: the achievable-bandwidth
     reference, and the kernel whose FETCH_SIZE / WRITE_SIZE counters scale
@@ -410,7 +437,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "longctx", "l2norm", "gate", "bwd",
-                                       "copy"],
+                                       "bwd2", "copy"],
                     default=None,
                     help="time one operation only (for profiling)")
     ap.add_argument("--skip", default="",
@@ -464,6 +491,9 @@ def main():
     if want("bwd"):
         log("timing gdr_chunk_bwd B8 H16 T4096 d128 ...")
         res["bwd"] = bench_bwd(gdr, torch, min(args.warmup, 5), min(args.steps, 10))
+    if want("bwd2"):
+        log("timing gdr2_chunk_bwd B4 H16 T4096 d128 ...")
+        res["bwd2"] = bench_bwd2(gdr, torch, min(args.warmup, 5), min(args.steps, 10))
     if want("copy"):
         log("timing a 512 MiB device copy ...")
         res["copy"] = bench_copy(torch, args.warmup, args.steps)
@@ -542,6 +572,17 @@ def main():
                            "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_PEAK_TFLOPS,
                                         "unit": "TFLOP/s", "frac": tf / FP32_PEAK_TFLOPS},
                            "flops_per_launch": r["flops"], "workspace_bytes": r["ws"]}
+    if "bwd2" in res:
+        r = res["bwd2"]
+        tf = r["flops"] / r["mean"] / 1e12
+        out["backward2"] = {"workload": "gdr2_chunk_bwd B4 H16 T4096 d128, bf16 inputs and "
+                                        "dL/do, fp32 gradients",
+                            "launch_us_mean": r["mean"] * 1e6,
+                            "tokens/s": r["tokens"] / r["mean"],
+                            "roofline": {"bound": "alu", "achieved": tf,
+                                         "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                         "frac": tf / FP32_PEAK_TFLOPS},
+                            "flops_per_launch": r["flops"], "workspace_bytes": r["ws"]}
     if "copy" in res:
         cp = res["copy"]
         out["copy_reference"] = {"what": "torch device-to-device copy, 512 MiB read + 512 MiB "

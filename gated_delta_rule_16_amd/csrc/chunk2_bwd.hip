@@ -33,6 +33,14 @@
 // per workgroup, dq, dk, db and dG go to per-row-block partials that a
 // second kernel adds (and turns dG into dalpha).  Chunks are 16 tokens so
 // that the per-channel decay tables of a chunk fit in LDS beside the state.
+//
+// The LDS footprint allows one workgroup per CU, one wave per SIMD, so
+// nothing hides memory latency but the kernel itself: every global input of
+// the next chunk (key-side rows, w, v, dL/do and the chunk-start state) is
+// loaded into registers as raw words while the current chunk computes, and
+// written to LDS at the top of the next iteration.  Thread t owns token
+// t / 16 and key channels NC (t % 16) .. + NC for the key-side loads and for
+// the per-channel gradient terms, so those need no further exchange.
 #include "gdr_device.h"
 #include "launch.h"
 #include "vtile.h"
@@ -80,7 +88,9 @@ struct BL2 {
     static constexpr int DT = DP + C2 * PC;
     static constexpr int DA = DT + C2 * PC;
     static constexpr int WV = DA + C2 * PC;      // n x rows tiles [C2][PR]
-    static constexpr int DO = WV + C2 * PR;
+    static constexpr int W = WV + C2 * PR;
+    static constexpr int V = W + C2 * PR;
+    static constexpr int DO = V + C2 * PR;
     static constexpr int R = DO + C2 * PR;
     static constexpr int U = R + C2 * PR;
     static constexpr int DU = U + C2 * PR;
@@ -90,11 +100,24 @@ struct BL2 {
     static_assert(PK % 4 == 0 && NK % 4 == 0 && S % 4 == 0 && G % 4 == 0, "16-byte rows");
 };
 
+// One chunk's global inputs for one thread, as raw words: key-side rows
+// (token tid / 16, channels j0 .. j0 + NC) and a pair of state rows of w, v
+// and dL/do (token tid / 16, rows 2 (tid % 16), + 1).
+template <typename TIn, typename TD, int NC>
+struct Pre2 {
+    static constexpr int WK = NC / packed<TIn>::PER_WORD;
+    static constexpr int WP = 2 / packed<TIn>::PER_WORD;
+    static constexpr int WD = 2 / packed<TD>::PER_WORD;
+    uint32_t k[WK], b[WK], a[WK], q[WK];
+    uint32_t w[WP], v[WP], d[WD];
+};
+
 template <int DK, int DV, typename TIn, typename TD>
 __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
     using L = BL2<DK>;
     constexpr int NRB = DV / R2;
     constexpr int NC = DK / 16;
+    constexpr int NSV = R2 * DK / 4 / NT2;     // 16-byte state pieces per thread
     extern __shared__ __align__(16) float sm[];
     float* Ks = sm + L::K;
     float* Qs = sm + L::Q;
@@ -116,6 +139,8 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
     float* dTs = sm + L::DT;
     float* dAs = sm + L::DA;
     float* WVs = sm + L::WV;
+    float* Wsm = sm + L::W;
+    float* Vsm = sm + L::V;
     float* dOs = sm + L::DO;
     float* Rs = sm + L::R;
     float* Us = sm + L::U;
@@ -132,56 +157,111 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
     const int64_t nch = (T + C2 - 1) / C2;
     float* ckb = p.ck + bh * nch * DV * DK;
     auto tok = [&](int64_t t) { return (b * T + t) * H + h; };
+    const int tr = tid >> 4;                   // this thread's token in the chunk
+    const int j0 = NC * (tid & 15);            // .. and its key channels
+    const int i2 = 2 * (tid & 15);             // .. and its pair of state rows
+    const int i0 = 2 * (tid >> 4);             // state-update tile: rows i0, i0 + 1
+    auto chunk_len = [&](int64_t c) { return (int)min((int64_t)C2, T - c * C2); };
 
-    // ---- chunk inputs (rows >= n: zero tokens with alpha = 1)
-    auto load_chunk = [&](int64_t t0, int n, bool bwd) {
-        for (int e = tid; e < C2 * DK; e += NT2) {
-            const int r = e / DK, c = e % DK;
-            float kv = 0.f, bv = 0.f, qv = 0.f, la = 0.f;
-            if (r < n) {
-                const int64_t off = tok(t0 + r) * DK + c;
-                kv = ldf<TIn>(p.k, off);
-                bv = ldf<TIn>(p.erase, off);
-                la = safe_log(ldf<TIn>(p.alpha, off));
-                if (bwd) qv = ldf<TIn>(p.q, off);
-            }
-            Ks[r * L::PK + c] = kv;
-            Bs[r * L::PK + c] = bv;
-            Es[r * L::PK + c] = bv * kv;
-            Gc[r * L::PK + c] = la;
-            if (bwd) Qs[r * L::PK + c] = qv;
+    using PF = Pre2<TIn, TD, NC>;
+    auto fetch = [&](PF& x, int64_t c, bool bwd) {
+        if (tr < chunk_len(c)) {
+            const int64_t tk = tok(c * C2 + tr);
+            const TIn* kp = reinterpret_cast<const TIn*>(p.k) + tk * DK + j0;
+            ldw(x.k, kp);
+            ldw(x.b, reinterpret_cast<const TIn*>(p.erase) + tk * DK + j0);
+            ldw(x.a, reinterpret_cast<const TIn*>(p.alpha) + tk * DK + j0);
+            if (bwd) ldw(x.q, reinterpret_cast<const TIn*>(p.q) + tk * DK + j0);
+            ldw(x.w, reinterpret_cast<const TIn*>(p.write) + tk * DV + row0 + i2);
+            ldw(x.v, reinterpret_cast<const TIn*>(p.v) + tk * DV + row0 + i2);
+            if (bwd) ldw(x.d, reinterpret_cast<const TD*>(p.dout) + tk * DV + row0 + i2);
         }
-        for (int e = tid; e < C2 * R2; e += NT2) {
-            const int r = e / R2, i = e % R2;
-            float wv = 0.f, dov = 0.f;
-            if (r < n) {
-                const int64_t off = tok(t0 + r) * DV + row0 + i;
-                wv = ldf<TIn>(p.write, off) * ldf<TIn>(p.v, off);
-                if (bwd) dov = ldf<TD>(p.dout, off);
+    };
+    // rows >= n: zero tokens with alpha = 1
+    auto commit = [&](const PF& x, int64_t c, bool bwd) {
+        const bool live = tr < chunk_len(c);
+        const int at = tr * L::PK + j0;
+#pragma unroll
+        for (int y0 = 0; y0 < NC; y0 += 4) {
+            f32x4 kv, bv, ev, gv, qv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int y = y0 + e;
+                kv[e] = live ? packed<TIn>::at(x.k, y) : 0.f;
+                bv[e] = live ? packed<TIn>::at(x.b, y) : 0.f;
+                ev[e] = bv[e] * kv[e];
+                gv[e] = live ? safe_log(packed<TIn>::at(x.a, y)) : 0.f;
+                qv[e] = (live && bwd) ? packed<TIn>::at(x.q, y) : 0.f;
             }
-            WVs[r * L::PR + i] = wv;
-            if (bwd) dOs[r * L::PR + i] = dov;
+            *reinterpret_cast<f32x4*>(Ks + at + y0) = kv;
+            *reinterpret_cast<f32x4*>(Bs + at + y0) = bv;
+            *reinterpret_cast<f32x4*>(Es + at + y0) = ev;
+            *reinterpret_cast<f32x4*>(Gc + at + y0) = gv;
+            if (bwd) *reinterpret_cast<f32x4*>(Qs + at + y0) = qv;
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float wv = live ? packed<TIn>::at(x.w, e) : 0.f;
+            const float vv = live ? packed<TIn>::at(x.v, e) : 0.f;
+            const int o = tr * L::PR + i2 + e;
+            WVs[o] = wv * vv;
+            Wsm[o] = wv;
+            Vsm[o] = vv;
+            if (bwd) dOs[o] = live ? packed<TD>::at(x.d, e) : 0.f;
+        }
+    };
+    auto fetch_s = [&](f32x4 (&sv)[NSV], int64_t c) {
+#pragma unroll
+        for (int it = 0; it < NSV; ++it) {
+            const int e4 = tid + it * NT2;
+            const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
+            sv[it] = *reinterpret_cast<const f32x4*>(ckb + (c * DV + row0 + i) * DK + j);
+        }
+    };
+    auto put_s = [&](const f32x4 (&sv)[NSV], float* dst) {
+#pragma unroll
+        for (int it = 0; it < NSV; ++it) {
+            const int e4 = tid + it * NT2;
+            const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
+            *reinterpret_cast<f32x4*>(dst + i * L::PK + j) = sv[it];
         }
     };
     // after a barrier: G by a scan down the tokens per channel, then the
     // decay tables (two barriers inside)
     auto tables = [&](bool bwd) {
         if (tid < DK) {
-            float acc = 0.f;
-            for (int r = 0; r < C2; ++r) {
-                acc += Gc[r * L::PK + tid];
-                Gc[r * L::PK + tid] = acc;
-            }
+            float g[C2];
+#pragma unroll
+            for (int r = 0; r < C2; ++r) g[r] = Gc[r * L::PK + tid];
+#pragma unroll
+            for (int r = 1; r < C2; ++r) g[r] += g[r - 1];
+#pragma unroll
+            for (int r = 0; r < C2; ++r) Gc[r * L::PK + tid] = g[r];
         }
         __syncthreads();
-        for (int e = tid; e < C2 * DK; e += NT2) {
-            const int r = e / DK, c = e % DK;
-            const float g = Gc[r * L::PK + c], gC = Gc[(C2 - 1) * L::PK + c];
-            const float lm = __expf(g);
-            Lm[r * L::PK + c] = lm;
-            Kt[r * L::PK + c] = Ks[r * L::PK + c] * __expf(gC - g);
-            Et[r * L::PK + c] = Es[r * L::PK + c] * lm;
-            if (bwd) Qt[r * L::PK + c] = Qs[r * L::PK + c] * lm;
+        {
+            const int at = tr * L::PK + j0;
+#pragma unroll
+            for (int y0 = 0; y0 < NC; y0 += 4) {
+                const f32x4 g = ld4(Gc + at + y0), gC = ld4(Gc + (C2 - 1) * L::PK + j0 + y0);
+                const f32x4 k = ld4(Ks + at + y0), e = ld4(Es + at + y0);
+                f32x4 lm, kt, et, qt;
+#pragma unroll
+                for (int z = 0; z < 4; ++z) {
+                    lm[z] = __expf(g[z]);
+                    kt[z] = k[z] * __expf(gC[z] - g[z]);
+                    et[z] = e[z] * lm[z];
+                }
+                *reinterpret_cast<f32x4*>(Lm + at + y0) = lm;
+                *reinterpret_cast<f32x4*>(Kt + at + y0) = kt;
+                *reinterpret_cast<f32x4*>(Et + at + y0) = et;
+                if (bwd) {
+                    const f32x4 q = ld4(Qs + at + y0);
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) qt[z] = q[z] * lm[z];
+                    *reinterpret_cast<f32x4*>(Qt + at + y0) = qt;
+                }
+            }
         }
         __syncthreads();
     };
@@ -191,18 +271,29 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             const int r = tid >> 4, s = tid & 15;
             float av = 0.f, pv = 0.f;
             if (s <= r) {
-                for (int c = 0; c < DK; ++c) {
-                    const float ks = Ks[s * L::PK + c] * __expf(Gc[r * L::PK + c] - Gc[s * L::PK + c]);
-                    av += Es[r * L::PK + c] * ks;
-                    if (bwd) pv += Qs[r * L::PK + c] * ks;
+#pragma unroll 4
+                for (int c = 0; c < DK; c += 4) {
+                    const f32x4 ks = ld4(Ks + s * L::PK + c), gr = ld4(Gc + r * L::PK + c);
+                    const f32x4 gs = ld4(Gc + s * L::PK + c), er = ld4(Es + r * L::PK + c);
+                    f32x4 qr = {0.f, 0.f, 0.f, 0.f};
+                    if (bwd) qr = ld4(Qs + r * L::PK + c);
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) {
+                        const float kd = ks[z] * __expf(gr[z] - gs[z]);
+                        av += er[z] * kd;
+                        pv += qr[z] * kd;
+                    }
                 }
             }
             As[r * L::PC + s] = s < r ? av : 0.f;
             if (bwd) Ps[r * L::PC + s] = pv;
         }
-        for (int e = tid; e < C2 * R2; e += NT2) {
+#pragma unroll
+        for (int it = 0; it < C2 * R2 / NT2; ++it) {
+            const int e = tid + it * NT2;
             const int r = e / R2, i = e % R2;
             float x = 0.f;
+#pragma unroll 8
             for (int c = 0; c < DK; c += 4) {
                 const f32x4 a = ld4(Et + r * L::PK + c), sv = ld4(Ss + i * L::PK + c);
                 x += a[0] * sv[0] + a[1] * sv[1] + a[2] * sv[2] + a[3] * sv[3];
@@ -210,23 +301,36 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             Rs[r * L::PR + i] = WVs[r * L::PR + i] - x;
         }
     };
-    // [rows] x DK tiles: rows 2 (tid / 16), +1; columns NC (tid % 16) ..
-    const int i0 = 2 * (tid >> 4), j0 = NC * (tid & 15);
 
+    PF x;
     // ======================= forward: chunk-start states =====================
-    for (int e = tid; e < R2 * DK; e += NT2) {
-        const int i = e / DK, j = e % DK;
-        Ss[i * L::PK + j] = p.s0 ? p.s0[(bh * DV + row0 + i) * DK + j] : 0.f;
-    }
-    for (int64_t c = 0; c < nch; ++c) {
-        const int64_t t0 = c * C2;
-        const int n = (int)min((int64_t)C2, T - t0);
-        __syncthreads();
-        for (int e = tid; e < R2 * DK; e += NT2) {
-            const int i = e / DK, j = e % DK;
-            ckb[(c * DV + row0 + i) * DK + j] = Ss[i * L::PK + j];
+    {
+        f32x4 sv[NSV];
+        if (p.s0) {
+#pragma unroll
+            for (int it = 0; it < NSV; ++it) {
+                const int e4 = tid + it * NT2;
+                const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
+                sv[it] = *reinterpret_cast<const f32x4*>(p.s0 + (bh * DV + row0 + i) * DK + j);
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < NSV; ++it) sv[it] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        load_chunk(t0, n, false);
+        put_s(sv, Ss);
+    }
+    fetch(x, 0, false);
+    for (int64_t c = 0; c < nch; ++c) {
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < NSV; ++it) {
+            const int e4 = tid + it * NT2;
+            const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
+            *reinterpret_cast<f32x4*>(ckb + (c * DV + row0 + i) * DK + j) =
+                ld4(Ss + i * L::PK + j);
+        }
+        commit(x, c, false);
+        if (c + 1 < nch) fetch(x, c + 1, false);
         __syncthreads();
         tables(false);
         form_ap_r(false);
@@ -237,11 +341,11 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             float u[C2];
 #pragma unroll
             for (int r = 0; r < C2; ++r) {
-                float x = Rs[r * L::PR + i];
+                float v = Rs[r * L::PR + i];
 #pragma unroll
-                for (int s = 0; s < r; ++s) x -= As[r * L::PC + s] * u[s];
-                u[r] = x;
-                Us[r * L::PR + i] = x;
+                for (int s = 0; s < r; ++s) v -= As[r * L::PC + s] * u[s];
+                u[r] = v;
+                Us[r * L::PR + i] = v;
             }
         }
         __syncthreads();
@@ -249,34 +353,45 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         {
             float acc[2][NC];
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
+            for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int y = 0; y < NC; ++y)
-                    acc[x][y] = Ss[(i0 + x) * L::PK + j0 + y] * Lm[(C2 - 1) * L::PK + j0 + y];
-            mm2n<C2, NC>(acc, [&](int x, int r) { return Us[r * L::PR + i0 + x]; }, Kt, L::PK, j0);
+                    acc[a][y] = Ss[(i0 + a) * L::PK + j0 + y] * Lm[(C2 - 1) * L::PK + j0 + y];
+            mm2n<C2, NC>(acc, [&](int a, int r) { return Us[r * L::PR + i0 + a]; }, Kt, L::PK, j0);
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
+            for (int a = 0; a < 2; ++a)
 #pragma unroll
-                for (int y = 0; y < NC; ++y) Ss[(i0 + x) * L::PK + j0 + y] = acc[x][y];
+                for (int y = 0; y < NC; ++y) Ss[(i0 + a) * L::PK + j0 + y] = acc[a][y];
         }
     }
 
     // ======================= reverse sweep ====================================
     __syncthreads();
-    for (int e = tid; e < R2 * DK; e += NT2) {
-        const int i = e / DK, j = e % DK;
-        Gs[i * L::PK + j] = p.dsf ? p.dsf[(bh * DV + row0 + i) * DK + j] : 0.f;
+    {
+        f32x4 gv[NSV];
+#pragma unroll
+        for (int it = 0; it < NSV; ++it) {
+            const int e4 = tid + it * NT2;
+            const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
+            gv[it] = p.dsf ? *reinterpret_cast<const f32x4*>(p.dsf + (bh * DV + row0 + i) * DK + j)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        put_s(gv, Gs);
     }
     const int64_t poff = (int64_t)rb * p.BTH * DK;
+    f32x4 sv[NSV];
+    fetch(x, nch - 1, true);
+    fetch_s(sv, nch - 1);
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int64_t t0 = c * C2;
-        const int n = (int)min((int64_t)C2, T - t0);
+        const int n = chunk_len(c);
         __syncthreads();
-        for (int e = tid; e < R2 * DK; e += NT2) {
-            const int i = e / DK, j = e % DK;
-            Ss[i * L::PK + j] = ckb[(c * DV + row0 + i) * DK + j];
+        put_s(sv, Ss);
+        commit(x, c, true);
+        if (c > 0) {
+            fetch(x, c - 1, true);
+            fetch_s(sv, c - 1);
         }
-        load_chunk(t0, n, true);
         __syncthreads();
         tables(true);
         form_ap_r(true);
@@ -287,20 +402,23 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             float tc[C2];
 #pragma unroll
             for (int r = 0; r < C2; ++r) {
-                float x = r == cc ? 1.f : 0.f;
+                float v = r == cc ? 1.f : 0.f;
 #pragma unroll
-                for (int m = 0; m < r; ++m) x -= As[r * L::PC + m] * tc[m];
-                tc[r] = r < cc ? 0.f : x;
+                for (int m = 0; m < r; ++m) v -= As[r * L::PC + m] * tc[m];
+                tc[r] = r < cc ? 0.f : v;
                 Ts[r * L::PC + cc] = tc[r];
             }
         }
         __syncthreads();
         // U = T R;  dU = P^T dO + K~ G'^T
-        for (int e = tid; e < C2 * R2; e += NT2) {
+#pragma unroll
+        for (int it = 0; it < C2 * R2 / NT2; ++it) {
+            const int e = tid + it * NT2;
             const int r = e / R2, i = e % R2;
             float u = 0.f, du = 0.f;
             for (int s = 0; s <= r; ++s) u += Ts[r * L::PC + s] * Rs[s * L::PR + i];
             for (int s = r; s < C2; ++s) du += Ps[s * L::PC + r] * dOs[s * L::PR + i];
+#pragma unroll 8
             for (int cc = 0; cc < DK; cc += 4) {
                 const f32x4 kt = ld4(Kt + r * L::PK + cc), gv = ld4(Gs + i * L::PK + cc);
                 du += kt[0] * gv[0] + kt[1] * gv[1] + kt[2] * gv[2] + kt[3] * gv[3];
@@ -310,91 +428,118 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         }
         __syncthreads();
         // dR = T^T dU (dw = dR (.) v, dv = dR (.) w to HBM);  dP = dO U^T (s <= r)
-        for (int e = tid; e < C2 * R2; e += NT2) {
+#pragma unroll
+        for (int it = 0; it < C2 * R2 / NT2; ++it) {
+            const int e = tid + it * NT2;
             const int r = e / R2, i = e % R2;
-            float x = 0.f;
-            for (int s = r; s < C2; ++s) x += Ts[s * L::PC + r] * dUs[s * L::PR + i];
-            dRs[r * L::PR + i] = x;
+            float v = 0.f;
+            for (int s = r; s < C2; ++s) v += Ts[s * L::PC + r] * dUs[s * L::PR + i];
+            dRs[r * L::PR + i] = v;
             if (r < n) {
                 const int64_t off = tok(t0 + r) * DV + row0 + i;
-                p.dw[off] = x * ldf<TIn>(p.v, off);
-                p.dv[off] = x * ldf<TIn>(p.write, off);
+                p.dw[off] = v * Vsm[r * L::PR + i];
+                p.dv[off] = v * Wsm[r * L::PR + i];
             }
         }
         {
             const int r = tid >> 4, s = tid & 15;
-            float x = 0.f;
-            if (s <= r)
-                for (int i = 0; i < R2; ++i) x += dOs[r * L::PR + i] * Us[s * L::PR + i];
-            dPs[r * L::PC + s] = x;
+            float v = 0.f;
+            if (s <= r) {
+#pragma unroll 8
+                for (int i = 0; i < R2; ++i) v += dOs[r * L::PR + i] * Us[s * L::PR + i];
+            }
+            dPs[r * L::PC + s] = v;
         }
         __syncthreads();
         {   // dT = dU R^T, strict lower
             const int r = tid >> 4, s = tid & 15;
-            float x = 0.f;
-            if (s < r)
-                for (int i = 0; i < R2; ++i) x += dUs[r * L::PR + i] * Rs[s * L::PR + i];
-            dTs[r * L::PC + s] = x;
+            float v = 0.f;
+            if (s < r) {
+#pragma unroll 8
+                for (int i = 0; i < R2; ++i) v += dUs[r * L::PR + i] * Rs[s * L::PR + i];
+            }
+            dTs[r * L::PC + s] = v;
         }
         __syncthreads();
         {   // Y = dT T^T into dA's tile
             const int r = tid >> 4, s = tid & 15;
-            float x = 0.f;
-            for (int bb = 0; bb <= s && bb < r; ++bb) x += dTs[r * L::PC + bb] * Ts[s * L::PC + bb];
-            dAs[r * L::PC + s] = x;
+            float v = 0.f;
+            for (int bb = 0; bb <= s && bb < r; ++bb) v += dTs[r * L::PC + bb] * Ts[s * L::PC + bb];
+            dAs[r * L::PC + s] = v;
         }
         __syncthreads();
         {   // dA = -T^T Y, strict lower, into dT's tile
             const int r = tid >> 4, s = tid & 15;
-            float x = 0.f;
+            float v = 0.f;
             if (s < r)
-                for (int a = r; a < C2; ++a) x -= Ts[a * L::PC + r] * dAs[a * L::PC + s];
-            dTs[r * L::PC + s] = x;
+                for (int a = r; a < C2; ++a) v -= Ts[a * L::PC + r] * dAs[a * L::PC + s];
+            dTs[r * L::PC + s] = v;
         }
         __syncthreads();
         const float* dA = dTs;
-        // ---- per (token r, channels j0 .. j0 + NC - 1)
+        // ---- per (token tr, channels j0 .. j0 + NC - 1)
         {
-            const int r = tid >> 4;
+            const int r = tr;
             float dEt[NC] = {}, dQt[NC] = {}, dKt[NC] = {};
             mm1n<R2, NC>(dEt, [&](int i) { return -dRs[r * L::PR + i]; }, Ss, L::PK, j0);
             mm1n<R2, NC>(dQt, [&](int i) { return dOs[r * L::PR + i]; }, Ss, L::PK, j0);
             mm1n<R2, NC>(dKt, [&](int i) { return Us[r * L::PR + i]; }, Gs, L::PK, j0);
+            float gr[NC];
+#pragma unroll
+            for (int y0 = 0; y0 < NC; y0 += 4) {
+                const f32x4 g = ld4(Gc + r * L::PK + j0 + y0);
+#pragma unroll
+                for (int z = 0; z < 4; ++z) gr[y0 + z] = g[z];
+            }
             float dEa[NC] = {}, dQa[NC] = {}, dKa[NC] = {};
             for (int s = 0; s <= r; ++s) {
                 const float da = dA[r * L::PC + s], dp = dPs[r * L::PC + s];
 #pragma unroll
-                for (int y = 0; y < NC; ++y) {
-                    const int cc = j0 + y;
-                    const float ks = Ks[s * L::PK + cc] *
-                                     __expf(Gc[r * L::PK + cc] - Gc[s * L::PK + cc]);
-                    dEa[y] += da * ks;
-                    dQa[y] += dp * ks;
+                for (int y0 = 0; y0 < NC; y0 += 4) {
+                    const f32x4 ks = ld4(Ks + s * L::PK + j0 + y0), gs = ld4(Gc + s * L::PK + j0 + y0);
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) {
+                        const float kd = ks[z] * __expf(gr[y0 + z] - gs[z]);
+                        dEa[y0 + z] += da * kd;
+                        dQa[y0 + z] += dp * kd;
+                    }
                 }
             }
             for (int r2 = r; r2 < C2; ++r2) {
                 const float da = dA[r2 * L::PC + r], dp = dPs[r2 * L::PC + r];
 #pragma unroll
-                for (int y = 0; y < NC; ++y) {
-                    const int cc = j0 + y;
-                    const float gm = __expf(Gc[r2 * L::PK + cc] - Gc[r * L::PK + cc]);
-                    dKa[y] += (da * Es[r2 * L::PK + cc] + dp * Qs[r2 * L::PK + cc]) * gm;
+                for (int y0 = 0; y0 < NC; y0 += 4) {
+                    const f32x4 g2 = ld4(Gc + r2 * L::PK + j0 + y0);
+                    const f32x4 e2 = ld4(Es + r2 * L::PK + j0 + y0), q2 = ld4(Qs + r2 * L::PK + j0 + y0);
+#pragma unroll
+                    for (int z = 0; z < 4; ++z)
+                        dKa[y0 + z] += (da * e2[z] + dp * q2[z]) * __expf(g2[z] - gr[y0 + z]);
                 }
             }
             float oq[NC], ok[NC], ob[NC];
 #pragma unroll
-            for (int y = 0; y < NC; ++y) {
-                const int at = r * L::PK + j0 + y;
-                const float lm = Lm[at];
-                const float dE = dEa[y] + dEt[y] * lm;
-                oq[y] = dQa[y] + dQt[y] * lm;
-                const float kdec = __expf(Gc[(C2 - 1) * L::PK + j0 + y] - Gc[at]);
-                ok[y] = dKa[y] + dKt[y] * kdec + dE * Bs[at];
-                ob[y] = dE * Ks[at];
-                const float ktk = dKt[y] * Kt[at];
-                Scr[at] = ktk;
-                Dg[at] = Es[at] * dEa[y] + Qs[at] * dQa[y] - Ks[at] * dKa[y] + dEt[y] * Et[at] +
-                         dQt[y] * Qt[at] - ktk;
+            for (int y0 = 0; y0 < NC; y0 += 4) {
+                const int at = r * L::PK + j0 + y0;
+                const f32x4 lm = ld4(Lm + at), ks = ld4(Ks + at), bs = ld4(Bs + at);
+                const f32x4 es = ld4(Es + at), qs = ld4(Qs + at), kt = ld4(Kt + at);
+                const f32x4 et = ld4(Et + at), qt = ld4(Qt + at);
+                const f32x4 gC = ld4(Gc + (C2 - 1) * L::PK + j0 + y0);
+                f32x4 scr, dg;
+#pragma unroll
+                for (int z = 0; z < 4; ++z) {
+                    const int y = y0 + z;
+                    const float dE = dEa[y] + dEt[y] * lm[z];
+                    oq[y] = dQa[y] + dQt[y] * lm[z];
+                    const float kdec = __expf(gC[z] - gr[y]);
+                    ok[y] = dKa[y] + dKt[y] * kdec + dE * bs[z];
+                    ob[y] = dE * ks[z];
+                    const float ktk = dKt[y] * kt[z];
+                    scr[z] = ktk;
+                    dg[z] = es[z] * dEa[y] + qs[z] * dQa[y] - ks[z] * dKa[y] + dEt[y] * et[z] +
+                            dQt[y] * qt[z] - ktk;
+                }
+                *reinterpret_cast<f32x4*>(Scr + at) = scr;
+                *reinterpret_cast<f32x4*>(Dg + at) = dg;
             }
             if (r < n) {
                 const int64_t o = poff + tok(t0 + r) * DK + j0;
@@ -415,36 +560,43 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         if (tid < DK) {
             const int cc = tid;
             float cs = 0.f, gs2 = 0.f;
+#pragma unroll
             for (int r = 0; r < C2; ++r) cs += Scr[r * L::PK + cc];
+#pragma unroll 8
             for (int i = 0; i < R2; ++i) gs2 += Gs[i * L::PK + cc] * Ss[i * L::PK + cc];
             Dg[(n - 1) * L::PK + cc] += cs + gs2 * Lm[(C2 - 1) * L::PK + cc];
         }
         __syncthreads();
-        for (int e = tid; e < n * DK; e += NT2) {
-            const int r = e / DK, cc = e % DK;
-            p.pg[poff + tok(t0 + r) * DK + cc] = Dg[r * L::PK + cc];
+        if (tr < n) {
+            const int64_t o = poff + tok(t0 + tr) * DK + j0;
+#pragma unroll
+            for (int y0 = 0; y0 < NC; y0 += 4)
+                *reinterpret_cast<f32x4*>(p.pg + o + y0) = ld4(Dg + tr * L::PK + j0 + y0);
         }
         // ---- G' <- G' diag(lambda_C) + dO^T Q~ - dR^T E~ (each thread its own entries)
         {
             float acc[2][NC];
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
+            for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int y = 0; y < NC; ++y)
-                    acc[x][y] = Gs[(i0 + x) * L::PK + j0 + y] * Lm[(C2 - 1) * L::PK + j0 + y];
-            mm2n<C2, NC>(acc, [&](int x, int r) { return dOs[r * L::PR + i0 + x]; }, Qt, L::PK, j0);
-            mm2n<C2, NC>(acc, [&](int x, int r) { return -dRs[r * L::PR + i0 + x]; }, Et, L::PK, j0);
+                    acc[a][y] = Gs[(i0 + a) * L::PK + j0 + y] * Lm[(C2 - 1) * L::PK + j0 + y];
+            mm2n<C2, NC>(acc, [&](int a, int r) { return dOs[r * L::PR + i0 + a]; }, Qt, L::PK, j0);
+            mm2n<C2, NC>(acc, [&](int a, int r) { return -dRs[r * L::PR + i0 + a]; }, Et, L::PK, j0);
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
+            for (int a = 0; a < 2; ++a)
 #pragma unroll
-                for (int y = 0; y < NC; ++y) Gs[(i0 + x) * L::PK + j0 + y] = acc[x][y];
+                for (int y = 0; y < NC; ++y) Gs[(i0 + a) * L::PK + j0 + y] = acc[a][y];
         }
     }
     __syncthreads();
     if (p.ds0) {
-        for (int e = tid; e < R2 * DK; e += NT2) {
-            const int i = e / DK, j = e % DK;
-            p.ds0[(bh * DV + row0 + i) * DK + j] = Gs[i * L::PK + j];
+#pragma unroll
+        for (int it = 0; it < NSV; ++it) {
+            const int e4 = tid + it * NT2;
+            const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
+            *reinterpret_cast<f32x4*>(p.ds0 + (bh * DV + row0 + i) * DK + j) =
+                ld4(Gs + i * L::PK + j);
         }
     }
 }
