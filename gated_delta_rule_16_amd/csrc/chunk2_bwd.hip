@@ -1,5 +1,5 @@
 // gdr2_chunk_bwd: reverse mode of Gated Delta Rule-2, chunk by chunk, in
-// fp32 vector-ALU arithmetic.
+// fp32 (matrix-core fp32 products, vector-ALU elsewhere).
 //
 // Per chunk of n <= 16 tokens (G the within-chunk cumulative log alpha per
 // channel, lambda = e^G, E = b (.) k, Gamma_rsc = e^{G_rc - G_sc}, E~ = E (.)
@@ -27,20 +27,28 @@
 // (dE_A, dQ_P, dK_AP the A and P parts), and dlog alpha is the reverse
 // cumulative sum of dG inside the chunk, per channel.
 //
-// Work split as in gdr_chunk_bwd: one 256-thread workgroup per (b, h, 32
-// state rows) runs the forward over its rows (chunk-start states to the
-// workspace), then walks the chunks in reverse; dv, dw and dS_0 are final
-// per workgroup, dq, dk, db and dG go to per-row-block partials that a
-// second kernel adds (and turns dG into dalpha).  Chunks are 16 tokens so
-// that the per-channel decay tables of a chunk fit in LDS beside the state.
+// Factored decay.  Gamma_rsc = e^{G_rc} e^{-G_sc}, so with K^ = K (.) e^{-G}
+// the decayed sums are plain products: A = E~ K^T, P = Q~ K^T,
+// dE_A = lambda (.) (dA K^), dQ_P = lambda (.) (dP K^),
+// dK_AP = e^{-G} (.) (dA^T E~ + dP^T Q~).  e^{-G} <= 1 / lambda_C, so a chunk
+// where some channel has G_C < -60 ("wide") forms A, P and those sums entry
+// by entry from the log decays instead; every other product is the same.
 //
-// The LDS footprint allows one workgroup per CU, one wave per SIMD, so
-// nothing hides memory latency but the kernel itself: every global input of
-// the next chunk (key-side rows, w, v, dL/do and the chunk-start state) is
-// loaded into registers as raw words while the current chunk computes, and
-// written to LDS at the top of the next iteration.  Thread t owns token
-// t / 16 and key channels NC (t % 16) .. + NC for the key-side loads and for
-// the per-channel gradient terms, so those need no further exchange.
+// Work split: one 256-thread workgroup (4 waves) per (b, h, 32 state rows)
+// runs the forward over its rows (chunk-start states to the workspace), then
+// walks the chunks in reverse.  dv, dw and dS_0 are final per workgroup; dq,
+// dk, db and the within-chunk d log alpha go to per-row-block partials that
+// a second kernel adds (and divides by alpha).  Every product is a set of 16 x 16 tiles on
+// the fp32 matrix cores (v_mfma_f32_16x16x4f32: fp32 operands and
+// accumulation, the vector ALU's precision), the tiles of a phase dealt to
+// the four waves; the triangular solves and the elementwise terms are
+// vector ALU.  Per chunk the per-channel gradients stay in the registers of
+// the wave that owns those channels, from the products to the HBM stores.
+//
+// The LDS footprint (~142 KB) allows one workgroup per CU, one wave per SIMD,
+// so every global input of the next chunk (key-side rows, w, v, dL/do, the
+// chunk-start state) is loaded into registers as raw words while the current
+// chunk computes, and written to LDS at the top of the next iteration.
 #include "gdr_device.h"
 #include "launch.h"
 #include "vtile.h"
@@ -49,9 +57,10 @@ namespace gdr {
 
 namespace {
 
-constexpr int C2 = 16;     // tokens per chunk
-constexpr int R2 = 32;     // state rows per workgroup
-constexpr int NT2 = 256;   // threads per workgroup
+constexpr int C2 = 16;         // tokens per chunk
+constexpr int R2 = 32;         // state rows per workgroup
+constexpr int NT2 = 256;       // threads per workgroup
+constexpr float WIDE = -60.f;  // G_C below this: entry-by-entry decays
 
 struct Bwd2Params {
     int64_t T, H, BTH;
@@ -62,11 +71,14 @@ struct Bwd2Params {
     float *pq, *pk, *pb, *pg;      // [NRB][BTH][Dk] each
 };
 
+// LDS tables.  Pitches: key-side rows PK = 4 (mod 64), n x rows PR = 36,
+// n x n PC = 20; with the operand order of mma16 these make both its row
+// reads (16-byte) and its column reads (4-byte) free of bank conflicts.
 template <int DK>
-struct BL2 {
+struct BL3 {
     static constexpr int PK = DK + 4;
-    static constexpr int PC = C2 + 1;
-    static constexpr int PR = R2 + 1;
+    static constexpr int PC = 20;
+    static constexpr int PR = 36;
     static constexpr int NK = C2 * PK;           // one token x key-dim table
     static constexpr int K = 0;
     static constexpr int Q = K + NK;
@@ -77,28 +89,66 @@ struct BL2 {
     static constexpr int KT = LM + NK;           // K~
     static constexpr int QT = KT + NK;           // Q~
     static constexpr int ET = QT + NK;           // E~
-    static constexpr int SCR = ET + NK;          // dK~ (.) K~ (column sums)
-    static constexpr int DG = SCR + NK;          // dG partial, staged
-    static constexpr int S = DG + NK;            // [R2][PK] chunk-start state rows
+    static constexpr int KH = ET + NK;           // K^ = K (.) e^{-G}
+    static constexpr int S = KH + NK;            // [R2][PK] chunk-start state rows
     static constexpr int G = S + R2 * PK;        // [R2][PK] dL/dS' rows
     static constexpr int A = G + R2 * PK;        // n x n tiles [C2][PC]
     static constexpr int TM = A + C2 * PC;
     static constexpr int P = TM + C2 * PC;
     static constexpr int DP = P + C2 * PC;
-    static constexpr int DT = DP + C2 * PC;
-    static constexpr int DA = DT + C2 * PC;
-    static constexpr int WV = DA + C2 * PC;      // n x rows tiles [C2][PR]
-    static constexpr int W = WV + C2 * PR;
+    static constexpr int DT = DP + C2 * PC;      // dT, then dA
+    static constexpr int Y = DT + C2 * PC;
+    static constexpr int W = Y + C2 * PC;        // n x rows tiles [C2][PR]
     static constexpr int V = W + C2 * PR;
     static constexpr int DO = V + C2 * PR;
     static constexpr int R = DO + C2 * PR;
     static constexpr int U = R + C2 * PR;
     static constexpr int DU = U + C2 * PR;
     static constexpr int DR = DU + C2 * PR;
-    static constexpr int TOTAL = DR + C2 * PR;
+    static constexpr int GS = DR + C2 * PR;      // [DK] sum_i G'_ic S_ic
+    static constexpr int TOTAL = GS + DK;
     static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget");
-    static_assert(PK % 4 == 0 && NK % 4 == 0 && S % 4 == 0 && G % 4 == 0, "16-byte rows");
+    static_assert(PK % 64 == 4 && NK % 4 == 0 && S % 4 == 0 && G % 4 == 0, "pitches");
+    static_assert(A % 4 == 0 && W % 4 == 0 && (Y - A) % 4 == 0, "16-byte rows");
 };
+
+// acc += A B for one 16 x 16 tile over K = 16 NQ on the fp32 matrix cores.
+// Lane l holds D[4 (l / 16) + i][l % 16] in acc[i].  Operands from LDS:
+// A(m, k) = AR ? A[m pa + k] : A[k pa + m], B(k, n) = BR ? B[n pb + k] : B[k pb + n]
+// (NEG negates A).  Inside each 16-deep block, lane group g = l / 16 takes
+// k = 16 q + 4 g + e on the e-th instruction, so a row operand is one 16-byte
+// read per block and a column operand reads rows 4 apart across the groups.
+template <int NQ, bool AR, bool BR, bool NEG = false>
+__device__ __forceinline__ f32x4 mma16(f32x4 acc, const float* A, int pa, const float* B, int pb) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int kb = 16 * q + 4 * g;
+        f32x4 av, bv;
+        if constexpr (AR) {
+            av = ld4(A + l16 * pa + kb);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) av[e] = A[(kb + e) * pa + l16];
+        }
+        if constexpr (BR) {
+            bv = ld4(B + l16 * pb + kb);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bv[e] = B[(kb + e) * pb + l16];
+        }
+        if constexpr (NEG) av = -av;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+}
 
 // One chunk's global inputs for one thread, as raw words: key-side rows
 // (token tid / 16, channels j0 .. j0 + NC) and a pair of state rows of w, v
@@ -114,10 +164,12 @@ struct Pre2 {
 
 template <int DK, int DV, typename TIn, typename TD>
 __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
-    using L = BL2<DK>;
+    using L = BL3<DK>;
     constexpr int NRB = DV / R2;
     constexpr int NC = DK / 16;
-    constexpr int NSV = R2 * DK / 4 / NT2;     // 16-byte state pieces per thread
+    constexpr int NQK = DK / 16;                // 16-deep blocks over the key dim
+    constexpr int CTW = DK / 64;                // channel tiles per wave
+    constexpr int NSV = R2 * DK / 4 / NT2;      // 16-byte state pieces per thread
     extern __shared__ __align__(16) float sm[];
     float* Ks = sm + L::K;
     float* Qs = sm + L::Q;
@@ -128,8 +180,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
     float* Kt = sm + L::KT;
     float* Qt = sm + L::QT;
     float* Et = sm + L::ET;
-    float* Scr = sm + L::SCR;
-    float* Dg = sm + L::DG;
+    float* Kh = sm + L::KH;
     float* Ss = sm + L::S;
     float* Gs = sm + L::G;
     float* As = sm + L::A;
@@ -137,8 +188,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
     float* Ps = sm + L::P;
     float* dPs = sm + L::DP;
     float* dTs = sm + L::DT;
-    float* dAs = sm + L::DA;
-    float* WVs = sm + L::WV;
+    float* Ys = sm + L::Y;
     float* Wsm = sm + L::W;
     float* Vsm = sm + L::V;
     float* dOs = sm + L::DO;
@@ -146,8 +196,10 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
     float* Us = sm + L::U;
     float* dUs = sm + L::DU;
     float* dRs = sm + L::DR;
+    float* GSc = sm + L::GS;
 
     const int tid = threadIdx.x;
+    const int wv = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
     const int rb = blockIdx.x % NRB;
     const int64_t bh = blockIdx.x / NRB;
     const int64_t h = bh % p.H;
@@ -157,18 +209,16 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
     const int64_t nch = (T + C2 - 1) / C2;
     float* ckb = p.ck + bh * nch * DV * DK;
     auto tok = [&](int64_t t) { return (b * T + t) * H + h; };
-    const int tr = tid >> 4;                   // this thread's token in the chunk
+    const int tr = tid >> 4;                   // this thread's token for the loads
     const int j0 = NC * (tid & 15);            // .. and its key channels
     const int i2 = 2 * (tid & 15);             // .. and its pair of state rows
-    const int i0 = 2 * (tid >> 4);             // state-update tile: rows i0, i0 + 1
     auto chunk_len = [&](int64_t c) { return (int)min((int64_t)C2, T - c * C2); };
 
     using PF = Pre2<TIn, TD, NC>;
     auto fetch = [&](PF& x, int64_t c, bool bwd) {
         if (tr < chunk_len(c)) {
             const int64_t tk = tok(c * C2 + tr);
-            const TIn* kp = reinterpret_cast<const TIn*>(p.k) + tk * DK + j0;
-            ldw(x.k, kp);
+            ldw(x.k, reinterpret_cast<const TIn*>(p.k) + tk * DK + j0);
             ldw(x.b, reinterpret_cast<const TIn*>(p.erase) + tk * DK + j0);
             ldw(x.a, reinterpret_cast<const TIn*>(p.alpha) + tk * DK + j0);
             if (bwd) ldw(x.q, reinterpret_cast<const TIn*>(p.q) + tk * DK + j0);
@@ -201,12 +251,9 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const float wv = live ? packed<TIn>::at(x.w, e) : 0.f;
-            const float vv = live ? packed<TIn>::at(x.v, e) : 0.f;
             const int o = tr * L::PR + i2 + e;
-            WVs[o] = wv * vv;
-            Wsm[o] = wv;
-            Vsm[o] = vv;
+            Wsm[o] = live ? packed<TIn>::at(x.w, e) : 0.f;
+            Vsm[o] = live ? packed<TIn>::at(x.v, e) : 0.f;
             if (bwd) dOs[o] = live ? packed<TD>::at(x.d, e) : 0.f;
         }
     };
@@ -226,9 +273,10 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             *reinterpret_cast<f32x4*>(dst + i * L::PK + j) = sv[it];
         }
     };
-    // after a barrier: G by a scan down the tokens per channel, then the
-    // decay tables (two barriers inside)
+    // after a barrier: G by a scan down the tokens per channel (and whether
+    // the chunk is wide), then the decay tables; ends on a barrier
     auto tables = [&](bool bwd) {
+        bool wide_here = false;
         if (tid < DK) {
             float g[C2];
 #pragma unroll
@@ -237,72 +285,81 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             for (int r = 1; r < C2; ++r) g[r] += g[r - 1];
 #pragma unroll
             for (int r = 0; r < C2; ++r) Gc[r * L::PK + tid] = g[r];
+            wide_here = g[C2 - 1] < WIDE;
+        }
+        const bool wide = __syncthreads_or(wide_here);
+        const int at = tr * L::PK + j0;
+#pragma unroll
+        for (int y0 = 0; y0 < NC; y0 += 4) {
+            const f32x4 g = ld4(Gc + at + y0), gC = ld4(Gc + (C2 - 1) * L::PK + j0 + y0);
+            const f32x4 k = ld4(Ks + at + y0), e = ld4(Es + at + y0);
+            f32x4 lm, kt, et, kh;
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                lm[z] = expf(g[z]);
+                kt[z] = k[z] * expf(gC[z] - g[z]);
+                et[z] = e[z] * lm[z];
+                kh[z] = wide ? 0.f : k[z] * expf(-g[z]);
+            }
+            *reinterpret_cast<f32x4*>(Lm + at + y0) = lm;
+            *reinterpret_cast<f32x4*>(Kt + at + y0) = kt;
+            *reinterpret_cast<f32x4*>(Et + at + y0) = et;
+            *reinterpret_cast<f32x4*>(Kh + at + y0) = kh;
+            if (bwd) {
+                const f32x4 q = ld4(Qs + at + y0);
+                f32x4 qt;
+#pragma unroll
+                for (int z = 0; z < 4; ++z) qt[z] = q[z] * lm[z];
+                *reinterpret_cast<f32x4*>(Qt + at + y0) = qt;
+            }
         }
         __syncthreads();
-        {
-            const int at = tr * L::PK + j0;
-#pragma unroll
-            for (int y0 = 0; y0 < NC; y0 += 4) {
-                const f32x4 g = ld4(Gc + at + y0), gC = ld4(Gc + (C2 - 1) * L::PK + j0 + y0);
-                const f32x4 k = ld4(Ks + at + y0), e = ld4(Es + at + y0);
-                f32x4 lm, kt, et, qt;
+        return wide;
+    };
+    // wide chunks: A (s < r) and P (s <= r) entry by entry from the log
+    // decays, one thread per (r, s)
+    auto ap_entries = [&](bool bwd) {
+        const int r = tid >> 4, s = tid & 15;
+        float av = 0.f, pv = 0.f;
+        if (s <= r) {
+#pragma unroll 4
+            for (int c = 0; c < DK; c += 4) {
+                const f32x4 ks = ld4(Ks + s * L::PK + c), gr = ld4(Gc + r * L::PK + c);
+                const f32x4 gs = ld4(Gc + s * L::PK + c), er = ld4(Es + r * L::PK + c);
+                f32x4 qr = {0.f, 0.f, 0.f, 0.f};
+                if (bwd) qr = ld4(Qs + r * L::PK + c);
 #pragma unroll
                 for (int z = 0; z < 4; ++z) {
-                    lm[z] = __expf(g[z]);
-                    kt[z] = k[z] * __expf(gC[z] - g[z]);
-                    et[z] = e[z] * lm[z];
-                }
-                *reinterpret_cast<f32x4*>(Lm + at + y0) = lm;
-                *reinterpret_cast<f32x4*>(Kt + at + y0) = kt;
-                *reinterpret_cast<f32x4*>(Et + at + y0) = et;
-                if (bwd) {
-                    const f32x4 q = ld4(Qs + at + y0);
-#pragma unroll
-                    for (int z = 0; z < 4; ++z) qt[z] = q[z] * lm[z];
-                    *reinterpret_cast<f32x4*>(Qt + at + y0) = qt;
+                    const float kd = ks[z] * __expf(gr[z] - gs[z]);
+                    av += er[z] * kd;
+                    pv += qr[z] * kd;
                 }
             }
         }
-        __syncthreads();
+        As[r * L::PC + s] = s < r ? av : 0.f;
+        if (bwd) Ps[r * L::PC + s] = pv;
     };
-    // A (s < r) and P (s <= r), the decay inside the dot product; R = w.v - E~ S^T
-    auto form_ap_r = [&](bool bwd) {
-        {
-            const int r = tid >> 4, s = tid & 15;
-            float av = 0.f, pv = 0.f;
-            if (s <= r) {
-#pragma unroll 4
-                for (int c = 0; c < DK; c += 4) {
-                    const f32x4 ks = ld4(Ks + s * L::PK + c), gr = ld4(Gc + r * L::PK + c);
-                    const f32x4 gs = ld4(Gc + s * L::PK + c), er = ld4(Es + r * L::PK + c);
-                    f32x4 qr = {0.f, 0.f, 0.f, 0.f};
-                    if (bwd) qr = ld4(Qs + r * L::PK + c);
+    // a 16 x 16 n x n tile from this wave's accumulator, masked to s < r
+    // (strict) or s <= r
+    auto put_nn = [&](const f32x4& acc, float* D, bool strict) {
 #pragma unroll
-                    for (int z = 0; z < 4; ++z) {
-                        const float kd = ks[z] * __expf(gr[z] - gs[z]);
-                        av += er[z] * kd;
-                        pv += qr[z] * kd;
-                    }
-                }
-            }
-            As[r * L::PC + s] = s < r ? av : 0.f;
-            if (bwd) Ps[r * L::PC + s] = pv;
-        }
-#pragma unroll
-        for (int it = 0; it < C2 * R2 / NT2; ++it) {
-            const int e = tid + it * NT2;
-            const int r = e / R2, i = e % R2;
-            float x = 0.f;
-#pragma unroll 8
-            for (int c = 0; c < DK; c += 4) {
-                const f32x4 a = ld4(Et + r * L::PK + c), sv = ld4(Ss + i * L::PK + c);
-                x += a[0] * sv[0] + a[1] * sv[1] + a[2] * sv[2] + a[3] * sv[3];
-            }
-            Rs[r * L::PR + i] = WVs[r * L::PR + i] - x;
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * lg + i;
+            D[r * L::PC + l16] = (strict ? l16 < r : l16 <= r) ? acc[i] : 0.f;
         }
     };
+    // R tile t (rows 16 t ..): R = w (.) v - E~ S^T
+    auto r_tile = [&](int t) {
+        f32x4 acc = mma16<NQK, true, true>(f32x4{0.f, 0.f, 0.f, 0.f}, Et, L::PK,
+                                           Ss + 16 * t * L::PK, L::PK);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int o = (4 * lg + i) * L::PR + 16 * t + l16;
+            Rs[o] = Wsm[o] * Vsm[o] - acc[i];
+        }
+    };
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    PF x;
     // ======================= forward: chunk-start states =====================
     {
         f32x4 sv[NSV];
@@ -315,10 +372,11 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             }
         } else {
 #pragma unroll
-            for (int it = 0; it < NSV; ++it) sv[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int it = 0; it < NSV; ++it) sv[it] = zero4;
         }
         put_s(sv, Ss);
     }
+    PF x;
     fetch(x, 0, false);
     for (int64_t c = 0; c < nch; ++c) {
         __syncthreads();
@@ -332,8 +390,10 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         commit(x, c, false);
         if (c + 1 < nch) fetch(x, c + 1, false);
         __syncthreads();
-        tables(false);
-        form_ap_r(false);
+        const bool wide = tables(false);
+        if (wide) ap_entries(false);
+        else if (wv == 0) put_nn(mma16<NQK, true, true>(zero4, Et, L::PK, Kh, L::PK), As, true);
+        if (wv == 1 || wv == 2) r_tile(wv - 1);
         __syncthreads();
         // (I + A) U = R by forward substitution, one thread per state row
         if (tid < R2) {
@@ -349,19 +409,20 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             }
         }
         __syncthreads();
-        // S <- S diag(lambda_C) + U^T K~ (each thread rewrites only what it read)
-        {
-            float acc[2][NC];
+        // S <- S diag(lambda_C) + U^T K~: row tiles a, this wave's channel tiles
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+        for (int ct = 0; ct < CTW; ++ct) {
+            const int t = CTW * wv + ct, cc = 16 * t + l16;
+            const float lmC = Lm[(C2 - 1) * L::PK + cc];
 #pragma unroll
-                for (int y = 0; y < NC; ++y)
-                    acc[a][y] = Ss[(i0 + a) * L::PK + j0 + y] * Lm[(C2 - 1) * L::PK + j0 + y];
-            mm2n<C2, NC>(acc, [&](int a, int r) { return Us[r * L::PR + i0 + a]; }, Kt, L::PK, j0);
+            for (int a = 0; a < 2; ++a) {
+                f32x4 acc;
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+                for (int i = 0; i < 4; ++i) acc[i] = Ss[(16 * a + 4 * lg + i) * L::PK + cc] * lmC;
+                acc = mma16<1, false, false>(acc, Us + 16 * a, L::PR, Kt + 16 * t, L::PK);
 #pragma unroll
-                for (int y = 0; y < NC; ++y) Ss[(i0 + a) * L::PK + j0 + y] = acc[a][y];
+                for (int i = 0; i < 4; ++i) Ss[(16 * a + 4 * lg + i) * L::PK + cc] = acc[i];
+            }
         }
     }
 
@@ -374,7 +435,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             const int e4 = tid + it * NT2;
             const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
             gv[it] = p.dsf ? *reinterpret_cast<const f32x4*>(p.dsf + (bh * DV + row0 + i) * DK + j)
-                           : f32x4{0.f, 0.f, 0.f, 0.f};
+                           : zero4;
         }
         put_s(gv, Gs);
     }
@@ -393,200 +454,222 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             fetch_s(sv, c - 1);
         }
         __syncthreads();
-        tables(true);
-        form_ap_r(true);
-        __syncthreads();
-        // T = (I + A)^{-1}, one thread per column, the column in registers
-        if (tid < C2) {
-            const int cc = tid;
-            float tc[C2];
-#pragma unroll
-            for (int r = 0; r < C2; ++r) {
-                float v = r == cc ? 1.f : 0.f;
-#pragma unroll
-                for (int m = 0; m < r; ++m) v -= As[r * L::PC + m] * tc[m];
-                tc[r] = r < cc ? 0.f : v;
-                Ts[r * L::PC + cc] = tc[r];
-            }
+        const bool wide = tables(true);
+        // ---- A, P (waves 0, 1, or all threads entry by entry); R (waves 2, 3)
+        if (wide) {
+            ap_entries(true);
+        } else if (wv == 0) {
+            put_nn(mma16<NQK, true, true>(zero4, Et, L::PK, Kh, L::PK), As, true);
+        } else if (wv == 1) {
+            put_nn(mma16<NQK, true, true>(zero4, Qt, L::PK, Kh, L::PK), Ps, false);
         }
+        if (wv >= 2) r_tile(wv - 2);
         __syncthreads();
-        // U = T R;  dU = P^T dO + K~ G'^T
+        // ---- T = (I + A)^{-1} (wave 0, a column per lane); K~ G'^T into dU
+        //      (waves 1, 2); sum_i G' (.) S per channel (wave 3)
+        if (wv == 0) {
+            if (lane < C2) {
+                const int cc = lane;
+                float tc[C2];
 #pragma unroll
-        for (int it = 0; it < C2 * R2 / NT2; ++it) {
-            const int e = tid + it * NT2;
-            const int r = e / R2, i = e % R2;
-            float u = 0.f, du = 0.f;
-            for (int s = 0; s <= r; ++s) u += Ts[r * L::PC + s] * Rs[s * L::PR + i];
-            for (int s = r; s < C2; ++s) du += Ps[s * L::PC + r] * dOs[s * L::PR + i];
+                for (int r = 0; r < C2; ++r) {
+                    float v = r == cc ? 1.f : 0.f;
+#pragma unroll
+                    for (int m = 0; m < r; ++m) v -= As[r * L::PC + m] * tc[m];
+                    tc[r] = r < cc ? 0.f : v;
+                    Ts[r * L::PC + cc] = tc[r];
+                }
+            }
+        } else if (wv <= 2) {
+            const int t = wv - 1;
+            const f32x4 acc = mma16<NQK, true, true>(zero4, Kt, L::PK, Gs + 16 * t * L::PK, L::PK);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dUs[(4 * lg + i) * L::PR + 16 * t + l16] = acc[i];
+        } else {
+#pragma unroll
+            for (int j = 0; j < DK / 64; ++j) {
+                const int cc = lane + 64 * j;
+                float sacc = 0.f;
 #pragma unroll 8
-            for (int cc = 0; cc < DK; cc += 4) {
-                const f32x4 kt = ld4(Kt + r * L::PK + cc), gv = ld4(Gs + i * L::PK + cc);
-                du += kt[0] * gv[0] + kt[1] * gv[1] + kt[2] * gv[2] + kt[3] * gv[3];
-            }
-            Us[r * L::PR + i] = u;
-            dUs[r * L::PR + i] = du;
-        }
-        __syncthreads();
-        // dR = T^T dU (dw = dR (.) v, dv = dR (.) w to HBM);  dP = dO U^T (s <= r)
-#pragma unroll
-        for (int it = 0; it < C2 * R2 / NT2; ++it) {
-            const int e = tid + it * NT2;
-            const int r = e / R2, i = e % R2;
-            float v = 0.f;
-            for (int s = r; s < C2; ++s) v += Ts[s * L::PC + r] * dUs[s * L::PR + i];
-            dRs[r * L::PR + i] = v;
-            if (r < n) {
-                const int64_t off = tok(t0 + r) * DV + row0 + i;
-                p.dw[off] = v * Vsm[r * L::PR + i];
-                p.dv[off] = v * Wsm[r * L::PR + i];
+                for (int i = 0; i < R2; ++i) sacc += Gs[i * L::PK + cc] * Ss[i * L::PK + cc];
+                GSc[cc] = sacc;
             }
         }
-        {
-            const int r = tid >> 4, s = tid & 15;
-            float v = 0.f;
-            if (s <= r) {
-#pragma unroll 8
-                for (int i = 0; i < R2; ++i) v += dOs[r * L::PR + i] * Us[s * L::PR + i];
+        __syncthreads();
+        // ---- U = T R (waves 0, 1);  dU = K~ G'^T + P^T dO (waves 2, 3)
+        if (wv < 2) {
+            const int t = wv;
+            const f32x4 acc = mma16<1, true, false>(zero4, Ts, L::PC, Rs + 16 * t, L::PR);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Us[(4 * lg + i) * L::PR + 16 * t + l16] = acc[i];
+        } else {
+            const int t = wv - 2;
+            f32x4 acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = dUs[(4 * lg + i) * L::PR + 16 * t + l16];
+            acc = mma16<1, false, false>(acc, Ps, L::PC, dOs + 16 * t, L::PR);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dUs[(4 * lg + i) * L::PR + 16 * t + l16] = acc[i];
+        }
+        __syncthreads();
+        // ---- dR = T^T dU (waves 0, 1; dw, dv to HBM);  dP = dO U^T (wave 2);
+        //      dT = dU R^T (wave 3)
+        if (wv < 2) {
+            const int t = wv;
+            const f32x4 acc = mma16<1, false, false>(zero4, Ts, L::PC, dUs + 16 * t, L::PR);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i, o = r * L::PR + 16 * t + l16;
+                dRs[o] = acc[i];
+                if (r < n) {
+                    const int64_t off = tok(t0 + r) * DV + row0 + 16 * t + l16;
+                    p.dw[off] = acc[i] * Vsm[o];
+                    p.dv[off] = acc[i] * Wsm[o];
+                }
             }
-            dPs[r * L::PC + s] = v;
+        } else if (wv == 2) {
+            put_nn(mma16<2, true, true>(zero4, dOs, L::PR, Us, L::PR), dPs, false);
+        } else {
+            put_nn(mma16<2, true, true>(zero4, dUs, L::PR, Rs, L::PR), dTs, true);
         }
         __syncthreads();
-        {   // dT = dU R^T, strict lower
-            const int r = tid >> 4, s = tid & 15;
-            float v = 0.f;
-            if (s < r) {
-#pragma unroll 8
-                for (int i = 0; i < R2; ++i) v += dUs[r * L::PR + i] * Rs[s * L::PR + i];
+        // ---- wave 0 first: Y = dT T^T, then dA = -T^T Y (strict) over dT
+        if (wv == 0) {
+            const f32x4 y = mma16<1, true, true>(zero4, dTs, L::PC, Ts, L::PC);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Ys[(4 * lg + i) * L::PC + l16] = y[i];
+            wave_sync();
+            put_nn(mma16<1, false, false, true>(zero4, Ts, L::PC, Ys, L::PC), dTs, true);
+        }
+        // ---- this wave's channel tiles: dE~ = -dR S, dQ~ = dO S, dK~ = U G';
+        //      the dP parts of dQ_P and dK_AP
+        f32x4 dEt[CTW], dQt[CTW], dKt[CTW], dEa[CTW], dQa[CTW], dKa[CTW];
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+            const int t = CTW * wv + ct;
+            dEt[ct] = mma16<2, true, false, true>(zero4, dRs, L::PR, Ss + 16 * t, L::PK);
+            dQt[ct] = mma16<2, true, false>(zero4, dOs, L::PR, Ss + 16 * t, L::PK);
+            dKt[ct] = mma16<2, true, false>(zero4, Us, L::PR, Gs + 16 * t, L::PK);
+            if (!wide) {
+                dQa[ct] = mma16<1, true, false>(zero4, dPs, L::PC, Kh + 16 * t, L::PK);
+                dKa[ct] = mma16<1, false, false>(zero4, dPs, L::PC, Qt + 16 * t, L::PK);
             }
-            dTs[r * L::PC + s] = v;
         }
-        __syncthreads();
-        {   // Y = dT T^T into dA's tile
-            const int r = tid >> 4, s = tid & 15;
-            float v = 0.f;
-            for (int bb = 0; bb <= s && bb < r; ++bb) v += dTs[r * L::PC + bb] * Ts[s * L::PC + bb];
-            dAs[r * L::PC + s] = v;
-        }
-        __syncthreads();
-        {   // dA = -T^T Y, strict lower, into dT's tile
-            const int r = tid >> 4, s = tid & 15;
-            float v = 0.f;
-            if (s < r)
-                for (int a = r; a < C2; ++a) v -= Ts[a * L::PC + r] * dAs[a * L::PC + s];
-            dTs[r * L::PC + s] = v;
-        }
-        __syncthreads();
-        const float* dA = dTs;
-        // ---- per (token tr, channels j0 .. j0 + NC - 1)
-        {
-            const int r = tr;
-            float dEt[NC] = {}, dQt[NC] = {}, dKt[NC] = {};
-            mm1n<R2, NC>(dEt, [&](int i) { return -dRs[r * L::PR + i]; }, Ss, L::PK, j0);
-            mm1n<R2, NC>(dQt, [&](int i) { return dOs[r * L::PR + i]; }, Ss, L::PK, j0);
-            mm1n<R2, NC>(dKt, [&](int i) { return Us[r * L::PR + i]; }, Gs, L::PK, j0);
-            float gr[NC];
+        __syncthreads();   // dA
+        const float* dAs = dTs;
 #pragma unroll
-            for (int y0 = 0; y0 < NC; y0 += 4) {
-                const f32x4 g = ld4(Gc + r * L::PK + j0 + y0);
+        for (int ct = 0; ct < CTW; ++ct) {
+            const int t = CTW * wv + ct, cc = 16 * t + l16;
+            if (!wide) {
+                dEa[ct] = mma16<1, true, false>(zero4, dAs, L::PC, Kh + 16 * t, L::PK);
+                dKa[ct] = mma16<1, false, false>(dKa[ct], dAs, L::PC, Et + 16 * t, L::PK);
 #pragma unroll
-                for (int z = 0; z < 4; ++z) gr[y0 + z] = g[z];
-            }
-            float dEa[NC] = {}, dQa[NC] = {}, dKa[NC] = {};
-            for (int s = 0; s <= r; ++s) {
-                const float da = dA[r * L::PC + s], dp = dPs[r * L::PC + s];
+                for (int i = 0; i < 4; ++i) {
+                    const int at = (4 * lg + i) * L::PK + cc;
+                    const float lm = Lm[at];
+                    dEa[ct][i] *= lm;
+                    dQa[ct][i] *= lm;
+                    dKa[ct][i] *= expf(-Gc[at]);
+                }
+            } else {
+                // entry by entry: token r = 4 lg + i, channel cc
 #pragma unroll
-                for (int y0 = 0; y0 < NC; y0 += 4) {
-                    const f32x4 ks = ld4(Ks + s * L::PK + j0 + y0), gs = ld4(Gc + s * L::PK + j0 + y0);
-#pragma unroll
-                    for (int z = 0; z < 4; ++z) {
-                        const float kd = ks[z] * __expf(gr[y0 + z] - gs[z]);
-                        dEa[y0 + z] += da * kd;
-                        dQa[y0 + z] += dp * kd;
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * lg + i;
+                    const float gr = Gc[r * L::PK + cc];
+                    float ea = 0.f, qa = 0.f, ka = 0.f;
+                    for (int s = 0; s <= r; ++s) {
+                        const float kd = Ks[s * L::PK + cc] * __expf(gr - Gc[s * L::PK + cc]);
+                        ea += dAs[r * L::PC + s] * kd;
+                        qa += dPs[r * L::PC + s] * kd;
                     }
+                    for (int r2 = r; r2 < C2; ++r2)
+                        ka += (dAs[r2 * L::PC + r] * Es[r2 * L::PK + cc] +
+                               dPs[r2 * L::PC + r] * Qs[r2 * L::PK + cc]) *
+                              __expf(Gc[r2 * L::PK + cc] - gr);
+                    dEa[ct][i] = ea;
+                    dQa[ct][i] = qa;
+                    dKa[ct][i] = ka;
                 }
             }
-            for (int r2 = r; r2 < C2; ++r2) {
-                const float da = dA[r2 * L::PC + r], dp = dPs[r2 * L::PC + r];
+            // ---- combine: dq, dk, db and d log alpha partials to HBM.
+            // d log alpha_t collects, inside the chunk, the suffix sums
+            // (t' >= t) of dE~ (.) E~ + dQ~ (.) Q~, the prefix sums (t' < t)
+            // of dK~ (.) K~ (K~ depends on alpha_t for tokens before t), the
+            // lambda_C term, and the pair terms pr = E (.) dE_A + Q (.) dQ_P
+            // - K (.) dK_AP, which sum to zero over the chunk: their suffix
+            // sum equals minus their prefix sum, and the half of the chunk
+            // nearer each end takes the form with fewer terms (the two share
+            // every pair on the far side, which would cancel in fp32).
+            const float gC = Gc[(C2 - 1) * L::PK + cc], lmC = Lm[(C2 - 1) * L::PK + cc];
+            float oq[4], ok[4], ob[4], pr[4], tl[4], kk4[4];
 #pragma unroll
-                for (int y0 = 0; y0 < NC; y0 += 4) {
-                    const f32x4 g2 = ld4(Gc + r2 * L::PK + j0 + y0);
-                    const f32x4 e2 = ld4(Es + r2 * L::PK + j0 + y0), q2 = ld4(Qs + r2 * L::PK + j0 + y0);
+            for (int i = 0; i < 4; ++i) {
+                const int at = (4 * lg + i) * L::PK + cc;
+                const float lm = Lm[at], kk = Ks[at], g = Gc[at];
+                const float dE = dEa[ct][i] + dEt[ct][i] * lm;
+                oq[i] = dQa[ct][i] + dQt[ct][i] * lm;
+                ok[i] = dKa[ct][i] + dKt[ct][i] * expf(gC - g) + dE * Bs[at];
+                ob[i] = dE * kk;
+                kk4[i] = dKt[ct][i] * Kt[at];
+                tl[i] = dEt[ct][i] * Et[at] + dQt[ct][i] * Qt[at];
+                pr[i] = Es[at] * dEa[ct][i] + Qs[at] * dQa[ct][i] - kk * dKa[ct][i];
+            }
+            // totals of the four token groups of this channel (lanes l16 + 16 g)
+            const float sp = pr[0] + pr[1] + pr[2] + pr[3];
+            const float st = tl[0] + tl[1] + tl[2] + tl[3];
+            const float sk = kk4[0] + kk4[1] + kk4[2] + kk4[3];
+            float ap = 0.f, bp = 0.f, at_ = 0.f, bk = 0.f;
 #pragma unroll
-                    for (int z = 0; z < 4; ++z)
-                        dKa[y0 + z] += (da * e2[z] + dp * q2[z]) * __expf(g2[z] - gr[y0 + z]);
+            for (int g2 = 0; g2 < 4; ++g2) {
+                const float vp = __shfl(sp, l16 + 16 * g2, 64);
+                const float vt = __shfl(st, l16 + 16 * g2, 64);
+                const float vk = __shfl(sk, l16 + 16 * g2, 64);
+                if (g2 > lg) { ap += vp; at_ += vt; }
+                if (g2 < lg) { bp += vp; bk += vk; }
+            }
+            const float lam = GSc[cc] * lmC;
+            float dl[4];
+            {
+                float sufp = ap, suft = at_, prep = bp, prek = bk;
+                float pp[4], pk4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {   // prefixes, tokens before 4 lg + i
+                    pp[i] = prep;
+                    pk4[i] = prek;
+                    prep += pr[i];
+                    prek += kk4[i];
+                }
+#pragma unroll
+                for (int i = 3; i >= 0; --i) {  // suffixes, tokens from 4 lg + i
+                    sufp += pr[i];
+                    suft += tl[i];
+                    dl[i] = suft + pk4[i] + lam + (lg >= 2 ? sufp : -pp[i]);
                 }
             }
-            float oq[NC], ok[NC], ob[NC];
 #pragma unroll
-            for (int y0 = 0; y0 < NC; y0 += 4) {
-                const int at = r * L::PK + j0 + y0;
-                const f32x4 lm = ld4(Lm + at), ks = ld4(Ks + at), bs = ld4(Bs + at);
-                const f32x4 es = ld4(Es + at), qs = ld4(Qs + at), kt = ld4(Kt + at);
-                const f32x4 et = ld4(Et + at), qt = ld4(Qt + at);
-                const f32x4 gC = ld4(Gc + (C2 - 1) * L::PK + j0 + y0);
-                f32x4 scr, dg;
-#pragma unroll
-                for (int z = 0; z < 4; ++z) {
-                    const int y = y0 + z;
-                    const float dE = dEa[y] + dEt[y] * lm[z];
-                    oq[y] = dQa[y] + dQt[y] * lm[z];
-                    const float kdec = __expf(gC[z] - gr[y]);
-                    ok[y] = dKa[y] + dKt[y] * kdec + dE * bs[z];
-                    ob[y] = dE * ks[z];
-                    const float ktk = dKt[y] * kt[z];
-                    scr[z] = ktk;
-                    dg[z] = es[z] * dEa[y] + qs[z] * dQa[y] - ks[z] * dKa[y] + dEt[y] * et[z] +
-                            dQt[y] * qt[z] - ktk;
-                }
-                *reinterpret_cast<f32x4*>(Scr + at) = scr;
-                *reinterpret_cast<f32x4*>(Dg + at) = dg;
-            }
-            if (r < n) {
-                const int64_t o = poff + tok(t0 + r) * DK + j0;
-#pragma unroll
-                for (int hh = 0; hh < NC / 4; ++hh) {
-                    *reinterpret_cast<f32x4*>(p.pq + o + 4 * hh) =
-                        f32x4{oq[4 * hh], oq[4 * hh + 1], oq[4 * hh + 2], oq[4 * hh + 3]};
-                    *reinterpret_cast<f32x4*>(p.pk + o + 4 * hh) =
-                        f32x4{ok[4 * hh], ok[4 * hh + 1], ok[4 * hh + 2], ok[4 * hh + 3]};
-                    *reinterpret_cast<f32x4*>(p.pb + o + 4 * hh) =
-                        f32x4{ob[4 * hh], ob[4 * hh + 1], ob[4 * hh + 2], ob[4 * hh + 3]};
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i;
+                if (r < n) {
+                    const int64_t o = poff + tok(t0 + r) * DK + cc;
+                    p.pq[o] = oq[i];
+                    p.pk[o] = ok[i];
+                    p.pb[o] = ob[i];
+                    p.pg[o] = dl[i];
                 }
             }
-        }
-        __syncthreads();
-        // ---- dG: the last live token takes sum_r dK~ (.) K~ and (sum_i G' (.) S) (.) lambda_C
-        //      (padding tokens have log alpha = 0, so G_C is the last live token's G)
-        if (tid < DK) {
-            const int cc = tid;
-            float cs = 0.f, gs2 = 0.f;
+            // ---- G' <- G' diag(lambda_C) + dO^T Q~ - dR^T E~ on this wave's
+            //      channels (only this wave reads them in this chunk)
 #pragma unroll
-            for (int r = 0; r < C2; ++r) cs += Scr[r * L::PK + cc];
-#pragma unroll 8
-            for (int i = 0; i < R2; ++i) gs2 += Gs[i * L::PK + cc] * Ss[i * L::PK + cc];
-            Dg[(n - 1) * L::PK + cc] += cs + gs2 * Lm[(C2 - 1) * L::PK + cc];
-        }
-        __syncthreads();
-        if (tr < n) {
-            const int64_t o = poff + tok(t0 + tr) * DK + j0;
+            for (int a = 0; a < 2; ++a) {
+                f32x4 acc;
 #pragma unroll
-            for (int y0 = 0; y0 < NC; y0 += 4)
-                *reinterpret_cast<f32x4*>(p.pg + o + y0) = ld4(Dg + tr * L::PK + j0 + y0);
-        }
-        // ---- G' <- G' diag(lambda_C) + dO^T Q~ - dR^T E~ (each thread its own entries)
-        {
-            float acc[2][NC];
+                for (int i = 0; i < 4; ++i) acc[i] = Gs[(16 * a + 4 * lg + i) * L::PK + cc] * lmC;
+                acc = mma16<1, false, false>(acc, dOs + 16 * a, L::PR, Qt + 16 * t, L::PK);
+                acc = mma16<1, false, false, true>(acc, dRs + 16 * a, L::PR, Et + 16 * t, L::PK);
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int y = 0; y < NC; ++y)
-                    acc[a][y] = Gs[(i0 + a) * L::PK + j0 + y] * Lm[(C2 - 1) * L::PK + j0 + y];
-            mm2n<C2, NC>(acc, [&](int a, int r) { return dOs[r * L::PR + i0 + a]; }, Qt, L::PK, j0);
-            mm2n<C2, NC>(acc, [&](int a, int r) { return -dRs[r * L::PR + i0 + a]; }, Et, L::PK, j0);
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int y = 0; y < NC; ++y) Gs[(i0 + a) * L::PK + j0 + y] = acc[a][y];
+                for (int i = 0; i < 4; ++i) Gs[(16 * a + 4 * lg + i) * L::PK + cc] = acc[i];
+            }
         }
     }
     __syncthreads();
@@ -601,51 +684,30 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
     }
 }
 
-// dq, dk, derase: the sum of the row blocks' partials
-template <int NRB>
-__global__ __launch_bounds__(256) void bwd2_reduce_qkb(int64_t n, const float* __restrict__ pq,
-                                                       const float* __restrict__ pk,
-                                                       const float* __restrict__ pb,
-                                                       float* __restrict__ dq, float* __restrict__ dk,
-                                                       float* __restrict__ db) {
+// dq, dk, derase and dalpha: the sums of the row blocks' partials, dalpha =
+// d log alpha / alpha with alpha clamped to FLT_MIN as in the forward's log
+template <int NRB, typename TIn>
+__global__ __launch_bounds__(256) void bwd2_reduce(int64_t n, const float* __restrict__ pq,
+                                                   const float* __restrict__ pk,
+                                                   const float* __restrict__ pb,
+                                                   const float* __restrict__ pg, const void* alpha,
+                                                   float* __restrict__ dq, float* __restrict__ dk,
+                                                   float* __restrict__ db,
+                                                   float* __restrict__ da) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    float a = 0.f, b = 0.f, c = 0.f;
+    float a = 0.f, b = 0.f, c = 0.f, d = 0.f;
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
         a += pq[r * n + i];
         b += pk[r * n + i];
         c += pb[r * n + i];
+        d += pg[r * n + i];
     }
     dq[i] = a;
     dk[i] = b;
     db[i] = c;
-}
-
-// dalpha: one thread per (b, h, chunk, channel); dlog alpha is the reverse
-// cumulative sum of dG inside the chunk, dalpha = dlog alpha / alpha (alpha
-// clamped to FLT_MIN as in the forward's logarithm)
-template <int NRB, typename TIn>
-__global__ __launch_bounds__(256) void bwd2_reduce_alpha(int64_t B, int64_t T, int64_t H, int DK,
-                                                         int64_t BTH, const float* __restrict__ pg,
-                                                         const void* alpha, float* __restrict__ da) {
-    const int64_t nch = (T + C2 - 1) / C2;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= B * H * nch * DK) return;
-    const int cc = (int)(idx % DK);
-    const int64_t rest = idx / DK;
-    const int64_t c = rest % nch, bh = rest / nch;
-    const int64_t h = bh % H, b = bh / H;
-    const int64_t t0 = c * C2, t1 = min(t0 + C2, T);
-    float acc = 0.f;
-    for (int64_t t = t1 - 1; t >= t0; --t) {
-        const int64_t i = ((b * T + t) * H + h) * DK + cc;
-        float g = 0.f;
-#pragma unroll
-        for (int r = 0; r < NRB; ++r) g += pg[r * BTH * DK + i];
-        acc += g;
-        da[i] = acc / fmaxf(ldf<TIn>(alpha, i), 1.17549435e-38f);
-    }
+    da[i] = d / fmaxf(ldf<TIn>(alpha, i), 1.17549435e-38f);
 }
 
 template <int DK, int DV, typename TIn, typename TD>
@@ -675,7 +737,7 @@ hipError_t launch_bwd2_t(const Bwd2Args& a) {
     p.pk = p.pq + NRB * BTH * DK;
     p.pb = p.pk + NRB * BTH * DK;
     p.pg = p.pb + NRB * BTH * DK;
-    const size_t lds = sizeof(float) * BL2<DK>::TOTAL;
+    const size_t lds = sizeof(float) * BL3<DK>::TOTAL;
     auto fn = chunk2_bwd_kernel<DK, DV, TIn, TD>;
     hipError_t e = hipFuncSetAttribute((const void*)fn,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -684,13 +746,9 @@ hipError_t launch_bwd2_t(const Bwd2Args& a) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nqk = BTH * DK;
-    hipLaunchKernelGGL((bwd2_reduce_qkb<NRB>), dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0,
-                       a.stream, nqk, p.pq, p.pk, p.pb, a.dq, a.dk, a.derase);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t na = BH * nch * DK;
-    hipLaunchKernelGGL((bwd2_reduce_alpha<NRB, TIn>), dim3((unsigned)((na + 255) / 256)), dim3(256),
-                       0, a.stream, a.B, a.T, a.H, (int)DK, BTH, p.pg, a.alpha, a.dalpha);
+    hipLaunchKernelGGL((bwd2_reduce<NRB, TIn>), dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0,
+                       a.stream, nqk, p.pq, p.pk, p.pb, p.pg, a.alpha, a.dq, a.dk, a.derase,
+                       a.dalpha);
     return hipGetLastError();
 }
 

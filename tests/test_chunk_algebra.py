@@ -333,6 +333,45 @@ def gdn2_chunk_bwd(q, k, v, a, e, w, s0, dO, dSf, C):
     return tuple(out) + (Gr,)
 
 
+def gdn2_dlog_alpha_split(Gr_S, Kt_, dKt, Et_, dEt, Qt_, dQt, E, dEa, Q, dQa, K, dKa, lC, n):
+    """d log alpha of one chunk without the cancelling cumulative sum:
+    suffix sums of dE~ (.) E~ + dQ~ (.) Q~, prefix sums of dK~ (.) K~, the
+    lambda_C term on every token, and the pair terms (which sum to zero over
+    the chunk) as a suffix sum for the later half of the chunk and minus a
+    prefix sum for the earlier half."""
+    pr = E * dEa + Q * dQa - K * dKa
+    tl = dEt * Et_ + dQt * Qt_
+    kk = dKt * Kt_
+    out = np.zeros_like(pr)
+    for t in range(n):
+        pair = pr[t:].sum(0) if t >= n // 2 else -pr[:t].sum(0)
+        out[t] = tl[t:].sum(0) + kk[:t].sum(0) + Gr_S * lC + pair
+    return out
+
+
+def test_gdn2_dlog_alpha_split_form():
+    """The split form equals the reverse cumulative sum of dG (the chunk's
+    pair terms cancel exactly) on random chunk quantities."""
+    g = np.random.Generator(np.random.PCG64(46))
+    n, d = 16, 7
+    E, K, Q = (g.standard_normal((n, d)) for _ in range(3))
+    Gm = np.cumsum(-np.abs(g.standard_normal((n, d))), axis=0)
+    Gam = np.exp(np.minimum(Gm[:, None, :] - Gm[None, :, :], 0.0))
+    dA = np.tril(g.standard_normal((n, n)), -1)
+    dP = np.tril(g.standard_normal((n, n)))
+    dEa = np.einsum('rs,sc,rsc->rc', dA, K, Gam)
+    dQa = np.einsum('rs,sc,rsc->rc', dP, K, Gam)
+    dKa = np.einsum('rs,rc,rsc->sc', dA, E, Gam) + np.einsum('rs,rc,rsc->sc', dP, Q, Gam)
+    Et_, Qt_, Kt_ = E * np.exp(Gm), Q * np.exp(Gm), K * np.exp(Gm[-1] - Gm)
+    dEt, dQt, dKt = (g.standard_normal((n, d)) for _ in range(3))
+    GS, lC = g.standard_normal(d), np.exp(Gm[-1])
+    dG = E * dEa + Q * dQa - K * dKa + dEt * Et_ + dQt * Qt_ - dKt * Kt_
+    dG[-1] += np.sum(dKt * Kt_, axis=0) + GS * lC
+    want = np.cumsum(dG[::-1], axis=0)[::-1]
+    got = gdn2_dlog_alpha_split(GS, Kt_, dKt, Et_, dEt, Qt_, dQt, E, dEa, Q, dQa, K, dKa, lC, n)
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-10 * np.abs(want).max())
+
+
 @pytest.mark.parametrize("C", [1, 4, 16, 32])
 def test_gdn2_chunk_bwd_matches_oracle(C):
     q, k, v, a, e, w, S0 = rand_gdn2(44, B=1, T=45, H=2, Dk=6, Dv=5)
