@@ -60,7 +60,9 @@ namespace {
 constexpr int C2 = 16;         // tokens per chunk
 constexpr int R2 = 32;         // state rows per workgroup
 constexpr int NT2 = 256;       // threads per workgroup
-constexpr float WIDE = -60.f;  // G_C below this: entry-by-entry decays
+// Decays are kept in log2 units (G2 = G / ln 2) so that every exponential is
+// one v_exp_f32; a chunk is wide when some channel's G_C < -60.
+constexpr float WIDE2 = -60.f * 1.44269504f;
 
 struct Bwd2Params {
     int64_t T, H, BTH;
@@ -84,7 +86,7 @@ struct BL3 {
     static constexpr int Q = K + NK;
     static constexpr int E = Q + NK;             // b (.) k
     static constexpr int BB = E + NK;            // b
-    static constexpr int GC = BB + NK;           // cumulative log alpha
+    static constexpr int GC = BB + NK;           // cumulative log2 alpha
     static constexpr int LM = GC + NK;           // lambda = e^G
     static constexpr int KT = LM + NK;           // K~
     static constexpr int QT = KT + NK;           // Q~
@@ -143,6 +145,22 @@ __device__ __forceinline__ f32x4 mma16(f32x4 acc, const float* A, int pa, const 
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc, 0, 0, 0);
     }
     return acc;
+}
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// log2 of a decay gate, clamped as safe_log: 0 (or a denormal) maps to -126
+__device__ __forceinline__ float safe_log2(float a) {
+    return fmaxf(__builtin_amdgcn_logf(fmaxf(a, 1.17549435e-38f)), -126.f);
+}
+
+// sum over the 4 lanes of each aligned quad (DPP quad_perm xor 1, then xor 2)
+__device__ __forceinline__ float qsum(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                0xB1, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                0x4E, 0xF, 0xF, false));
+    return x;
 }
 
 __device__ __forceinline__ void wave_sync() {
@@ -240,7 +258,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
                 kv[e] = live ? packed<TIn>::at(x.k, y) : 0.f;
                 bv[e] = live ? packed<TIn>::at(x.b, y) : 0.f;
                 ev[e] = bv[e] * kv[e];
-                gv[e] = live ? safe_log(packed<TIn>::at(x.a, y)) : 0.f;
+                gv[e] = live ? safe_log2(packed<TIn>::at(x.a, y)) : 0.f;
                 qv[e] = (live && bwd) ? packed<TIn>::at(x.q, y) : 0.f;
             }
             *reinterpret_cast<f32x4*>(Ks + at + y0) = kv;
@@ -285,7 +303,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             for (int r = 1; r < C2; ++r) g[r] += g[r - 1];
 #pragma unroll
             for (int r = 0; r < C2; ++r) Gc[r * L::PK + tid] = g[r];
-            wide_here = g[C2 - 1] < WIDE;
+            wide_here = g[C2 - 1] < WIDE2;
         }
         const bool wide = __syncthreads_or(wide_here);
         const int at = tr * L::PK + j0;
@@ -296,10 +314,10 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             f32x4 lm, kt, et, kh;
 #pragma unroll
             for (int z = 0; z < 4; ++z) {
-                lm[z] = expf(g[z]);
-                kt[z] = k[z] * expf(gC[z] - g[z]);
+                lm[z] = ex2(g[z]);
+                kt[z] = k[z] * ex2(gC[z] - g[z]);
                 et[z] = e[z] * lm[z];
-                kh[z] = wide ? 0.f : k[z] * expf(-g[z]);
+                kh[z] = wide ? 0.f : k[z] * ex2(-g[z]);
             }
             *reinterpret_cast<f32x4*>(Lm + at + y0) = lm;
             *reinterpret_cast<f32x4*>(Kt + at + y0) = kt;
@@ -330,7 +348,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
                 if (bwd) qr = ld4(Qs + r * L::PK + c);
 #pragma unroll
                 for (int z = 0; z < 4; ++z) {
-                    const float kd = ks[z] * __expf(gr[z] - gs[z]);
+                    const float kd = ks[z] * ex2(gr[z] - gs[z]);
                     av += er[z] * kd;
                     pv += qr[z] * kd;
                 }
@@ -346,6 +364,24 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * lg + i;
             D[r * L::PC + l16] = (strict ? l16 < r : l16 <= r) ? acc[i] : 0.f;
+        }
+    };
+    // T = (I + A)^{-1} by wave 0: lane 4 c + q owns column c and the rows
+    // m = q (mod 4); row r of the column is delta_rc - sum_{m < r} A_rm T_mc
+    // (A's upper part is stored as zeros), the four partial sums joined by a
+    // quad reduction
+    auto tsolve = [&]() {
+        const int c = lane >> 2, q = lane & 3;
+        float tq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < C2; ++r) {
+            float part = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) part += As[r * L::PC + 4 * j + q] * tq[j];
+            part = qsum(part);
+            const float t = r < c ? 0.f : (r == c ? 1.f : 0.f) - part;
+            if ((r & 3) == q) tq[r >> 2] = t;
+            if (q == 0) Ts[r * L::PC + c] = t;
         }
     };
     // R tile t (rows 16 t ..): R = w (.) v - E~ S^T
@@ -391,22 +427,26 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         if (c + 1 < nch) fetch(x, c + 1, false);
         __syncthreads();
         const bool wide = tables(false);
-        if (wide) ap_entries(false);
-        else if (wv == 0) put_nn(mma16<NQK, true, true>(zero4, Et, L::PK, Kh, L::PK), As, true);
-        if (wv == 1 || wv == 2) r_tile(wv - 1);
-        __syncthreads();
-        // (I + A) U = R by forward substitution, one thread per state row
-        if (tid < R2) {
-            const int i = tid;
-            float u[C2];
-#pragma unroll
-            for (int r = 0; r < C2; ++r) {
-                float v = Rs[r * L::PR + i];
-#pragma unroll
-                for (int s = 0; s < r; ++s) v -= As[r * L::PC + s] * u[s];
-                u[r] = v;
-                Us[r * L::PR + i] = v;
+        if (wide) {
+            ap_entries(false);
+            __syncthreads();
+        }
+        if (wv == 0) {
+            if (!wide) {
+                put_nn(mma16<NQK, true, true>(zero4, Et, L::PK, Kh, L::PK), As, true);
+                wave_sync();
             }
+            tsolve();
+        } else if (wv <= 2) {
+            r_tile(wv - 1);
+        }
+        __syncthreads();
+        // U = T R (waves 0, 1)
+        if (wv < 2) {
+            const int t = wv;
+            const f32x4 acc = mma16<1, true, false>(zero4, Ts, L::PC, Rs + 16 * t, L::PR);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Us[(4 * lg + i) * L::PR + 16 * t + l16] = acc[i];
         }
         __syncthreads();
         // S <- S diag(lambda_C) + U^T K~: row tiles a, this wave's channel tiles
@@ -455,37 +495,32 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         }
         __syncthreads();
         const bool wide = tables(true);
-        // ---- A, P (waves 0, 1, or all threads entry by entry); R (waves 2, 3)
+        // ---- wave 0: A, then T = (I + A)^{-1};  wave 1: P and K~ G'^T rows
+        //      0..15 (into dU);  wave 2: R rows 0..15 and K~ G'^T rows 16..31;
+        //      wave 3: R rows 16..31 and sum_i G' (.) S per channel
+        //      (wide chunks: A and P entry by entry by all threads first)
         if (wide) {
             ap_entries(true);
-        } else if (wv == 0) {
-            put_nn(mma16<NQK, true, true>(zero4, Et, L::PK, Kh, L::PK), As, true);
-        } else if (wv == 1) {
-            put_nn(mma16<NQK, true, true>(zero4, Qt, L::PK, Kh, L::PK), Ps, false);
+            __syncthreads();
         }
-        if (wv >= 2) r_tile(wv - 2);
-        __syncthreads();
-        // ---- T = (I + A)^{-1} (wave 0, a column per lane); K~ G'^T into dU
-        //      (waves 1, 2); sum_i G' (.) S per channel (wave 3)
         if (wv == 0) {
-            if (lane < C2) {
-                const int cc = lane;
-                float tc[C2];
-#pragma unroll
-                for (int r = 0; r < C2; ++r) {
-                    float v = r == cc ? 1.f : 0.f;
-#pragma unroll
-                    for (int m = 0; m < r; ++m) v -= As[r * L::PC + m] * tc[m];
-                    tc[r] = r < cc ? 0.f : v;
-                    Ts[r * L::PC + cc] = tc[r];
-                }
+            if (!wide) {
+                put_nn(mma16<NQK, true, true>(zero4, Et, L::PK, Kh, L::PK), As, true);
+                wave_sync();
             }
+            tsolve();
         } else if (wv <= 2) {
+            if (wv == 1) {
+                if (!wide) put_nn(mma16<NQK, true, true>(zero4, Qt, L::PK, Kh, L::PK), Ps, false);
+            } else {
+                r_tile(0);
+            }
             const int t = wv - 1;
             const f32x4 acc = mma16<NQK, true, true>(zero4, Kt, L::PK, Gs + 16 * t * L::PK, L::PK);
 #pragma unroll
             for (int i = 0; i < 4; ++i) dUs[(4 * lg + i) * L::PR + 16 * t + l16] = acc[i];
         } else {
+            r_tile(1);
 #pragma unroll
             for (int j = 0; j < DK / 64; ++j) {
                 const int cc = lane + 64 * j;
@@ -569,7 +604,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
                     const float lm = Lm[at];
                     dEa[ct][i] *= lm;
                     dQa[ct][i] *= lm;
-                    dKa[ct][i] *= expf(-Gc[at]);
+                    dKa[ct][i] *= ex2(-Gc[at]);
                 }
             } else {
                 // entry by entry: token r = 4 lg + i, channel cc
@@ -579,14 +614,14 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
                     const float gr = Gc[r * L::PK + cc];
                     float ea = 0.f, qa = 0.f, ka = 0.f;
                     for (int s = 0; s <= r; ++s) {
-                        const float kd = Ks[s * L::PK + cc] * __expf(gr - Gc[s * L::PK + cc]);
+                        const float kd = Ks[s * L::PK + cc] * ex2(gr - Gc[s * L::PK + cc]);
                         ea += dAs[r * L::PC + s] * kd;
                         qa += dPs[r * L::PC + s] * kd;
                     }
                     for (int r2 = r; r2 < C2; ++r2)
                         ka += (dAs[r2 * L::PC + r] * Es[r2 * L::PK + cc] +
                                dPs[r2 * L::PC + r] * Qs[r2 * L::PK + cc]) *
-                              __expf(Gc[r2 * L::PK + cc] - gr);
+                              ex2(Gc[r2 * L::PK + cc] - gr);
                     dEa[ct][i] = ea;
                     dQa[ct][i] = qa;
                     dKa[ct][i] = ka;
@@ -609,7 +644,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
                 const float lm = Lm[at], kk = Ks[at], g = Gc[at];
                 const float dE = dEa[ct][i] + dEt[ct][i] * lm;
                 oq[i] = dQa[ct][i] + dQt[ct][i] * lm;
-                ok[i] = dKa[ct][i] + dKt[ct][i] * expf(gC - g) + dE * Bs[at];
+                ok[i] = dKa[ct][i] + dKt[ct][i] * ex2(gC - g) + dE * Bs[at];
                 ob[i] = dE * kk;
                 kk4[i] = dKt[ct][i] * Kt[at];
                 tl[i] = dEt[ct][i] * Et[at] + dQt[ct][i] * Qt[at];
