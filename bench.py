@@ -352,11 +352,9 @@ def bench_gate(gdr, torch, warmup, steps):
 
 def bench_bwd(gdr, torch, warmup, steps):
     """gdr_chunk_bwd on B8 H16 T4096 d128 (bf16 q/k/v and dL/do, dL/dS_T
-    given, zero S_0).  Algorithmic flops per token-head, chunk C = 32:
-    2 x (10 dk dv + 7 C dk + 5.5 C dv) -- ten state-sized products (the
-    forward's K S^T and state update, Q S^T, K S^T, K G^T, dO S, dR S, U G,
-    the two terms of the G update), the key-side Gram and P / A terms, and
-    the n x n-by-rows products."""
+    given, zero S_0).  It runs the GDN-2 backward with broadcast gates, so
+    the flops are counted as for bench_bwd2: per token-head, chunk C = 16,
+    2 x (9 dk dv + 3 C dk + 3 C dv)."""
     from gdr_gen import make_gdn
     inp = make_gdn(B=8, T=4096, H=16, Dk=128, Dv=128, dtype="bf16", seed=1001)
     dev = torch.device("cuda:0")
@@ -370,8 +368,8 @@ def bench_bwd(gdr, torch, warmup, steps):
     mean, mn, med, wall = time_launches(
         lambda: gdr.gdr_chunk_bwd(q, k, v, a, b, None, do, dsf, workspace=ws), warmup, steps)
     th = 8 * 4096 * 16
-    C, d = 32, 128
-    flops = th * 2 * (10 * d * d + 7 * C * d + 5.5 * C * d)
+    C, d = 16, 128
+    flops = th * 2 * (9 * d * d + 3 * C * d + 3 * C * d)
     return dict(mean=mean, min=mn, flops=flops, tokens=8 * 4096, ws=ws.numel())
 
 

@@ -71,6 +71,12 @@ struct Bwd2Params {
     float *dv, *dw, *ds0;
     float* ck;                     // [BH][nch][Dv][Dk]
     float *pq, *pk, *pb, *pg;      // [NRB][BTH][Dk] each
+    // scalar gates (the gated delta rule as GDN-2 with alpha broadcast over
+    // the channels and erase = write = beta): alpha, beta [B,T,H] fp32 in,
+    // and per-token partials of dbeta (erase part, write part) and d log alpha
+    const float *alpha_s, *beta_s;
+    float *pbs, *pgs;              // [4 NRB][BTH]: per (row block, wave)
+    float* pws;                    // [2 NRB][BTH]: per (row block, row tile)
 };
 
 // LDS tables.  Pitches: key-side rows PK = 4 (mod 64), n x rows PR = 36,
@@ -178,9 +184,21 @@ struct Pre2 {
     static constexpr int WD = 2 / packed<TD>::PER_WORD;
     uint32_t k[WK], b[WK], a[WK], q[WK];
     uint32_t w[WP], v[WP], d[WD];
+    float as, bs;                  // scalar gates
 };
 
-template <int DK, int DV, typename TIn, typename TD>
+// sum over the 16 lanes of each DPP row; every lane gets the sum
+__device__ __forceinline__ float rsum16(float x) {
+    x = qsum(x);
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                0x141, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                0x140, 0xF, 0xF, false));
+    return x;
+}
+
+// SC: scalar gates (alpha, beta per token, fp32), the gated delta rule.
+template <int DK, int DV, typename TIn, typename TD, bool SC>
 __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
     using L = BL3<DK>;
     constexpr int NRB = DV / R2;
@@ -237,10 +255,15 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         if (tr < chunk_len(c)) {
             const int64_t tk = tok(c * C2 + tr);
             ldw(x.k, reinterpret_cast<const TIn*>(p.k) + tk * DK + j0);
-            ldw(x.b, reinterpret_cast<const TIn*>(p.erase) + tk * DK + j0);
-            ldw(x.a, reinterpret_cast<const TIn*>(p.alpha) + tk * DK + j0);
+            if constexpr (SC) {
+                x.as = p.alpha_s[tk];
+                x.bs = p.beta_s[tk];
+            } else {
+                ldw(x.b, reinterpret_cast<const TIn*>(p.erase) + tk * DK + j0);
+                ldw(x.a, reinterpret_cast<const TIn*>(p.alpha) + tk * DK + j0);
+                ldw(x.w, reinterpret_cast<const TIn*>(p.write) + tk * DV + row0 + i2);
+            }
             if (bwd) ldw(x.q, reinterpret_cast<const TIn*>(p.q) + tk * DK + j0);
-            ldw(x.w, reinterpret_cast<const TIn*>(p.write) + tk * DV + row0 + i2);
             ldw(x.v, reinterpret_cast<const TIn*>(p.v) + tk * DV + row0 + i2);
             if (bwd) ldw(x.d, reinterpret_cast<const TD*>(p.dout) + tk * DV + row0 + i2);
         }
@@ -249,6 +272,8 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
     auto commit = [&](const PF& x, int64_t c, bool bwd) {
         const bool live = tr < chunk_len(c);
         const int at = tr * L::PK + j0;
+        float sg = 0.f;
+        if constexpr (SC) sg = live ? safe_log2(x.as) : 0.f;
 #pragma unroll
         for (int y0 = 0; y0 < NC; y0 += 4) {
             f32x4 kv, bv, ev, gv, qv;
@@ -256,9 +281,14 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             for (int e = 0; e < 4; ++e) {
                 const int y = y0 + e;
                 kv[e] = live ? packed<TIn>::at(x.k, y) : 0.f;
-                bv[e] = live ? packed<TIn>::at(x.b, y) : 0.f;
+                if constexpr (SC) {
+                    bv[e] = live ? x.bs : 0.f;
+                    gv[e] = sg;
+                } else {
+                    bv[e] = live ? packed<TIn>::at(x.b, y) : 0.f;
+                    gv[e] = live ? safe_log2(packed<TIn>::at(x.a, y)) : 0.f;
+                }
                 ev[e] = bv[e] * kv[e];
-                gv[e] = live ? safe_log2(packed<TIn>::at(x.a, y)) : 0.f;
                 qv[e] = (live && bwd) ? packed<TIn>::at(x.q, y) : 0.f;
             }
             *reinterpret_cast<f32x4*>(Ks + at + y0) = kv;
@@ -270,7 +300,8 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int o = tr * L::PR + i2 + e;
-            Wsm[o] = live ? packed<TIn>::at(x.w, e) : 0.f;
+            if constexpr (SC) Wsm[o] = live ? x.bs : 0.f;
+            else Wsm[o] = live ? packed<TIn>::at(x.w, e) : 0.f;
             Vsm[o] = live ? packed<TIn>::at(x.v, e) : 0.f;
             if (bwd) dOs[o] = live ? packed<TD>::at(x.d, e) : 0.f;
         }
@@ -556,9 +587,15 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * lg + i, o = r * L::PR + 16 * t + l16;
                 dRs[o] = acc[i];
+                float dwv = acc[i] * Vsm[o];
+                if constexpr (SC) dwv = rsum16(dwv);   // over this tile's 16 rows
                 if (r < n) {
                     const int64_t off = tok(t0 + r) * DV + row0 + 16 * t + l16;
-                    p.dw[off] = acc[i] * Vsm[o];
+                    if constexpr (SC) {
+                        if (l16 == 0) p.pws[(2 * rb + t) * p.BTH + tok(t0 + r)] = dwv;
+                    } else {
+                        p.dw[off] = dwv;
+                    }
                     p.dv[off] = acc[i] * Wsm[o];
                 }
             }
@@ -592,6 +629,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         }
         __syncthreads();   // dA
         const float* dAs = dTs;
+        f32x4 sb = zero4, sgl = zero4;   // scalar gates: this wave's channel sums
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
             const int t = CTW * wv + ct, cc = 16 * t + l16;
@@ -689,8 +727,14 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
                     const int64_t o = poff + tok(t0 + r) * DK + cc;
                     p.pq[o] = oq[i];
                     p.pk[o] = ok[i];
-                    p.pb[o] = ob[i];
-                    p.pg[o] = dl[i];
+                    if constexpr (!SC) {
+                        p.pb[o] = ob[i];
+                        p.pg[o] = dl[i];
+                    }
+                }
+                if constexpr (SC) {
+                    sb[i] += ob[i];
+                    sgl[i] += dl[i];
                 }
             }
             // ---- G' <- G' diag(lambda_C) + dO^T Q~ - dR^T E~ on this wave's
@@ -704,6 +748,19 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
                 acc = mma16<1, false, false, true>(acc, dRs + 16 * a, L::PR, Et + 16 * t, L::PK);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) Gs[(16 * a + 4 * lg + i) * L::PK + cc] = acc[i];
+            }
+        }
+        if constexpr (SC) {
+            // dbeta (erase part) and d log alpha: sums over this wave's channels
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float vb = rsum16(sb[i]), vg = rsum16(sgl[i]);
+                const int r = 4 * lg + i;
+                if (l16 == 0 && r < n) {
+                    const int64_t o = (int64_t)(4 * rb + wv) * p.BTH + tok(t0 + r);
+                    p.pbs[o] = vb;
+                    p.pgs[o] = vg;
+                }
             }
         }
     }
@@ -745,12 +802,64 @@ __global__ __launch_bounds__(256) void bwd2_reduce(int64_t n, const float* __res
     da[i] = d / fmaxf(ldf<TIn>(alpha, i), 1.17549435e-38f);
 }
 
+// scalar gates: dq, dk from the row blocks' partials
+template <int NRB>
+__global__ __launch_bounds__(256) void bwd_reduce_qk(int64_t n, const float* __restrict__ pq,
+                                                     const float* __restrict__ pk,
+                                                     float* __restrict__ dq,
+                                                     float* __restrict__ dk) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+        a += pq[r * n + i];
+        b += pk[r * n + i];
+    }
+    dq[i] = a;
+    dk[i] = b;
+}
+
+// scalar gates, per token: dbeta = erase part (per row block and wave) +
+// write part (per row block and row tile); dalpha = d log alpha / alpha
+template <int NRB>
+__global__ __launch_bounds__(256) void bwd_reduce_gates(int64_t n, const float* __restrict__ pbs,
+                                                        const float* __restrict__ pgs,
+                                                        const float* __restrict__ pws,
+                                                        const float* __restrict__ alpha,
+                                                        float* __restrict__ dbeta,
+                                                        float* __restrict__ dalpha) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float b = 0.f, g = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4 * NRB; ++r) {
+        b += pbs[r * n + i];
+        g += pgs[r * n + i];
+    }
+#pragma unroll
+    for (int r = 0; r < 2 * NRB; ++r) b += pws[r * n + i];
+    dbeta[i] = b;
+    dalpha[i] = g / fmaxf(alpha[i], 1.17549435e-38f);
+}
+
+template <int DK, int DV, typename TIn, typename TD, bool SC>
+hipError_t launch_main(const Bwd2Params& p, int64_t BH, hipStream_t st) {
+    const size_t lds = sizeof(float) * BL3<DK>::TOTAL;
+    auto fn = chunk2_bwd_kernel<DK, DV, TIn, TD, SC>;
+    hipError_t e = hipFuncSetAttribute((const void*)fn,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, dim3((unsigned)(BH * (DV / R2))), dim3(NT2), lds, st, p);
+    return hipGetLastError();
+}
+
 template <int DK, int DV, typename TIn, typename TD>
 hipError_t launch_bwd2_t(const Bwd2Args& a) {
     constexpr int NRB = DV / R2;
     const int64_t BH = a.B * a.H, BTH = a.B * a.T * a.H;
     const int64_t nch = (a.T + C2 - 1) / C2;
-    Bwd2Params p;
+    Bwd2Params p{};
     p.T = a.T;
     p.H = a.H;
     p.BTH = BTH;
@@ -766,24 +875,54 @@ hipError_t launch_bwd2_t(const Bwd2Args& a) {
     p.dv = a.dv;
     p.dw = a.dwrite;
     p.ds0 = a.ds0;
-    float* ws = reinterpret_cast<float*>(a.workspace);
-    p.ck = ws;
+    p.ck = reinterpret_cast<float*>(a.workspace);
     p.pq = p.ck + BH * nch * DV * DK;
     p.pk = p.pq + NRB * BTH * DK;
     p.pb = p.pk + NRB * BTH * DK;
     p.pg = p.pb + NRB * BTH * DK;
-    const size_t lds = sizeof(float) * BL3<DK>::TOTAL;
-    auto fn = chunk2_bwd_kernel<DK, DV, TIn, TD>;
-    hipError_t e = hipFuncSetAttribute((const void*)fn,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fn, dim3((unsigned)(BH * NRB)), dim3(NT2), lds, a.stream, p);
-    e = hipGetLastError();
+    hipError_t e = launch_main<DK, DV, TIn, TD, false>(p, BH, a.stream);
     if (e != hipSuccess) return e;
     const int64_t nqk = BTH * DK;
     hipLaunchKernelGGL((bwd2_reduce<NRB, TIn>), dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0,
                        a.stream, nqk, p.pq, p.pk, p.pb, p.pg, a.alpha, a.dq, a.dk, a.derase,
                        a.dalpha);
+    return hipGetLastError();
+}
+
+template <int DK, int DV, typename TIn, typename TD>
+hipError_t launch_bwd_t(const BwdArgs& a) {
+    constexpr int NRB = DV / R2;
+    const int64_t BH = a.B * a.H, BTH = a.B * a.T * a.H;
+    const int64_t nch = (a.T + C2 - 1) / C2;
+    Bwd2Params p{};
+    p.T = a.T;
+    p.H = a.H;
+    p.BTH = BTH;
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.dout = a.dout;
+    p.s0 = a.s0;
+    p.dsf = a.ds_final;
+    p.dv = a.dv;
+    p.ds0 = a.ds0;
+    p.alpha_s = a.alpha;
+    p.beta_s = a.beta;
+    p.ck = reinterpret_cast<float*>(a.workspace);
+    p.pq = p.ck + BH * nch * DV * DK;
+    p.pk = p.pq + NRB * BTH * DK;
+    p.pbs = p.pk + NRB * BTH * DK;
+    p.pgs = p.pbs + 4 * NRB * BTH;
+    p.pws = p.pgs + 4 * NRB * BTH;
+    hipError_t e = launch_main<DK, DV, TIn, TD, true>(p, BH, a.stream);
+    if (e != hipSuccess) return e;
+    const int64_t nqk = BTH * DK;
+    hipLaunchKernelGGL((bwd_reduce_qk<NRB>), dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0,
+                       a.stream, nqk, p.pq, p.pk, a.dq, a.dk);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_reduce_gates<NRB>), dim3((unsigned)((BTH + 255) / 256)), dim3(256), 0,
+                       a.stream, BTH, p.pbs, p.pgs, p.pws, a.alpha, a.dbeta, a.dalpha);
     return hipGetLastError();
 }
 
@@ -796,6 +935,15 @@ hipError_t launch_bwd2_d(const Bwd2Args& a) {
                        : launch_bwd2_t<DK, DV, float, float>(a);
 }
 
+template <int DK, int DV>
+hipError_t launch_bwd_d(const BwdArgs& a) {
+    if (a.in_bf16)
+        return a.dout_bf16 ? launch_bwd_t<DK, DV, bf16_t, bf16_t>(a)
+                           : launch_bwd_t<DK, DV, bf16_t, float>(a);
+    return a.dout_bf16 ? launch_bwd_t<DK, DV, float, bf16_t>(a)
+                       : launch_bwd_t<DK, DV, float, float>(a);
+}
+
 }  // namespace
 
 size_t bwd2_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv) {
@@ -804,11 +952,25 @@ size_t bwd2_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t
     return sizeof(float) * (size_t)(B * H * nch * Dv * Dk + 4 * nrb * B * T * H * Dk);
 }
 
+size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv) {
+    const int64_t nch = (T + C2 - 1) / C2;
+    const int64_t nrb = Dv / R2;
+    const int64_t BTH = B * T * H;
+    return sizeof(float) * (size_t)(B * H * nch * Dv * Dk + 2 * nrb * BTH * Dk + 10 * nrb * BTH);
+}
+
 hipError_t launch_chunk2_bwd(const Bwd2Args& a) {
     if (a.Dk == 128 && a.Dv == 128) return launch_bwd2_d<128, 128>(a);
     if (a.Dk == 128 && a.Dv == 64) return launch_bwd2_d<128, 64>(a);
     if (a.Dk == 64 && a.Dv == 128) return launch_bwd2_d<64, 128>(a);
     return launch_bwd2_d<64, 64>(a);
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs& a) {
+    if (a.Dk == 128 && a.Dv == 128) return launch_bwd_d<128, 128>(a);
+    if (a.Dk == 128 && a.Dv == 64) return launch_bwd_d<128, 64>(a);
+    if (a.Dk == 64 && a.Dv == 128) return launch_bwd_d<64, 128>(a);
+    return launch_bwd_d<64, 64>(a);
 }
 
 }  // namespace gdr

@@ -249,7 +249,10 @@ gdr_status_t gdr_output_gate(int64_t N, int64_t H, int64_t Dv, gdr_dtype_t o_dt,
  * Networks", agihunt.info, "Method"; GDN review on meaningful96.github.io,
  * section 3.7), evaluated chunk by chunk in fp32: the pages' throughput
  * figures are for training, and the GDN-2 summary notes that a chunked
- * backward carries the gates inside its dot products.
+ * backward carries the gates inside its dot products.  The rule is Gated
+ * Delta Rule-2 with alpha broadcast over the key channels and
+ * erase = write = beta, and this call runs the gdr2_chunk_bwd kernels in
+ * that form, reducing the per-channel gate gradients to per-token ones.
  *
  *   q, k, v, alpha, beta, s0, in_dt  the forward's inputs, as for gdr_chunk_fwd
  *   dout_dt, dout  [B, T, H, Dv] dL/do (GDR_F32 or GDR_BF16)
@@ -264,7 +267,7 @@ gdr_status_t gdr_output_gate(int64_t N, int64_t H, int64_t Dv, gdr_dtype_t o_dt,
  *                  gdr_chunk_bwd_workspace_size(B, T, H, Dk, Dv) bytes,
  *                  16-byte aligned, owned by the caller; its contents on
  *                  entry do not matter and on return are unspecified.
- *                  It holds the chunk-start states (B H ceil(T/32) Dv Dk
+ *                  It holds the chunk-start states (B H ceil(T/16) Dv Dk
  *                  floats) and per-row-block partial sums.  A smaller
  *                  workspace_bytes is GDR_ERR_INVALID.
  *

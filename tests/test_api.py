@@ -174,10 +174,11 @@ def bwd(gdr, B=1, T=8, H=1, Dk=64, Dv=64, dt=1, q=A16, k=A16, v=A16, a=A16, b=A1
 
 
 def test_bwd_workspace_size(gdr):
-    """Chunk-start states (B H ceil(T/32) Dv Dk floats) plus partials for
-    Dv/32 row blocks (2 Dk + 2 floats per token-head each)."""
+    """Chunk-start states (B H ceil(T/16) Dv Dk floats) plus, for Dv/32 row
+    blocks, dq and dk partials (2 Dk floats per token-head each) and gate
+    partials (10 floats per token-head each)."""
     assert gdr.gdr_chunk_bwd_workspace_size(2, 100, 3, 128, 64) == \
-        4 * (2 * 3 * 4 * 64 * 128 + 2 * 2 * 600 * 128 + 2 * 2 * 600)
+        4 * (2 * 3 * 7 * 64 * 128 + 2 * 2 * 600 * 128 + 10 * 2 * 600)
     assert gdr.gdr_chunk_bwd_workspace_size(1, 8, 1, 96, 64) == 0
     assert gdr.gdr_chunk_bwd_workspace_size(-1, 8, 1, 64, 64) == 0
 
