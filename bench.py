@@ -64,6 +64,10 @@ KERNELS = {"gdn": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, 
            "decode": "void gdr::step_kernel<128, 128, unsigned short, float>",
            "gate": "void gdr::(anonymous namespace)::output_gate_kernel<128, float, unsigned short, "
                    "unsigned short>",
+           "bwd": "void gdr::(anonymous namespace)::chunk2_bwd_kernel<128, 128, unsigned short, "
+                  "unsigned short, true>",
+           "bwd2": "void gdr::(anonymous namespace)::chunk2_bwd_kernel<128, 128, unsigned short, "
+                   "unsigned short, false>",
            "copy": "__amd_rocclr_copyBuffer"}
 
 
@@ -111,14 +115,15 @@ def summarize(trace_dir, fetch_dir, write_dir, out_txt, command, timed=20):
     # `timed` dispatches of each kernel; the warm-up launches before them
     # include the clock ramp after idle)
     trace = list(csv.DictReader(open(glob.glob(os.path.join(trace_dir, "*kernel_trace.csv"))[0])))
-    lines += ["", f"Timed launches (the last {timed} dispatches of each kernel in the trace, as the "
-              "bench times them):", f"  {'leg':8s} {'kernel':44s} {'n':>4s} {'avg us':>10s} {'min us':>10s}"]
+    lines += ["", f"Timed launches (the last {timed} dispatches of each kernel in the trace, 10 for "
+              "the backward legs, as the bench times them):", f"  {'leg':8s} {'kernel':44s} {'n':>4s} {'avg us':>10s} {'min us':>10s}"]
     for leg, prefix in KERNELS.items():
         d = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in trace
                    if r["Kernel_Name"].startswith(prefix))
         if not d:
             continue
-        dur = [(e - b) / 1e3 for b, e in d[-timed:]]
+        n_timed = min(timed, 10) if leg in ("bwd", "bwd2") else timed   # legs capped at 10
+        dur = [(e - b) / 1e3 for b, e in d[-n_timed:]]
         lines.append(f"  {leg:8s} {prefix[:44]:44s} {len(dur):4d} {sum(dur) / len(dur):10.1f} "
                      f"{min(dur):10.1f}")
     lines += ["", "HBM counters per dispatch (KiB as read; scale = copy's known bytes / reading):",
@@ -569,7 +574,8 @@ def main():
                            "launch_us_mean": r["mean"] * 1e6, "tokens/s": r["tokens"] / r["mean"],
                            "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_PEAK_TFLOPS,
                                         "unit": "TFLOP/s", "frac": tf / FP32_PEAK_TFLOPS},
-                           "flops_per_launch": r["flops"], "workspace_bytes": r["ws"]}
+                           "flops_per_launch": r["flops"], "workspace_bytes": r["ws"],
+                           "traffic": measured_traffic("bwd")}
     if "bwd2" in res:
         r = res["bwd2"]
         tf = r["flops"] / r["mean"] / 1e12
@@ -580,7 +586,8 @@ def main():
                             "roofline": {"bound": "alu", "achieved": tf,
                                          "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                                          "frac": tf / FP32_PEAK_TFLOPS},
-                            "flops_per_launch": r["flops"], "workspace_bytes": r["ws"]}
+                            "flops_per_launch": r["flops"], "workspace_bytes": r["ws"],
+                            "traffic": measured_traffic("bwd2")}
     if "copy" in res:
         cp = res["copy"]
         out["copy_reference"] = {"what": "torch device-to-device copy, 512 MiB read + 512 MiB "

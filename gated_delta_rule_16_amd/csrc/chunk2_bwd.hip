@@ -45,6 +45,11 @@
 // vector ALU.  Per chunk the per-channel gradients stay in the registers of
 // the wave that owns those channels, from the products to the HBM stores.
 //
+// The scalar-gate rule (gdr_chunk_bwd) is this rule with alpha broadcast
+// over the key channels and erase = write = beta; template flag SC reads
+// alpha and beta per token and sums the per-channel gate gradients (and the
+// per-row write gradient) into per-token partials inside the kernel.
+//
 // The LDS footprint (~142 KB) allows one workgroup per CU, one wave per SIMD,
 // so every global input of the next chunk (key-side rows, w, v, dL/do, the
 // chunk-start state) is loaded into registers as raw words while the current
