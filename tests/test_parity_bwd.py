@@ -25,7 +25,11 @@ def _grads_in(inp, dout_dtype, seed, with_dsf=True):
     return do, dsf
 
 
-def _check(gdr_lib, inp, dout_dtype=torch.float32, seed=0, with_dsf=True, tol=TOL):
+def _check(gdr_lib, inp, dout_dtype=torch.float32, seed=0, with_dsf=True, tol=TOL,
+           log_alpha=False):
+    """``log_alpha``: compare alpha * dalpha (the gradient with respect to
+    log alpha, which keeps fp32 accuracy where alpha is near 0; the kernels
+    divide it by alpha) instead of dalpha."""
     print(f"bwd {inp.meta} dout={dout_dtype} dsf={with_dsf}", flush=True)
     do, dsf = _grads_in(inp, dout_dtype, seed, with_dsf)
     ref = oracle.gdn_bwd(inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.s0, do, dsf)
@@ -35,7 +39,11 @@ def _check(gdr_lib, inp, dout_dtype=torch.float32, seed=0, with_dsf=True, tol=TO
     torch.cuda.synchronize()
     errs = {}
     for name, x, y in zip(NAMES, got, ref):
-        errs[name] = oracle.err_rms(x.cpu(), y)
+        x = x.cpu()
+        if log_alpha and name == "dalpha":
+            a = inp.alpha.double().numpy()
+            x, y = x.double().numpy() * a, y * a
+        errs[name] = oracle.err_rms(x, y)
     print("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     bad = {n: e for n, e in errs.items() if not e <= tol}
     assert not bad, bad
@@ -73,6 +81,18 @@ def test_bwd_gate_regimes(gdr_lib):
                    s0_std=0.2)
     inp.beta = inp.beta * 2.0
     _check(gdr_lib, inp, seed=4)
+
+
+def test_bwd_reset_gates(gdr_lib):
+    """alpha = 0 and 1e-12 on some tokens: their chunks take the entry-by-entry
+    decays (the factored form would overflow), the others stay factored."""
+    inp = make_gdn(B=1, T=130, H=2, Dk=64, Dv=64, dtype="f32", seed=545, s0_std=0.2)
+    a = inp.alpha.clone()
+    a[0, 20, 0] = 0.0
+    a[0, 57:60, 1] = 1e-12
+    a[0, 129, 0] = 0.0
+    inp.alpha = a
+    _check(gdr_lib, inp, seed=6, log_alpha=True)
 
 
 def test_bwd_workload_sampled(gdr_lib):
