@@ -199,9 +199,12 @@ def bench_gdn(gdr, torch, warmup, steps):
                 Dv=Dv, bytes=bytes_launch, flops=flops_launch)
 
 
-def bench_longctx(gdr, torch, warmup, steps):
-    """The long-context workload: B1 H16 T32768 d128 with an initial state
-    (16 sequential chains of 1024 chunks; few heads, so narrow row blocks)."""
+def bench_longctx(gdr, torch, warmup, steps, nseg=8):
+    """The long-context workload: B1 H16 T32768 d128 with an initial state.
+    Run plainly it is 16 sequential chains of 1024 chunks (few heads, so
+    narrow row blocks and half the compute units idle); the split call runs
+    it as nseg = 8 segments side by side (three passes plus a scan).  Both
+    are timed; the bytes and flops are the workload's algorithmic ones."""
     from gdr_gen import make_config
     inp = make_config(2)
     B, T, H, Dk = inp.q.shape
@@ -212,16 +215,24 @@ def bench_longctx(gdr, torch, warmup, steps):
     s0 = inp.s0.to(dev)
     o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
     sf = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdr.gdr_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, q.dtype, nseg),
+                     dtype=torch.uint8, device=dev)
 
-    def fn():
+    def plain():
         gdr.gdr_chunk_fwd(q, k, v, a, b, s0, out_dtype=torch.float32, o=o, s_final=sf)
 
-    mean, mn, med, wall = time_launches(fn, warmup, steps)
+    def split():
+        gdr.gdr_chunk_fwd_split(q, k, v, a, b, s0, nseg=nseg, out_dtype=torch.float32, o=o,
+                                s_final=sf, workspace=ws)
+
+    mean, mn, med, wall = time_launches(split, warmup, steps)
+    pmean, pmn, _, _ = time_launches(plain, warmup, steps)
     th = B * T * H
     bytes_launch = th * (2 * (Dk + Dk + Dv) + 8 + 4 * Dv) + 2 * 4 * B * H * Dv * Dk
     C = 64
     flops_launch = th * 2 * (3 * Dk * Dv + 5 * C * (Dk + Dv) // 2)
-    return dict(mean=mean, min=mn, B=B, T=T, H=H, bytes=bytes_launch, flops=flops_launch)
+    return dict(mean=mean, min=mn, plain_mean=pmean, plain_min=pmn, nseg=nseg, B=B, T=T, H=H,
+                bytes=bytes_launch, flops=flops_launch)
 
 
 def bench_decode(gdr, torch, warmup):
@@ -548,11 +559,14 @@ def main():
         r = res["longctx"]
         gbs = r["bytes"] / r["mean"] / 1e9
         out["long_context"] = {
-            "workload": "gdr_chunk_fwd B1 H16 T32768 d128 bf16, fp32 alpha/beta/o, initial state",
+            "workload": "B1 H16 T32768 d128 bf16, fp32 alpha/beta/o, initial state: "
+                        f"gdr_chunk_fwd_split, {r['nseg']} segments of {r['T'] // r['nseg']}",
             "tokens/s": r["B"] * r["T"] / r["mean"], "launch_us_mean": r["mean"] * 1e6,
             "launch_us_min": r["min"] * 1e6, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
             "mfma_frac": r["flops"] / r["mean"] / 1e12 / BF16_PEAK_TFLOPS,
-            "algorithmic_bytes_per_launch": r["bytes"]}
+            "algorithmic_bytes_per_launch": r["bytes"],
+            "plain_gdr_chunk_fwd": {"launch_us_mean": r["plain_mean"] * 1e6,
+                                    "tokens/s": r["B"] * r["T"] / r["plain_mean"]}}
     if "l2norm" in res:
         out["l2norm"] = {"what": "launch us with raw q, k: fused GDR_L2NORM_QK, plain call "
                                  "(no normalisation), separate PyTorch normalise pass + plain call",

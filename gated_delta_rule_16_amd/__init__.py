@@ -8,6 +8,7 @@ fallback — importing this package without the built ``libgdr.so`` fails.
 Functions mirror the C calls:
 
     gdr_chunk_fwd(q, k, v, alpha, beta, s0=None, ...)            -> (o, s_final)
+    gdr_chunk_fwd_split(q, k, v, alpha, beta, s0=None, nseg=8, ...) -> (o, s_final)
     gdr_recurrent_step(q, k, v, alpha, beta, state, ...)         -> o
     gdr2_chunk_fwd(q, k, v, alpha, erase, write, s0=None, ...)   -> (o, s_final)
     gdr_output_gate(o, g, w=None, eps=1e-6, ...)                -> y
@@ -29,6 +30,7 @@ import torch  # loads the HIP runtime libgdr.so binds to
 __all__ = ["gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd", "gdr_output_gate",
            "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size",
            "gdr2_chunk_bwd", "gdr2_chunk_bwd_workspace_size",
+           "gdr_chunk_fwd_split", "gdr_chunk_fwd_split_workspace_size",
            "GdrError", "status_string", "lib", "LIB_PATH", "GDR_F32",
            "GDR_BF16", "GDR_L2NORM_QK"]
 
@@ -70,6 +72,11 @@ lib.gdr2_chunk_bwd_workspace_size.restype = ctypes.c_size_t
 lib.gdr2_chunk_bwd.argtypes = ([_I64] * 5 + [_E] + [_P] * 7 + [_E, _P, _P] + [_P] * 7 +
                                [_P, ctypes.c_size_t, _P])
 lib.gdr2_chunk_bwd.restype = ctypes.c_int
+lib.gdr_chunk_fwd_split_workspace_size.argtypes = [_I64] * 5 + [_E, _I64]
+lib.gdr_chunk_fwd_split_workspace_size.restype = ctypes.c_size_t
+lib.gdr_chunk_fwd_split.argtypes = ([_I64] * 5 + [_E] + [_P] * 6 + [_E, _P, _P, _I64, _U, _P,
+                                    ctypes.c_size_t, _P])
+lib.gdr_chunk_fwd_split.restype = ctypes.c_int
 lib.gdr_status_string.argtypes = [ctypes.c_int]
 lib.gdr_status_string.restype = ctypes.c_char_p
 lib.gdr_version.restype = ctypes.c_int
@@ -150,6 +157,50 @@ def gdr_chunk_fwd(q, k, v, alpha, beta, s0=None, *, out_dtype=None, o=None,
         _run("gdr_chunk_fwd_ex", lib.gdr_chunk_fwd_ex(*args, GDR_L2NORM_QK, _stream(stream)))
     else:
         _run("gdr_chunk_fwd", lib.gdr_chunk_fwd(*args, _stream(stream)))
+    return o, s_final
+
+
+def gdr_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, dtype, nseg) -> int:
+    """Bytes of device workspace gdr_chunk_fwd_split needs (0: none)."""
+    return int(lib.gdr_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, _DT[dtype], nseg))
+
+
+def gdr_chunk_fwd_split(q, k, v, alpha, beta, s0=None, *, nseg=8, out_dtype=None, o=None,
+                        s_final=None, want_state=True, l2norm_qk=False, workspace=None,
+                        stream=None):
+    """gdr_chunk_fwd with each sequence split into ``nseg`` segments that run
+    side by side (T divisible by nseg).  Same arguments and results as
+    gdr_chunk_fwd; ``workspace`` is a uint8 GPU tensor of at least
+    gdr_chunk_fwd_split_workspace_size(...) bytes, allocated here when None."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if q.dtype not in _DT:
+        raise TypeError(f"unsupported input dtype {q.dtype}")
+    _check("q", q, q.dtype, (B, T, H, Dk))
+    _check("k", k, q.dtype, (B, T, H, Dk))
+    _check("v", v, q.dtype, (B, T, H, Dv))
+    _check("alpha", alpha, torch.float32, (B, T, H))
+    _check("beta", beta, torch.float32, (B, T, H))
+    if s0 is not None:
+        _check("s0", s0, torch.float32, (B, H, Dv, Dk))
+    odt = q.dtype if out_dtype is None else out_dtype
+    if odt not in _DT:
+        raise TypeError(f"unsupported output dtype {odt}")
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=odt, device=q.device)
+    _check("o", o, odt, (B, T, H, Dv))
+    if s_final is None and want_state:
+        s_final = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=q.device)
+    if s_final is not None:
+        _check("s_final", s_final, torch.float32, (B, H, Dv, Dk))
+    need = gdr_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, q.dtype, nseg)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check("workspace", workspace, torch.uint8)
+    _run("gdr_chunk_fwd_split", lib.gdr_chunk_fwd_split(
+        B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _ptr(s0), _DT[odt], _ptr(o), _ptr(s_final), nseg, GDR_L2NORM_QK if l2norm_qk else 0,
+        _ptr(workspace), workspace.numel(), _stream(stream)))
     return o, s_final
 
 

@@ -137,6 +137,109 @@ extern "C" gdr_status_t gdr_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t D
                             s_final, 0u, stream);
 }
 
+// Sequence-split forward: workspace pieces, each rounded up to 256 bytes.
+namespace {
+struct SplitLayout {
+    size_t R, P, Sin, vz, oP, total;
+};
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+SplitLayout split_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                         gdr_dtype_t in_dt, int64_t nseg) {
+    SplitLayout l{};
+    const size_t bn = (size_t)(B * nseg * H);
+    l.R = up256(bn * Dv * Dk * 4);
+    l.P = up256(bn * Dk * Dk * 4);
+    l.Sin = up256(bn * Dv * Dk * 4);
+    l.vz = up256((size_t)(B * T * H * Dk) * (in_dt == GDR_BF16 ? 2 : 4));
+    l.oP = Dk == Dv ? 0 : up256((size_t)(B * T * H * Dk) * 2);
+    l.total = l.R + l.P + l.Sin + l.vz + l.oP;
+    return l;
+}
+}  // namespace
+
+extern "C" size_t gdr_chunk_fwd_split_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                                     int64_t Dv, gdr_dtype_t in_dt,
+                                                     int64_t nseg) {
+    if (B < 0 || T < 0 || H < 0 || nseg < 1 || nseg > (1 << 20)) return 0;
+    if (!dims_ok(Dk, Dv) || !dtype_ok(in_dt)) return 0;
+    if (!sizes_ok(B, T, H) || !sizes_ok(B * T * H, Dk > Dv ? Dk : Dv, 1)) return 0;
+    if (!sizes_ok(B * nseg, H, 1)) return 0;
+    if (nseg == 1 || T == 0 || B == 0 || H == 0) return 0;
+    if (T % nseg != 0) return 0;
+    return split_layout(B, T, H, Dk, Dv, in_dt, nseg).total;
+}
+
+extern "C" gdr_status_t gdr_chunk_fwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                            int64_t Dv, gdr_dtype_t in_dt, const void* q,
+                                            const void* k, const void* v, const float* alpha,
+                                            const float* beta, const float* s0,
+                                            gdr_dtype_t out_dt, void* o, float* s_final,
+                                            int64_t nseg, uint32_t flags, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream) {
+    if (nseg < 1 || nseg > (1 << 20)) return GDR_ERR_INVALID;
+    if (nseg == 1 || T == 0 || B == 0 || H == 0)
+        return gdr_chunk_fwd_ex(B, T, H, Dk, Dv, in_dt, q, k, v, alpha, beta, s0, out_dt, o,
+                                s_final, flags, stream);
+    if (!flags_ok(flags)) return GDR_ERR_UNSUPPORTED;
+    ChunkArgs a{};
+    gdr_status_t st = chunk_common(B, T, H, Dk, Dv, in_dt, out_dt, a);
+    if (st != GDR_OK) return st;
+    if (T % nseg != 0 || !sizes_ok(B * nseg, H, 1)) return GDR_ERR_INVALID;
+    if (B * nseg * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
+    if (!ptrs_ok({q, k, v, workspace}) || !elem_ok(alpha, 4) || !elem_ok(beta, 4) ||
+        !elem_ok(o, out_dt == GDR_BF16 ? 2 : 4))
+        return GDR_ERR_INVALID;
+    if (!opt_ok(s0) || !opt_ok(s_final)) return GDR_ERR_INVALID;
+    const SplitLayout l = split_layout(B, T, H, Dk, Dv, in_dt, nseg);
+    if (workspace_bytes < l.total) return GDR_ERR_INVALID;
+    char* w = static_cast<char*>(workspace);
+    float* R = reinterpret_cast<float*>(w);
+    float* P = reinterpret_cast<float*>(w + l.R);
+    float* Sin = reinterpret_cast<float*>(w + l.R + l.P);
+    void* vz = w + l.R + l.P + l.Sin;
+    void* oP = l.oP ? static_cast<void*>(w + l.R + l.P + l.Sin + l.vz) : o;
+    // the segments as a batch: [B, T, H, d] is [B nseg, T / nseg, H, d]
+    a.B = B * nseg;
+    a.T = T / nseg;
+    a.gated2 = false;
+    a.l2norm = (flags & GDR_L2NORM_QK) != 0;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.stream = stream;
+    // 1. each segment from a zero state: R
+    ChunkArgs r = a;
+    r.s0 = nullptr;
+    r.o = o;
+    r.s_final = R;
+    if ((st = chunk_run(r)) != GDR_OK) return st;
+    // 2. each segment with v = 0 from the identity: P (d_k x d_k)
+    hipError_t e = launch_identity(P, B * nseg * H, (int)Dk, stream);
+    if (e == hipSuccess) e = launch_zero(vz, (int64_t)l.vz, stream);
+    if (e != hipSuccess) return GDR_ERR_DEVICE;
+    ChunkArgs pa = a;
+    pa.Dv = Dk;
+    pa.v = vz;
+    pa.s0 = P;
+    pa.s_final = P;
+    pa.o = oP;
+    pa.out_bf16 = l.oP ? true : a.out_bf16;
+    if ((st = chunk_run(pa)) != GDR_OK) return st;
+    // 3. segment start states
+    SplitScanArgs sc{B, H, Dk, Dv, (int)nseg, s0, R, P, Sin, stream};
+    if ((e = launch_split_scan(sc)) != hipSuccess) return GDR_ERR_DEVICE;
+    // 4. every segment from its start state: o, and the final states in place
+    ChunkArgs f = a;
+    f.s0 = Sin;
+    f.s_final = Sin;
+    f.o = o;
+    if ((st = chunk_run(f)) != GDR_OK) return st;
+    if (s_final) return from_hip(launch_last_state(Sin, s_final, B, (int)nseg, H * Dv * Dk, stream));
+    return GDR_OK;
+}
+
 extern "C" gdr_status_t gdr2_chunk_fwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                           int64_t Dv, gdr_dtype_t in_dt, const void* q,
                                           const void* k, const void* v, const void* alpha,

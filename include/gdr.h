@@ -7,7 +7,8 @@
  *   gdr_recurrent_step  one decode token of the same rule, state in place
  *   gdr2_chunk_fwd      chunkwise forward of Gated Delta Rule-2 (channel gates)
  *
- * plus their _ex variants (q, k L2-normalised on load), the block's
+ * plus their _ex variants (q, k L2-normalised on load), a sequence-split
+ * form of the first for few long sequences (gdr_chunk_fwd_split), the block's
  * output gate on their result (gdr_output_gate) and the reverse modes of
  * the two chunkwise forwards (gdr_chunk_bwd, gdr2_chunk_bwd).
  *
@@ -214,6 +215,49 @@ gdr_status_t gdr2_chunk_fwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                const void *write, const float *s0,
                                gdr_dtype_t out_dt, void *o, float *s_final,
                                uint32_t flags, hipStream_t stream);
+
+/*
+ * Sequence-split form of gdr_chunk_fwd_ex, for few long sequences (few
+ * (b, h) pairs leave most compute units idle when each sequence runs as one
+ * chain).  The rule maps a segment's start state affinely, S -> S P + R,
+ * with R the segment's final state from a zero start and
+ * P = prod_t alpha_t (I - beta_t k_t k_t^T) (the chunkwise form of the rule,
+ * "Gated Delta Networks", agihunt.info, "Method"; GDN review on
+ * meaningful96.github.io, section 3.4).  The call splits each sequence into
+ * nseg segments of T / nseg tokens and runs the chunk kernels three times
+ * over all segments side by side: for R, for P (v = 0 from the identity),
+ * and, after a scan S_in(p) = S_in(p - 1) P_{p-1} + R_{p-1} with
+ * S_in(0) = s0, for o and the final states.
+ *
+ *   arguments as for gdr_chunk_fwd_ex, plus
+ *   nseg       segments per sequence, >= 1, dividing T; 1 is the plain call
+ *              (no workspace needed)
+ *   workspace  device memory of at least
+ *              gdr_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, in_dt,
+ *              nseg) bytes, 16-byte aligned, owned by the caller, contents
+ *              irrelevant on entry and unspecified on return: R, P and the
+ *              start states (fp32, B nseg H Dv Dk, B nseg H Dk Dk and
+ *              B nseg H Dv Dk floats), a zero v for the P pass
+ *              (B T H Dk in_dt elements) and, when Dk != Dv, that pass's
+ *              discarded output (B T H Dk bf16)
+ *
+ * The results equal the plain call's up to rounding (the segments' states
+ * are composed in fp32).  o is written three times (the first two are
+ * overwritten).  The workspace size is 0 for arguments the call rejects
+ * and when no workspace is needed.  Calls on one workspace must not overlap.
+ */
+size_t gdr_chunk_fwd_split_workspace_size(int64_t B, int64_t T, int64_t H,
+                                          int64_t Dk, int64_t Dv,
+                                          gdr_dtype_t in_dt, int64_t nseg);
+
+gdr_status_t gdr_chunk_fwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                 int64_t Dv, gdr_dtype_t in_dt, const void *q,
+                                 const void *k, const void *v,
+                                 const float *alpha, const float *beta,
+                                 const float *s0, gdr_dtype_t out_dt, void *o,
+                                 float *s_final, int64_t nseg, uint32_t flags,
+                                 void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 /*
  * Output gate of the block, applied to the rule's output o per token and

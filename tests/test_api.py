@@ -29,6 +29,7 @@ def test_header_declares_the_three_operations():
               "gdr_chunk_fwd_ex", "gdr_recurrent_step_ex", "gdr2_chunk_fwd_ex",
               "gdr_output_gate", "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size",
               "gdr2_chunk_bwd", "gdr2_chunk_bwd_workspace_size",
+              "gdr_chunk_fwd_split", "gdr_chunk_fwd_split_workspace_size",
               "gdr_status_string", "gdr_version"):
         assert n in names, names
 
@@ -230,3 +231,40 @@ def test_bwd2_validation(gdr, kw, code):
 def test_bwd2_empty(gdr):
     assert bwd2(gdr, H=0, q=None, k=None, v=None, a=None, e=None, w=None, do=None, dq=None,
                 dk=None, dv=None, da=None, de=None, dw=None, ws=None, wsb=0) == 0
+
+
+def split(gdr, B=1, T=64, H=1, Dk=64, Dv=64, dt=1, q=A16, k=A16, v=A16, a=A16, b=A16, s0=None,
+          odt=1, o=A16, sf=None, nseg=4, flags=0, ws=A16, wsb=None):
+    if wsb is None:
+        wsb = gdr.lib.gdr_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, dt, nseg)
+    return gdr.lib.gdr_chunk_fwd_split(B, T, H, Dk, Dv, dt, q, k, v, a, b, s0, odt, o, sf, nseg,
+                                       flags, ws, wsb, None)
+
+
+def test_split_workspace_size(gdr):
+    """R, P and start states (fp32, 256-byte rounded), the zero v of the P pass
+    in the input dtype, and the P pass's output (bf16) only when Dk != Dv."""
+    up = lambda x: (x + 255) // 256 * 256
+    f = gdr.lib.gdr_chunk_fwd_split_workspace_size
+    bn = 2 * 4 * 3
+    assert f(2, 96, 3, 128, 128, 1, 4) == (up(bn * 128 * 128 * 4) * 3 + up(2 * 96 * 3 * 128 * 2))
+    assert f(2, 96, 3, 128, 64, 0, 4) == (up(bn * 64 * 128 * 4) * 2 + up(bn * 128 * 128 * 4) +
+                                          up(2 * 96 * 3 * 128 * 4) + up(2 * 96 * 3 * 128 * 2))
+    assert f(2, 96, 3, 128, 128, 1, 1) == 0     # the plain call
+    assert f(2, 96, 3, 128, 128, 1, 5) == 0     # 5 does not divide 96
+    assert f(2, 96, 3, 96, 128, 1, 4) == 0
+    assert f(2, 96, 3, 128, 128, 1, 0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nseg=0), 1), (dict(nseg=5), 1), (dict(q=None), 1), (dict(ws=None), 1),
+    (dict(ws=BAD), 1), (dict(wsb=100), 1), (dict(s0=BAD), 1), (dict(sf=BAD), 1),
+    (dict(a=None), 1), (dict(o=None), 1), (dict(Dk=96), 2), (dict(dt=7), 2),
+    (dict(flags=8), 2),
+])
+def test_split_validation(gdr, kw, code):
+    assert split(gdr, **kw) == code
+
+
+def test_split_empty(gdr):
+    assert split(gdr, B=0, q=None, k=None, v=None, a=None, b=None, o=None, ws=None, wsb=0) == 0
