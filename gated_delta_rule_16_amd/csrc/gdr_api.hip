@@ -50,6 +50,9 @@ bool sizes_ok(int64_t a, int64_t b, int64_t c) {
     return n < 4.0e18;
 }
 
+// An elementwise launch over n items, 256 per workgroup, fits the grid.
+bool grid_ok(int64_t n) { return (n + 255) / 256 <= 0x7fffffffLL; }
+
 }  // namespace
 
 hipError_t launch_state_copy(const float* s0, float* s_final, int64_t n, hipStream_t st) {
@@ -185,6 +188,8 @@ extern "C" gdr_status_t gdr_chunk_fwd_split(int64_t B, int64_t T, int64_t H, int
     gdr_status_t st = chunk_common(B, T, H, Dk, Dv, in_dt, out_dt, a);
     if (st != GDR_OK) return st;
     if (T % nseg != 0 || !sizes_ok(B * nseg, H, 1)) return GDR_ERR_INVALID;
+    if (!grid_ok(B * T * H * Dk) || !grid_ok(B * nseg * H * Dk * Dk) || !grid_ok(B * H * Dv * Dk))
+        return GDR_ERR_INVALID;
     if (B * nseg * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
     if (!ptrs_ok({q, k, v, workspace}) || !elem_ok(alpha, 4) || !elem_ok(beta, 4) ||
         !elem_ok(o, out_dt == GDR_BF16 ? 2 : 4))
@@ -379,6 +384,7 @@ extern "C" gdr_status_t gdr_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t D
     if (!ptrs_ok({q, k, v, dout, dq, dk, dv, workspace}) || !elem_ok(alpha, 4) ||
         !elem_ok(beta, 4) || !elem_ok(dalpha, 4) || !elem_ok(dbeta, 4))
         return GDR_ERR_INVALID;
+    if (!grid_ok(B * T * H * Dk)) return GDR_ERR_INVALID;
     if (workspace_bytes < bwd_workspace_bytes(B, T, H, Dk, Dv)) return GDR_ERR_INVALID;
     BwdArgs a;
     a.B = B;
@@ -436,6 +442,7 @@ extern "C" gdr_status_t gdr2_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t 
     if (!ptrs_ok({q, k, v, alpha, erase, write, dout, dq, dk, dv, dalpha, derase, dwrite,
                   workspace}))
         return GDR_ERR_INVALID;
+    if (!grid_ok(B * T * H * Dk)) return GDR_ERR_INVALID;
     if (workspace_bytes < bwd2_workspace_bytes(B, T, H, Dk, Dv)) return GDR_ERR_INVALID;
     Bwd2Args a;
     a.B = B;
