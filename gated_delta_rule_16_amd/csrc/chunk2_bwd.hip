@@ -37,12 +37,13 @@
 // Work split: one 256-thread workgroup (4 waves) per (b, h, 32 state rows)
 // runs the forward over its rows (chunk-start states to the workspace), then
 // walks the chunks in reverse.  dv, dw and dS_0 are final per workgroup; dq,
-// dk, db and the within-chunk d log alpha go to per-row-block partials that
-// a second kernel adds (and divides by alpha).  Every product is a set of 16 x 16 tiles on
-// the fp32 matrix cores (v_mfma_f32_16x16x4f32: fp32 operands and
-// accumulation, the vector ALU's precision), the tiles of a phase dealt to
-// the four waves; the triangular solves and the elementwise terms are
-// vector ALU.  Per chunk the per-channel gradients stay in the registers of
+// dk, db and the within-chunk d log alpha (formed without the cancelling
+// cumulative sum, see the combine below) go to per-row-block partials that
+// a second kernel adds (and divides by alpha).  Every product is a set of
+// 16 x 16 tiles on the fp32 matrix cores (v_mfma_f32_16x16x4f32: fp32
+// operands and accumulation, the vector ALU's precision), the tiles of a
+// phase dealt to the four waves; the triangular solves and the elementwise
+// terms are vector ALU.  Per chunk the per-channel gradients stay in the registers of
 // the wave that owns those channels, from the products to the HBM stores.
 //
 // The scalar-gate rule (gdr_chunk_bwd) is this rule with alpha broadcast
