@@ -387,3 +387,32 @@ def test_gdn2_chunk_bwd_matches_oracle(C):
         for name, x, y in zip(names, got, want):
             np.testing.assert_allclose(x, y, rtol=1e-9, atol=1e-10 * max(1.0, np.abs(y).max()),
                                        err_msg=f"{name} C={C} h={h}")
+
+
+@pytest.mark.parametrize("nseg", [2, 3, 6])
+def test_segment_split_composes_to_the_recurrence(nseg):
+    """The sequence-split forward's identity, with the oracle only: each
+    segment maps its start state affinely, S -> S P + R, where R is the
+    segment run from zero and P the run with v = 0 from the identity; the
+    scan S_in(p) = S_in(p-1) P_{p-1} + R_{p-1} from S_0 gives every
+    segment's start state, and re-running each segment from it gives the
+    whole sequence's o and final state."""
+    T, H, Dk, Dv = 36, 2, 6, 5
+    q, k, v, a, b, S0 = rand_gdn(47 + nseg, T=T, H=H, Dk=Dk, Dv=Dv)
+    o_ref, s_ref = oracle.gdn_fwd(q, k, v, a, b, S0)
+    L = T // nseg
+    seg = lambda x, p: x[:, p * L:(p + 1) * L]
+    eye = np.broadcast_to(np.eye(Dk), (1, H, Dk, Dk)).copy()
+    Sin = S0.copy()
+    o = np.empty_like(o_ref)
+    s_last = None
+    for p in range(nseg):
+        qs, ks, vs, as_, bs = (seg(x, p) for x in (q, k, v, a, b))
+        _, R = oracle.gdn_fwd(qs, ks, vs, as_, bs, None)
+        _, P = oracle.gdn_fwd(qs, ks, np.zeros((1, L, H, Dk)), as_, bs, eye)
+        op, s_last = oracle.gdn_fwd(qs, ks, vs, as_, bs, Sin)
+        o[:, p * L:(p + 1) * L] = op
+        np.testing.assert_allclose(s_last, Sin @ P + R, rtol=1e-11, atol=1e-11)
+        Sin = Sin @ P + R
+    np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(s_last, s_ref, rtol=1e-11, atol=1e-11)
