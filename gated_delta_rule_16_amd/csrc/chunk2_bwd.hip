@@ -120,7 +120,8 @@ struct BL3 {
     static constexpr int DU = U + C2 * PR;
     static constexpr int DR = DU + C2 * PR;
     static constexpr int GS = DR + C2 * PR;      // [DK] sum_i G'_ic S_ic
-    static constexpr int TOTAL = GS + DK;
+    static constexpr int WF = GS + DK;           // [4] per-wave "wide" flags
+    static constexpr int TOTAL = WF + 4;
     static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget");
     static_assert(PK % 64 == 4 && NK % 4 == 0 && S % 4 == 0 && G % 4 == 0, "pitches");
     static_assert(A % 4 == 0 && W % 4 == 0 && (Y - A) % 4 == 0, "16-byte rows");
@@ -238,6 +239,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
     float* Us = sm + L::U;
     float* dUs = sm + L::DU;
     float* dRs = sm + L::DR;
+    int* WFs = reinterpret_cast<int*>(sm + L::WF);
     float* GSc = sm + L::GS;
 
     const int tid = threadIdx.x;
@@ -342,7 +344,10 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             for (int r = 0; r < C2; ++r) Gc[r * L::PK + tid] = g[r];
             wide_here = g[C2 - 1] < WIDE2;
         }
-        const bool wide = __syncthreads_or(wide_here);
+        // per-wave flags, read after the closing barrier
+        const bool wide_wave = __ballot(wide_here) != 0;
+        if (lane == 0) WFs[wv] = wide_wave;
+        __syncthreads();
         const int at = tr * L::PK + j0;
 #pragma unroll
         for (int y0 = 0; y0 < NC; y0 += 4) {
@@ -354,7 +359,9 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
                 lm[z] = ex2(g[z]);
                 kt[z] = k[z] * ex2(gC[z] - g[z]);
                 et[z] = e[z] * lm[z];
-                kh[z] = wide ? 0.f : k[z] * ex2(-g[z]);
+                // used in narrow chunks only (-g < 87 there); clamped so that a
+                // wide chunk's unused entries stay finite
+                kh[z] = k[z] * ex2(fminf(-g[z], 120.f));
             }
             *reinterpret_cast<f32x4*>(Lm + at + y0) = lm;
             *reinterpret_cast<f32x4*>(Kt + at + y0) = kt;
@@ -369,7 +376,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             }
         }
         __syncthreads();
-        return wide;
+        return (WFs[0] | WFs[1] | WFs[2] | WFs[3]) != 0;
     };
     // wide chunks: A (s < r) and P (s <= r) entry by entry from the log
     // decays, one thread per (r, s)
