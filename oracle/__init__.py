@@ -90,6 +90,8 @@ class OracleLib:
         lib.oracle_gdn2_bwd.restype = ctypes.c_int
         lib.oracle_l2norm_rows.argtypes = [L, L, P, ctypes.c_double, P]
         lib.oracle_l2norm_rows.restype = ctypes.c_int
+        lib.oracle_l2norm_rows_bwd.argtypes = [L, L, P, P, ctypes.c_double, P]
+        lib.oracle_l2norm_rows_bwd.restype = ctypes.c_int
         lib.oracle_rmsnorm_gate_rows.argtypes = [L, L, P, P, P, ctypes.c_double, P]
         lib.oracle_rmsnorm_gate_rows.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -218,6 +220,19 @@ class OracleLib:
             raise RuntimeError(f"oracle_l2norm_rows failed ({rc})")
         return out
 
+    def l2norm_bwd(self, x, dy, eps=1e-6):
+        """Gradient with respect to the raw rows x of a loss whose gradient
+        with respect to l2norm(x) is dy (``oracle_l2norm_rows_bwd``).  float64."""
+        x, dy = _f64(x), _f64(dy)
+        assert x.shape == dy.shape
+        d = x.shape[-1] if x.ndim else 1
+        n = x.size // d if d else 0
+        out = np.empty_like(x)
+        rc = self.lib.oracle_l2norm_rows_bwd(n, d, _p(x), _p(dy), float(eps), _p(out))
+        if rc:
+            raise RuntimeError(f"oracle_l2norm_rows_bwd failed ({rc})")
+        return out
+
     def rmsnorm_gate(self, o, g, w=None, eps=1e-6):
         """Output gate on rows of the last axis (``oracle_rmsnorm_gate_rows``):
         o / sqrt(mean(o^2) + eps) * w * g * sigmoid(g); w of the last axis'
@@ -294,6 +309,13 @@ def l2norm(*a, **kw):
 
 
 l2norm.__doc__ = OracleLib.l2norm.__doc__
+
+
+def l2norm_bwd(*a, **kw):
+    return default().l2norm_bwd(*a, **kw)
+
+
+l2norm_bwd.__doc__ = OracleLib.l2norm_bwd.__doc__
 
 
 def rmsnorm_gate(*a, **kw):

@@ -344,6 +344,29 @@ int oracle_l2norm_rows(long n, long d, const double *x, double eps, double *out)
 }
 
 /*
+ * Reverse mode of oracle_l2norm_rows: given the rows x and the gradient dy
+ * with respect to y = x / n, n = sqrt(sum_c x_c^2 + eps), the gradient with
+ * respect to x is the transposed Jacobian of the map applied to dy,
+ *
+ *   dx_j = sum_i dy_i (delta_ij / n - x_i x_j / n^3).
+ */
+int oracle_l2norm_rows_bwd(long n, long d, const double *x, const double *dy, double eps,
+                           double *dx) {
+    if (n < 0 || d < 0 || !(eps >= 0.0)) return 1;
+    for (long r = 0; r < n; ++r) {
+        const double *xr = x + r * d, *gr = dy + r * d;
+        double ss = 0.0, xg = 0.0;
+        for (long c = 0; c < d; ++c) {
+            ss += xr[c] * xr[c];
+            xg += xr[c] * gr[c];
+        }
+        const double nn = sqrt(ss + eps);
+        for (long j = 0; j < d; ++j) dx[r * d + j] = gr[j] / nn - xr[j] * xg / (nn * nn * nn);
+    }
+    return 0;
+}
+
+/*
  * Output gate of the block on each row of d values (one token and head):
  *
  *   y_i = o_i / sqrt(mean_j o_j^2 + eps) * w_i * g_i * sigmoid(g_i),

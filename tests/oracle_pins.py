@@ -625,6 +625,38 @@ def pin_l2norm_rows(orc):
     np.testing.assert_allclose(out * nrm, x, rtol=1e-13, atol=0)
 
 
+def pin_l2norm_bwd_finite_differences(orc):
+    """The reverse mode of the norm against central differences of
+    l2norm itself, for eps = 1e-6 and 0.3 (eps enters the Jacobian)."""
+    g = _rng(30)
+    x = g.standard_normal((3, 5)) * g.uniform(0.1, 3.0, (3, 1))
+    dy = g.standard_normal((3, 5))
+    for eps in (1e-6, 0.3):
+        dx = orc.l2norm_bwd(x, dy, eps=eps)
+        h = 1e-6
+        fd = np.zeros_like(x)
+        for r in range(3):
+            for c in range(5):
+                xp, xm = x.copy(), x.copy()
+                xp[r, c] += h
+                xm[r, c] -= h
+                fd[r, c] = np.sum(dy * (orc.l2norm(xp, eps=eps) - orc.l2norm(xm, eps=eps))) / (2 * h)
+        np.testing.assert_allclose(dx, fd, rtol=1e-6, atol=1e-8)
+
+
+def pin_l2norm_bwd_radial(orc):
+    """Closed form along the row: x . dx = eps (x . dy) / n^3 with
+    n = sqrt(|x|^2 + eps) (zero when eps = 0: the map ignores the length)."""
+    g = _rng(31)
+    x = g.standard_normal((4, 6))
+    dy = g.standard_normal((4, 6))
+    for eps in (0.0, 0.7):
+        dx = orc.l2norm_bwd(x, dy, eps=eps)
+        n = np.sqrt(np.sum(x * x, axis=-1) + eps)
+        np.testing.assert_allclose(np.sum(x * dx, axis=-1), eps * np.sum(x * dy, axis=-1) / n ** 3,
+                                   rtol=1e-12, atol=1e-14)
+
+
 # --- the block's output gate -------------------------------------------------
 def _silu(x):
     return x / (1.0 + np.exp(-x))
@@ -683,6 +715,7 @@ ALL_PINS = [
     pin_j_contraction, pin_k_kda, pin_gdn2_pure_decay, pin_gdn2_write_only,
     pin_gdn2_erase_axis, pin_gdn2_householder, pin_gdn_negative_beta,
     pin_l2norm_worked, pin_l2norm_eps, pin_l2norm_rows,
+    pin_l2norm_bwd_finite_differences, pin_l2norm_bwd_radial,
     pin_gate_worked, pin_gate_rms_and_eps, pin_gate_weight_axis,
     pin_bwd_finite_differences, pin_bwd_directional, pin_bwd_autograd_matrix_form,
     pin_bwd2_finite_differences, pin_bwd2_autograd_matrix_form,

@@ -39,6 +39,11 @@ MUTANTS = [
     ("l2norm_row_shift", "const double *xr = x + r * d;",
      "const double *xr = x + (r + 1 < n ? r + 1 : r) * d;"),
     ("l2norm_sign_lost", "out[r * d + c] = xr[c] * inv", "out[r * d + c] = fabs(xr[c]) * inv"),
+    ("l2norm_bwd_projection_dropped", "dx[r * d + j] = gr[j] / nn - xr[j] * xg / (nn * nn * nn);",
+     "dx[r * d + j] = gr[j] / nn;"),
+    ("l2norm_bwd_eps_outside_root", "const double nn = sqrt(ss + eps);",
+     "const double nn = sqrt(ss) + eps;"),
+    ("l2norm_bwd_wrong_power", "xr[j] * xg / (nn * nn * nn)", "xr[j] * xg / (nn * nn)"),
     ("gate_sum_not_mean", "sqrt(ss / (double)d + eps)", "sqrt(ss + eps)"),
     ("gate_eps_outside_root", "sqrt(ss / (double)d + eps)", "(sqrt(ss / (double)d) + eps)"),
     ("gate_sigmoid_not_silu", "const double gate = grow[c] / (1.0 + exp(-grow[c]));",
