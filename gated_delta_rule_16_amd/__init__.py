@@ -67,11 +67,17 @@ lib.gdr_chunk_bwd_workspace_size.restype = ctypes.c_size_t
 lib.gdr_chunk_bwd.argtypes = ([_I64] * 5 + [_E] + [_P] * 6 + [_E, _P, _P] + [_P] * 6 +
                               [_P, ctypes.c_size_t, _P])
 lib.gdr_chunk_bwd.restype = ctypes.c_int
+lib.gdr_chunk_bwd_ex.argtypes = ([_I64] * 5 + [_E] + [_P] * 6 + [_E, _P, _P] + [_P] * 6 +
+                                 [_P, ctypes.c_size_t, _U, _P])
+lib.gdr_chunk_bwd_ex.restype = ctypes.c_int
 lib.gdr2_chunk_bwd_workspace_size.argtypes = [_I64] * 5
 lib.gdr2_chunk_bwd_workspace_size.restype = ctypes.c_size_t
 lib.gdr2_chunk_bwd.argtypes = ([_I64] * 5 + [_E] + [_P] * 7 + [_E, _P, _P] + [_P] * 7 +
                                [_P, ctypes.c_size_t, _P])
 lib.gdr2_chunk_bwd.restype = ctypes.c_int
+lib.gdr2_chunk_bwd_ex.argtypes = ([_I64] * 5 + [_E] + [_P] * 7 + [_E, _P, _P] + [_P] * 7 +
+                                  [_P, ctypes.c_size_t, _U, _P])
+lib.gdr2_chunk_bwd_ex.restype = ctypes.c_int
 lib.gdr_chunk_fwd_split_workspace_size.argtypes = [_I64] * 5 + [_E, _I64]
 lib.gdr_chunk_fwd_split_workspace_size.restype = ctypes.c_size_t
 lib.gdr_chunk_fwd_split.argtypes = ([_I64] * 5 + [_E] + [_P] * 6 + [_E, _P, _P, _I64, _U, _P,
@@ -306,7 +312,7 @@ def gdr_chunk_bwd_workspace_size(B, T, H, Dk, Dv) -> int:
 
 
 def gdr_chunk_bwd(q, k, v, alpha, beta, s0, dout, ds_final=None, *, workspace=None,
-                  want_ds0=True, stream=None):
+                  want_ds0=True, l2norm_qk=False, stream=None):
     """Reverse mode of gdr_chunk_fwd: returns fp32 (dq, dk, dv, dalpha,
     dbeta, ds0) for dL/do = ``dout`` [B,T,H,Dv] (fp32 or bf16) and
     dL/dS_T = ``ds_final`` [B,H,Dv,Dk] fp32 or None.  Inputs as for
@@ -337,10 +343,13 @@ def gdr_chunk_bwd(q, k, v, alpha, beta, s0, dout, ds_final=None, *, workspace=No
     da = torch.empty((B, T, H), **f32)
     db = torch.empty((B, T, H), **f32)
     ds0 = torch.empty((B, H, Dv, Dk), **f32) if want_ds0 else None
-    _run("gdr_chunk_bwd", lib.gdr_chunk_bwd(
-        B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-        _ptr(s0), _DT[dout.dtype], _ptr(dout), _ptr(ds_final), _ptr(dq), _ptr(dk), _ptr(dv),
-        _ptr(da), _ptr(db), _ptr(ds0), _ptr(workspace), workspace.numel(), _stream(stream)))
+    args = (B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+            _ptr(s0), _DT[dout.dtype], _ptr(dout), _ptr(ds_final), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(da), _ptr(db), _ptr(ds0), _ptr(workspace), workspace.numel())
+    if l2norm_qk:
+        _run("gdr_chunk_bwd_ex", lib.gdr_chunk_bwd_ex(*args, GDR_L2NORM_QK, _stream(stream)))
+    else:
+        _run("gdr_chunk_bwd", lib.gdr_chunk_bwd(*args, _stream(stream)))
     return dq, dk, dv, da, db, ds0
 
 
@@ -350,7 +359,7 @@ def gdr2_chunk_bwd_workspace_size(B, T, H, Dk, Dv) -> int:
 
 
 def gdr2_chunk_bwd(q, k, v, alpha, erase, write, s0, dout, ds_final=None, *, workspace=None,
-                   want_ds0=True, stream=None):
+                   want_ds0=True, l2norm_qk=False, stream=None):
     """Reverse mode of gdr2_chunk_fwd: returns fp32 (dq, dk, dv, dalpha,
     derase, dwrite, ds0) for dL/do = ``dout`` [B,T,H,Dv] (fp32 or bf16) and
     dL/dS_T = ``ds_final`` [B,H,Dv,Dk] fp32 or None.  Inputs as for
@@ -380,9 +389,12 @@ def gdr2_chunk_bwd(q, k, v, alpha, erase, write, s0, dout, ds_final=None, *, wor
     de = torch.empty((B, T, H, Dk), **f32)
     dw = torch.empty((B, T, H, Dv), **f32)
     ds0 = torch.empty((B, H, Dv, Dk), **f32) if want_ds0 else None
-    _run("gdr2_chunk_bwd", lib.gdr2_chunk_bwd(
-        B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase),
-        _ptr(write), _ptr(s0), _DT[dout.dtype], _ptr(dout), _ptr(ds_final), _ptr(dq), _ptr(dk),
-        _ptr(dv), _ptr(da), _ptr(de), _ptr(dw), _ptr(ds0), _ptr(workspace), workspace.numel(),
-        _stream(stream)))
+    args = (B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase),
+            _ptr(write), _ptr(s0), _DT[dout.dtype], _ptr(dout), _ptr(ds_final), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(da), _ptr(de), _ptr(dw), _ptr(ds0), _ptr(workspace),
+            workspace.numel())
+    if l2norm_qk:
+        _run("gdr2_chunk_bwd_ex", lib.gdr2_chunk_bwd_ex(*args, GDR_L2NORM_QK, _stream(stream)))
+    else:
+        _run("gdr2_chunk_bwd", lib.gdr2_chunk_bwd(*args, _stream(stream)))
     return dq, dk, dv, da, de, dw, ds0

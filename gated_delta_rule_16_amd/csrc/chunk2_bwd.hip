@@ -83,6 +83,7 @@ struct Bwd2Params {
     const float *alpha_s, *beta_s;
     float *pbs, *pgs;              // [4 NRB][BTH]: per (row block, wave)
     float* pws;                    // [2 NRB][BTH]: per (row block, row tile)
+    bool l2norm;                   // q, k normalised on load (GDR_L2NORM_QK)
 };
 
 // LDS tables.  Pitches: key-side rows PK = 4 (mod 64), n x rows PR = 36,
@@ -282,13 +283,27 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         const int at = tr * L::PK + j0;
         float sg = 0.f;
         if constexpr (SC) sg = live ? safe_log2(x.as) : 0.f;
+        // GDR_L2NORM_QK: the 16 lanes of a token (one DPP row) hold its row
+        float kn = 1.f, qn = 1.f;
+        if (p.l2norm) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int y = 0; y < NC; ++y) {
+                const float kk = live ? packed<TIn>::at(x.k, y) : 0.f;
+                const float qq = (live && bwd) ? packed<TIn>::at(x.q, y) : 0.f;
+                sk += kk * kk;
+                sq += qq * qq;
+            }
+            kn = l2_inv(rsum16(sk));
+            qn = l2_inv(rsum16(sq));
+        }
 #pragma unroll
         for (int y0 = 0; y0 < NC; y0 += 4) {
             f32x4 kv, bv, ev, gv, qv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int y = y0 + e;
-                kv[e] = live ? packed<TIn>::at(x.k, y) : 0.f;
+                kv[e] = live ? packed<TIn>::at(x.k, y) * kn : 0.f;
                 if constexpr (SC) {
                     bv[e] = live ? x.bs : 0.f;
                     gv[e] = sg;
@@ -297,7 +312,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
                     gv[e] = live ? safe_log2(packed<TIn>::at(x.a, y)) : 0.f;
                 }
                 ev[e] = bv[e] * kv[e];
-                qv[e] = (live && bwd) ? packed<TIn>::at(x.q, y) : 0.f;
+                qv[e] = (live && bwd) ? packed<TIn>::at(x.q, y) * qn : 0.f;
             }
             *reinterpret_cast<f32x4*>(Ks + at + y0) = kv;
             *reinterpret_cast<f32x4*>(Bs + at + y0) = bv;
@@ -856,6 +871,67 @@ __global__ __launch_bounds__(256) void bwd_reduce_gates(int64_t n, const float* 
     dalpha[i] = g / fmaxf(alpha[i], 1.17549435e-38f);
 }
 
+// GDR_L2NORM_QK: the kernel's dq, dk are gradients with respect to q_hat,
+// k_hat; one wave per (token, head) row adds the row blocks' partials and
+// applies the norm's reverse mode, dx = (dx_hat - x_hat (x_hat . dx_hat)) / n
+// with n = sqrt(|x|^2 + eps).  G2: derase and dalpha too (elementwise).
+template <int NRB, int DK, typename TIn, bool G2>
+__global__ __launch_bounds__(256) void bwd_reduce_rows_norm(
+    int64_t rows, const float* __restrict__ pq, const float* __restrict__ pk,
+    const float* __restrict__ pb, const float* __restrict__ pg, const void* q, const void* k,
+    const void* alpha, float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ db,
+    float* __restrict__ da) {
+    constexpr int E = DK / 64;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;   // whole waves
+    const int lane = threadIdx.x & 63;
+    const int64_t n = rows * DK;
+    float dqh[E], dkh[E], qv[E], kv[E];
+    float sq = 0.f, sk = 0.f, tq = 0.f, tk = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int64_t i = row * DK + lane + 64 * e;
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int r = 0; r < NRB; ++r) {
+            a += pq[r * n + i];
+            b += pk[r * n + i];
+        }
+        dqh[e] = a;
+        dkh[e] = b;
+        qv[e] = ldf<TIn>(q, i);
+        kv[e] = ldf<TIn>(k, i);
+        sq += qv[e] * qv[e];
+        sk += kv[e] * kv[e];
+        tq += qv[e] * a;
+        tk += kv[e] * b;
+        if constexpr (G2) {
+            float c = 0.f, d = 0.f;
+#pragma unroll
+            for (int r = 0; r < NRB; ++r) {
+                c += pb[r * n + i];
+                d += pg[r * n + i];
+            }
+            db[i] = c;
+            da[i] = d / fmaxf(ldf<TIn>(alpha, i), 1.17549435e-38f);
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        sq += __shfl_xor(sq, m, 64);
+        sk += __shfl_xor(sk, m, 64);
+        tq += __shfl_xor(tq, m, 64);
+        tk += __shfl_xor(tk, m, 64);
+    }
+    const float iq = l2_inv(sq), ik = l2_inv(sk);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int64_t i = row * DK + lane + 64 * e;
+        dq[i] = iq * (dqh[e] - qv[e] * iq * (tq * iq));
+        dk[i] = ik * (dkh[e] - kv[e] * ik * (tk * ik));
+    }
+}
+
 template <int DK, int DV, typename TIn, typename TD, bool SC>
 hipError_t launch_main(const Bwd2Params& p, int64_t BH, hipStream_t st) {
     const size_t lds = sizeof(float) * BL3<DK>::TOTAL;
@@ -893,8 +969,15 @@ hipError_t launch_bwd2_t(const Bwd2Args& a) {
     p.pk = p.pq + NRB * BTH * DK;
     p.pb = p.pk + NRB * BTH * DK;
     p.pg = p.pb + NRB * BTH * DK;
+    p.l2norm = a.l2norm;
     hipError_t e = launch_main<DK, DV, TIn, TD, false>(p, BH, a.stream);
     if (e != hipSuccess) return e;
+    if (a.l2norm) {
+        hipLaunchKernelGGL((bwd_reduce_rows_norm<NRB, DK, TIn, true>),
+                           dim3((unsigned)((BTH + 3) / 4)), dim3(256), 0, a.stream, BTH, p.pq, p.pk,
+                           p.pb, p.pg, a.q, a.k, a.alpha, a.dq, a.dk, a.derase, a.dalpha);
+        return hipGetLastError();
+    }
     const int64_t nqk = BTH * DK;
     hipLaunchKernelGGL((bwd2_reduce<NRB, TIn>), dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0,
                        a.stream, nqk, p.pq, p.pk, p.pb, p.pg, a.alpha, a.dq, a.dk, a.derase,
@@ -927,11 +1010,18 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
     p.pbs = p.pk + NRB * BTH * DK;
     p.pgs = p.pbs + 4 * NRB * BTH;
     p.pws = p.pgs + 4 * NRB * BTH;
+    p.l2norm = a.l2norm;
     hipError_t e = launch_main<DK, DV, TIn, TD, true>(p, BH, a.stream);
     if (e != hipSuccess) return e;
     const int64_t nqk = BTH * DK;
-    hipLaunchKernelGGL((bwd_reduce_qk<NRB>), dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0,
-                       a.stream, nqk, p.pq, p.pk, a.dq, a.dk);
+    if (a.l2norm) {
+        hipLaunchKernelGGL((bwd_reduce_rows_norm<NRB, DK, TIn, false>),
+                           dim3((unsigned)((BTH + 3) / 4)), dim3(256), 0, a.stream, BTH, p.pq, p.pk,
+                           nullptr, nullptr, a.q, a.k, nullptr, a.dq, a.dk, nullptr, nullptr);
+    } else {
+        hipLaunchKernelGGL((bwd_reduce_qk<NRB>), dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0,
+                           a.stream, nqk, p.pq, p.pk, a.dq, a.dk);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_reduce_gates<NRB>), dim3((unsigned)((BTH + 255) / 256)), dim3(256), 0,

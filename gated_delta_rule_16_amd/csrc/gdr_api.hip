@@ -362,13 +362,16 @@ extern "C" size_t gdr_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, 
     return bwd_workspace_bytes(B, T, H, Dk, Dv);
 }
 
-extern "C" gdr_status_t gdr_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
-                                      gdr_dtype_t in_dt, const void* q, const void* k,
-                                      const void* v, const float* alpha, const float* beta,
-                                      const float* s0, gdr_dtype_t dout_dt, const void* dout,
-                                      const float* ds_final, float* dq, float* dk, float* dv,
-                                      float* dalpha, float* dbeta, float* ds0, void* workspace,
-                                      size_t workspace_bytes, hipStream_t stream) {
+extern "C" gdr_status_t gdr_chunk_bwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                         int64_t Dv, gdr_dtype_t in_dt, const void* q,
+                                         const void* k, const void* v, const float* alpha,
+                                         const float* beta, const float* s0,
+                                         gdr_dtype_t dout_dt, const void* dout,
+                                         const float* ds_final, float* dq, float* dk, float* dv,
+                                         float* dalpha, float* dbeta, float* ds0,
+                                         void* workspace, size_t workspace_bytes, uint32_t flags,
+                                         hipStream_t stream) {
+    if (!flags_ok(flags)) return GDR_ERR_UNSUPPORTED;
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0) return GDR_ERR_INVALID;
     if (!sizes_ok(B, T, H) || !sizes_ok(B * T * H, Dk > Dv ? Dk : Dv, 1)) return GDR_ERR_INVALID;
     if (!dtype_ok(in_dt) || !dtype_ok(dout_dt)) return GDR_ERR_UNSUPPORTED;
@@ -386,7 +389,8 @@ extern "C" gdr_status_t gdr_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t D
         return GDR_ERR_INVALID;
     if (!grid_ok(B * T * H * Dk)) return GDR_ERR_INVALID;
     if (workspace_bytes < bwd_workspace_bytes(B, T, H, Dk, Dv)) return GDR_ERR_INVALID;
-    BwdArgs a;
+    BwdArgs a{};
+    a.l2norm = (flags & GDR_L2NORM_QK) != 0;
     a.B = B;
     a.T = T;
     a.H = H;
@@ -413,6 +417,18 @@ extern "C" gdr_status_t gdr_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t D
     return from_hip(launch_chunk_bwd(a));
 }
 
+extern "C" gdr_status_t gdr_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                      gdr_dtype_t in_dt, const void* q, const void* k,
+                                      const void* v, const float* alpha, const float* beta,
+                                      const float* s0, gdr_dtype_t dout_dt, const void* dout,
+                                      const float* ds_final, float* dq, float* dk, float* dv,
+                                      float* dalpha, float* dbeta, float* ds0, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+    return gdr_chunk_bwd_ex(B, T, H, Dk, Dv, in_dt, q, k, v, alpha, beta, s0, dout_dt, dout,
+                            ds_final, dq, dk, dv, dalpha, dbeta, ds0, workspace, workspace_bytes,
+                            0u, stream);
+}
+
 extern "C" size_t gdr2_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                                 int64_t Dv) {
     if (B < 0 || T < 0 || H < 0 || !dims_ok(Dk, Dv)) return 0;
@@ -420,14 +436,16 @@ extern "C" size_t gdr2_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H,
     return bwd2_workspace_bytes(B, T, H, Dk, Dv);
 }
 
-extern "C" gdr_status_t gdr2_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
-                                       gdr_dtype_t in_dt, const void* q, const void* k,
-                                       const void* v, const void* alpha, const void* erase,
-                                       const void* write, const float* s0, gdr_dtype_t dout_dt,
-                                       const void* dout, const float* ds_final, float* dq,
-                                       float* dk, float* dv, float* dalpha, float* derase,
-                                       float* dwrite, float* ds0, void* workspace,
-                                       size_t workspace_bytes, hipStream_t stream) {
+extern "C" gdr_status_t gdr2_chunk_bwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                          int64_t Dv, gdr_dtype_t in_dt, const void* q,
+                                          const void* k, const void* v, const void* alpha,
+                                          const void* erase, const void* write, const float* s0,
+                                          gdr_dtype_t dout_dt, const void* dout,
+                                          const float* ds_final, float* dq, float* dk, float* dv,
+                                          float* dalpha, float* derase, float* dwrite,
+                                          float* ds0, void* workspace, size_t workspace_bytes,
+                                          uint32_t flags, hipStream_t stream) {
+    if (!flags_ok(flags)) return GDR_ERR_UNSUPPORTED;
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0) return GDR_ERR_INVALID;
     if (!sizes_ok(B, T, H) || !sizes_ok(B * T * H, Dk > Dv ? Dk : Dv, 1)) return GDR_ERR_INVALID;
     if (!dtype_ok(in_dt) || !dtype_ok(dout_dt)) return GDR_ERR_UNSUPPORTED;
@@ -444,7 +462,8 @@ extern "C" gdr_status_t gdr2_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t 
         return GDR_ERR_INVALID;
     if (!grid_ok(B * T * H * Dk)) return GDR_ERR_INVALID;
     if (workspace_bytes < bwd2_workspace_bytes(B, T, H, Dk, Dv)) return GDR_ERR_INVALID;
-    Bwd2Args a;
+    Bwd2Args a{};
+    a.l2norm = (flags & GDR_L2NORM_QK) != 0;
     a.B = B;
     a.T = T;
     a.H = H;
@@ -473,6 +492,19 @@ extern "C" gdr_status_t gdr2_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t 
     return from_hip(launch_chunk2_bwd(a));
 }
 
+extern "C" gdr_status_t gdr2_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                       gdr_dtype_t in_dt, const void* q, const void* k,
+                                       const void* v, const void* alpha, const void* erase,
+                                       const void* write, const float* s0, gdr_dtype_t dout_dt,
+                                       const void* dout, const float* ds_final, float* dq,
+                                       float* dk, float* dv, float* dalpha, float* derase,
+                                       float* dwrite, float* ds0, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    return gdr2_chunk_bwd_ex(B, T, H, Dk, Dv, in_dt, q, k, v, alpha, erase, write, s0, dout_dt,
+                             dout, ds_final, dq, dk, dv, dalpha, derase, dwrite, ds0, workspace,
+                             workspace_bytes, 0u, stream);
+}
+
 extern "C" const char* gdr_status_string(gdr_status_t s) {
     switch (s) {
         case GDR_OK: return "ok";
@@ -483,4 +515,4 @@ extern "C" const char* gdr_status_string(gdr_status_t s) {
     return "unknown status";
 }
 
-extern "C" int gdr_version(void) { return 300; }
+extern "C" int gdr_version(void) { return 400; }

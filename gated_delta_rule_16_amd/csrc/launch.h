@@ -50,6 +50,7 @@ struct GateArgs {
 struct BwdArgs {
     int64_t B, T, H, Dk, Dv;
     bool in_bf16, dout_bf16;
+    bool l2norm;            // q, k normalised on load (GDR_L2NORM_QK)
     const void *q, *k, *v, *dout;
     const float *alpha, *beta, *s0, *ds_final;
     float *dq, *dk, *dv, *dalpha, *dbeta, *ds0;
@@ -62,6 +63,7 @@ struct BwdArgs {
 struct Bwd2Args {
     int64_t B, T, H, Dk, Dv;
     bool in_bf16, dout_bf16;
+    bool l2norm;            // q, k normalised on load (GDR_L2NORM_QK)
     const void *q, *k, *v, *alpha, *erase, *write, *dout;
     const float *s0, *ds_final;
     float *dq, *dk, *dv, *dalpha, *derase, *dwrite, *ds0;

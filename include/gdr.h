@@ -377,6 +377,41 @@ gdr_status_t gdr2_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
                             void *workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
+/*
+ * Backward of the _ex forwards: the same arguments as gdr_chunk_bwd and
+ * gdr2_chunk_bwd plus `flags` (before the stream).  With GDR_L2NORM_QK the
+ * forward normalised q and k on load; q and k here are the same raw
+ * tensors, the kernels normalise them the same way, and dq, dk are the
+ * gradients with respect to the raw q and k: the rule's gradients with
+ * respect to q_hat, k_hat taken through the normalisation,
+ *
+ *   dx = (dx_hat - x_hat (x_hat . dx_hat)) / sqrt(|x|^2 + GDR_L2NORM_EPS)
+ *
+ * per token and head.  derase (GDN-2) is then with respect to b given
+ * k_hat.  flags == 0 is the plain call; another bit is GDR_ERR_UNSUPPORTED.
+ */
+gdr_status_t gdr_chunk_bwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                              int64_t Dv, gdr_dtype_t in_dt, const void *q,
+                              const void *k, const void *v, const float *alpha,
+                              const float *beta, const float *s0,
+                              gdr_dtype_t dout_dt, const void *dout,
+                              const float *ds_final, float *dq, float *dk,
+                              float *dv, float *dalpha, float *dbeta,
+                              float *ds0, void *workspace,
+                              size_t workspace_bytes, uint32_t flags,
+                              hipStream_t stream);
+
+gdr_status_t gdr2_chunk_bwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                               int64_t Dv, gdr_dtype_t in_dt, const void *q,
+                               const void *k, const void *v, const void *alpha,
+                               const void *erase, const void *write,
+                               const float *s0, gdr_dtype_t dout_dt,
+                               const void *dout, const float *ds_final,
+                               float *dq, float *dk, float *dv, float *dalpha,
+                               float *derase, float *dwrite, float *ds0,
+                               void *workspace, size_t workspace_bytes,
+                               uint32_t flags, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *gdr_status_string(gdr_status_t s);
 

@@ -30,6 +30,7 @@ def test_header_declares_the_three_operations():
               "gdr_output_gate", "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size",
               "gdr2_chunk_bwd", "gdr2_chunk_bwd_workspace_size",
               "gdr_chunk_fwd_split", "gdr_chunk_fwd_split_workspace_size",
+              "gdr_chunk_bwd_ex", "gdr2_chunk_bwd_ex",
               "gdr_status_string", "gdr_version"):
         assert n in names, names
 
@@ -268,3 +269,16 @@ def test_split_validation(gdr, kw, code):
 
 def test_split_empty(gdr):
     assert split(gdr, B=0, q=None, k=None, v=None, a=None, b=None, o=None, ws=None, wsb=0) == 0
+
+
+def test_bwd_ex_flags(gdr):
+    """The _ex backward calls reject unknown flag bits before anything else
+    and take GDR_L2NORM_QK like the plain call otherwise (empty call)."""
+    L = gdr.lib
+    z = [None] * 20
+    assert L.gdr_chunk_bwd_ex(0, 8, 1, 64, 64, 1, *z[:6], 1, *z[:2], *z[:6], None, 0, 2, None) == 2
+    assert L.gdr_chunk_bwd_ex(0, 8, 1, 64, 64, 1, *z[:6], 1, *z[:2], *z[:6], None, 0, 1, None) == 0
+    assert L.gdr2_chunk_bwd_ex(1, 8, 0, 64, 64, 1, *z[:7], 1, *z[:2], *z[:7], None, 0, 4,
+                               None) == 2
+    assert L.gdr2_chunk_bwd_ex(1, 8, 0, 64, 64, 1, *z[:7], 1, *z[:2], *z[:7], None, 0, 1,
+                               None) == 0
