@@ -92,6 +92,8 @@ class OracleLib:
         lib.oracle_l2norm_rows.restype = ctypes.c_int
         lib.oracle_l2norm_rows_bwd.argtypes = [L, L, P, P, ctypes.c_double, P]
         lib.oracle_l2norm_rows_bwd.restype = ctypes.c_int
+        lib.oracle_rmsnorm_gate_rows_bwd.argtypes = [L, L, P, P, P, ctypes.c_double, P, P, P, P]
+        lib.oracle_rmsnorm_gate_rows_bwd.restype = ctypes.c_int
         lib.oracle_rmsnorm_gate_rows.argtypes = [L, L, P, P, P, ctypes.c_double, P]
         lib.oracle_rmsnorm_gate_rows.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -248,6 +250,22 @@ class OracleLib:
             raise RuntimeError(f"oracle_rmsnorm_gate_rows failed ({rc})")
         return y
 
+    def rmsnorm_gate_bwd(self, o, g, w, dy, eps=1e-6):
+        """Reverse mode of rmsnorm_gate (``oracle_rmsnorm_gate_rows_bwd``):
+        returns float64 (do, dg, dw), dw summed over all rows (None when w is
+        None)."""
+        o, g, w, dy = _f64(o), _f64(g), _f64(w), _f64(dy)
+        assert o.shape == g.shape == dy.shape and o.ndim >= 1
+        d = o.shape[-1]
+        assert w is None or w.shape == (d,)
+        do, dg = np.empty_like(o), np.empty_like(o)
+        dw = None if w is None else np.empty(d)
+        rc = self.lib.oracle_rmsnorm_gate_rows_bwd(o.size // d, d, _p(o), _p(g), _p(w),
+                                                   float(eps), _p(dy), _p(do), _p(dg), _p(dw))
+        if rc:
+            raise RuntimeError(f"oracle_rmsnorm_gate_rows_bwd failed ({rc})")
+        return do, dg, dw
+
 
 _default = None
 
@@ -323,6 +341,13 @@ def rmsnorm_gate(*a, **kw):
 
 
 rmsnorm_gate.__doc__ = OracleLib.rmsnorm_gate.__doc__
+
+
+def rmsnorm_gate_bwd(*a, **kw):
+    return default().rmsnorm_gate_bwd(*a, **kw)
+
+
+rmsnorm_gate_bwd.__doc__ = OracleLib.rmsnorm_gate_bwd.__doc__
 
 
 def err_rms(x_hat, x) -> float:

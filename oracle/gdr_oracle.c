@@ -396,6 +396,46 @@ int oracle_rmsnorm_gate_rows(long n, long d, const double *o, const double *g,
 }
 
 /*
+ * Reverse mode of oracle_rmsnorm_gate_rows by the chain rule, per row with
+ * r = 1 / sqrt(mean_j o_j^2 + eps), n = r o, s(g) = g sigmoid(g):
+ *
+ *   y_i = n_i w_i s(g_i)
+ *   dn_i = dy_i w_i s(g_i)
+ *   do_j = sum_i dn_i dn_i/do_j = sum_i dn_i (r delta_ij - o_i o_j r^3 / d)
+ *   dg_i = dy_i n_i w_i s'(g_i),  s'(g) = sigmoid(g) (1 + g (1 - sigmoid(g)))
+ *   dw_i = sum over rows of dy_i n_i s(g_i)   (when w is given; dw may be
+ *          NULL; w NULL means ones)
+ */
+int oracle_rmsnorm_gate_rows_bwd(long n, long d, const double *o, const double *g,
+                                 const double *w, double eps, const double *dy, double *dout,
+                                 double *dg, double *dw) {
+    if (n < 0 || d <= 0 || !(eps >= 0.0)) return 1;
+    if (dw)
+        for (long c = 0; c < d; ++c) dw[c] = 0.0;
+    for (long rr = 0; rr < n; ++rr) {
+        const double *orow = o + rr * d, *grow = g + rr * d, *dyr = dy + rr * d;
+        double ss = 0.0;
+        for (long c = 0; c < d; ++c) ss += orow[c] * orow[c];
+        const double r = 1.0 / sqrt(ss / (double)d + eps);
+        double on = 0.0;   /* sum_i dn_i o_i */
+        for (long i = 0; i < d; ++i) {
+            const double sg = 1.0 / (1.0 + exp(-grow[i]));
+            const double wi = w ? w[i] : 1.0;
+            const double dn = dyr[i] * wi * grow[i] * sg;
+            on += dn * orow[i];
+            dg[rr * d + i] = dyr[i] * orow[i] * r * wi * sg * (1.0 + grow[i] * (1.0 - sg));
+            if (dw) dw[i] += dyr[i] * orow[i] * r * grow[i] * sg;
+        }
+        for (long j = 0; j < d; ++j) {
+            const double sg = 1.0 / (1.0 + exp(-grow[j]));
+            const double dn = dyr[j] * (w ? w[j] : 1.0) * grow[j] * sg;
+            dout[rr * d + j] = dn * r - orow[j] * on * r * r * r / (double)d;
+        }
+    }
+    return 0;
+}
+
+/*
  * Reverse mode of Gated Delta Rule-2 (the derivative of oracle_gdn2_fwd,
  * token by token by the chain rule; the GDN-2 summary notes that its
  * chunked backward must carry the gates inside the dot products).  Per

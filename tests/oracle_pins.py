@@ -706,6 +706,54 @@ def pin_gate_weight_axis(orc):
     np.testing.assert_allclose(y3[1, 3] / y2[1, 3], _silu(g2[1, 3]) / _silu(g[1, 3]), rtol=1e-13)
 
 
+def pin_gate_bwd_finite_differences(orc):
+    """The output gate's reverse mode against central differences of the
+    forward in o, g and w, with eps = 1e-6 and 0.5 (eps enters the root)."""
+    rng = _rng(32)
+    o = rng.standard_normal((3, 5))
+    g = rng.standard_normal((3, 5)) * 2.0
+    w = rng.uniform(0.5, 1.5, 5)
+    dy = rng.standard_normal((3, 5))
+    h = 1e-6
+    for eps in (1e-6, 0.5):
+        do, dg, dw = orc.rmsnorm_gate_bwd(o, g, w, dy, eps=eps)
+        f = lambda oo, gg, ww: np.sum(dy * orc.rmsnorm_gate(oo, gg, ww, eps=eps))
+        for x, grad, which in ((o, do, 0), (g, dg, 1)):
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = [o, g, w]
+                args_m = [o, g, w]
+                args_p[which], args_m[which] = xp, xm
+                fd[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+            np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-8)
+        fdw = np.zeros_like(w)
+        for c in range(5):
+            wp, wm = w.copy(), w.copy()
+            wp[c] += h
+            wm[c] -= h
+            fdw[c] = (f(o, g, wp) - f(o, g, wm)) / (2 * h)
+        np.testing.assert_allclose(dw, fdw, rtol=1e-6, atol=1e-8)
+    _, _, dw_none = orc.rmsnorm_gate_bwd(o, g, None, dy)
+    assert dw_none is None
+
+
+def pin_gate_bwd_scale_invariance(orc):
+    """With eps = 0 the normalised row ignores the row's scale, so do is
+    orthogonal to o in every row; and do scales as 1 / c when o is scaled
+    by c."""
+    rng = _rng(33)
+    o = rng.standard_normal((4, 6))
+    g = rng.standard_normal((4, 6))
+    dy = rng.standard_normal((4, 6))
+    do, _, _ = orc.rmsnorm_gate_bwd(o, g, None, dy, eps=0.0)
+    np.testing.assert_allclose(np.sum(o * do, axis=-1), 0.0, atol=1e-13)
+    do3, _, _ = orc.rmsnorm_gate_bwd(3.0 * o, g, None, dy, eps=0.0)
+    np.testing.assert_allclose(do3, do / 3.0, rtol=1e-12, atol=1e-15)
+
+
 ALL_PINS = [
     pin_golden_gdn, pin_golden_step, pin_golden_gdn2,
     pin_exact_matrix_form_gdn, pin_exact_matrix_form_gdn2,
@@ -717,6 +765,7 @@ ALL_PINS = [
     pin_l2norm_worked, pin_l2norm_eps, pin_l2norm_rows,
     pin_l2norm_bwd_finite_differences, pin_l2norm_bwd_radial,
     pin_gate_worked, pin_gate_rms_and_eps, pin_gate_weight_axis,
+    pin_gate_bwd_finite_differences, pin_gate_bwd_scale_invariance,
     pin_bwd_finite_differences, pin_bwd_directional, pin_bwd_autograd_matrix_form,
     pin_bwd2_finite_differences, pin_bwd2_autograd_matrix_form,
 ]

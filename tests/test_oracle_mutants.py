@@ -49,6 +49,14 @@ MUTANTS = [
     ("gate_sigmoid_not_silu", "const double gate = grow[c] / (1.0 + exp(-grow[c]));",
      "const double gate = 1.0 / (1.0 + exp(-grow[c]));"),
     ("gate_weight_by_row", "(w ? w[c] : 1.0)", "(w ? w[r < d ? r : 0] : 1.0)"),
+    ("gate_bwd_projection_dropped", "dout[rr * d + j] = dn * r - orow[j] * on * r * r * r / (double)d;",
+     "dout[rr * d + j] = dn * r;"),
+    ("gate_bwd_silu_derivative_as_sigmoid",
+     "dg[rr * d + i] = dyr[i] * orow[i] * r * wi * sg * (1.0 + grow[i] * (1.0 - sg));",
+     "dg[rr * d + i] = dyr[i] * orow[i] * r * wi * sg;"),
+    ("gate_bwd_dw_without_gate", "if (dw) dw[i] += dyr[i] * orow[i] * r * grow[i] * sg;",
+     "if (dw) dw[i] += dyr[i] * orow[i] * r;"),
+    ("gate_bwd_sum_not_mean", "orow[j] * on * r * r * r / (double)d", "orow[j] * on * r * r * r"),
     ("bwd_dalpha_missing_read_term", "dat += gs - be * dc * u;", "dat += gs;"),
     ("bwd_dk_missing_read_path", "x += G[i * Dk + j] * cv[i] - a * be * dcv[i] * Sp[i * Dk + j];",
      "x += G[i * Dk + j] * cv[i];"),
