@@ -12,6 +12,7 @@ Functions mirror the C calls:
     gdr_recurrent_step(q, k, v, alpha, beta, state, ...)         -> o
     gdr2_chunk_fwd(q, k, v, alpha, erase, write, s0=None, ...)   -> (o, s_final)
     gdr_output_gate(o, g, w=None, eps=1e-6, ...)                -> y
+    gdr_output_gate_bwd(o, g, w, dy, eps=1e-6, ...)             -> (do, dg, dw)
     gdr_chunk_bwd(q, k, v, alpha, beta, s0, dout, ds_final=None)
         -> (dq, dk, dv, dalpha, dbeta, ds0)
     gdr2_chunk_bwd(q, k, v, alpha, erase, write, s0, dout, ds_final=None)
@@ -31,6 +32,7 @@ __all__ = ["gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd", "gdr_output_
            "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size",
            "gdr2_chunk_bwd", "gdr2_chunk_bwd_workspace_size",
            "gdr_chunk_fwd_split", "gdr_chunk_fwd_split_workspace_size",
+           "gdr_output_gate_bwd", "gdr_output_gate_bwd_workspace_size",
            "GdrError", "status_string", "lib", "LIB_PATH", "GDR_F32",
            "GDR_BF16", "GDR_L2NORM_QK"]
 
@@ -83,6 +85,11 @@ lib.gdr_chunk_fwd_split_workspace_size.restype = ctypes.c_size_t
 lib.gdr_chunk_fwd_split.argtypes = ([_I64] * 5 + [_E] + [_P] * 6 + [_E, _P, _P, _I64, _U, _P,
                                     ctypes.c_size_t, _P])
 lib.gdr_chunk_fwd_split.restype = ctypes.c_int
+lib.gdr_output_gate_bwd_workspace_size.argtypes = [_I64] * 3
+lib.gdr_output_gate_bwd_workspace_size.restype = ctypes.c_size_t
+lib.gdr_output_gate_bwd.argtypes = ([_I64] * 3 + [_E, _P, _E, _P, _P, ctypes.c_float, _E, _P] +
+                                    [_P] * 4 + [ctypes.c_size_t, _P])
+lib.gdr_output_gate_bwd.restype = ctypes.c_int
 lib.gdr_status_string.argtypes = [ctypes.c_int]
 lib.gdr_status_string.restype = ctypes.c_char_p
 lib.gdr_version.restype = ctypes.c_int
@@ -398,3 +405,38 @@ def gdr2_chunk_bwd(q, k, v, alpha, erase, write, s0, dout, ds_final=None, *, wor
     else:
         _run("gdr2_chunk_bwd", lib.gdr2_chunk_bwd(*args, _stream(stream)))
     return dq, dk, dv, da, de, dw, ds0
+
+
+def gdr_output_gate_bwd_workspace_size(N, H, Dv) -> int:
+    """Bytes of device workspace gdr_output_gate_bwd needs for dw."""
+    return int(lib.gdr_output_gate_bwd_workspace_size(N, H, Dv))
+
+
+def gdr_output_gate_bwd(o, g, w, dy, eps=1e-6, *, want_dw=True, workspace=None, stream=None):
+    """Reverse mode of gdr_output_gate: o, g, dy [..., H, Dv] (fp32 or bf16
+    each), w [Dv] fp32 or None (ones).  Returns fp32 (do, dg, dw); dw [Dv]
+    is None when ``want_dw`` is False."""
+    if o.dim() < 2:
+        raise ValueError("o must be [..., H, Dv]")
+    H, Dv = o.shape[-2], o.shape[-1]
+    N = o.numel() // (H * Dv) if o.numel() else 0
+    for name, t in (("o", o), ("g", g), ("dy", dy)):
+        if t.dtype not in _DT:
+            raise TypeError(f"{name} must be float32 or bfloat16")
+        _check(name, t, t.dtype, tuple(o.shape))
+    if w is not None:
+        _check("w", w, torch.float32, (Dv,))
+    f32 = dict(dtype=torch.float32, device=o.device)
+    do = torch.empty(o.shape, **f32)
+    dg = torch.empty(o.shape, **f32)
+    dw = torch.empty((Dv,), **f32) if want_dw else None
+    if dw is not None and workspace is None:
+        workspace = torch.empty(max(gdr_output_gate_bwd_workspace_size(N, H, Dv), 16),
+                                dtype=torch.uint8, device=o.device)
+    if workspace is not None:
+        _check("workspace", workspace, torch.uint8)
+    _run("gdr_output_gate_bwd", lib.gdr_output_gate_bwd(
+        N, H, Dv, _DT[o.dtype], _ptr(o), _DT[g.dtype], _ptr(g), _ptr(w), float(eps),
+        _DT[dy.dtype], _ptr(dy), _ptr(do), _ptr(dg), _ptr(dw), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream(stream)))
+    return do, dg, dw

@@ -127,7 +127,154 @@ hipError_t launch_gate_d(const GateArgs& a) {
     return a.o_bf16 ? launch_gate_g<DV, bf16_t>(a) : launch_gate_g<DV, float>(a);
 }
 
+// Reverse mode of the gate, per row with r = 1 / sqrt(mean o^2 + eps),
+// n = r o, s(g) = g sigmoid(g):
+//
+//   dn = dy w s(g),  do = r (dn - n mean(n dn)),
+//   dg = dy n w sigmoid(g) (1 + g (1 - sigmoid(g))),
+//   dw = sum over rows of dy n s(g).
+//
+// Same lane layout as the forward.  dw: each lane sums its 4 channels over
+// the rows it visits; lanes of a wave that share channels, then the four
+// waves, are added in the workgroup, which writes one partial row of DV
+// floats; gate_dw_reduce adds the workgroups' rows.
+template <int DV, typename TO, typename TG, typename TD>
+__global__ __launch_bounds__(256) void output_gate_bwd_kernel(int64_t rows, const TO* o,
+                                                              const TG* __restrict__ g,
+                                                              const float* __restrict__ w,
+                                                              float eps, const TD* dy,
+                                                              float* __restrict__ dout,
+                                                              float* __restrict__ dg,
+                                                              float* __restrict__ dwp) {
+    constexpr int LPR = DV / 4;
+    constexpr int RPW = 64 / LPR;
+    constexpr int RPB = 4 * RPW;
+    __shared__ f32x4 red[4][LPR];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int c0 = 4 * (lane % LPR);
+    const int64_t rsub = wv * RPW + lane / LPR;
+    f32x4 wv4 = {1.f, 1.f, 1.f, 1.f};
+    if (w) wv4 = *reinterpret_cast<const f32x4*>(w + c0);
+    f32x4 dwacc = {0.f, 0.f, 0.f, 0.f};
+    const int64_t stride = (int64_t)gridDim.x * RPB;
+    for (int64_t r = (int64_t)blockIdx.x * RPB + rsub; r - rsub < rows; r += stride) {
+        // every lane runs the row reductions; rows past the end contribute 0
+        const bool live = r < rows;
+        f32x4 ov = {0.f, 0.f, 0.f, 0.f}, gv = ov, yv = ov;
+        if (live) {
+            ov = v4<TO>::ld(o + r * DV + c0);
+            gv = v4<TG>::ld(g + r * DV + c0);
+            yv = v4<TD>::ld(dy + r * DV + c0);
+        }
+        float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
+        ss += dpp_mov<0xB1>(ss);
+        ss += dpp_mov<0x4E>(ss);
+        ss += dpp_mov<0x141>(ss);
+        ss += dpp_mov<0x140>(ss);
+        if constexpr (LPR == 32) ss += __shfl_xor(ss, 16, 64);
+        const float rr = rsqrtf(ss * (1.f / DV) + eps);
+        f32x4 nv, dn, sgm;
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sgm[e] = __builtin_amdgcn_rcpf(1.f + __expf(-gv[e]));
+            nv[e] = ov[e] * rr;
+            dn[e] = yv[e] * wv4[e] * gv[e] * sgm[e];
+            t += nv[e] * dn[e];
+        }
+        t += dpp_mov<0xB1>(t);
+        t += dpp_mov<0x4E>(t);
+        t += dpp_mov<0x141>(t);
+        t += dpp_mov<0x140>(t);
+        if constexpr (LPR == 32) t += __shfl_xor(t, 16, 64);
+        const float tm = t * (1.f / DV);
+        if (live) {
+            f32x4 dov, dgv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dov[e] = rr * (dn[e] - nv[e] * tm);
+                dgv[e] = yv[e] * nv[e] * wv4[e] * sgm[e] * (1.f + gv[e] * (1.f - sgm[e]));
+                dwacc[e] += yv[e] * nv[e] * gv[e] * sgm[e];
+            }
+            st4(dout + r * DV + c0, dov);
+            st4(dg + r * DV + c0, dgv);
+        }
+    }
+    if (!dwp) return;
+    // lanes of this wave with the same channels: lane % LPR
+#pragma unroll
+    for (int m = LPR; m < 64; m <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dwacc[e] += __shfl_xor(dwacc[e], m, 64);
+    if (lane < LPR) red[wv][lane] = dwacc;
+    __syncthreads();
+    if (threadIdx.x < LPR) {
+        f32x4 sacc = red[0][threadIdx.x];
+#pragma unroll
+        for (int k = 1; k < 4; ++k) sacc += red[k][threadIdx.x];
+        *reinterpret_cast<f32x4*>(dwp + (int64_t)blockIdx.x * DV + 4 * threadIdx.x) = sacc;
+    }
+}
+
+// dw[c] = sum of the workgroups' partial rows
+__global__ __launch_bounds__(256) void gate_dw_reduce(const float* __restrict__ dwp, int nblk,
+                                                     int dv, float* __restrict__ dw) {
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= dv) return;
+    float sacc = 0.f;
+    for (int b = 0; b < nblk; ++b) sacc += dwp[(int64_t)b * dv + c];
+    dw[c] = sacc;
+}
+
+constexpr int GATE_BWD_MAX_BLOCKS = 1024;
+
+template <int DV>
+int64_t gate_bwd_blocks(int64_t rows) {
+    constexpr int RPB = 4 * (64 / (DV / 4));
+    int64_t blocks = (rows + RPB - 1) / RPB;
+    return blocks < GATE_BWD_MAX_BLOCKS ? blocks : GATE_BWD_MAX_BLOCKS;
+}
+
+template <int DV, typename TO, typename TG, typename TD>
+hipError_t launch_gate_bwd_t(const GateBwdArgs& a) {
+    const int64_t rows = a.N * a.H;
+    const int64_t blocks = gate_bwd_blocks<DV>(rows);
+    float* dwp = a.dw ? reinterpret_cast<float*>(a.workspace) : nullptr;
+    hipLaunchKernelGGL((output_gate_bwd_kernel<DV, TO, TG, TD>), dim3((unsigned)blocks), dim3(256),
+                       0, a.stream, rows, (const TO*)a.o, (const TG*)a.g, a.w, a.eps,
+                       (const TD*)a.dy, a.dout, a.dg, dwp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.dw) return e;
+    hipLaunchKernelGGL(gate_dw_reduce, dim3(1), dim3(DV), 0, a.stream, dwp, (int)blocks, DV, a.dw);
+    return hipGetLastError();
+}
+
+template <int DV, typename TO, typename TG>
+hipError_t launch_gate_bwd_y(const GateBwdArgs& a) {
+    return a.dy_bf16 ? launch_gate_bwd_t<DV, TO, TG, bf16_t>(a)
+                     : launch_gate_bwd_t<DV, TO, TG, float>(a);
+}
+
+template <int DV, typename TO>
+hipError_t launch_gate_bwd_g(const GateBwdArgs& a) {
+    return a.g_bf16 ? launch_gate_bwd_y<DV, TO, bf16_t>(a) : launch_gate_bwd_y<DV, TO, float>(a);
+}
+
+template <int DV>
+hipError_t launch_gate_bwd_d(const GateBwdArgs& a) {
+    return a.o_bf16 ? launch_gate_bwd_g<DV, bf16_t>(a) : launch_gate_bwd_g<DV, float>(a);
+}
+
 }  // namespace
+
+size_t gate_bwd_workspace_bytes(int64_t rows, int64_t Dv) {
+    const int64_t blocks = Dv == 128 ? gate_bwd_blocks<128>(rows) : gate_bwd_blocks<64>(rows);
+    return sizeof(float) * (size_t)(blocks * Dv);
+}
+
+hipError_t launch_output_gate_bwd(const GateBwdArgs& a) {
+    return a.Dv == 128 ? launch_gate_bwd_d<128>(a) : launch_gate_bwd_d<64>(a);
+}
 
 hipError_t launch_output_gate(const GateArgs& a) {
     return a.Dv == 128 ? launch_gate_d<128>(a) : launch_gate_d<64>(a);

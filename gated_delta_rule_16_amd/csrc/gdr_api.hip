@@ -355,6 +355,51 @@ extern "C" gdr_status_t gdr_output_gate(int64_t N, int64_t H, int64_t Dv, gdr_dt
     return from_hip(launch_output_gate(a));
 }
 
+extern "C" size_t gdr_output_gate_bwd_workspace_size(int64_t N, int64_t H, int64_t Dv) {
+    if (N < 0 || H < 0 || (Dv != 64 && Dv != 128) || !sizes_ok(N, H, Dv)) return 0;
+    return gate_bwd_workspace_bytes(N * H, Dv);
+}
+
+extern "C" gdr_status_t gdr_output_gate_bwd(int64_t N, int64_t H, int64_t Dv, gdr_dtype_t o_dt,
+                                            const void* o, gdr_dtype_t g_dt, const void* g,
+                                            const float* w, float eps, gdr_dtype_t dy_dt,
+                                            const void* dy, float* dout, float* dg, float* dw,
+                                            void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+    if (N < 0 || H < 0 || Dv < 0) return GDR_ERR_INVALID;
+    if (!sizes_ok(N, H, Dv)) return GDR_ERR_INVALID;
+    if (!dtype_ok(o_dt) || !dtype_ok(g_dt) || !dtype_ok(dy_dt)) return GDR_ERR_UNSUPPORTED;
+    if (Dv != 64 && Dv != 128) return GDR_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f) || eps > 3.0e38f) return GDR_ERR_INVALID;
+    if (!opt_ok(w) || !opt_ok(dw)) return GDR_ERR_INVALID;
+    if (N == 0 || H == 0) {
+        // no rows: dw is zero
+        if (dw) return from_hip(launch_state_copy(nullptr, dw, Dv, stream));
+        return GDR_OK;
+    }
+    if (!ptrs_ok({o, g, dy, dout, dg})) return GDR_ERR_INVALID;
+    if (dw && (!ptrs_ok({workspace}) || workspace_bytes < gate_bwd_workspace_bytes(N * H, Dv)))
+        return GDR_ERR_INVALID;
+    GateBwdArgs a{};
+    a.N = N;
+    a.H = H;
+    a.Dv = Dv;
+    a.o_bf16 = o_dt == GDR_BF16;
+    a.g_bf16 = g_dt == GDR_BF16;
+    a.dy_bf16 = dy_dt == GDR_BF16;
+    a.o = o;
+    a.g = g;
+    a.dy = dy;
+    a.w = w;
+    a.eps = eps;
+    a.dout = dout;
+    a.dg = dg;
+    a.dw = dw;
+    a.workspace = workspace;
+    a.stream = stream;
+    return from_hip(launch_output_gate_bwd(a));
+}
+
 extern "C" size_t gdr_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                                int64_t Dv) {
     if (B < 0 || T < 0 || H < 0 || !dims_ok(Dk, Dv)) return 0;

@@ -46,6 +46,19 @@ struct GateArgs {
     hipStream_t stream;
 };
 
+// Backward of the output gate: o, g, dy [N, H, Dv]; dout, dg fp32; dw [Dv]
+// fp32 or NULL (then no workspace).
+struct GateBwdArgs {
+    int64_t N, H, Dv;
+    bool o_bf16, g_bf16, dy_bf16;
+    const void *o, *g, *dy;
+    const float* w;
+    float eps;
+    float *dout, *dg, *dw;
+    void* workspace;
+    hipStream_t stream;
+};
+
 // Backward of the scalar-gate rule; gradients fp32, workspace from the caller.
 struct BwdArgs {
     int64_t B, T, H, Dk, Dv;
@@ -92,6 +105,8 @@ size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t 
 hipError_t launch_chunk2_bwd(const Bwd2Args& a);
 size_t bwd2_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv);
 hipError_t launch_output_gate(const GateArgs& a);
+hipError_t launch_output_gate_bwd(const GateBwdArgs& a);
+size_t gate_bwd_workspace_bytes(int64_t rows, int64_t Dv);
 // fp32 inputs: VALU kernels, both rules.
 hipError_t launch_chunk_f32(const ChunkArgs& a);
 // bf16 inputs, scalar gates: bf16 MFMA kernel.

@@ -10,7 +10,8 @@
  * plus their _ex variants (q, k L2-normalised on load), a sequence-split
  * form of the first for few long sequences (gdr_chunk_fwd_split), the block's
  * output gate on their result (gdr_output_gate) and the reverse modes of
- * the two chunkwise forwards (gdr_chunk_bwd, gdr2_chunk_bwd).
+ * the two chunkwise forwards and of the gate (gdr_chunk_bwd, gdr2_chunk_bwd,
+ * gdr_output_gate_bwd).
  *
  * The rule ("Gated Delta Networks", agihunt.info, "Method"; review of GDN on
  * meaningful96.github.io, section 3.4; inputs and outputs from its
@@ -285,6 +286,36 @@ gdr_status_t gdr_output_gate(int64_t N, int64_t H, int64_t Dv, gdr_dtype_t o_dt,
                              const void *o, gdr_dtype_t g_dt, const void *g,
                              const float *w, float eps, gdr_dtype_t out_dt,
                              void *y, hipStream_t stream);
+
+/*
+ * Reverse mode of gdr_output_gate: with r = 1 / sqrt(mean o^2 + eps),
+ * n = r o and s(g) = g sigmoid(g) per row, given dy = dL/dy,
+ *
+ *   dout = r (dn - n mean(n dn)),   dn = dy w s(g)
+ *   dg   = dy n w sigmoid(g) (1 + g (1 - sigmoid(g)))
+ *   dw   = sum over all rows of dy n s(g)
+ *
+ *   N, H, Dv, o_dt, o, g_dt, g, w, eps  as for gdr_output_gate (w NULL: ones)
+ *   dy_dt, dy   [N, H, Dv] dL/dy
+ *   dout, dg    [N, H, Dv] fp32 (written)
+ *   dw          [Dv] fp32 (written), or NULL: not computed, no workspace
+ *   workspace   when dw is given: device memory of at least
+ *               gdr_output_gate_bwd_workspace_size(N, H, Dv) bytes (the
+ *               workgroups' partial sums of dw, at most 1024 rows of Dv
+ *               floats), 16-byte aligned, owned by the caller
+ *
+ * One pass over o, g and dy plus a small reduction for dw.  All tensors
+ * 16-byte aligned.  fp32 arithmetic; N H == 0 writes dw = 0.
+ */
+size_t gdr_output_gate_bwd_workspace_size(int64_t N, int64_t H, int64_t Dv);
+
+gdr_status_t gdr_output_gate_bwd(int64_t N, int64_t H, int64_t Dv,
+                                 gdr_dtype_t o_dt, const void *o,
+                                 gdr_dtype_t g_dt, const void *g,
+                                 const float *w, float eps, gdr_dtype_t dy_dt,
+                                 const void *dy, float *dout, float *dg,
+                                 float *dw, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Reverse mode of gdr_chunk_fwd (the scalar-gate rule): the gradients of a

@@ -31,6 +31,7 @@ def test_header_declares_the_three_operations():
               "gdr2_chunk_bwd", "gdr2_chunk_bwd_workspace_size",
               "gdr_chunk_fwd_split", "gdr_chunk_fwd_split_workspace_size",
               "gdr_chunk_bwd_ex", "gdr2_chunk_bwd_ex",
+              "gdr_output_gate_bwd", "gdr_output_gate_bwd_workspace_size",
               "gdr_status_string", "gdr_version"):
         assert n in names, names
 
@@ -282,3 +283,36 @@ def test_bwd_ex_flags(gdr):
                                None) == 2
     assert L.gdr2_chunk_bwd_ex(1, 8, 0, 64, 64, 1, *z[:7], 1, *z[:2], *z[:7], None, 0, 1,
                                None) == 0
+
+
+def gate_bwd(gdr, N=4, H=2, Dv=64, odt=0, o=A16, gdt=1, g=A16, w=None, eps=1e-6, dyt=1, dy=A16,
+             do=A16, dg=A16, dw=A16, ws=A16, wsb=None):
+    if wsb is None:
+        wsb = gdr.lib.gdr_output_gate_bwd_workspace_size(N, H, Dv)
+    return gdr.lib.gdr_output_gate_bwd(N, H, Dv, odt, o, gdt, g, w, eps, dyt, dy, do, dg, dw, ws,
+                                       wsb, None)
+
+
+def test_gate_bwd_workspace_size(gdr):
+    """One partial row of Dv floats per workgroup, at most 1024 workgroups;
+    a workgroup takes 8 rows (Dv = 128) or 16 (Dv = 64)."""
+    f = gdr.lib.gdr_output_gate_bwd_workspace_size
+    assert f(100, 3, 128) == 4 * 128 * 38
+    assert f(100, 3, 64) == 4 * 64 * 19
+    assert f(10 ** 6, 16, 128) == 4 * 128 * 1024
+    assert f(4, 2, 96) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=None), 1), (dict(dy=BAD), 1), (dict(do=None), 1), (dict(dg=None), 1),
+    (dict(w=BAD), 1), (dict(dw=BAD), 1), (dict(ws=None), 1), (dict(wsb=16), 1),
+    (dict(eps=-1.0), 1), (dict(N=-1), 1), (dict(Dv=96), 2), (dict(dyt=3), 2),
+])
+def test_gate_bwd_validation(gdr, kw, code):
+    assert gate_bwd(gdr, **kw) == code
+
+
+def test_gate_bwd_no_workspace_without_dw(gdr):
+    """dw NULL needs no workspace: only the pointer checks of the tensors
+    remain (a misaligned dy is still rejected)."""
+    assert gate_bwd(gdr, dw=None, ws=None, wsb=0, dy=BAD) == 1
