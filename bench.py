@@ -24,6 +24,7 @@ The JSON line (stdout, last line) carries:
                      normalise pass in PyTorch followed by the plain call
   output_gate        gdr_output_gate (RMSNorm x SiLU gate) on the B8 T4096 H16
                      d128 output: fp32 o, bf16 gate, bf16 y; GB/s of HBM
+  output_gate_bwd    gdr_output_gate_bwd on the same gate: GB/s of HBM
   backward           gdr_chunk_bwd on the B8 H16 T4096 d128 workload (bf16 inputs
                      and dL/do, fp32 gradients): launch time and fp32 vector-ALU
                      fraction of its algorithmic flops
@@ -366,6 +367,23 @@ def bench_gate(gdr, torch, warmup, steps):
     return dict(mean=mean, min=mn, bytes=n * (4 + 2 + 2) + 4 * 128)
 
 
+def bench_gate_bwd(gdr, torch, warmup, steps):
+    """gdr_output_gate_bwd on the B8 T4096 H16 d128 gate: fp32 o, bf16 gate
+    and dL/dy in, fp32 do and dg out, dw over all rows.  Algorithmic bytes:
+    (4 + 2 + 2) read + (4 + 4) written per element."""
+    from gdr_gen import make_gate
+    inp = make_gate(8 * 4096, 16, 128, "f32", "bf16", seed=451)
+    dev = torch.device("cuda:0")
+    o, g, w = inp.o.to(dev), inp.g.to(dev), inp.w.to(dev)
+    dy = torch.randn(o.shape, generator=torch.Generator().manual_seed(9)).to(torch.bfloat16).to(dev)
+    ws = torch.empty(gdr.gdr_output_gate_bwd_workspace_size(8 * 4096, 16, 128), dtype=torch.uint8,
+                     device=dev)
+    mean, mn, med, wall = time_launches(
+        lambda: gdr.gdr_output_gate_bwd(o, g, w, dy, 1e-6, workspace=ws), warmup, steps)
+    n = o.numel()
+    return dict(mean=mean, min=mn, bytes=n * (4 + 2 + 2 + 4 + 4) + 4 * 128 * 2)
+
+
 def bench_bwd(gdr, torch, warmup, steps):
     """gdr_chunk_bwd on B8 H16 T4096 d128 (bf16 q/k/v and dL/do, dL/dS_T
     given, zero S_0).  It runs the GDN-2 backward with broadcast gates, so
@@ -450,8 +468,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
-    ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "longctx", "l2norm", "gate", "bwd",
-                                       "bwd2", "copy"],
+    ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "longctx", "l2norm", "gate", "gate_bwd",
+                                       "bwd", "bwd2", "copy"],
                     default=None,
                     help="time one operation only (for profiling)")
     ap.add_argument("--skip", default="",
@@ -502,6 +520,9 @@ def main():
     if want("gate"):
         log("timing gdr_output_gate B8 T4096 H16 d128 ...")
         res["gate"] = bench_gate(gdr, torch, args.warmup, args.steps)
+    if want("gate_bwd"):
+        log("timing gdr_output_gate_bwd B8 T4096 H16 d128 ...")
+        res["gate_bwd"] = bench_gate_bwd(gdr, torch, args.warmup, args.steps)
     if want("bwd"):
         log("timing gdr_chunk_bwd B8 H16 T4096 d128 ...")
         res["bwd"] = bench_bwd(gdr, torch, min(args.warmup, 5), min(args.steps, 10))
@@ -580,6 +601,13 @@ def main():
                               "launch_us_mean": r["mean"] * 1e6, "GB/s": gbs,
                               "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_launch": r["bytes"],
                               "traffic": measured_traffic("gate")}
+    if "gate_bwd" in res:
+        r = res["gate_bwd"]
+        gbs = r["bytes"] / r["mean"] / 1e9
+        out["output_gate_bwd"] = {"workload": "gdr_output_gate_bwd B8 T4096 H16 d128: fp32 o, "
+                                              "bf16 gate and dL/dy, fp32 do, dg, dw",
+                                  "launch_us_mean": r["mean"] * 1e6, "GB/s": gbs,
+                                  "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_launch": r["bytes"]}
     if "bwd" in res:
         r = res["bwd"]
         tf = r["flops"] / r["mean"] / 1e12

@@ -134,10 +134,11 @@ hipError_t launch_gate_d(const GateArgs& a) {
 //   dg = dy n w sigmoid(g) (1 + g (1 - sigmoid(g))),
 //   dw = sum over rows of dy n s(g).
 //
-// Same lane layout as the forward.  dw: each lane sums its 4 channels over
-// the rows it visits; lanes of a wave that share channels, then the four
-// waves, are added in the workgroup, which writes one partial row of DV
-// floats; gate_dw_reduce adds the workgroups' rows.
+// Same lane layout and UNROLL-row steps as the forward (all loads of a step
+// before its arithmetic).  dw: each lane sums its 4 channels over the rows
+// it visits; lanes of a wave that share channels, then the four waves, are
+// added in the workgroup, which writes its partial sums channel-major
+// (dwp[c][workgroup]); gate_dw_reduce adds them, one workgroup per channel.
 template <int DV, typename TO, typename TG, typename TD>
 __global__ __launch_bounds__(256) void output_gate_bwd_kernel(int64_t rows, const TO* o,
                                                               const TG* __restrict__ g,
@@ -157,47 +158,57 @@ __global__ __launch_bounds__(256) void output_gate_bwd_kernel(int64_t rows, cons
     if (w) wv4 = *reinterpret_cast<const f32x4*>(w + c0);
     f32x4 dwacc = {0.f, 0.f, 0.f, 0.f};
     const int64_t stride = (int64_t)gridDim.x * RPB;
-    for (int64_t r = (int64_t)blockIdx.x * RPB + rsub; r - rsub < rows; r += stride) {
-        // every lane runs the row reductions; rows past the end contribute 0
-        const bool live = r < rows;
-        f32x4 ov = {0.f, 0.f, 0.f, 0.f}, gv = ov, yv = ov;
-        if (live) {
-            ov = v4<TO>::ld(o + r * DV + c0);
-            gv = v4<TG>::ld(g + r * DV + c0);
-            yv = v4<TD>::ld(dy + r * DV + c0);
-        }
-        float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
-        ss += dpp_mov<0xB1>(ss);
-        ss += dpp_mov<0x4E>(ss);
-        ss += dpp_mov<0x141>(ss);
-        ss += dpp_mov<0x140>(ss);
-        if constexpr (LPR == 32) ss += __shfl_xor(ss, 16, 64);
-        const float rr = rsqrtf(ss * (1.f / DV) + eps);
-        f32x4 nv, dn, sgm;
-        float t = 0.f;
+    // every lane runs every step's row reductions (the step base is uniform
+    // over the workgroup); rows past the end load zeros and store nothing
+    for (int64_t base = (int64_t)blockIdx.x * RPB; base < rows; base += UNROLL * stride) {
+        f32x4 ov[UNROLL], gv[UNROLL], yv[UNROLL];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sgm[e] = __builtin_amdgcn_rcpf(1.f + __expf(-gv[e]));
-            nv[e] = ov[e] * rr;
-            dn[e] = yv[e] * wv4[e] * gv[e] * sgm[e];
-            t += nv[e] * dn[e];
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t r = base + u * stride + rsub;
+            ov[u] = gv[u] = yv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (r < rows) {
+                ov[u] = v4<TO>::ld(o + r * DV + c0);
+                gv[u] = v4<TG>::ld(g + r * DV + c0);
+                yv[u] = v4<TD>::ld(dy + r * DV + c0);
+            }
         }
-        t += dpp_mov<0xB1>(t);
-        t += dpp_mov<0x4E>(t);
-        t += dpp_mov<0x141>(t);
-        t += dpp_mov<0x140>(t);
-        if constexpr (LPR == 32) t += __shfl_xor(t, 16, 64);
-        const float tm = t * (1.f / DV);
-        if (live) {
-            f32x4 dov, dgv;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t r = base + u * stride + rsub;
+            float ss = ov[u][0] * ov[u][0] + ov[u][1] * ov[u][1] + ov[u][2] * ov[u][2] +
+                       ov[u][3] * ov[u][3];
+            ss += dpp_mov<0xB1>(ss);
+            ss += dpp_mov<0x4E>(ss);
+            ss += dpp_mov<0x141>(ss);
+            ss += dpp_mov<0x140>(ss);
+            if constexpr (LPR == 32) ss += __shfl_xor(ss, 16, 64);
+            const float rr = rsqrtf(ss * (1.f / DV) + eps);
+            f32x4 nv, dn, sgm;
+            float t = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                dov[e] = rr * (dn[e] - nv[e] * tm);
-                dgv[e] = yv[e] * nv[e] * wv4[e] * sgm[e] * (1.f + gv[e] * (1.f - sgm[e]));
-                dwacc[e] += yv[e] * nv[e] * gv[e] * sgm[e];
+                sgm[e] = __builtin_amdgcn_rcpf(1.f + __expf(-gv[u][e]));
+                nv[e] = ov[u][e] * rr;
+                dn[e] = yv[u][e] * wv4[e] * gv[u][e] * sgm[e];
+                t += nv[e] * dn[e];
             }
-            st4(dout + r * DV + c0, dov);
-            st4(dg + r * DV + c0, dgv);
+            t += dpp_mov<0xB1>(t);
+            t += dpp_mov<0x4E>(t);
+            t += dpp_mov<0x141>(t);
+            t += dpp_mov<0x140>(t);
+            if constexpr (LPR == 32) t += __shfl_xor(t, 16, 64);
+            const float tm = t * (1.f / DV);
+            if (r < rows) {
+                f32x4 dov, dgv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dov[e] = rr * (dn[e] - nv[e] * tm);
+                    dgv[e] = yv[u][e] * nv[e] * wv4[e] * sgm[e] * (1.f + gv[u][e] * (1.f - sgm[e]));
+                    dwacc[e] += yv[u][e] * nv[e] * gv[u][e] * sgm[e];
+                }
+                st4(dout + r * DV + c0, dov);
+                st4(dg + r * DV + c0, dgv);
+            }
         }
     }
     if (!dwp) return;
@@ -212,26 +223,35 @@ __global__ __launch_bounds__(256) void output_gate_bwd_kernel(int64_t rows, cons
         f32x4 sacc = red[0][threadIdx.x];
 #pragma unroll
         for (int k = 1; k < 4; ++k) sacc += red[k][threadIdx.x];
-        *reinterpret_cast<f32x4*>(dwp + (int64_t)blockIdx.x * DV + 4 * threadIdx.x) = sacc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dwp[(int64_t)(4 * threadIdx.x + e) * gridDim.x + blockIdx.x] = sacc[e];
     }
 }
 
-// dw[c] = sum of the workgroups' partial rows
+// dw[c] = sum over the workgroups' partial sums dwp[c][0 .. nblk), one
+// 256-thread workgroup per channel
 __global__ __launch_bounds__(256) void gate_dw_reduce(const float* __restrict__ dwp, int nblk,
-                                                     int dv, float* __restrict__ dw) {
-    const int c = blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= dv) return;
+                                                     float* __restrict__ dw) {
+    __shared__ float red[256];
+    const int c = blockIdx.x;
     float sacc = 0.f;
-    for (int b = 0; b < nblk; ++b) sacc += dwp[(int64_t)b * dv + c];
-    dw[c] = sacc;
+    for (int b = threadIdx.x; b < nblk; b += 256) sacc += dwp[(int64_t)c * nblk + b];
+    red[threadIdx.x] = sacc;
+    __syncthreads();
+    for (int m = 128; m >= 1; m >>= 1) {
+        if (threadIdx.x < m) red[threadIdx.x] += red[threadIdx.x + m];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) dw[c] = red[0];
 }
 
-constexpr int GATE_BWD_MAX_BLOCKS = 1024;
+constexpr int GATE_BWD_MAX_BLOCKS = 2048;
 
 template <int DV>
 int64_t gate_bwd_blocks(int64_t rows) {
     constexpr int RPB = 4 * (64 / (DV / 4));
-    int64_t blocks = (rows + RPB - 1) / RPB;
+    int64_t blocks = (rows + RPB * UNROLL - 1) / (RPB * UNROLL);
     return blocks < GATE_BWD_MAX_BLOCKS ? blocks : GATE_BWD_MAX_BLOCKS;
 }
 
@@ -245,7 +265,7 @@ hipError_t launch_gate_bwd_t(const GateBwdArgs& a) {
                        (const TD*)a.dy, a.dout, a.dg, dwp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.dw) return e;
-    hipLaunchKernelGGL(gate_dw_reduce, dim3(1), dim3(DV), 0, a.stream, dwp, (int)blocks, DV, a.dw);
+    hipLaunchKernelGGL(gate_dw_reduce, dim3(DV), dim3(256), 0, a.stream, dwp, (int)blocks, a.dw);
     return hipGetLastError();
 }
 

@@ -301,8 +301,8 @@ gdr_status_t gdr_output_gate(int64_t N, int64_t H, int64_t Dv, gdr_dtype_t o_dt,
  *   dw          [Dv] fp32 (written), or NULL: not computed, no workspace
  *   workspace   when dw is given: device memory of at least
  *               gdr_output_gate_bwd_workspace_size(N, H, Dv) bytes (the
- *               workgroups' partial sums of dw, at most 1024 rows of Dv
- *               floats), 16-byte aligned, owned by the caller
+ *               workgroups' partial sums of dw, at most 2048 x Dv floats),
+ *               16-byte aligned, owned by the caller
  *
  * One pass over o, g and dy plus a small reduction for dw.  All tensors
  * 16-byte aligned.  fp32 arithmetic; N H == 0 writes dw = 0.

@@ -294,12 +294,12 @@ def gate_bwd(gdr, N=4, H=2, Dv=64, odt=0, o=A16, gdt=1, g=A16, w=None, eps=1e-6,
 
 
 def test_gate_bwd_workspace_size(gdr):
-    """One partial row of Dv floats per workgroup, at most 1024 workgroups;
-    a workgroup takes 8 rows (Dv = 128) or 16 (Dv = 64)."""
+    """Dv partial sums per workgroup, at most 2048 workgroups; a workgroup
+    step takes 4 x 8 rows (Dv = 128) or 4 x 16 (Dv = 64)."""
     f = gdr.lib.gdr_output_gate_bwd_workspace_size
-    assert f(100, 3, 128) == 4 * 128 * 38
-    assert f(100, 3, 64) == 4 * 64 * 19
-    assert f(10 ** 6, 16, 128) == 4 * 128 * 1024
+    assert f(100, 3, 128) == 4 * 128 * 10
+    assert f(100, 3, 64) == 4 * 64 * 5
+    assert f(10 ** 6, 16, 128) == 4 * 128 * 2048
     assert f(4, 2, 96) == 0
 
 
