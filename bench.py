@@ -30,6 +30,8 @@ The JSON line (stdout, last line) carries:
                      fraction of its algorithmic flops
   backward2          gdr2_chunk_bwd on the B4 H16 T4096 d128 GDN-2 workload, as
                      for backward
+  backward_long_context  the backward on the long-context workload, plain
+                     and by gdr_chunk_bwd_split
   copy_reference     a plain 512 MiB device copy (achievable bandwidth)
   cpu_baseline       the fp64 oracle timed on the host on the same workload
 """
@@ -432,6 +434,30 @@ def bench_bwd2(gdr, torch, warmup, steps):
     return dict(mean=mean, min=mn, flops=flops, tokens=4 * 4096, ws=ws.numel())
 
 
+def bench_bwd_long(gdr, torch, warmup, steps, nseg=4):
+    """The backward on the long-context workload (B1 H16 T32768 d128, bf16
+    inputs and dL/do, initial state, dL/dS_T given): the plain call (64
+    workgroups) and the split call with nseg segments side by side."""
+    from gdr_gen import make_config
+    inp = make_config(2)
+    dev = torch.device("cuda:0")
+    args = [x.to(dev) for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.s0)]
+    B, T, H, Dk = inp.q.shape
+    Dv = inp.v.shape[-1]
+    g = torch.Generator(device="cpu").manual_seed(10)
+    do = torch.randn((B, T, H, Dv), generator=g).to(torch.bfloat16).to(dev)
+    dsf = (0.1 * torch.randn((B, H, Dv, Dk), generator=g)).to(dev)
+    wsp = torch.empty(gdr.gdr_chunk_bwd_workspace_size(B, T, H, Dk, Dv), dtype=torch.uint8,
+                      device=dev)
+    wss = torch.empty(gdr.gdr_chunk_bwd_split_workspace_size(B, T, H, Dk, Dv, inp.q.dtype, nseg),
+                      dtype=torch.uint8, device=dev)
+    pmean, pmin, _, _ = time_launches(
+        lambda: gdr.gdr_chunk_bwd(*args, do, dsf, workspace=wsp), warmup, steps)
+    smean, smin, _, _ = time_launches(
+        lambda: gdr.gdr_chunk_bwd_split(*args, do, dsf, nseg=nseg, workspace=wss), warmup, steps)
+    return dict(plain=pmean, split=smean, nseg=nseg, tokens=B * T)
+
+
 def bench_copy(torch, warmup, steps, nbytes=512 << 20):
     """A plain device-to-device copy of known size: the achievable-bandwidth
     reference, and the kernel whose FETCH_SIZE / WRITE_SIZE counters scale
@@ -469,7 +495,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "longctx", "l2norm", "gate", "gate_bwd",
-                                       "bwd", "bwd2", "copy"],
+                                       "bwd", "bwd2", "bwd_long", "copy"],
                     default=None,
                     help="time one operation only (for profiling)")
     ap.add_argument("--skip", default="",
@@ -529,6 +555,9 @@ def main():
     if want("bwd2"):
         log("timing gdr2_chunk_bwd B4 H16 T4096 d128 ...")
         res["bwd2"] = bench_bwd2(gdr, torch, min(args.warmup, 5), min(args.steps, 10))
+    if want("bwd_long"):
+        log("timing the backward on B1 H16 T32768 d128 (plain and split) ...")
+        res["bwd_long"] = bench_bwd_long(gdr, torch, 1, min(args.steps, 3))
     if want("copy"):
         log("timing a 512 MiB device copy ...")
         res["copy"] = bench_copy(torch, args.warmup, args.steps)
@@ -630,6 +659,12 @@ def main():
                                          "frac": tf / FP32_PEAK_TFLOPS},
                             "flops_per_launch": r["flops"], "workspace_bytes": r["ws"],
                             "traffic": measured_traffic("bwd2")}
+    if "bwd_long" in res:
+        r = res["bwd_long"]
+        out["backward_long_context"] = {
+            "workload": "B1 H16 T32768 d128 bf16 inputs and dL/do, initial state, dL/dS_T",
+            "split_ms": r["split"] * 1e3, "plain_ms": r["plain"] * 1e3, "nseg": r["nseg"],
+            "tokens/s_split": r["tokens"] / r["split"], "tokens/s_plain": r["tokens"] / r["plain"]}
     if "copy" in res:
         cp = res["copy"]
         out["copy_reference"] = {"what": "torch device-to-device copy, 512 MiB read + 512 MiB "

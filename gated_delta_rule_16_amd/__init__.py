@@ -33,6 +33,7 @@ __all__ = ["gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd", "gdr_output_
            "gdr2_chunk_bwd", "gdr2_chunk_bwd_workspace_size",
            "gdr_chunk_fwd_split", "gdr_chunk_fwd_split_workspace_size",
            "gdr_output_gate_bwd", "gdr_output_gate_bwd_workspace_size",
+           "gdr_chunk_bwd_split", "gdr_chunk_bwd_split_workspace_size",
            "GdrError", "status_string", "lib", "LIB_PATH", "GDR_F32",
            "GDR_BF16", "GDR_L2NORM_QK"]
 
@@ -90,6 +91,11 @@ lib.gdr_output_gate_bwd_workspace_size.restype = ctypes.c_size_t
 lib.gdr_output_gate_bwd.argtypes = ([_I64] * 3 + [_E, _P, _E, _P, _P, ctypes.c_float, _E, _P] +
                                     [_P] * 4 + [ctypes.c_size_t, _P])
 lib.gdr_output_gate_bwd.restype = ctypes.c_int
+lib.gdr_chunk_bwd_split_workspace_size.argtypes = [_I64] * 5 + [_E, _I64]
+lib.gdr_chunk_bwd_split_workspace_size.restype = ctypes.c_size_t
+lib.gdr_chunk_bwd_split.argtypes = ([_I64] * 5 + [_E] + [_P] * 6 + [_E, _P, _P] + [_P] * 6 +
+                                    [_I64, _U, _P, ctypes.c_size_t, _P])
+lib.gdr_chunk_bwd_split.restype = ctypes.c_int
 lib.gdr_status_string.argtypes = [ctypes.c_int]
 lib.gdr_status_string.restype = ctypes.c_char_p
 lib.gdr_version.restype = ctypes.c_int
@@ -440,3 +446,46 @@ def gdr_output_gate_bwd(o, g, w, dy, eps=1e-6, *, want_dw=True, workspace=None, 
         _DT[dy.dtype], _ptr(dy), _ptr(do), _ptr(dg), _ptr(dw), _ptr(workspace),
         0 if workspace is None else workspace.numel(), _stream(stream)))
     return do, dg, dw
+
+
+def gdr_chunk_bwd_split_workspace_size(B, T, H, Dk, Dv, dtype, nseg) -> int:
+    """Bytes of device workspace gdr_chunk_bwd_split needs."""
+    return int(lib.gdr_chunk_bwd_split_workspace_size(B, T, H, Dk, Dv, _DT[dtype], nseg))
+
+
+def gdr_chunk_bwd_split(q, k, v, alpha, beta, s0, dout, ds_final=None, *, nseg=8, workspace=None,
+                        want_ds0=True, l2norm_qk=False, stream=None):
+    """gdr_chunk_bwd with each sequence split into ``nseg`` segments that run
+    side by side (T divisible by nseg).  Same arguments and results as
+    gdr_chunk_bwd."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if q.dtype not in _DT or dout.dtype not in _DT:
+        raise TypeError("q and dout must be float32 or bfloat16")
+    _check("q", q, q.dtype, (B, T, H, Dk))
+    _check("k", k, q.dtype, (B, T, H, Dk))
+    _check("v", v, q.dtype, (B, T, H, Dv))
+    _check("alpha", alpha, torch.float32, (B, T, H))
+    _check("beta", beta, torch.float32, (B, T, H))
+    _check("dout", dout, dout.dtype, (B, T, H, Dv))
+    if s0 is not None:
+        _check("s0", s0, torch.float32, (B, H, Dv, Dk))
+    if ds_final is not None:
+        _check("ds_final", ds_final, torch.float32, (B, H, Dv, Dk))
+    need = gdr_chunk_bwd_split_workspace_size(B, T, H, Dk, Dv, q.dtype, nseg)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check("workspace", workspace, torch.uint8)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((B, T, H, Dk), **f32)
+    dk = torch.empty((B, T, H, Dk), **f32)
+    dv = torch.empty((B, T, H, Dv), **f32)
+    da = torch.empty((B, T, H), **f32)
+    db = torch.empty((B, T, H), **f32)
+    ds0 = torch.empty((B, H, Dv, Dk), **f32) if want_ds0 else None
+    _run("gdr_chunk_bwd_split", lib.gdr_chunk_bwd_split(
+        B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _ptr(s0), _DT[dout.dtype], _ptr(dout), _ptr(ds_final), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(da), _ptr(db), _ptr(ds0), nseg, GDR_L2NORM_QK if l2norm_qk else 0,
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dq, dk, dv, da, db, ds0

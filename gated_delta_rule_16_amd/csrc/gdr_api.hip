@@ -147,18 +147,58 @@ struct SplitLayout {
 };
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 SplitLayout split_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
-                         gdr_dtype_t in_dt, int64_t nseg) {
+                         gdr_dtype_t in_dt, int64_t nseg, bool discard = false) {
     SplitLayout l{};
     const size_t bn = (size_t)(B * nseg * H);
     l.R = up256(bn * Dv * Dk * 4);
     l.P = up256(bn * Dk * Dk * 4);
     l.Sin = up256(bn * Dv * Dk * 4);
     l.vz = up256((size_t)(B * T * H * Dk) * (in_dt == GDR_BF16 ? 2 : 4));
-    l.oP = Dk == Dv ? 0 : up256((size_t)(B * T * H * Dk) * 2);
+    // the P pass's output (and, with `discard`, the R pass's) when it
+    // cannot go to o: bf16, max(Dk, Dv) columns
+    l.oP = discard ? up256((size_t)(B * T * H * (Dk > Dv ? Dk : Dv)) * 2)
+                   : Dk == Dv ? 0 : up256((size_t)(B * T * H * Dk) * 2);
     l.total = l.R + l.P + l.Sin + l.vz + l.oP;
     return l;
 }
 }  // namespace
+
+// Passes 1-3 of the sequence split, on the segment batch `a` (B nseg
+// segments of T / nseg tokens, inputs set): R (each segment from zero), P
+// (v = 0 from the identity) and the scan into the start states Sin.  The
+// passes' outputs go to `o` (overwritten by the caller's last pass) or to
+// the workspace's discard buffer when the layout has one.
+static gdr_status_t split_states(const ChunkArgs& a, const SplitLayout& l, char* w, int64_t B,
+                                 int64_t nseg, const float* s0, void* o) {
+    float* R = reinterpret_cast<float*>(w);
+    float* P = reinterpret_cast<float*>(w + l.R);
+    float* Sin = reinterpret_cast<float*>(w + l.R + l.P);
+    void* vz = w + l.R + l.P + l.Sin;
+    void* oP = l.oP ? static_cast<void*>(w + l.R + l.P + l.Sin + l.vz) : o;
+    gdr_status_t st;
+    // 1. each segment from a zero state: R
+    ChunkArgs r = a;
+    r.s0 = nullptr;
+    r.o = l.oP && !o ? oP : o;
+    r.out_bf16 = l.oP && !o ? true : a.out_bf16;
+    r.s_final = R;
+    if ((st = chunk_run(r)) != GDR_OK) return st;
+    // 2. each segment with v = 0 from the identity: P (d_k x d_k)
+    hipError_t e = launch_identity(P, a.B * a.H, (int)a.Dk, a.stream);
+    if (e == hipSuccess) e = launch_zero(vz, (int64_t)l.vz, a.stream);
+    if (e != hipSuccess) return GDR_ERR_DEVICE;
+    ChunkArgs pa = a;
+    pa.Dv = a.Dk;
+    pa.v = vz;
+    pa.s0 = P;
+    pa.s_final = P;
+    pa.o = oP;
+    pa.out_bf16 = l.oP ? true : a.out_bf16;
+    if ((st = chunk_run(pa)) != GDR_OK) return st;
+    // 3. segment start states
+    SplitScanArgs sc{B, a.H, a.Dk, a.Dv, (int)nseg, s0, R, P, Sin, a.stream};
+    return from_hip(launch_split_scan(sc));
+}
 
 extern "C" size_t gdr_chunk_fwd_split_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                                      int64_t Dv, gdr_dtype_t in_dt,
@@ -198,11 +238,7 @@ extern "C" gdr_status_t gdr_chunk_fwd_split(int64_t B, int64_t T, int64_t H, int
     const SplitLayout l = split_layout(B, T, H, Dk, Dv, in_dt, nseg);
     if (workspace_bytes < l.total) return GDR_ERR_INVALID;
     char* w = static_cast<char*>(workspace);
-    float* R = reinterpret_cast<float*>(w);
-    float* P = reinterpret_cast<float*>(w + l.R);
     float* Sin = reinterpret_cast<float*>(w + l.R + l.P);
-    void* vz = w + l.R + l.P + l.Sin;
-    void* oP = l.oP ? static_cast<void*>(w + l.R + l.P + l.Sin + l.vz) : o;
     // the segments as a batch: [B, T, H, d] is [B nseg, T / nseg, H, d]
     a.B = B * nseg;
     a.T = T / nseg;
@@ -214,34 +250,132 @@ extern "C" gdr_status_t gdr_chunk_fwd_split(int64_t B, int64_t T, int64_t H, int
     a.alpha = alpha;
     a.beta = beta;
     a.stream = stream;
-    // 1. each segment from a zero state: R
-    ChunkArgs r = a;
-    r.s0 = nullptr;
-    r.o = o;
-    r.s_final = R;
-    if ((st = chunk_run(r)) != GDR_OK) return st;
-    // 2. each segment with v = 0 from the identity: P (d_k x d_k)
-    hipError_t e = launch_identity(P, B * nseg * H, (int)Dk, stream);
-    if (e == hipSuccess) e = launch_zero(vz, (int64_t)l.vz, stream);
-    if (e != hipSuccess) return GDR_ERR_DEVICE;
-    ChunkArgs pa = a;
-    pa.Dv = Dk;
-    pa.v = vz;
-    pa.s0 = P;
-    pa.s_final = P;
-    pa.o = oP;
-    pa.out_bf16 = l.oP ? true : a.out_bf16;
-    if ((st = chunk_run(pa)) != GDR_OK) return st;
-    // 3. segment start states
-    SplitScanArgs sc{B, H, Dk, Dv, (int)nseg, s0, R, P, Sin, stream};
-    if ((e = launch_split_scan(sc)) != hipSuccess) return GDR_ERR_DEVICE;
+    if ((st = split_states(a, l, w, B, nseg, s0, o)) != GDR_OK) return st;
     // 4. every segment from its start state: o, and the final states in place
     ChunkArgs f = a;
     f.s0 = Sin;
     f.s_final = Sin;
     f.o = o;
     if ((st = chunk_run(f)) != GDR_OK) return st;
-    if (s_final) return from_hip(launch_last_state(Sin, s_final, B, (int)nseg, H * Dv * Dk, stream));
+    if (s_final)
+        return from_hip(launch_seg_state(Sin, s_final, B, (int)nseg, (int)nseg - 1, H * Dv * Dk,
+                                         stream));
+    return GDR_OK;
+}
+
+// Sequence-split backward (scalar gates): the forward's split pieces, the
+// segments' own contributions N and end gradients Gend, and the backward
+// workspace of the segment batch.
+namespace {
+struct BwdSplitLayout {
+    SplitLayout f;
+    size_t N, G, bw, total;
+};
+BwdSplitLayout bwd_split_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                gdr_dtype_t in_dt, int64_t nseg) {
+    BwdSplitLayout l{};
+    l.f = split_layout(B, T, H, Dk, Dv, in_dt, nseg, true);
+    const size_t bn = (size_t)(B * nseg * H);
+    l.N = up256(bn * Dv * Dk * 4);
+    l.G = up256(bn * Dv * Dk * 4);
+    l.bw = up256(bwd_workspace_bytes(B * nseg, T / nseg, H, Dk, Dv));
+    l.total = l.f.total + l.N + l.G + l.bw;
+    return l;
+}
+}  // namespace
+
+extern "C" size_t gdr_chunk_bwd_split_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                                     int64_t Dv, gdr_dtype_t in_dt,
+                                                     int64_t nseg) {
+    if (nseg == 1 && dtype_ok(in_dt)) return gdr_chunk_bwd_workspace_size(B, T, H, Dk, Dv);
+    if (gdr_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, in_dt, nseg) == 0) return 0;
+    return bwd_split_layout(B, T, H, Dk, Dv, in_dt, nseg).total;
+}
+
+extern "C" gdr_status_t gdr_chunk_bwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                            int64_t Dv, gdr_dtype_t in_dt, const void* q,
+                                            const void* k, const void* v, const float* alpha,
+                                            const float* beta, const float* s0,
+                                            gdr_dtype_t dout_dt, const void* dout,
+                                            const float* ds_final, float* dq, float* dk,
+                                            float* dv, float* dalpha, float* dbeta, float* ds0,
+                                            int64_t nseg, uint32_t flags, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream) {
+    if (nseg < 1 || nseg > (1 << 20)) return GDR_ERR_INVALID;
+    if (nseg == 1 || T == 0 || B == 0 || H == 0)   // the plain call
+        return gdr_chunk_bwd_ex(B, T, H, Dk, Dv, in_dt, q, k, v, alpha, beta, s0, dout_dt, dout,
+                                ds_final, dq, dk, dv, dalpha, dbeta, ds0, workspace,
+                                workspace_bytes, flags, stream);
+    if (!flags_ok(flags)) return GDR_ERR_UNSUPPORTED;
+    ChunkArgs a{};
+    gdr_status_t st = chunk_common(B, T, H, Dk, Dv, in_dt, GDR_BF16, a);
+    if (st != GDR_OK) return st;
+    if (!dtype_ok(dout_dt)) return GDR_ERR_UNSUPPORTED;
+    if (T % nseg != 0 || !sizes_ok(B * nseg, H, 1)) return GDR_ERR_INVALID;
+    if (!grid_ok(B * T * H * Dk) || !grid_ok(B * nseg * H * Dk * Dk) || !grid_ok(B * H * Dv * Dk))
+        return GDR_ERR_INVALID;
+    if (B * nseg * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
+    if (!ptrs_ok({q, k, v, dout, dq, dk, dv, workspace}) || !elem_ok(alpha, 4) ||
+        !elem_ok(beta, 4) || !elem_ok(dalpha, 4) || !elem_ok(dbeta, 4))
+        return GDR_ERR_INVALID;
+    if (!opt_ok(s0) || !opt_ok(ds_final) || !opt_ok(ds0)) return GDR_ERR_INVALID;
+    const BwdSplitLayout l = bwd_split_layout(B, T, H, Dk, Dv, in_dt, nseg);
+    if (workspace_bytes < l.total) return GDR_ERR_INVALID;
+    char* w = static_cast<char*>(workspace);
+    float* P = reinterpret_cast<float*>(w + l.f.R);
+    float* Sin = reinterpret_cast<float*>(w + l.f.R + l.f.P);
+    float* N = reinterpret_cast<float*>(w + l.f.total);
+    float* G = reinterpret_cast<float*>(w + l.f.total + l.N);
+    void* bw = w + l.f.total + l.N + l.G;
+    a.B = B * nseg;
+    a.T = T / nseg;
+    a.gated2 = false;
+    a.l2norm = (flags & GDR_L2NORM_QK) != 0;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.stream = stream;
+    // the segments' start states S_in and transitions P
+    if ((st = split_states(a, l.f, w, B, nseg, s0, nullptr)) != GDR_OK) return st;
+    BwdArgs b{};
+    b.B = B * nseg;
+    b.T = T / nseg;
+    b.H = H;
+    b.Dk = Dk;
+    b.Dv = Dv;
+    b.in_bf16 = in_dt == GDR_BF16;
+    b.dout_bf16 = dout_dt == GDR_BF16;
+    b.l2norm = a.l2norm;
+    b.q = q;
+    b.k = k;
+    b.v = v;
+    b.dout = dout;
+    b.alpha = alpha;
+    b.beta = beta;
+    b.s0 = Sin;
+    b.dq = dq;
+    b.dk = dk;
+    b.dv = dv;
+    b.dalpha = dalpha;
+    b.dbeta = dbeta;
+    b.workspace = bw;
+    b.stream = stream;
+    // each segment's own contribution to dL/dS_in: its backward from a zero
+    // end gradient (the other gradients are overwritten below)
+    b.ds_final = nullptr;
+    b.ds0 = N;
+    hipError_t e = launch_chunk_bwd(b);
+    if (e != hipSuccess) return GDR_ERR_DEVICE;
+    // the segments' end gradients, last to first
+    SplitScanArgs rs{B, H, Dk, Dv, (int)nseg, ds_final, N, P, G, stream};
+    if ((e = launch_split_rscan(rs)) != hipSuccess) return GDR_ERR_DEVICE;
+    // every segment from its start state with its end gradient
+    b.ds_final = G;
+    b.ds0 = N;
+    if ((e = launch_chunk_bwd(b)) != hipSuccess) return GDR_ERR_DEVICE;
+    if (ds0) return from_hip(launch_seg_state(N, ds0, B, (int)nseg, 0, H * Dv * Dk, stream));
     return GDR_OK;
 }
 

@@ -98,8 +98,9 @@ hipError_t launch_step(const StepArgs& a);
 hipError_t launch_identity(float* x, int64_t n, int d, hipStream_t st);
 hipError_t launch_zero(void* x, int64_t bytes, hipStream_t st);
 hipError_t launch_split_scan(const SplitScanArgs& a);
-hipError_t launch_last_state(const float* F, float* sf, int64_t B, int nseg, int64_t per,
-                             hipStream_t st);
+hipError_t launch_split_rscan(const SplitScanArgs& a);
+hipError_t launch_seg_state(const float* F, float* sf, int64_t B, int nseg, int seg,
+                            int64_t per, hipStream_t st);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
 size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv);
 hipError_t launch_chunk2_bwd(const Bwd2Args& a);

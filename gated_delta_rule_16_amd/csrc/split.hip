@@ -1,6 +1,7 @@
-// Kernels of gdr_chunk_fwd_split, the sequence-split forward: identity and
-// zero fills, the scan over segment transitions, and the gather of the
-// last segment's state.
+// Kernels of the sequence-split calls (gdr_chunk_fwd_split,
+// gdr_chunk_bwd_split): identity and zero fills, the scans over segment
+// transitions (forward for the start states, reverse for the backward's
+// carry), and the gather of one segment's state per sequence.
 //
 // The state map of a segment is affine in its start state: running the rule
 // over tokens t0 .. t1 from S gives S P + R, where R is the result from a
@@ -102,14 +103,95 @@ __global__ __launch_bounds__(256) void split_scan_kernel(int64_t H, int nseg,
     }
 }
 
-// s_final[b] = F[b nseg + nseg - 1] (each H Dv Dk floats)
-__global__ __launch_bounds__(256) void last_state_kernel(const float* __restrict__ F,
-                                                         float* __restrict__ sf, int64_t B,
-                                                         int nseg, int64_t per) {
+// The backward's carry composes the same way in reverse: dL/dS_in(p) =
+// G_end(p) P_p^T + N_p, with N_p the segment's own contribution (its
+// backward from G_end = 0).  For each (b, h) and rows row0 .. row0 + 15:
+// G = dsf (or 0) for the last segment; for p = nseg - 1 .. 1,
+// Gend[b nseg + p] = G, then G = G P[b nseg + p]^T + N[b nseg + p];
+// Gend[b nseg] = G.  P_p^T staged in LDS, as in split_scan_kernel.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void split_rscan_kernel(int64_t H, int nseg,
+                                                          const float* __restrict__ dsf,
+                                                          const float* __restrict__ N,
+                                                          const float* __restrict__ P,
+                                                          float* __restrict__ Gend) {
+    constexpr int PK = DK + 4;
+    constexpr int NCOL = DK / 16;
+    constexpr int NP = DK * DK / 4 / 256;
+    __shared__ __align__(16) float Pt[DK * PK];   // Pt[m][j] = P[j][m]
+    __shared__ __align__(16) float Gr[SROWS * PK];
+    const int tid = threadIdx.x;
+    const int64_t unit = blockIdx.x / (DV / SROWS);
+    const int row0 = (int)(blockIdx.x % (DV / SROWS)) * SROWS;
+    const int64_t h = unit % H, b = unit / H;
+    const int i = tid >> 4, j0 = NCOL * (tid & 15);
+    auto seg_of = [&](int p) { return (b * nseg + p) * H + h; };
+    f32x4 pr[NP];
+    float nr[NCOL];
+    auto fetch = [&](int p) {
+        const int64_t seg = seg_of(p);
+#pragma unroll
+        for (int it = 0; it < NP; ++it) {
+            const int e = tid + 256 * it;
+            const int m = e / (DK / 4), c = 4 * (e % (DK / 4));
+            pr[it] = *reinterpret_cast<const f32x4*>(P + (seg * DK + m) * DK + c);
+        }
+#pragma unroll
+        for (int j = 0; j < NCOL; ++j) nr[j] = N[(seg * DV + row0 + i) * DK + j0 + j];
+    };
+    float gv[NCOL];
+#pragma unroll
+    for (int j = 0; j < NCOL; ++j)
+        gv[j] = dsf ? dsf[((b * H + h) * DV + row0 + i) * DK + j0 + j] : 0.f;
+    if (nseg > 1) fetch(nseg - 1);
+    for (int p = nseg - 1; p >= 0; --p) {
+        const int64_t seg = seg_of(p);
+#pragma unroll
+        for (int j = 0; j < NCOL; ++j) Gend[(seg * DV + row0 + i) * DK + j0 + j] = gv[j];
+        if (p == 0) break;
+        __syncthreads();   // the previous step's reads of Pt and Gr are done
+#pragma unroll
+        for (int it = 0; it < NP; ++it) {   // transposed into LDS
+            const int e = tid + 256 * it;
+            const int m = e / (DK / 4), c = 4 * (e % (DK / 4));
+#pragma unroll
+            for (int z = 0; z < 4; ++z) Pt[(c + z) * PK + m] = pr[it][z];
+        }
+#pragma unroll
+        for (int j = 0; j < NCOL; ++j) Gr[i * PK + j0 + j] = gv[j];
+        float acc[NCOL];
+#pragma unroll
+        for (int j = 0; j < NCOL; ++j) acc[j] = nr[j];
+        if (p - 1 > 0) fetch(p - 1);
+        __syncthreads();
+#pragma unroll 4
+        for (int m = 0; m < DK; ++m) {
+            const float gm = Gr[i * PK + m];
+#pragma unroll
+            for (int j = 0; j < NCOL; ++j) acc[j] += gm * Pt[m * PK + j0 + j];
+        }
+#pragma unroll
+        for (int j = 0; j < NCOL; ++j) gv[j] = acc[j];
+    }
+}
+
+// sf[b] = F[b nseg + seg] (each `per` floats): one segment's state per
+// sequence (the last segment's final state, the first segment's dS_0)
+__global__ __launch_bounds__(256) void seg_state_kernel(const float* __restrict__ F,
+                                                        float* __restrict__ sf, int64_t B,
+                                                        int nseg, int seg, int64_t per) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= B * per) return;
     const int64_t b = i / per, e = i % per;
-    sf[i] = F[(b * nseg + nseg - 1) * per + e];
+    sf[i] = F[(b * nseg + seg) * per + e];
+}
+
+template <int DK, int DV>
+hipError_t rscan_t(const SplitScanArgs& a) {
+    const int64_t blocks = a.B * a.H * (DV / SROWS);
+    hipLaunchKernelGGL((split_rscan_kernel<DK, DV>), dim3((unsigned)blocks), dim3(256), 0,
+                       a.stream, a.H, a.nseg, a.s0, a.R, a.P, a.Sin);
+    return hipGetLastError();
 }
 
 template <int DK, int DV>
@@ -145,12 +227,20 @@ hipError_t launch_split_scan(const SplitScanArgs& a) {
     return scan_t<64, 64>(a);
 }
 
-hipError_t launch_last_state(const float* F, float* sf, int64_t B, int nseg, int64_t per,
-                             hipStream_t st) {
+// the same arguments, read as: s0 = dL/dS_T or NULL, R = N, P = P, Sin = Gend
+hipError_t launch_split_rscan(const SplitScanArgs& a) {
+    if (a.Dk == 128 && a.Dv == 128) return rscan_t<128, 128>(a);
+    if (a.Dk == 128 && a.Dv == 64) return rscan_t<128, 64>(a);
+    if (a.Dk == 64 && a.Dv == 128) return rscan_t<64, 128>(a);
+    return rscan_t<64, 64>(a);
+}
+
+hipError_t launch_seg_state(const float* F, float* sf, int64_t B, int nseg, int seg,
+                            int64_t per, hipStream_t st) {
     const int64_t total = B * per;
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL(last_state_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                       F, sf, B, nseg, per);
+    hipLaunchKernelGGL(seg_state_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                       F, sf, B, nseg, seg, per);
     return hipGetLastError();
 }
 

@@ -261,6 +261,40 @@ gdr_status_t gdr_chunk_fwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                  hipStream_t stream);
 
 /*
+ * Sequence-split form of gdr_chunk_bwd_ex, for few long sequences.  The
+ * backward's carry composes like the state: dL/dS_in(p) = G_end(p) P_p^T +
+ * N_p, where P_p is segment p's transition (as in gdr_chunk_fwd_split) and
+ * N_p its own contribution (its backward from G_end = 0).  The call forms
+ * every segment's start state and P_p with the split forward's passes,
+ * runs the backward over all segments side by side from a zero end
+ * gradient (N_p), scans the end gradients from the last segment to the
+ * first, and runs the backward over all segments once more with them.
+ *
+ *   arguments as for gdr_chunk_bwd_ex, plus nseg (>= 1, dividing T; 1 is
+ *   the plain call) and a workspace of at least
+ *   gdr_chunk_bwd_split_workspace_size(B, T, H, Dk, Dv, in_dt, nseg) bytes
+ *   (for nseg = 1 the plain call's), 16-byte aligned, owned by the caller
+ *
+ * Results equal the plain call's up to rounding.  The gradient outputs are
+ * written twice (the first pass's values are overwritten).
+ */
+size_t gdr_chunk_bwd_split_workspace_size(int64_t B, int64_t T, int64_t H,
+                                          int64_t Dk, int64_t Dv,
+                                          gdr_dtype_t in_dt, int64_t nseg);
+
+gdr_status_t gdr_chunk_bwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                 int64_t Dv, gdr_dtype_t in_dt, const void *q,
+                                 const void *k, const void *v,
+                                 const float *alpha, const float *beta,
+                                 const float *s0, gdr_dtype_t dout_dt,
+                                 const void *dout, const float *ds_final,
+                                 float *dq, float *dk, float *dv,
+                                 float *dalpha, float *dbeta, float *ds0,
+                                 int64_t nseg, uint32_t flags,
+                                 void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/*
  * Output gate of the block, applied to the rule's output o per token and
  * head over the Dv channels ("Gated DeltaNet-2", agihunt.info: the
  * recurrent output passes an RMSNorm and a SiLU output gate; GDN review on

@@ -32,6 +32,7 @@ def test_header_declares_the_three_operations():
               "gdr_chunk_fwd_split", "gdr_chunk_fwd_split_workspace_size",
               "gdr_chunk_bwd_ex", "gdr2_chunk_bwd_ex",
               "gdr_output_gate_bwd", "gdr_output_gate_bwd_workspace_size",
+              "gdr_chunk_bwd_split", "gdr_chunk_bwd_split_workspace_size",
               "gdr_status_string", "gdr_version"):
         assert n in names, names
 
@@ -316,3 +317,33 @@ def test_gate_bwd_no_workspace_without_dw(gdr):
     """dw NULL needs no workspace: only the pointer checks of the tensors
     remain (a misaligned dy is still rejected)."""
     assert gate_bwd(gdr, dw=None, ws=None, wsb=0, dy=BAD) == 1
+
+
+def test_bwd_split_workspace_size(gdr):
+    """nseg = 1: the plain backward's workspace; otherwise the split
+    forward's pieces (with a discard buffer for the passes' outputs), N and
+    the end gradients (fp32 per segment state), and the backward workspace
+    of the segment batch; 0 where the call would reject the sizes."""
+    f = gdr.lib.gdr_chunk_bwd_split_workspace_size
+    up = lambda x: (x + 255) // 256 * 256
+    assert f(2, 96, 3, 128, 128, 1, 1) == gdr.gdr_chunk_bwd_workspace_size(2, 96, 3, 128, 128)
+    bn = 2 * 4 * 3
+    fwd = up(bn * 128 * 128 * 4) * 3 + up(2 * 96 * 3 * 128 * 2) * 2
+    bw = up(gdr.gdr_chunk_bwd_workspace_size(8, 24, 3, 128, 128))
+    assert f(2, 96, 3, 128, 128, 1, 4) == fwd + up(bn * 128 * 128 * 4) * 2 + bw
+    assert f(2, 96, 3, 128, 128, 1, 5) == 0
+    assert f(2, 96, 3, 96, 128, 1, 4) == 0
+
+
+@pytest.mark.parametrize("kw,code", [(dict(nseg=0), 1), (dict(nseg=7), 1), (dict(flags=4), 2),
+                                     (dict(ws=None), 1), (dict(wsb=64), 1), (dict(ddt=9), 2)])
+def test_bwd_split_validation(gdr, kw, code):
+    nseg = kw.get("nseg", 4)
+    flags = kw.get("flags", 0)
+    wsb = kw.get("wsb", gdr.lib.gdr_chunk_bwd_split_workspace_size(1, 64, 1, 64, 64, 1,
+                                                                     max(nseg, 1)))
+    ws = kw.get("ws", A16)
+    ddt = kw.get("ddt", 1)
+    assert gdr.lib.gdr_chunk_bwd_split(1, 64, 1, 64, 64, 1, A16, A16, A16, A16, A16, None, ddt,
+                                       A16, None, A16, A16, A16, A16, A16, None, nseg, flags, ws,
+                                       wsb, None) == code

@@ -416,3 +416,43 @@ def test_segment_split_composes_to_the_recurrence(nseg):
         Sin = Sin @ P + R
     np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-11)
     np.testing.assert_allclose(s_last, s_ref, rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("nseg", [2, 3])
+def test_segment_split_backward_composes(nseg):
+    """The sequence-split backward's identity, with the oracle only: a
+    segment's dL/dS_in is G_end P^T + N, N its backward from G_end = 0 and P
+    its transition; scanning G_end from the last segment and re-running each
+    segment's backward from its start state gives the whole sequence's
+    gradients."""
+    T, H, Dk, Dv = 24, 2, 5, 4
+    q, k, v, a, b, S0 = rand_gdn(60 + nseg, T=T, H=H, Dk=Dk, Dv=Dv)
+    g = np.random.Generator(np.random.PCG64(61))
+    do = g.standard_normal(v.shape)
+    dsf = g.standard_normal(S0.shape)
+    ref = oracle.gdn_bwd(q, k, v, a, b, S0, do, dsf)
+    L = T // nseg
+    seg = lambda x, p: x[:, p * L:(p + 1) * L]
+    eye = np.broadcast_to(np.eye(Dk), (1, H, Dk, Dk)).copy()
+    Sin, P, N = [], [], []
+    S = S0.copy()
+    for p in range(nseg):
+        qs, ks, vs, as_, bs = (seg(x, p) for x in (q, k, v, a, b))
+        Sin.append(S)
+        _, Pp = oracle.gdn_fwd(qs, ks, np.zeros((1, L, H, Dk)), as_, bs, eye)
+        _, S = oracle.gdn_fwd(qs, ks, vs, as_, bs, S)
+        P.append(Pp)
+        N.append(oracle.gdn_bwd(qs, ks, vs, as_, bs, Sin[p], seg(do, p), None)[5])
+    G = dsf.copy()
+    got = [np.zeros_like(x) for x in ref[:5]]
+    for p in reversed(range(nseg)):
+        qs, ks, vs, as_, bs = (seg(x, p) for x in (q, k, v, a, b))
+        gp = oracle.gdn_bwd(qs, ks, vs, as_, bs, Sin[p], seg(do, p), G)
+        np.testing.assert_allclose(gp[5], G @ np.swapaxes(P[p], -1, -2) + N[p], rtol=1e-10,
+                                   atol=1e-10)
+        for i in range(5):
+            got[i][:, p * L:(p + 1) * L] = gp[i]
+        G = gp[5]
+    for i in range(5):
+        np.testing.assert_allclose(got[i], ref[i], rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(G, ref[5], rtol=1e-9, atol=1e-10)

@@ -1,0 +1,75 @@
+"""GPU parity of gdr_chunk_bwd_split (the backward over segments side by
+side, composed through the carry's affine map) against the oracle's
+backward, at the plain backward's tolerance (1e-3 of rms per gradient)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gdr_gen import make_gdn
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+NAMES = ("dq", "dk", "dv", "dalpha", "dbeta", "ds0")
+
+
+def _check(gdr_lib, inp, nseg, seed, dout_dtype=torch.float32, norm=False, with_dsf=True):
+    print(f"bwd split nseg={nseg} {inp.meta} norm={norm}", flush=True)
+    g = np.random.Generator(np.random.PCG64(seed))
+    B, T, H, Dk = inp.q.shape
+    Dv = inp.v.shape[-1]
+    do = torch.from_numpy(g.standard_normal((B, T, H, Dv)).astype(np.float32)).to(dout_dtype)
+    dsf = (torch.from_numpy((0.1 * g.standard_normal((B, H, Dv, Dk))).astype(np.float32))
+           if with_dsf else None)
+    qn = torch.from_numpy(oracle.l2norm(inp.q)) if norm else inp.q
+    kn = torch.from_numpy(oracle.l2norm(inp.k)) if norm else inp.k
+    ref = list(oracle.gdn_bwd(qn, kn, inp.v, inp.alpha, inp.beta, inp.s0, do, dsf))
+    if norm:
+        ref[0], ref[1] = oracle.l2norm_bwd(inp.q, ref[0]), oracle.l2norm_bwd(inp.k, ref[1])
+    c = lambda x: None if x is None else x.cuda()
+    got = gdr_lib.gdr_chunk_bwd_split(c(inp.q), c(inp.k), c(inp.v), c(inp.alpha), c(inp.beta),
+                                      c(inp.s0), c(do), c(dsf), nseg=nseg, l2norm_qk=norm)
+    torch.cuda.synchronize()
+    errs = {n: oracle.err_rms(x.cpu(), y) for n, x, y in zip(NAMES, got, ref)}
+    print("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e <= TOL}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("nseg", [2, 4, 8])
+def test_bwd_split_long_memory(gdr_lib, nseg):
+    """alpha near 1: the carry through P^T matters."""
+    _check(gdr_lib, make_gdn(B=1, T=256, H=2, Dk=128, Dv=128, dtype="f32", seed=760 + nseg,
+                             alpha_shift=-4.0, s0_std=0.1), nseg, nseg)
+
+
+@pytest.mark.parametrize("nseg", [3, 5])
+def test_bwd_split_ragged_segments(gdr_lib, nseg):
+    """Segments of 30 and 18 tokens (not multiples of the 16-token chunk)."""
+    _check(gdr_lib, make_gdn(B=2, T=90, H=2, Dk=64, Dv=64, dtype="f32", seed=770 + nseg,
+                             alpha_shift=-1.0, s0_std=0.2), nseg, 10 + nseg)
+
+
+@pytest.mark.parametrize("dims", [(128, 64), (64, 128)])
+def test_bwd_split_dims(gdr_lib, dims):
+    _check(gdr_lib, make_gdn(B=1, T=128, H=3, Dk=dims[0], Dv=dims[1], dtype="f32",
+                             seed=780 + dims[0], alpha_shift=-2.0, s0_std=0.1), 4, 20)
+
+
+def test_bwd_split_bf16_norm_no_state(gdr_lib):
+    """bf16 inputs and dL/do, q, k normalised on load, no S_0 or dL/dS_T."""
+    _check(gdr_lib, make_gdn(B=1, T=192, H=2, Dk=128, Dv=128, dtype="bf16", seed=790,
+                             alpha_shift=-3.0, raw_qk=True), 4, 21, dout_dtype=torch.bfloat16,
+           norm=True, with_dsf=False)
+
+
+def test_bwd_split_one_segment_is_plain(gdr_lib):
+    inp = make_gdn(B=1, T=64, H=2, Dk=64, Dv=64, dtype="f32", seed=795, s0_std=0.1)
+    do = torch.randn((1, 64, 2, 64))
+    args = [x.cuda() for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.s0)] + [do.cuda()]
+    a = gdr_lib.gdr_chunk_bwd(*args)
+    b = gdr_lib.gdr_chunk_bwd_split(*args, nseg=1)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
