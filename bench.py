@@ -455,7 +455,36 @@ def bench_bwd_long(gdr, torch, warmup, steps, nseg=4):
         lambda: gdr.gdr_chunk_bwd(*args, do, dsf, workspace=wsp), warmup, steps)
     smean, smin, _, _ = time_launches(
         lambda: gdr.gdr_chunk_bwd_split(*args, do, dsf, nseg=nseg, workspace=wss), warmup, steps)
-    return dict(plain=pmean, split=smean, nseg=nseg, tokens=B * T)
+    del wsp, wss
+    # Gated Delta Rule-2 at the same shape (alpha per channel near 1)
+    from gdr_gen import make_gdn2
+    inp2 = make_gdn2(B=B, T=T, H=H, Dk=Dk, Dv=Dv, dtype="bf16", seed=1006, alpha_shift=-4.0,
+                     s0_std=0.02)
+    a2 = [x.to(dev) for x in (inp2.q, inp2.k, inp2.v, inp2.alpha, inp2.erase, inp2.write,
+                              inp2.s0)]
+    o2 = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+    sf2 = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+    wf = torch.empty(gdr.gdr_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, inp2.q.dtype, nseg),
+                     dtype=torch.uint8, device=dev)
+    fp, _, _, _ = time_launches(lambda: gdr.gdr2_chunk_fwd(*a2, out_dtype=torch.float32, o=o2,
+                                                           s_final=sf2), warmup, steps)
+    fs, _, _, _ = time_launches(lambda: gdr.gdr2_chunk_fwd_split(*a2, nseg=nseg,
+                                                                 out_dtype=torch.float32, o=o2,
+                                                                 s_final=sf2, workspace=wf),
+                                warmup, steps)
+    del wf
+    w2p = torch.empty(gdr.gdr2_chunk_bwd_workspace_size(B, T, H, Dk, Dv), dtype=torch.uint8,
+                      device=dev)
+    bp, _, _, _ = time_launches(lambda: gdr.gdr2_chunk_bwd(*a2, do, dsf, workspace=w2p),
+                                warmup, steps)
+    del w2p
+    w2s = torch.empty(gdr.gdr2_chunk_bwd_split_workspace_size(B, T, H, Dk, Dv, inp2.q.dtype,
+                                                              nseg),
+                      dtype=torch.uint8, device=dev)
+    bs, _, _, _ = time_launches(lambda: gdr.gdr2_chunk_bwd_split(*a2, do, dsf, nseg=nseg,
+                                                                 workspace=w2s), warmup, steps)
+    return dict(plain=pmean, split=smean, nseg=nseg, tokens=B * T, gdr2_fwd_plain=fp,
+                gdr2_fwd_split=fs, gdr2_bwd_plain=bp, gdr2_bwd_split=bs)
 
 
 def bench_copy(torch, warmup, steps, nbytes=512 << 20):
@@ -664,7 +693,11 @@ def main():
         out["backward_long_context"] = {
             "workload": "B1 H16 T32768 d128 bf16 inputs and dL/do, initial state, dL/dS_T",
             "split_ms": r["split"] * 1e3, "plain_ms": r["plain"] * 1e3, "nseg": r["nseg"],
-            "tokens/s_split": r["tokens"] / r["split"], "tokens/s_plain": r["tokens"] / r["plain"]}
+            "tokens/s_split": r["tokens"] / r["split"], "tokens/s_plain": r["tokens"] / r["plain"],
+            "gdr2": {"fwd_plain_ms": r["gdr2_fwd_plain"] * 1e3,
+                     "fwd_split_ms": r["gdr2_fwd_split"] * 1e3,
+                     "bwd_plain_ms": r["gdr2_bwd_plain"] * 1e3,
+                     "bwd_split_ms": r["gdr2_bwd_split"] * 1e3}}
     if "copy" in res:
         cp = res["copy"]
         out["copy_reference"] = {"what": "torch device-to-device copy, 512 MiB read + 512 MiB "

@@ -34,6 +34,7 @@ __all__ = ["gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd", "gdr_output_
            "gdr_chunk_fwd_split", "gdr_chunk_fwd_split_workspace_size",
            "gdr_output_gate_bwd", "gdr_output_gate_bwd_workspace_size",
            "gdr_chunk_bwd_split", "gdr_chunk_bwd_split_workspace_size",
+           "gdr2_chunk_fwd_split", "gdr2_chunk_bwd_split", "gdr2_chunk_bwd_split_workspace_size",
            "GdrError", "status_string", "lib", "LIB_PATH", "GDR_F32",
            "GDR_BF16", "GDR_L2NORM_QK"]
 
@@ -96,6 +97,14 @@ lib.gdr_chunk_bwd_split_workspace_size.restype = ctypes.c_size_t
 lib.gdr_chunk_bwd_split.argtypes = ([_I64] * 5 + [_E] + [_P] * 6 + [_E, _P, _P] + [_P] * 6 +
                                     [_I64, _U, _P, ctypes.c_size_t, _P])
 lib.gdr_chunk_bwd_split.restype = ctypes.c_int
+lib.gdr2_chunk_fwd_split.argtypes = ([_I64] * 5 + [_E] + [_P] * 7 + [_E, _P, _P, _I64, _U, _P,
+                                     ctypes.c_size_t, _P])
+lib.gdr2_chunk_fwd_split.restype = ctypes.c_int
+lib.gdr2_chunk_bwd_split_workspace_size.argtypes = [_I64] * 5 + [_E, _I64]
+lib.gdr2_chunk_bwd_split_workspace_size.restype = ctypes.c_size_t
+lib.gdr2_chunk_bwd_split.argtypes = ([_I64] * 5 + [_E] + [_P] * 7 + [_E, _P, _P] + [_P] * 7 +
+                                     [_I64, _U, _P, ctypes.c_size_t, _P])
+lib.gdr2_chunk_bwd_split.restype = ctypes.c_int
 lib.gdr_status_string.argtypes = [ctypes.c_int]
 lib.gdr_status_string.restype = ctypes.c_char_p
 lib.gdr_version.restype = ctypes.c_int
@@ -489,3 +498,75 @@ def gdr_chunk_bwd_split(q, k, v, alpha, beta, s0, dout, ds_final=None, *, nseg=8
         _ptr(da), _ptr(db), _ptr(ds0), nseg, GDR_L2NORM_QK if l2norm_qk else 0,
         _ptr(workspace), workspace.numel(), _stream(stream)))
     return dq, dk, dv, da, db, ds0
+
+
+def gdr2_chunk_fwd_split(q, k, v, alpha, erase, write, s0=None, *, nseg=8, out_dtype=None,
+                         o=None, s_final=None, want_state=True, l2norm_qk=False, workspace=None,
+                         stream=None):
+    """gdr2_chunk_fwd with each sequence split into ``nseg`` segments that
+    run side by side (T divisible by nseg); workspace as for
+    gdr_chunk_fwd_split."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if q.dtype not in _DT:
+        raise TypeError(f"unsupported input dtype {q.dtype}")
+    for name, x, d in (("q", q, Dk), ("k", k, Dk), ("v", v, Dv), ("alpha", alpha, Dk),
+                       ("erase", erase, Dk), ("write", write, Dv)):
+        _check(name, x, q.dtype, (B, T, H, d))
+    if s0 is not None:
+        _check("s0", s0, torch.float32, (B, H, Dv, Dk))
+    odt = q.dtype if out_dtype is None else out_dtype
+    if odt not in _DT:
+        raise TypeError(f"unsupported output dtype {odt}")
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=odt, device=q.device)
+    _check("o", o, odt, (B, T, H, Dv))
+    if s_final is None and want_state:
+        s_final = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=q.device)
+    if s_final is not None:
+        _check("s_final", s_final, torch.float32, (B, H, Dv, Dk))
+    need = gdr_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, q.dtype, nseg)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check("workspace", workspace, torch.uint8)
+    _run("gdr2_chunk_fwd_split", lib.gdr2_chunk_fwd_split(
+        B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase),
+        _ptr(write), _ptr(s0), _DT[odt], _ptr(o), _ptr(s_final), nseg,
+        GDR_L2NORM_QK if l2norm_qk else 0, _ptr(workspace), workspace.numel(), _stream(stream)))
+    return o, s_final
+
+
+def gdr2_chunk_bwd_split_workspace_size(B, T, H, Dk, Dv, dtype, nseg) -> int:
+    """Bytes of device workspace gdr2_chunk_bwd_split needs."""
+    return int(lib.gdr2_chunk_bwd_split_workspace_size(B, T, H, Dk, Dv, _DT[dtype], nseg))
+
+
+def gdr2_chunk_bwd_split(q, k, v, alpha, erase, write, s0, dout, ds_final=None, *, nseg=8,
+                         workspace=None, want_ds0=True, l2norm_qk=False, stream=None):
+    """gdr2_chunk_bwd with each sequence split into ``nseg`` segments that
+    run side by side.  Same arguments and results as gdr2_chunk_bwd."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if q.dtype not in _DT or dout.dtype not in _DT:
+        raise TypeError("q and dout must be float32 or bfloat16")
+    for name, x, d in (("q", q, Dk), ("k", k, Dk), ("v", v, Dv), ("alpha", alpha, Dk),
+                       ("erase", erase, Dk), ("write", write, Dv)):
+        _check(name, x, q.dtype, (B, T, H, d))
+    _check("dout", dout, dout.dtype, (B, T, H, Dv))
+    if s0 is not None:
+        _check("s0", s0, torch.float32, (B, H, Dv, Dk))
+    if ds_final is not None:
+        _check("ds_final", ds_final, torch.float32, (B, H, Dv, Dk))
+    need = gdr2_chunk_bwd_split_workspace_size(B, T, H, Dk, Dv, q.dtype, nseg)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check("workspace", workspace, torch.uint8)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    out = [torch.empty((B, T, H, d), **f32) for d in (Dk, Dk, Dv, Dk, Dk, Dv)]
+    ds0 = torch.empty((B, H, Dv, Dk), **f32) if want_ds0 else None
+    _run("gdr2_chunk_bwd_split", lib.gdr2_chunk_bwd_split(
+        B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase),
+        _ptr(write), _ptr(s0), _DT[dout.dtype], _ptr(dout), _ptr(ds_final),
+        *[_ptr(x) for x in out], _ptr(ds0), nseg, GDR_L2NORM_QK if l2norm_qk else 0,
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return tuple(out) + (ds0,)

@@ -190,6 +190,7 @@ static gdr_status_t split_states(const ChunkArgs& a, const SplitLayout& l, char*
     ChunkArgs pa = a;
     pa.Dv = a.Dk;
     pa.v = vz;
+    if (a.gated2) pa.write = vz;   // w (.) v = 0 either way; w needs Dk columns here
     pa.s0 = P;
     pa.s_final = P;
     pa.o = oP;
@@ -212,6 +213,38 @@ extern "C" size_t gdr_chunk_fwd_split_workspace_size(int64_t B, int64_t T, int64
     return split_layout(B, T, H, Dk, Dv, in_dt, nseg).total;
 }
 
+// The split forward once the segment batch `a` (inputs, B nseg x T / nseg)
+// is set and the common arguments are validated.
+static gdr_status_t fwd_split_run(ChunkArgs& a, int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                  int64_t Dv, gdr_dtype_t in_dt, const float* s0, void* o,
+                                  float* s_final, int64_t nseg, void* workspace,
+                                  size_t workspace_bytes) {
+    if (T % nseg != 0 || !sizes_ok(B * nseg, H, 1)) return GDR_ERR_INVALID;
+    if (!grid_ok(B * T * H * Dk) || !grid_ok(B * nseg * H * Dk * Dk) || !grid_ok(B * H * Dv * Dk))
+        return GDR_ERR_INVALID;
+    if (B * nseg * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
+    if (!ptrs_ok({workspace}) || !opt_ok(s0) || !opt_ok(s_final)) return GDR_ERR_INVALID;
+    const SplitLayout l = split_layout(B, T, H, Dk, Dv, in_dt, nseg);
+    if (workspace_bytes < l.total) return GDR_ERR_INVALID;
+    char* w = static_cast<char*>(workspace);
+    float* Sin = reinterpret_cast<float*>(w + l.R + l.P);
+    // the segments as a batch: [B, T, H, d] is [B nseg, T / nseg, H, d]
+    a.B = B * nseg;
+    a.T = T / nseg;
+    gdr_status_t st;
+    if ((st = split_states(a, l, w, B, nseg, s0, o)) != GDR_OK) return st;
+    // 4. every segment from its start state: o, and the final states in place
+    ChunkArgs f = a;
+    f.s0 = Sin;
+    f.s_final = Sin;
+    f.o = o;
+    if ((st = chunk_run(f)) != GDR_OK) return st;
+    if (s_final)
+        return from_hip(launch_seg_state(Sin, s_final, B, (int)nseg, (int)nseg - 1, H * Dv * Dk,
+                                         a.stream));
+    return GDR_OK;
+}
+
 extern "C" gdr_status_t gdr_chunk_fwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                             int64_t Dv, gdr_dtype_t in_dt, const void* q,
                                             const void* k, const void* v, const float* alpha,
@@ -227,21 +260,9 @@ extern "C" gdr_status_t gdr_chunk_fwd_split(int64_t B, int64_t T, int64_t H, int
     ChunkArgs a{};
     gdr_status_t st = chunk_common(B, T, H, Dk, Dv, in_dt, out_dt, a);
     if (st != GDR_OK) return st;
-    if (T % nseg != 0 || !sizes_ok(B * nseg, H, 1)) return GDR_ERR_INVALID;
-    if (!grid_ok(B * T * H * Dk) || !grid_ok(B * nseg * H * Dk * Dk) || !grid_ok(B * H * Dv * Dk))
-        return GDR_ERR_INVALID;
-    if (B * nseg * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
-    if (!ptrs_ok({q, k, v, workspace}) || !elem_ok(alpha, 4) || !elem_ok(beta, 4) ||
+    if (!ptrs_ok({q, k, v}) || !elem_ok(alpha, 4) || !elem_ok(beta, 4) ||
         !elem_ok(o, out_dt == GDR_BF16 ? 2 : 4))
         return GDR_ERR_INVALID;
-    if (!opt_ok(s0) || !opt_ok(s_final)) return GDR_ERR_INVALID;
-    const SplitLayout l = split_layout(B, T, H, Dk, Dv, in_dt, nseg);
-    if (workspace_bytes < l.total) return GDR_ERR_INVALID;
-    char* w = static_cast<char*>(workspace);
-    float* Sin = reinterpret_cast<float*>(w + l.R + l.P);
-    // the segments as a batch: [B, T, H, d] is [B nseg, T / nseg, H, d]
-    a.B = B * nseg;
-    a.T = T / nseg;
     a.gated2 = false;
     a.l2norm = (flags & GDR_L2NORM_QK) != 0;
     a.q = q;
@@ -250,46 +271,124 @@ extern "C" gdr_status_t gdr_chunk_fwd_split(int64_t B, int64_t T, int64_t H, int
     a.alpha = alpha;
     a.beta = beta;
     a.stream = stream;
-    if ((st = split_states(a, l, w, B, nseg, s0, o)) != GDR_OK) return st;
-    // 4. every segment from its start state: o, and the final states in place
-    ChunkArgs f = a;
-    f.s0 = Sin;
-    f.s_final = Sin;
-    f.o = o;
-    if ((st = chunk_run(f)) != GDR_OK) return st;
-    if (s_final)
-        return from_hip(launch_seg_state(Sin, s_final, B, (int)nseg, (int)nseg - 1, H * Dv * Dk,
-                                         stream));
-    return GDR_OK;
+    return fwd_split_run(a, B, T, H, Dk, Dv, in_dt, s0, o, s_final, nseg, workspace,
+                         workspace_bytes);
 }
 
-// Sequence-split backward (scalar gates): the forward's split pieces, the
-// segments' own contributions N and end gradients Gend, and the backward
-// workspace of the segment batch.
+extern "C" gdr_status_t gdr2_chunk_fwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                             int64_t Dv, gdr_dtype_t in_dt, const void* q,
+                                             const void* k, const void* v, const void* alpha,
+                                             const void* erase, const void* write,
+                                             const float* s0, gdr_dtype_t out_dt, void* o,
+                                             float* s_final, int64_t nseg, uint32_t flags,
+                                             void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream) {
+    if (nseg < 1 || nseg > (1 << 20)) return GDR_ERR_INVALID;
+    if (nseg == 1 || T == 0 || B == 0 || H == 0)
+        return gdr2_chunk_fwd_ex(B, T, H, Dk, Dv, in_dt, q, k, v, alpha, erase, write, s0,
+                                 out_dt, o, s_final, flags, stream);
+    if (!flags_ok(flags)) return GDR_ERR_UNSUPPORTED;
+    ChunkArgs a{};
+    gdr_status_t st = chunk_common(B, T, H, Dk, Dv, in_dt, out_dt, a);
+    if (st != GDR_OK) return st;
+    if (!ptrs_ok({q, k, v, alpha, erase, write}) || !elem_ok(o, out_dt == GDR_BF16 ? 2 : 4))
+        return GDR_ERR_INVALID;
+    a.gated2 = true;
+    a.l2norm = (flags & GDR_L2NORM_QK) != 0;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.erase = erase;
+    a.write = write;
+    a.stream = stream;
+    return fwd_split_run(a, B, T, H, Dk, Dv, in_dt, s0, o, s_final, nseg, workspace,
+                         workspace_bytes);
+}
+
+// Sequence-split backward: the forward's split pieces, the segments' own
+// contributions N and end gradients Gend, and the backward workspace of the
+// segment batch.
 namespace {
 struct BwdSplitLayout {
     SplitLayout f;
     size_t N, G, bw, total;
 };
 BwdSplitLayout bwd_split_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
-                                gdr_dtype_t in_dt, int64_t nseg) {
+                                gdr_dtype_t in_dt, int64_t nseg, bool gated2) {
     BwdSplitLayout l{};
     l.f = split_layout(B, T, H, Dk, Dv, in_dt, nseg, true);
     const size_t bn = (size_t)(B * nseg * H);
     l.N = up256(bn * Dv * Dk * 4);
     l.G = up256(bn * Dv * Dk * 4);
-    l.bw = up256(bwd_workspace_bytes(B * nseg, T / nseg, H, Dk, Dv));
+    l.bw = up256(gated2 ? bwd2_workspace_bytes(B * nseg, T / nseg, H, Dk, Dv)
+                        : bwd_workspace_bytes(B * nseg, T / nseg, H, Dk, Dv));
     l.total = l.f.total + l.N + l.G + l.bw;
     return l;
 }
 }  // namespace
+
+// The split backward once the segment batch `a` (forward inputs) is set and
+// the arguments are validated.  run_bwd(s0, ds_final, ds0, workspace) runs
+// the backward over the segment batch.
+template <typename RunBwd>
+static gdr_status_t bwd_split_run(ChunkArgs& a, const BwdSplitLayout& l, void* workspace,
+                                  int64_t B, int64_t T, int64_t H, int64_t nseg, const float* s0,
+                                  const float* ds_final, float* ds0, RunBwd run_bwd) {
+    char* w = static_cast<char*>(workspace);
+    float* P = reinterpret_cast<float*>(w + l.f.R);
+    float* Sin = reinterpret_cast<float*>(w + l.f.R + l.f.P);
+    float* N = reinterpret_cast<float*>(w + l.f.total);
+    float* G = reinterpret_cast<float*>(w + l.f.total + l.N);
+    void* bw = w + l.f.total + l.N + l.G;
+    a.B = B * nseg;
+    a.T = T / nseg;
+    gdr_status_t st;
+    // the segments' start states S_in and transitions P
+    if ((st = split_states(a, l.f, w, B, nseg, s0, nullptr)) != GDR_OK) return st;
+    // each segment's own contribution to dL/dS_in: its backward from a zero
+    // end gradient (its other gradients are overwritten below)
+    hipError_t e = run_bwd(Sin, nullptr, N, bw);
+    if (e != hipSuccess) return GDR_ERR_DEVICE;
+    // the segments' end gradients, last to first
+    SplitScanArgs rs{B, H, a.Dk, a.Dv, (int)nseg, ds_final, N, P, G, a.stream};
+    if ((e = launch_split_rscan(rs)) != hipSuccess) return GDR_ERR_DEVICE;
+    // every segment from its start state with its end gradient
+    if ((e = run_bwd(Sin, G, N, bw)) != hipSuccess) return GDR_ERR_DEVICE;
+    if (ds0)
+        return from_hip(launch_seg_state(N, ds0, B, (int)nseg, 0, H * a.Dv * a.Dk, a.stream));
+    return GDR_OK;
+}
+
+static gdr_status_t bwd_split_check(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                    gdr_dtype_t in_dt, gdr_dtype_t dout_dt, int64_t nseg,
+                                    uint32_t flags, ChunkArgs& a) {
+    if (!flags_ok(flags)) return GDR_ERR_UNSUPPORTED;
+    gdr_status_t st = chunk_common(B, T, H, Dk, Dv, in_dt, GDR_BF16, a);
+    if (st != GDR_OK) return st;
+    if (!dtype_ok(dout_dt)) return GDR_ERR_UNSUPPORTED;
+    if (T % nseg != 0 || !sizes_ok(B * nseg, H, 1)) return GDR_ERR_INVALID;
+    if (!grid_ok(B * T * H * Dk) || !grid_ok(B * nseg * H * Dk * Dk) || !grid_ok(B * H * Dv * Dk))
+        return GDR_ERR_INVALID;
+    if (B * nseg * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
+    a.l2norm = (flags & GDR_L2NORM_QK) != 0;
+    return GDR_OK;
+}
 
 extern "C" size_t gdr_chunk_bwd_split_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                                      int64_t Dv, gdr_dtype_t in_dt,
                                                      int64_t nseg) {
     if (nseg == 1 && dtype_ok(in_dt)) return gdr_chunk_bwd_workspace_size(B, T, H, Dk, Dv);
     if (gdr_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, in_dt, nseg) == 0) return 0;
-    return bwd_split_layout(B, T, H, Dk, Dv, in_dt, nseg).total;
+    return bwd_split_layout(B, T, H, Dk, Dv, in_dt, nseg, false).total;
+}
+
+extern "C" size_t gdr2_chunk_bwd_split_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                                      int64_t Dv, gdr_dtype_t in_dt,
+                                                      int64_t nseg) {
+    if (nseg == 1 && dtype_ok(in_dt)) return gdr2_chunk_bwd_workspace_size(B, T, H, Dk, Dv);
+    if (gdr_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, in_dt, nseg) == 0) return 0;
+    return bwd_split_layout(B, T, H, Dk, Dv, in_dt, nseg, true).total;
 }
 
 extern "C" gdr_status_t gdr_chunk_bwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
@@ -306,39 +405,22 @@ extern "C" gdr_status_t gdr_chunk_bwd_split(int64_t B, int64_t T, int64_t H, int
         return gdr_chunk_bwd_ex(B, T, H, Dk, Dv, in_dt, q, k, v, alpha, beta, s0, dout_dt, dout,
                                 ds_final, dq, dk, dv, dalpha, dbeta, ds0, workspace,
                                 workspace_bytes, flags, stream);
-    if (!flags_ok(flags)) return GDR_ERR_UNSUPPORTED;
     ChunkArgs a{};
-    gdr_status_t st = chunk_common(B, T, H, Dk, Dv, in_dt, GDR_BF16, a);
+    gdr_status_t st = bwd_split_check(B, T, H, Dk, Dv, in_dt, dout_dt, nseg, flags, a);
     if (st != GDR_OK) return st;
-    if (!dtype_ok(dout_dt)) return GDR_ERR_UNSUPPORTED;
-    if (T % nseg != 0 || !sizes_ok(B * nseg, H, 1)) return GDR_ERR_INVALID;
-    if (!grid_ok(B * T * H * Dk) || !grid_ok(B * nseg * H * Dk * Dk) || !grid_ok(B * H * Dv * Dk))
-        return GDR_ERR_INVALID;
-    if (B * nseg * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
     if (!ptrs_ok({q, k, v, dout, dq, dk, dv, workspace}) || !elem_ok(alpha, 4) ||
         !elem_ok(beta, 4) || !elem_ok(dalpha, 4) || !elem_ok(dbeta, 4))
         return GDR_ERR_INVALID;
     if (!opt_ok(s0) || !opt_ok(ds_final) || !opt_ok(ds0)) return GDR_ERR_INVALID;
-    const BwdSplitLayout l = bwd_split_layout(B, T, H, Dk, Dv, in_dt, nseg);
+    const BwdSplitLayout l = bwd_split_layout(B, T, H, Dk, Dv, in_dt, nseg, false);
     if (workspace_bytes < l.total) return GDR_ERR_INVALID;
-    char* w = static_cast<char*>(workspace);
-    float* P = reinterpret_cast<float*>(w + l.f.R);
-    float* Sin = reinterpret_cast<float*>(w + l.f.R + l.f.P);
-    float* N = reinterpret_cast<float*>(w + l.f.total);
-    float* G = reinterpret_cast<float*>(w + l.f.total + l.N);
-    void* bw = w + l.f.total + l.N + l.G;
-    a.B = B * nseg;
-    a.T = T / nseg;
     a.gated2 = false;
-    a.l2norm = (flags & GDR_L2NORM_QK) != 0;
     a.q = q;
     a.k = k;
     a.v = v;
     a.alpha = alpha;
     a.beta = beta;
     a.stream = stream;
-    // the segments' start states S_in and transitions P
-    if ((st = split_states(a, l.f, w, B, nseg, s0, nullptr)) != GDR_OK) return st;
     BwdArgs b{};
     b.B = B * nseg;
     b.T = T / nseg;
@@ -354,29 +436,85 @@ extern "C" gdr_status_t gdr_chunk_bwd_split(int64_t B, int64_t T, int64_t H, int
     b.dout = dout;
     b.alpha = alpha;
     b.beta = beta;
-    b.s0 = Sin;
     b.dq = dq;
     b.dk = dk;
     b.dv = dv;
     b.dalpha = dalpha;
     b.dbeta = dbeta;
-    b.workspace = bw;
     b.stream = stream;
-    // each segment's own contribution to dL/dS_in: its backward from a zero
-    // end gradient (the other gradients are overwritten below)
-    b.ds_final = nullptr;
-    b.ds0 = N;
-    hipError_t e = launch_chunk_bwd(b);
-    if (e != hipSuccess) return GDR_ERR_DEVICE;
-    // the segments' end gradients, last to first
-    SplitScanArgs rs{B, H, Dk, Dv, (int)nseg, ds_final, N, P, G, stream};
-    if ((e = launch_split_rscan(rs)) != hipSuccess) return GDR_ERR_DEVICE;
-    // every segment from its start state with its end gradient
-    b.ds_final = G;
-    b.ds0 = N;
-    if ((e = launch_chunk_bwd(b)) != hipSuccess) return GDR_ERR_DEVICE;
-    if (ds0) return from_hip(launch_seg_state(N, ds0, B, (int)nseg, 0, H * Dv * Dk, stream));
-    return GDR_OK;
+    return bwd_split_run(a, l, workspace, B, T, H, nseg, s0, ds_final, ds0,
+                         [&](const float* sin, const float* gend, float* d0, void* bw) {
+                             b.s0 = sin;
+                             b.ds_final = gend;
+                             b.ds0 = d0;
+                             b.workspace = bw;
+                             return launch_chunk_bwd(b);
+                         });
+}
+
+extern "C" gdr_status_t gdr2_chunk_bwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                             int64_t Dv, gdr_dtype_t in_dt, const void* q,
+                                             const void* k, const void* v, const void* alpha,
+                                             const void* erase, const void* write,
+                                             const float* s0, gdr_dtype_t dout_dt,
+                                             const void* dout, const float* ds_final, float* dq,
+                                             float* dk, float* dv, float* dalpha, float* derase,
+                                             float* dwrite, float* ds0, int64_t nseg,
+                                             uint32_t flags, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
+    if (nseg < 1 || nseg > (1 << 20)) return GDR_ERR_INVALID;
+    if (nseg == 1 || T == 0 || B == 0 || H == 0)   // the plain call
+        return gdr2_chunk_bwd_ex(B, T, H, Dk, Dv, in_dt, q, k, v, alpha, erase, write, s0,
+                                 dout_dt, dout, ds_final, dq, dk, dv, dalpha, derase, dwrite, ds0,
+                                 workspace, workspace_bytes, flags, stream);
+    ChunkArgs a{};
+    gdr_status_t st = bwd_split_check(B, T, H, Dk, Dv, in_dt, dout_dt, nseg, flags, a);
+    if (st != GDR_OK) return st;
+    if (!ptrs_ok({q, k, v, alpha, erase, write, dout, dq, dk, dv, dalpha, derase, dwrite,
+                  workspace}))
+        return GDR_ERR_INVALID;
+    if (!opt_ok(s0) || !opt_ok(ds_final) || !opt_ok(ds0)) return GDR_ERR_INVALID;
+    const BwdSplitLayout l = bwd_split_layout(B, T, H, Dk, Dv, in_dt, nseg, true);
+    if (workspace_bytes < l.total) return GDR_ERR_INVALID;
+    a.gated2 = true;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.erase = erase;
+    a.write = write;
+    a.stream = stream;
+    Bwd2Args b{};
+    b.B = B * nseg;
+    b.T = T / nseg;
+    b.H = H;
+    b.Dk = Dk;
+    b.Dv = Dv;
+    b.in_bf16 = in_dt == GDR_BF16;
+    b.dout_bf16 = dout_dt == GDR_BF16;
+    b.l2norm = a.l2norm;
+    b.q = q;
+    b.k = k;
+    b.v = v;
+    b.alpha = alpha;
+    b.erase = erase;
+    b.write = write;
+    b.dout = dout;
+    b.dq = dq;
+    b.dk = dk;
+    b.dv = dv;
+    b.dalpha = dalpha;
+    b.derase = derase;
+    b.dwrite = dwrite;
+    b.stream = stream;
+    return bwd_split_run(a, l, workspace, B, T, H, nseg, s0, ds_final, ds0,
+                         [&](const float* sin, const float* gend, float* d0, void* bw) {
+                             b.s0 = sin;
+                             b.ds_final = gend;
+                             b.ds0 = d0;
+                             b.workspace = bw;
+                             return launch_chunk2_bwd(b);
+                         });
 }
 
 extern "C" gdr_status_t gdr2_chunk_fwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk,

@@ -295,6 +295,41 @@ gdr_status_t gdr_chunk_bwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                  hipStream_t stream);
 
 /*
+ * The same two sequence-split calls for Gated Delta Rule-2: the rule maps a
+ * segment's start state affinely as well (per token S -> S diag(alpha)
+ * (I - e k^T) + ...), so P_p is again the segment run with v = 0 from the
+ * identity (the P pass uses a zero write gate too).  Arguments as for
+ * gdr2_chunk_fwd_ex and gdr2_chunk_bwd_ex plus nseg, flags and the
+ * workspace; gdr2_chunk_fwd_split takes gdr_chunk_fwd_split_workspace_size
+ * bytes (the same layout), gdr2_chunk_bwd_split its own size below.
+ */
+gdr_status_t gdr2_chunk_fwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                  int64_t Dv, gdr_dtype_t in_dt, const void *q,
+                                  const void *k, const void *v,
+                                  const void *alpha, const void *erase,
+                                  const void *write, const float *s0,
+                                  gdr_dtype_t out_dt, void *o, float *s_final,
+                                  int64_t nseg, uint32_t flags,
+                                  void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+size_t gdr2_chunk_bwd_split_workspace_size(int64_t B, int64_t T, int64_t H,
+                                           int64_t Dk, int64_t Dv,
+                                           gdr_dtype_t in_dt, int64_t nseg);
+
+gdr_status_t gdr2_chunk_bwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                  int64_t Dv, gdr_dtype_t in_dt, const void *q,
+                                  const void *k, const void *v,
+                                  const void *alpha, const void *erase,
+                                  const void *write, const float *s0,
+                                  gdr_dtype_t dout_dt, const void *dout,
+                                  const float *ds_final, float *dq, float *dk,
+                                  float *dv, float *dalpha, float *derase,
+                                  float *dwrite, float *ds0, int64_t nseg,
+                                  uint32_t flags, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Output gate of the block, applied to the rule's output o per token and
  * head over the Dv channels ("Gated DeltaNet-2", agihunt.info: the
  * recurrent output passes an RMSNorm and a SiLU output gate; GDN review on

@@ -33,6 +33,8 @@ def test_header_declares_the_three_operations():
               "gdr_chunk_bwd_ex", "gdr2_chunk_bwd_ex",
               "gdr_output_gate_bwd", "gdr_output_gate_bwd_workspace_size",
               "gdr_chunk_bwd_split", "gdr_chunk_bwd_split_workspace_size",
+              "gdr2_chunk_fwd_split", "gdr2_chunk_bwd_split",
+              "gdr2_chunk_bwd_split_workspace_size",
               "gdr_status_string", "gdr_version"):
         assert n in names, names
 
