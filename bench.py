@@ -529,7 +529,8 @@ def main():
                     help="time one operation only (for profiling)")
     ap.add_argument("--skip", default="",
                     help="comma-separated legs not to run (the profiled command skips l2norm, "
-                         "whose plain calls reuse the headline kernels)")
+                         "longctx and bwd_long, whose calls reuse the headline and backward "
+                         "kernels' names at other shapes)")
     ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarize rocprofv3 CSV output into OUT and the traffic JSON, then exit")
     ap.add_argument("--command", default="", help="the profiling command, recorded in --summarize")
