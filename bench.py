@@ -498,10 +498,21 @@ def bench_copy(torch, warmup, steps, nbytes=512 << 20):
     return dict(mean=mean, min=mn, bytes=2 * nbytes)
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(inp, repeats=3):
-    """The fp64 oracle on the whole workload (B8 H16 T4096 d128: it finishes
-    in about a second on the host), best of `repeats`, on every thread the
-    oracle's OpenMP runtime uses."""
+    """The fp64 oracle on the whole workload (B8 H16 T4096 d128 finishes in
+    about half a second on 16 host threads), best of `repeats`, on every thread the
+    oracle's OpenMP runtime uses; then once more on one thread."""
     import oracle
     qq, kk, vv, aa, bb = (oracle._f64(x) for x in (inp.q, inp.k, inp.v, inp.alpha,
                                                      inp.beta))   # conversion excluded
@@ -510,11 +521,22 @@ def cpu_baseline(inp, repeats=3):
         t0 = time.perf_counter()
         oracle.gdn_fwd(qq, kk, vv, aa, bb, None)
         best = min(best, time.perf_counter() - t0)
-    tokens = inp.q.shape[0] * inp.q.shape[1]
-    return dict(value=tokens / best, unit="tokens/s", cores=oracle.num_threads(),
-                kind="oracle",
-                sample=f"whole workload B8 H16 T4096 d128 ({tokens} tokens x 16 heads), "
-                       f"fp64 token-by-token recurrence, best of {repeats}: {best:.2f} s")
+    B, T, H, Dk = inp.q.shape
+    tokens = B * T
+    cores = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.gdn_fwd(qq, kk, vv, aa, bb, None)
+        one = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(cores)
+    return dict(value=tokens / best, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"whole workload B{B} H{H} T{T} d{Dk} ({tokens} tokens x {H} heads), "
+                       f"fp64 token-by-token recurrence, best of {repeats}: {best:.2f} s; "
+                       f"one thread, one run: {one:.2f} s",
+                one_thread=dict(value=tokens / one, unit="tokens/s", seconds=one),
+                cpu_model=_cpu_model())
 
 
 def main():
