@@ -629,7 +629,8 @@ def main():
                            "traffic": measured_traffic("gdn"),
                            "kernel": "chunk_bf16_kernel<128,128,64,float,false>",
                            "algorithmic_bytes_per_launch": g["bytes"],
-                           "launch_us_mean": g["mean"] * 1e6, "launch_us_min": g["min"] * 1e6}
+                           "launch_us_mean": g["mean"] * 1e6, "launch_us_median": g["median"] * 1e6,
+                           "launch_us_min": g["min"] * 1e6}
         tf = g["flops"] / g["mean"] / 1e12
         out["mfma"] = {"achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                        "frac": tf / BF16_PEAK_TFLOPS, "flops_per_launch": g["flops"]}
