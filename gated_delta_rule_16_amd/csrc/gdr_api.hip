@@ -53,6 +53,10 @@ bool sizes_ok(int64_t a, int64_t b, int64_t c) {
 // An elementwise launch over n items, 256 per workgroup, fits the grid.
 bool grid_ok(int64_t n) { return (n + 255) / 256 <= 0x7fffffffLL; }
 
+// The chunk kernels address one chunk of tokens (H heads x d channels each)
+// with 32-bit byte offsets from a 64-bit chunk base.
+bool heads_ok(int64_t H) { return H <= GDR_MAX_HEADS; }
+
 }  // namespace
 
 hipError_t launch_state_copy(const float* s0, float* s_final, int64_t n, hipStream_t st) {
@@ -71,6 +75,7 @@ static gdr_status_t chunk_common(int64_t B, int64_t T, int64_t H, int64_t Dk, in
                                  gdr_dtype_t in_dt, gdr_dtype_t out_dt, ChunkArgs& a) {
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0) return GDR_ERR_INVALID;
     if (!sizes_ok(B, T, H) || !sizes_ok(B * T * H, Dk > Dv ? Dk : Dv, 1)) return GDR_ERR_INVALID;
+    if (!heads_ok(H)) return GDR_ERR_INVALID;
     if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return GDR_ERR_UNSUPPORTED;
     if (!dims_ok(Dk, Dv)) return GDR_ERR_UNSUPPORTED;
     if (B * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
@@ -207,6 +212,7 @@ extern "C" size_t gdr_chunk_fwd_split_workspace_size(int64_t B, int64_t T, int64
     if (B < 0 || T < 0 || H < 0 || nseg < 1 || nseg > (1 << 20)) return 0;
     if (!dims_ok(Dk, Dv) || !dtype_ok(in_dt)) return 0;
     if (!sizes_ok(B, T, H) || !sizes_ok(B * T * H, Dk > Dv ? Dk : Dv, 1)) return 0;
+    if (!heads_ok(H)) return 0;
     if (!sizes_ok(B * nseg, H, 1)) return 0;
     if (nseg == 1 || T == 0 || B == 0 || H == 0) return 0;
     if (T % nseg != 0) return 0;
@@ -676,6 +682,7 @@ extern "C" size_t gdr_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, 
                                                int64_t Dv) {
     if (B < 0 || T < 0 || H < 0 || !dims_ok(Dk, Dv)) return 0;
     if (!sizes_ok(B, T, H) || !sizes_ok(B * T * H, Dk > Dv ? Dk : Dv, 1)) return 0;
+    if (!heads_ok(H)) return 0;
     return bwd_workspace_bytes(B, T, H, Dk, Dv);
 }
 
@@ -691,6 +698,7 @@ extern "C" gdr_status_t gdr_chunk_bwd_ex(int64_t B, int64_t T, int64_t H, int64_
     if (!flags_ok(flags)) return GDR_ERR_UNSUPPORTED;
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0) return GDR_ERR_INVALID;
     if (!sizes_ok(B, T, H) || !sizes_ok(B * T * H, Dk > Dv ? Dk : Dv, 1)) return GDR_ERR_INVALID;
+    if (!heads_ok(H)) return GDR_ERR_INVALID;
     if (!dtype_ok(in_dt) || !dtype_ok(dout_dt)) return GDR_ERR_UNSUPPORTED;
     if (!dims_ok(Dk, Dv)) return GDR_ERR_UNSUPPORTED;
     if (B * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
@@ -750,6 +758,7 @@ extern "C" size_t gdr2_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H,
                                                 int64_t Dv) {
     if (B < 0 || T < 0 || H < 0 || !dims_ok(Dk, Dv)) return 0;
     if (!sizes_ok(B, T, H) || !sizes_ok(B * T * H, Dk > Dv ? Dk : Dv, 1)) return 0;
+    if (!heads_ok(H)) return 0;
     return bwd2_workspace_bytes(B, T, H, Dk, Dv);
 }
 
@@ -765,6 +774,7 @@ extern "C" gdr_status_t gdr2_chunk_bwd_ex(int64_t B, int64_t T, int64_t H, int64
     if (!flags_ok(flags)) return GDR_ERR_UNSUPPORTED;
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0) return GDR_ERR_INVALID;
     if (!sizes_ok(B, T, H) || !sizes_ok(B * T * H, Dk > Dv ? Dk : Dv, 1)) return GDR_ERR_INVALID;
+    if (!heads_ok(H)) return GDR_ERR_INVALID;
     if (!dtype_ok(in_dt) || !dtype_ok(dout_dt)) return GDR_ERR_UNSUPPORTED;
     if (!dims_ok(Dk, Dv)) return GDR_ERR_UNSUPPORTED;
     if (B * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;

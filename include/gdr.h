@@ -36,7 +36,9 @@
  *   - Arguments are validated on the host before anything is launched; on
  *     any error nothing is written.  Status codes:
  *       GDR_ERR_INVALID      a required pointer is NULL, a size is negative,
- *                            or a pointer is misaligned: q, k, v, the
+ *                            H exceeds GDR_MAX_HEADS in a chunkwise call
+ *                            (forward, split or backward), or a pointer is
+ *                            misaligned: q, k, v, the
  *                            channel gates, s0, s_final and the decode
  *                            state need 16-byte alignment; the scalar gates
  *                            and o need element alignment;
@@ -76,6 +78,11 @@ typedef enum {
     GDR_ERR_UNSUPPORTED = 2,
     GDR_ERR_DEVICE = 3
 } gdr_status_t;
+
+/* Largest head count the chunkwise calls accept: their kernels address one
+ * chunk of tokens (H heads x d channels per token) with 32-bit byte offsets
+ * from a 64-bit chunk base. */
+#define GDR_MAX_HEADS 65536
 
 typedef enum {
     GDR_F32 = 0,   /* IEEE binary32 */

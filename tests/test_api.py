@@ -349,3 +349,24 @@ def test_bwd_split_validation(gdr, kw, code):
     assert gdr.lib.gdr_chunk_bwd_split(1, 64, 1, 64, 64, 1, A16, A16, A16, A16, A16, None, ddt,
                                        A16, None, A16, A16, A16, A16, A16, None, nseg, flags, ws,
                                        wsb, None) == code
+
+
+def test_head_count_bound(gdr):
+    """The chunkwise calls take at most GDR_MAX_HEADS heads (their kernels
+    address a chunk of tokens with 32-bit byte offsets): one more is
+    rejected before anything is launched, the bound itself is accepted
+    (B = 0, so nothing is launched either way)."""
+    hdr = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    hmax = int(re.search(r"#define GDR_MAX_HEADS (\d+)", hdr).group(1))
+    assert hmax == 65536
+    for H, code in ((hmax, 0), (hmax + 1, 1)):
+        assert chunk(gdr, B=0, H=H) == code
+        assert chunk2(gdr, B=0, H=H) == code
+        assert split(gdr, B=0, H=H, wsb=0) == code
+        assert bwd(gdr, B=0, H=H, wsb=0) == code
+        assert bwd2(gdr, B=0, H=H, wsb=0) == code
+    big = hmax + 1
+    assert gdr.gdr_chunk_bwd_workspace_size(1, 8, big, 64, 64) == 0
+    assert gdr.gdr2_chunk_bwd_workspace_size(1, 8, big, 64, 64) == 0
+    assert gdr.lib.gdr_chunk_fwd_split_workspace_size(1, 64, big, 64, 64, 1, 4) == 0
+    assert gdr.gdr_chunk_bwd_workspace_size(1, 8, hmax, 64, 64) > 0
