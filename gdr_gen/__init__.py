@@ -36,6 +36,7 @@ import torch
 __all__ = [
     "GdnInputs", "Gdn2Inputs", "DecodeInputs",
     "make_gdn", "make_gdn2", "make_decode", "make_config", "CONFIGS", "make_gate",
+    "make_device",
 ]
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -252,3 +253,39 @@ def make_config(idx, seed: Optional[int] = None, **overrides):
     if kind == "gdn2":
         return make_gdn2(seed=seed, name=name, **c)
     return make_decode(seed=seed, name=name, **c)
+
+
+def make_device(shapes: dict, seed: int, device="cuda", slab: int = 1 << 27) -> dict:
+    """Large inputs drawn directly in device memory, for sizes a host draw
+    would take minutes to produce (flat offsets past 2^31 elements).
+
+    ``shapes`` maps a name to (shape, kind, dtype): kind "unit" is N(0, 1)
+    rows L2-normalised over the last axis (in fp32), "normal" is N(0, 1),
+    "decay" is exp(-softplus(N(0, 1) + 2)), "gate" is sigmoid(N(0, 1)).
+    Tensors are drawn in the dict's order from one seeded
+    ``torch.Generator`` on ``device``, ``slab`` elements (whole rows) at a
+    time, in fp32, then cast to ``dtype``.  Same seed, same device type:
+    same values.  Callers copy the parts they check to the host and give
+    those bits to the oracle."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = {}
+    for name, (shape, kind, dtype) in shapes.items():
+        t = torch.empty(shape, dtype=dtype, device=device)
+        flat = t.view(-1, shape[-1])
+        rows = max(1, slab // shape[-1])
+        for r0 in range(0, flat.shape[0], rows):
+            n = min(rows, flat.shape[0] - r0)
+            x = torch.randn((n, shape[-1]), generator=gen, device=device)
+            if kind == "unit":
+                x = x / x.norm(dim=-1, keepdim=True)
+            elif kind == "decay":
+                x = torch.exp(-torch.nn.functional.softplus(x + 2.0))
+            elif kind == "gate":
+                x = torch.sigmoid(x)
+            elif kind != "normal":
+                raise ValueError(kind)
+            flat[r0:r0 + n] = x.to(dtype)
+            del x
+        out[name] = t
+    return out
