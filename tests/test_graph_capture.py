@@ -97,3 +97,33 @@ def test_graph_split_forward(gdr_lib):
     torch.cuda.synchronize()
     eager = [x.clone() for x in (o, sf)]
     _replays_match(fn, eager)
+
+
+def test_graph_split_backward_and_gate(gdr_lib):
+    """The sequence-split backward (identity and zero fills are kernels),
+    then the output gate and its reverse mode with the dw reduction."""
+    from gdr_gen import make_gate
+    inp = make_gdn(B=1, T=128, H=2, Dk=64, Dv=64, dtype="bf16", seed=904, alpha_shift=-2.0,
+                   s0_std=0.05)
+    args = [x.cuda() for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.s0)]
+    do = torch.randn((1, 128, 2, 64), device="cuda")
+    dsf = 0.1 * torch.randn((1, 2, 64, 64), device="cuda")
+    ws = torch.empty(gdr_lib.gdr_chunk_bwd_split_workspace_size(1, 128, 2, 64, 64,
+                                                                torch.bfloat16, 4),
+                     dtype=torch.uint8, device="cuda")
+    gi = make_gate(64, 2, 128, "f32", "bf16", seed=905)
+    o, g, w = gi.o.cuda(), gi.g.cuda(), gi.w.cuda()
+    dy = torch.randn(o.shape, device="cuda").to(torch.bfloat16)
+    gws = torch.empty(gdr_lib.gdr_output_gate_bwd_workspace_size(64, 2, 128), dtype=torch.uint8,
+                      device="cuda")
+
+    def fn():
+        grads = gdr_lib.gdr_chunk_bwd_split(*args, do, dsf, nseg=4, workspace=ws)
+        y = gdr_lib.gdr_output_gate(o, g, w, 1e-6, out_dtype=torch.float32)
+        gb = gdr_lib.gdr_output_gate_bwd(o, g, w, dy, 1e-6, workspace=gws)
+        return tuple(grads) + (y,) + tuple(gb)
+
+    outs = fn()
+    torch.cuda.synchronize()
+    eager = [x.clone() for x in outs]
+    _replays_match(fn, eager)
