@@ -55,8 +55,12 @@ def test_split_bf16_dims(gdr_lib, dims):
                              seed=720 + dims[0] + dims[1], alpha_shift=-2.0, s0_std=0.1), 4)
 
 
-def test_split_f32(gdr_lib):
-    _check(gdr_lib, make_gdn(B=1, T=256, H=2, Dk=64, Dv=64, dtype="f32", seed=730,
+@pytest.mark.parametrize("dims", [(64, 64), (128, 64), (64, 128)])
+def test_split_f32(gdr_lib, dims):
+    """fp32 inputs run the vector-ALU chunk kernel in every pass; with
+    Dk != Dv its P pass writes the workspace's bf16 buffer."""
+    _check(gdr_lib, make_gdn(B=1, T=256, H=2, Dk=dims[0], Dv=dims[1], dtype="f32",
+                             seed=730 + (dims != (64, 64)) * (dims[0] + 2 * dims[1]),
                              alpha_shift=-3.0, s0_std=0.2), 4)
 
 

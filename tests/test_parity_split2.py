@@ -20,10 +20,15 @@ def _args(inp):
     return (inp.q, inp.k, inp.v, inp.alpha, inp.erase, inp.write, inp.s0)
 
 
-@pytest.mark.parametrize("nseg,dt", [(2, "bf16"), (4, "bf16"), (5, "f32")])
-def test_gdr2_fwd_split(gdr_lib, nseg, dt):
-    inp = make_gdn2(B=1, T=160, H=2, Dk=128, Dv=128, dtype=dt, seed=820 + nseg,
-                    alpha_shift=-3.0, s0_std=0.1)
+@pytest.mark.parametrize("nseg,dt,dims", [(2, "bf16", (128, 128)), (4, "bf16", (128, 128)),
+                                          (5, "f32", (128, 128)), (4, "bf16", (64, 128)),
+                                          (5, "f32", (128, 64)), (2, "f32", (64, 128))])
+def test_gdr2_fwd_split(gdr_lib, nseg, dt, dims):
+    """Dk != Dv sends the P pass's output to the workspace's bf16 buffer."""
+    inp = make_gdn2(B=1, T=160, H=2, Dk=dims[0], Dv=dims[1], dtype=dt,
+                    seed=820 + nseg + (0 if dims == (128, 128) else 40 + dims[0] // 16 + dims[1]),
+                    alpha_shift=-3.0,
+                    s0_std=0.1)
     print(f"gdr2 split fwd nseg={nseg} {inp.meta}", flush=True)
     o_ref, s_ref = oracle.gdn2_fwd(*_args(inp))
     o, s = gdr_lib.gdr2_chunk_fwd_split(*[_g(x) for x in _args(inp)], nseg=nseg,
