@@ -36,7 +36,7 @@ __all__ = ["gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd", "gdr_output_
            "gdr_chunk_bwd_split", "gdr_chunk_bwd_split_workspace_size",
            "gdr2_chunk_fwd_split", "gdr2_chunk_bwd_split", "gdr2_chunk_bwd_split_workspace_size",
            "GdrError", "status_string", "lib", "LIB_PATH", "GDR_F32",
-           "GDR_BF16", "GDR_L2NORM_QK"]
+           "GDR_BF16", "GDR_L2NORM_QK", "GDR_SPLIT_FP32_STATES"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "libgdr.so")
@@ -50,6 +50,7 @@ lib = ctypes.CDLL(LIB_PATH)
 
 GDR_F32, GDR_BF16 = 0, 1
 GDR_L2NORM_QK = 1
+GDR_SPLIT_FP32_STATES = 2
 _I64, _P, _E, _U = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32
 
 lib.gdr_chunk_fwd.argtypes = [_I64] * 5 + [_E] + [_P] * 6 + [_E, _P, _P, _P]
@@ -542,9 +543,13 @@ def gdr2_chunk_bwd_split_workspace_size(B, T, H, Dk, Dv, dtype, nseg) -> int:
 
 
 def gdr2_chunk_bwd_split(q, k, v, alpha, erase, write, s0, dout, ds_final=None, *, nseg=8,
-                         workspace=None, want_ds0=True, l2norm_qk=False, stream=None):
+                         workspace=None, want_ds0=True, l2norm_qk=False, fp32_states=False,
+                         stream=None):
     """gdr2_chunk_bwd with each sequence split into ``nseg`` segments that
-    run side by side.  Same arguments and results as gdr2_chunk_bwd."""
+    run side by side.  Same arguments and results as gdr2_chunk_bwd.
+    ``fp32_states`` (GDR_SPLIT_FP32_STATES) builds the segments' start
+    states with the fp32 forward when the inputs are bf16: slower, and the
+    gradients through the state keep fp32 accuracy."""
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     if q.dtype not in _DT or dout.dtype not in _DT:
@@ -567,6 +572,7 @@ def gdr2_chunk_bwd_split(q, k, v, alpha, erase, write, s0, dout, ds_final=None, 
     _run("gdr2_chunk_bwd_split", lib.gdr2_chunk_bwd_split(
         B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase),
         _ptr(write), _ptr(s0), _DT[dout.dtype], _ptr(dout), _ptr(ds_final),
-        *[_ptr(x) for x in out], _ptr(ds0), nseg, GDR_L2NORM_QK if l2norm_qk else 0,
+        *[_ptr(x) for x in out], _ptr(ds0), nseg,
+        (GDR_L2NORM_QK if l2norm_qk else 0) | (GDR_SPLIT_FP32_STATES if fp32_states else 0),
         _ptr(workspace), workspace.numel(), _stream(stream)))
     return tuple(out) + (ds0,)

@@ -38,10 +38,13 @@ constexpr int C = 32;    // tokens per chunk
 constexpr int RB = 32;   // state rows per workgroup
 constexpr int NT = 256;  // threads per workgroup
 
+// q, k, v, and for rule 2 alpha, erase and write, are in the input type
+// (fp32 or bf16); the scalar gates of rule 1 are fp32.
 struct F32Params {
     int64_t T, H;
-    const float *q, *k, *v;
-    const float *alpha, *beta, *erase, *write;
+    const void *q, *k, *v;
+    const void *alpha, *erase, *write;
+    const float* beta;
     const float* s0;
     void* o;
     float* s_final;
@@ -68,9 +71,10 @@ struct Lds {
     static constexpr int TOTAL = BE + C;
 };
 
-template <int DK, int DV, bool G2, typename TOut>
+template <int DK, int DV, bool G2, typename TIn, typename TOut>
 __global__ __launch_bounds__(NT) void chunk_f32_kernel(F32Params p) {
     using L = Lds<DK>;
+    auto in = [](const void* x, int64_t off) { return io<TIn>::ld(static_cast<const TIn*>(x) + off); };
     constexpr int NRB = DV / RB;
     extern __shared__ float sm[];
     float* Ss = sm + L::S;
@@ -110,11 +114,11 @@ __global__ __launch_bounds__(NT) void chunk_f32_kernel(F32Params p) {
             float kv = 0.f, qv = 0.f, ev = 0.f, gv = 0.f;
             if (r < n) {
                 const int64_t off = ((b * T + t0 + r) * H + h) * DK + j;
-                kv = p.k[off];
-                qv = p.q[off];
+                kv = in(p.k, off);
+                qv = in(p.q, off);
                 if (G2) {
-                    ev = p.erase[off] * kv;
-                    gv = safe_log(p.alpha[off]);
+                    ev = in(p.erase, off) * kv;
+                    gv = safe_log(in(p.alpha, off));
                 }
             }
             Ks[r * L::PK + j] = kv;
@@ -129,15 +133,15 @@ __global__ __launch_bounds__(NT) void chunk_f32_kernel(F32Params p) {
             float vv = 0.f;
             if (r < n) {
                 const int64_t off = ((b * T + t0 + r) * H + h) * DV + row0 + i;
-                vv = p.v[off];
-                if (G2) vv *= p.write[off];
+                vv = in(p.v, off);
+                if (G2) vv *= in(p.write, off);
             }
             Vs[r * L::PR + i] = vv;
         }
         if (!G2 && tid < C) {
             const int r = tid;
             const int64_t off = (b * T + t0 + r) * H + h;
-            lg[r] = r < n ? safe_log(p.alpha[off]) : 0.f;
+            lg[r] = r < n ? safe_log(static_cast<const float*>(p.alpha)[off]) : 0.f;
             be[r] = r < n ? p.beta[off] : 0.f;
         }
         __syncthreads();
@@ -299,24 +303,24 @@ __global__ __launch_bounds__(NT) void chunk_f32_kernel(F32Params p) {
     }
 }
 
-template <int DK, int DV, bool G2, typename TOut>
+template <int DK, int DV, bool G2, typename TIn, typename TOut>
 hipError_t launch_f32_t(const ChunkArgs& a) {
     F32Params p;
     p.T = a.T;
     p.H = a.H;
-    p.q = (const float*)a.q;
-    p.k = (const float*)a.k;
-    p.v = (const float*)a.v;
-    p.alpha = (const float*)a.alpha;
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.alpha = a.alpha;
     p.beta = (const float*)a.beta;
-    p.erase = (const float*)a.erase;
-    p.write = (const float*)a.write;
+    p.erase = a.erase;
+    p.write = a.write;
     p.s0 = a.s0;
     p.o = a.o;
     p.s_final = a.s_final;
     p.l2norm = a.l2norm;
     const size_t lds = sizeof(float) * Lds<DK>::TOTAL;
-    auto fn = chunk_f32_kernel<DK, DV, G2, TOut>;
+    auto fn = chunk_f32_kernel<DK, DV, G2, TIn, TOut>;
     hipError_t e = hipFuncSetAttribute((const void*)fn,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -325,13 +329,24 @@ hipError_t launch_f32_t(const ChunkArgs& a) {
     return hipGetLastError();
 }
 
+template <int DK, int DV, typename TIn>
+hipError_t launch_f32_i(const ChunkArgs& a) {
+    if (a.gated2)
+        return a.out_bf16 ? launch_f32_t<DK, DV, true, TIn, bf16_t>(a)
+                          : launch_f32_t<DK, DV, true, TIn, float>(a);
+    return a.out_bf16 ? launch_f32_t<DK, DV, false, TIn, bf16_t>(a)
+                      : launch_f32_t<DK, DV, false, TIn, float>(a);
+}
+
+// bf16 inputs come here only for rule 2 when full fp32 arithmetic is asked
+// for (the sequence-split backward's start states)
 template <int DK, int DV>
 hipError_t launch_f32_d(const ChunkArgs& a) {
-    if (a.gated2)
-        return a.out_bf16 ? launch_f32_t<DK, DV, true, bf16_t>(a)
-                          : launch_f32_t<DK, DV, true, float>(a);
-    return a.out_bf16 ? launch_f32_t<DK, DV, false, bf16_t>(a)
-                      : launch_f32_t<DK, DV, false, float>(a);
+    if (a.in_bf16) {
+        if (!a.gated2) return hipErrorNotSupported;
+        return launch_f32_i<DK, DV, bf16_t>(a);
+    }
+    return launch_f32_i<DK, DV, float>(a);
 }
 
 }  // namespace

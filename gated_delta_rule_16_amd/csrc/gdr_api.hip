@@ -96,7 +96,7 @@ static gdr_status_t chunk_run(ChunkArgs& a) {
         return from_hip(launch_state_copy(a.s0, a.s_final, a.B * a.H * a.Dv * a.Dk, a.stream));
     }
     hipError_t e;
-    if (!a.in_bf16)
+    if (!a.in_bf16 || (a.gated2 && a.precise))
         e = launch_chunk_f32(a);
     else if (a.gated2)
         e = launch_gdr2_bf16(a);
@@ -368,8 +368,8 @@ static gdr_status_t bwd_split_run(ChunkArgs& a, const BwdSplitLayout& l, void* w
 
 static gdr_status_t bwd_split_check(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
                                     gdr_dtype_t in_dt, gdr_dtype_t dout_dt, int64_t nseg,
-                                    uint32_t flags, ChunkArgs& a) {
-    if (!flags_ok(flags)) return GDR_ERR_UNSUPPORTED;
+                                    uint32_t flags, ChunkArgs& a, uint32_t extra = 0u) {
+    if (!flags_ok(flags & ~extra)) return GDR_ERR_UNSUPPORTED;
     gdr_status_t st = chunk_common(B, T, H, Dk, Dv, in_dt, GDR_BF16, a);
     if (st != GDR_OK) return st;
     if (!dtype_ok(dout_dt)) return GDR_ERR_UNSUPPORTED;
@@ -469,12 +469,14 @@ extern "C" gdr_status_t gdr2_chunk_bwd_split(int64_t B, int64_t T, int64_t H, in
                                              uint32_t flags, void* workspace,
                                              size_t workspace_bytes, hipStream_t stream) {
     if (nseg < 1 || nseg > (1 << 20)) return GDR_ERR_INVALID;
-    if (nseg == 1 || T == 0 || B == 0 || H == 0)   // the plain call
+    if (nseg == 1 || T == 0 || B == 0 || H == 0)   // the plain call (fp32 states already)
         return gdr2_chunk_bwd_ex(B, T, H, Dk, Dv, in_dt, q, k, v, alpha, erase, write, s0,
                                  dout_dt, dout, ds_final, dq, dk, dv, dalpha, derase, dwrite, ds0,
-                                 workspace, workspace_bytes, flags, stream);
+                                 workspace, workspace_bytes, flags & ~GDR_SPLIT_FP32_STATES,
+                                 stream);
     ChunkArgs a{};
-    gdr_status_t st = bwd_split_check(B, T, H, Dk, Dv, in_dt, dout_dt, nseg, flags, a);
+    gdr_status_t st = bwd_split_check(B, T, H, Dk, Dv, in_dt, dout_dt, nseg, flags, a,
+                                      GDR_SPLIT_FP32_STATES);
     if (st != GDR_OK) return st;
     if (!ptrs_ok({q, k, v, alpha, erase, write, dout, dq, dk, dv, dalpha, derase, dwrite,
                   workspace}))
@@ -483,6 +485,11 @@ extern "C" gdr_status_t gdr2_chunk_bwd_split(int64_t B, int64_t T, int64_t H, in
     const BwdSplitLayout l = bwd_split_layout(B, T, H, Dk, Dv, in_dt, nseg, true);
     if (workspace_bytes < l.total) return GDR_ERR_INVALID;
     a.gated2 = true;
+    // with GDR_SPLIT_FP32_STATES the start states come from the fp32
+    // vector-ALU forward instead of the bf16 matrix-core one, which rounds
+    // E, A and T once (a few 1e-3 of the states over long memory, inherited
+    // by the gradients through S)
+    a.precise = (flags & GDR_SPLIT_FP32_STATES) != 0;
     a.q = q;
     a.k = k;
     a.v = v;

@@ -198,7 +198,23 @@ gdr_status_t gdr2_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
  * intermediate results or to operands that are split into hi/lo pairs.
  */
 #define GDR_L2NORM_QK 1u
+
 #define GDR_L2NORM_EPS 1e-6f
+
+/*
+ * Accepted by gdr2_chunk_bwd_split only (other calls return
+ * GDR_ERR_UNSUPPORTED for it): with bf16 inputs, build the segments' start
+ * states and transitions with the fp32 vector-ALU forward instead of the
+ * bf16 matrix-core one.  The default rounds E (.) lambda, A and T to bf16
+ * once in those passes; over long memory (alpha near 1) that leaves a few
+ * 1e-3 of rms on the start states and on the gradients that go through S
+ * (dq, dk, dalpha, derase: up to 4e-3 at B1 H16 T32768 d128 in 4 segments,
+ * against ~1e-5 for the plain call).  With this bit those gradients keep
+ * fp32 accuracy, at a higher cost: 42 ms against 17 ms for that workload,
+ * where the plain call takes 31 ms.  fp32 inputs always take the fp32
+ * forward; with nseg == 1 the bit is ignored.
+ */
+#define GDR_SPLIT_FP32_STATES 2u
 
 gdr_status_t gdr_chunk_fwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk,
                               int64_t Dv, gdr_dtype_t in_dt, const void *q,

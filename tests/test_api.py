@@ -370,3 +370,22 @@ def test_head_count_bound(gdr):
     assert gdr.gdr2_chunk_bwd_workspace_size(1, 8, big, 64, 64) == 0
     assert gdr.lib.gdr_chunk_fwd_split_workspace_size(1, 64, big, 64, 64, 1, 4) == 0
     assert gdr.gdr_chunk_bwd_workspace_size(1, 8, hmax, 64, 64) > 0
+
+
+def test_split_fp32_states_flag(gdr):
+    """GDR_SPLIT_FP32_STATES (2) is a gdr2_chunk_bwd_split bit only."""
+    hdr = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    assert int(re.search(r"#define GDR_SPLIT_FP32_STATES (\d+)u", hdr).group(1)) == 2
+    assert gdr.GDR_SPLIT_FP32_STATES == 2
+    wsb = gdr.lib.gdr_chunk_bwd_split_workspace_size(1, 64, 1, 64, 64, 1, 4)
+    assert gdr.lib.gdr_chunk_bwd_split(1, 64, 1, 64, 64, 1, A16, A16, A16, A16, A16, None, 1,
+                                       A16, None, A16, A16, A16, A16, A16, None, 4, 2, A16,
+                                       wsb, None) == 2
+    assert split(gdr, flags=2) == 2
+    wsb2 = gdr.lib.gdr2_chunk_bwd_split_workspace_size(1, 64, 1, 64, 64, 1, 4)
+    call2 = lambda B, flags, n=4: gdr.lib.gdr2_chunk_bwd_split(
+        B, 64, 1, 64, 64, 1, A16, A16, A16, A16, A16, A16, None, 1, A16, None, A16, A16, A16,
+        A16, A16, A16, None, n, flags, A16, wsb2, None)
+    assert call2(1, 2 | 4) == 2          # an unknown bit beside it
+    assert call2(0, 2) == 0              # accepted (nothing to launch)
+    assert call2(0, 2 | 1, n=1) == 0     # nseg = 1: ignored by the plain call

@@ -73,3 +73,51 @@ def test_bwd_split_one_segment_is_plain(gdr_lib):
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_bwd_split_long_context_workload(gdr_lib):
+    """The long-context backward the benchmark times: B1 H16 T32768 d128,
+    bf16 inputs and dL/do, an initial state and dL/dS_T, in 4 segments;
+    every head against the oracle (it keeps segment checkpoints, so the
+    whole sequence fits)."""
+    from gdr_gen import make_config
+    _check(gdr_lib, make_config(2), 4, 22, dout_dtype=torch.bfloat16)
+
+
+def test_gdr2_split_long_context_workload(gdr_lib):
+    """Gated Delta Rule-2 at the same shape (per-channel alpha near 1), as
+    timed: the split forward's o and final state, then the split backward,
+    every head against the oracle.  By default the backward's start states
+    come from the bf16 forward: the gradients through S (dq, dk, dalpha,
+    derase) are held to the bf16-input tolerance, 2e-2, the others to 1e-3.
+    With fp32 start states (GDR_SPLIT_FP32_STATES) every gradient is held
+    to 1e-3."""
+    from gdr_gen import make_gdn2
+    inp = make_gdn2(B=1, T=32768, H=16, Dk=128, Dv=128, dtype="bf16", seed=1006,
+                    alpha_shift=-4.0, s0_std=0.02)
+    args = (inp.q, inp.k, inp.v, inp.alpha, inp.erase, inp.write, inp.s0)
+    print(f"gdr2 split long context {inp.meta}", flush=True)
+    c = lambda x: None if x is None else x.cuda()
+    o, s = gdr_lib.gdr2_chunk_fwd_split(*map(c, args), nseg=4, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.gdn2_fwd(*args)
+    eo, es = oracle.err_rms(o.cpu(), o_ref), oracle.err_rms(s.cpu(), s_ref)
+    print(f"  fwd err(o)={eo:.2e} err(S)={es:.2e}")
+    assert eo <= 2e-2 and es <= 2e-2, (eo, es)
+    g = np.random.Generator(np.random.PCG64(23))
+    do = torch.from_numpy(g.standard_normal((1, 32768, 16, 128)).astype(np.float32)).to(
+        torch.bfloat16)
+    dsf = torch.from_numpy((0.1 * g.standard_normal((1, 16, 128, 128))).astype(np.float32))
+    ref = oracle.gdn2_bwd(*args, do, dsf)
+    names = ("dq", "dk", "dv", "dalpha", "derase", "dwrite", "ds0")
+    through_s = {"dq", "dk", "dalpha", "derase"}
+    for fp32_states in (False, True):
+        got = gdr_lib.gdr2_chunk_bwd_split(*map(c, args), c(do), c(dsf), nseg=4,
+                                           fp32_states=fp32_states)
+        torch.cuda.synchronize()
+        errs = {n: oracle.err_rms(x.cpu(), y) for n, x, y in zip(names, got, ref)}
+        print(f"  bwd fp32_states={fp32_states} " +
+              " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+        tol = {n: 2e-2 if (n in through_s and not fp32_states) else TOL for n in names}
+        bad = {n: e for n, e in errs.items() if not e <= tol[n]}
+        assert not bad, (fp32_states, bad)
