@@ -483,8 +483,12 @@ def bench_bwd_long(gdr, torch, warmup, steps, nseg=4):
                       dtype=torch.uint8, device=dev)
     bs, _, _, _ = time_launches(lambda: gdr.gdr2_chunk_bwd_split(*a2, do, dsf, nseg=nseg,
                                                                  workspace=w2s), warmup, steps)
+    # the same with the start states from the fp32 forward (GDR_SPLIT_FP32_STATES)
+    bs32, _, _, _ = time_launches(lambda: gdr.gdr2_chunk_bwd_split(
+        *a2, do, dsf, nseg=nseg, workspace=w2s, fp32_states=True), warmup, steps)
     return dict(plain=pmean, split=smean, nseg=nseg, tokens=B * T, gdr2_fwd_plain=fp,
-                gdr2_fwd_split=fs, gdr2_bwd_plain=bp, gdr2_bwd_split=bs)
+                gdr2_fwd_split=fs, gdr2_bwd_plain=bp, gdr2_bwd_split=bs,
+                gdr2_bwd_split_fp32_states=bs32)
 
 
 def bench_copy(torch, warmup, steps, nbytes=512 << 20):
@@ -721,7 +725,8 @@ def main():
             "gdr2": {"fwd_plain_ms": r["gdr2_fwd_plain"] * 1e3,
                      "fwd_split_ms": r["gdr2_fwd_split"] * 1e3,
                      "bwd_plain_ms": r["gdr2_bwd_plain"] * 1e3,
-                     "bwd_split_ms": r["gdr2_bwd_split"] * 1e3}}
+                     "bwd_split_ms": r["gdr2_bwd_split"] * 1e3,
+                     "bwd_split_fp32_states_ms": r["gdr2_bwd_split_fp32_states"] * 1e3}}
     if "copy" in res:
         cp = res["copy"]
         out["copy_reference"] = {"what": "torch device-to-device copy, 512 MiB read + 512 MiB "

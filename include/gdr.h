@@ -210,7 +210,7 @@ gdr_status_t gdr2_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
  * 1e-3 of rms on the start states and on the gradients that go through S
  * (dq, dk, dalpha, derase: up to 4e-3 at B1 H16 T32768 d128 in 4 segments,
  * against ~1e-5 for the plain call).  With this bit those gradients keep
- * fp32 accuracy, at a higher cost: 42 ms against 17 ms for that workload,
+ * fp32 accuracy, at a higher cost: 42 ms against 18 ms for that workload,
  * where the plain call takes 31 ms.  fp32 inputs always take the fp32
  * forward; with nseg == 1 the bit is ignored.
  */
