@@ -7,11 +7,12 @@
  *   gdr_recurrent_step  one decode token of the same rule, state in place
  *   gdr2_chunk_fwd      chunkwise forward of Gated Delta Rule-2 (channel gates)
  *
- * plus their _ex variants (q, k L2-normalised on load), a sequence-split
- * form of the first for few long sequences (gdr_chunk_fwd_split), the block's
- * output gate on their result (gdr_output_gate) and the reverse modes of
- * the two chunkwise forwards and of the gate (gdr_chunk_bwd, gdr2_chunk_bwd,
- * gdr_output_gate_bwd).
+ * plus their _ex variants (q, k L2-normalised on load), the block's output
+ * gate on their result (gdr_output_gate), the reverse modes of the two
+ * chunkwise forwards and of the gate (gdr_chunk_bwd, gdr2_chunk_bwd,
+ * gdr_output_gate_bwd), and sequence-split forms of both chunkwise
+ * directions for few long sequences (gdr_chunk_fwd_split,
+ * gdr_chunk_bwd_split, gdr2_chunk_fwd_split, gdr2_chunk_bwd_split).
  *
  * The rule ("Gated Delta Networks", agihunt.info, "Method"; review of GDN on
  * meaningful96.github.io, section 3.4; inputs and outputs from its
