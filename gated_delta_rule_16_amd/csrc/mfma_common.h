@@ -1,16 +1,16 @@
 // bf16 matrix-core building blocks for the chunked kernels (gfx950).
 //
-// All products use v_mfma_f32_32x32x16_bf16: a 32x32 fp32 tile C += A B with
-// a 16-deep contraction.  Lane layouts (lane l = 0..63, l32 = l % 32,
-// hi = l / 32):
-//   A operand  lane holds A[m = l32][k = 8 hi .. 8 hi + 7]
-//   B operand  lane holds B[k = 8 hi .. 8 hi + 7][n = l32]
-//   C tile     register r holds C[m = 8 (r / 4) + 4 hi + r % 4][n = l32]
-// So both operands are read as 16 contiguous bytes from a row-major bf16
-// matrix whose rows run along m (for A) or n (for B) and whose columns run
-// along the contraction, and a C tile is naturally written transposed:
-// C^T[n][m .. m + 3] is 4 contiguous values.  Every tile stored to LDS by
-// these kernels is therefore kept "contraction-major" for its next use.
+// The bf16 products use v_mfma_f32_16x16x32_bf16: a 16x16 fp32 tile C += A B
+// with a 32-deep contraction.  Lane layouts (lane l = 0..63, g = l / 16,
+// m = l % 16):
+//   A operand  lane holds A[m][k = 8 g .. 8 g + 7]
+//   B operand  lane holds B[k = 8 g .. 8 g + 7][n = m]
+//   C tile     register r holds C[4 g + r][m]
+// So both operands are 16 contiguous bytes of a row-major bf16 matrix whose
+// rows run along m (for A) or n (for B) and whose columns run along the
+// contraction; the kernels store their tiles in that "contraction-major"
+// order, permuted within each 32-wide block where a later product wants the
+// C layout of an earlier one as its operand.
 //
 // Precision: a computed fp32 operand x enters as two bf16 terms,
 // x = hi + lo with hi = bf16(x), lo = bf16(x - hi); products of two computed
@@ -22,16 +22,6 @@
 #include "gdr_device.h"
 
 namespace gdr {
-
-__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// 16-byte operand fragment: row `row` of a row-major bf16 matrix (pitch in
-// elements), contraction offset `k` (a multiple of 8).
-__device__ __forceinline__ bf16x8 frag(const bf16_t* base, int pitch, int row, int k) {
-    return *reinterpret_cast<const bf16x8*>(base + row * pitch + k);
-}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -60,23 +50,6 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& h, uint32_t& 
     l = cvt_pk(ra, rb);
 }
 
-__device__ __forceinline__ void split_bf16(float x, bf16_t& h, bf16_t& l) {
-    uint32_t ph, pl;
-    split2(x, 0.f, ph, pl);
-    h = (bf16_t)(ph & 0xffffu);
-    l = (bf16_t)(pl & 0xffffu);
-}
-
-// Store 4 consecutive values at ph / pl as bf16 hi/lo quads (8 bytes each).
-__device__ __forceinline__ void st4_split(bf16_t* ph, bf16_t* pl, float x0, float x1, float x2,
-                                          float x3) {
-    uint2 vh, vl;
-    split2(x0, x1, vh.x, vl.x);
-    split2(x2, x3, vh.y, vl.y);
-    *reinterpret_cast<uint2*>(ph) = vh;
-    *reinterpret_cast<uint2*>(pl) = vl;
-}
-
 // Transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane 4r + c supplies the address of 4 consecutive 16-bit elements; lane i
 // of the group receives element (i & 3) of the chunk supplied by lane
@@ -88,21 +61,6 @@ __device__ __forceinline__ s16x4 lds_tr16(const bf16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_s16x4*)((__attribute__((address_space(3))) char*)(
             (__attribute__((address_space(3))) void*)(p))));
-}
-
-// Operand fragment with the contraction running down the rows of a
-// row-major bf16 matrix M (pitch in elements): lane l receives
-// M[k0 + 8 (l / 32) + e][n0 + (l % 32)], e = 0..7 -- the layout of both MFMA
-// operands when M is stored contraction-major-transposed.
-__device__ __forceinline__ bf16x8 frag_tr(const bf16_t* M, int pitch, int k0, int n0) {
-    const int lane = threadIdx.x & 63;
-    const int g = lane >> 4, j = lane & 15;
-    const int kb = k0 + 8 * (g >> 1) + (j >> 2);
-    const int nb = n0 + 16 * (g & 1) + 4 * (j & 3);
-    const s16x4 a = lds_tr16(M + kb * pitch + nb);
-    const s16x4 b = lds_tr16(M + (kb + 4) * pitch + nb);
-    const s16x4 r8[2] = {a, b};
-    return __builtin_bit_cast(bf16x8, r8);
 }
 
 // fp32 matrix core 16x16x4: A lane l holds A[l % 16][l / 16], B lane l
@@ -138,21 +96,6 @@ __device__ __forceinline__ float wave_scan(float x) {
 }
 
 typedef float f32x8 __attribute__((ext_vector_type(8)));
-
-// 8 consecutive fp32 from LDS (two 16-byte reads).
-__device__ __forceinline__ f32x8 ld8f(const float* p) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-__device__ __forceinline__ f32x8 ld8bf(const bf16_t* p) {
-    const u32x4 u = *reinterpret_cast<const u32x4*>(p);
-    return f32x8{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
-                 __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u),
-                 __uint_as_float(u[2] << 16), __uint_as_float(u[2] & 0xffff0000u),
-                 __uint_as_float(u[3] << 16), __uint_as_float(u[3] & 0xffff0000u)};
-}
 
 // fp32 x8 -> hi/lo bf16 operand fragments.
 __device__ __forceinline__ void split8(const f32x8& x, bf16x8& h, bf16x8& l) {
