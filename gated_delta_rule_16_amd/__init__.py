@@ -13,6 +13,7 @@ Functions mirror the C calls:
     gdr2_chunk_fwd(q, k, v, alpha, erase, write, s0=None, ...)   -> (o, s_final)
     gdr_output_gate(o, g, w=None, eps=1e-6, ...)                -> y
     gdr_output_gate_bwd(o, g, w, dy, eps=1e-6, ...)             -> (do, dg, dw)
+    gdr_output_gate_bwd_noalloc(o, g, w, dy, eps=1e-6, ...)     -> (do, dg, dw)
     gdr_chunk_bwd(q, k, v, alpha, beta, s0, dout, ds_final=None)
         -> (dq, dk, dv, dalpha, dbeta, ds0)
     gdr2_chunk_bwd(q, k, v, alpha, erase, write, s0, dout, ds_final=None)
@@ -33,6 +34,7 @@ __all__ = ["gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd", "gdr_output_
            "gdr2_chunk_bwd", "gdr2_chunk_bwd_workspace_size",
            "gdr_chunk_fwd_split", "gdr_chunk_fwd_split_workspace_size",
            "gdr_output_gate_bwd", "gdr_output_gate_bwd_workspace_size",
+           "gdr_output_gate_bwd_noalloc",
            "gdr_chunk_bwd_split", "gdr_chunk_bwd_split_workspace_size",
            "gdr2_chunk_fwd_split", "gdr2_chunk_bwd_split", "gdr2_chunk_bwd_split_workspace_size",
            "GdrError", "status_string", "lib", "LIB_PATH", "GDR_F32",
@@ -93,6 +95,9 @@ lib.gdr_output_gate_bwd_workspace_size.restype = ctypes.c_size_t
 lib.gdr_output_gate_bwd.argtypes = ([_I64] * 3 + [_E, _P, _E, _P, _P, ctypes.c_float, _E, _P] +
                                     [_P] * 4 + [ctypes.c_size_t, _P])
 lib.gdr_output_gate_bwd.restype = ctypes.c_int
+lib.gdr_output_gate_bwd_noalloc.argtypes = ([_I64] * 3 + [_E, _P, _E, _P, _P, ctypes.c_float, _E,
+                                            _P] + [_P] * 3 + [_P])
+lib.gdr_output_gate_bwd_noalloc.restype = ctypes.c_int
 lib.gdr_chunk_bwd_split_workspace_size.argtypes = [_I64] * 5 + [_E, _I64]
 lib.gdr_chunk_bwd_split_workspace_size.restype = ctypes.c_size_t
 lib.gdr_chunk_bwd_split.argtypes = ([_I64] * 5 + [_E] + [_P] * 6 + [_E, _P, _P] + [_P] * 6 +
@@ -455,6 +460,36 @@ def gdr_output_gate_bwd(o, g, w, dy, eps=1e-6, *, want_dw=True, workspace=None, 
         N, H, Dv, _DT[o.dtype], _ptr(o), _DT[g.dtype], _ptr(g), _ptr(w), float(eps),
         _DT[dy.dtype], _ptr(dy), _ptr(do), _ptr(dg), _ptr(dw), _ptr(workspace),
         0 if workspace is None else workspace.numel(), _stream(stream)))
+    return do, dg, dw
+
+
+def gdr_output_gate_bwd_noalloc(o, g, w, dy, eps=1e-6, *, want_dw=True, out=None, stream=None):
+    """gdr_output_gate_bwd through the C call that takes no workspace (its
+    dw partials go to the library's own per-GPU array).  ``out`` may give
+    preallocated fp32 (do, dg, dw) tensors; otherwise they are created here.
+    Returns (do, dg, dw), dw None when ``want_dw`` is False."""
+    if o.dim() < 2:
+        raise ValueError("o must be [..., H, Dv]")
+    H, Dv = o.shape[-2], o.shape[-1]
+    N = o.numel() // (H * Dv) if o.numel() else 0
+    for name, t in (("o", o), ("g", g), ("dy", dy)):
+        if t.dtype not in _DT:
+            raise TypeError(f"{name} must be float32 or bfloat16")
+        _check(name, t, t.dtype, tuple(o.shape))
+    if w is not None:
+        _check("w", w, torch.float32, (Dv,))
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=o.device)
+        out = (torch.empty(o.shape, **f32), torch.empty(o.shape, **f32),
+               torch.empty((Dv,), **f32) if want_dw else None)
+    do, dg, dw = out
+    _check("do", do, torch.float32, tuple(o.shape))
+    _check("dg", dg, torch.float32, tuple(o.shape))
+    if dw is not None:
+        _check("dw", dw, torch.float32, (Dv,))
+    _run("gdr_output_gate_bwd_noalloc", lib.gdr_output_gate_bwd_noalloc(
+        N, H, Dv, _DT[o.dtype], _ptr(o), _DT[g.dtype], _ptr(g), _ptr(w), float(eps),
+        _DT[dy.dtype], _ptr(dy), _ptr(do), _ptr(dg), _ptr(dw), _stream(stream)))
     return do, dg, dw
 
 

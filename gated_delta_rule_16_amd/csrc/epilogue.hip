@@ -16,6 +16,8 @@
 // lane keeps UNROLL rows in flight, all loads issued before any arithmetic.
 // y may be o itself: every element is read and written by the same lane,
 // its loads before its stores.
+#include <mutex>
+
 #include "launch.h"
 #include "mfma_common.h"
 
@@ -285,7 +287,41 @@ hipError_t launch_gate_bwd_d(const GateBwdArgs& a) {
     return a.o_bf16 ? launch_gate_bwd_g<DV, bf16_t>(a) : launch_gate_bwd_g<DV, float>(a);
 }
 
+// Scratch of the allocation-free gate backward (gdr_output_gate_bwd_noalloc):
+// the workgroups' dw partials, at most GATE_BWD_MAX_BLOCKS x 128 floats
+// (1 MiB).  Each GPU the library runs on holds its own copy until the process
+// ends.  Host code never passes the array's name to a kernel: on the host it
+// is only a stand-in for the symbol, whose device address is looked up once
+// per device below.
+static __device__ __align__(256) float scratch[GATE_BWD_MAX_BLOCKS * 128];
+static_assert(sizeof(scratch) == GDR_GATE_BWD_SCRATCH_BYTES, "scratch size as declared");
+
+constexpr int kMaxDevices = 256;
+
 }  // namespace
+
+size_t gate_bwd_scratch_bytes() { return sizeof(scratch); }
+
+// Device address of `scratch` on the current device: hipGetSymbolAddress is
+// called once per device, with that device current, and its result kept.
+hipError_t gate_bwd_scratch(float** out) {
+    static std::mutex mu;
+    static float* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = static_cast<float*>(p);
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
 
 size_t gate_bwd_workspace_bytes(int64_t rows, int64_t Dv) {
     const int64_t blocks = Dv == 128 ? gate_bwd_blocks<128>(rows) : gate_bwd_blocks<64>(rows);

@@ -645,27 +645,19 @@ extern "C" size_t gdr_output_gate_bwd_workspace_size(int64_t N, int64_t H, int64
     return gate_bwd_workspace_bytes(N * H, Dv);
 }
 
-extern "C" gdr_status_t gdr_output_gate_bwd(int64_t N, int64_t H, int64_t Dv, gdr_dtype_t o_dt,
-                                            const void* o, gdr_dtype_t g_dt, const void* g,
-                                            const float* w, float eps, gdr_dtype_t dy_dt,
-                                            const void* dy, float* dout, float* dg, float* dw,
-                                            void* workspace, size_t workspace_bytes,
-                                            hipStream_t stream) {
+// Checks shared by both gate backward calls; fills `a` except the workspace.
+static gdr_status_t gate_bwd_check(int64_t N, int64_t H, int64_t Dv, gdr_dtype_t o_dt,
+                                   const void* o, gdr_dtype_t g_dt, const void* g,
+                                   const float* w, float eps, gdr_dtype_t dy_dt,
+                                   const void* dy, float* dout, float* dg, float* dw,
+                                   hipStream_t stream, GateBwdArgs& a) {
     if (N < 0 || H < 0 || Dv < 0) return GDR_ERR_INVALID;
     if (!sizes_ok(N, H, Dv)) return GDR_ERR_INVALID;
     if (!dtype_ok(o_dt) || !dtype_ok(g_dt) || !dtype_ok(dy_dt)) return GDR_ERR_UNSUPPORTED;
     if (Dv != 64 && Dv != 128) return GDR_ERR_UNSUPPORTED;
     if (!(eps >= 0.f) || eps > 3.0e38f) return GDR_ERR_INVALID;
     if (!opt_ok(w) || !opt_ok(dw)) return GDR_ERR_INVALID;
-    if (N == 0 || H == 0) {
-        // no rows: dw is zero
-        if (dw) return from_hip(launch_state_copy(nullptr, dw, Dv, stream));
-        return GDR_OK;
-    }
-    if (!ptrs_ok({o, g, dy, dout, dg})) return GDR_ERR_INVALID;
-    if (dw && (!ptrs_ok({workspace}) || workspace_bytes < gate_bwd_workspace_bytes(N * H, Dv)))
-        return GDR_ERR_INVALID;
-    GateBwdArgs a{};
+    if (N > 0 && H > 0 && !ptrs_ok({o, g, dy, dout, dg})) return GDR_ERR_INVALID;
     a.N = N;
     a.H = H;
     a.Dv = Dv;
@@ -680,8 +672,61 @@ extern "C" gdr_status_t gdr_output_gate_bwd(int64_t N, int64_t H, int64_t Dv, gd
     a.dout = dout;
     a.dg = dg;
     a.dw = dw;
-    a.workspace = workspace;
     a.stream = stream;
+    return GDR_OK;
+}
+
+extern "C" gdr_status_t gdr_output_gate_bwd(int64_t N, int64_t H, int64_t Dv, gdr_dtype_t o_dt,
+                                            const void* o, gdr_dtype_t g_dt, const void* g,
+                                            const float* w, float eps, gdr_dtype_t dy_dt,
+                                            const void* dy, float* dout, float* dg, float* dw,
+                                            void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+    GateBwdArgs a{};
+    gdr_status_t st = gate_bwd_check(N, H, Dv, o_dt, o, g_dt, g, w, eps, dy_dt, dy, dout, dg,
+                                     dw, stream, a);
+    if (st != GDR_OK) return st;
+    if (N == 0 || H == 0) {
+        // no rows: dw is zero
+        if (dw) return from_hip(launch_state_copy(nullptr, dw, Dv, stream));
+        return GDR_OK;
+    }
+    if (dw && (!ptrs_ok({workspace}) || workspace_bytes < gate_bwd_workspace_bytes(N * H, Dv)))
+        return GDR_ERR_INVALID;
+    a.workspace = workspace;
+    return from_hip(launch_output_gate_bwd(a));
+}
+
+extern "C" gdr_status_t gdr_output_gate_bwd_noalloc(int64_t N, int64_t H, int64_t Dv,
+                                                    gdr_dtype_t o_dt, const void* o,
+                                                    gdr_dtype_t g_dt, const void* g,
+                                                    const float* w, float eps,
+                                                    gdr_dtype_t dy_dt, const void* dy,
+                                                    float* dout, float* dg, float* dw,
+                                                    hipStream_t stream) {
+    GateBwdArgs a{};
+    gdr_status_t st = gate_bwd_check(N, H, Dv, o_dt, o, g_dt, g, w, eps, dy_dt, dy, dout, dg,
+                                     dw, stream, a);
+    if (st != GDR_OK) return st;
+    if (N == 0 || H == 0) {
+        if (dw) return from_hip(launch_state_copy(nullptr, dw, Dv, stream));
+        return GDR_OK;
+    }
+    if (dw) {
+        // the partials go to the library's own array on the stream's device,
+        // which must be the current device
+        if (gate_bwd_workspace_bytes(N * H, Dv) > gate_bwd_scratch_bytes()) return GDR_ERR_INVALID;
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return GDR_ERR_DEVICE;
+        if (stream) {
+            hipDevice_t sdev = -1;
+            if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return GDR_ERR_DEVICE;
+            if (cur != (int)sdev) return GDR_ERR_INVALID;
+        }
+        float* p = nullptr;
+        if (gate_bwd_scratch(&p) != hipSuccess) return GDR_ERR_DEVICE;
+        a.workspace = p;
+    }
     return from_hip(launch_output_gate_bwd(a));
 }
 

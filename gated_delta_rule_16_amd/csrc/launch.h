@@ -109,6 +109,10 @@ size_t bwd2_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t
 hipError_t launch_output_gate(const GateArgs& a);
 hipError_t launch_output_gate_bwd(const GateBwdArgs& a);
 size_t gate_bwd_workspace_bytes(int64_t rows, int64_t Dv);
+// The library's own dw-partials array for gdr_output_gate_bwd_noalloc: its
+// size in bytes, and its device address on the current device.
+size_t gate_bwd_scratch_bytes();
+hipError_t gate_bwd_scratch(float** out);
 // fp32 inputs: VALU kernels, both rules.
 hipError_t launch_chunk_f32(const ChunkArgs& a);
 // bf16 inputs, scalar gates: bf16 MFMA kernel.

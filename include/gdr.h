@@ -13,6 +13,8 @@
  * gdr_output_gate_bwd), and sequence-split forms of both chunkwise
  * directions for few long sequences (gdr_chunk_fwd_split,
  * gdr_chunk_bwd_split, gdr2_chunk_fwd_split, gdr2_chunk_bwd_split).
+ * gdr_output_gate_bwd_noalloc is the gate's reverse mode without a caller
+ * workspace, for callers that cannot allocate.
  *
  * The rule ("Gated Delta Networks", agihunt.info, "Method"; review of GDN on
  * meaningful96.github.io, section 3.4; inputs and outputs from its
@@ -30,8 +32,9 @@
  * Conventions shared by every call
  *   - Every tensor pointer is a DEVICE pointer owned by the caller; tensors
  *     are contiguous and row-major in the layouts given per argument.  The
- *     library keeps no allocation and no state between calls and calls no
- *     allocator.
+ *     library calls no allocator and keeps no state between calls, with one
+ *     exception: gdr_output_gate_bwd_noalloc writes its partial sums to a
+ *     1 MiB array the library holds per GPU (see there).
  *   - Calls are asynchronous on `stream` (0 = the null stream) and return
  *     after the kernels are enqueued.
  *   - Arguments are validated on the host before anything is launched; on
@@ -61,7 +64,9 @@
  *     state is not written.  s0 and s_final may be the same buffer.  q, k, v
  *     and the gates must not overlap o or s_final.
  *   - Thread safety: calls carry no shared mutable state and may be issued
- *     from several host threads on different streams.
+ *     from several host threads on different streams, except that
+ *     overlapping gdr_output_gate_bwd_noalloc calls on one GPU share its
+ *     array.
  */
 #ifndef GDR_H
 #define GDR_H
@@ -409,6 +414,34 @@ gdr_status_t gdr_output_gate_bwd(int64_t N, int64_t H, int64_t Dv,
                                  const void *dy, float *dout, float *dg,
                                  float *dw, void *workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdr_output_gate_bwd without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving or training
+ * loops, harnesses that forbid hipMalloc.  Same arguments and results as
+ * gdr_output_gate_bwd minus workspace and workspace_bytes.
+ *
+ * The workgroups' dw partials go to an array the library holds in device
+ * memory, GDR_GATE_BWD_SCRATCH_BYTES (1 MiB) per GPU, kept until the process
+ * ends.  The partial count is capped at 2048 x Dv floats, so every valid
+ * (N, H, Dv) fits; a call that would not fit returns GDR_ERR_INVALID.
+ * The call allocates nothing: it enqueues the same kernels as
+ * gdr_output_gate_bwd on `stream`.  `stream` must belong to the current
+ * device (GDR_ERR_INVALID otherwise).  Every call on one GPU uses that GPU's
+ * one array, and each call rewrites every partial it reads, so calls that
+ * run one after another need no clearing; calls on one GPU that may
+ * overlap (other streams, other host threads) race on the array and must be
+ * ordered by the caller.  With dw NULL the array is not used.
+ */
+#define GDR_GATE_BWD_SCRATCH_BYTES (2048u * 128u * 4u)
+
+gdr_status_t gdr_output_gate_bwd_noalloc(int64_t N, int64_t H, int64_t Dv,
+                                         gdr_dtype_t o_dt, const void *o,
+                                         gdr_dtype_t g_dt, const void *g,
+                                         const float *w, float eps,
+                                         gdr_dtype_t dy_dt, const void *dy,
+                                         float *dout, float *dg, float *dw,
+                                         hipStream_t stream);
 
 /*
  * Reverse mode of gdr_chunk_fwd (the scalar-gate rule): the gradients of a

@@ -321,6 +321,32 @@ def test_gate_bwd_no_workspace_without_dw(gdr):
     assert gate_bwd(gdr, dw=None, ws=None, wsb=0, dy=BAD) == 1
 
 
+def gate_bwd_noalloc(gdr, N=4, H=2, Dv=64, odt=0, o=A16, gdt=1, g=A16, w=None, eps=1e-6, dyt=1,
+                     dy=A16, do=A16, dg=A16, dw=A16):
+    return gdr.lib.gdr_output_gate_bwd_noalloc(N, H, Dv, odt, o, gdt, g, w, eps, dyt, dy, do, dg,
+                                               dw, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=None), 1), (dict(dy=BAD), 1), (dict(do=None), 1), (dict(dg=None), 1),
+    (dict(w=BAD), 1), (dict(dw=BAD), 1), (dict(eps=-1.0), 1), (dict(N=-1), 1),
+    (dict(Dv=96), 2), (dict(dyt=3), 2), (dict(odt=5), 2),
+])
+def test_gate_bwd_noalloc_validation(gdr, kw, code):
+    """The allocation-free gate backward rejects what gdr_output_gate_bwd
+    rejects, on the host, before it touches the device."""
+    assert gate_bwd_noalloc(gdr, **kw) == code
+
+
+def test_gate_bwd_noalloc_scratch_limit():
+    """The library's array holds the largest partial count the call can
+    launch: 2048 workgroups x 128 channels of fp32, GDR_GATE_BWD_SCRATCH_BYTES
+    in gdr.h."""
+    hdr = open(HEADER).read()
+    m = re.search(r"#define GDR_GATE_BWD_SCRATCH_BYTES \((\d+)u \* (\d+)u \* (\d+)u\)", hdr)
+    assert m and int(m[1]) * int(m[2]) * int(m[3]) == 2048 * 128 * 4
+
+
 def test_bwd_split_workspace_size(gdr):
     """nseg = 1: the plain backward's workspace; otherwise the split
     forward's pieces (with a discard buffer for the passes' outputs), N and
