@@ -14,6 +14,7 @@ Functions mirror the C calls:
     gdr_output_gate(o, g, w=None, eps=1e-6, ...)                -> y
     gdr_output_gate_bwd(o, g, w, dy, eps=1e-6, ...)             -> (do, dg, dw)
     gdr_output_gate_bwd_noalloc(o, g, w, dy, eps=1e-6, ...)     -> (do, dg, dw)
+    gdr_chunk_fwd_gate(q, k, v, alpha, beta, s0, g, w, eps, ...) -> (y, s_final)
     gdr_chunk_bwd(q, k, v, alpha, beta, s0, dout, ds_final=None)
         -> (dq, dk, dv, dalpha, dbeta, ds0)
     gdr2_chunk_bwd(q, k, v, alpha, erase, write, s0, dout, ds_final=None)
@@ -34,7 +35,8 @@ __all__ = ["gdr_chunk_fwd", "gdr_recurrent_step", "gdr2_chunk_fwd", "gdr_output_
            "gdr2_chunk_bwd", "gdr2_chunk_bwd_workspace_size",
            "gdr_chunk_fwd_split", "gdr_chunk_fwd_split_workspace_size",
            "gdr_output_gate_bwd", "gdr_output_gate_bwd_workspace_size",
-           "gdr_output_gate_bwd_noalloc",
+           "gdr_output_gate_bwd_noalloc", "gdr_chunk_fwd_gate",
+           "gdr_chunk_fwd_gate_workspace_size",
            "gdr_chunk_bwd_split", "gdr_chunk_bwd_split_workspace_size",
            "gdr2_chunk_fwd_split", "gdr2_chunk_bwd_split", "gdr2_chunk_bwd_split_workspace_size",
            "GdrError", "status_string", "lib", "LIB_PATH", "GDR_F32",
@@ -98,6 +100,11 @@ lib.gdr_output_gate_bwd.restype = ctypes.c_int
 lib.gdr_output_gate_bwd_noalloc.argtypes = ([_I64] * 3 + [_E, _P, _E, _P, _P, ctypes.c_float, _E,
                                             _P] + [_P] * 3 + [_P])
 lib.gdr_output_gate_bwd_noalloc.restype = ctypes.c_int
+lib.gdr_chunk_fwd_gate_workspace_size.argtypes = [_I64] * 5 + [_E]
+lib.gdr_chunk_fwd_gate_workspace_size.restype = ctypes.c_size_t
+lib.gdr_chunk_fwd_gate.argtypes = ([_I64] * 5 + [_E] + [_P] * 6 + [_E, _P, _P, ctypes.c_float, _E,
+                                   _P, _P, _U, _P, ctypes.c_size_t, _P])
+lib.gdr_chunk_fwd_gate.restype = ctypes.c_int
 lib.gdr_chunk_bwd_split_workspace_size.argtypes = [_I64] * 5 + [_E, _I64]
 lib.gdr_chunk_bwd_split_workspace_size.restype = ctypes.c_size_t
 lib.gdr_chunk_bwd_split.argtypes = ([_I64] * 5 + [_E] + [_P] * 6 + [_E, _P, _P] + [_P] * 6 +
@@ -192,6 +199,53 @@ def gdr_chunk_fwd(q, k, v, alpha, beta, s0=None, *, out_dtype=None, o=None,
     else:
         _run("gdr_chunk_fwd", lib.gdr_chunk_fwd(*args, _stream(stream)))
     return o, s_final
+
+
+def gdr_chunk_fwd_gate_workspace_size(B, T, H, Dk, Dv, dtype) -> int:
+    """Bytes of device workspace gdr_chunk_fwd_gate needs (0: none)."""
+    return int(lib.gdr_chunk_fwd_gate_workspace_size(B, T, H, Dk, Dv, _DT[dtype]))
+
+
+def gdr_chunk_fwd_gate(q, k, v, alpha, beta, s0, g, w=None, eps=1e-6, *, out_dtype=None, y=None,
+                       s_final=None, want_state=True, l2norm_qk=False, workspace=None,
+                       stream=None):
+    """gdr_chunk_fwd followed by the output gate, y = o / sqrt(mean o^2 + eps)
+    w SiLU(g), fused on the forward's stores (bf16 inputs).  g [B,T,H,Dv]
+    fp32 or bf16, w [Dv] fp32 or None.  Returns (y [B,T,H,Dv], s_final or
+    None); ``workspace`` (uint8 GPU tensor) is allocated here when None."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if q.dtype not in _DT or g.dtype not in _DT:
+        raise TypeError("q and g must be float32 or bfloat16")
+    _check("q", q, q.dtype, (B, T, H, Dk))
+    _check("k", k, q.dtype, (B, T, H, Dk))
+    _check("v", v, q.dtype, (B, T, H, Dv))
+    _check("alpha", alpha, torch.float32, (B, T, H))
+    _check("beta", beta, torch.float32, (B, T, H))
+    _check("g", g, g.dtype, (B, T, H, Dv))
+    if s0 is not None:
+        _check("s0", s0, torch.float32, (B, H, Dv, Dk))
+    if w is not None:
+        _check("w", w, torch.float32, (Dv,))
+    odt = q.dtype if out_dtype is None else out_dtype
+    if odt not in _DT:
+        raise TypeError(f"unsupported output dtype {odt}")
+    if y is None:
+        y = torch.empty((B, T, H, Dv), dtype=odt, device=q.device)
+    _check("y", y, odt, (B, T, H, Dv))
+    if s_final is None and want_state:
+        s_final = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=q.device)
+    if s_final is not None:
+        _check("s_final", s_final, torch.float32, (B, H, Dv, Dk))
+    if workspace is None:
+        workspace = torch.empty(max(gdr_chunk_fwd_gate_workspace_size(B, T, H, Dk, Dv, q.dtype), 16),
+                                dtype=torch.uint8, device=q.device)
+    _check("workspace", workspace, torch.uint8)
+    _run("gdr_chunk_fwd_gate", lib.gdr_chunk_fwd_gate(
+        B, T, H, Dk, Dv, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _ptr(s0), _DT[g.dtype], _ptr(g), _ptr(w), float(eps), _DT[odt], _ptr(y), _ptr(s_final),
+        GDR_L2NORM_QK if l2norm_qk else 0, _ptr(workspace), workspace.numel(), _stream(stream)))
+    return y, s_final
 
 
 def gdr_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, dtype, nseg) -> int:

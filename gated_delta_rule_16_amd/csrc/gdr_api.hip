@@ -145,6 +145,87 @@ extern "C" gdr_status_t gdr_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t D
                             s_final, 0u, stream);
 }
 
+// Forward with the output gate fused on its stores.  bf16 inputs: one pass
+// of the bf16 kernel writing y, the workspace holding the row blocks'
+// exchange words; fp32 inputs: the vector-ALU forward into an fp32 o in the
+// workspace, then the gate kernel.
+extern "C" size_t gdr_chunk_fwd_gate_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                                    int64_t Dv, gdr_dtype_t in_dt) {
+    if (B < 0 || T < 0 || H < 0 || !dims_ok(Dk, Dv) || !dtype_ok(in_dt)) return 0;
+    if (!sizes_ok(B, T, H) || !sizes_ok(B * T * H, Dk > Dv ? Dk : Dv, 1)) return 0;
+    if (!heads_ok(H)) return 0;
+    if (B == 0 || T == 0 || H == 0) return 0;
+    if (in_dt == GDR_BF16) return chunk_gate_xch_bytes(B, H, Dv);
+    return (size_t)(B * T * H * Dv) * 4;
+}
+
+extern "C" gdr_status_t gdr_chunk_fwd_gate(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                           int64_t Dv, gdr_dtype_t in_dt, const void* q,
+                                           const void* k, const void* v, const float* alpha,
+                                           const float* beta, const float* s0,
+                                           gdr_dtype_t g_dt, const void* g, const float* w,
+                                           float eps, gdr_dtype_t out_dt, void* y,
+                                           float* s_final, uint32_t flags, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+    if (!flags_ok(flags)) return GDR_ERR_UNSUPPORTED;
+    ChunkArgs a{};
+    gdr_status_t st = chunk_common(B, T, H, Dk, Dv, in_dt, out_dt, a);
+    if (st != GDR_OK) return st;
+    if (!dtype_ok(g_dt)) return GDR_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f) || eps > 3.0e38f) return GDR_ERR_INVALID;
+    if (!opt_ok(s0) || !opt_ok(s_final) || !opt_ok(w)) return GDR_ERR_INVALID;
+    const bool empty = B == 0 || T == 0 || H == 0;
+    if (!empty) {
+        if (!ptrs_ok({q, k, v, g, y}) || !elem_ok(alpha, 4) || !elem_ok(beta, 4))
+            return GDR_ERR_INVALID;
+        if (!grid_ok(B * T * H * Dv)) return GDR_ERR_INVALID;
+        const size_t need = gdr_chunk_fwd_gate_workspace_size(B, T, H, Dk, Dv, in_dt);
+        if (!ptrs_ok({workspace}) || workspace_bytes < need) return GDR_ERR_INVALID;
+    }
+    a.gated2 = false;
+    a.l2norm = (flags & GDR_L2NORM_QK) != 0;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.s0 = s0;
+    a.s_final = s_final;
+    a.stream = stream;
+    if (empty) {
+        a.o = y;
+        return chunk_run(a);   // no tokens: s_final gets s0 (or zeros)
+    }
+    if (a.in_bf16) {
+        a.o = y;
+        a.gate = g;
+        a.gate_bf16 = g_dt == GDR_BF16;
+        a.w = w;
+        a.eps = eps;
+        a.xch = workspace;
+        const hipError_t e = launch_chunk_bf16_gate(a);
+        if (e == hipErrorNotSupported) return GDR_ERR_UNSUPPORTED;
+        return from_hip(e);
+    }
+    a.o = workspace;
+    a.out_bf16 = false;
+    if ((st = chunk_run(a)) != GDR_OK) return st;
+    GateArgs ga;
+    ga.N = B * T;
+    ga.H = H;
+    ga.Dv = Dv;
+    ga.o_bf16 = false;
+    ga.g_bf16 = g_dt == GDR_BF16;
+    ga.out_bf16 = out_dt == GDR_BF16;
+    ga.o = workspace;
+    ga.g = g;
+    ga.w = w;
+    ga.eps = eps;
+    ga.y = y;
+    ga.stream = stream;
+    return from_hip(launch_output_gate(ga));
+}
+
 // Sequence-split forward: workspace pieces, each rounded up to 256 bytes.
 namespace {
 struct SplitLayout {

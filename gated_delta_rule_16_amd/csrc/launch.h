@@ -34,6 +34,14 @@ struct ChunkArgs {
     void* o;
     float* s_final;
     hipStream_t stream;
+    // output gate fused on the stores of the bf16 scalar-gate kernel
+    // (gdr_chunk_fwd_gate): o receives y; gate [B,T,H,Dv], w [Dv] or NULL,
+    // xch the row blocks' exchange words (chunk_gate_xch_bytes)
+    const void* gate;
+    bool gate_bf16;
+    const float* w;
+    float eps;
+    void* xch;
 };
 
 // Output gate: o, g [N, H, Dv]; w [Dv] fp32 or NULL.
@@ -117,6 +125,9 @@ hipError_t gate_bwd_scratch(float** out);
 hipError_t launch_chunk_f32(const ChunkArgs& a);
 // bf16 inputs, scalar gates: bf16 MFMA kernel.
 hipError_t launch_chunk_bf16(const ChunkArgs& a);
+// The same with the output gate fused on its stores (zeroes a.xch first).
+hipError_t launch_chunk_bf16_gate(const ChunkArgs& a);
+size_t chunk_gate_xch_bytes(int64_t B, int64_t H, int64_t Dv);
 // bf16 inputs, channel gates: bf16 MFMA kernel.
 hipError_t launch_gdr2_bf16(const ChunkArgs& a);
 // Copy s0 (or zeros) into s_final for an empty sequence.

@@ -8,7 +8,8 @@
  *   gdr2_chunk_fwd      chunkwise forward of Gated Delta Rule-2 (channel gates)
  *
  * plus their _ex variants (q, k L2-normalised on load), the block's output
- * gate on their result (gdr_output_gate), the reverse modes of the two
+ * gate on their result (gdr_output_gate, and fused on the forward's stores:
+ * gdr_chunk_fwd_gate), the reverse modes of the two
  * chunkwise forwards and of the gate (gdr_chunk_bwd, gdr2_chunk_bwd,
  * gdr_output_gate_bwd), and sequence-split forms of both chunkwise
  * directions for few long sequences (gdr_chunk_fwd_split,
@@ -375,15 +376,55 @@ gdr_status_t gdr2_chunk_bwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
  *   eps         >= 0, added to the mean square inside the root
  *   out_dt, y   [N, H, Dv]; y may be o itself when out_dt == o_dt
  *
- * One pass over HBM (o, g in, y out).  It is a call of its own and not a
- * store-side epilogue of the chunk calls because those split a head's Dv
- * channels over workgroups.  o, g and y need 16-byte alignment, w too when
- * given.  Arithmetic in fp32; a bf16 y is rounded to nearest even.
+ * One pass over HBM (o, g in, y out).  gdr_chunk_fwd_gate below fuses the
+ * same gate onto the stores of the scalar-gate forward.  o, g and y need
+ * 16-byte alignment, w too when given.  Arithmetic in fp32; a bf16 y is
+ * rounded to nearest even.
  */
 gdr_status_t gdr_output_gate(int64_t N, int64_t H, int64_t Dv, gdr_dtype_t o_dt,
                              const void *o, gdr_dtype_t g_dt, const void *g,
                              const float *w, float eps, gdr_dtype_t out_dt,
                              void *y, hipStream_t stream);
+
+/*
+ * gdr_chunk_fwd followed by gdr_output_gate, with the gate fused on the
+ * forward's stores: o is never written, y = o / sqrt(mean_c o_c^2 + eps) *
+ * w * g * sigmoid(g) is (the block's RMSNorm and SiLU output gate after the
+ * recurrence: "Gated DeltaNet-2", agihunt.info, block paragraph; GDN review
+ * on meaningful96.github.io, section 3.8).
+ *
+ *   B, T, H, Dk, Dv, in_dt, q, k, v, alpha, beta, s0, s_final, flags
+ *                 as for gdr_chunk_fwd_ex
+ *   g_dt, g       [B, T, H, Dv] the gate branch's pre-activation
+ *   w             [Dv] fp32 norm weight, or NULL (ones)
+ *   eps           >= 0, inside the root
+ *   out_dt, y     [B, T, H, Dv] (written)
+ *   workspace     device memory of at least
+ *                 gdr_chunk_fwd_gate_workspace_size(B, T, H, Dk, Dv, in_dt)
+ *                 bytes, 16-byte aligned, owned by the caller: for bf16
+ *                 inputs the row blocks' exchange of per-token sums of
+ *                 squares (a few KB per head), for fp32 inputs an fp32 o
+ *                 between the forward and the gate
+ *
+ * With bf16 inputs one kernel pass computes and gates o: a head's Dv rows
+ * are split over workgroups, which trade per-token sums of squares through
+ * the workspace.  The heads go out in cooperative launches of as many
+ * workgroups as the GPU holds at once, so the call is not for HIP graph
+ * capture.  Equals gdr_output_gate(gdr_chunk_fwd(...)) up to fp32 rounding;
+ * GDR_ERR_DEVICE if a cooperative launch is refused.  q, k, v, g, y need
+ * 16-byte alignment; alpha, beta element alignment; w 16 bytes when given.
+ */
+size_t gdr_chunk_fwd_gate_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                         int64_t Dv, gdr_dtype_t in_dt);
+
+gdr_status_t gdr_chunk_fwd_gate(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                int64_t Dv, gdr_dtype_t in_dt, const void *q,
+                                const void *k, const void *v, const float *alpha,
+                                const float *beta, const float *s0,
+                                gdr_dtype_t g_dt, const void *g, const float *w,
+                                float eps, gdr_dtype_t out_dt, void *y,
+                                float *s_final, uint32_t flags, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Reverse mode of gdr_output_gate: with r = 1 / sqrt(mean o^2 + eps),

@@ -347,6 +347,36 @@ def test_gate_bwd_noalloc_scratch_limit():
     assert m and int(m[1]) * int(m[2]) * int(m[3]) == 2048 * 128 * 4
 
 
+def fwd_gate(gdr, B=2, T=5, H=2, Dk=64, Dv=64, dt=1, q=A16, k=A16, v=A16, a=A16, b=A16,
+             s0=None, gdt=1, g=A16, w=None, eps=1e-6, odt=0, y=A16, sf=None, flags=0, ws=A16,
+             wsb=None):
+    if wsb is None:
+        wsb = gdr.lib.gdr_chunk_fwd_gate_workspace_size(B, T, H, Dk, Dv, dt)
+    return gdr.lib.gdr_chunk_fwd_gate(B, T, H, Dk, Dv, dt, q, k, v, a, b, s0, gdt, g, w, eps, odt,
+                                      y, sf, flags, ws, wsb, None)
+
+
+def test_fwd_gate_workspace_size(gdr):
+    """bf16 inputs: per head, row block and one of four chunks, 32 words of 8
+    bytes (16-row blocks when B H Dv / 64 < 128, else 64-row blocks); fp32
+    inputs: an fp32 o; 0 for no tokens or unsupported sizes."""
+    f = gdr.lib.gdr_chunk_fwd_gate_workspace_size
+    assert f(8, 4096, 16, 128, 128, 1) == 8 * 16 * 2 * 4 * 32 * 8
+    assert f(1, 100, 2, 128, 128, 1) == 2 * 8 * 4 * 32 * 8
+    assert f(1, 100, 2, 128, 64, 1) == 2 * 4 * 4 * 32 * 8
+    assert f(2, 10, 3, 64, 128, 0) == 2 * 10 * 3 * 128 * 4
+    assert f(2, 0, 3, 64, 128, 1) == 0 and f(2, 10, 3, 96, 128, 1) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(g=None), 1), (dict(g=BAD), 1), (dict(y=None), 1), (dict(w=BAD), 1),
+    (dict(ws=None), 1), (dict(wsb=16), 1), (dict(eps=-1.0), 1), (dict(a=None), 1),
+    (dict(Dv=96), 2), (dict(gdt=3), 2), (dict(odt=3), 2), (dict(flags=8), 2),
+])
+def test_fwd_gate_validation(gdr, kw, code):
+    assert fwd_gate(gdr, **kw) == code
+
+
 def test_bwd_split_workspace_size(gdr):
     """nseg = 1: the plain backward's workspace; otherwise the split
     forward's pieces (with a discard buffer for the passes' outputs), N and
