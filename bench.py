@@ -4,20 +4,31 @@
 One step = one chunkwise gated delta rule forward (gdr_chunk_fwd) over the
 1.3B-layer workload: B=8, H=16, T=4096, d_k = d_v = 128, bf16 q/k/v, fp32
 alpha/beta, zero initial state, fp32 output and final state.  Inputs are
-seeded synthetic tensors resident in HBM before timing starts.
+seeded synthetic tensors resident in HBM before timing starts.  The
+headline leg runs after the decode, GDN-2 and long-context legs, so that
+its launches see the steady clock rather than the ramp after idle; its
+warm-up and timed calls are exactly --warmup and --steps.
 
 The JSON line (stdout, last line) carries:
-  value / unit       tokens/s of that forward (B*T tokens per call)
-  roofline           the chunked kernel against HBM bandwidth (its bound):
-                     algorithmic bytes per launch / mean launch time
+  value / unit       tokens/s of that forward (B*T tokens per call, from the
+                     median launch time)
+  roofline           the chunked kernel against HBM bandwidth: the
+                     algorithmic bytes of the workload (1,032 B per
+                     token-head for bf16 q, k, v, o and fp32 alpha, beta,
+                     plus the fp32 final state) / mean launch time; the
+                     fp32-o byte count (+256 B per token-head) beside it
   mfma               the same launches against the dense bf16 MFMA peak,
                      counting 2 (3 dk dv + 5 C d) flops per token-head
+  gdn_bf16_o         the same forward writing bf16 o
   decode             gdr_recurrent_step on 256 sequences x 16 heads, d=128,
                      64 consecutive steps: GB/s of state + token traffic
-  gdr2               gdr2_chunk_fwd on B=4 H=16 T=4096 d=128 (bf16 gates)
+  gdr2               gdr2_chunk_fwd on B=4 H=16 T=4096 d=128 (bf16 gates):
+                     tokens/s, HBM and MFMA fractions
   long_context       gdr_chunk_fwd on B=1 H=16 T=32768 d=128 with an initial
                      state (16 sequential chains; tokens/s, HBM and MFMA
                      fractions)
+  gate_fused         gdr_chunk_fwd_gate (output gate fused on the stores)
+                     against gdr_chunk_fwd + gdr_output_gate, interleaved
   l2norm             the fused L2 normalisation of q, k (GDR_L2NORM_QK) on
                      the GDN and GDN-2 workloads with raw q, k: launch time
                      fused, plain (no normalisation), and a separate
@@ -33,7 +44,9 @@ The JSON line (stdout, last line) carries:
   backward_long_context  the backward on the long-context workload, plain
                      and by gdr_chunk_bwd_split
   copy_reference     a plain 512 MiB device copy (achievable bandwidth)
-  cpu_baseline       the fp64 oracle timed on the host on the same workload
+  cpu_baseline       the fp64 oracle timed on the host on the same inputs:
+                     the headline workload at top level, and one entry in
+                     each of the decode, gdr2 and long_context legs
 """
 from __future__ import annotations
 
@@ -43,6 +56,7 @@ import glob
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -62,7 +76,12 @@ def log(*a):
 CSRC = os.path.join(ROOT, "gated_delta_rule_16_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
 # kernel-name prefix in rocprofv3 output -> the bench leg it belongs to
-KERNELS = {"gdn": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, 64, float, false>",
+KERNELS = {"gdn": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, 64, float, false, "
+                  "false>",
+           "gdn_bf16o": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, 64, "
+                        "unsigned short, false, false>",
+           "gdn_gate": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, 64, "
+                       "unsigned short, false, true>",
            "gdr2": "void gdr::(anonymous namespace)::gdr2_bf16_kernel<128, 128, float, false>",
            "decode": "void gdr::step_kernel<128, 128, unsigned short, float>",
            "gate": "void gdr::(anonymous namespace)::output_gate_kernel<128, float, unsigned short, "
@@ -84,32 +103,48 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def summarize(trace_dir, fetch_dir, write_dir, out_txt, command, timed=20):
-    """Turn rocprofv3 CSV output (a --kernel-trace --stats run and two --pmc
-    runs, FETCH_SIZE then WRITE_SIZE) into a short text summary and the JSON
-    the benchmark reads its `traffic` figures from.  Counter KiB are scaled
-    by what the same counter reads for the plain 512 MiB device copy."""
-    stats = list(csv.DictReader(open(glob.glob(os.path.join(trace_dir, "*kernel_stats.csv"))[0])))
+def _csv(d, suffix):
+    files = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return list(csv.DictReader(open(files[0])))
+
+
+def _counter_means(dirs):
+    """Mean per dispatch of every counter in the --pmc runs under `dirs`,
+    per bench leg (kernel-name prefix in KERNELS)."""
     per = {}
-    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        rows = list(csv.DictReader(open(glob.glob(os.path.join(d, "*counter_collection.csv"))[0])))
-        for leg, prefix in KERNELS.items():
-            vals = [float(r["Counter_Value"]) for r in rows
-                    if r["Kernel_Name"].startswith(prefix) and r["Counter_Name"] == name]
-            if vals:
-                per.setdefault(leg, {})[name] = sum(vals) / len(vals)
-    copy_bytes_kib = 512 * 1024   # the copy reads and writes 512 MiB each
-    scale = {"FETCH_SIZE": copy_bytes_kib / per["copy"]["FETCH_SIZE"],
-             "WRITE_SIZE": copy_bytes_kib / per["copy"]["WRITE_SIZE"]}
-    traffic = {}
-    for leg, c in per.items():
-        if leg == "copy":
-            continue
-        rd = c["FETCH_SIZE"] * scale["FETCH_SIZE"] * 1024
-        wr = c["WRITE_SIZE"] * scale["WRITE_SIZE"] * 1024
-        traffic[leg] = {"read_bytes": rd, "write_bytes": wr, "bytes": rd + wr}
+    for d in dirs:
+        vals = {}
+        for r in _csv(d, "counter_collection.csv"):
+            for leg, prefix in KERNELS.items():
+                if r["Kernel_Name"].startswith(prefix):
+                    vals.setdefault((leg, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+        for (leg, name), v in vals.items():
+            per.setdefault(leg, {})[name] = sum(v) / len(v)
+    return per
+
+
+def summarize(trace_dir, pmc_dirs, out_txt, command, timed=20):
+    """Turn rocprofv3 CSV output -- one --kernel-trace --stats run and
+    several --pmc runs of the same command -- into a short text summary and
+    the JSON the benchmark reads its counter figures from.
+
+    HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, TCC-to-memory
+    requests weighted by size) are scaled by what the same counter reads for
+    the plain 512 MiB device copy, whose bytes are known.  The per-size
+    request counts (TCC_EA0_RDREQ_32B/64B/128B, WRREQ/WRREQ_64B) are summed
+    into bytes beside them, with the same scale.  MFMA: executed bf16 flops
+    = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16; matrix-core busy fraction =
+    SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CYCLES-normalised active cycles x
+    CUs x 4 SIMDs), see below.  Decode: TCC_EA0_RDREQ_DRAM / TCC_EA0_RDREQ,
+    the share of L2 read misses sent to the memory controllers."""
+    stats = _csv(trace_dir, "kernel_stats.csv")
+    trace = _csv(trace_dir, "kernel_trace.csv")
+    per = _counter_means(pmc_dirs)
     lines = [f"# rocprofv3 summary (HIP sources hash {source_hash()})", "",
-             "Command:", f"  {command}", "", "Kernel trace (--kernel-trace --stats):",
+             "Commands:"] + [f"  {c}" for c in command.split(" ;; ")] + [
+             "", "Kernel trace (--kernel-trace --stats):",
              f"  {'kernel':60s} {'calls':>6s} {'avg us':>10s} {'min us':>10s} {'max us':>10s}"]
     for r in stats:
         lines.append(f"  {r['Name'][:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
@@ -117,9 +152,10 @@ def summarize(trace_dir, fetch_dir, write_dir, out_txt, command, timed=20):
     # the same trace, per bench leg: the timed launches only (the last
     # `timed` dispatches of each kernel; the warm-up launches before them
     # include the clock ramp after idle)
-    trace = list(csv.DictReader(open(glob.glob(os.path.join(trace_dir, "*kernel_trace.csv"))[0])))
     lines += ["", f"Timed launches (the last {timed} dispatches of each kernel in the trace, 10 for "
-              "the backward legs, as the bench times them):", f"  {'leg':8s} {'kernel':44s} {'n':>4s} {'avg us':>10s} {'min us':>10s}"]
+              "the backward legs, as the bench times them):",
+              f"  {'leg':9s} {'kernel':50s} {'n':>4s} {'avg us':>10s} {'min us':>10s}"]
+    dur_us = {}
     for leg, prefix in KERNELS.items():
         d = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in trace
                    if r["Kernel_Name"].startswith(prefix))
@@ -127,32 +163,152 @@ def summarize(trace_dir, fetch_dir, write_dir, out_txt, command, timed=20):
             continue
         n_timed = min(timed, 10) if leg in ("bwd", "bwd2") else timed   # legs capped at 10
         dur = [(e - b) / 1e3 for b, e in d[-n_timed:]]
-        lines.append(f"  {leg:8s} {prefix[:44]:44s} {len(dur):4d} {sum(dur) / len(dur):10.1f} "
-                     f"{min(dur):10.1f}")
-    lines += ["", "HBM counters per dispatch (KiB as read; scale = copy's known bytes / reading):",
-              f"  FETCH_SIZE scale {scale['FETCH_SIZE']:.4f}, WRITE_SIZE scale {scale['WRITE_SIZE']:.4f}"]
+        dur_us[leg] = sum(dur) / len(dur)
+        lines.append(f"  {leg:9s} {prefix.split('::')[-1][:50]:50s} {len(dur):4d} "
+                     f"{dur_us[leg]:10.1f} {min(dur):10.1f}")
+    traffic, scale = {}, {}
+    copy = per.get("copy", {})
+    for name in ("FETCH_SIZE", "WRITE_SIZE"):
+        if copy.get(name):
+            scale[name] = 512 * 1024 / copy[name]   # the copy reads and writes 512 MiB each
+    ea = {}
     for leg, c in per.items():
+        if "FETCH_SIZE" in c and "WRITE_SIZE" in c and scale:
+            rd = c["FETCH_SIZE"] * scale["FETCH_SIZE"] * 1024
+            wr = c["WRITE_SIZE"] * scale["WRITE_SIZE"] * 1024
+            traffic[leg] = {"read_bytes": rd, "write_bytes": wr, "bytes": rd + wr}
+        if all(k in c for k in ("TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
+                                "TCC_EA0_RDREQ_128B_sum")):
+            ea.setdefault(leg, {})["read_raw"] = (32 * c["TCC_EA0_RDREQ_32B_sum"] + 64 *
+                                                  c["TCC_EA0_RDREQ_64B_sum"] + 128 *
+                                                  c["TCC_EA0_RDREQ_128B_sum"])
+        if all(k in c for k in ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum")):
+            ea.setdefault(leg, {})["write_raw"] = (64 * c["TCC_EA0_WRREQ_64B_sum"] + 32 *
+                                                   (c["TCC_EA0_WRREQ_sum"] -
+                                                    c["TCC_EA0_WRREQ_64B_sum"]))
+    ea_scale = {}
+    if "copy" in ea:
+        if ea["copy"].get("read_raw"):
+            ea_scale["read"] = (512 << 20) / ea["copy"]["read_raw"]
+        if ea["copy"].get("write_raw"):
+            ea_scale["write"] = (512 << 20) / ea["copy"]["write_raw"]
+    lines += ["", "HBM bytes per dispatch.  FETCH_SIZE / WRITE_SIZE as read (KiB), scaled by "
+                  "the 512 MiB copy's reading:"]
+    if scale:
+        lines.append(f"  scale FETCH {scale['FETCH_SIZE']:.4f}, WRITE {scale['WRITE_SIZE']:.4f}")
+    for leg, c in per.items():
+        if "FETCH_SIZE" not in c:
+            continue
         t = traffic.get(leg)
-        extra = "" if t is None else (f" -> read {t['read_bytes'] / 1e6:.1f} MB, write "
-                                      f"{t['write_bytes'] / 1e6:.1f} MB per launch")
-        lines.append(f"  {leg:7s} FETCH {c['FETCH_SIZE']:12.1f}  WRITE {c['WRITE_SIZE']:12.1f}{extra}")
+        extra = "" if t is None else (f" -> read {t['read_bytes'] / 1e6:8.1f} MB, write "
+                                      f"{t['write_bytes'] / 1e6:8.1f} MB")
+        lines.append(f"  {leg:9s} FETCH {c['FETCH_SIZE']:12.1f}  WRITE {c.get('WRITE_SIZE', 0):12.1f}"
+                     f"{extra}")
+    if ea:
+        lines += ["", "Request-size sums: read 32 n32 + 64 n64 + 128 n128 (TCC_EA0_RDREQ_*B_sum), "
+                      "write 64 n64 + 32 (n - n64) (TCC_EA0_WRREQ*_sum), raw and copy-scaled:"]
+        if ea_scale:
+            lines.append("  scale read {:.4f}, write {:.4f}".format(ea_scale.get("read", 0),
+                                                                      ea_scale.get("write", 0)))
+        for leg, e in ea.items():
+            r, w = e.get("read_raw"), e.get("write_raw")
+            rs = "" if r is None else (f"read raw {r / 1e6:8.1f} MB -> "
+                                       f"{r * ea_scale.get('read', 0) / 1e6:8.1f} MB")
+            ws = "" if w is None else (f"  write raw {w / 1e6:8.1f} MB -> "
+                                       f"{w * ea_scale.get('write', 0) / 1e6:8.1f} MB")
+            lines.append(f"  {leg:9s} {rs}{ws}")
+    mfma = {}
+    for leg, c in per.items():
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" not in c:
+            continue
+        m = {"exec_bf16_flops": 512 * c["SQ_INSTS_VALU_MFMA_MOPS_BF16"]}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "GRBM_GUI_ACTIVE" in c and c["GRBM_GUI_ACTIVE"]:
+            m["busy_frac"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * 256 * 4)
+        if leg in dur_us:
+            m["exec_tflops"] = m["exec_bf16_flops"] / dur_us[leg] / 1e6
+            m["exec_frac"] = m["exec_tflops"] / BF16_PEAK_TFLOPS
+        m["raw"] = {k: v for k, v in c.items() if k.startswith(("SQ_", "GRBM_"))}
+        mfma[leg] = m
+    if mfma:
+        lines += ["", "Matrix cores per dispatch: executed bf16 flops = 512 x "
+                      "SQ_INSTS_VALU_MFMA_MOPS_BF16; busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+                      "(GRBM_GUI_ACTIVE x 256 CU x 4 SIMD); raw counters beside:"]
+        for leg, m in mfma.items():
+            raw = "  ".join(f"{k} {v:.4g}" for k, v in m["raw"].items())
+            lines.append(f"  {leg:9s} exec {m['exec_bf16_flops'] / 1e9:8.2f} GFLOP"
+                         + (f" = {m['exec_tflops']:7.1f} TFLOP/s over the timed launch "
+                            f"({m['exec_frac']:.3f} of peak)" if "exec_tflops" in m else "")
+                         + (f", busy {m['busy_frac']:.3f}" if "busy_frac" in m else ""))
+            lines.append(f"            {raw}")
+    dram = {}
+    for leg, c in per.items():
+        if c.get("TCC_EA0_RDREQ_sum") and "TCC_EA0_RDREQ_DRAM_sum" in c:
+            dram[leg] = c["TCC_EA0_RDREQ_DRAM_sum"] / c["TCC_EA0_RDREQ_sum"]
+    if dram:
+        lines += ["", "Read requests sent to the memory controllers "
+                      "(TCC_EA0_RDREQ_DRAM_sum / TCC_EA0_RDREQ_sum):"]
+        for leg, f in dram.items():
+            lines.append(f"  {leg:9s} {f:.4f}")
     open(out_txt, "w").write("\n".join(lines) + "\n")
-    json.dump({"source_hash": source_hash(), "scale": scale, "traffic": traffic,
-               "command": command}, open(TRAFFIC_FILE, "w"), indent=1)
+    json.dump({"source_hash": source_hash(), "scale": scale, "traffic": traffic, "ea": ea,
+               "ea_scale": ea_scale, "mfma": {k: {kk: vv for kk, vv in v.items() if kk != "raw"}
+                                              for k, v in mfma.items()},
+               "dram_read_share": dram, "command": command},
+              open(TRAFFIC_FILE, "w"), indent=1)
     print("\n".join(lines))
 
 
-def measured_traffic(leg):
-    """HBM bytes per launch from the committed counter summary, or None when
-    the kernels have changed since the counters were taken."""
+def _measured(key, leg):
     try:
         d = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     if d.get("source_hash") != source_hash():
         return None
-    t = d.get("traffic", {}).get(leg)
+    return d.get(key, {}).get(leg)
+
+
+def measured_traffic(leg):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernels have changed since the counters were taken."""
+    t = _measured("traffic", leg)
     return None if t is None else t["bytes"]
+
+
+def measured_mfma(leg):
+    """Executed bf16 MFMA flops and busy fraction from the committed counter
+    summary (None when the kernels have changed since)."""
+    return _measured("mfma", leg)
+
+
+def measured_dram(leg):
+    return _measured("dram_read_share", leg)
+
+
+_INPUTS = {}
+
+
+def config_inputs(idx):
+    """The seeded host inputs of workload `idx`, drawn once per process."""
+    if idx not in _INPUTS:
+        from gdr_gen import make_config
+        _INPUTS[idx] = make_config(idx)
+    return _INPUTS[idx]
+
+
+_DEVICE = {}
+
+
+def on_device(idx, *fields):
+    """Fields of workload `idx` copied to cuda:0 once per process: main()
+    stages every forward leg's inputs before the first timed leg, so no
+    host-side generation or copy idles the GPU between the legs."""
+    out = []
+    for f in fields:
+        if (idx, f) not in _DEVICE:
+            _DEVICE[(idx, f)] = getattr(config_inputs(idx), f).to("cuda:0")
+        out.append(_DEVICE[(idx, f)])
+    return out
 
 
 def time_launches(fn, warmup, steps):
@@ -176,30 +332,37 @@ def time_launches(fn, warmup, steps):
     return mean, ms[0] / 1e3, ms[len(ms) // 2] / 1e3, wall
 
 
-def bench_gdn(gdr, torch, warmup, steps):
-    from gdr_gen import make_config
-    inp = make_config(1)
+def gdn_bytes(B, T, H, Dk, Dv, o_bytes=2, states=1):
+    """Algorithmic HBM bytes of one forward call: per token-head q, k, v in
+    bf16, alpha and beta in fp32 and o (bf16: 1,032 B at d = 128), plus
+    each fp32 state read or written once."""
+    return B * T * H * (2 * (Dk + Dk + Dv) + 8 + o_bytes * Dv) + states * 4 * B * H * Dv * Dk
+
+
+def gdn_flops(B, T, H, Dk, Dv, C=64):
+    """Algorithmic matrix flops of one forward call, 2 (3 dk dv + 5 C d)
+    per token-head at the reference chunk C = 64 (d = (dk + dv) / 2)."""
+    return B * T * H * 2 * (3 * Dk * Dv + 5 * C * (Dk + Dv) // 2)
+
+
+def bench_gdn(gdr, torch, warmup, steps, out_dtype="f32"):
+    inp = config_inputs(1)
     B, T, H, Dk = inp.q.shape
     Dv = inp.v.shape[-1]
     dev = torch.device("cuda:0")
-    q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
-    a, b = inp.alpha.to(dev), inp.beta.to(dev)
-    o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+    q, k, v, a, b = on_device(1, "q", "k", "v", "alpha", "beta")
+    odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    o = torch.empty((B, T, H, Dv), dtype=odt, device=dev)
     sf = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
 
     def fn():
-        gdr.gdr_chunk_fwd(q, k, v, a, b, None, out_dtype=torch.float32, o=o,
-                          s_final=sf)
+        gdr.gdr_chunk_fwd(q, k, v, a, b, None, out_dtype=odt, o=o, s_final=sf)
 
     mean, mn, med, wall = time_launches(fn, warmup, steps)
-    th = B * T * H
-    # algorithmic bytes: q, k, v bf16 + alpha, beta fp32 + o fp32 per
-    # token-head, plus the fp32 final state once
-    bytes_launch = th * (2 * (Dk + Dk + Dv) + 8 + 4 * Dv) + 4 * B * H * Dv * Dk
-    C = 64
-    flops_launch = th * 2 * (3 * Dk * Dv + 5 * C * (Dk + Dv) // 2)
     return dict(inp=inp, mean=mean, min=mn, median=med, wall=wall, B=B, T=T, H=H, Dk=Dk,
-                Dv=Dv, bytes=bytes_launch, flops=flops_launch)
+                Dv=Dv, bytes=gdn_bytes(B, T, H, Dk, Dv),
+                bytes_as_run=gdn_bytes(B, T, H, Dk, Dv, o_bytes=4 if out_dtype == "f32" else 2),
+                flops=gdn_flops(B, T, H, Dk, Dv))
 
 
 def bench_longctx(gdr, torch, warmup, steps, nseg=8):
@@ -208,14 +371,11 @@ def bench_longctx(gdr, torch, warmup, steps, nseg=8):
     narrow row blocks and half the compute units idle); the split call runs
     it as nseg = 8 segments side by side (three passes plus a scan).  Both
     are timed; the bytes and flops are the workload's algorithmic ones."""
-    from gdr_gen import make_config
-    inp = make_config(2)
+    inp = config_inputs(2)
     B, T, H, Dk = inp.q.shape
     Dv = inp.v.shape[-1]
     dev = torch.device("cuda:0")
-    q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
-    a, b = inp.alpha.to(dev), inp.beta.to(dev)
-    s0 = inp.s0.to(dev)
+    q, k, v, a, b, s0 = on_device(2, "q", "k", "v", "alpha", "beta", "s0")
     o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
     sf = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
     ws = torch.empty(gdr.gdr_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, q.dtype, nseg),
@@ -230,23 +390,18 @@ def bench_longctx(gdr, torch, warmup, steps, nseg=8):
 
     mean, mn, med, wall = time_launches(split, warmup, steps)
     pmean, pmn, _, _ = time_launches(plain, warmup, steps)
-    th = B * T * H
-    bytes_launch = th * (2 * (Dk + Dk + Dv) + 8 + 4 * Dv) + 2 * 4 * B * H * Dv * Dk
-    C = 64
-    flops_launch = th * 2 * (3 * Dk * Dv + 5 * C * (Dk + Dv) // 2)
-    return dict(mean=mean, min=mn, plain_mean=pmean, plain_min=pmn, nseg=nseg, B=B, T=T, H=H,
-                bytes=bytes_launch, flops=flops_launch)
+    return dict(inp=inp, mean=mean, min=mn, median=med, plain_mean=pmean, plain_min=pmn,
+                nseg=nseg, B=B, T=T, H=H, bytes=gdn_bytes(B, T, H, Dk, Dv, states=2),
+                bytes_as_run=gdn_bytes(B, T, H, Dk, Dv, o_bytes=4, states=2),
+                flops=gdn_flops(B, T, H, Dk, Dv))
 
 
 def bench_decode(gdr, torch, warmup):
-    from gdr_gen import make_config
-    inp = make_config(3)
+    inp = config_inputs(3)
     steps, N, H, Dk = inp.q.shape
     Dv = inp.v.shape[-1]
     dev = torch.device("cuda:0")
-    S = inp.state0.to(dev)
-    q, k, v = (x.to(dev) for x in (inp.q, inp.k, inp.v))
-    a, b = inp.alpha.to(dev), inp.beta.to(dev)
+    S, q, k, v, a, b = on_device(3, "state0", "q", "k", "v", "alpha", "beta")
     o = torch.empty((N, H, Dv), dtype=torch.float32, device=dev)
     for s in range(warmup):
         gdr.gdr_recurrent_step(q[s], k[s], v[s], a[s], b[s], S, out_dtype=torch.float32, o=o)
@@ -261,18 +416,21 @@ def bench_decode(gdr, torch, warmup):
     ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     med = ms[len(ms) // 2] / 1e3
     nh = N * H
-    bytes_step = nh * (2 * 4 * Dv * Dk + 2 * (2 * Dk + Dv) + 8 + 4 * Dv)
-    return dict(median=med, min=ms[0] / 1e3, mean=sum(ms) / len(ms) / 1e3, bytes=bytes_step,
-                N=N, H=H, steps=steps)
+    # per head-step: the fp32 state read and written, q, k, v and o in bf16,
+    # alpha and beta in fp32 (132,104 B at d = 128); o is written in fp32
+    # here, +2 dv B per head-step
+    bytes_step = nh * (2 * 4 * Dv * Dk + 2 * (2 * Dk + Dv) + 8 + 2 * Dv)
+    bytes_as_run = bytes_step + nh * 2 * Dv
+    return dict(inp=inp, median=med, min=ms[0] / 1e3, mean=sum(ms) / len(ms) / 1e3,
+                bytes=bytes_step, bytes_as_run=bytes_as_run, N=N, H=H, steps=steps)
 
 
 def bench_gdr2(gdr, torch, warmup, steps):
-    from gdr_gen import make_config
-    inp = make_config(4)
+    inp = config_inputs(4)
     B, T, H, Dk = inp.q.shape
     Dv = inp.v.shape[-1]
     dev = torch.device("cuda:0")
-    args = [x.to(dev) for x in (inp.q, inp.k, inp.v, inp.alpha, inp.erase, inp.write)]
+    args = on_device(4, "q", "k", "v", "alpha", "erase", "write")
     o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
     sf = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
 
@@ -285,8 +443,12 @@ def bench_gdr2(gdr, torch, warmup, steps):
         return dict(error=str(e))
     mean, mn, med, wall = time_launches(fn, warmup, steps)
     th = B * T * H
-    bytes_launch = th * (2 * (4 * Dk + 2 * Dv) + 4 * Dv) + 4 * B * H * Dv * Dk
-    return dict(mean=mean, min=mn, median=med, B=B, T=T, H=H, bytes=bytes_launch)
+    # algorithmic bytes: q, k, alpha, erase bf16 (d_k each), v, write, o
+    # bf16 (d_v each) per token-head, plus the fp32 final state
+    bytes_launch = th * 2 * (4 * Dk + 3 * Dv) + 4 * B * H * Dv * Dk
+    bytes_as_run = th * (2 * (4 * Dk + 2 * Dv) + 4 * Dv) + 4 * B * H * Dv * Dk   # fp32 o
+    return dict(inp=inp, mean=mean, min=mn, median=med, B=B, T=T, H=H, bytes=bytes_launch,
+                bytes_as_run=bytes_as_run, flops=gdn_flops(B, T, H, Dk, Dv))
 
 
 def time_interleaved(fns, warmup, rounds):
@@ -386,6 +548,42 @@ def bench_gate_bwd(gdr, torch, warmup, steps):
     return dict(mean=mean, min=mn, bytes=n * (4 + 2 + 2 + 4 + 4) + 4 * 128 * 2)
 
 
+def bench_gate_fused(gdr, torch, warmup, steps):
+    """The forward with the output gate on the B8 H16 T4096 d128 workload
+    (bf16 gate, fp32 weight, bf16 y): gdr_chunk_fwd_gate against
+    gdr_chunk_fwd (fp32 o) followed by gdr_output_gate, and the plain
+    forward alone, timed interleaved so that all three see the same clocks."""
+    from gdr_gen import make_gate
+    inp = config_inputs(1)
+    B, T, H, Dk = inp.q.shape
+    Dv = inp.v.shape[-1]
+    dev = torch.device("cuda:0")
+    q, k, v, a, b = on_device(1, "q", "k", "v", "alpha", "beta")
+    gi = make_gate(B * T, H, Dv, "f32", "bf16", seed=452)
+    g = gi.g.reshape(B, T, H, Dv).to(dev)
+    w = gi.w.to(dev)
+    o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+    y = torch.empty((B, T, H, Dv), dtype=torch.bfloat16, device=dev)
+    sf = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdr.gdr_chunk_fwd_gate_workspace_size(B, T, H, Dk, Dv, q.dtype),
+                     dtype=torch.uint8, device=dev)
+
+    def two_calls():
+        gdr.gdr_chunk_fwd(q, k, v, a, b, None, out_dtype=torch.float32, o=o, s_final=sf)
+        gdr.gdr_output_gate(o, g, w, 1e-6, y=y)
+
+    def fused():
+        gdr.gdr_chunk_fwd_gate(q, k, v, a, b, None, g, w, 1e-6, out_dtype=torch.bfloat16, y=y,
+                               s_final=sf, workspace=ws)
+
+    def plain():
+        gdr.gdr_chunk_fwd(q, k, v, a, b, None, out_dtype=torch.float32, o=o, s_final=sf)
+
+    t = time_interleaved({"fused": fused, "two_calls": two_calls, "forward_only": plain},
+                         warmup, steps)
+    return dict(t=t, tokens=B * T)
+
+
 def bench_bwd(gdr, torch, warmup, steps):
     """gdr_chunk_bwd on B8 H16 T4096 d128 (bf16 q/k/v and dL/do, dL/dS_T
     given, zero S_0).  It runs the GDN-2 backward with broadcast gates, so
@@ -438,8 +636,7 @@ def bench_bwd_long(gdr, torch, warmup, steps, nseg=4):
     """The backward on the long-context workload (B1 H16 T32768 d128, bf16
     inputs and dL/do, initial state, dL/dS_T given): the plain call (64
     workgroups) and the split call with nseg segments side by side."""
-    from gdr_gen import make_config
-    inp = make_config(2)
+    inp = config_inputs(2)
     dev = torch.device("cuda:0")
     args = [x.to(dev) for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.s0)]
     B, T, H, Dk = inp.q.shape
@@ -503,44 +700,126 @@ def bench_copy(torch, warmup, steps, nbytes=512 << 20):
 
 
 def _cpu_model():
+    """The host CPU as lscpu describes it: model name, family / model /
+    stepping numbers and logical CPU count (/proc/cpuinfo if lscpu is
+    missing)."""
+    fields = {}
     try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
-    except OSError:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    except (OSError, subprocess.SubprocessError):
         pass
-    return None
+    if "Model name" not in fields:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        fields["Model name"] = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            return None
+    desc = fields.get("Model name")
+    extra = ", ".join(f"{k.lower()} {fields[k]}" for k in ("CPU family", "Model", "Stepping",
+                                                            "CPU(s)") if k in fields)
+    return f"{desc} ({extra})" if extra else desc
 
 
-def cpu_baseline(inp, repeats=3):
-    """The fp64 oracle on the whole workload (B8 H16 T4096 d128 finishes in
-    about half a second on 16 host threads), best of `repeats`, on every thread the
-    oracle's OpenMP runtime uses; then once more on one thread."""
+def _oracle_timed(fn, threads, repeats=1):
+    """Best wall time (s) of `repeats` runs of fn() with the oracle's OpenMP
+    runtime on `threads` threads (restored afterwards)."""
     import oracle
-    qq, kk, vv, aa, bb = (oracle._f64(x) for x in (inp.q, inp.k, inp.v, inp.alpha,
-                                                     inp.beta))   # conversion excluded
-    best = float("inf")
-    for _ in range(repeats):
-        t0 = time.perf_counter()
-        oracle.gdn_fwd(qq, kk, vv, aa, bb, None)
-        best = min(best, time.perf_counter() - t0)
-    B, T, H, Dk = inp.q.shape
-    tokens = B * T
-    cores = oracle.num_threads()
-    oracle.set_num_threads(1)
+    all_threads = oracle.num_threads()
+    oracle.set_num_threads(threads)
     try:
-        t0 = time.perf_counter()
-        oracle.gdn_fwd(qq, kk, vv, aa, bb, None)
-        one = time.perf_counter() - t0
+        best = float("inf")
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            fn()
+            best = min(best, time.perf_counter() - t0)
     finally:
-        oracle.set_num_threads(cores)
-    return dict(value=tokens / best, unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"whole workload B{B} H{H} T{T} d{Dk} ({tokens} tokens x {H} heads), "
-                       f"fp64 token-by-token recurrence, best of {repeats}: {best:.2f} s; "
-                       f"one thread, one run: {one:.2f} s",
-                one_thread=dict(value=tokens / one, unit="tokens/s", seconds=one),
-                cpu_model=_cpu_model())
+        oracle.set_num_threads(all_threads)
+    return best
+
+
+def cpu_baselines(inputs):
+    """The fp64 oracle on the host, on the inputs the GPU legs used (their
+    conversion to fp64 excluded).  Per leg: the whole workload on every
+    thread of the oracle's OpenMP runtime (best of two runs), and a stated
+    slice of it on one thread (one run), each scaled to the leg's unit.
+    About 15 s of host time in all on a 16-thread host."""
+    import numpy as np
+    import oracle
+    cores = oracle.num_threads()
+    model = _cpu_model()
+    f64 = oracle._f64
+    res = {}
+
+    def entry(unit, value, seconds, sample, one_value, one_seconds, one_sample, **extra):
+        d = dict(value=value, unit=unit, cores=cores, kind="oracle", seconds=seconds,
+                 sample=sample, cpu_model=model,
+                 one_thread=dict(value=one_value, unit=unit, cores=1, seconds=one_seconds,
+                                 sample=one_sample))
+        d.update(extra)
+        return d
+
+    if "gdn" in inputs:
+        inp = inputs["gdn"]
+        x = [f64(t) for t in (inp.q, inp.k, inp.v, inp.alpha, inp.beta)]
+        B, T, H, Dk = inp.q.shape
+        full = _oracle_timed(lambda: oracle.gdn_fwd(*x, None), cores, 2)
+        one = _oracle_timed(lambda: oracle.gdn_fwd(*[t[:1] for t in x], None), 1)
+        res["gdn"] = entry("tokens/s", B * T / full, full,
+                           f"whole B{B} H{H} T{T} d{Dk} workload, fp64 token-by-token "
+                           f"recurrence, best of 2", T / one, one,
+                           f"batch 0 of {B} (T{T}, {H} heads), one run")
+    if "gdr2" in inputs:
+        inp = inputs["gdr2"]
+        x = [f64(t) for t in (inp.q, inp.k, inp.v, inp.alpha, inp.erase, inp.write)]
+        B, T, H, Dk = inp.q.shape
+        full = _oracle_timed(lambda: oracle.gdn2_fwd(*x, None), cores, 2)
+        one = _oracle_timed(lambda: oracle.gdn2_fwd(*[t[:1] for t in x], None), 1)
+        res["gdr2"] = entry("tokens/s", B * T / full, full,
+                            f"whole GDN-2 B{B} H{H} T{T} d{Dk} workload, fp64, best of 2",
+                            T / one, one, f"batch 0 of {B} (T{T}, {H} heads), one run")
+    if "longctx" in inputs:
+        inp = inputs["longctx"]
+        x = [f64(t) for t in (inp.q, inp.k, inp.v, inp.alpha, inp.beta)]
+        s0 = f64(inp.s0)
+        B, T, H, Dk = inp.q.shape
+        full = _oracle_timed(lambda: oracle.gdn_fwd(*x, s0), cores, 2)
+        Ts = T // 8
+        one = _oracle_timed(lambda: oracle.gdn_fwd(*[t[:, :Ts] for t in x], s0), 1)
+        res["longctx"] = entry("tokens/s", B * T / full, full,
+                               f"whole B{B} H{H} T{T} d{Dk} workload with its initial state "
+                               f"({H} sequential chains), fp64, best of 2", B * Ts / one, one,
+                               f"the first {Ts} of {T} tokens, one run")
+    if "decode" in inputs:
+        inp, nbytes = inputs["decode"]
+        steps, N, H, Dk = inp.q.shape
+        x = [f64(t) for t in (inp.q, inp.k, inp.v, inp.alpha, inp.beta)]
+        S = f64(inp.state0)
+
+        def run(n_steps, state):
+            for s in range(n_steps):
+                oracle.gdn_step(*[t[s] for t in x], state)
+
+        st = S.copy()
+        full = _oracle_timed(lambda: run(steps, st), cores)
+        ns = 8
+        st = np.ascontiguousarray(S[:N // 8])
+        one = _oracle_timed(lambda: [oracle.gdn_step(*[t[s, :N // 8] for t in x], st)
+                                     for s in range(ns)], 1)
+        res["decode"] = entry("steps/s", steps / full, full,
+                              f"all {steps} steps on N{N} H{H} d{Dk}, fp64 state, one run",
+                              ns / (8 * one), one,
+                              f"{ns} steps on sequences 0..{N // 8 - 1} of {N}, scaled to a "
+                              f"full step (x8), one run",
+                              GBps=nbytes * steps / full / 1e9,
+                              one_thread_GBps=nbytes / 8 * ns / one / 1e9)
+    return res
 
 
 def main():
@@ -549,20 +828,25 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
-    ap.add_argument("--only", choices=["gdn", "decode", "gdr2", "longctx", "l2norm", "gate", "gate_bwd",
-                                       "bwd", "bwd2", "bwd_long", "copy"],
+    ap.add_argument("--only", choices=["gdn", "gdn_bf16o", "decode", "gdr2", "longctx", "gate_fused",
+                                       "l2norm", "gate", "gate_bwd", "bwd", "bwd2", "bwd_long",
+                                       "copy"],
                     default=None,
                     help="time one operation only (for profiling)")
     ap.add_argument("--skip", default="",
                     help="comma-separated legs not to run (the profiled command skips l2norm, "
                          "longctx and bwd_long, whose calls reuse the headline and backward "
                          "kernels' names at other shapes)")
-    ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT"),
-                    help="summarize rocprofv3 CSV output into OUT and the traffic JSON, then exit")
-    ap.add_argument("--command", default="", help="the profiling command, recorded in --summarize")
+    ap.add_argument("--summarize", nargs=2, metavar=("TRACE_DIR", "OUT"),
+                    help="summarize rocprofv3 CSV output (a kernel trace in TRACE_DIR and the "
+                         "--pmc runs named by --pmc-dir) into OUT and the counter JSON, then exit")
+    ap.add_argument("--pmc-dir", action="append", default=[],
+                    help="a rocprofv3 --pmc output folder (repeatable)")
+    ap.add_argument("--command", default="",
+                    help="the profiling commands (' ;; '-separated), recorded in --summarize")
     args = ap.parse_args()
     if args.summarize:
-        summarize(*args.summarize, command=args.command)
+        summarize(args.summarize[0], args.pmc_dir, args.summarize[1], command=args.command)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this "
@@ -581,11 +865,23 @@ def main():
     def want(leg):
         return args.only in (None, leg) and leg not in skip
 
+    # Stage the forward legs' inputs in HBM first.  The headline leg then
+    # runs right after the decode, GDN-2 and long-context legs: after idle
+    # the GPU takes some tens of milliseconds of sustained load to reach its
+    # steady clocks, and back-to-back launches from a cold start time
+    # 20-30 % slower.  Its own warm-up and timed calls are --warmup and
+    # --steps.
+    stage = {1: ("q", "k", "v", "alpha", "beta"), 2: ("q", "k", "v", "alpha", "beta", "s0"),
+             3: ("state0", "q", "k", "v", "alpha", "beta"),
+             4: ("q", "k", "v", "alpha", "erase", "write")}
+    legs_of = {1: ("gdn", "gdn_bf16o", "gate_fused"), 2: ("longctx",), 3: ("decode",),
+               4: ("gdr2",)}
+    for idx, fields in stage.items():
+        if any(want(leg) for leg in legs_of[idx]):
+            log(f"staging workload {idx} inputs ...")
+            on_device(idx, *fields)
+    torch.cuda.synchronize()
     res = {}
-    if want("gdn"):
-        log("timing gdr_chunk_fwd B8 H16 T4096 d128 ...")
-        res["gdn"] = bench_gdn(gdr, torch, args.warmup, args.steps)
-        log(f"  mean {res['gdn']['mean'] * 1e6:.1f} us")
     if want("decode"):
         log("timing gdr_recurrent_step N256 H16 d128 x 64 steps ...")
         res["decode"] = bench_decode(gdr, torch, args.warmup)
@@ -596,6 +892,16 @@ def main():
     if want("longctx"):
         log("timing gdr_chunk_fwd B1 H16 T32768 d128 (long context) ...")
         res["longctx"] = bench_longctx(gdr, torch, min(args.warmup, 10), min(args.steps, 10))
+    if want("gdn"):
+        log("timing gdr_chunk_fwd B8 H16 T4096 d128 ...")
+        res["gdn"] = bench_gdn(gdr, torch, args.warmup, args.steps)
+        log(f"  median {res['gdn']['median'] * 1e6:.1f} us, mean {res['gdn']['mean'] * 1e6:.1f} us")
+    if want("gdn_bf16o"):
+        log("timing gdr_chunk_fwd B8 H16 T4096 d128, bf16 o ...")
+        res["gdn_bf16o"] = bench_gdn(gdr, torch, args.warmup, args.steps, out_dtype="bf16")
+    if want("gate_fused"):
+        log("timing gdr_chunk_fwd_gate against gdr_chunk_fwd + gdr_output_gate ...")
+        res["gate_fused"] = bench_gate_fused(gdr, torch, args.warmup, args.steps)
     if want("l2norm"):
         log("timing the fused q, k normalisation (GDN and GDN-2 workloads) ...")
         res["l2norm"] = bench_l2norm(gdr, torch, args.warmup, min(args.steps, 30))
@@ -618,62 +924,110 @@ def main():
         log("timing a 512 MiB device copy ...")
         res["copy"] = bench_copy(torch, args.warmup, args.steps)
 
+    cpu = {}
+    if not args.no_cpu:
+        log("timing the fp64 oracle on the host ...")
+        cin = {leg: res[leg]["inp"] for leg in ("gdn", "gdr2", "longctx") if leg in res
+               and "inp" in res[leg]}
+        if "decode" in res:
+            cin["decode"] = (res["decode"]["inp"], res["decode"]["bytes"])
+        cpu = cpu_baselines(cin)
+
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16", "data": "synthetic (seeded; shapes of a 1.3B GDN layer)"}
     if "gdn" in res:
         g = res["gdn"]
         tok = g["B"] * g["T"]
-        out["value"] = tok / g["mean"]
+        out["value"] = tok / g["median"]
         out["unit"] = "tokens/s"
         out["ms_per_step"] = g["wall"] / args.steps * 1e3
         gbs = g["bytes"] / g["mean"] / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                            "traffic": measured_traffic("gdn"),
-                           "kernel": "chunk_bf16_kernel<128,128,64,float,false>",
+                           "kernel": "chunk_bf16_kernel<128,128,64,float,false,false>",
                            "algorithmic_bytes_per_launch": g["bytes"],
+                           "bytes_with_fp32_o": g["bytes_as_run"],
+                           "frac_with_fp32_o": g["bytes_as_run"] / g["mean"] / 1e9 / HBM_PEAK_GBS,
                            "launch_us_mean": g["mean"] * 1e6, "launch_us_median": g["median"] * 1e6,
                            "launch_us_min": g["min"] * 1e6}
         tf = g["flops"] / g["mean"] / 1e12
         out["mfma"] = {"achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                       "frac": tf / BF16_PEAK_TFLOPS, "flops_per_launch": g["flops"]}
+                       "frac": tf / BF16_PEAK_TFLOPS, "flops_per_launch": g["flops"],
+                       "counters": measured_mfma("gdn")}
         out["config"] = {"workload": "gdr_chunk_fwd B8 H16 T4096 d128, bf16 q/k/v, "
                                      "fp32 alpha/beta/o/state, zero initial state",
                          "B": g["B"], "T": g["T"], "H": g["H"], "Dk": g["Dk"], "Dv": g["Dv"],
                          "chunk": 32, "global_batch": g["B"], "seq_len": g["T"]}
+    if "gdn_bf16o" in res:
+        g = res["gdn_bf16o"]
+        gbs = g["bytes"] / g["mean"] / 1e9
+        out["gdn_bf16_o"] = {"workload": "gdr_chunk_fwd B8 H16 T4096 d128, bf16 q/k/v/o",
+                             "tokens/s": g["B"] * g["T"] / g["median"],
+                             "launch_us_mean": g["mean"] * 1e6,
+                             "launch_us_median": g["median"] * 1e6,
+                             "launch_us_min": g["min"] * 1e6, "GB/s": gbs,
+                             "frac_hbm": gbs / HBM_PEAK_GBS,
+                             "frac_mfma": g["flops"] / g["mean"] / 1e12 / BF16_PEAK_TFLOPS}
     if "decode" in res:
         d = res["decode"]
         gbs = d["bytes"] / d["median"] / 1e9
-        out["decode"] = {"workload": "gdr_recurrent_step N256 H16 d128, 64 steps",
+        out["decode"] = {"workload": "gdr_recurrent_step N256 H16 d128, 64 steps, fp32 o",
                          "us_per_step_median": d["median"] * 1e6,
                          "us_per_step_min": d["min"] * 1e6, "GB/s": gbs,
                          "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_step": d["bytes"],
-                         "traffic": measured_traffic("decode")}
+                         "bytes_with_fp32_o": d["bytes_as_run"],
+                         "traffic": measured_traffic("decode"),
+                         "dram_read_share": measured_dram("decode")}
+        if "decode" in cpu:
+            out["decode"]["cpu_baseline"] = cpu["decode"]
     if "gdr2" in res:
         r = res["gdr2"]
         if "error" in r:
             out["gdr2"] = {"error": r["error"]}
         else:
             gbs = r["bytes"] / r["mean"] / 1e9
+            tf = r["flops"] / r["mean"] / 1e12
             out["gdr2"] = {"workload": "gdr2_chunk_fwd B4 H16 T4096 d128 bf16, fp32 o",
-                           "tokens/s": r["B"] * r["T"] / r["mean"],
-                           "launch_us_mean": r["mean"] * 1e6, "GB/s": gbs,
+                           "tokens/s": r["B"] * r["T"] / r["median"],
+                           "launch_us_mean": r["mean"] * 1e6,
+                           "launch_us_median": r["median"] * 1e6,
+                           "launch_us_min": r["min"] * 1e6, "GB/s": gbs,
                            "frac_hbm": gbs / HBM_PEAK_GBS,
                            "algorithmic_bytes_per_launch": r["bytes"],
+                           "bytes_with_fp32_o": r["bytes_as_run"],
+                           "mfma": {"achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                    "frac": tf / BF16_PEAK_TFLOPS,
+                                    "flops_per_launch": r["flops"],
+                                    "counters": measured_mfma("gdr2")},
                            "traffic": measured_traffic("gdr2")}
+            if "gdr2" in cpu:
+                out["gdr2"]["cpu_baseline"] = cpu["gdr2"]
     if "longctx" in res:
         r = res["longctx"]
         gbs = r["bytes"] / r["mean"] / 1e9
         out["long_context"] = {
             "workload": "B1 H16 T32768 d128 bf16, fp32 alpha/beta/o, initial state: "
                         f"gdr_chunk_fwd_split, {r['nseg']} segments of {r['T'] // r['nseg']}",
-            "tokens/s": r["B"] * r["T"] / r["mean"], "launch_us_mean": r["mean"] * 1e6,
+            "tokens/s": r["B"] * r["T"] / r["median"], "launch_us_mean": r["mean"] * 1e6,
+            "launch_us_median": r["median"] * 1e6,
             "launch_us_min": r["min"] * 1e6, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
             "mfma_frac": r["flops"] / r["mean"] / 1e12 / BF16_PEAK_TFLOPS,
-            "algorithmic_bytes_per_launch": r["bytes"],
+            "algorithmic_bytes_per_launch": r["bytes"], "bytes_with_fp32_o": r["bytes_as_run"],
             "plain_gdr_chunk_fwd": {"launch_us_mean": r["plain_mean"] * 1e6,
                                     "tokens/s": r["B"] * r["T"] / r["plain_mean"]}}
+        if "longctx" in cpu:
+            out["long_context"]["cpu_baseline"] = cpu["longctx"]
+    if "gate_fused" in res:
+        t = res["gate_fused"]["t"]
+        tok = res["gate_fused"]["tokens"]
+        out["gate_fused"] = {"workload": "B8 H16 T4096 d128 forward + output gate (bf16 gate, "
+                                         "fp32 weight, bf16 y); interleaved launches",
+                             **{f"{n}_us_median": v["median"] for n, v in t.items()},
+                             **{f"{n}_us_min": v["min"] for n, v in t.items()},
+                             "fused_tokens/s": tok / t["fused"]["median"] * 1e6,
+                             "two_calls_tokens/s": tok / t["two_calls"]["median"] * 1e6}
     if "l2norm" in res:
         out["l2norm"] = {"what": "launch us with raw q, k: fused GDR_L2NORM_QK, plain call "
                                  "(no normalisation), separate PyTorch normalise pass + plain call",
@@ -732,9 +1086,8 @@ def main():
         out["copy_reference"] = {"what": "torch device-to-device copy, 512 MiB read + 512 MiB "
                                          "written", "GB/s": cp["bytes"] / cp["mean"] / 1e9,
                                  "frac_hbm": cp["bytes"] / cp["mean"] / 1e9 / HBM_PEAK_GBS}
-    if not args.no_cpu and "gdn" in res:
-        log("timing the fp64 oracle on the host ...")
-        out["cpu_baseline"] = cpu_baseline(res["gdn"]["inp"])
+    if "gdn" in cpu:
+        out["cpu_baseline"] = cpu["gdn"]
     print(json.dumps(out), flush=True)
 
 

@@ -341,8 +341,9 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                 for (int t = 0; t < NS; ++t) sa[t] *= lam[t];
             }
             {
+                // p.o NULL: no o (an empty range drops every store)
                 const int64_t t0 = c * CH;
-                const int n = (int)min((int64_t)CH, T - t0);
+                const int n = p.o ? (int)min((int64_t)CH, T - t0) : 0;
                 const __amdgpu_buffer_rsrc_t ores = __builtin_amdgcn_make_buffer_rsrc(
                     obase + t0 * H * DV, (short)0, n * (int)(H * DV * sizeof(TOut)), 0x00020000);
 #pragma unroll

@@ -12,8 +12,9 @@ namespace {
 
 __global__ void state_copy_kernel(const float* __restrict__ s0, float* __restrict__ s,
                                   int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) s[i] = s0 ? s0[i] : 0.f;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        s[i] = s0 ? s0[i] : 0.f;
 }
 
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -42,16 +43,22 @@ bool elem_ok(const void* p, size_t bytes) {
     return p && (reinterpret_cast<uintptr_t>(p) % bytes) == 0;
 }
 
-// Largest element count of any tensor must fit the kernels' 64-bit offsets
-// and the grid must fit 2^31 - 1 workgroups.
+// Largest element count of any tensor must fit the kernels' 64-bit offsets.
 bool sizes_ok(int64_t a, int64_t b, int64_t c) {
     if (a < 0 || b < 0 || c < 0) return false;
     const double n = (double)a * (double)b * (double)c;
     return n < 4.0e18;
 }
 
-// An elementwise launch over n items, 256 per workgroup, fits the grid.
-bool grid_ok(int64_t n) { return (n + 255) / 256 <= 0x7fffffffLL; }
+// One work-item per element over n elements, 256 per workgroup, fits a
+// dispatch (the backward's reductions).
+bool grid_ok(int64_t n) { return n >= 0 && (n + 255) / 256 <= kMaxWorkItems / 256; }
+
+// The per-head launches (the chunk kernels of both rules and both
+// directions, the segment scans) run at most 2048 work-items per head
+// (d_v = 128: the rule-2 forward's 4 row blocks x 512, the scans' 8 x 256)
+// on a grid rounded up to 8 heads; BH heads must fit one dispatch.
+bool heads_grid_ok(int64_t BH) { return BH >= 0 && (BH + 7) / 8 * 8 <= kMaxWorkItems / 2048; }
 
 // The chunk kernels address one chunk of tokens (H heads x d channels each)
 // with 32-bit byte offsets from a 64-bit chunk base.
@@ -61,9 +68,8 @@ bool heads_ok(int64_t H) { return H <= GDR_MAX_HEADS; }
 
 hipError_t launch_state_copy(const float* s0, float* s_final, int64_t n, hipStream_t st) {
     if (n == 0) return hipSuccess;
-    const int64_t blocks = (n + 255) / 256;
-    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st, s0,
-                       s_final, n);
+    hipLaunchKernelGGL(state_copy_kernel, dim3(stride_blocks(n)), dim3(256), 0, st, s0, s_final,
+                       n);
     return hipGetLastError();
 }
 
@@ -78,7 +84,7 @@ static gdr_status_t chunk_common(int64_t B, int64_t T, int64_t H, int64_t Dk, in
     if (!heads_ok(H)) return GDR_ERR_INVALID;
     if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return GDR_ERR_UNSUPPORTED;
     if (!dims_ok(Dk, Dv)) return GDR_ERR_UNSUPPORTED;
-    if (B * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
+    if (!heads_grid_ok(B * H)) return GDR_ERR_INVALID;
     a.B = B;
     a.T = T;
     a.H = H;
@@ -178,7 +184,6 @@ extern "C" gdr_status_t gdr_chunk_fwd_gate(int64_t B, int64_t T, int64_t H, int6
     if (!empty) {
         if (!ptrs_ok({q, k, v, g, y}) || !elem_ok(alpha, 4) || !elem_ok(beta, 4))
             return GDR_ERR_INVALID;
-        if (!grid_ok(B * T * H * Dv)) return GDR_ERR_INVALID;
         const size_t need = gdr_chunk_fwd_gate_workspace_size(B, T, H, Dk, Dv, in_dt);
         if (!ptrs_ok({workspace}) || workspace_bytes < need) return GDR_ERR_INVALID;
     }
@@ -251,9 +256,11 @@ SplitLayout split_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv
 
 // Passes 1-3 of the sequence split, on the segment batch `a` (B nseg
 // segments of T / nseg tokens, inputs set): R (each segment from zero), P
-// (v = 0 from the identity) and the scan into the start states Sin.  The
-// passes' outputs go to `o` (overwritten by the caller's last pass) or to
-// the workspace's discard buffer when the layout has one.
+// (v = 0 from the identity) and the scan into the start states Sin.  Only
+// the passes' final states are wanted: the bf16 matrix-core kernels write
+// no o for them; the fp32 vector-ALU kernels write theirs to `o`
+// (overwritten by the caller's last pass) or to the workspace's discard
+// buffer when the layout has one.
 static gdr_status_t split_states(const ChunkArgs& a, const SplitLayout& l, char* w, int64_t B,
                                  int64_t nseg, const float* s0, void* o) {
     float* R = reinterpret_cast<float*>(w);
@@ -261,11 +268,12 @@ static gdr_status_t split_states(const ChunkArgs& a, const SplitLayout& l, char*
     float* Sin = reinterpret_cast<float*>(w + l.R + l.P);
     void* vz = w + l.R + l.P + l.Sin;
     void* oP = l.oP ? static_cast<void*>(w + l.R + l.P + l.Sin + l.vz) : o;
+    const bool no_o = a.in_bf16 && !(a.gated2 && a.precise);
     gdr_status_t st;
     // 1. each segment from a zero state: R
     ChunkArgs r = a;
     r.s0 = nullptr;
-    r.o = l.oP && !o ? oP : o;
+    r.o = no_o ? nullptr : l.oP && !o ? oP : o;
     r.out_bf16 = l.oP && !o ? true : a.out_bf16;
     r.s_final = R;
     if ((st = chunk_run(r)) != GDR_OK) return st;
@@ -279,7 +287,7 @@ static gdr_status_t split_states(const ChunkArgs& a, const SplitLayout& l, char*
     if (a.gated2) pa.write = vz;   // w (.) v = 0 either way; w needs Dk columns here
     pa.s0 = P;
     pa.s_final = P;
-    pa.o = oP;
+    pa.o = no_o ? nullptr : oP;
     pa.out_bf16 = l.oP ? true : a.out_bf16;
     if ((st = chunk_run(pa)) != GDR_OK) return st;
     // 3. segment start states
@@ -307,9 +315,7 @@ static gdr_status_t fwd_split_run(ChunkArgs& a, int64_t B, int64_t T, int64_t H,
                                   float* s_final, int64_t nseg, void* workspace,
                                   size_t workspace_bytes) {
     if (T % nseg != 0 || !sizes_ok(B * nseg, H, 1)) return GDR_ERR_INVALID;
-    if (!grid_ok(B * T * H * Dk) || !grid_ok(B * nseg * H * Dk * Dk) || !grid_ok(B * H * Dv * Dk))
-        return GDR_ERR_INVALID;
-    if (B * nseg * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
+    if (!heads_grid_ok(B * nseg * H)) return GDR_ERR_INVALID;
     if (!ptrs_ok({workspace}) || !opt_ok(s0) || !opt_ok(s_final)) return GDR_ERR_INVALID;
     const SplitLayout l = split_layout(B, T, H, Dk, Dv, in_dt, nseg);
     if (workspace_bytes < l.total) return GDR_ERR_INVALID;
@@ -455,9 +461,7 @@ static gdr_status_t bwd_split_check(int64_t B, int64_t T, int64_t H, int64_t Dk,
     if (st != GDR_OK) return st;
     if (!dtype_ok(dout_dt)) return GDR_ERR_UNSUPPORTED;
     if (T % nseg != 0 || !sizes_ok(B * nseg, H, 1)) return GDR_ERR_INVALID;
-    if (!grid_ok(B * T * H * Dk) || !grid_ok(B * nseg * H * Dk * Dk) || !grid_ok(B * H * Dv * Dk))
-        return GDR_ERR_INVALID;
-    if (B * nseg * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
+    if (!grid_ok(B * T * H * Dk) || !heads_grid_ok(B * nseg * H)) return GDR_ERR_INVALID;
     a.l2norm = (flags & GDR_L2NORM_QK) != 0;
     return GDR_OK;
 }
@@ -659,7 +663,8 @@ extern "C" gdr_status_t gdr_recurrent_step_ex(int64_t N, int64_t H, int64_t Dk, 
                                               hipStream_t stream) {
     if (!flags_ok(flags)) return GDR_ERR_UNSUPPORTED;
     if (N < 0 || H < 0 || Dk < 0 || Dv < 0) return GDR_ERR_INVALID;
-    if (!sizes_ok(N, H, 1) || N * H > 0x7fffffffLL) return GDR_ERR_INVALID;
+    // one 256-thread workgroup per (sequence, head)
+    if (!sizes_ok(N, H, 1) || N * H > kMaxWorkItems / 256) return GDR_ERR_INVALID;
     if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return GDR_ERR_UNSUPPORTED;
     if (!dims_ok(Dk, Dv)) return GDR_ERR_UNSUPPORTED;
     if (N == 0 || H == 0) return GDR_OK;
@@ -834,7 +839,7 @@ extern "C" gdr_status_t gdr_chunk_bwd_ex(int64_t B, int64_t T, int64_t H, int64_
     if (!heads_ok(H)) return GDR_ERR_INVALID;
     if (!dtype_ok(in_dt) || !dtype_ok(dout_dt)) return GDR_ERR_UNSUPPORTED;
     if (!dims_ok(Dk, Dv)) return GDR_ERR_UNSUPPORTED;
-    if (B * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
+    if (!heads_grid_ok(B * H)) return GDR_ERR_INVALID;
     if (!opt_ok(s0) || !opt_ok(ds_final) || !opt_ok(ds0)) return GDR_ERR_INVALID;
     if (B == 0 || H == 0) return GDR_OK;
     if (T == 0) {
@@ -910,7 +915,7 @@ extern "C" gdr_status_t gdr2_chunk_bwd_ex(int64_t B, int64_t T, int64_t H, int64
     if (!heads_ok(H)) return GDR_ERR_INVALID;
     if (!dtype_ok(in_dt) || !dtype_ok(dout_dt)) return GDR_ERR_UNSUPPORTED;
     if (!dims_ok(Dk, Dv)) return GDR_ERR_UNSUPPORTED;
-    if (B * H * (Dv / 32) > 0x7fffffffLL) return GDR_ERR_INVALID;
+    if (!heads_grid_ok(B * H)) return GDR_ERR_INVALID;
     if (!opt_ok(s0) || !opt_ok(ds_final) || !opt_ok(ds0)) return GDR_ERR_INVALID;
     if (B == 0 || H == 0) return GDR_OK;
     if (T == 0) {

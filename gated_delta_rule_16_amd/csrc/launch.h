@@ -31,7 +31,7 @@ struct ChunkArgs {
     const void *q, *k, *v;
     const void *alpha, *beta, *erase, *write;
     const float* s0;
-    void* o;
+    void* o;                // NULL: no o (bf16 matrix-core kernels only)
     float* s_final;
     hipStream_t stream;
     // output gate fused on the stores of the bf16 scalar-gate kernel
@@ -102,6 +102,17 @@ struct SplitScanArgs {
     float* Sin;
     hipStream_t stream;
 };
+
+// An HSA dispatch covers at most 2^32 - 1 work-items in each grid dimension
+// (workgroups x workgroup size); every launch here is one-dimensional.
+constexpr int64_t kMaxWorkItems = 0xffffffffLL;
+
+// Workgroups of a grid-stride elementwise launch over n items, 256 threads
+// each: enough to fill the chip, never past the work-item limit.
+inline unsigned stride_blocks(int64_t n) {
+    const int64_t b = (n + 255) / 256;
+    return (unsigned)(b < 16384 ? b : 16384);
+}
 
 hipError_t launch_step(const StepArgs& a);
 hipError_t launch_identity(float* x, int64_t n, int d, hipStream_t st);

@@ -22,16 +22,19 @@ constexpr int SROWS = 16;   // state rows per scan workgroup
 
 // x[n][i][j] = (i == j) for n matrices of d x d
 __global__ __launch_bounds__(256) void identity_kernel(float* __restrict__ x, int64_t n, int d) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n * d * d) return;
-    const int64_t e = i % ((int64_t)d * d);
-    x[i] = (e / d == e % d) ? 1.f : 0.f;
+    const int64_t dd = (int64_t)d * d;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n * dd;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e = i % dd;
+        x[i] = (e / d == e % d) ? 1.f : 0.f;
+    }
 }
 
 // n16 16-byte words of zeros
 __global__ __launch_bounds__(256) void zero_kernel(u32x4* __restrict__ x, int64_t n16) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n16) x[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+         i += (int64_t)gridDim.x * blockDim.x)
+        x[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
 // For each (b, h) and rows row0 .. row0 + 15: S = s0 (or 0); for p < nseg,
@@ -180,10 +183,11 @@ __global__ __launch_bounds__(256) void split_rscan_kernel(int64_t H, int nseg,
 __global__ __launch_bounds__(256) void seg_state_kernel(const float* __restrict__ F,
                                                         float* __restrict__ sf, int64_t B,
                                                         int nseg, int seg, int64_t per) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= B * per) return;
-    const int64_t b = i / per, e = i % per;
-    sf[i] = F[(b * nseg + seg) * per + e];
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < B * per;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t b = i / per, e = i % per;
+        sf[i] = F[(b * nseg + seg) * per + e];
+    }
 }
 
 template <int DK, int DV>
@@ -207,15 +211,14 @@ hipError_t scan_t(const SplitScanArgs& a) {
 hipError_t launch_identity(float* x, int64_t n, int d, hipStream_t st) {
     const int64_t total = n * d * d;
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL(identity_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, x,
-                       n, d);
+    hipLaunchKernelGGL(identity_kernel, dim3(stride_blocks(total)), dim3(256), 0, st, x, n, d);
     return hipGetLastError();
 }
 
 hipError_t launch_zero(void* x, int64_t bytes, hipStream_t st) {
     const int64_t n16 = bytes / 16;
     if (n16 == 0) return hipSuccess;
-    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(zero_kernel, dim3(stride_blocks(n16)), dim3(256), 0, st,
                        reinterpret_cast<u32x4*>(x), n16);
     return hipGetLastError();
 }
@@ -239,8 +242,8 @@ hipError_t launch_seg_state(const float* F, float* sf, int64_t B, int nseg, int 
                             int64_t per, hipStream_t st) {
     const int64_t total = B * per;
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL(seg_state_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                       F, sf, B, nseg, seg, per);
+    hipLaunchKernelGGL(seg_state_kernel, dim3(stride_blocks(total)), dim3(256), 0, st, F, sf, B,
+                       nseg, seg, per);
     return hipGetLastError();
 }
 

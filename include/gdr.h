@@ -42,7 +42,12 @@
  *     any error nothing is written.  Status codes:
  *       GDR_ERR_INVALID      a required pointer is NULL, a size is negative,
  *                            H exceeds GDR_MAX_HEADS in a chunkwise call
- *                            (forward, split or backward), or a pointer is
+ *                            (forward, split or backward), a launch would
+ *                            exceed the 2^32 - 1 work-items of one dispatch
+ *                            (more than 2^21 - 8 heads B H -- B nseg H in a
+ *                            split call -- in a chunkwise call, 2^24 - 1
+ *                            N H in a decode step, or 2^32 - 256 elements
+ *                            B T H Dk in a backward), or a pointer is
  *                            misaligned: q, k, v, the
  *                            channel gates, s0, s_final and the decode
  *                            state need 16-byte alignment; the scalar gates

@@ -445,3 +445,36 @@ def test_split_fp32_states_flag(gdr):
     assert call2(1, 2 | 4) == 2          # an unknown bit beside it
     assert call2(0, 2) == 0              # accepted (nothing to launch)
     assert call2(0, 2 | 1, n=1) == 0     # nseg = 1: ignored by the plain call
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="calls that pass validation launch kernels on the "
+                                          "fake addresses; host-only test")
+def test_dispatch_work_item_bound(gdr):
+    """One dispatch covers at most 2^32 - 1 work-items (workgroups x
+    workgroup size).  Past the bound a call is rejected on the host
+    (GDR_ERR_INVALID = 1) before anything is launched; at the bound it
+    passes validation and reaches the launch, which fails here for want of
+    a GPU (GDR_ERR_DEVICE = 3).  Bounds: 2^21 - 8 heads in a chunkwise call
+    (2048 work-items per head on a grid rounded up to 8 heads), 2^24 - 1
+    (sequence, head) pairs in a decode step (256 each), 2^32 - 256 elements
+    B T H Dk in a backward (one work-item per element)."""
+    heads = (1 << 21) - 8
+    assert chunk(gdr, B=heads, T=1) == 3
+    assert chunk(gdr, B=heads + 1, T=1) == 1
+    assert chunk2(gdr, B=heads, T=1) == 3
+    assert chunk2(gdr, B=heads + 1, T=1) == 1
+    assert split(gdr, B=heads // 4, T=4, nseg=4, wsb=1 << 60) == 3
+    assert split(gdr, B=heads // 4 + 1, T=4, nseg=4, wsb=1 << 60) == 1
+    assert step(gdr, N=(1 << 24) - 1) == 3
+    assert step(gdr, N=1 << 24) == 1
+    assert step(gdr, N=1 << 23, H=2) == 1
+    elems = (1 << 32) - 256                     # B T H Dk with Dk = 64
+    assert bwd(gdr, T=elems // 64, wsb=1 << 60) == 3
+    assert bwd(gdr, T=elems // 64 + 1, wsb=1 << 60) == 1
+    assert bwd2(gdr, T=elems // 64, wsb=1 << 60) == 3
+    assert bwd2(gdr, T=elems // 64 + 1, wsb=1 << 60) == 1
