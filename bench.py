@@ -74,7 +74,7 @@ def log(*a):
 
 
 CSRC = os.path.join(ROOT, "gated_delta_rule_16_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bench_kernel_counters.json")
 # kernel-name prefix in rocprofv3 output -> the bench leg it belongs to
 KERNELS = {"gdn": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, 64, float, false, "
                   "false>",
@@ -93,13 +93,43 @@ KERNELS = {"gdn": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, 
            "copy": "__amd_rocclr_copyBuffer"}
 
 
-def source_hash() -> str:
-    """Hash of every HIP source and header: counter readings are only valid
-    for the kernels they were taken on."""
+# the HIP source each profiled kernel is compiled from
+KERNEL_SOURCE = {"gdn": "chunk_mfma.hip", "gdn_bf16o": "chunk_mfma.hip", "gdn_gate": "chunk_gate.hip",
+                 "gdr2": "gdr2_mfma.hip", "decode": "step.hip", "gate": "epilogue.hip",
+                 "bwd": "chunk2_bwd.hip", "bwd2": "chunk2_bwd.hip"}
+
+
+def _code_text(path):
+    """A source file without its comments and blank space: edits to the
+    comments do not change a kernel."""
+    import re
+    t = open(path).read()
+    t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+    t = re.sub(r"//[^\n]*", " ", t)
+    return " ".join(t.split())
+
+
+def source_hash(leg=None) -> str:
+    """Hash of the code a kernel is built from (its source file and every
+    file it includes, transitively; all HIP sources when leg is None):
+    counter readings are only valid for the kernels they were taken on."""
+    import re
+    if leg is None:
+        files = sorted(f for f in glob.glob(os.path.join(CSRC, "*")) if f.endswith((".hip", ".h")))
+    else:
+        todo, files = [os.path.join(CSRC, KERNEL_SOURCE[leg])], []
+        while todo:
+            f = os.path.normpath(todo.pop())
+            if f in files or not os.path.exists(f):
+                continue
+            files.append(f)
+            for inc in re.findall(r'#include "([^"]+)"', open(f).read()):
+                todo.append(os.path.join(os.path.dirname(f), inc))
+        files.sort()
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        if f.endswith((".hip", ".h")):
-            h.update(open(f, "rb").read())
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        h.update(_code_text(f).encode())
     return h.hexdigest()[:16]
 
 
@@ -112,17 +142,33 @@ def _csv(d, suffix):
 
 def _counter_means(dirs):
     """Mean per dispatch of every counter in the --pmc runs under `dirs`,
-    per bench leg (kernel-name prefix in KERNELS)."""
-    per = {}
+    per bench leg (kernel-name prefix in KERNELS), with each leg's mean
+    dispatch duration in those runs (ns).  For the copy only the
+    dispatches of the largest grid count (the 512 MiB copy; the host-to-
+    device copies of the inputs use the same kernel)."""
+    per, dur = {}, {}
     for d in dirs:
-        vals = {}
-        for r in _csv(d, "counter_collection.csv"):
+        rows = _csv(d, "counter_collection.csv")
+        big = max((int(r["Grid_Size"]) for r in rows if r["Kernel_Name"].startswith(KERNELS["copy"])),
+                  default=0)
+        vals, spans = {}, {}
+        for r in rows:
             for leg, prefix in KERNELS.items():
-                if r["Kernel_Name"].startswith(prefix):
-                    vals.setdefault((leg, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+                if not r["Kernel_Name"].startswith(prefix):
+                    continue
+                if leg == "copy" and int(r["Grid_Size"]) != big:
+                    continue
+                vals.setdefault((leg, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+                spans.setdefault(leg, {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) -
+                                                               int(r["Start_Timestamp"]))
         for (leg, name), v in vals.items():
             per.setdefault(leg, {})[name] = sum(v) / len(v)
-    return per
+        for leg, sp in spans.items():
+            dur.setdefault(leg, {})[d] = sum(sp.values()) / len(sp)
+    return per, dur
+
+
+N_XCD = 8          # accelerator complex dies of an MI355X (GRBM_GUI_ACTIVE sums over them)
 
 
 def summarize(trace_dir, pmc_dirs, out_txt, command, timed=20):
@@ -130,20 +176,23 @@ def summarize(trace_dir, pmc_dirs, out_txt, command, timed=20):
     several --pmc runs of the same command -- into a short text summary and
     the JSON the benchmark reads its counter figures from.
 
-    HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, TCC-to-memory
-    requests weighted by size) are scaled by what the same counter reads for
-    the plain 512 MiB device copy, whose bytes are known.  The per-size
-    request counts (TCC_EA0_RDREQ_32B/64B/128B, WRREQ/WRREQ_64B) are summed
-    into bytes beside them, with the same scale.  MFMA: executed bf16 flops
-    = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16; matrix-core busy fraction =
-    SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CYCLES-normalised active cycles x
-    CUs x 4 SIMDs), see below.  Decode: TCC_EA0_RDREQ_DRAM / TCC_EA0_RDREQ,
-    the share of L2 read misses sent to the memory controllers."""
+    HBM bytes: the TCC-to-memory requests summed by size,
+    32 TCC_EA0_RDREQ_32B + 64 TCC_EA0_RDREQ_64B + 128 TCC_EA0_RDREQ_128B for
+    reads and 64 TCC_EA0_WRREQ_64B + 32 (TCC_EA0_WRREQ - WRREQ_64B) for
+    writes; the plain 512 MiB copy checks them (its known bytes over the
+    reading).  FETCH_SIZE / WRITE_SIZE beside them, scaled by the copy.
+    Matrix cores: executed bf16 flops = 512 SQ_INSTS_VALU_MFMA_MOPS_BF16;
+    busy fraction = SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) /
+    (GRBM_GUI_ACTIVE / 8 XCDs x 256 CUs x 4 SIMDs).  Decode:
+    TCC_EA0_RDREQ_DRAM / TCC_EA0_RDREQ, the share of L2 read misses sent to
+    the memory controllers."""
     stats = _csv(trace_dir, "kernel_stats.csv")
     trace = _csv(trace_dir, "kernel_trace.csv")
-    per = _counter_means(pmc_dirs)
-    lines = [f"# rocprofv3 summary (HIP sources hash {source_hash()})", "",
-             "Commands:"] + [f"  {c}" for c in command.split(" ;; ")] + [
+    per, _ = _counter_means(pmc_dirs)
+    lines = ["# rocprofv3 summary", "", "Kernel source hashes (code without comments; the bench uses a "
+             "leg's counters only while its hash matches):",
+             "  " + ", ".join(f"{leg} {source_hash(leg)}" for leg in KERNEL_SOURCE), "",
+             "Commands:"] + [f"  {c.strip()}" for c in command.split(" ;; ")] + [
              "", "Kernel trace (--kernel-trace --stats):",
              f"  {'kernel':60s} {'calls':>6s} {'avg us':>10s} {'min us':>10s} {'max us':>10s}"]
     for r in stats:
@@ -166,93 +215,86 @@ def summarize(trace_dir, pmc_dirs, out_txt, command, timed=20):
         dur_us[leg] = sum(dur) / len(dur)
         lines.append(f"  {leg:9s} {prefix.split('::')[-1][:50]:50s} {len(dur):4d} "
                      f"{dur_us[leg]:10.1f} {min(dur):10.1f}")
-    traffic, scale = {}, {}
+    copy_bytes = 512 << 20          # the copy reads and writes 512 MiB each
+    ea, traffic = {}, {}
+    for leg, c in per.items():
+        if all(k in c for k in ("TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
+                                "TCC_EA0_RDREQ_128B_sum")):
+            ea.setdefault(leg, {})["read"] = (32 * c["TCC_EA0_RDREQ_32B_sum"] + 64 *
+                                              c["TCC_EA0_RDREQ_64B_sum"] + 128 *
+                                              c["TCC_EA0_RDREQ_128B_sum"])
+        if all(k in c for k in ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum")):
+            ea.setdefault(leg, {})["write"] = (64 * c["TCC_EA0_WRREQ_64B_sum"] + 32 *
+                                               (c["TCC_EA0_WRREQ_sum"] -
+                                                c["TCC_EA0_WRREQ_64B_sum"]))
+    for leg, e in ea.items():
+        if "read" in e and "write" in e and leg != "copy":
+            traffic[leg] = {"read_bytes": e["read"], "write_bytes": e["write"],
+                            "bytes": e["read"] + e["write"]}
+    check = {k: ea.get("copy", {}).get(k, 0) / copy_bytes for k in ("read", "write")}
+    lines += ["", "HBM bytes per dispatch, from the request counts by size (the 512 MiB copy "
+                  "reads as {:.4f} x and {:.4f} x its known read and write bytes):".format(
+                      check["read"], check["write"])]
+    for leg, e in ea.items():
+        lines.append(f"  {leg:9s} read {e.get('read', 0) / 1e6:9.1f} MB   write "
+                     f"{e.get('write', 0) / 1e6:9.1f} MB")
+    scale = {}
     copy = per.get("copy", {})
     for name in ("FETCH_SIZE", "WRITE_SIZE"):
         if copy.get(name):
-            scale[name] = 512 * 1024 / copy[name]   # the copy reads and writes 512 MiB each
-    ea = {}
-    for leg, c in per.items():
-        if "FETCH_SIZE" in c and "WRITE_SIZE" in c and scale:
-            rd = c["FETCH_SIZE"] * scale["FETCH_SIZE"] * 1024
-            wr = c["WRITE_SIZE"] * scale["WRITE_SIZE"] * 1024
-            traffic[leg] = {"read_bytes": rd, "write_bytes": wr, "bytes": rd + wr}
-        if all(k in c for k in ("TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
-                                "TCC_EA0_RDREQ_128B_sum")):
-            ea.setdefault(leg, {})["read_raw"] = (32 * c["TCC_EA0_RDREQ_32B_sum"] + 64 *
-                                                  c["TCC_EA0_RDREQ_64B_sum"] + 128 *
-                                                  c["TCC_EA0_RDREQ_128B_sum"])
-        if all(k in c for k in ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum")):
-            ea.setdefault(leg, {})["write_raw"] = (64 * c["TCC_EA0_WRREQ_64B_sum"] + 32 *
-                                                   (c["TCC_EA0_WRREQ_sum"] -
-                                                    c["TCC_EA0_WRREQ_64B_sum"]))
-    ea_scale = {}
-    if "copy" in ea:
-        if ea["copy"].get("read_raw"):
-            ea_scale["read"] = (512 << 20) / ea["copy"]["read_raw"]
-        if ea["copy"].get("write_raw"):
-            ea_scale["write"] = (512 << 20) / ea["copy"]["write_raw"]
-    lines += ["", "HBM bytes per dispatch.  FETCH_SIZE / WRITE_SIZE as read (KiB), scaled by "
-                  "the 512 MiB copy's reading:"]
+            scale[name] = copy_bytes / 1024 / copy[name]
     if scale:
-        lines.append(f"  scale FETCH {scale['FETCH_SIZE']:.4f}, WRITE {scale['WRITE_SIZE']:.4f}")
-    for leg, c in per.items():
-        if "FETCH_SIZE" not in c:
-            continue
-        t = traffic.get(leg)
-        extra = "" if t is None else (f" -> read {t['read_bytes'] / 1e6:8.1f} MB, write "
-                                      f"{t['write_bytes'] / 1e6:8.1f} MB")
-        lines.append(f"  {leg:9s} FETCH {c['FETCH_SIZE']:12.1f}  WRITE {c.get('WRITE_SIZE', 0):12.1f}"
-                     f"{extra}")
-    if ea:
-        lines += ["", "Request-size sums: read 32 n32 + 64 n64 + 128 n128 (TCC_EA0_RDREQ_*B_sum), "
-                      "write 64 n64 + 32 (n - n64) (TCC_EA0_WRREQ*_sum), raw and copy-scaled:"]
-        if ea_scale:
-            lines.append("  scale read {:.4f}, write {:.4f}".format(ea_scale.get("read", 0),
-                                                                      ea_scale.get("write", 0)))
-        for leg, e in ea.items():
-            r, w = e.get("read_raw"), e.get("write_raw")
-            rs = "" if r is None else (f"read raw {r / 1e6:8.1f} MB -> "
-                                       f"{r * ea_scale.get('read', 0) / 1e6:8.1f} MB")
-            ws = "" if w is None else (f"  write raw {w / 1e6:8.1f} MB -> "
-                                       f"{w * ea_scale.get('write', 0) / 1e6:8.1f} MB")
-            lines.append(f"  {leg:9s} {rs}{ws}")
+        lines += ["", "FETCH_SIZE / WRITE_SIZE (KiB per dispatch as read), and scaled by the copy's "
+                      f"reading (FETCH x {scale.get('FETCH_SIZE', 0):.4f}, WRITE x "
+                      f"{scale.get('WRITE_SIZE', 0):.4f}):"]
+        for leg, c in per.items():
+            if "FETCH_SIZE" in c and "WRITE_SIZE" in c:
+                lines.append(f"  {leg:9s} FETCH {c['FETCH_SIZE']:12.1f} -> "
+                             f"{c['FETCH_SIZE'] * 1024 * scale['FETCH_SIZE'] / 1e6:9.1f} MB   WRITE "
+                             f"{c['WRITE_SIZE']:12.1f} -> "
+                             f"{c['WRITE_SIZE'] * 1024 * scale['WRITE_SIZE'] / 1e6:9.1f} MB")
     mfma = {}
     for leg, c in per.items():
-        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" not in c:
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in c or not c.get("GRBM_GUI_ACTIVE"):
             continue
-        m = {"exec_bf16_flops": 512 * c["SQ_INSTS_VALU_MFMA_MOPS_BF16"]}
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "GRBM_GUI_ACTIVE" in c and c["GRBM_GUI_ACTIVE"]:
-            m["busy_frac"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * 256 * 4)
-        if leg in dur_us:
-            m["exec_tflops"] = m["exec_bf16_flops"] / dur_us[leg] / 1e6
-            m["exec_frac"] = m["exec_tflops"] / BF16_PEAK_TFLOPS
+        cyc = c["GRBM_GUI_ACTIVE"] / N_XCD
+        m = {"busy_frac": c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 256 * 4)}
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+            m["exec_bf16_flops"] = 512 * c["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+            if leg in dur_us:
+                m["exec_tflops"] = m["exec_bf16_flops"] / dur_us[leg] / 1e6
+                m["exec_frac"] = m["exec_tflops"] / BF16_PEAK_TFLOPS
         m["raw"] = {k: v for k, v in c.items() if k.startswith(("SQ_", "GRBM_"))}
         mfma[leg] = m
     if mfma:
         lines += ["", "Matrix cores per dispatch: executed bf16 flops = 512 x "
-                      "SQ_INSTS_VALU_MFMA_MOPS_BF16; busy = SQ_VALU_MFMA_BUSY_CYCLES / "
-                      "(GRBM_GUI_ACTIVE x 256 CU x 4 SIMD); raw counters beside:"]
+                      "SQ_INSTS_VALU_MFMA_MOPS_BF16 (its rate over the timed launches above); "
+                      "busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 256 CU x 4 SIMD), "
+                      "the fraction of SIMD cycles the matrix cores were busy:"]
         for leg, m in mfma.items():
             raw = "  ".join(f"{k} {v:.4g}" for k, v in m["raw"].items())
-            lines.append(f"  {leg:9s} exec {m['exec_bf16_flops'] / 1e9:8.2f} GFLOP"
-                         + (f" = {m['exec_tflops']:7.1f} TFLOP/s over the timed launch "
-                            f"({m['exec_frac']:.3f} of peak)" if "exec_tflops" in m else "")
-                         + (f", busy {m['busy_frac']:.3f}" if "busy_frac" in m else ""))
+            lines.append(f"  {leg:9s}"
+                         + (f" exec {m['exec_bf16_flops'] / 1e9:8.2f} GFLOP" if "exec_bf16_flops" in m
+                            else "")
+                         + (f" = {m['exec_tflops']:7.1f} TFLOP/s ({m['exec_frac']:.3f} of the "
+                            f"2.4 GHz peak)" if "exec_tflops" in m else "")
+                         + f", busy {m['busy_frac']:.3f}")
             lines.append(f"            {raw}")
     dram = {}
     for leg, c in per.items():
         if c.get("TCC_EA0_RDREQ_sum") and "TCC_EA0_RDREQ_DRAM_sum" in c:
             dram[leg] = c["TCC_EA0_RDREQ_DRAM_sum"] / c["TCC_EA0_RDREQ_sum"]
     if dram:
-        lines += ["", "Read requests sent to the memory controllers "
-                      "(TCC_EA0_RDREQ_DRAM_sum / TCC_EA0_RDREQ_sum):"]
+        lines += ["", "L2 read misses sent to the memory controllers (TCC_EA0_RDREQ_DRAM_sum / "
+                      "TCC_EA0_RDREQ_sum; the memory-side cache sits behind them, so its hits "
+                      "are inside this share):"]
         for leg, f in dram.items():
             lines.append(f"  {leg:9s} {f:.4f}")
     open(out_txt, "w").write("\n".join(lines) + "\n")
-    json.dump({"source_hash": source_hash(), "scale": scale, "traffic": traffic, "ea": ea,
-               "ea_scale": ea_scale, "mfma": {k: {kk: vv for kk, vv in v.items() if kk != "raw"}
-                                              for k, v in mfma.items()},
+    json.dump({"source_hash": {leg: source_hash(leg) for leg in KERNEL_SOURCE},
+               "copy_check": check, "fetch_write_scale": scale, "traffic": traffic,
+               "mfma": {k: {kk: vv for kk, vv in v.items() if kk != "raw"}
+                        for k, v in mfma.items()},
                "dram_read_share": dram, "command": command},
               open(TRAFFIC_FILE, "w"), indent=1)
     print("\n".join(lines))
@@ -263,7 +305,8 @@ def _measured(key, leg):
         d = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if d.get("source_hash") != source_hash():
+    hashes = d.get("source_hash")
+    if not isinstance(hashes, dict) or hashes.get(leg) != source_hash(leg):
         return None
     return d.get(key, {}).get(leg)
 
