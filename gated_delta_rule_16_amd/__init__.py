@@ -636,9 +636,8 @@ def gdr2_chunk_bwd_split(q, k, v, alpha, erase, write, s0, dout, ds_final=None, 
                          stream=None):
     """gdr2_chunk_bwd with each sequence split into ``nseg`` segments that
     run side by side.  Same arguments and results as gdr2_chunk_bwd.
-    ``fp32_states`` (GDR_SPLIT_FP32_STATES) builds the segments' start
-    states with the fp32 forward when the inputs are bf16: slower, and the
-    gradients through the state keep fp32 accuracy."""
+    ``fp32_states`` (GDR_SPLIT_FP32_STATES) runs the plain backward over
+    the whole sequence instead (fp32 states throughout, no split)."""
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     if q.dtype not in _DT or dout.dtype not in _DT:

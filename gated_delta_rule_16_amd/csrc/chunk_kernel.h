@@ -126,13 +126,14 @@ struct Lay {
     static constexpr int AF = GR + 3 * GRS;         // A fp32 [32][P36], two copies
     static constexpr int TF = AF + 2 * CH * P36 * 4;   // B1 private: T fp32 [32][P36]
     // output gate: team A's per-token partial sums of squares of o, three
-    // chunks [3][RB / 16][32], each wave's 1 / rms of its tokens
-    // [RB / 16][32], and the gate values of three chunks, fp32 and
-    // row-major [RB][P36] (rows are value channels, columns tokens)
+    // chunks [3][RB / 16][32], and the gate values of three chunks as
+    // loaded, token-major [32][GP] in the gate's dtype (GP = RB + 8
+    // elements: rows 16 or 32 bytes apart in banks)
+    static constexpr int GP = RB + 8;
     static constexpr int PSQ = TF + CH * P36 * 4;
-    static constexpr int RR = PSQ + (GATE ? 3 * (RB / 16) * CH * 4 : 0);
-    static constexpr int GGR = RR + (GATE ? (RB / 16) * CH * 4 : 0);
-    static constexpr int TOTAL = GGR + (GATE ? 3 * RB * P36 * 4 : 0);
+    static constexpr int GGR = PSQ + (GATE ? 3 * (RB / 16) * CH * 4 : 0);
+    static constexpr int GGS = CH * GP * 4;            // one chunk, fp32 gate
+    static constexpr int TOTAL = GGR + (GATE ? 3 * GGS : 0);
     static_assert(SET % 16 == 0 && (CH * PV * 2) % 16 == 0, "alignment");
 };
 
@@ -274,7 +275,6 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
         const int tok = 16 * (jt >> 2) + 4 * g + (jt & 3);
         const float wr = GATE && p.w ? p.w[row0 + i] : 1.f;
         float* psq = reinterpret_cast<float*>(smem + L::PSQ);   // [3][NA][CH]
-        float* rrb = reinterpret_cast<float*>(smem + L::RR) + a * CH;
         // squares of o summed over the wave's 16 rows (a reduce-scatter over
         // the DPP row: partners lane ^ 15, ^ 7, ^ 3, ^ 1, keeping half each
         // time), written to LDS by the owners of each token
@@ -308,12 +308,28 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
             }
             return s;
         };
-        // o w SiLU(gate) for chunk cn, the gate staged by B0; SiLU(x) = x / (1 + e^-x)
+        // o w SiLU(gate) for chunk cn, the gate staged by B0 token-major;
+        // SiLU(x) = x / (1 + e^-x).  The lane's gate values (tokens 16 rt +
+        // 4 g + r, channel i): bf16 by two transposed reads, fp32 one by one.
         auto gate_apply = [&](const f32x4 (&ov)[2], int64_t cn, f32x4 (&og)[2]) {
-            const float* gg = reinterpret_cast<const float*>(smem + L::GGR) +
-                              (int)(cn % 3) * RB * P36 + i * P36;
-            const f32x4 gv[2] = {*reinterpret_cast<const f32x4*>(gg + 4 * g),
-                                 *reinterpret_cast<const f32x4*>(gg + 16 + 4 * g)};
+            const unsigned char* gs = smem + L::GGR + (int)(cn % 3) * L::GGS;
+            f32x4 gv[2];
+            if (p.gate_bf16) {
+                const bf16_t* gb = reinterpret_cast<const bf16_t*>(gs);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    const s16x4 x = lds_tr16(gb + (16 * rt + 4 * g + (m >> 2)) * L::GP + 16 * a +
+                                             4 * (m & 3));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) gv[rt][r] = bf2f((bf16_t)x[r]);
+                }
+            } else {
+                const float* gf = reinterpret_cast<const float*>(gs);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) gv[rt][r] = gf[(16 * rt + 4 * g + r) * L::GP + i];
+            }
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -336,8 +352,9 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
         };
         // y of chunk cn: the other row blocks' sums (a word not yet tagged
         // with the chunk is read again, with a bounded spin; a sum that never
-        // arrives leaves NaN), 1 / rms per token handed across the wave
-        // through LDS, then the stores
+        // arrives leaves NaN), then 1 / rms of the lane's tokens from their
+        // owners in its 16-lane row (token 16 rt + 4 g + r is owned by lane
+        // 8 rt + 2 r of the row: a row broadcast), then the stores
         auto gate_out = [&](int64_t cn, const f32x4 (&og)[2], float wsum,
                             unsigned long long (&pw)[NP]) {
             float tot = wsum;
@@ -352,10 +369,11 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                 tot += (uint32_t)(x >> 32) == (uint32_t)(cn + 1) ? __uint_as_float((uint32_t)x)
                                                                  : __builtin_nanf("");
             }
-            if (!(m & 1)) rrb[tok] = rsqrtf(tot * (1.f / DV) + p.eps);
-            wave_lds_sync();
-            const f32x4 rv[2] = {*reinterpret_cast<const f32x4*>(rrb + 4 * g),
-                                 *reinterpret_cast<const f32x4*>(rrb + 16 + 4 * g)};
+            const float rr = rsqrtf(tot * (1.f / DV) + p.eps);
+            const f32x4 rv[2] = {f32x4{dpp_mov<0x150>(rr), dpp_mov<0x152>(rr), dpp_mov<0x154>(rr),
+                                       dpp_mov<0x156>(rr)},
+                                 f32x4{dpp_mov<0x158>(rr), dpp_mov<0x15A>(rr), dpp_mov<0x15C>(rr),
+                                       dpp_mov<0x15E>(rr)}};
             const int n = (int)min((int64_t)CH, T - cn * CH);
             const __amdgpu_buffer_rsrc_t ores = __builtin_amdgcn_make_buffer_rsrc(
                 obase + cn * CH * H * DV, (short)0, n * (int)(H * DV * sizeof(TOut)), 0x00020000);
@@ -716,55 +734,46 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
         };
         if constexpr (GATE) {
             // and the output gate's values of the chunk, for team A one period
-            // later: RB rows x 32 tokens, fp32 in LDS.  Lane pieces of 16 bytes
-            // along a token's rows; VPC per token, GPL per lane.
-            constexpr int VPC4 = RB * 4 / 16, GPL = CH * VPC4 / 64;   // fp32 gate
-            constexpr int VPC2 = RB * 2 / 16;                          // bf16 gate
-            struct GBuf {
-                u32x4 v[GPL];
-            };
-            const char* gbase = reinterpret_cast<const char*>(p.gate);
-            const int es = p.gate_bf16 ? 2 : 4;
-            const int vpc = p.gate_bf16 ? VPC2 : VPC4;
-            auto load = [&](int64_t cn, GBuf& f) {
-                const int last = last_row(cn);
-                const char* cb = gbase + ((b * T * H + h) * DV + row0 + cn * CH * H * DV) * es;
+            // later: 32 tokens x RB channels, copied token-major into LDS in
+            // 16-byte pieces (VPC per token, GPL per lane)
+            auto stage = [&](auto esz) {
+                constexpr int ES = decltype(esz)::value;   // gate element bytes
+                constexpr int VPC = RB * ES / 16, NPC = CH * VPC, GPL = (NPC + 63) / 64;
+                struct GBuf {
+                    u32x4 v[GPL];
+                };
+                const char* gbase = reinterpret_cast<const char*>(p.gate);
+                auto load = [&](int64_t cn, GBuf& f) {
+                    const int last = last_row(cn);
+                    const char* cb = gbase + ((b * T * H + h) * DV + row0 + cn * CH * H * DV) * ES;
 #pragma unroll
-                for (int u = 0; u < GPL; ++u) {
-                    const int pc = lane + 64 * u;
-                    if (pc < CH * vpc) {
-                        const uint32_t off =
-                            (uint32_t)(min(pc / vpc, last) * (int)(H * DV) * es + 16 * (pc % vpc));
-                        f.v[u] = *reinterpret_cast<const u32x4*>(cb + off);
-                    }
-                }
-            };
-            auto prepare_g = [&](int64_t cn, const GBuf& f) {
-                prepare(cn);
-                float* gg = reinterpret_cast<float*>(smem + L::GGR) + (int)(cn % 3) * RB * P36;
-#pragma unroll
-                for (int u = 0; u < GPL; ++u) {
-                    const int pc = lane + 64 * u;
-                    if (pc < CH * vpc) {
-                        const int t = pc / vpc;
-                        if (p.gate_bf16) {
-                            const int r0 = 8 * (pc % vpc);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                gg[(r0 + 2 * e) * P36 + t] = __uint_as_float(f.v[u][e] << 16);
-                                gg[(r0 + 2 * e + 1) * P36 + t] =
-                                    __uint_as_float(f.v[u][e] & 0xffff0000u);
-                            }
-                        } else {
-                            const int r0 = 4 * (pc % vpc);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) gg[(r0 + e) * P36 + t] = __uint_as_float(f.v[u][e]);
+                    for (int u = 0; u < GPL; ++u) {
+                        const int pc = lane + 64 * u;
+                        if (NPC % 64 == 0 || pc < NPC) {
+                            const uint32_t off = (uint32_t)(min(pc / VPC, last) * (int)(H * DV) * ES +
+                                                            16 * (pc % VPC));
+                            f.v[u] = *reinterpret_cast<const u32x4*>(cb + off);
                         }
                     }
-                }
+                };
+                auto prepare_g = [&](int64_t cn, const GBuf& f) {
+                    prepare(cn);
+                    unsigned char* gs = smem + L::GGR + (int)(cn % 3) * L::GGS;
+#pragma unroll
+                    for (int u = 0; u < GPL; ++u) {
+                        const int pc = lane + 64 * u;
+                        if (NPC % 64 == 0 || pc < NPC)
+                            *reinterpret_cast<u32x4*>(gs + ((pc / VPC) * L::GP * ES + 16 * (pc % VPC))) =
+                                f.v[u];
+                    }
+                };
+                GBuf fa, fb, fc;
+                run(1, load, prepare_g, fa, fb, fc);
             };
-            GBuf fa, fb, fc;
-            run(1, load, prepare_g, fa, fb, fc);
+            if (p.gate_bf16)
+                stage(std::integral_constant<int, 2>{});
+            else
+                stage(std::integral_constant<int, 4>{});
         } else {
             run_noload(1, prepare);
         }

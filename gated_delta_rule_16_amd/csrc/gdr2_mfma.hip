@@ -72,7 +72,11 @@
 // substitution does not amplify; a simulation of this chunk algorithm
 // against the fp64 recurrence (1024 tokens; decays from fast to near 1,
 // with and without an initial state) puts the error at <= 2.3e-3 (o) and
-// <= 1.8e-3 (S) of rms, against 2e-4 with every operand split.
+// <= 1.8e-3 (S) of rms, against 2e-4 with every operand split.  The
+// FULL form splits those three too (E's lo half beside E S^T and A, K''s
+// lo half in A, T's lo half in T R: four more products a chunk in team A,
+// two in AP-A); the sequence-split backward takes its segment start states
+// from it, since its gradients inherit the states' error.
 #include <type_traits>
 
 #include "launch.h"
@@ -99,7 +103,7 @@ struct Gdr2Params {
     float* s_final;
 };
 
-template <int DK, bool NORM>
+template <int DK, bool NORM, bool FULL = false>
 struct Lay2 {
     static constexpr int PKN = DK + 16;            // K' row pitch (elements)
     // elementwise operands, chunk mod 4
@@ -110,13 +114,15 @@ struct Lay2 {
     static constexpr int KL = KH + CH * PKN * 2;
     static constexpr int LC = KL + CH * PKN * 2;    // lambda_C [DK] fp32, then the wide flag
     static constexpr int NR = LC + DK * 4 + 16;     // NORM: rho^2, pi, rho [16] fp32 each
-    static constexpr int ESET = NR + (NORM ? 3 * CH * 4 : 0);
+    static constexpr int EL = NR + (NORM ? 3 * CH * 4 : 0);   // FULL: E lo [16][DK]
+    static constexpr int ESET = EL + (FULL ? CH * DK * 2 : 0);
     // T, P, w . v, chunk mod 2
     static constexpr int TH = 0;                    // T [16][P24] bf16
     static constexpr int PH = TH + CH * P24 * 2;    // P hi, lo [16][P24]
     static constexpr int PL = PH + CH * P24 * 2;
     static constexpr int WV = PL + CH * P24 * 2;    // w . v [RB][P24] fp32, by state row
-    static constexpr int TSET = WV + RB * P24 * 4;
+    static constexpr int TL = WV + RB * P24 * 4;    // FULL: T lo [16][P24]
+    static constexpr int TSET = TL + (FULL ? CH * P24 * 2 : 0);
     static constexpr int ER = 0;
     static constexpr int TR = ER + 4 * ESET;
     static constexpr int AF = TR + 2 * TSET;        // A fp32 [16][PAF], chunk mod 2
@@ -180,9 +186,9 @@ __device__ __forceinline__ int ps_at(int t, int l) {
     return t * 128 + 4 * ((l >> 1) ^ (4 * (t & 3))) + 2 * (l & 1);
 }
 
-template <int DK, int DV, typename TOut, bool NORM>
+template <int DK, int DV, typename TOut, bool NORM, bool FULL = false>
 __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
-    using L = Lay2<DK, NORM>;
+    using L = Lay2<DK, NORM, FULL>;
     constexpr int KJ = DK / 32;   // 32-deep contraction steps over the key dim
     constexpr int NS = DK / 16;   // S^T tiles per team A wave
     constexpr int NRB = DV / RB;
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
         TOut* obase = reinterpret_cast<TOut*>(p.o) + (b * T * H + h) * DV;
         // E and Q fragments of the next chunk are read during this one (its
         // elementwise set is complete two periods ahead)
-        bf16x8 eh[KJ], qh[KJ], ql[KJ];
+        bf16x8 eh[KJ], qh[KJ], ql[KJ], el[FULL ? KJ : 1];
         auto read_eq = [&](int64_t c) {
             unsigned char* es = eset(c);
 #pragma unroll
@@ -251,6 +257,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                 eh[j] = *reinterpret_cast<const bf16x8*>(bfp(es, L::EH) + at);
                 qh[j] = *reinterpret_cast<const bf16x8*>(bfp(es, L::QH) + at);
                 ql[j] = *reinterpret_cast<const bf16x8*>(bfp(es, L::QL) + at);
+                if constexpr (FULL) el[j] = *reinterpret_cast<const bf16x8*>(bfp(es, L::EL) + at);
             }
         };
         read_eq(0);
@@ -267,6 +274,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
             const f32x4 wv = *reinterpret_cast<const f32x4*>(
                 reinterpret_cast<const float*>(ts + L::WV) + i * P24 + 4 * g);
             const s16x4 th = *reinterpret_cast<const s16x4*>(bfp(ts, L::TH) + m * P24 + 4 * g);
+            s16x4 tl = {0, 0, 0, 0};
+            if constexpr (FULL) tl = *reinterpret_cast<const s16x4*>(bfp(ts, L::TL) + m * P24 + 4 * g);
             const s16x4 ph = *reinterpret_cast<const s16x4*>(bfp(ts, L::PH) + m * P24 + 4 * g);
             const s16x4 pl = *reinterpret_cast<const s16x4*>(bfp(ts, L::PL) + m * P24 + 4 * g);
             // K'^T[16 t + m][4 g + e] by transposed reads; lambda_C
@@ -283,7 +292,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
             __builtin_amdgcn_sched_barrier(0);
 
             // ---- S as hi/lo B operands, slab by slab beside E S^T, Q S^T -----
-            f32x4 k2[2] = {}, q3[3] = {};
+            f32x4 k2[3] = {}, q3[3] = {};
 #pragma unroll
             for (int j = 0; j < KJ; ++j) {
                 bf16x8 sh, sl;
@@ -293,6 +302,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                        sh, sl);
                 k2[0] = mfma16(eh[j], sh, k2[0]);
                 k2[1] = mfma16(eh[j], sl, k2[1]);
+                if constexpr (FULL) k2[2] = mfma16(el[j], sh, k2[2]);
                 q3[0] = mfma16(qh[j], sh, q3[0]);
                 q3[1] = mfma16(qh[j], sl, q3[1]);
                 q3[2] = mfma16(ql[j], sh, q3[2]);
@@ -300,19 +310,21 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
 #pragma unroll
             for (int j = 0; j < KJ; ++j) {
                 __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);   // this slab's split
-                __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);    // its five products
+                __builtin_amdgcn_sched_group_barrier(0x008, FULL ? 6 : 5, 0);   // its products
             }
             __builtin_amdgcn_sched_barrier(0);
 
             // ---- R = w.v - E S^T;  V_new = [T | T] [R_hi; R_lo] ---------------
             //      (NORM: R~ = rho w.v - rho^2 E S^T, w.v already scaled)
             s16x4 rh, rl;
+            const f32x4 es2 = FULL ? k2[0] + k2[1] + k2[2] : k2[0] + k2[1];
             if constexpr (NORM)
-                split4(wv - *reinterpret_cast<const f32x4*>(nrc + NR_RHO2 + 4 * g) * (k2[0] + k2[1]),
-                       rh, rl);
+                split4(wv - *reinterpret_cast<const f32x4*>(nrc + NR_RHO2 + 4 * g) * es2, rh, rl);
             else
-                split4(wv - (k2[0] + k2[1]), rh, rl);
-            const f32x4 vn = mfma16(cat44(th, th), cat44(rh, rl), f32x4{0.f, 0.f, 0.f, 0.f});
+                split4(wv - es2, rh, rl);
+            f32x4 vn = mfma16(cat44(th, th), cat44(rh, rl), f32x4{0.f, 0.f, 0.f, 0.f});
+            if constexpr (FULL)
+                vn = mfma16(cat44(tl, s16x4{0, 0, 0, 0}), cat44(rh, s16x4{0, 0, 0, 0}), vn);
             s16x4 nh, nl;
             split4(vn, nh, nl);
             const bf16x8 nn = cat44(nh, nh);
@@ -524,6 +536,13 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                         const int at = m * L::PKN + 32 * j + 4 * g;
                         const bf16x8 kh = ld2x4(bfp(es, L::KH) + at, bfp(es, L::KH) + at + 16);
                         acc = mfma16(kh, xh, acc);
+                        if constexpr (FULL) {
+                            const bf16x8 xl = *reinterpret_cast<const bf16x8*>(
+                                bfp(es, L::EL) + kq_at<DK>(m, 32 * j + 8 * g));
+                            const bf16x8 kl = ld2x4(bfp(es, L::KL) + at, bfp(es, L::KL) + at + 16);
+                            acc = mfma16(kl, xh, acc);
+                            acc = mfma16(kh, xl, acc);
+                        }
                     }
                     f32x4 av;
 #pragma unroll
@@ -566,10 +585,22 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                 for (int e = 0; e < 8; ++e)
                     xs[e] = __uint_as_float((__float_as_uint(x[8 + e]) & msk) |
                                             (__float_as_uint(x[e]) & ~msk));
-                const u32x4 xh = u32x4{cvt_pk(xs[0], xs[1]), cvt_pk(xs[2], xs[3]),
-                                       cvt_pk(xs[4], xs[5]), cvt_pk(xs[6], xs[7])};
-                if (lane < 32)
-                    *reinterpret_cast<u32x4*>(bfp(tset(x1), L::TH) + rr * P24 + 8 * half) = xh;
+                if constexpr (FULL) {
+                    uint32_t h[4], l[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) split2(xs[2 * e], xs[2 * e + 1], h[e], l[e]);
+                    if (lane < 32) {
+                        *reinterpret_cast<u32x4*>(bfp(tset(x1), L::TH) + rr * P24 + 8 * half) =
+                            u32x4{h[0], h[1], h[2], h[3]};
+                        *reinterpret_cast<u32x4*>(bfp(tset(x1), L::TL) + rr * P24 + 8 * half) =
+                            u32x4{l[0], l[1], l[2], l[3]};
+                    }
+                } else {
+                    const u32x4 xh = u32x4{cvt_pk(xs[0], xs[1]), cvt_pk(xs[2], xs[3]),
+                                           cvt_pk(xs[4], xs[5]), cvt_pk(xs[6], xs[7])};
+                    if (lane < 32)
+                        *reinterpret_cast<u32x4*>(bfp(tset(x1), L::TH) + rr * P24 + 8 * half) = xh;
+                }
             }
             lds_barrier();
         }
@@ -709,8 +740,14 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                     const float e0 = lv ? lo_bf(f.b[u]) * k0 : 0.f;
                     const float e1 = lv ? hi_bf(f.b[u]) * k1 : 0.f;
                     const int ot = kq_at<DK>(t, pc);
-                    *reinterpret_cast<uint32_t*>(bfp(es, L::EH) + ot) = cvt_pk(e0 * l0, e1 * l1);
                     uint32_t xh, xl;
+                    if constexpr (FULL) {
+                        split2(e0 * l0, e1 * l1, xh, xl);
+                        *reinterpret_cast<uint32_t*>(bfp(es, L::EH) + ot) = xh;
+                        *reinterpret_cast<uint32_t*>(bfp(es, L::EL) + ot) = xl;
+                    } else {
+                        *reinterpret_cast<uint32_t*>(bfp(es, L::EH) + ot) = cvt_pk(e0 * l0, e1 * l1);
+                    }
                     split2(lo_bf(f.q[u]) * l0, hi_bf(f.q[u]) * l1, xh, xl);
                     *reinterpret_cast<uint32_t*>(bfp(es, L::QH) + ot) = xh;
                     *reinterpret_cast<uint32_t*>(bfp(es, L::QL) + ot) = xl;
@@ -746,7 +783,7 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
     }
 }
 
-template <int DK, int DV, typename TOut, bool NORM>
+template <int DK, int DV, typename TOut, bool NORM, bool FULL = false>
 hipError_t launch_n(const ChunkArgs& a) {
     Gdr2Params p;
     p.T = a.T;
@@ -761,8 +798,8 @@ hipError_t launch_n(const ChunkArgs& a) {
     p.s0 = a.s0;
     p.o = a.o;
     p.s_final = a.s_final;
-    const size_t lds = Lay2<DK, NORM>::TOTAL;
-    auto fn = gdr2_bf16_kernel<DK, DV, TOut, NORM>;
+    const size_t lds = Lay2<DK, NORM, FULL>::TOTAL;
+    auto fn = gdr2_bf16_kernel<DK, DV, TOut, NORM, FULL>;
     hipError_t e =
         hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -779,6 +816,11 @@ hipError_t launch_t(const ChunkArgs& a) {
 
 template <int DK, int DV>
 hipError_t launch_d(const ChunkArgs& a) {
+    if (a.full) {
+        // only the sequence split's state passes ask for it (no o)
+        return a.l2norm ? launch_n<DK, DV, float, true, true>(a)
+                        : launch_n<DK, DV, float, false, true>(a);
+    }
     return a.out_bf16 ? launch_t<DK, DV, bf16_t>(a) : launch_t<DK, DV, float>(a);
 }
 

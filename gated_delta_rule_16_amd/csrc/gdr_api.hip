@@ -102,7 +102,7 @@ static gdr_status_t chunk_run(ChunkArgs& a) {
         return from_hip(launch_state_copy(a.s0, a.s_final, a.B * a.H * a.Dv * a.Dk, a.stream));
     }
     hipError_t e;
-    if (!a.in_bf16 || (a.gated2 && a.precise))
+    if (!a.in_bf16)
         e = launch_chunk_f32(a);
     else if (a.gated2)
         e = launch_gdr2_bf16(a);
@@ -268,7 +268,7 @@ static gdr_status_t split_states(const ChunkArgs& a, const SplitLayout& l, char*
     float* Sin = reinterpret_cast<float*>(w + l.R + l.P);
     void* vz = w + l.R + l.P + l.Sin;
     void* oP = l.oP ? static_cast<void*>(w + l.R + l.P + l.Sin + l.vz) : o;
-    const bool no_o = a.in_bf16 && !(a.gated2 && a.precise);
+    const bool no_o = a.in_bf16;
     gdr_status_t st;
     // 1. each segment from a zero state: R
     ChunkArgs r = a;
@@ -479,7 +479,10 @@ extern "C" size_t gdr2_chunk_bwd_split_workspace_size(int64_t B, int64_t T, int6
                                                       int64_t nseg) {
     if (nseg == 1 && dtype_ok(in_dt)) return gdr2_chunk_bwd_workspace_size(B, T, H, Dk, Dv);
     if (gdr_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, in_dt, nseg) == 0) return 0;
-    return bwd_split_layout(B, T, H, Dk, Dv, in_dt, nseg, true).total;
+    // enough for the plain call too (GDR_SPLIT_FP32_STATES)
+    const size_t split = bwd_split_layout(B, T, H, Dk, Dv, in_dt, nseg, true).total;
+    const size_t plain = gdr2_chunk_bwd_workspace_size(B, T, H, Dk, Dv);
+    return split > plain ? split : plain;
 }
 
 extern "C" gdr_status_t gdr_chunk_bwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
@@ -554,7 +557,9 @@ extern "C" gdr_status_t gdr2_chunk_bwd_split(int64_t B, int64_t T, int64_t H, in
                                              uint32_t flags, void* workspace,
                                              size_t workspace_bytes, hipStream_t stream) {
     if (nseg < 1 || nseg > (1 << 20)) return GDR_ERR_INVALID;
-    if (nseg == 1 || T == 0 || B == 0 || H == 0)   // the plain call (fp32 states already)
+    // one segment, or fp32 start states asked for: the plain call over the
+    // whole sequence
+    if (nseg == 1 || T == 0 || B == 0 || H == 0 || (flags & GDR_SPLIT_FP32_STATES))
         return gdr2_chunk_bwd_ex(B, T, H, Dk, Dv, in_dt, q, k, v, alpha, erase, write, s0,
                                  dout_dt, dout, ds_final, dq, dk, dv, dalpha, derase, dwrite, ds0,
                                  workspace, workspace_bytes, flags & ~GDR_SPLIT_FP32_STATES,
@@ -570,11 +575,9 @@ extern "C" gdr_status_t gdr2_chunk_bwd_split(int64_t B, int64_t T, int64_t H, in
     const BwdSplitLayout l = bwd_split_layout(B, T, H, Dk, Dv, in_dt, nseg, true);
     if (workspace_bytes < l.total) return GDR_ERR_INVALID;
     a.gated2 = true;
-    // with GDR_SPLIT_FP32_STATES the start states come from the fp32
-    // vector-ALU forward instead of the bf16 matrix-core one, which rounds
-    // E, A and T once (a few 1e-3 of the states over long memory, inherited
-    // by the gradients through S)
-    a.precise = (flags & GDR_SPLIT_FP32_STATES) != 0;
+    // the start states from the matrix-core forward with every computed
+    // operand split: the gradients inherit the states' error through S
+    a.full = true;
     a.q = q;
     a.k = k;
     a.v = v;

@@ -27,7 +27,7 @@ struct ChunkArgs {
     bool in_bf16, out_bf16;
     bool gated2;
     bool l2norm;            // normalise q, k on load (GDR_L2NORM_QK)
-    bool precise;           // rule 2, bf16 inputs: fp32 vector-ALU kernel
+    bool full;              // rule 2, bf16 inputs: every computed operand split
     const void *q, *k, *v;
     const void *alpha, *beta, *erase, *write;
     const float* s0;

@@ -215,16 +215,14 @@ gdr_status_t gdr2_chunk_fwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
 
 /*
  * Accepted by gdr2_chunk_bwd_split only (other calls return
- * GDR_ERR_UNSUPPORTED for it): with bf16 inputs, build the segments' start
- * states and transitions with the fp32 vector-ALU forward instead of the
- * bf16 matrix-core one.  The default rounds E (.) lambda, A and T to bf16
- * once in those passes; over long memory (alpha near 1) that leaves a few
- * 1e-3 of rms on the start states and on the gradients that go through S
- * (dq, dk, dalpha, derase: up to 4e-3 at B1 H16 T32768 d128 in 4 segments,
- * against ~1e-5 for the plain call).  With this bit those gradients keep
- * fp32 accuracy, at a higher cost: 42 ms against 18 ms for that workload,
- * where the plain call takes 31 ms.  fp32 inputs always take the fp32
- * forward; with nseg == 1 the bit is ignored.
+ * GDR_ERR_UNSUPPORTED for it): skip the sequence split and run the plain
+ * gdr2_chunk_bwd_ex over the whole sequence, whose states are fp32
+ * throughout (nseg is then only range-checked; the split's workspace size
+ * covers the plain call's).  Without the bit the split builds the
+ * segments' start states with a matrix-core forward whose computed
+ * operands all enter as hi/lo bf16 pairs, which keeps the gradients within
+ * 1e-3 of rms of the oracle on the B1 H16 T32768 d128 long-context
+ * workload (4 segments).
  */
 #define GDR_SPLIT_FP32_STATES 2u
 
@@ -336,7 +334,11 @@ gdr_status_t gdr_chunk_bwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
  * identity (the P pass uses a zero write gate too).  Arguments as for
  * gdr2_chunk_fwd_ex and gdr2_chunk_bwd_ex plus nseg, flags and the
  * workspace; gdr2_chunk_fwd_split takes gdr_chunk_fwd_split_workspace_size
- * bytes (the same layout), gdr2_chunk_bwd_split its own size below.
+ * bytes (the same layout), gdr2_chunk_bwd_split its own size below.  The
+ * backward's start-state passes split every computed operand into hi/lo
+ * bf16 terms (the forward's own passes round E (.) lambda, A and T once,
+ * which its o and S tolerate but the gradients through S would inherit);
+ * GDR_SPLIT_FP32_STATES in flags runs the plain backward instead.
  */
 gdr_status_t gdr2_chunk_fwd_split(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                   int64_t Dv, gdr_dtype_t in_dt, const void *q,

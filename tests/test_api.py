@@ -478,3 +478,12 @@ def test_dispatch_work_item_bound(gdr):
     assert bwd(gdr, T=elems // 64 + 1, wsb=1 << 60) == 1
     assert bwd2(gdr, T=elems // 64, wsb=1 << 60) == 3
     assert bwd2(gdr, T=elems // 64 + 1, wsb=1 << 60) == 1
+
+
+def test_gdr2_bwd_split_workspace_covers_plain(gdr):
+    """GDR_SPLIT_FP32_STATES runs the plain backward in the split call's
+    workspace, so the split size covers the plain one."""
+    f = gdr.lib.gdr2_chunk_bwd_split_workspace_size
+    for B, T, H, nseg in ((1, 64, 2, 4), (2, 90, 1, 3), (1, 32768, 16, 4)):
+        assert f(B, T, H, 128, 128, 1, nseg) >= gdr.gdr2_chunk_bwd_workspace_size(B, T, H, 128,
+                                                                                   128)
