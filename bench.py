@@ -77,12 +77,12 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_16_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bench_kernel_counters.json")
 # kernel-name prefix in rocprofv3 output -> the bench leg it belongs to
 KERNELS = {"gdn": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, 64, float, false, "
-                  "false>",
+                  "false, false>",
            "gdn_bf16o": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, 64, "
-                        "unsigned short, false, false>",
+                        "unsigned short, false, false, false>",
            "gdn_gate": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, 64, "
-                       "unsigned short, false, true>",
-           "gdr2": "void gdr::(anonymous namespace)::gdr2_bf16_kernel<128, 128, float, false>",
+                       "unsigned short, false, true, false>",
+           "gdr2": "void gdr::(anonymous namespace)::gdr2_bf16_kernel<128, 128, float, false, false>",
            "decode": "void gdr::step_kernel<128, 128, unsigned short, float>",
            "gate": "void gdr::(anonymous namespace)::output_gate_kernel<128, float, unsigned short, "
                    "unsigned short>",
@@ -989,7 +989,7 @@ def main():
         out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                            "traffic": measured_traffic("gdn"),
-                           "kernel": "chunk_bf16_kernel<128,128,64,float,false,false>",
+                           "kernel": "chunk_bf16_kernel<128,128,64,float,false,false,false>",
                            "algorithmic_bytes_per_launch": g["bytes"],
                            "bytes_with_fp32_o": g["bytes_as_run"],
                            "frac_with_fp32_o": g["bytes_as_run"] / g["mean"] / 1e9 / HBM_PEAK_GBS,

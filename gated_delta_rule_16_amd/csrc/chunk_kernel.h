@@ -168,7 +168,9 @@ __device__ __forceinline__ void st8(bf16_t* p, const uint2& x) {
     *reinterpret_cast<uint2*>(p) = x;
 }
 
-template <int DK, int DV, int RB, typename TOut, bool NORM, bool GATE = false>
+// NOO: no o at all (the sequence split's state passes want only the final
+// state): team A skips Q S^T, P V_new and the stores, B2 stages V only.
+template <int DK, int DV, int RB, typename TOut, bool NORM, bool GATE = false, bool NOO = false>
 __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Params p) {
     using L = Lay<DK, RB, NORM, GATE>;
     constexpr int NA = RB / 16;   // team A waves
@@ -426,11 +428,13 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
 #pragma unroll
                 for (int j = 0; j < KJ; ++j)
                     kf[tt][j] = *reinterpret_cast<const bf16x8*>(Kb + kq_at<DK>(16 * tt + m, 32 * j + 8 * g));
+            if constexpr (!NOO) {
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+                for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int j = 0; j < KJ; ++j)
-                    qf[tt][j] = *reinterpret_cast<const bf16x8*>(Qb + kq_at<DK>(16 * tt + m, 32 * j + 8 * g));
+                    for (int j = 0; j < KJ; ++j)
+                        qf[tt][j] = *reinterpret_cast<const bf16x8*>(Qb + kq_at<DK>(16 * tt + m, 32 * j + 8 * g));
+            }
             f32x4 ks[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int j = 0; j < KJ; ++j)
@@ -460,13 +464,15 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
 
             // ---- R = FR1 V - FR2 (K S_hat^T), beside Q S_hat^T -------------
             f32x4 qs[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            if constexpr (!NOO) {
 #pragma unroll
-            for (int j = 0; j < KJ; ++j)
+                for (int j = 0; j < KJ; ++j)
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    qs[tt] = mfma16(qf[tt][j], sh[j], qs[tt]);
-                    qs[tt] = mfma16(qf[tt][j], sl[j], qs[tt]);
-                }
+                    for (int tt = 0; tt < 2; ++tt) {
+                        qs[tt] = mfma16(qf[tt][j], sh[j], qs[tt]);
+                        qs[tt] = mfma16(qf[tt][j], sl[j], qs[tt]);
+                    }
+            }
             f32x4 rr[2];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
@@ -476,10 +482,12 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                                                fr1[tt][r] * bf2f((bf16_t)vv[tt][r]));
             bf16x8 rh, rl;
             split44(rr[0], rr[1], rh, rl);
+            if constexpr (!NOO) {
 #pragma unroll
-            for (int u = 0; u < 4 * KJ; ++u) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+                for (int u = 0; u < 4 * KJ; ++u) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
 
@@ -494,11 +502,14 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
             bf16x8 ph[2], pl[2], kt[NS];
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                const int at = (16 * rt + m) * P48 + 8 * g;
-                ph[rt] = *reinterpret_cast<const bf16x8*>(Ph + at);
-                pl[rt] = *reinterpret_cast<const bf16x8*>(Pl + at);
-                fo[rt] = *reinterpret_cast<const f32x4*>(G + FO + 16 * rt + 4 * g);
-                if constexpr (NORM) fo[rt] *= *reinterpret_cast<const f32x4*>(G + FPI + 16 * rt + 4 * g);
+                if constexpr (!NOO) {
+                    const int at = (16 * rt + m) * P48 + 8 * g;
+                    ph[rt] = *reinterpret_cast<const bf16x8*>(Ph + at);
+                    pl[rt] = *reinterpret_cast<const bf16x8*>(Pl + at);
+                    fo[rt] = *reinterpret_cast<const f32x4*>(G + FO + 16 * rt + 4 * g);
+                    if constexpr (NORM)
+                        fo[rt] *= *reinterpret_cast<const f32x4*>(G + FPI + 16 * rt + 4 * g);
+                }
                 fv[rt] = *reinterpret_cast<const f32x4*>(G + FV + 16 * rt + 4 * g);
             }
 #pragma unroll
@@ -517,12 +528,14 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
             split44(vn[0] * fv[0], vn[1] * fv[1], mh, ml);
             split44(vn[0], vn[1], nh, nl);
             f32x4 o[2];
+            if constexpr (!NOO) {
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                o[rt] = qs[rt] * fo[rt];
-                o[rt] = mfma16(ph[rt], nh, o[rt]);
-                o[rt] = mfma16(ph[rt], nl, o[rt]);
-                o[rt] = mfma16(pl[rt], nh, o[rt]);
+                for (int rt = 0; rt < 2; ++rt) {
+                    o[rt] = qs[rt] * fo[rt];
+                    o[rt] = mfma16(ph[rt], nh, o[rt]);
+                    o[rt] = mfma16(ph[rt], nl, o[rt]);
+                    o[rt] = mfma16(pl[rt], nh, o[rt]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
 
@@ -541,7 +554,7 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
             }
 #pragma unroll
             for (int j = 0; j < KJ; ++j) split44(sa[2 * j], sa[2 * j + 1], sh[j], sl[j]);
-            if constexpr (!GATE) {
+            if constexpr (!GATE && !NOO) {
                 // no o (p.o NULL: a pass that only wants the final state):
                 // an empty range drops every store
                 const int64_t t0 = c * CH;
@@ -569,7 +582,7 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
-            __builtin_amdgcn_sched_group_barrier(0x040, 8, 0);
+            if constexpr (!NOO) __builtin_amdgcn_sched_group_barrier(0x040, 8, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
             if constexpr (GATE) {
                 // this chunk's partial sums and gate; the previous chunk's
@@ -864,7 +877,7 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
             u32x4 v[VL];
         };
         auto load = [&](int64_t cn, Buf& f) {
-            load_k(cn, f.q, qbase);
+            if constexpr (!NOO) load_k(cn, f.q, qbase);
             const int last = last_row(cn);
             const char* cb = reinterpret_cast<const char*>(vbase + cn * CH * H * DV);
 #pragma unroll
@@ -880,12 +893,13 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
             bf16_t* Ph = reinterpret_cast<bf16_t*>(setp(cn, L::PH));
             bf16_t* Pl = reinterpret_cast<bf16_t*>(setp(cn, L::PL));
             const bf16_t* Kb = kring(cn);
-            stage_kq(Qb, f.q);
+            if constexpr (!NOO) stage_kq(Qb, f.q);
 #pragma unroll
             for (int u = 0; u < VL; ++u) {
                 const int pc = lane + 64 * u;
                 *reinterpret_cast<u32x4*>(Vb + (pc / VC) * L::PV + 8 * (pc % VC)) = f.v[u];
             }
+            if constexpr (NOO) return;   // no P without o
             wave_lds_sync();   // this wave's Q tile, read back in operand order
             // C[4 g + r][m] = k_{16 st + 4 g + r} . q_{16 rt + m}
             bf16x8 kf[2][KJ], qf[2][KJ];

@@ -7,7 +7,7 @@ namespace gdr {
 
 namespace {
 
-template <int DK, int DV, int RB, typename TOut, bool NORM>
+template <int DK, int DV, int RB, typename TOut, bool NORM, bool NOO = false>
 hipError_t launch_bf16_n(const ChunkArgs& a) {
     Bf16Params p{};   // bh0 = 0: all heads in one launch
     p.T = a.T;
@@ -22,7 +22,7 @@ hipError_t launch_bf16_n(const ChunkArgs& a) {
     p.o = a.o;
     p.s_final = a.s_final;
     const size_t lds = Lay<DK, RB, NORM>::TOTAL;
-    auto fn = chunk_bf16_kernel<DK, DV, RB, TOut, NORM>;
+    auto fn = chunk_bf16_kernel<DK, DV, RB, TOut, NORM, false, NOO>;
     hipError_t e =
         hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -34,6 +34,9 @@ hipError_t launch_bf16_n(const ChunkArgs& a) {
 
 template <int DK, int DV, int RB, typename TOut>
 hipError_t launch_bf16_t(const ChunkArgs& a) {
+    if (!a.o)   // only the final state wanted (the sequence split's state passes)
+        return a.l2norm ? launch_bf16_n<DK, DV, RB, float, true, true>(a)
+                        : launch_bf16_n<DK, DV, RB, float, false, true>(a);
     return a.l2norm ? launch_bf16_n<DK, DV, RB, TOut, true>(a)
                     : launch_bf16_n<DK, DV, RB, TOut, false>(a);
 }

@@ -257,9 +257,10 @@ SplitLayout split_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv
 // Passes 1-3 of the sequence split, on the segment batch `a` (B nseg
 // segments of T / nseg tokens, inputs set): R (each segment from zero), P
 // (v = 0 from the identity) and the scan into the start states Sin.  Only
-// the passes' final states are wanted: the bf16 matrix-core kernels write
-// no o for them; the fp32 vector-ALU kernels write theirs to `o`
-// (overwritten by the caller's last pass) or to the workspace's discard
+// the passes' final states are wanted: the bf16 matrix-core kernels get
+// o = NULL (the scalar-gate one then skips the output products, the
+// channel-gate one its stores); the fp32 vector-ALU kernels write theirs to
+// `o` (overwritten by the caller's last pass) or to the workspace's discard
 // buffer when the layout has one.
 static gdr_status_t split_states(const ChunkArgs& a, const SplitLayout& l, char* w, int64_t B,
                                  int64_t nseg, const float* s0, void* o) {
