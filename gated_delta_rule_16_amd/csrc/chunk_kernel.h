@@ -277,6 +277,11 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
         const int tok = 16 * (jt >> 2) + 4 * g + (jt & 3);
         const float wr = GATE && p.w ? p.w[row0 + i] : 1.f;
         float* psq = reinterpret_cast<float*>(smem + L::PSQ);   // [3][NA][CH]
+        // chunk slots in 32-bit arithmetic (the call keeps T below 2^36)
+        auto mod3 = [](int64_t cn) { return (int)((uint32_t)cn % 3u); };
+        auto mod4 = [](int64_t cn) { return (int)((uint32_t)cn & 3u); };
+        // this lane's token in the head's exchange words
+        unsigned long long* xhead = p.xch + bh * NRB * 4 * CH + tok;
         // squares of o summed over the wave's 16 rows (a reduce-scatter over
         // the DPP row: partners lane ^ 15, ^ 7, ^ 3, ^ 1, keeping half each
         // time), written to LDS by the owners of each token
@@ -294,18 +299,18 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                 s2[k] = (b2 ? s4[2 + k] : s4[k]) + dpp_mov<0x141>(b2 ? s4[k] : s4[2 + k]);
             float s1 = (b1 ? s2[1] : s2[0]) + dpp_mov<0x1B>(b1 ? s2[0] : s2[1]);
             s1 += dpp_mov<0xB1>(s1);
-            if (!(m & 1)) psq[((int)(cn % 3) * NA + a) * CH + tok] = s1;
+            if (!(m & 1)) psq[(mod3(cn) * NA + a) * CH + tok] = s1;
         };
         // the workgroup's sum for the lane's token; wave 0 publishes it to
         // the head's other row blocks, tagged with the chunk
         auto gate_wsum = [&](int64_t cn) {
             float s = 0.f;
 #pragma unroll
-            for (int aa = 0; aa < NA; ++aa) s += psq[((int)(cn % 3) * NA + aa) * CH + tok];
+            for (int aa = 0; aa < NA; ++aa) s += psq[(mod3(cn) * NA + aa) * CH + tok];
             if (NRB > 1 && a == 0 && !(m & 1)) {
                 const unsigned long long word =
                     ((unsigned long long)(uint32_t)(cn + 1) << 32) | __float_as_uint(s);
-                __hip_atomic_store(p.xch + ((bh * NRB + rbk) * 4 + (cn & 3)) * CH + tok, word,
+                __hip_atomic_store(xhead + (rbk * 4 + mod4(cn)) * CH, word,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             return s;
@@ -314,7 +319,7 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
         // SiLU(x) = x / (1 + e^-x).  The lane's gate values (tokens 16 rt +
         // 4 g + r, channel i): bf16 by two transposed reads, fp32 one by one.
         auto gate_apply = [&](const f32x4 (&ov)[2], int64_t cn, f32x4 (&og)[2]) {
-            const unsigned char* gs = smem + L::GGR + (int)(cn % 3) * L::GGS;
+            const unsigned char* gs = smem + L::GGR + mod3(cn) * L::GGS;
             f32x4 gv[2];
             if (p.gate_bf16) {
                 const bf16_t* gb = reinterpret_cast<const bf16_t*>(gs);
@@ -345,7 +350,7 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
         constexpr int NP = NRB > 1 ? NRB - 1 : 1;
         auto xsrc = [&](int64_t cn, int k) {   // k-th other row block
             const int rb = k + (k >= rbk ? 1 : 0);
-            return p.xch + ((bh * NRB + rb) * 4 + (cn & 3)) * CH + tok;
+            return xhead + (rb * 4 + mod4(cn)) * CH;
         };
         auto gate_fetch = [&](int64_t cn, unsigned long long (&pw)[NP]) {
 #pragma unroll
@@ -360,16 +365,21 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
         auto gate_out = [&](int64_t cn, const f32x4 (&og)[2], float wsum,
                             unsigned long long (&pw)[NP]) {
             float tot = wsum;
+            const uint32_t tag = (uint32_t)(cn + 1);
 #pragma unroll
             for (int k = 0; k < NRB - 1; ++k) {
                 unsigned long long x = pw[k];
-                for (int spin = 0; spin < (1 << 18); ++spin) {
-                    if ((uint32_t)(x >> 32) == (uint32_t)(cn + 1)) break;
-                    __builtin_amdgcn_s_sleep(2);
-                    x = __hip_atomic_load(xsrc(cn, k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                // the usual case is one uniform test: every word has arrived
+                if (__builtin_amdgcn_ballot_w64((uint32_t)(x >> 32) != tag) != 0) {
+#pragma nounroll
+                    for (int spin = 0; spin < (1 << 18); ++spin) {
+                        if ((uint32_t)(x >> 32) == tag) break;
+                        __builtin_amdgcn_s_sleep(2);
+                        x = __hip_atomic_load(xsrc(cn, k), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+                    }
                 }
-                tot += (uint32_t)(x >> 32) == (uint32_t)(cn + 1) ? __uint_as_float((uint32_t)x)
-                                                                 : __builtin_nanf("");
+                tot += (uint32_t)(x >> 32) == tag ? __uint_as_float((uint32_t)x) : __builtin_nanf("");
             }
             const float rr = rsqrtf(tot * (1.f / DV) + p.eps);
             const f32x4 rv[2] = {f32x4{dpp_mov<0x150>(rr), dpp_mov<0x152>(rr), dpp_mov<0x154>(rr),
@@ -380,16 +390,17 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
             const __amdgpu_buffer_rsrc_t ores = __builtin_amdgcn_make_buffer_rsrc(
                 obase + cn * CH * H * DV, (short)0, n * (int)(H * DV * sizeof(TOut)), 0x00020000);
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < 2; ++rt) {
+                const f32x4 y = og[rt] * rv[rt];
+                if constexpr (sizeof(TOut) == 4) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float y = og[rt][r] * rv[rt][r];
-                    if constexpr (sizeof(TOut) == 4)
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), ores,
+                    for (int r = 0; r < 4; ++r)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[r]), ores,
                                                               (int)ooff[rt][r], 0, 0);
-                    else
-                        __builtin_amdgcn_raw_buffer_store_b16(f2bf(y), ores, (int)ooff[rt][r], 0, 0);
+                } else {
+                    store4_bf16(y, ores, ooff[rt]);
                 }
+            }
         };
         // held across periods: o of the previous chunk, the gated o and
         // workgroup sum of the one before
@@ -562,16 +573,16 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                 const __amdgpu_buffer_rsrc_t ores = __builtin_amdgcn_make_buffer_rsrc(
                     obase + t0 * H * DV, (short)0, n * (int)(H * DV * sizeof(TOut)), 0x00020000);
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
+                for (int rt = 0; rt < 2; ++rt) {
+                    if constexpr (sizeof(TOut) == 4) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if constexpr (sizeof(TOut) == 4)
+                        for (int r = 0; r < 4; ++r)
                             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[rt][r]), ores,
                                                                   (int)ooff[rt][r], 0, 0);
-                        else
-                            __builtin_amdgcn_raw_buffer_store_b16(f2bf(o[rt][r]), ores,
-                                                                  (int)ooff[rt][r], 0, 0);
+                    } else {
+                        store4_bf16(o[rt], ores, ooff[rt]);
                     }
+                }
             }
             // products of tile pairs 0, 1 first, then each pair's split
             // beside the next pair's products, the stores before the last

@@ -358,13 +358,13 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
                 const int n = p.o ? (int)min((int64_t)CH, T - t0) : 0;
                 const __amdgpu_buffer_rsrc_t ores = __builtin_amdgcn_make_buffer_rsrc(
                     obase + t0 * H * DV, (short)0, n * (int)(H * DV * sizeof(TOut)), 0x00020000);
+                if constexpr (sizeof(TOut) == 4) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if constexpr (sizeof(TOut) == 4)
+                    for (int r = 0; r < 4; ++r)
                         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[r]), ores,
                                                               (int)ooff[r], 0, 0);
-                    else
-                        __builtin_amdgcn_raw_buffer_store_b16(f2bf(o[r]), ores, (int)ooff[r], 0, 0);
+                } else {
+                    store4_bf16(o, ores, ooff);
                 }
             }
             read_eq(c + 1);

@@ -180,6 +180,7 @@ extern "C" gdr_status_t gdr_chunk_fwd_gate(int64_t B, int64_t T, int64_t H, int6
     if (!dtype_ok(g_dt)) return GDR_ERR_UNSUPPORTED;
     if (!(eps >= 0.f) || eps > 3.0e38f) return GDR_ERR_INVALID;
     if (!opt_ok(s0) || !opt_ok(s_final) || !opt_ok(w)) return GDR_ERR_INVALID;
+    if (T >= ((int64_t)1 << 36)) return GDR_ERR_INVALID;   // 32-bit chunk slots
     const bool empty = B == 0 || T == 0 || H == 0;
     if (!empty) {
         if (!ptrs_ok({q, k, v, g, y}) || !elem_ok(alpha, 4) || !elem_ok(beta, 4))

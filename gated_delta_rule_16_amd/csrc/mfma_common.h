@@ -33,6 +33,17 @@ __device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Four fp32 values stored as bf16 (v_cvt_pk_bf16_f32: round to nearest
+// even, NaN kept) at four byte offsets of a buffer resource.
+__device__ __forceinline__ void store4_bf16(const f32x4& x, __amdgpu_buffer_rsrc_t r,
+                                            const uint32_t (&off)[4]) {
+    const uint32_t a = cvt_pk(x[0], x[1]), b = cvt_pk(x[2], x[3]);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)a, r, (int)off[0], 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(a >> 16), r, (int)off[1], 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)b, r, (int)off[2], 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(b >> 16), r, (int)off[3], 0, 0);
+}
+
 // hi/lo split of two values: hi = bf16(x), lo = bf16(x - hi).  The
 // residuals x - hi come from v_dot2c_f32_bf16 on the packed hi pair,
 // dot((hi_a, hi_b), (-1, 0)) + a (and (0, -1) for b): -hi is exact and the

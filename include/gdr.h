@@ -420,6 +420,8 @@ gdr_status_t gdr_output_gate(int64_t N, int64_t H, int64_t Dv, gdr_dtype_t o_dt,
  * capture.  Equals gdr_output_gate(gdr_chunk_fwd(...)) up to fp32 rounding;
  * GDR_ERR_DEVICE if a cooperative launch is refused.  q, k, v, g, y need
  * 16-byte alignment; alpha, beta element alignment; w 16 bytes when given.
+ * T must stay below 2^36 (the kernel keeps chunk slots in 32 bits;
+ * GDR_ERR_INVALID otherwise).
  */
 size_t gdr_chunk_fwd_gate_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                          int64_t Dv, gdr_dtype_t in_dt);
