@@ -5,13 +5,14 @@ One step = one chunkwise gated delta rule forward (gdr_chunk_fwd) over the
 1.3B-layer workload: B=8, H=16, T=4096, d_k = d_v = 128, bf16 q/k/v, fp32
 alpha/beta, zero initial state, fp32 output and final state.  Inputs are
 seeded synthetic tensors resident in HBM before timing starts.  The
-headline leg runs after the decode, GDN-2 and long-context legs, so that
-its launches see the steady clock rather than the ramp after idle; its
-warm-up and timed calls are exactly --warmup and --steps.
+headline leg runs after the decode, GDN-2, long-context and bf16-o legs,
+so that its launches see the steady clock rather than the ramp after idle;
+its warm-up and timed calls are exactly --warmup and --steps.
 
 The JSON line (stdout, last line) carries:
-  value / unit       tokens/s of that forward (B*T tokens per call, from the
-                     median launch time)
+  value / unit       tokens/s of that forward: B*T tokens per call over the
+                     mean call time of the timed region (per-call median
+                     and minimum beside it, from a second pass)
   roofline           the chunked kernel against HBM bandwidth: the
                      algorithmic bytes of the workload (1,032 B per
                      token-head for bf16 q, k, v, o and fp32 alpha, beta,
@@ -28,7 +29,8 @@ The JSON line (stdout, last line) carries:
                      state (16 sequential chains; tokens/s, HBM and MFMA
                      fractions)
   gate_fused         gdr_chunk_fwd_gate (output gate fused on the stores)
-                     against gdr_chunk_fwd + gdr_output_gate, interleaved
+                     against gdr_chunk_fwd + gdr_output_gate, in rounds of
+                     back-to-back calls
   l2norm             the fused L2 normalisation of q, k (GDR_L2NORM_QK) on
                      the GDN and GDN-2 workloads with raw q, k: launch time
                      fused, plain (no normalisation), and a separate
@@ -171,7 +173,9 @@ def _counter_means(dirs):
 N_XCD = 8          # accelerator complex dies of an MI355X (GRBM_GUI_ACTIVE sums over them)
 
 
-def summarize(trace_dir, pmc_dirs, out_txt, command, timed=20):
+def summarize(trace_dir, pmc_dirs, out_txt, command, timed=20, warmup=5,
+              legs_run=("decode", "gdr2", "longctx", "gdn", "gdn_bf16o", "gate_fused", "l2norm",
+                        "gate", "gate_bwd", "bwd", "bwd2", "bwd_long", "copy")):
     """Turn rocprofv3 CSV output -- one --kernel-trace --stats run and
     several --pmc runs of the same command -- into a short text summary and
     the JSON the benchmark reads its counter figures from.
@@ -198,20 +202,40 @@ def summarize(trace_dir, pmc_dirs, out_txt, command, timed=20):
     for r in stats:
         lines.append(f"  {r['Name'][:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
                      f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f}")
-    # the same trace, per bench leg: the timed launches only (the last
-    # `timed` dispatches of each kernel; the warm-up launches before them
-    # include the clock ramp after idle)
-    lines += ["", f"Timed launches (the last {timed} dispatches of each kernel in the trace, 10 for "
-              "the backward legs, as the bench times them):",
+    # the same trace, per bench leg: its timed launches only.  Legs run in
+    # a fixed order and some kernels serve several legs, so a leg's
+    # dispatches are counted from the start of the trace: the dispatches of
+    # its kernel by earlier legs are skipped, then its warm-up calls, then
+    # come its timed ones (time_launches' timed region; all the rounds of
+    # the fused-gate leg); the copy is the 512 MiB one (the largest grid).
+    W, K = warmup, timed
+    Wb, Kb = min(W, 5), min(K, 10)   # the backward legs' caps
+    fused_two_calls = W + 10 * K if "gate_fused" in legs_run else 0
+    # the long-context split's last pass runs the headline kernel (8 x 16
+    # segment-heads of 4096 tokens) once per call, before the headline leg
+    longctx_calls = min(W, 10) + 2 * min(K, 10) if "longctx" in legs_run else 0
+    first = {  # leg: (index of the first timed dispatch of its kernel, timed count)
+        "decode": (W, 64), "gdr2": (1 + W, K), "gdn": (longctx_calls + W, K), "gdn_bf16o": (W, K),
+        "gdn_gate": (W, 10 * K), "gate": (fused_two_calls + W, K), "bwd": (Wb, Kb),
+        "bwd2": (Wb, Kb), "copy": (W, K)}
+    lines += ["", f"Timed launches of each leg (--warmup {W} --steps {K}; per leg the dispatches "
+              "of its timed region, counted from the start of the trace; the copy's 512 MiB "
+              "dispatches):",
               f"  {'leg':9s} {'kernel':50s} {'n':>4s} {'avg us':>10s} {'min us':>10s}"]
     dur_us = {}
     for leg, prefix in KERNELS.items():
-        d = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in trace
-                   if r["Kernel_Name"].startswith(prefix))
+        rows = [r for r in trace if r["Kernel_Name"].startswith(prefix)]
+        if leg == "copy" and rows:
+            gk = "Grid_Size" if "Grid_Size" in rows[0] else "Grid_Size_X"
+            big = max(int(r[gk]) for r in rows)
+            rows = [r for r in rows if int(r[gk]) == big]
+        d = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows)
+        if leg in first:
+            i0, n = first[leg]
+            d = d[i0:i0 + n]
         if not d:
             continue
-        n_timed = min(timed, 10) if leg in ("bwd", "bwd2") else timed   # legs capped at 10
-        dur = [(e - b) / 1e3 for b, e in d[-n_timed:]]
+        dur = [(e - b) / 1e3 for b, e in d]
         dur_us[leg] = sum(dur) / len(dur)
         lines.append(f"  {leg:9s} {prefix.split('::')[-1][:50]:50s} {len(dur):4d} "
                      f"{dur_us[leg]:10.1f} {min(dur):10.1f}")
@@ -355,23 +379,35 @@ def on_device(idx, *fields):
 
 
 def time_launches(fn, warmup, steps):
-    """Mean and min per-call time (s) from HIP events on the current stream,
-    plus the wall time of the `steps` calls bracketed by synchronize."""
+    """The timed region: after `warmup` untimed calls, `steps` calls back to
+    back between two HIP events recorded on the current stream (the stream
+    the calls launch on); mean per call = elapsed / steps, and the wall time
+    of the region, bracketed by synchronize.  Then `steps` more calls, each
+    between its own pair of events, for the per-call minimum and median (an
+    event pair per call leaves the GPU idle a few microseconds between
+    launches, so these run after the timed region).  Returns seconds:
+    (mean, min, median, wall)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean = start.elapsed_time(end) / steps / 1e3
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
-    t0 = time.perf_counter()
     for a, b in evs:
         a.record()
         fn()
         b.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ms = sorted(a.elapsed_time(b) for a, b in evs)
-    mean = sum(ms) / len(ms) / 1e3
     return mean, ms[0] / 1e3, ms[len(ms) // 2] / 1e3, wall
 
 
@@ -520,6 +556,34 @@ def time_interleaved(fns, warmup, rounds):
     return out
 
 
+def time_rounds(fns, warmup, rounds, per_round=10):
+    """Median and min over `rounds` of the mean call time (us) of each
+    callable in `fns`: a round runs `per_round` calls of each back to back
+    between two events (rotating the order each round), so all see the same
+    sustained clocks and no event sits between two calls."""
+    import torch
+    names = list(fns)
+    for _ in range(warmup):
+        for n in names:
+            fns[n]()
+    torch.cuda.synchronize()
+    t = {n: [] for n in names}
+    for r in range(rounds):
+        for n in names[r % len(names):] + names[:r % len(names)]:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(per_round):
+                fns[n]()
+            b.record()
+            torch.cuda.synchronize()
+            t[n].append(a.elapsed_time(b) * 1e3 / per_round)
+    out = {}
+    for n in names:
+        x = sorted(t[n])
+        out[n] = {"median": x[len(x) // 2], "min": x[0]}
+    return out
+
+
 def bench_l2norm(gdr, torch, warmup, steps):
     """Fused q, k normalisation against the plain call and against a
     separate normalise pass (fp32 sum of squares in PyTorch, bf16 result)
@@ -622,8 +686,8 @@ def bench_gate_fused(gdr, torch, warmup, steps):
     def plain():
         gdr.gdr_chunk_fwd(q, k, v, a, b, None, out_dtype=torch.float32, o=o, s_final=sf)
 
-    t = time_interleaved({"fused": fused, "two_calls": two_calls, "forward_only": plain},
-                         warmup, steps)
+    t = time_rounds({"fused": fused, "two_calls": two_calls, "forward_only": plain},
+                    warmup, steps)
     return dict(t=t, tokens=B * T)
 
 
@@ -889,7 +953,8 @@ def main():
                     help="the profiling commands (' ;; '-separated), recorded in --summarize")
     args = ap.parse_args()
     if args.summarize:
-        summarize(args.summarize[0], args.pmc_dir, args.summarize[1], command=args.command)
+        summarize(args.summarize[0], args.pmc_dir, args.summarize[1], command=args.command,
+                  timed=args.steps, warmup=args.warmup)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this "
@@ -909,11 +974,11 @@ def main():
         return args.only in (None, leg) and leg not in skip
 
     # Stage the forward legs' inputs in HBM first.  The headline leg then
-    # runs right after the decode, GDN-2 and long-context legs: after idle
-    # the GPU takes some tens of milliseconds of sustained load to reach its
-    # steady clocks, and back-to-back launches from a cold start time
-    # 20-30 % slower.  Its own warm-up and timed calls are --warmup and
-    # --steps.
+    # runs right after the decode, GDN-2, long-context and bf16-o legs (the
+    # last one the same kernel with bf16 o): after idle the GPU takes ~100
+    # launches of sustained load to settle its clocks, and back-to-back
+    # launches from a cold start time 20-30 % slower.  Its own warm-up and
+    # timed calls are exactly --warmup and --steps.
     stage = {1: ("q", "k", "v", "alpha", "beta"), 2: ("q", "k", "v", "alpha", "beta", "s0"),
              3: ("state0", "q", "k", "v", "alpha", "beta"),
              4: ("q", "k", "v", "alpha", "erase", "write")}
@@ -935,13 +1000,13 @@ def main():
     if want("longctx"):
         log("timing gdr_chunk_fwd B1 H16 T32768 d128 (long context) ...")
         res["longctx"] = bench_longctx(gdr, torch, min(args.warmup, 10), min(args.steps, 10))
+    if want("gdn_bf16o"):
+        log("timing gdr_chunk_fwd B8 H16 T4096 d128, bf16 o ...")
+        res["gdn_bf16o"] = bench_gdn(gdr, torch, args.warmup, args.steps, out_dtype="bf16")
     if want("gdn"):
         log("timing gdr_chunk_fwd B8 H16 T4096 d128 ...")
         res["gdn"] = bench_gdn(gdr, torch, args.warmup, args.steps)
         log(f"  median {res['gdn']['median'] * 1e6:.1f} us, mean {res['gdn']['mean'] * 1e6:.1f} us")
-    if want("gdn_bf16o"):
-        log("timing gdr_chunk_fwd B8 H16 T4096 d128, bf16 o ...")
-        res["gdn_bf16o"] = bench_gdn(gdr, torch, args.warmup, args.steps, out_dtype="bf16")
     if want("gate_fused"):
         log("timing gdr_chunk_fwd_gate against gdr_chunk_fwd + gdr_output_gate ...")
         res["gate_fused"] = bench_gate_fused(gdr, torch, args.warmup, args.steps)
@@ -982,7 +1047,7 @@ def main():
     if "gdn" in res:
         g = res["gdn"]
         tok = g["B"] * g["T"]
-        out["value"] = tok / g["median"]
+        out["value"] = tok / g["mean"]
         out["unit"] = "tokens/s"
         out["ms_per_step"] = g["wall"] / args.steps * 1e3
         gbs = g["bytes"] / g["mean"] / 1e9
@@ -1007,7 +1072,7 @@ def main():
         g = res["gdn_bf16o"]
         gbs = g["bytes"] / g["mean"] / 1e9
         out["gdn_bf16_o"] = {"workload": "gdr_chunk_fwd B8 H16 T4096 d128, bf16 q/k/v/o",
-                             "tokens/s": g["B"] * g["T"] / g["median"],
+                             "tokens/s": g["B"] * g["T"] / g["mean"],
                              "launch_us_mean": g["mean"] * 1e6,
                              "launch_us_median": g["median"] * 1e6,
                              "launch_us_min": g["min"] * 1e6, "GB/s": gbs,
@@ -1033,7 +1098,7 @@ def main():
             gbs = r["bytes"] / r["mean"] / 1e9
             tf = r["flops"] / r["mean"] / 1e12
             out["gdr2"] = {"workload": "gdr2_chunk_fwd B4 H16 T4096 d128 bf16, fp32 o",
-                           "tokens/s": r["B"] * r["T"] / r["median"],
+                           "tokens/s": r["B"] * r["T"] / r["mean"],
                            "launch_us_mean": r["mean"] * 1e6,
                            "launch_us_median": r["median"] * 1e6,
                            "launch_us_min": r["min"] * 1e6, "GB/s": gbs,
@@ -1053,7 +1118,7 @@ def main():
         out["long_context"] = {
             "workload": "B1 H16 T32768 d128 bf16, fp32 alpha/beta/o, initial state: "
                         f"gdr_chunk_fwd_split, {r['nseg']} segments of {r['T'] // r['nseg']}",
-            "tokens/s": r["B"] * r["T"] / r["median"], "launch_us_mean": r["mean"] * 1e6,
+            "tokens/s": r["B"] * r["T"] / r["mean"], "launch_us_mean": r["mean"] * 1e6,
             "launch_us_median": r["median"] * 1e6,
             "launch_us_min": r["min"] * 1e6, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
             "mfma_frac": r["flops"] / r["mean"] / 1e12 / BF16_PEAK_TFLOPS,
@@ -1066,7 +1131,8 @@ def main():
         t = res["gate_fused"]["t"]
         tok = res["gate_fused"]["tokens"]
         out["gate_fused"] = {"workload": "B8 H16 T4096 d128 forward + output gate (bf16 gate, "
-                                         "fp32 weight, bf16 y); interleaved launches",
+                                         "fp32 weight, bf16 y); rounds of 10 back-to-back calls "
+                                         "of each, medians over rounds",
                              **{f"{n}_us_median": v["median"] for n, v in t.items()},
                              **{f"{n}_us_min": v["min"] for n, v in t.items()},
                              "fused_tokens/s": tok / t["fused"]["median"] * 1e6,
