@@ -175,7 +175,7 @@ N_XCD = 8          # accelerator complex dies of an MI355X (GRBM_GUI_ACTIVE sums
 
 def summarize(trace_dir, pmc_dirs, out_txt, command, timed=20, warmup=5,
               legs_run=("decode", "gdr2", "longctx", "gdn", "gdn_bf16o", "gate_fused", "l2norm",
-                        "gate", "gate_bwd", "bwd", "bwd2", "bwd_long", "copy")):
+                        "gate", "gate_bwd", "bwd", "bwd2", "bwd_long", "copy"), json_out=None):
     """Turn rocprofv3 CSV output -- one --kernel-trace --stats run and
     several --pmc runs of the same command -- into a short text summary and
     the JSON the benchmark reads its counter figures from.
@@ -319,8 +319,9 @@ def summarize(trace_dir, pmc_dirs, out_txt, command, timed=20, warmup=5,
                "copy_check": check, "fetch_write_scale": scale, "traffic": traffic,
                "mfma": {k: {kk: vv for kk, vv in v.items() if kk != "raw"}
                         for k, v in mfma.items()},
-               "dram_read_share": dram, "command": command},
-              open(TRAFFIC_FILE, "w"), indent=1)
+               "dram_read_share": dram, "command": command,
+               "timed_launch_us": dur_us},
+              open(json_out or TRAFFIC_FILE, "w"), indent=1)
     print("\n".join(lines))
 
 

@@ -45,3 +45,70 @@ def test_kernel_hash_ignores_comments(tmp_path):
     assert bench._code_text(str(a)) == t1
     a.write_text("int x; int z;\n")
     assert bench._code_text(str(a)) != t1
+
+
+def _write_csv(path, header, rows):
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f, quoting=csv.QUOTE_NONNUMERIC)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_summary_finds_each_legs_timed_dispatches(tmp_path):
+    """summarize() on a synthetic trace laid out as the round-end command
+    makes it (--warmup 5 --steps 20): the headline kernel's first
+    dispatches belong to the long-context split (25) and the headline's
+    warm-up (5), the output gate's first ones to the fused-gate leg's two
+    calls (5 + 10 x 20), and only the largest copies are the 512 MiB one.
+    Each timed dispatch lasts 100 us more than its neighbours outside the
+    timed region, so a wrong window changes the average."""
+    sys.path.insert(0, ROOT)
+    import bench
+    W, K = 5, 20
+    rows, t = [], [1000]
+
+    def emit(name, n, us, grid=256):
+        for _ in range(n):
+            rows.append([name, t[0], t[0] + int(us * 1e3), grid])
+            t[0] += int(us * 1e3) + 10
+
+    gdn, gate, copy = bench.KERNELS["gdn"] + "(P)", bench.KERNELS["gate"] + "(P)", \
+        bench.KERNELS["copy"]
+    emit(copy, 3, 5.0, grid=512)                    # input uploads
+    emit(gdn, 25, 900.0)                            # long-context split, last pass
+    emit(gdn, W, 900.0)                             # headline warm-up
+    emit(gdn, K, 250.0)                             # headline timed region
+    emit(gdn, K, 900.0)                             # headline per-call pass
+    emit(gate, W + 10 * K, 900.0)                   # fused-gate leg's two calls
+    emit(gate, W, 900.0)
+    emit(gate, K, 100.0)                            # gate timed region
+    emit(gate, K, 900.0)
+    emit(copy, W, 900.0, grid=131072)
+    emit(copy, K, 200.0, grid=131072)               # copy timed region
+    emit(copy, K, 900.0, grid=131072)
+    tr = tmp_path / "trace"
+    tr.mkdir()
+    _write_csv(tr / "run_kernel_trace.csv",
+               ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X"], rows)
+    _write_csv(tr / "run_kernel_stats.csv", ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"],
+               [[gdn, 70, 1.0, 1.0, 1.0]])
+    pmc = tmp_path / "pmc"
+    pmc.mkdir()
+    crow = []
+    for i, (grid, n128) in enumerate(((512, 4), (131072, 4194304))):
+        for name, v in (("TCC_EA0_RDREQ_32B_sum", 0), ("TCC_EA0_RDREQ_64B_sum", 0),
+                        ("TCC_EA0_RDREQ_128B_sum", n128), ("TCC_EA0_WRREQ_sum", 2 * n128),
+                        ("TCC_EA0_WRREQ_64B_sum", 2 * n128)):
+            crow.append([i, grid, copy, name, v, 0, 1])
+    _write_csv(pmc / "run_counter_collection.csv",
+               ["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value",
+                "Start_Timestamp", "End_Timestamp"], crow)
+    out = tmp_path / "sum.json"
+    bench.summarize(str(tr), [str(pmc)], str(tmp_path / "sum.txt"), "test", timed=K,
+                    warmup=W, json_out=str(out))
+    d = json.load(open(out))
+    assert abs(d["timed_launch_us"]["gdn"] - 250.0) < 0.01
+    assert abs(d["timed_launch_us"]["gate"] - 100.0) < 0.01
+    assert abs(d["timed_launch_us"]["copy"] - 200.0) < 0.01
+    assert abs(d["copy_check"]["read"] - 1.0) < 1e-9 and abs(d["copy_check"]["write"] - 1.0) < 1e-9
