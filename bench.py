@@ -88,17 +88,17 @@ KERNELS = {"gdn": "void gdr::(anonymous namespace)::chunk_bf16_kernel<128, 128, 
            "decode": "void gdr::step_kernel<128, 128, unsigned short, float>",
            "gate": "void gdr::(anonymous namespace)::output_gate_kernel<128, float, unsigned short, "
                    "unsigned short>",
-           "bwd": "void gdr::(anonymous namespace)::chunk2_bwd_kernel<128, 128, unsigned short, "
-                  "unsigned short, true>",
+           "bwd": "void gdr::(anonymous namespace)::gdn_bwd_kernel<128, 128, unsigned short, "
+                  "unsigned short>",
            "bwd2": "void gdr::(anonymous namespace)::chunk2_bwd_kernel<128, 128, unsigned short, "
-                   "unsigned short, false>",
+                   "unsigned short>",
            "copy": "__amd_rocclr_copyBuffer"}
 
 
 # the HIP source each profiled kernel is compiled from
 KERNEL_SOURCE = {"gdn": "chunk_mfma.hip", "gdn_bf16o": "chunk_mfma.hip", "gdn_gate": "chunk_gate.hip",
                  "gdr2": "gdr2_mfma.hip", "decode": "step.hip", "gate": "epilogue.hip",
-                 "bwd": "chunk2_bwd.hip", "bwd2": "chunk2_bwd.hip"}
+                 "bwd": "chunk_bwd.hip", "bwd2": "chunk2_bwd.hip"}
 
 
 def _code_text(path):

@@ -46,11 +46,6 @@
 // terms are vector ALU.  Per chunk the per-channel gradients stay in the registers of
 // the wave that owns those channels, from the products to the HBM stores.
 //
-// The scalar-gate rule (gdr_chunk_bwd) is this rule with alpha broadcast
-// over the key channels and erase = write = beta; template flag SC reads
-// alpha and beta per token and sums the per-channel gate gradients (and the
-// per-row write gradient) into per-token partials inside the kernel.
-//
 // The LDS footprint (~142 KB) allows one workgroup per CU, one wave per SIMD,
 // so every global input of the next chunk (key-side rows, w, v, dL/do, the
 // chunk-start state) is loaded into registers as raw words while the current
@@ -77,12 +72,6 @@ struct Bwd2Params {
     float *dv, *dw, *ds0;
     float* ck;                     // [BH][nch][Dv][Dk]
     float *pq, *pk, *pb, *pg;      // [NRB][BTH][Dk] each
-    // scalar gates (the gated delta rule as GDN-2 with alpha broadcast over
-    // the channels and erase = write = beta): alpha, beta [B,T,H] fp32 in,
-    // and per-token partials of dbeta (erase part, write part) and d log alpha
-    const float *alpha_s, *beta_s;
-    float *pbs, *pgs;              // [4 NRB][BTH]: per (row block, wave)
-    float* pws;                    // [2 NRB][BTH]: per (row block, row tile)
     bool l2norm;                   // q, k normalised on load (GDR_L2NORM_QK)
 };
 
@@ -128,60 +117,6 @@ struct BL3 {
     static_assert(A % 4 == 0 && W % 4 == 0 && (Y - A) % 4 == 0, "16-byte rows");
 };
 
-// acc += A B for one 16 x 16 tile over K = 16 NQ on the fp32 matrix cores.
-// Lane l holds D[4 (l / 16) + i][l % 16] in acc[i].  Operands from LDS:
-// A(m, k) = AR ? A[m pa + k] : A[k pa + m], B(k, n) = BR ? B[n pb + k] : B[k pb + n]
-// (NEG negates A).  Inside each 16-deep block, lane group g = l / 16 takes
-// k = 16 q + 4 g + e on the e-th instruction, so a row operand is one 16-byte
-// read per block and a column operand reads rows 4 apart across the groups.
-template <int NQ, bool AR, bool BR, bool NEG = false>
-__device__ __forceinline__ f32x4 mma16(f32x4 acc, const float* A, int pa, const float* B, int pb) {
-    const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const int kb = 16 * q + 4 * g;
-        f32x4 av, bv;
-        if constexpr (AR) {
-            av = ld4(A + l16 * pa + kb);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) av[e] = A[(kb + e) * pa + l16];
-        }
-        if constexpr (BR) {
-            bv = ld4(B + l16 * pb + kb);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) bv[e] = B[(kb + e) * pb + l16];
-        }
-        if constexpr (NEG) av = -av;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc, 0, 0, 0);
-    }
-    return acc;
-}
-
-__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// log2 of a decay gate, clamped as safe_log: 0 (or a denormal) maps to -126
-__device__ __forceinline__ float safe_log2(float a) {
-    return fmaxf(__builtin_amdgcn_logf(fmaxf(a, 1.17549435e-38f)), -126.f);
-}
-
-// sum over the 4 lanes of each aligned quad (DPP quad_perm xor 1, then xor 2)
-__device__ __forceinline__ float qsum(float x) {
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                0xB1, 0xF, 0xF, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                0x4E, 0xF, 0xF, false));
-    return x;
-}
-
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-}
-
 // One chunk's global inputs for one thread, as raw words: key-side rows
 // (token tid / 16, channels j0 .. j0 + NC) and a pair of state rows of w, v
 // and dL/do (token tid / 16, rows 2 (tid % 16), + 1).
@@ -192,21 +127,9 @@ struct Pre2 {
     static constexpr int WD = 2 / packed<TD>::PER_WORD;
     uint32_t k[WK], b[WK], a[WK], q[WK];
     uint32_t w[WP], v[WP], d[WD];
-    float as, bs;                  // scalar gates
 };
 
-// sum over the 16 lanes of each DPP row; every lane gets the sum
-__device__ __forceinline__ float rsum16(float x) {
-    x = qsum(x);
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                0x141, 0xF, 0xF, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                0x140, 0xF, 0xF, false));
-    return x;
-}
-
-// SC: scalar gates (alpha, beta per token, fp32), the gated delta rule.
-template <int DK, int DV, typename TIn, typename TD, bool SC>
+template <int DK, int DV, typename TIn, typename TD>
 __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
     using L = BL3<DK>;
     constexpr int NRB = DV / R2;
@@ -264,14 +187,9 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         if (tr < chunk_len(c)) {
             const int64_t tk = tok(c * C2 + tr);
             ldw(x.k, reinterpret_cast<const TIn*>(p.k) + tk * DK + j0);
-            if constexpr (SC) {
-                x.as = p.alpha_s[tk];
-                x.bs = p.beta_s[tk];
-            } else {
-                ldw(x.b, reinterpret_cast<const TIn*>(p.erase) + tk * DK + j0);
-                ldw(x.a, reinterpret_cast<const TIn*>(p.alpha) + tk * DK + j0);
-                ldw(x.w, reinterpret_cast<const TIn*>(p.write) + tk * DV + row0 + i2);
-            }
+            ldw(x.b, reinterpret_cast<const TIn*>(p.erase) + tk * DK + j0);
+            ldw(x.a, reinterpret_cast<const TIn*>(p.alpha) + tk * DK + j0);
+            ldw(x.w, reinterpret_cast<const TIn*>(p.write) + tk * DV + row0 + i2);
             if (bwd) ldw(x.q, reinterpret_cast<const TIn*>(p.q) + tk * DK + j0);
             ldw(x.v, reinterpret_cast<const TIn*>(p.v) + tk * DV + row0 + i2);
             if (bwd) ldw(x.d, reinterpret_cast<const TD*>(p.dout) + tk * DV + row0 + i2);
@@ -281,8 +199,6 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
     auto commit = [&](const PF& x, int64_t c, bool bwd) {
         const bool live = tr < chunk_len(c);
         const int at = tr * L::PK + j0;
-        float sg = 0.f;
-        if constexpr (SC) sg = live ? safe_log2(x.as) : 0.f;
         // GDR_L2NORM_QK: the 16 lanes of a token (one DPP row) hold its row
         float kn = 1.f, qn = 1.f;
         if (p.l2norm) {
@@ -304,13 +220,8 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             for (int e = 0; e < 4; ++e) {
                 const int y = y0 + e;
                 kv[e] = live ? packed<TIn>::at(x.k, y) * kn : 0.f;
-                if constexpr (SC) {
-                    bv[e] = live ? x.bs : 0.f;
-                    gv[e] = sg;
-                } else {
-                    bv[e] = live ? packed<TIn>::at(x.b, y) : 0.f;
-                    gv[e] = live ? safe_log2(packed<TIn>::at(x.a, y)) : 0.f;
-                }
+                bv[e] = live ? packed<TIn>::at(x.b, y) : 0.f;
+                gv[e] = live ? safe_log2(packed<TIn>::at(x.a, y)) : 0.f;
                 ev[e] = bv[e] * kv[e];
                 qv[e] = (live && bwd) ? packed<TIn>::at(x.q, y) * qn : 0.f;
             }
@@ -323,8 +234,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int o = tr * L::PR + i2 + e;
-            if constexpr (SC) Wsm[o] = live ? x.bs : 0.f;
-            else Wsm[o] = live ? packed<TIn>::at(x.w, e) : 0.f;
+            Wsm[o] = live ? packed<TIn>::at(x.w, e) : 0.f;
             Vsm[o] = live ? packed<TIn>::at(x.v, e) : 0.f;
             if (bwd) dOs[o] = live ? packed<TD>::at(x.d, e) : 0.f;
         }
@@ -615,15 +525,9 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * lg + i, o = r * L::PR + 16 * t + l16;
                 dRs[o] = acc[i];
-                float dwv = acc[i] * Vsm[o];
-                if constexpr (SC) dwv = rsum16(dwv);   // over this tile's 16 rows
                 if (r < n) {
                     const int64_t off = tok(t0 + r) * DV + row0 + 16 * t + l16;
-                    if constexpr (SC) {
-                        if (l16 == 0) p.pws[(2 * rb + t) * p.BTH + tok(t0 + r)] = dwv;
-                    } else {
-                        p.dw[off] = dwv;
-                    }
+                    p.dw[off] = acc[i] * Vsm[o];
                     p.dv[off] = acc[i] * Wsm[o];
                 }
             }
@@ -657,7 +561,6 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         }
         __syncthreads();   // dA
         const float* dAs = dTs;
-        f32x4 sb = zero4, sgl = zero4;   // scalar gates: this wave's channel sums
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
             const int t = CTW * wv + ct, cc = 16 * t + l16;
@@ -755,14 +658,8 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
                     const int64_t o = poff + tok(t0 + r) * DK + cc;
                     p.pq[o] = oq[i];
                     p.pk[o] = ok[i];
-                    if constexpr (!SC) {
-                        p.pb[o] = ob[i];
-                        p.pg[o] = dl[i];
-                    }
-                }
-                if constexpr (SC) {
-                    sb[i] += ob[i];
-                    sgl[i] += dl[i];
+                    p.pb[o] = ob[i];
+                    p.pg[o] = dl[i];
                 }
             }
             // ---- G' <- G' diag(lambda_C) + dO^T Q~ - dR^T E~ on this wave's
@@ -776,19 +673,6 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
                 acc = mma16<1, false, false, true>(acc, dRs + 16 * a, L::PR, Et + 16 * t, L::PK);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) Gs[(16 * a + 4 * lg + i) * L::PK + cc] = acc[i];
-            }
-        }
-        if constexpr (SC) {
-            // dbeta (erase part) and d log alpha: sums over this wave's channels
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float vb = rsum16(sb[i]), vg = rsum16(sgl[i]);
-                const int r = 4 * lg + i;
-                if (l16 == 0 && r < n) {
-                    const int64_t o = (int64_t)(4 * rb + wv) * p.BTH + tok(t0 + r);
-                    p.pbs[o] = vb;
-                    p.pgs[o] = vg;
-                }
             }
         }
     }
@@ -830,112 +714,10 @@ __global__ __launch_bounds__(256) void bwd2_reduce(int64_t n, const float* __res
     da[i] = d / fmaxf(ldf<TIn>(alpha, i), 1.17549435e-38f);
 }
 
-// scalar gates: dq, dk from the row blocks' partials
-template <int NRB>
-__global__ __launch_bounds__(256) void bwd_reduce_qk(int64_t n, const float* __restrict__ pq,
-                                                     const float* __restrict__ pk,
-                                                     float* __restrict__ dq,
-                                                     float* __restrict__ dk) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    float a = 0.f, b = 0.f;
-#pragma unroll
-    for (int r = 0; r < NRB; ++r) {
-        a += pq[r * n + i];
-        b += pk[r * n + i];
-    }
-    dq[i] = a;
-    dk[i] = b;
-}
-
-// scalar gates, per token: dbeta = erase part (per row block and wave) +
-// write part (per row block and row tile); dalpha = d log alpha / alpha
-template <int NRB>
-__global__ __launch_bounds__(256) void bwd_reduce_gates(int64_t n, const float* __restrict__ pbs,
-                                                        const float* __restrict__ pgs,
-                                                        const float* __restrict__ pws,
-                                                        const float* __restrict__ alpha,
-                                                        float* __restrict__ dbeta,
-                                                        float* __restrict__ dalpha) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    float b = 0.f, g = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4 * NRB; ++r) {
-        b += pbs[r * n + i];
-        g += pgs[r * n + i];
-    }
-#pragma unroll
-    for (int r = 0; r < 2 * NRB; ++r) b += pws[r * n + i];
-    dbeta[i] = b;
-    dalpha[i] = g / fmaxf(alpha[i], 1.17549435e-38f);
-}
-
-// GDR_L2NORM_QK: the kernel's dq, dk are gradients with respect to q_hat,
-// k_hat; one wave per (token, head) row adds the row blocks' partials and
-// applies the norm's reverse mode, dx = (dx_hat - x_hat (x_hat . dx_hat)) / n
-// with n = sqrt(|x|^2 + eps).  G2: derase and dalpha too (elementwise).
-template <int NRB, int DK, typename TIn, bool G2>
-__global__ __launch_bounds__(256) void bwd_reduce_rows_norm(
-    int64_t rows, const float* __restrict__ pq, const float* __restrict__ pk,
-    const float* __restrict__ pb, const float* __restrict__ pg, const void* q, const void* k,
-    const void* alpha, float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ db,
-    float* __restrict__ da) {
-    constexpr int E = DK / 64;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;   // whole waves
-    const int lane = threadIdx.x & 63;
-    const int64_t n = rows * DK;
-    float dqh[E], dkh[E], qv[E], kv[E];
-    float sq = 0.f, sk = 0.f, tq = 0.f, tk = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int64_t i = row * DK + lane + 64 * e;
-        float a = 0.f, b = 0.f;
-#pragma unroll
-        for (int r = 0; r < NRB; ++r) {
-            a += pq[r * n + i];
-            b += pk[r * n + i];
-        }
-        dqh[e] = a;
-        dkh[e] = b;
-        qv[e] = ldf<TIn>(q, i);
-        kv[e] = ldf<TIn>(k, i);
-        sq += qv[e] * qv[e];
-        sk += kv[e] * kv[e];
-        tq += qv[e] * a;
-        tk += kv[e] * b;
-        if constexpr (G2) {
-            float c = 0.f, d = 0.f;
-#pragma unroll
-            for (int r = 0; r < NRB; ++r) {
-                c += pb[r * n + i];
-                d += pg[r * n + i];
-            }
-            db[i] = c;
-            da[i] = d / fmaxf(ldf<TIn>(alpha, i), 1.17549435e-38f);
-        }
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        sq += __shfl_xor(sq, m, 64);
-        sk += __shfl_xor(sk, m, 64);
-        tq += __shfl_xor(tq, m, 64);
-        tk += __shfl_xor(tk, m, 64);
-    }
-    const float iq = l2_inv(sq), ik = l2_inv(sk);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int64_t i = row * DK + lane + 64 * e;
-        dq[i] = iq * (dqh[e] - qv[e] * iq * (tq * iq));
-        dk[i] = ik * (dkh[e] - kv[e] * ik * (tk * ik));
-    }
-}
-
-template <int DK, int DV, typename TIn, typename TD, bool SC>
+template <int DK, int DV, typename TIn, typename TD>
 hipError_t launch_main(const Bwd2Params& p, int64_t BH, hipStream_t st) {
     const size_t lds = sizeof(float) * BL3<DK>::TOTAL;
-    auto fn = chunk2_bwd_kernel<DK, DV, TIn, TD, SC>;
+    auto fn = chunk2_bwd_kernel<DK, DV, TIn, TD>;
     hipError_t e = hipFuncSetAttribute((const void*)fn,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -970,7 +752,7 @@ hipError_t launch_bwd2_t(const Bwd2Args& a) {
     p.pb = p.pk + NRB * BTH * DK;
     p.pg = p.pb + NRB * BTH * DK;
     p.l2norm = a.l2norm;
-    hipError_t e = launch_main<DK, DV, TIn, TD, false>(p, BH, a.stream);
+    hipError_t e = launch_main<DK, DV, TIn, TD>(p, BH, a.stream);
     if (e != hipSuccess) return e;
     if (a.l2norm) {
         hipLaunchKernelGGL((bwd_reduce_rows_norm<NRB, DK, TIn, true>),
@@ -985,50 +767,6 @@ hipError_t launch_bwd2_t(const Bwd2Args& a) {
     return hipGetLastError();
 }
 
-template <int DK, int DV, typename TIn, typename TD>
-hipError_t launch_bwd_t(const BwdArgs& a) {
-    constexpr int NRB = DV / R2;
-    const int64_t BH = a.B * a.H, BTH = a.B * a.T * a.H;
-    const int64_t nch = (a.T + C2 - 1) / C2;
-    Bwd2Params p{};
-    p.T = a.T;
-    p.H = a.H;
-    p.BTH = BTH;
-    p.q = a.q;
-    p.k = a.k;
-    p.v = a.v;
-    p.dout = a.dout;
-    p.s0 = a.s0;
-    p.dsf = a.ds_final;
-    p.dv = a.dv;
-    p.ds0 = a.ds0;
-    p.alpha_s = a.alpha;
-    p.beta_s = a.beta;
-    p.ck = reinterpret_cast<float*>(a.workspace);
-    p.pq = p.ck + BH * nch * DV * DK;
-    p.pk = p.pq + NRB * BTH * DK;
-    p.pbs = p.pk + NRB * BTH * DK;
-    p.pgs = p.pbs + 4 * NRB * BTH;
-    p.pws = p.pgs + 4 * NRB * BTH;
-    p.l2norm = a.l2norm;
-    hipError_t e = launch_main<DK, DV, TIn, TD, true>(p, BH, a.stream);
-    if (e != hipSuccess) return e;
-    const int64_t nqk = BTH * DK;
-    if (a.l2norm) {
-        hipLaunchKernelGGL((bwd_reduce_rows_norm<NRB, DK, TIn, false>),
-                           dim3((unsigned)((BTH + 3) / 4)), dim3(256), 0, a.stream, BTH, p.pq, p.pk,
-                           nullptr, nullptr, a.q, a.k, nullptr, a.dq, a.dk, nullptr, nullptr);
-    } else {
-        hipLaunchKernelGGL((bwd_reduce_qk<NRB>), dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0,
-                           a.stream, nqk, p.pq, p.pk, a.dq, a.dk);
-    }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_reduce_gates<NRB>), dim3((unsigned)((BTH + 255) / 256)), dim3(256), 0,
-                       a.stream, BTH, p.pbs, p.pgs, p.pws, a.alpha, a.dbeta, a.dalpha);
-    return hipGetLastError();
-}
-
 template <int DK, int DV>
 hipError_t launch_bwd2_d(const Bwd2Args& a) {
     if (a.in_bf16)
@@ -1036,15 +774,6 @@ hipError_t launch_bwd2_d(const Bwd2Args& a) {
                            : launch_bwd2_t<DK, DV, bf16_t, float>(a);
     return a.dout_bf16 ? launch_bwd2_t<DK, DV, float, bf16_t>(a)
                        : launch_bwd2_t<DK, DV, float, float>(a);
-}
-
-template <int DK, int DV>
-hipError_t launch_bwd_d(const BwdArgs& a) {
-    if (a.in_bf16)
-        return a.dout_bf16 ? launch_bwd_t<DK, DV, bf16_t, bf16_t>(a)
-                           : launch_bwd_t<DK, DV, bf16_t, float>(a);
-    return a.dout_bf16 ? launch_bwd_t<DK, DV, float, bf16_t>(a)
-                       : launch_bwd_t<DK, DV, float, float>(a);
 }
 
 }  // namespace
@@ -1055,25 +784,11 @@ size_t bwd2_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t
     return sizeof(float) * (size_t)(B * H * nch * Dv * Dk + 4 * nrb * B * T * H * Dk);
 }
 
-size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv) {
-    const int64_t nch = (T + C2 - 1) / C2;
-    const int64_t nrb = Dv / R2;
-    const int64_t BTH = B * T * H;
-    return sizeof(float) * (size_t)(B * H * nch * Dv * Dk + 2 * nrb * BTH * Dk + 10 * nrb * BTH);
-}
-
 hipError_t launch_chunk2_bwd(const Bwd2Args& a) {
     if (a.Dk == 128 && a.Dv == 128) return launch_bwd2_d<128, 128>(a);
     if (a.Dk == 128 && a.Dv == 64) return launch_bwd2_d<128, 64>(a);
     if (a.Dk == 64 && a.Dv == 128) return launch_bwd2_d<64, 128>(a);
     return launch_bwd2_d<64, 64>(a);
-}
-
-hipError_t launch_chunk_bwd(const BwdArgs& a) {
-    if (a.Dk == 128 && a.Dv == 128) return launch_bwd_d<128, 128>(a);
-    if (a.Dk == 128 && a.Dv == 64) return launch_bwd_d<128, 64>(a);
-    if (a.Dk == 64 && a.Dv == 128) return launch_bwd_d<64, 128>(a);
-    return launch_bwd_d<64, 64>(a);
 }
 
 }  // namespace gdr

@@ -1,0 +1,812 @@
+// gdr_chunk_bwd: reverse mode of the gated delta rule with scalar gates
+// (alpha_t, beta_t per token and head), chunk by chunk, in fp32.
+//
+// Per chunk of n <= 16 tokens ("Gated Delta Networks", Method; the chunkwise
+// form of the GDN review, section 3.7), with G_r the within-chunk cumulative
+// log alpha, lambda_r = e^{G_r}, rho_r = lambda_C / lambda_r (lambda_C of the
+// last token) and Gamma_rs = e^{G_r - G_s} (s <= r), the forward is
+//
+//   A_rs = beta_r Gamma_rs (k_r . k_s) (s < r),   P_rs = Gamma_rs (q_r . k_s) (s <= r)
+//   T = (I + A)^{-1},  X = V - diag(lambda) K S^T,  R = diag(beta) X,  U = T R
+//   O = diag(lambda) Q S^T + P U,   S' = lambda_C S + (diag(rho) U)^T K.
+//
+// Every decay is a scalar per token, so the reverse mode needs no table per
+// channel: with G' = dL/dS' carried back from the next chunk,
+//
+//   dU = P^T dO + diag(rho) K G'^T,  dR = T^T dU,  dP = dO U^T (s <= r),
+//   dA = -T^T (dU R^T) T^T (s < r),  dv = diag(beta) dR,
+//   D_P = dP (.) Gamma,  D_A = dA (.) Gamma,  M_rs = beta_r D_A,rs + beta_s D_A,sr,
+//   dq = D_P K + (diag(lambda) dO) S,
+//   dk = M K + D_P^T Q + (diag(rho) U) G' - (diag(beta lambda) dR) S,
+//   G  = lambda_C G' + (diag(lambda) dO)^T Q - (diag(beta lambda) dR)^T K,
+//
+// and the gate gradients are sums per token:
+//
+//   dbeta_r = sum_i dR_ri X_ri + sum_s dA_rs Gamma_rs (k_r . k_s),
+//   dlog alpha_t = sum_{r >= t} tau_r + sum_{r < t} kappa_r + lambda_C <G', S>
+//                  + sum_{r >= t > s} (dA_rs A_rs + dP_rs P_rs),
+//   tau_r = -beta_r sum_i dR_ri (V_ri - X_ri) + sum_c q_rc ((diag(lambda) dO) S)_rc,
+//   kappa_r = rho_r sum_i U_ri (K G'^T)_ri,
+//
+// (lambda_r depends on alpha_t for t <= r, rho_r for r < t, Gamma_rs for
+// s < t <= r, lambda_C for every token of the chunk).  The pair sum takes
+// each (r, s) once, so nothing cancels.
+//
+// Work split: one 256-thread workgroup (4 waves) per (b, h, 32 state rows),
+// two workgroups per CU (about 78 KB of LDS each).  It runs the forward over
+// its rows (chunk-start states to the workspace), then walks the chunks in
+// reverse.  dv and dS_0 are final per workgroup; dq, dk, dbeta and d log alpha
+// go to per-row-block partials (every term is linear in the row block's
+// share of dU, dR, dP and dA) that a second kernel adds.  Every product is a
+// set of 16 x 16 tiles on the fp32 matrix cores (v_mfma_f32_16x16x4f32),
+// the triangular solve and the elementwise terms are vector ALU.  Each wave
+// forms the chunk's gate scalars itself (a DPP scan of log2 alpha across the
+// 16 lanes of each row), so the gates cost no barrier.
+#include "gdr_device.h"
+#include "launch.h"
+#include "vtile.h"
+
+namespace gdr {
+
+namespace {
+
+constexpr int CB = 16;    // tokens per chunk
+constexpr int RBW = 32;   // state rows per workgroup
+constexpr int NTB = 256;  // threads per workgroup
+
+struct BwdParams {
+    int64_t T, H, BTH;
+    const void *q, *k, *v, *dout;
+    const float *alpha, *beta, *s0, *dsf;
+    float *dv, *ds0;
+    float* ck;                     // [BH][nch][Dv][Dk] chunk-start states
+    float *pq, *pk;                // [NRB][BTH][Dk]
+    float *pb, *pg;                // [NRB][BTH]: dbeta, d log alpha
+    bool l2norm;                   // q, k normalised on load (GDR_L2NORM_QK)
+};
+
+// LDS tables (floats).  Pitches as in the GDN-2 backward: key-side rows
+// PK = 4 (mod 64), n x n PC = 20, n x rows PR = 36, so the row (16-byte) and
+// column (4-byte) operand reads of mma16 are free of bank conflicts.
+template <int DK>
+struct BL {
+    static constexpr int PK = DK + 4;
+    static constexpr int PC = 20;
+    static constexpr int PR = 36;
+    static constexpr int NK = CB * PK;           // one token x key-dim table
+    static constexpr int NN = CB * PC;           // one n x n tile
+    static constexpr int NR = CB * PR;           // one n x rows tile
+    static constexpr int K = 0;
+    static constexpr int Q = K + NK;
+    static constexpr int S = Q + NK;             // [RBW][PK] chunk-start state rows
+    static constexpr int G = S + RBW * PK;       // [RBW][PK] dL/dS' rows
+    static constexpr int AK = G + RBW * PK;      // Gamma (.) K K^T, s < r
+    static constexpr int TM = AK + NN;           // T
+    static constexpr int P = TM + NN;
+    static constexpr int DP = P + NN;            // D_P
+    static constexpr int DA = DP + NN;           // dU R^T, then D_A
+    static constexpr int Y = DA + NN;            // (dU R^T) T^T, then M
+    static constexpr int V = Y + NN;
+    static constexpr int X = V + NR;
+    static constexpr int R = X + NR;
+    static constexpr int DO = R + NR;            // dL/do, then diag(lambda) dL/do
+    static constexpr int U = DO + NR;
+    static constexpr int UT = U + NR;            // diag(rho) U
+    static constexpr int DU = UT + NR;
+    static constexpr int KG = DU + NR;           // K G'^T
+    static constexpr int DRB = KG + NR;          // diag(beta lambda) dR
+    static constexpr int SC = DRB + NR;          // per-token partial sums:
+    static constexpr int TAUR = SC;              //   [2 row tiles][16] dR terms of tau
+    static constexpr int BER = TAUR + 32;        //   [2][16] sum_i dR X
+    static constexpr int KAP = BER + 32;         //   [2][16] kappa
+    static constexpr int TAUO = KAP + 32;        //   [4 waves][16] dO terms of tau
+    static constexpr int BEA = TAUO + 64;        //   [16] A term of dbeta
+    static constexpr int PRA = BEA + 16;         //   [16] pair sums of dA (.) A
+    static constexpr int PRP = PRA + 16;         //   [16] pair sums of dP (.) P
+    static constexpr int GSUM = PRP + 16;        //   lambda_C <G', S>
+    static constexpr int TOTAL = GSUM + 4;
+    static_assert(TOTAL * 4 <= 80 * 1024, "two workgroups per CU");
+    static_assert(PK % 64 == 4 && NK % 4 == 0 && S % 4 == 0 && G % 4 == 0, "pitches");
+    static_assert(AK % 4 == 0 && V % 4 == 0 && SC % 4 == 0, "16-byte rows");
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// inclusive prefix sum over the 16 lanes of each DPP row (row_shr 1, 2, 4, 8;
+// lanes shifted in from outside the row add 0)
+__device__ __forceinline__ float rscan16(float x) {
+    x += dpp<0x111>(x);
+    x += dpp<0x112>(x);
+    x += dpp<0x114>(x);
+    x += dpp<0x118>(x);
+    return x;
+}
+
+// inclusive suffix sum over the 16 lanes of each DPP row (row_shl 1, 2, 4, 8)
+__device__ __forceinline__ float rsuffix16(float x) {
+    x += dpp<0x101>(x);
+    x += dpp<0x102>(x);
+    x += dpp<0x104>(x);
+    x += dpp<0x108>(x);
+    return x;
+}
+
+__device__ __forceinline__ float lane_value(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// One chunk's global inputs for one thread, as raw words: key-side rows
+// (token tid / 16, channels j0 .. j0 + NC), a pair of state rows of v and
+// dL/do (token tid / 16, rows 2 (tid % 16), + 1), and the gates of token
+// lane % 16.
+template <typename TIn, typename TD, int NC>
+struct Pre {
+    static constexpr int WK = NC / packed<TIn>::PER_WORD;
+    static constexpr int WP = 2 / packed<TIn>::PER_WORD;
+    static constexpr int WD = 2 / packed<TD>::PER_WORD;
+    uint32_t k[WK], q[WK];
+    uint32_t v[WP], d[WD];
+    float a, b;
+};
+
+// The chunk's gate scalars in one wave.  Lane l holds those of token l % 16;
+// the r-arrays those of token r = 4 (l / 16) + i, the rows of an
+// accumulator tile.
+struct Gates {
+    float be, G, lam, rho, lamC;
+    float br[4], Gr[4], lr[4], rr[4];
+};
+
+template <int DK, int DV, typename TIn, typename TD>
+__global__ __launch_bounds__(NTB) __attribute__((amdgpu_waves_per_eu(2)))
+void gdn_bwd_kernel(BwdParams p) {
+    using L = BL<DK>;
+    constexpr int NRB = DV / RBW;
+    constexpr int NC = DK / 16;
+    constexpr int NQK = DK / 16;                // 16-deep blocks over the key dim
+    constexpr int CTW = DK / 64;                // channel tiles per wave
+    constexpr int NSV = RBW * DK / 4 / NTB;     // 16-byte state pieces per thread
+    constexpr int NSW = RBW * DK / 4 / 64;      // .. per lane of one wave
+    extern __shared__ __align__(16) float sm[];
+    float* Ks = sm + L::K;
+    float* Qs = sm + L::Q;
+    float* Ss = sm + L::S;
+    float* Gs = sm + L::G;
+    float* AKs = sm + L::AK;
+    float* Ts = sm + L::TM;
+    float* Ps = sm + L::P;
+    float* DPs = sm + L::DP;
+    float* DAs = sm + L::DA;
+    float* Ys = sm + L::Y;
+    float* Vs = sm + L::V;
+    float* Xs = sm + L::X;
+    float* Rs = sm + L::R;
+    float* DOs = sm + L::DO;
+    float* Us = sm + L::U;
+    float* UTs = sm + L::UT;
+    float* DUs = sm + L::DU;
+    float* KGs = sm + L::KG;
+    float* DRBs = sm + L::DRB;
+
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6;
+    // lane indices, renewed at the top of every chunk through an opaque copy
+    // so that the many LDS addresses formed from them are computed where they
+    // are used rather than hoisted out of the chunk loops into registers
+    int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+    auto renew_lane = [&]() {
+        asm volatile("" : "+v"(lane));
+        l16 = lane & 15;
+        lg = lane >> 4;
+    };
+    // the row blocks of a head on one XCD (blocks are dealt to the 8 XCDs in
+    // turn): they read the same key-side rows
+    const int64_t nb = gridDim.x;
+    const int64_t wid = (nb % (8 * NRB) == 0) ? (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8
+                                              : (int64_t)blockIdx.x;
+    const int rb = (int)(wid % NRB);
+    const int64_t bh = wid / NRB;
+    const int64_t h = bh % p.H;
+    const int64_t b = bh / p.H;
+    const int64_t T = p.T, H = p.H;
+    const int row0 = rb * RBW;
+    const int64_t nch = (T + CB - 1) / CB;
+    float* ckb = p.ck + bh * nch * DV * DK;
+    auto tok = [&](int64_t t) { return (b * T + t) * H + h; };
+    const int tr = tid >> 4;                   // this thread's token for the loads
+    const int j0 = NC * (tid & 15);            // .. and its key channels
+    const int i2 = 2 * (tid & 15);             // .. and its pair of state rows
+    auto chunk_len = [&](int64_t c) { return (int)min((int64_t)CB, T - c * CB); };
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+    using PF = Pre<TIn, TD, NC>;
+    auto fetch = [&](PF& x, int64_t c, bool bwd) {
+        const int n = chunk_len(c);
+        if (tr < n) {
+            const int64_t tk = tok(c * CB + tr);
+            ldw(x.k, reinterpret_cast<const TIn*>(p.k) + tk * DK + j0);
+            if (bwd) ldw(x.q, reinterpret_cast<const TIn*>(p.q) + tk * DK + j0);
+            ldw(x.v, reinterpret_cast<const TIn*>(p.v) + tk * DV + row0 + i2);
+            if (bwd) ldw(x.d, reinterpret_cast<const TD*>(p.dout) + tk * DV + row0 + i2);
+        }
+        // tokens past the end: alpha = 1, beta = 0
+        x.a = 1.f;
+        x.b = 0.f;
+        if (l16 < n) {
+            const int64_t tg = tok(c * CB + l16);
+            x.a = p.alpha[tg];
+            x.b = p.beta[tg];
+        }
+    };
+    // rows >= n: zero tokens
+    auto commit = [&](const PF& x, int64_t c, bool bwd) {
+        const bool live = tr < chunk_len(c);
+        const int at = tr * L::PK + j0;
+        // GDR_L2NORM_QK: the 16 lanes of a token (one DPP row) hold its row
+        float kn = 1.f, qn = 1.f;
+        if (p.l2norm) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int y = 0; y < NC; ++y) {
+                const float kk = live ? packed<TIn>::at(x.k, y) : 0.f;
+                const float qq = (live && bwd) ? packed<TIn>::at(x.q, y) : 0.f;
+                sk += kk * kk;
+                sq += qq * qq;
+            }
+            kn = l2_inv(rsum16(sk));
+            qn = l2_inv(rsum16(sq));
+        }
+#pragma unroll
+        for (int y0 = 0; y0 < NC; y0 += 4) {
+            f32x4 kv, qv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kv[e] = live ? packed<TIn>::at(x.k, y0 + e) * kn : 0.f;
+                qv[e] = (live && bwd) ? packed<TIn>::at(x.q, y0 + e) * qn : 0.f;
+            }
+            *reinterpret_cast<f32x4*>(Ks + at + y0) = kv;
+            if (bwd) *reinterpret_cast<f32x4*>(Qs + at + y0) = qv;
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int o = tr * L::PR + i2 + e;
+            Vs[o] = live ? packed<TIn>::at(x.v, e) : 0.f;
+            if (bwd) DOs[o] = live ? packed<TD>::at(x.d, e) : 0.f;
+        }
+    };
+    auto gates = [&](const PF& x) {
+        Gates g;
+        g.be = x.b;
+        g.G = rscan16(safe_log2(x.a));
+        const float GC = lane_value(g.G, 15);
+        g.lam = ex2(g.G);
+        g.rho = ex2(GC - g.G);
+        g.lamC = ex2(GC);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * lg + i;
+            g.br[i] = __shfl(g.be, r, 64);
+            g.Gr[i] = __shfl(g.G, r, 64);
+            g.lr[i] = __shfl(g.lam, r, 64);
+            g.rr[i] = __shfl(g.rho, r, 64);
+        }
+        return g;
+    };
+    // Gamma at the accumulator entries (r, s = l16), masked to s < r or s <= r
+    auto gamma = [&](const Gates& g, bool strict) {
+        f32x4 gm;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * lg + i;
+            gm[i] = (strict ? l16 < r : l16 <= r) ? ex2(g.Gr[i] - g.G) : 0.f;
+        }
+        return gm;
+    };
+    // sum over the pairs s < t <= r of W_rs (accumulator layout), for t = l16
+    auto straddle = [&](const f32x4& w) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float e = rscan16(w[i]) - w[i];   // sum over s < l16 of W_rs
+            if (4 * lg + i >= l16) acc += e;
+        }
+        acc += __shfl_xor(acc, 16, 64);
+        acc += __shfl_xor(acc, 32, 64);
+        return acc;
+    };
+    // A = diag(beta) AK, K K^T scaled by Gamma below the diagonal (wave 0)
+    auto ak_tile = [&](const Gates& g) {
+        const f32x4 kk = mma16<NQK, true, true>(zero4, Ks, L::PK, Ks, L::PK, lane);
+        const f32x4 gm = gamma(g, true);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) AKs[(4 * lg + i) * L::PC + l16] = kk[i] * gm[i];
+    };
+    // T = (I + A)^{-1} by one wave: lane 4 c + q owns column c and the rows
+    // m = q (mod 4); row r of the column is delta_rc - beta_r sum_{m < r}
+    // AK_rm T_mc (AK's upper part is zero), the four partial sums joined by
+    // a quad reduction
+    auto tsolve = [&](const Gates& g) {
+        const int c = lane >> 2, q = lane & 3;
+        float tq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < CB; ++r) {
+            float part = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) part += AKs[r * L::PC + 4 * j + q] * tq[j];
+            part = qsum(part);
+            const float t = r < c ? 0.f : (r == c ? 1.f : 0.f) - lane_value(g.be, r) * part;
+            if ((r & 3) == q) tq[r >> 2] = t;
+            if (q == 0) Ts[r * L::PC + c] = t;
+        }
+    };
+    // K S^T (or K G'^T) for state-row tile t
+    auto ks_tile = [&](const float* M, int t) {
+        return mma16<NQK, true, true>(zero4, Ks, L::PK, M + 16 * t * L::PK, L::PK, lane);
+    };
+
+    // ======================= forward: chunk-start states =====================
+    {
+        f32x4 sv[NSV];
+#pragma unroll
+        for (int it = 0; it < NSV; ++it) {
+            const int e4 = tid + it * NTB;
+            const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
+            sv[it] = p.s0 ? *reinterpret_cast<const f32x4*>(p.s0 + (bh * DV + row0 + i) * DK + j)
+                          : zero4;
+            *reinterpret_cast<f32x4*>(Ss + i * L::PK + j) = sv[it];
+        }
+    }
+    PF x;
+    fetch(x, 0, false);
+    for (int64_t c = 0; c < nch; ++c) {
+        renew_lane();
+        __syncthreads();
+        commit(x, c, false);
+        const Gates g = gates(x);
+        if (c + 1 < nch) fetch(x, c + 1, false);
+        __syncthreads();
+        // wave 0: A and T;  waves 1, 2: R;  wave 3: S to the workspace
+        if (wv == 0) {
+            ak_tile(g);
+            wave_sync();
+            tsolve(g);
+        } else if (wv <= 2) {
+            const int t = wv - 1;
+            const f32x4 ks = ks_tile(Ss, t);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int o = (4 * lg + i) * L::PR + 16 * t + l16;
+                Rs[o] = g.br[i] * (Vs[o] - g.lr[i] * ks[i]);
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < NSW; ++it) {
+                const int e4 = lane + 64 * it;
+                const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
+                *reinterpret_cast<f32x4*>(ckb + (c * DV + row0 + i) * DK + j) =
+                    ld4(Ss + i * L::PK + j);
+            }
+        }
+        __syncthreads();
+        // diag(rho) T R (waves 0, 1)
+        if (wv < 2) {
+            const int t = wv;
+            const f32x4 u = mma16<1, true, false>(zero4, Ts, L::PC, Rs + 16 * t, L::PR, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) UTs[(4 * lg + i) * L::PR + 16 * t + l16] = g.rr[i] * u[i];
+        }
+        __syncthreads();
+        // S <- lambda_C S + (diag(rho) U)^T K on this wave's channel tiles
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+            const int t = CTW * wv + ct, cc = 16 * t + l16;
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                f32x4 acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = Ss[(16 * a + 4 * lg + i) * L::PK + cc] * g.lamC;
+                acc = mma16<1, false, false>(acc, UTs + 16 * a, L::PR, Ks + 16 * t, L::PK, lane);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Ss[(16 * a + 4 * lg + i) * L::PK + cc] = acc[i];
+            }
+        }
+    }
+
+    // ======================= reverse sweep ====================================
+    __syncthreads();
+    {
+        f32x4 gv[NSV];
+#pragma unroll
+        for (int it = 0; it < NSV; ++it) {
+            const int e4 = tid + it * NTB;
+            const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
+            gv[it] = p.dsf ? *reinterpret_cast<const f32x4*>(p.dsf + (bh * DV + row0 + i) * DK + j)
+                           : zero4;
+            *reinterpret_cast<f32x4*>(Gs + i * L::PK + j) = gv[it];
+        }
+    }
+    const int64_t poff = (int64_t)rb * p.BTH * DK;
+    // the gate gradients of chunk cp from the per-token partial sums (one
+    // wave; lane l sums token l % 16's partials, DPP scans over the tokens)
+    auto finalize = [&](int64_t cp) {
+        const int t = l16;
+        const float tau = sm[L::TAUR + t] + sm[L::TAUR + 16 + t] + sm[L::TAUO + t] +
+                          sm[L::TAUO + 16 + t] + sm[L::TAUO + 32 + t] + sm[L::TAUO + 48 + t];
+        const float kap = sm[L::KAP + t] + sm[L::KAP + 16 + t];
+        // sum_{r >= t} tau_r + sum_{r < t} kappa_r
+        const float dl = rsuffix16(tau) + (rscan16(kap) - kap) + sm[L::GSUM] + sm[L::PRA + t] +
+                         sm[L::PRP + t];
+        const float db = sm[L::BER + t] + sm[L::BER + 16 + t] + sm[L::BEA + t];
+        if (lane < 16 && t < chunk_len(cp)) {
+            const int64_t o = (int64_t)rb * p.BTH + tok(cp * CB + t);
+            p.pb[o] = db;
+            p.pg[o] = dl;
+        }
+    };
+    f32x4 sv[NSV];
+    auto fetch_s = [&](int64_t c) {
+#pragma unroll
+        for (int it = 0; it < NSV; ++it) {
+            const int e4 = tid + it * NTB;
+            const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
+            sv[it] = *reinterpret_cast<const f32x4*>(ckb + (c * DV + row0 + i) * DK + j);
+        }
+    };
+    fetch(x, nch - 1, true);
+    fetch_s(nch - 1);
+    for (int64_t c = nch - 1; c >= 0; --c) {
+        const int64_t t0 = c * CB;
+        const int n = chunk_len(c);
+        renew_lane();
+        __syncthreads();
+        if (c + 1 < nch && wv == 3) finalize(c + 1);
+#pragma unroll
+        for (int it = 0; it < NSV; ++it) {
+            const int e4 = tid + it * NTB;
+            const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
+            *reinterpret_cast<f32x4*>(Ss + i * L::PK + j) = sv[it];
+        }
+        commit(x, c, true);
+        const Gates g = gates(x);
+        if (c > 0) {
+            fetch(x, c - 1, true);
+            fetch_s(c - 1);
+        }
+        __syncthreads();
+        // ---- wave 0: A, then T;  wave 1: P and K G'^T rows 0..15;
+        //      wave 2: X, R rows 0..15 and K G'^T rows 16..31;
+        //      wave 3: X, R rows 16..31 and lambda_C <G', S>
+        if (wv == 0) {
+            ak_tile(g);
+            wave_sync();
+            tsolve(g);
+        } else if (wv == 1) {
+            const f32x4 qk = mma16<NQK, true, true>(zero4, Qs, L::PK, Ks, L::PK, lane);
+            const f32x4 gm = gamma(g, false);
+            const f32x4 kg = ks_tile(Gs, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i;
+                Ps[r * L::PC + l16] = qk[i] * gm[i];
+                KGs[r * L::PR + l16] = kg[i];
+            }
+        } else {
+            const int t = wv - 2;
+            const f32x4 ks = ks_tile(Ss, t);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int o = (4 * lg + i) * L::PR + 16 * t + l16;
+                const float xv = Vs[o] - g.lr[i] * ks[i];
+                Xs[o] = xv;
+                Rs[o] = g.br[i] * xv;
+            }
+            if (wv == 2) {
+                const f32x4 kg = ks_tile(Gs, 1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) KGs[(4 * lg + i) * L::PR + 16 + l16] = kg[i];
+            } else {
+                float s = 0.f;
+#pragma unroll
+                for (int j = 0; j < DK / 64; ++j) {
+                    const int cc = lane + 64 * j;
+#pragma unroll 8
+                    for (int i = 0; i < RBW; ++i) s += Gs[i * L::PK + cc] * Ss[i * L::PK + cc];
+                }
+#pragma unroll
+                for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+                if (lane == 0) sm[L::GSUM] = g.lamC * s;
+            }
+        }
+        __syncthreads();
+        // ---- U = T R and kappa (waves 0, 1);
+        //      dU = diag(rho) K G'^T + P^T dO (waves 2, 3)
+        if (wv < 2) {
+            const int t = wv;
+            const f32x4 u = mma16<1, true, false>(zero4, Ts, L::PC, Rs + 16 * t, L::PR, lane);
+            float kp[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int o = (4 * lg + i) * L::PR + 16 * t + l16;
+                const float ut = g.rr[i] * u[i];
+                Us[o] = u[i];
+                UTs[o] = ut;
+                kp[i] = rsum16(ut * KGs[o]);
+            }
+            if (l16 == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm[L::KAP + 16 * t + 4 * lg + i] = kp[i];
+            }
+        } else {
+            const int t = wv - 2;
+            f32x4 acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = g.rr[i] * KGs[(4 * lg + i) * L::PR + 16 * t + l16];
+            acc = mma16<1, false, false>(acc, Ps, L::PC, DOs + 16 * t, L::PR, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) DUs[(4 * lg + i) * L::PR + 16 * t + l16] = acc[i];
+        }
+        __syncthreads();
+        // ---- dR = T^T dU (waves 0, 1: dv to HBM, dbeta and tau row sums);
+        //      dP = dO U^T, D_P, pair sums, then dO -> diag(lambda) dO (wave 2);
+        //      dU R^T (wave 3)
+        if (wv < 2) {
+            const int t = wv;
+            const f32x4 dr = mma16<1, false, false>(zero4, Ts, L::PC, DUs + 16 * t, L::PR, lane);
+            float sb[4], st[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i, o = r * L::PR + 16 * t + l16;
+                DRBs[o] = g.br[i] * g.lr[i] * dr[i];
+                const float xv = Xs[o];
+                sb[i] = rsum16(dr[i] * xv);
+                st[i] = rsum16(dr[i] * (Vs[o] - xv));
+                if (r < n) p.dv[tok(t0 + r) * DV + row0 + 16 * t + l16] = g.br[i] * dr[i];
+            }
+            if (l16 == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sm[L::BER + 16 * t + 4 * lg + i] = sb[i];
+                    sm[L::TAUR + 16 * t + 4 * lg + i] = -g.br[i] * st[i];
+                }
+            }
+        } else if (wv == 2) {
+            const f32x4 dp = mma16<2, true, true>(zero4, DOs, L::PR, Us, L::PR, lane);
+            const f32x4 gm = gamma(g, false);
+            f32x4 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i;
+                const bool m = l16 <= r;
+                w[i] = m ? dp[i] * Ps[r * L::PC + l16] : 0.f;
+                DPs[r * L::PC + l16] = m ? dp[i] * gm[i] : 0.f;
+            }
+            const float pr = straddle(w);
+            if (lane < 16) sm[L::PRP + lane] = pr;
+            // only this wave reads dL/do in this phase
+#pragma unroll
+            for (int e = 0; e < CB * RBW / 64; ++e) {
+                const int idx = lane + 64 * e, r = idx / RBW, i = idx % RBW;
+                DOs[r * L::PR + i] *= __shfl(g.lam, r, 64);
+            }
+        } else {
+            const f32x4 dt = mma16<2, true, true>(zero4, DUs, L::PR, Rs, L::PR, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i;
+                DAs[r * L::PC + l16] = l16 < r ? dt[i] : 0.f;
+            }
+        }
+        __syncthreads();
+        // ---- wave 0 first: Y = (dU R^T) T^T, dA = -T^T Y (strict), D_A, the
+        //      A term of dbeta, its pair sums and M
+        if (wv == 0) {
+            const f32x4 y = mma16<1, true, true>(zero4, DAs, L::PC, Ts, L::PC, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Ys[(4 * lg + i) * L::PC + l16] = y[i];
+            wave_sync();
+            const f32x4 da = mma16<1, false, false, true>(zero4, Ts, L::PC, Ys, L::PC, lane);
+            const f32x4 gm = gamma(g, true);
+            f32x4 w;
+            float sb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i;
+                const float dv = l16 < r ? da[i] : 0.f;
+                const float ak = dv * AKs[r * L::PC + l16];
+                w[i] = g.br[i] * ak;
+                sb[i] = rsum16(ak);
+                DAs[r * L::PC + l16] = dv * gm[i];
+            }
+            const float pr = straddle(w);
+            if (lane < 16) sm[L::PRA + lane] = pr;
+            if (l16 == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm[L::BEA + 4 * lg + i] = sb[i];
+            }
+            wave_sync();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i;
+                Ys[r * L::PC + l16] = g.br[i] * DAs[r * L::PC + l16] + g.be * DAs[l16 * L::PC + r];
+            }
+        }
+        // ---- this wave's channel tiles: dq; dk but for M K; the dO terms of
+        //      tau; then G' <- lambda_C G' + (lambda dO)^T Q - (beta lambda dR)^T K
+        //      (only this wave reads these channels of G' from here on)
+        f32x4 dk[CTW];
+        float tq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+            const int t = CTW * wv + ct, cc = 16 * t + l16;
+            f32x4 dq = mma16<2, true, false>(zero4, DOs, L::PR, Ss + 16 * t, L::PK, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tq[i] += dq[i] * Qs[(4 * lg + i) * L::PK + cc];
+            dq = mma16<1, true, false>(dq, DPs, L::PC, Ks + 16 * t, L::PK, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i;
+                if (r < n) p.pq[poff + tok(t0 + r) * DK + cc] = dq[i];
+            }
+            f32x4 a = mma16<2, true, false>(zero4, UTs, L::PR, Gs + 16 * t, L::PK, lane);
+            a = mma16<2, true, false, true>(a, DRBs, L::PR, Ss + 16 * t, L::PK, lane);
+            dk[ct] = mma16<1, false, false>(a, DPs, L::PC, Qs + 16 * t, L::PK, lane);
+#pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2) {
+                f32x4 acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[i] = Gs[(16 * a2 + 4 * lg + i) * L::PK + cc] * g.lamC;
+                acc = mma16<1, false, false>(acc, DOs + 16 * a2, L::PR, Qs + 16 * t, L::PK, lane);
+                acc = mma16<1, false, false, true>(acc, DRBs + 16 * a2, L::PR, Ks + 16 * t, L::PK, lane);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Gs[(16 * a2 + 4 * lg + i) * L::PK + cc] = acc[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tq[i] = rsum16(tq[i]);
+        if (l16 == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm[L::TAUO + 16 * wv + 4 * lg + i] = tq[i];
+        }
+        __syncthreads();   // M
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+            const int t = CTW * wv + ct, cc = 16 * t + l16;
+            dk[ct] = mma16<1, true, false>(dk[ct], Ys, L::PC, Ks + 16 * t, L::PK, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i;
+                if (r < n) p.pk[poff + tok(t0 + r) * DK + cc] = dk[ct][i];
+            }
+        }
+    }
+    __syncthreads();
+    if (wv == 3) finalize(0);
+    if (p.ds0) {
+#pragma unroll
+        for (int it = 0; it < NSV; ++it) {
+            const int e4 = tid + it * NTB;
+            const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
+            *reinterpret_cast<f32x4*>(p.ds0 + (bh * DV + row0 + i) * DK + j) =
+                ld4(Gs + i * L::PK + j);
+        }
+    }
+}
+
+// dq, dk from the row blocks' partials
+template <int NRB>
+__global__ __launch_bounds__(256) void bwd_reduce_qk(int64_t n, const float* __restrict__ pq,
+                                                     const float* __restrict__ pk,
+                                                     float* __restrict__ dq,
+                                                     float* __restrict__ dk) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+        a += pq[r * n + i];
+        b += pk[r * n + i];
+    }
+    dq[i] = a;
+    dk[i] = b;
+}
+
+// per token: dbeta and dalpha = d log alpha / alpha (alpha clamped to FLT_MIN
+// as in the forward's log) from the row blocks' partials
+template <int NRB>
+__global__ __launch_bounds__(256) void bwd_reduce_gates(int64_t n, const float* __restrict__ pb,
+                                                        const float* __restrict__ pg,
+                                                        const float* __restrict__ alpha,
+                                                        float* __restrict__ dbeta,
+                                                        float* __restrict__ dalpha) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float b = 0.f, g = 0.f;
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+        b += pb[r * n + i];
+        g += pg[r * n + i];
+    }
+    dbeta[i] = b;
+    dalpha[i] = g / fmaxf(alpha[i], 1.17549435e-38f);
+}
+
+template <int DK, int DV, typename TIn, typename TD>
+hipError_t launch_bwd_t(const BwdArgs& a) {
+    constexpr int NRB = DV / RBW;
+    const int64_t BH = a.B * a.H, BTH = a.B * a.T * a.H;
+    const int64_t nch = (a.T + CB - 1) / CB;
+    BwdParams p{};
+    p.T = a.T;
+    p.H = a.H;
+    p.BTH = BTH;
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.dout = a.dout;
+    p.alpha = a.alpha;
+    p.beta = a.beta;
+    p.s0 = a.s0;
+    p.dsf = a.ds_final;
+    p.dv = a.dv;
+    p.ds0 = a.ds0;
+    p.ck = reinterpret_cast<float*>(a.workspace);
+    p.pq = p.ck + BH * nch * DV * DK;
+    p.pk = p.pq + NRB * BTH * DK;
+    p.pb = p.pk + NRB * BTH * DK;
+    p.pg = p.pb + NRB * BTH;
+    p.l2norm = a.l2norm;
+    const size_t lds = sizeof(float) * BL<DK>::TOTAL;
+    auto fn = gdn_bwd_kernel<DK, DV, TIn, TD>;
+    hipError_t e = hipFuncSetAttribute((const void*)fn,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, dim3((unsigned)(BH * NRB)), dim3(NTB), lds, a.stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nqk = BTH * DK;
+    if (a.l2norm) {
+        hipLaunchKernelGGL((bwd_reduce_rows_norm<NRB, DK, TIn, false>),
+                           dim3((unsigned)((BTH + 3) / 4)), dim3(256), 0, a.stream, BTH, p.pq, p.pk,
+                           nullptr, nullptr, a.q, a.k, nullptr, a.dq, a.dk, nullptr, nullptr);
+    } else {
+        hipLaunchKernelGGL((bwd_reduce_qk<NRB>), dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0,
+                           a.stream, nqk, p.pq, p.pk, a.dq, a.dk);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_reduce_gates<NRB>), dim3((unsigned)((BTH + 255) / 256)), dim3(256), 0,
+                       a.stream, BTH, p.pb, p.pg, a.alpha, a.dbeta, a.dalpha);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_bwd_d(const BwdArgs& a) {
+    if (a.in_bf16)
+        return a.dout_bf16 ? launch_bwd_t<DK, DV, bf16_t, bf16_t>(a)
+                           : launch_bwd_t<DK, DV, bf16_t, float>(a);
+    return a.dout_bf16 ? launch_bwd_t<DK, DV, float, bf16_t>(a)
+                       : launch_bwd_t<DK, DV, float, float>(a);
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv) {
+    const int64_t nch = (T + CB - 1) / CB;
+    const int64_t nrb = Dv / RBW;
+    const int64_t BTH = B * T * H;
+    return sizeof(float) * (size_t)(B * H * nch * Dv * Dk + 2 * nrb * BTH * Dk + 2 * nrb * BTH);
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs& a) {
+    if (a.Dk == 128 && a.Dv == 128) return launch_bwd_d<128, 128>(a);
+    if (a.Dk == 128 && a.Dv == 64) return launch_bwd_d<128, 64>(a);
+    if (a.Dk == 64 && a.Dv == 128) return launch_bwd_d<64, 128>(a);
+    return launch_bwd_d<64, 64>(a);
+}
+
+}  // namespace gdr

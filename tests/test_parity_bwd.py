@@ -84,8 +84,8 @@ def test_bwd_gate_regimes(gdr_lib):
 
 
 def test_bwd_reset_gates(gdr_lib):
-    """alpha = 0 and 1e-12 on some tokens: their chunks take the entry-by-entry
-    decays (the factored form would overflow), the others stay factored."""
+    """alpha = 0 and 1e-12 on some tokens: the within-chunk decays across them
+    underflow to 0 (every decay the kernel forms is at most 1)."""
     inp = make_gdn(B=1, T=130, H=2, Dk=64, Dv=64, dtype="f32", seed=545, s0_std=0.2)
     a = inp.alpha.clone()
     a[0, 20, 0] = 0.0
