@@ -95,16 +95,19 @@ struct BL {
     static constexpr int DU = UT + NR;
     static constexpr int KG = DU + NR;           // K G'^T
     static constexpr int DRB = KG + NR;          // diag(beta lambda) dR
-    static constexpr int SC = DRB + NR;          // per-token partial sums:
-    static constexpr int TAUR = SC;              //   [2 row tiles][16] dR terms of tau
+    // per-token partial sums, two sets (chunk parity: a chunk's set is read
+    // while the next chunk writes the other), offsets within a set:
+    static constexpr int SC = DRB + NR;
+    static constexpr int TAUR = 0;               //   [2 row tiles][16] dR terms of tau
     static constexpr int BER = TAUR + 32;        //   [2][16] sum_i dR X
     static constexpr int KAP = BER + 32;         //   [2][16] kappa
     static constexpr int TAUO = KAP + 32;        //   [4 waves][16] dO terms of tau
     static constexpr int BEA = TAUO + 64;        //   [16] A term of dbeta
     static constexpr int PRA = BEA + 16;         //   [16] pair sums of dA (.) A
     static constexpr int PRP = PRA + 16;         //   [16] pair sums of dP (.) P
-    static constexpr int GSUM = PRP + 16;        //   lambda_C <G', S>
-    static constexpr int TOTAL = GSUM + 4;
+    static constexpr int GSUM = PRP + 16;        //   [2 row tiles] lambda_C <G', S>
+    static constexpr int NSC = GSUM + 4;
+    static constexpr int TOTAL = SC + 2 * NSC;
     static_assert(TOTAL * 4 <= 80 * 1024, "two workgroups per CU");
     static_assert(PK % 64 == 4 && NK % 4 == 0 && S % 4 == 0 && G % 4 == 0, "pitches");
     static_assert(AK % 4 == 0 && V % 4 == 0 && SC % 4 == 0, "16-byte rows");
@@ -325,23 +328,25 @@ void gdn_bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) AKs[(4 * lg + i) * L::PC + l16] = kk[i] * gm[i];
     };
-    // T = (I + A)^{-1} by one wave: lane 4 c + q owns column c and the rows
-    // m = q (mod 4); row r of the column is delta_rc - beta_r sum_{m < r}
+    // T = (I + A)^{-1} by one wave: lane 4 c + q owns column c, rows
+    // 4 q .. 4 q + 3; row r of the column is delta_rc - beta_r sum_{m < r}
     // AK_rm T_mc (AK's upper part is zero), the four partial sums joined by
-    // a quad reduction
+    // a quad reduction.  The lane's AK entries are read before the first row.
     auto tsolve = [&](const Gates& g) {
         const int c = lane >> 2, q = lane & 3;
+        f32x4 ak[CB];
+#pragma unroll
+        for (int r = 0; r < CB; ++r) ak[r] = ld4(AKs + r * L::PC + 4 * q);
         float tq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < CB; ++r) {
-            float part = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) part += AKs[r * L::PC + 4 * j + q] * tq[j];
+            float part = (ak[r][0] * tq[0] + ak[r][1] * tq[1]) + (ak[r][2] * tq[2] + ak[r][3] * tq[3]);
             part = qsum(part);
             const float t = r < c ? 0.f : (r == c ? 1.f : 0.f) - lane_value(g.be, r) * part;
-            if ((r & 3) == q) tq[r >> 2] = t;
-            if (q == 0) Ts[r * L::PC + c] = t;
+            if (q == (r >> 2)) tq[r & 3] = t;
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Ts[(4 * q + j) * L::PC + c] = tq[j];
     };
     // K S^T (or K G'^T) for state-row tile t
     auto ks_tile = [&](const float* M, int t) {
@@ -430,22 +435,32 @@ void gdn_bwd_kernel(BwdParams p) {
         }
     }
     const int64_t poff = (int64_t)rb * p.BTH * DK;
-    // the gate gradients of chunk cp from the per-token partial sums (one
-    // wave; lane l sums token l % 16's partials, DPP scans over the tokens)
-    auto finalize = [&](int64_t cp) {
+    const int HDK = (int)(H * DK), HDV = (int)(H * DV), HI = (int)H;
+    // a chunk's outputs leave through buffer stores whose range ends at its
+    // last token: rows past it are dropped without a branch
+    auto rsrc = [&](const float* base, int bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes,
+                                                 0x00020000);
+    };
+    auto bstore = [&](float v, __amdgpu_buffer_rsrc_t r, int off) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+    };
+    // the gate gradients of chunk cp from its per-token partial sums (one
+    // wave; lane l takes token l % 16, DPP scans over the tokens; the four
+    // lane rows store the same values)
+    auto finalize = [&](int64_t cp, const float* sc) {
         const int t = l16;
-        const float tau = sm[L::TAUR + t] + sm[L::TAUR + 16 + t] + sm[L::TAUO + t] +
-                          sm[L::TAUO + 16 + t] + sm[L::TAUO + 32 + t] + sm[L::TAUO + 48 + t];
-        const float kap = sm[L::KAP + t] + sm[L::KAP + 16 + t];
+        const float tau = sc[L::TAUR + t] + sc[L::TAUR + 16 + t] + sc[L::TAUO + t] +
+                          sc[L::TAUO + 16 + t] + sc[L::TAUO + 32 + t] + sc[L::TAUO + 48 + t];
+        const float kap = sc[L::KAP + t] + sc[L::KAP + 16 + t];
         // sum_{r >= t} tau_r + sum_{r < t} kappa_r
-        const float dl = rsuffix16(tau) + (rscan16(kap) - kap) + sm[L::GSUM] + sm[L::PRA + t] +
-                         sm[L::PRP + t];
-        const float db = sm[L::BER + t] + sm[L::BER + 16 + t] + sm[L::BEA + t];
-        if (lane < 16 && t < chunk_len(cp)) {
-            const int64_t o = (int64_t)rb * p.BTH + tok(cp * CB + t);
-            p.pb[o] = db;
-            p.pg[o] = dl;
-        }
+        const float dl = rsuffix16(tau) + (rscan16(kap) - kap) + (sc[L::GSUM] + sc[L::GSUM + 1]) +
+                         sc[L::PRA + t] + sc[L::PRP + t];
+        const float db = sc[L::BER + t] + sc[L::BER + 16 + t] + sc[L::BEA + t];
+        const int bytes = chunk_len(cp) * HI * 4;
+        const int64_t o = (int64_t)rb * p.BTH + tok(cp * CB);
+        bstore(db, rsrc(p.pb + o, bytes), t * HI * 4);
+        bstore(dl, rsrc(p.pg + o, bytes), t * HI * 4);
     };
     f32x4 sv[NSV];
     auto fetch_s = [&](int64_t c) {
@@ -458,12 +473,18 @@ void gdn_bwd_kernel(BwdParams p) {
     };
     fetch(x, nch - 1, true);
     fetch_s(nch - 1);
+    // wait for the first chunk's loads here: entering the loop with nothing
+    // in flight lets the compiler count the stores each later chunk issues
+    // after its prefetch, instead of waiting for all of them at the top
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int64_t t0 = c * CB;
         const int n = chunk_len(c);
+        const int64_t tb = tok(t0);
+        float* scw = sm + L::SC + (int)(c & 1) * L::NSC;                // this chunk's sums
+        const float* scr = sm + L::SC + (int)((c + 1) & 1) * L::NSC;    // the later chunk's
         renew_lane();
         __syncthreads();
-        if (c + 1 < nch && wv == 3) finalize(c + 1);
 #pragma unroll
         for (int it = 0; it < NSV; ++it) {
             const int e4 = tid + it * NTB;
@@ -477,23 +498,25 @@ void gdn_bwd_kernel(BwdParams p) {
             fetch_s(c - 1);
         }
         __syncthreads();
-        // ---- wave 0: A, then T;  wave 1: P and K G'^T rows 0..15;
-        //      wave 2: X, R rows 0..15 and K G'^T rows 16..31;
-        //      wave 3: X, R rows 16..31 and lambda_C <G', S>
+        // ---- wave 0: A, then T;  wave 1: P, K G'^T rows 0..15, the later
+        //      chunk's gate gradients;  wave 2: X, R rows 0..15, K G'^T rows
+        //      16..31;  wave 3: X, R rows 16..31;  waves 2, 3: <G', S> over
+        //      their 16 rows
         if (wv == 0) {
             ak_tile(g);
             wave_sync();
             tsolve(g);
         } else if (wv == 1) {
             const f32x4 qk = mma16<NQK, true, true>(zero4, Qs, L::PK, Ks, L::PK, lane);
-            const f32x4 gm = gamma(g, false);
             const f32x4 kg = ks_tile(Gs, 0);
+            const f32x4 gm = gamma(g, false);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * lg + i;
                 Ps[r * L::PC + l16] = qk[i] * gm[i];
                 KGs[r * L::PR + l16] = kg[i];
             }
+            if (c + 1 < nch) finalize(c + 1, scr);
         } else {
             const int t = wv - 2;
             const f32x4 ks = ks_tile(Ss, t);
@@ -508,18 +531,20 @@ void gdn_bwd_kernel(BwdParams p) {
                 const f32x4 kg = ks_tile(Gs, 1);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) KGs[(4 * lg + i) * L::PR + 16 + l16] = kg[i];
-            } else {
-                float s = 0.f;
-#pragma unroll
-                for (int j = 0; j < DK / 64; ++j) {
-                    const int cc = lane + 64 * j;
-#pragma unroll 8
-                    for (int i = 0; i < RBW; ++i) s += Gs[i * L::PK + cc] * Ss[i * L::PK + cc];
-                }
-#pragma unroll
-                for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
-                if (lane == 0) sm[L::GSUM] = g.lamC * s;
             }
+            // lane: 4 channels (16-byte reads), CG / 4 of the wave's rows
+            constexpr int CG = DK / 4;
+            const int c4 = 4 * (lane % CG), rg = lane / CG;
+            float sg = 0.f;
+#pragma unroll
+            for (int m = 0; m < CG / 4; ++m) {
+                const int i = 16 * t + (CG / 4) * rg + m;
+                const f32x4 gv = ld4(Gs + i * L::PK + c4), sv4 = ld4(Ss + i * L::PK + c4);
+                sg += (gv[0] * sv4[0] + gv[1] * sv4[1]) + (gv[2] * sv4[2] + gv[3] * sv4[3]);
+            }
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) sg += __shfl_xor(sg, m, 64);
+            if (lane == 0) scw[L::GSUM + t] = g.lamC * sg;
         }
         __syncthreads();
         // ---- U = T R and kappa (waves 0, 1);
@@ -538,7 +563,7 @@ void gdn_bwd_kernel(BwdParams p) {
             }
             if (l16 == 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sm[L::KAP + 16 * t + 4 * lg + i] = kp[i];
+                for (int i = 0; i < 4; ++i) scw[L::KAP + 16 * t + 4 * lg + i] = kp[i];
             }
         } else {
             const int t = wv - 2;
@@ -552,10 +577,11 @@ void gdn_bwd_kernel(BwdParams p) {
         __syncthreads();
         // ---- dR = T^T dU (waves 0, 1: dv to HBM, dbeta and tau row sums);
         //      dP = dO U^T, D_P, pair sums, then dO -> diag(lambda) dO (wave 2);
-        //      dU R^T (wave 3)
+        //      dA and M (wave 3)
         if (wv < 2) {
             const int t = wv;
             const f32x4 dr = mma16<1, false, false>(zero4, Ts, L::PC, DUs + 16 * t, L::PR, lane);
+            const __amdgpu_buffer_rsrc_t rdv = rsrc(p.dv + tb * DV, n * HDV * 4);
             float sb[4], st[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -564,13 +590,13 @@ void gdn_bwd_kernel(BwdParams p) {
                 const float xv = Xs[o];
                 sb[i] = rsum16(dr[i] * xv);
                 st[i] = rsum16(dr[i] * (Vs[o] - xv));
-                if (r < n) p.dv[tok(t0 + r) * DV + row0 + 16 * t + l16] = g.br[i] * dr[i];
+                bstore(g.br[i] * dr[i], rdv, (r * HDV + row0 + 16 * t + l16) * 4);
             }
             if (l16 == 0) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    sm[L::BER + 16 * t + 4 * lg + i] = sb[i];
-                    sm[L::TAUR + 16 * t + 4 * lg + i] = -g.br[i] * st[i];
+                    scw[L::BER + 16 * t + 4 * lg + i] = sb[i];
+                    scw[L::TAUR + 16 * t + 4 * lg + i] = -g.br[i] * st[i];
                 }
             }
         } else if (wv == 2) {
@@ -585,25 +611,24 @@ void gdn_bwd_kernel(BwdParams p) {
                 DPs[r * L::PC + l16] = m ? dp[i] * gm[i] : 0.f;
             }
             const float pr = straddle(w);
-            if (lane < 16) sm[L::PRP + lane] = pr;
-            // only this wave reads dL/do in this phase
+            if (lane < 16) scw[L::PRP + lane] = pr;
+            // only this wave reads dL/do in this phase: element lane + 64 e
+            // is token 2 e + lane / 32, row lane % 32
 #pragma unroll
             for (int e = 0; e < CB * RBW / 64; ++e) {
-                const int idx = lane + 64 * e, r = idx / RBW, i = idx % RBW;
-                DOs[r * L::PR + i] *= __shfl(g.lam, r, 64);
+                const float lm = lane < 32 ? lane_value(g.lam, 2 * e) : lane_value(g.lam, 2 * e + 1);
+                DOs[(2 * e + (lane >> 5)) * L::PR + (lane & 31)] *= lm;
             }
         } else {
+            // dT = dU R^T, Y = dT T^T, dA = -T^T Y (strict), D_A, the A term
+            // of dbeta, its pair sums and M
             const f32x4 dt = mma16<2, true, true>(zero4, DUs, L::PR, Rs, L::PR, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * lg + i;
                 DAs[r * L::PC + l16] = l16 < r ? dt[i] : 0.f;
             }
-        }
-        __syncthreads();
-        // ---- wave 0 first: Y = (dU R^T) T^T, dA = -T^T Y (strict), D_A, the
-        //      A term of dbeta, its pair sums and M
-        if (wv == 0) {
+            wave_sync();
             const f32x4 y = mma16<1, true, true>(zero4, DAs, L::PC, Ts, L::PC, lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) Ys[(4 * lg + i) * L::PC + l16] = y[i];
@@ -622,10 +647,10 @@ void gdn_bwd_kernel(BwdParams p) {
                 DAs[r * L::PC + l16] = dv * gm[i];
             }
             const float pr = straddle(w);
-            if (lane < 16) sm[L::PRA + lane] = pr;
+            if (lane < 16) scw[L::PRA + lane] = pr;
             if (l16 == 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sm[L::BEA + 4 * lg + i] = sb[i];
+                for (int i = 0; i < 4; ++i) scw[L::BEA + 4 * lg + i] = sb[i];
             }
             wave_sync();
 #pragma unroll
@@ -634,58 +659,84 @@ void gdn_bwd_kernel(BwdParams p) {
                 Ys[r * L::PC + l16] = g.br[i] * DAs[r * L::PC + l16] + g.be * DAs[l16 * L::PC + r];
             }
         }
-        // ---- this wave's channel tiles: dq; dk but for M K; the dO terms of
-        //      tau; then G' <- lambda_C G' + (lambda dO)^T Q - (beta lambda dR)^T K
-        //      (only this wave reads these channels of G' from here on)
-        f32x4 dk[CTW];
+        __syncthreads();
+        // ---- this wave's channel tiles, the tiles' chains side by side: dq,
+        //      dk, the dO terms of tau; then G' <- lambda_C G' + (lambda dO)^T Q
+        //      - (beta lambda dR)^T K (only this wave reads these channels of
+        //      G' from here on)
+        const __amdgpu_buffer_rsrc_t rq = rsrc(p.pq + poff + tb * DK, n * HDK * 4);
+        f32x4 dq[CTW], dk[CTW];
         float tq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
+        for (int ct = 0; ct < CTW; ++ct)
+            dq[ct] = mma16<2, true, false>(zero4, DOs, L::PR, Ss + 16 * (CTW * wv + ct), L::PK, lane);
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct)
+            dk[ct] = mma16<2, true, false>(zero4, UTs, L::PR, Gs + 16 * (CTW * wv + ct), L::PK, lane);
+#pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
-            const int t = CTW * wv + ct, cc = 16 * t + l16;
-            f32x4 dq = mma16<2, true, false>(zero4, DOs, L::PR, Ss + 16 * t, L::PK, lane);
+            const int cc = 16 * (CTW * wv + ct) + l16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) tq[i] += dq[i] * Qs[(4 * lg + i) * L::PK + cc];
-            dq = mma16<1, true, false>(dq, DPs, L::PC, Ks + 16 * t, L::PK, lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * lg + i;
-                if (r < n) p.pq[poff + tok(t0 + r) * DK + cc] = dq[i];
-            }
-            f32x4 a = mma16<2, true, false>(zero4, UTs, L::PR, Gs + 16 * t, L::PK, lane);
-            a = mma16<2, true, false, true>(a, DRBs, L::PR, Ss + 16 * t, L::PK, lane);
-            dk[ct] = mma16<1, false, false>(a, DPs, L::PC, Qs + 16 * t, L::PK, lane);
-#pragma unroll
-            for (int a2 = 0; a2 < 2; ++a2) {
-                f32x4 acc;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[i] = Gs[(16 * a2 + 4 * lg + i) * L::PK + cc] * g.lamC;
-                acc = mma16<1, false, false>(acc, DOs + 16 * a2, L::PR, Qs + 16 * t, L::PK, lane);
-                acc = mma16<1, false, false, true>(acc, DRBs + 16 * a2, L::PR, Ks + 16 * t, L::PK, lane);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Gs[(16 * a2 + 4 * lg + i) * L::PK + cc] = acc[i];
-            }
+            for (int i = 0; i < 4; ++i) tq[i] += dq[ct][i] * Qs[(4 * lg + i) * L::PK + cc];
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tq[i] = rsum16(tq[i]);
-        if (l16 == 0) {
+        for (int ct = 0; ct < CTW; ++ct)
+            dq[ct] = mma16<1, true, false>(dq[ct], DPs, L::PC, Ks + 16 * (CTW * wv + ct), L::PK, lane);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sm[L::TAUO + 16 * wv + 4 * lg + i] = tq[i];
+        for (int ct = 0; ct < CTW; ++ct)
+            dk[ct] = mma16<2, true, false, true>(dk[ct], DRBs, L::PR, Ss + 16 * (CTW * wv + ct), L::PK,
+                                                 lane);
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+            const int cc = 16 * (CTW * wv + ct) + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bstore(dq[ct][i], rq, ((4 * lg + i) * HDK + cc) * 4);
         }
-        __syncthreads();   // M
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct)
+            dk[ct] = mma16<1, false, false>(dk[ct], DPs, L::PC, Qs + 16 * (CTW * wv + ct), L::PK, lane);
+        const __amdgpu_buffer_rsrc_t rk = rsrc(p.pk + poff + tb * DK, n * HDK * 4);
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
             const int t = CTW * wv + ct, cc = 16 * t + l16;
             dk[ct] = mma16<1, true, false>(dk[ct], Ys, L::PC, Ks + 16 * t, L::PK, lane);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * lg + i;
-                if (r < n) p.pk[poff + tok(t0 + r) * DK + cc] = dk[ct][i];
-            }
+            for (int i = 0; i < 4; ++i) bstore(dk[ct][i], rk, ((4 * lg + i) * HDK + cc) * 4);
+        }
+        {
+            f32x4 gu[2][CTW];
+#pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+                for (int ct = 0; ct < CTW; ++ct) {
+                    const int cc = 16 * (CTW * wv + ct) + l16;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        gu[a2][ct][i] = Gs[(16 * a2 + 4 * lg + i) * L::PK + cc] * g.lamC;
+                    gu[a2][ct] = mma16<1, false, false>(gu[a2][ct], DOs + 16 * a2, L::PR,
+                                                        Qs + 16 * (CTW * wv + ct), L::PK, lane);
+                }
+#pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+                for (int ct = 0; ct < CTW; ++ct) {
+                    const int cc = 16 * (CTW * wv + ct) + l16;
+                    gu[a2][ct] = mma16<1, false, false, true>(gu[a2][ct], DRBs + 16 * a2, L::PR,
+                                                              Ks + 16 * (CTW * wv + ct), L::PK, lane);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        Gs[(16 * a2 + 4 * lg + i) * L::PK + cc] = gu[a2][ct][i];
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tq[i] = rsum16(tq[i]);
+        if (l16 == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) scw[L::TAUO + 16 * wv + 4 * lg + i] = tq[i];
         }
     }
     __syncthreads();
-    if (wv == 3) finalize(0);
+    if (wv == 1) finalize(0, sm + L::SC);
     if (p.ds0) {
 #pragma unroll
         for (int it = 0; it < NSV; ++it) {
