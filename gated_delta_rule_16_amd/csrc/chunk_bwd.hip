@@ -142,6 +142,34 @@ __device__ __forceinline__ float lane_value(float x, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
+// Buffer resource over [base, base + bytes): loads past the end read 0,
+// stores past it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// W 32-bit words at byte offset off of a buffer, in 16-, 8- or 4-byte loads
+template <int W>
+__device__ __forceinline__ void bld(uint32_t (&w)[W], __amdgpu_buffer_rsrc_t r, int off) {
+    if constexpr (W % 4 == 0) {
+#pragma unroll
+        for (int h = 0; h < W / 4; ++h) {
+            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * h, 0, 0);
+            w[4 * h] = x[0];
+            w[4 * h + 1] = x[1];
+            w[4 * h + 2] = x[2];
+            w[4 * h + 3] = x[3];
+        }
+    } else if constexpr (W == 2) {
+        const u32x2w x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        w[0] = x[0];
+        w[1] = x[1];
+    } else {
+        static_assert(W == 1, "1, 2 or a multiple of 4 words");
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    }
+}
+
 // One chunk's global inputs for one thread, as raw words: key-side rows
 // (token tid / 16, channels j0 .. j0 + NC), a pair of state rows of v and
 // dL/do (token tid / 16, rows 2 (tid % 16), + 1), and the gates of token
@@ -226,28 +254,30 @@ void gdn_bwd_kernel(BwdParams p) {
     auto chunk_len = [&](int64_t c) { return (int)min((int64_t)CB, T - c * CB); };
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
+    const int HDK = (int)(H * DK), HDV = (int)(H * DV), HI = (int)H;
     using PF = Pre<TIn, TD, NC>;
+    // a chunk's rows through buffer resources that end at its last token:
+    // rows past it read as zeros (beta = 0; gates() sets alpha to 1 there)
     auto fetch = [&](PF& x, int64_t c, bool bwd) {
         const int n = chunk_len(c);
-        if (tr < n) {
-            const int64_t tk = tok(c * CB + tr);
-            ldw(x.k, reinterpret_cast<const TIn*>(p.k) + tk * DK + j0);
-            if (bwd) ldw(x.q, reinterpret_cast<const TIn*>(p.q) + tk * DK + j0);
-            ldw(x.v, reinterpret_cast<const TIn*>(p.v) + tk * DV + row0 + i2);
-            if (bwd) ldw(x.d, reinterpret_cast<const TD*>(p.dout) + tk * DV + row0 + i2);
-        }
-        // tokens past the end: alpha = 1, beta = 0
-        x.a = 1.f;
-        x.b = 0.f;
-        if (l16 < n) {
-            const int64_t tg = tok(c * CB + l16);
-            x.a = p.alpha[tg];
-            x.b = p.beta[tg];
-        }
+        const int64_t tb = tok(c * CB);
+        constexpr int SI = sizeof(TIn), SD = sizeof(TD);
+        bld(x.k, rsrc(reinterpret_cast<const TIn*>(p.k) + tb * DK, n * HDK * SI),
+            (tr * HDK + j0) * SI);
+        if (bwd)
+            bld(x.q, rsrc(reinterpret_cast<const TIn*>(p.q) + tb * DK, n * HDK * SI),
+                (tr * HDK + j0) * SI);
+        bld(x.v, rsrc(reinterpret_cast<const TIn*>(p.v) + tb * DV, n * HDV * SI),
+            (tr * HDV + row0 + i2) * SI);
+        if (bwd)
+            bld(x.d, rsrc(reinterpret_cast<const TD*>(p.dout) + tb * DV, n * HDV * SD),
+                (tr * HDV + row0 + i2) * SD);
+        x.a = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rsrc(p.alpha + tb, n * HI * 4), l16 * HI * 4, 0, 0));
+        x.b = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rsrc(p.beta + tb, n * HI * 4), l16 * HI * 4, 0, 0));
     };
-    // rows >= n: zero tokens
     auto commit = [&](const PF& x, int64_t c, bool bwd) {
-        const bool live = tr < chunk_len(c);
         const int at = tr * L::PK + j0;
         // GDR_L2NORM_QK: the 16 lanes of a token (one DPP row) hold its row
         float kn = 1.f, qn = 1.f;
@@ -255,8 +285,8 @@ void gdn_bwd_kernel(BwdParams p) {
             float sk = 0.f, sq = 0.f;
 #pragma unroll
             for (int y = 0; y < NC; ++y) {
-                const float kk = live ? packed<TIn>::at(x.k, y) : 0.f;
-                const float qq = (live && bwd) ? packed<TIn>::at(x.q, y) : 0.f;
+                const float kk = packed<TIn>::at(x.k, y);
+                const float qq = bwd ? packed<TIn>::at(x.q, y) : 0.f;
                 sk += kk * kk;
                 sq += qq * qq;
             }
@@ -268,8 +298,8 @@ void gdn_bwd_kernel(BwdParams p) {
             f32x4 kv, qv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                kv[e] = live ? packed<TIn>::at(x.k, y0 + e) * kn : 0.f;
-                qv[e] = (live && bwd) ? packed<TIn>::at(x.q, y0 + e) * qn : 0.f;
+                kv[e] = packed<TIn>::at(x.k, y0 + e) * kn;
+                qv[e] = bwd ? packed<TIn>::at(x.q, y0 + e) * qn : 0.f;
             }
             *reinterpret_cast<f32x4*>(Ks + at + y0) = kv;
             if (bwd) *reinterpret_cast<f32x4*>(Qs + at + y0) = qv;
@@ -277,14 +307,15 @@ void gdn_bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int o = tr * L::PR + i2 + e;
-            Vs[o] = live ? packed<TIn>::at(x.v, e) : 0.f;
-            if (bwd) DOs[o] = live ? packed<TD>::at(x.d, e) : 0.f;
+            Vs[o] = packed<TIn>::at(x.v, e);
+            if (bwd) DOs[o] = packed<TD>::at(x.d, e);
         }
     };
-    auto gates = [&](const PF& x) {
+    // the gate scalars of a chunk of n tokens (alpha = 1 past the end)
+    auto gates = [&](const PF& x, int n) {
         Gates g;
         g.be = x.b;
-        g.G = rscan16(safe_log2(x.a));
+        g.G = rscan16(l16 < n ? safe_log2(x.a) : 0.f);
         const float GC = lane_value(g.G, 15);
         g.lam = ex2(g.G);
         g.rho = ex2(GC - g.G);
@@ -371,7 +402,7 @@ void gdn_bwd_kernel(BwdParams p) {
         renew_lane();
         __syncthreads();
         commit(x, c, false);
-        const Gates g = gates(x);
+        const Gates g = gates(x, chunk_len(c));
         if (c + 1 < nch) fetch(x, c + 1, false);
         __syncthreads();
         // wave 0: A and T;  waves 1, 2: R;  wave 3: S to the workspace
@@ -388,12 +419,14 @@ void gdn_bwd_kernel(BwdParams p) {
                 Rs[o] = g.br[i] * (Vs[o] - g.lr[i] * ks[i]);
             }
         } else {
+            const __amdgpu_buffer_rsrc_t rc = rsrc(ckb + c * DV * DK, DV * DK * 4);
 #pragma unroll
             for (int it = 0; it < NSW; ++it) {
                 const int e4 = lane + 64 * it;
                 const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
-                *reinterpret_cast<f32x4*>(ckb + (c * DV + row0 + i) * DK + j) =
-                    ld4(Ss + i * L::PK + j);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, ld4(Ss + i * L::PK + j)), rc,
+                    ((row0 + i) * DK + j) * 4, 0, 0);
             }
         }
         __syncthreads();
@@ -435,13 +468,8 @@ void gdn_bwd_kernel(BwdParams p) {
         }
     }
     const int64_t poff = (int64_t)rb * p.BTH * DK;
-    const int HDK = (int)(H * DK), HDV = (int)(H * DV), HI = (int)H;
     // a chunk's outputs leave through buffer stores whose range ends at its
     // last token: rows past it are dropped without a branch
-    auto rsrc = [&](const float* base, int bytes) {
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes,
-                                                 0x00020000);
-    };
     auto bstore = [&](float v, __amdgpu_buffer_rsrc_t r, int off) {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
     };
@@ -464,11 +492,13 @@ void gdn_bwd_kernel(BwdParams p) {
     };
     f32x4 sv[NSV];
     auto fetch_s = [&](int64_t c) {
+        const __amdgpu_buffer_rsrc_t rc = rsrc(ckb + c * DV * DK, DV * DK * 4);
 #pragma unroll
         for (int it = 0; it < NSV; ++it) {
             const int e4 = tid + it * NTB;
             const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
-            sv[it] = *reinterpret_cast<const f32x4*>(ckb + (c * DV + row0 + i) * DK + j);
+            sv[it] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, ((row0 + i) * DK + j) * 4, 0, 0));
         }
     };
     fetch(x, nch - 1, true);
@@ -492,7 +522,7 @@ void gdn_bwd_kernel(BwdParams p) {
             *reinterpret_cast<f32x4*>(Ss + i * L::PK + j) = sv[it];
         }
         commit(x, c, true);
-        const Gates g = gates(x);
+        const Gates g = gates(x, n);
         if (c > 0) {
             fetch(x, c - 1, true);
             fetch_s(c - 1);
