@@ -35,9 +35,13 @@
 // Work split: one 256-thread workgroup (4 waves) per (b, h, 32 state rows),
 // two workgroups per CU (about 78 KB of LDS each).  It runs the forward over
 // its rows (chunk-start states to the workspace), then walks the chunks in
-// reverse.  dv and dS_0 are final per workgroup; dq, dk, dbeta and d log alpha
-// go to per-row-block partials (every term is linear in the row block's
-// share of dU, dR, dP and dA) that a second kernel adds.  Every product is a
+// reverse.  dv and dS_0 are final per workgroup.  dq and dk are sums over the
+// row blocks (every term is linear in the row block's share of dU, dR, dP
+// and dA): each workgroup adds its share by fp32 atomic adds, which the L2
+// of the XCD that holds all of a head's row blocks performs, so the order of
+// the four additions, and the last bits of dq and dk, vary from run to run.
+// dbeta and d log alpha go to per-row-block partials that a second kernel
+// adds.  Every product is a
 // set of 16 x 16 tiles on the fp32 matrix cores (v_mfma_f32_16x16x4f32),
 // the triangular solve and the elementwise terms are vector ALU.  Each wave
 // forms the chunk's gate scalars itself (a DPP scan of log2 alpha across the
@@ -60,7 +64,7 @@ struct BwdParams {
     const float *alpha, *beta, *s0, *dsf;
     float *dv, *ds0;
     float* ck;                     // [BH][nch][Dv][Dk] chunk-start states
-    float *pq, *pk;                // [NRB][BTH][Dk]
+    float *aq, *ak;                // [BTH][Dk] dq, dk accumulators (zero on entry)
     float *pb, *pg;                // [NRB][BTH]: dbeta, d log alpha
     bool l2norm;                   // q, k normalised on load (GDR_L2NORM_QK)
 };
@@ -467,11 +471,13 @@ void gdn_bwd_kernel(BwdParams p) {
             *reinterpret_cast<f32x4*>(Gs + i * L::PK + j) = gv[it];
         }
     }
-    const int64_t poff = (int64_t)rb * p.BTH * DK;
     // a chunk's outputs leave through buffer stores whose range ends at its
     // last token: rows past it are dropped without a branch
     auto bstore = [&](float v, __amdgpu_buffer_rsrc_t r, int off) {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+    };
+    auto badd = [&](float v, __amdgpu_buffer_rsrc_t r, int off) {
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, off, 0, 0);
     };
     // the gate gradients of chunk cp from its per-token partial sums (one
     // wave; lane l takes token l % 16, DPP scans over the tokens; the four
@@ -694,7 +700,7 @@ void gdn_bwd_kernel(BwdParams p) {
         //      dk, the dO terms of tau; then G' <- lambda_C G' + (lambda dO)^T Q
         //      - (beta lambda dR)^T K (only this wave reads these channels of
         //      G' from here on)
-        const __amdgpu_buffer_rsrc_t rq = rsrc(p.pq + poff + tb * DK, n * HDK * 4);
+        const __amdgpu_buffer_rsrc_t rq = rsrc(p.aq + tb * DK, n * HDK * 4);
         f32x4 dq[CTW], dk[CTW];
         float tq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -720,18 +726,18 @@ void gdn_bwd_kernel(BwdParams p) {
         for (int ct = 0; ct < CTW; ++ct) {
             const int cc = 16 * (CTW * wv + ct) + l16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bstore(dq[ct][i], rq, ((4 * lg + i) * HDK + cc) * 4);
+            for (int i = 0; i < 4; ++i) badd(dq[ct][i], rq, ((4 * lg + i) * HDK + cc) * 4);
         }
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct)
             dk[ct] = mma16<1, false, false>(dk[ct], DPs, L::PC, Qs + 16 * (CTW * wv + ct), L::PK, lane);
-        const __amdgpu_buffer_rsrc_t rk = rsrc(p.pk + poff + tb * DK, n * HDK * 4);
+        const __amdgpu_buffer_rsrc_t rk = rsrc(p.ak + tb * DK, n * HDK * 4);
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
             const int t = CTW * wv + ct, cc = 16 * t + l16;
             dk[ct] = mma16<1, true, false>(dk[ct], Ys, L::PC, Ks + 16 * t, L::PK, lane);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bstore(dk[ct][i], rk, ((4 * lg + i) * HDK + cc) * 4);
+            for (int i = 0; i < 4; ++i) badd(dk[ct][i], rk, ((4 * lg + i) * HDK + cc) * 4);
         }
         {
             f32x4 gu[2][CTW];
@@ -778,24 +784,6 @@ void gdn_bwd_kernel(BwdParams p) {
     }
 }
 
-// dq, dk from the row blocks' partials
-template <int NRB>
-__global__ __launch_bounds__(256) void bwd_reduce_qk(int64_t n, const float* __restrict__ pq,
-                                                     const float* __restrict__ pk,
-                                                     float* __restrict__ dq,
-                                                     float* __restrict__ dk) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    float a = 0.f, b = 0.f;
-#pragma unroll
-    for (int r = 0; r < NRB; ++r) {
-        a += pq[r * n + i];
-        b += pk[r * n + i];
-    }
-    dq[i] = a;
-    dk[i] = b;
-}
-
 // per token: dbeta and dalpha = d log alpha / alpha (alpha clamped to FLT_MIN
 // as in the forward's log) from the row blocks' partials
 template <int NRB>
@@ -836,30 +824,33 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
     p.dv = a.dv;
     p.ds0 = a.ds0;
     p.ck = reinterpret_cast<float*>(a.workspace);
-    p.pq = p.ck + BH * nch * DV * DK;
-    p.pk = p.pq + NRB * BTH * DK;
-    p.pb = p.pk + NRB * BTH * DK;
+    float* wq = p.ck + BH * nch * DV * DK;     // accumulators of the fused norm's input
+    float* wk = wq + BTH * DK;
+    p.pb = wk + BTH * DK;
     p.pg = p.pb + NRB * BTH;
     p.l2norm = a.l2norm;
+    // dq, dk (or, with the fused norm, the gradients with respect to the
+    // normalised q, k) are accumulated in place: zero them first
+    p.aq = a.l2norm ? wq : a.dq;
+    p.ak = a.l2norm ? wk : a.dk;
+    hipError_t e = launch_zero(p.aq, BTH * DK * 4, a.stream);
+    if (e == hipSuccess) e = launch_zero(p.ak, BTH * DK * 4, a.stream);
+    if (e != hipSuccess) return e;
     const size_t lds = sizeof(float) * BL<DK>::TOTAL;
     auto fn = gdn_bwd_kernel<DK, DV, TIn, TD>;
-    hipError_t e = hipFuncSetAttribute((const void*)fn,
+    e = hipFuncSetAttribute((const void*)fn,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fn, dim3((unsigned)(BH * NRB)), dim3(NTB), lds, a.stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t nqk = BTH * DK;
     if (a.l2norm) {
-        hipLaunchKernelGGL((bwd_reduce_rows_norm<NRB, DK, TIn, false>),
-                           dim3((unsigned)((BTH + 3) / 4)), dim3(256), 0, a.stream, BTH, p.pq, p.pk,
+        hipLaunchKernelGGL((bwd_reduce_rows_norm<1, DK, TIn, false>),
+                           dim3((unsigned)((BTH + 3) / 4)), dim3(256), 0, a.stream, BTH, wq, wk,
                            nullptr, nullptr, a.q, a.k, nullptr, a.dq, a.dk, nullptr, nullptr);
-    } else {
-        hipLaunchKernelGGL((bwd_reduce_qk<NRB>), dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0,
-                           a.stream, nqk, p.pq, p.pk, a.dq, a.dk);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_reduce_gates<NRB>), dim3((unsigned)((BTH + 255) / 256)), dim3(256), 0,
                        a.stream, BTH, p.pb, p.pg, a.alpha, a.dbeta, a.dalpha);
     return hipGetLastError();
@@ -880,7 +871,7 @@ size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t 
     const int64_t nch = (T + CB - 1) / CB;
     const int64_t nrb = Dv / RBW;
     const int64_t BTH = B * T * H;
-    return sizeof(float) * (size_t)(B * H * nch * Dv * Dk + 2 * nrb * BTH * Dk + 2 * nrb * BTH);
+    return sizeof(float) * (size_t)(B * H * nch * Dv * Dk + 2 * BTH * Dk + 2 * nrb * BTH);
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a) {

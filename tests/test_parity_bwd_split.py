@@ -71,8 +71,13 @@ def test_bwd_split_one_segment_is_plain(gdr_lib):
     a = gdr_lib.gdr_chunk_bwd(*args)
     b = gdr_lib.gdr_chunk_bwd_split(*args, nseg=1)
     torch.cuda.synchronize()
-    for x, y in zip(a, b):
-        assert torch.equal(x, y)
+    # dq and dk are sums over row blocks by atomic adds, whose order varies
+    # from run to run: equal to fp32 rounding; the rest bit for bit
+    for name, x, y in zip(NAMES, a, b):
+        if name in ("dq", "dk"):
+            assert ((x - y).abs().max() <= 1e-5 * x.abs().max()).item(), name
+        else:
+            assert torch.equal(x, y), name
 
 
 def test_bwd_split_long_context_workload(gdr_lib):
