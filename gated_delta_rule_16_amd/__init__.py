@@ -399,7 +399,9 @@ def gdr_chunk_bwd(q, k, v, alpha, beta, s0, dout, ds_final=None, *, workspace=No
     dbeta, ds0) for dL/do = ``dout`` [B,T,H,Dv] (fp32 or bf16) and
     dL/dS_T = ``ds_final`` [B,H,Dv,Dk] fp32 or None.  Inputs as for
     gdr_chunk_fwd.  ``workspace`` is a uint8 GPU tensor of at least
-    gdr_chunk_bwd_workspace_size(...) bytes, allocated here when None."""
+    gdr_chunk_bwd_workspace_size(...) bytes, allocated here when None.
+    dq and dk are summed over blocks of state rows by atomic adds, so they
+    can differ from run to run in the last bits."""
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     if q.dtype not in _DT or dout.dtype not in _DT:

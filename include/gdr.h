@@ -500,15 +500,18 @@ gdr_status_t gdr_output_gate_bwd_noalloc(int64_t N, int64_t H, int64_t Dv,
  * Networks", agihunt.info, "Method"; GDN review on meaningful96.github.io,
  * section 3.7), evaluated chunk by chunk in fp32: the pages' throughput
  * figures are for training, and the GDN-2 summary notes that a chunked
- * backward carries the gates inside its dot products.  The rule is Gated
- * Delta Rule-2 with alpha broadcast over the key channels and
- * erase = write = beta, and this call runs the gdr2_chunk_bwd kernels in
- * that form, reducing the per-channel gate gradients to per-token ones.
+ * backward carries the gates inside its dot products.  With one decay per
+ * token, every decay factor is a scalar per token or token pair, so the
+ * gate gradients are formed per token (no per-channel decay tables).
  *
  *   q, k, v, alpha, beta, s0, in_dt  the forward's inputs, as for gdr_chunk_fwd
  *   dout_dt, dout  [B, T, H, Dv] dL/do (GDR_F32 or GDR_BF16)
  *   ds_final       [B, H, Dv, Dk] fp32 dL/dS_T, or NULL (zero)
- *   dq, dk         [B, T, H, Dk] fp32 (written)
+ *   dq, dk         [B, T, H, Dk] fp32 (written).  Each is a sum over the
+ *                  Dv/32 blocks of state rows, which the kernel adds with
+ *                  fp32 atomic adds: the order of those additions varies,
+ *                  so dq and dk can differ from run to run in the last
+ *                  bits (every other output is the same bit for bit)
  *   dv             [B, T, H, Dv] fp32 (written)
  *   dalpha, dbeta  [B, T, H] fp32 (written).  dalpha is dL/d(log alpha)
  *                  divided by alpha, alpha clamped to FLT_MIN as in the
@@ -519,7 +522,9 @@ gdr_status_t gdr_output_gate_bwd_noalloc(int64_t N, int64_t H, int64_t Dv,
  *                  16-byte aligned, owned by the caller; its contents on
  *                  entry do not matter and on return are unspecified.
  *                  It holds the chunk-start states (B H ceil(T/16) Dv Dk
- *                  floats) and per-row-block partial sums.  A smaller
+ *                  floats), dq and dk accumulators for GDR_L2NORM_QK
+ *                  (2 B T H Dk floats) and per-row-block partial sums of
+ *                  the gate gradients (2 (Dv/32) B T H floats).  A smaller
  *                  workspace_bytes is GDR_ERR_INVALID.
  *
  * Calls on one workspace must not overlap.  T == 0 copies ds_final (or
