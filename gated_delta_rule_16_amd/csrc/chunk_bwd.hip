@@ -64,6 +64,7 @@ struct BwdParams {
     const float *alpha, *beta, *s0, *dsf;
     float *dv, *ds0;
     float* ck;                     // [BH][nch][Dv][Dk] chunk-start states
+    float* ta;                     // [BH NRB][nch][2][16][16]: T and AK of each chunk
     float *aq, *ak;                // [BTH][Dk] dq, dk accumulators (zero on entry)
     float *pb, *pg;                // [NRB][BTH]: dbeta, d log alpha
     bool l2norm;                   // q, k normalised on load (GDR_L2NORM_QK)
@@ -251,6 +252,7 @@ void gdn_bwd_kernel(BwdParams p) {
     const int row0 = rb * RBW;
     const int64_t nch = (T + CB - 1) / CB;
     float* ckb = p.ck + bh * nch * DV * DK;
+    float* tab = p.ta + wid * nch * 512;
     auto tok = [&](int64_t t) { return (b * T + t) * H + h; };
     const int tr = tid >> 4;                   // this thread's token for the loads
     const int j0 = NC * (tid & 15);            // .. and its key channels
@@ -409,11 +411,19 @@ void gdn_bwd_kernel(BwdParams p) {
         const Gates g = gates(x, chunk_len(c));
         if (c + 1 < nch) fetch(x, c + 1, false);
         __syncthreads();
-        // wave 0: A and T;  waves 1, 2: R;  wave 3: S to the workspace
+        // wave 0: A and T (kept for the reverse sweep);  waves 1, 2: R;
+        // wave 3: S to the workspace
         if (wv == 0) {
             ak_tile(g);
             wave_sync();
             tsolve(g);
+            wave_sync();
+            const __amdgpu_buffer_rsrc_t rt = rsrc(tab + c * 512, 512 * 4);
+            const int r = lane >> 2, c4 = 4 * (lane & 3);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ld4(Ts + r * L::PC + c4)),
+                                                   rt, (r * 16 + c4) * 4, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ld4(AKs + r * L::PC + c4)),
+                                                   rt, (256 + r * 16 + c4) * 4, 0, 0);
         } else if (wv <= 2) {
             const int t = wv - 1;
             const f32x4 ks = ks_tile(Ss, t);
@@ -496,6 +506,10 @@ void gdn_bwd_kernel(BwdParams p) {
         bstore(db, rsrc(p.pb + o, bytes), t * HI * 4);
         bstore(dl, rsrc(p.pg + o, bytes), t * HI * 4);
     };
+    u32x2w tv;   // this thread's two entries of the chunk's T and AK
+    auto fetch_t = [&](int64_t c) {
+        tv = __builtin_amdgcn_raw_buffer_load_b64(rsrc(tab + c * 512, 512 * 4), 8 * tid, 0, 0);
+    };
     f32x4 sv[NSV];
     auto fetch_s = [&](int64_t c) {
         const __amdgpu_buffer_rsrc_t rc = rsrc(ckb + c * DV * DK, DV * DK * 4);
@@ -509,6 +523,7 @@ void gdn_bwd_kernel(BwdParams p) {
     };
     fetch(x, nch - 1, true);
     fetch_s(nch - 1);
+    fetch_t(nch - 1);
     // wait for the first chunk's loads here: entering the loop with nothing
     // in flight lets the compiler count the stores each later chunk issues
     // after its prefetch, instead of waiting for all of them at the top
@@ -528,21 +543,24 @@ void gdn_bwd_kernel(BwdParams p) {
             *reinterpret_cast<f32x4*>(Ss + i * L::PK + j) = sv[it];
         }
         commit(x, c, true);
+        {
+            const int e = 2 * tid, r = (e & 255) >> 4, col = e & 15;
+            float* d = (e < 256 ? Ts : AKs) + r * L::PC + col;
+            d[0] = __uint_as_float(tv[0]);
+            d[1] = __uint_as_float(tv[1]);
+        }
         const Gates g = gates(x, n);
         if (c > 0) {
             fetch(x, c - 1, true);
             fetch_s(c - 1);
+            fetch_t(c - 1);
         }
         __syncthreads();
-        // ---- wave 0: A, then T;  wave 1: P, K G'^T rows 0..15, the later
-        //      chunk's gate gradients;  wave 2: X, R rows 0..15, K G'^T rows
-        //      16..31;  wave 3: X, R rows 16..31;  waves 2, 3: <G', S> over
-        //      their 16 rows
-        if (wv == 0) {
-            ak_tile(g);
-            wave_sync();
-            tsolve(g);
-        } else if (wv == 1) {
+        // ---- (T and AK come from the forward sweep)  waves 0, 3: X, R rows
+        //      0..15, 16..31;  wave 1: P, K G'^T rows 0..15 and the later
+        //      chunk's gate gradients;  wave 2: K G'^T rows 16..31;
+        //      waves 2, 3: <G', S> over rows 0..15, 16..31
+        if (wv == 1) {
             const f32x4 qk = mma16<NQK, true, true>(zero4, Qs, L::PK, Ks, L::PK, lane);
             const f32x4 kg = ks_tile(Gs, 0);
             const f32x4 gm = gamma(g, false);
@@ -554,33 +572,37 @@ void gdn_bwd_kernel(BwdParams p) {
             }
             if (c + 1 < nch) finalize(c + 1, scr);
         } else {
-            const int t = wv - 2;
-            const f32x4 ks = ks_tile(Ss, t);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int o = (4 * lg + i) * L::PR + 16 * t + l16;
-                const float xv = Vs[o] - g.lr[i] * ks[i];
-                Xs[o] = xv;
-                Rs[o] = g.br[i] * xv;
-            }
             if (wv == 2) {
                 const f32x4 kg = ks_tile(Gs, 1);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) KGs[(4 * lg + i) * L::PR + 16 + l16] = kg[i];
-            }
-            // lane: 4 channels (16-byte reads), CG / 4 of the wave's rows
-            constexpr int CG = DK / 4;
-            const int c4 = 4 * (lane % CG), rg = lane / CG;
-            float sg = 0.f;
+            } else {
+                const int t = wv == 0 ? 0 : 1;
+                const f32x4 ks = ks_tile(Ss, t);
 #pragma unroll
-            for (int m = 0; m < CG / 4; ++m) {
-                const int i = 16 * t + (CG / 4) * rg + m;
-                const f32x4 gv = ld4(Gs + i * L::PK + c4), sv4 = ld4(Ss + i * L::PK + c4);
-                sg += (gv[0] * sv4[0] + gv[1] * sv4[1]) + (gv[2] * sv4[2] + gv[3] * sv4[3]);
+                for (int i = 0; i < 4; ++i) {
+                    const int o = (4 * lg + i) * L::PR + 16 * t + l16;
+                    const float xv = Vs[o] - g.lr[i] * ks[i];
+                    Xs[o] = xv;
+                    Rs[o] = g.br[i] * xv;
+                }
             }
+            if (wv >= 2) {
+                // lane: 4 channels (16-byte reads), CG / 4 of the 16 rows
+                const int t = wv - 2;
+                constexpr int CG = DK / 4;
+                const int c4 = 4 * (lane % CG), rg = lane / CG;
+                float sg = 0.f;
 #pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) sg += __shfl_xor(sg, m, 64);
-            if (lane == 0) scw[L::GSUM + t] = g.lamC * sg;
+                for (int m = 0; m < CG / 4; ++m) {
+                    const int i = 16 * t + (CG / 4) * rg + m;
+                    const f32x4 gv = ld4(Gs + i * L::PK + c4), sv4 = ld4(Ss + i * L::PK + c4);
+                    sg += (gv[0] * sv4[0] + gv[1] * sv4[1]) + (gv[2] * sv4[2] + gv[3] * sv4[3]);
+                }
+#pragma unroll
+                for (int m = 32; m >= 1; m >>= 1) sg += __shfl_xor(sg, m, 64);
+                if (lane == 0) scw[L::GSUM + t] = g.lamC * sg;
+            }
         }
         __syncthreads();
         // ---- U = T R and kappa (waves 0, 1);
@@ -824,7 +846,8 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
     p.dv = a.dv;
     p.ds0 = a.ds0;
     p.ck = reinterpret_cast<float*>(a.workspace);
-    float* wq = p.ck + BH * nch * DV * DK;     // accumulators of the fused norm's input
+    p.ta = p.ck + BH * nch * DV * DK;
+    float* wq = p.ta + BH * NRB * nch * 512;   // accumulators of the fused norm's input
     float* wk = wq + BTH * DK;
     p.pb = wk + BTH * DK;
     p.pg = p.pb + NRB * BTH;
@@ -871,7 +894,8 @@ size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t 
     const int64_t nch = (T + CB - 1) / CB;
     const int64_t nrb = Dv / RBW;
     const int64_t BTH = B * T * H;
-    return sizeof(float) * (size_t)(B * H * nch * Dv * Dk + 2 * BTH * Dk + 2 * nrb * BTH);
+    return sizeof(float) *
+           (size_t)(B * H * nch * Dv * Dk + B * H * nrb * nch * 512 + 2 * BTH * Dk + 2 * nrb * BTH);
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a) {
