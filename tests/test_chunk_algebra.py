@@ -262,6 +262,98 @@ def test_gdn_chunk_bwd_small_gates():
         np.testing.assert_allclose(x, y, rtol=1e-8, atol=1e-9 * max(1.0, np.abs(y).max()))
 
 
+def gdn_chunk_bwd_tokens(q, k, v, a, b, s0, dO, dSf, C, nrb):
+    """The scalar-gate reverse mode in the form gdr_chunk_bwd's kernel
+    evaluates: the state rows in nrb blocks, each block's share of every
+    gradient summed, and the gate gradients formed per token.  Per chunk
+    (lam = e^g, rho = lam_C / lam, Gamma_rs = e^{g_r - g_s}) and row block:
+
+      X = V - diag(lam) K S^T,  R = diag(beta) X,  U = T R,  KG = K G^T,
+      dU = P^T dO + diag(rho) KG,  dR = T^T dU,  dP = dO U^T,  dA = -T^T (dU R^T) T^T,
+      D_P = dP o Gamma,  D_A = dA o Gamma,  M = diag(beta) D_A + D_A^T diag(beta),
+      dq += D_P K + (diag(lam) dO) S,
+      dk += M K + D_P^T Q + (diag(rho) U) G - (diag(beta lam) dR) S,
+      dbeta += rowsum(dR o X) + rowsum(dA o AK)            (AK = Gamma o K K^T, s < r)
+      tau = -beta rowsum(dR o (V - X)) + rowsum(Q o (diag(lam) dO) S)
+      kappa = rho rowsum(U o KG),  W = dA o A + dP o P,
+      dlog alpha_t += sum_{r >= t} tau_r + sum_{r < t} kappa_r
+                      + lam_C <G, S> + sum_{r >= t > s} W_rs,
+      G <- lam_C G + (diag(lam) dO)^T Q - (diag(beta lam) dR)^T K."""
+    T, Dk = q.shape
+    Dv = v.shape[1]
+    blocks = np.array_split(np.arange(Dv), nrb)
+    chunks = [slice(c0, min(c0 + C, T)) for c0 in range(0, T, C)]
+    S = s0.copy()
+    starts = []
+    for sl in chunks:
+        starts.append(S.copy())
+        _, S = gdn_chunk(q[sl], k[sl], v[sl], a[sl], b[sl], S, C)
+    G = dSf.copy()
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dla, db = np.zeros_like(a), np.zeros_like(b)
+    for sl, S in zip(reversed(chunks), reversed(starts)):
+        Q, K, al, be = q[sl], k[sl], a[sl], b[sl]
+        n = Q.shape[0]
+        g = np.cumsum(np.log(al))
+        lam, lC = np.exp(g), np.exp(g[-1])
+        rho = np.exp(g[-1] - g)
+        ge = np.tril(np.ones((n, n), dtype=bool))
+        gt = np.tril(np.ones((n, n), dtype=bool), -1)
+        Gam = np.exp(np.where(ge, g[:, None] - g[None, :], -np.inf))
+        AK = np.where(gt, Gam * (K @ K.T), 0.0)
+        A = be[:, None] * AK
+        Tm = np.linalg.inv(np.eye(n) + A)
+        P = np.where(ge, Gam * (Q @ K.T), 0.0)
+        Gn = np.empty_like(G)
+        for rows in blocks:
+            Sb, Gb, V, dOb = S[rows], G[rows], v[sl][:, rows], dO[sl][:, rows]
+            X = V - lam[:, None] * (K @ Sb.T)
+            R = be[:, None] * X
+            U = Tm @ R
+            KG = K @ Gb.T
+            dU = P.T @ dOb + rho[:, None] * KG
+            dR = Tm.T @ dU
+            dP = np.where(ge, dOb @ U.T, 0.0)
+            dA = np.where(gt, -(Tm.T @ (dU @ R.T) @ Tm.T), 0.0)
+            DP, DA = dP * Gam, dA * Gam
+            M = be[:, None] * DA + DA.T * be[None, :]
+            dOl = lam[:, None] * dOb
+            dRbl = (be * lam)[:, None] * dR
+            dOlS = dOl @ Sb
+            dq[sl] += DP @ K + dOlS
+            dk[sl] += M @ K + DP.T @ Q + (rho[:, None] * U) @ Gb - dRbl @ Sb
+            dv[sl][:, rows] = be[:, None] * dR
+            db[sl] += np.sum(dR * X, axis=1) + np.sum(dA * AK, axis=1)
+            tau = -be * np.sum(dR * (V - X), axis=1) + np.sum(Q * dOlS, axis=1)
+            kap = rho * np.sum(U * KG, axis=1)
+            W = dA * A + dP * P
+            gs = lC * np.sum(Gb * Sb)
+            for t in range(n):
+                dla[sl][t] += (tau[t:].sum() + kap[:t].sum() + gs + W[t:, :t].sum())
+            Gn[rows] = lC * Gb + dOl.T @ Q - dRbl.T @ K
+        G = Gn
+    return dq, dk, dv, dla / a, db, G
+
+
+@pytest.mark.parametrize("C,nrb", [(1, 1), (4, 2), (16, 1), (16, 2), (16, 5)])
+def test_gdn_chunk_bwd_token_form_matches_oracle(C, nrb):
+    """The kernel's per-token gate gradients (suffix sums of tau, prefix sums
+    of kappa, pair sums across t, lam_C <G, S>) and its row-block split of
+    every gradient give the oracle's backward."""
+    q, k, v, a, b, S0 = rand_gdn(40, B=1, T=53, H=1, Dk=6, Dv=5)
+    g = np.random.Generator(np.random.PCG64(41))
+    do = g.standard_normal(v.shape)
+    dsf = g.standard_normal(S0.shape)
+    ref = oracle.gdn_bwd(q, k, v, a, b, S0, do, dsf)
+    got = gdn_chunk_bwd_tokens(q[0, :, 0], k[0, :, 0], v[0, :, 0], a[0, :, 0], b[0, :, 0],
+                               S0[0, 0], do[0, :, 0], dsf[0, 0], C, nrb)
+    want = [ref[0][0, :, 0], ref[1][0, :, 0], ref[2][0, :, 0], ref[3][0, :, 0], ref[4][0, :, 0],
+            ref[5][0, 0]]
+    for name, x, y in zip(("dq", "dk", "dv", "dalpha", "dbeta", "ds0"), got, want):
+        np.testing.assert_allclose(x, y, rtol=1e-9, atol=1e-10 * max(1.0, np.abs(y).max()),
+                                   err_msg=f"{name} C={C} nrb={nrb}")
+
+
 def gdn2_chunk_bwd(q, k, v, a, e, w, s0, dO, dSf, C):
     """Chunkwise reverse mode of Gated Delta Rule-2 for one (b, h).  Per chunk
     (G the within-chunk cumulative log alpha per channel, E = b (.) k,
