@@ -71,7 +71,8 @@ struct Bwd2Params {
     const float *s0, *dsf;
     float *dv, *dw, *ds0;
     float* ck;                     // [BH][nch][Dv][Dk]
-    float *pq, *pk, *pb, *pg;      // [NRB][BTH][Dk] each
+    float *pq, *pk, *pb, *pg;      // [BTH][Dk] accumulators of dq, dk, derase, d log alpha
+                                   // (zero on entry)
     bool l2norm;                   // q, k normalised on load (GDR_L2NORM_QK)
 };
 
@@ -448,10 +449,12 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         }
         put_s(gv, Gs);
     }
-    const int64_t poff = (int64_t)rb * p.BTH * DK;
     f32x4 sv[NSV];
     fetch(x, nch - 1, true);
     fetch_s(sv, nch - 1);
+    // nothing in flight on entry: the compiler can then count the stores
+    // each chunk issues after its prefetch instead of waiting for them all
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int64_t t0 = c * C2;
         const int n = chunk_len(c);
@@ -521,15 +524,17 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         if (wv < 2) {
             const int t = wv;
             const f32x4 acc = mma16<1, false, false>(zero4, Ts, L::PC, dUs + 16 * t, L::PR);
+            // stores past the chunk's last token are dropped by the range
+            const int bytes = n * (int)(p.H * DV) * 4;
+            const __amdgpu_buffer_rsrc_t rw = rsrc(p.dw + tok(t0) * DV, bytes);
+            const __amdgpu_buffer_rsrc_t rv = rsrc(p.dv + tok(t0) * DV, bytes);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * lg + i, o = r * L::PR + 16 * t + l16;
                 dRs[o] = acc[i];
-                if (r < n) {
-                    const int64_t off = tok(t0 + r) * DV + row0 + 16 * t + l16;
-                    p.dw[off] = acc[i] * Vsm[o];
-                    p.dv[off] = acc[i] * Wsm[o];
-                }
+                const int off = (r * (int)(p.H * DV) + row0 + 16 * t + l16) * 4;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i] * Vsm[o]), rw, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i] * Wsm[o]), rv, off, 0, 0);
             }
         } else if (wv == 2) {
             put_nn(mma16<2, true, true>(zero4, dOs, L::PR, Us, L::PR), dPs, false);
@@ -651,15 +656,22 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
                     dl[i] = suft + pk4[i] + lam + (lg >= 2 ? sufp : -pp[i]);
                 }
             }
+            // this row block's share, added by fp32 atomics in L2; tokens
+            // past the chunk's end are dropped by the range
+            {
+                const int bytes = n * (int)(p.H * DK) * 4;
+                const int64_t base = tok(t0) * DK;
+                const __amdgpu_buffer_rsrc_t rq = rsrc(p.pq + base, bytes);
+                const __amdgpu_buffer_rsrc_t rk = rsrc(p.pk + base, bytes);
+                const __amdgpu_buffer_rsrc_t rb_ = rsrc(p.pb + base, bytes);
+                const __amdgpu_buffer_rsrc_t rg = rsrc(p.pg + base, bytes);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * lg + i;
-                if (r < n) {
-                    const int64_t o = poff + tok(t0 + r) * DK + cc;
-                    p.pq[o] = oq[i];
-                    p.pk[o] = ok[i];
-                    p.pb[o] = ob[i];
-                    p.pg[o] = dl[i];
+                for (int i = 0; i < 4; ++i) {
+                    const int off = ((4 * lg + i) * (int)(p.H * DK) + cc) * 4;
+                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(oq[i], rq, off, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(ok[i], rk, off, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(ob[i], rb_, off, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dl[i], rg, off, 0, 0);
                 }
             }
             // ---- G' <- G' diag(lambda_C) + dO^T Q~ - dR^T E~ on this wave's
@@ -688,30 +700,13 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
     }
 }
 
-// dq, dk, derase and dalpha: the sums of the row blocks' partials, dalpha =
-// d log alpha / alpha with alpha clamped to FLT_MIN as in the forward's log
-template <int NRB, typename TIn>
-__global__ __launch_bounds__(256) void bwd2_reduce(int64_t n, const float* __restrict__ pq,
-                                                   const float* __restrict__ pk,
-                                                   const float* __restrict__ pb,
-                                                   const float* __restrict__ pg, const void* alpha,
-                                                   float* __restrict__ dq, float* __restrict__ dk,
-                                                   float* __restrict__ db,
-                                                   float* __restrict__ da) {
+// dalpha = d log alpha / alpha, alpha clamped to FLT_MIN as in the forward's log
+template <typename TIn>
+__global__ __launch_bounds__(256) void bwd2_dalpha(int64_t n, const float* __restrict__ dl,
+                                                   const void* alpha, float* __restrict__ da) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    float a = 0.f, b = 0.f, c = 0.f, d = 0.f;
-#pragma unroll
-    for (int r = 0; r < NRB; ++r) {
-        a += pq[r * n + i];
-        b += pk[r * n + i];
-        c += pb[r * n + i];
-        d += pg[r * n + i];
-    }
-    dq[i] = a;
-    dk[i] = b;
-    db[i] = c;
-    da[i] = d / fmaxf(ldf<TIn>(alpha, i), 1.17549435e-38f);
+    da[i] = dl[i] / fmaxf(ldf<TIn>(alpha, i), 1.17549435e-38f);
 }
 
 template <int DK, int DV, typename TIn, typename TD>
@@ -727,7 +722,6 @@ hipError_t launch_main(const Bwd2Params& p, int64_t BH, hipStream_t st) {
 
 template <int DK, int DV, typename TIn, typename TD>
 hipError_t launch_bwd2_t(const Bwd2Args& a) {
-    constexpr int NRB = DV / R2;
     const int64_t BH = a.B * a.H, BTH = a.B * a.T * a.H;
     const int64_t nch = (a.T + C2 - 1) / C2;
     Bwd2Params p{};
@@ -747,23 +741,29 @@ hipError_t launch_bwd2_t(const Bwd2Args& a) {
     p.dw = a.dwrite;
     p.ds0 = a.ds0;
     p.ck = reinterpret_cast<float*>(a.workspace);
-    p.pq = p.ck + BH * nch * DV * DK;
-    p.pk = p.pq + NRB * BTH * DK;
-    p.pb = p.pk + NRB * BTH * DK;
-    p.pg = p.pb + NRB * BTH * DK;
+    // accumulators: dq, dk and derase go straight into the outputs unless the
+    // fused norm's reverse mode follows; d log alpha always in the workspace
+    float* w = p.ck + BH * nch * DV * DK;
+    const int64_t nqk = BTH * DK;
+    p.pq = a.l2norm ? w : a.dq;
+    p.pk = a.l2norm ? w + nqk : a.dk;
+    p.pb = a.l2norm ? w + 2 * nqk : a.derase;
+    p.pg = w + 3 * nqk;
     p.l2norm = a.l2norm;
-    hipError_t e = launch_main<DK, DV, TIn, TD>(p, BH, a.stream);
+    hipError_t e = hipSuccess;
+    for (float* acc : {p.pq, p.pk, p.pb, p.pg})
+        if (e == hipSuccess) e = launch_zero(acc, nqk * 4, a.stream);
+    if (e != hipSuccess) return e;
+    e = launch_main<DK, DV, TIn, TD>(p, BH, a.stream);
     if (e != hipSuccess) return e;
     if (a.l2norm) {
-        hipLaunchKernelGGL((bwd_reduce_rows_norm<NRB, DK, TIn, true>),
+        hipLaunchKernelGGL((bwd_reduce_rows_norm<1, DK, TIn, true>),
                            dim3((unsigned)((BTH + 3) / 4)), dim3(256), 0, a.stream, BTH, p.pq, p.pk,
                            p.pb, p.pg, a.q, a.k, a.alpha, a.dq, a.dk, a.derase, a.dalpha);
         return hipGetLastError();
     }
-    const int64_t nqk = BTH * DK;
-    hipLaunchKernelGGL((bwd2_reduce<NRB, TIn>), dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0,
-                       a.stream, nqk, p.pq, p.pk, p.pb, p.pg, a.alpha, a.dq, a.dk, a.derase,
-                       a.dalpha);
+    hipLaunchKernelGGL((bwd2_dalpha<TIn>), dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0,
+                       a.stream, nqk, p.pg, a.alpha, a.dalpha);
     return hipGetLastError();
 }
 
@@ -781,7 +781,8 @@ hipError_t launch_bwd2_d(const Bwd2Args& a) {
 size_t bwd2_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv) {
     const int64_t nch = (T + C2 - 1) / C2;
     const int64_t nrb = Dv / R2;
-    return sizeof(float) * (size_t)(B * H * nch * Dv * Dk + 4 * nrb * B * T * H * Dk);
+    (void)nrb;
+    return sizeof(float) * (size_t)(B * H * nch * Dv * Dk + 4 * B * T * H * Dk);
 }
 
 hipError_t launch_chunk2_bwd(const Bwd2Args& a) {

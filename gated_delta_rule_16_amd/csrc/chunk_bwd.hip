@@ -147,12 +147,6 @@ __device__ __forceinline__ float lane_value(float x, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
-// Buffer resource over [base, base + bytes): loads past the end read 0,
-// stores past it are dropped.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-
 // W 32-bit words at byte offset off of a buffer, in 16-, 8- or 4-byte loads
 template <int W>
 __device__ __forceinline__ void bld(uint32_t (&w)[W], __amdgpu_buffer_rsrc_t r, int off) {

@@ -16,6 +16,12 @@ __device__ __forceinline__ float ldf(const void* p, int64_t i) {
 
 typedef uint32_t u32x2w __attribute__((ext_vector_type(2)));
 
+// Buffer resource over [base, base + bytes): loads past the end read 0,
+// stores and atomics past it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
 // W 32-bit words from global memory in one or a few vector loads; the
 // address is aligned to min(16, 4 W) bytes.  Loads kept as raw words so that
 // they can be issued a chunk ahead and converted when they are used.

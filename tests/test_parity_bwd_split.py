@@ -153,9 +153,14 @@ def _check2(gdr_lib, inp, nseg, seed, norm=False):
     print("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     bad = {n: e for n, e in errs.items() if not e <= TOL}
     assert not bad, bad
-    # GDR_SPLIT_FP32_STATES is the plain call
+    # GDR_SPLIT_FP32_STATES is the plain call: dq, dk, derase and dalpha are
+    # sums over row blocks by atomic adds, whose order varies from run to
+    # run (equal to fp32 rounding); the rest bit for bit
     for n, x, y in zip(NAMES2, flag, plain):
-        assert torch.equal(x, y), n
+        if n in ("dq", "dk", "dalpha", "derase"):
+            assert ((x - y).abs().max() <= 1e-5 * x.abs().max()).item(), n
+        else:
+            assert torch.equal(x, y), n
 
 
 @pytest.mark.parametrize("dims", [(128, 64), (64, 128), (128, 128)])
