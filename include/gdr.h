@@ -565,13 +565,17 @@ gdr_status_t gdr_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
  *   derase         [B, T, H, Dk] fp32 dL/db (written)
  *   dwrite         [B, T, H, Dv] fp32 dL/dw (written)
  *   ds0            [B, H, Dv, Dk] fp32 dL/dS_0, or NULL (not written)
+ *                  dq, dk, dalpha and derase are sums over the Dv/32
+ *                  blocks of state rows, added by fp32 atomic adds whose
+ *                  order varies: they can differ from run to run in the
+ *                  last bits (dv, dwrite and ds0 are the same bit for bit)
  *   workspace      device memory of at least
  *                  gdr2_chunk_bwd_workspace_size(B, T, H, Dk, Dv) bytes,
  *                  16-byte aligned, owned by the caller, contents on entry
  *                  irrelevant and on return unspecified: the chunk-start
- *                  states (B H ceil(T/16) Dv Dk floats) and per-row-block
- *                  partial sums.  A smaller workspace_bytes is
- *                  GDR_ERR_INVALID.
+ *                  states (B H ceil(T/16) Dv Dk floats) and four
+ *                  accumulators of B T H Dk floats.  A smaller
+ *                  workspace_bytes is GDR_ERR_INVALID.
  *
  * Calls on one workspace must not overlap.  T == 0 copies ds_final (or
  * zeros) into ds0.  Every tensor argument needs 16-byte alignment.
