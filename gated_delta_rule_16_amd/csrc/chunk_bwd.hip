@@ -64,7 +64,7 @@ struct BwdParams {
     const float *alpha, *beta, *s0, *dsf;
     float *dv, *ds0;
     float* ck;                     // [BH][nch][Dv][Dk] chunk-start states
-    float* ta;                     // [BH NRB][nch][2][16][16]: T and AK of each chunk
+    const float* ta;               // [BH][nch][2][16][16]: T and AK of each chunk
     float *aq, *ak;                // [BTH][Dk] dq, dk accumulators (zero on entry)
     float *pb, *pg;                // [NRB][BTH]: dbeta, d log alpha
     bool l2norm;                   // q, k normalised on load (GDR_L2NORM_QK)
@@ -191,6 +191,135 @@ struct Gates {
     float br[4], Gr[4], lr[4], rr[4];
 };
 
+// The gate scalars of a chunk of n tokens in one wave, from token
+// lane % 16's alpha and beta (alpha = 1 past the end): a DPP scan of
+// log2 alpha across the 16 lanes of each row, bpermutes for the r-arrays.
+__device__ __forceinline__ Gates chunk_gates(float a, float b, int n, int lane) {
+    const int l16 = lane & 15, lg = lane >> 4;
+    Gates g;
+    g.be = b;
+    g.G = rscan16(l16 < n ? safe_log2(a) : 0.f);
+    const float GC = lane_value(g.G, 15);
+    g.lam = ex2(g.G);
+    g.rho = ex2(GC - g.G);
+    g.lamC = ex2(GC);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * lg + i;
+        g.br[i] = __shfl(g.be, r, 64);
+        g.Gr[i] = __shfl(g.G, r, 64);
+        g.lr[i] = __shfl(g.lam, r, 64);
+        g.rr[i] = __shfl(g.rho, r, 64);
+    }
+    return g;
+}
+
+// Gamma at the accumulator entries (r = 4 (lane / 16) + i, s = lane % 16),
+// masked to s < r (strict) or s <= r
+__device__ __forceinline__ f32x4 gamma_tile(const Gates& g, bool strict, int lane) {
+    const int l16 = lane & 15, lg = lane >> 4;
+    f32x4 gm;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * lg + i;
+        gm[i] = (strict ? l16 < r : l16 <= r) ? ex2(g.Gr[i] - g.G) : 0.f;
+    }
+    return gm;
+}
+
+// T = (I + A)^{-1}, A = diag(beta) AK, by one wave (tables at row pitch PC):
+// lane 4 c + q owns column c, rows 4 q .. 4 q + 3; row r of the column is
+// delta_rc - beta_r sum_{m < r} AK_rm T_mc (AK's upper part is zero), the
+// four partial sums joined by a quad reduction.  The lane's AK entries are
+// read before the first row.
+template <int PC>
+__device__ __forceinline__ void solve_t(const float* AKs, float* Ts, const Gates& g, int lane) {
+    const int c = lane >> 2, q = lane & 3;
+    f32x4 ak[CB];
+#pragma unroll
+    for (int r = 0; r < CB; ++r) ak[r] = ld4(AKs + r * PC + 4 * q);
+    float tq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < CB; ++r) {
+        float part = (ak[r][0] * tq[0] + ak[r][1] * tq[1]) + (ak[r][2] * tq[2] + ak[r][3] * tq[3]);
+        part = qsum(part);
+        const float t = r < c ? 0.f : (r == c ? 1.f : 0.f) - lane_value(g.be, r) * part;
+        if (q == (r >> 2)) tq[r & 3] = t;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Ts[(4 * q + j) * PC + c] = tq[j];
+}
+
+struct SolveParams {
+    int64_t T, H, nch, nchunks;    // nchunks = B H nch
+    const void* k;
+    const float *alpha, *beta;
+    float* ta;                     // [B H nch][2][16][16]: T, then AK
+    bool l2norm;
+};
+
+// T and AK = Gamma (.) K K^T (s < r) of every chunk, one wave per (b, h,
+// chunk): they depend on the chunk's keys and gates only, so the main
+// kernel's sweeps read them instead of solving one triangle per chunk in
+// sequence.  Lane l loads channels DK/4 (l % 4) .. of token l / 4.
+template <int DK, typename TIn>
+__global__ __launch_bounds__(256) void gdn_bwd_solve(SolveParams p) {
+    constexpr int PK = DK + 4, PC = 20, NQK = DK / 16, CW = DK / 4;
+    constexpr int PER = CB * PK + 2 * CB * PC;
+    __shared__ __align__(16) float sm[4 * PER];
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
+    const int64_t ci = (int64_t)blockIdx.x * 4 + wv;
+    if (ci >= p.nchunks) return;   // whole waves; no workgroup barrier below
+    const int64_t bh = ci / p.nch, c = ci % p.nch;
+    const int64_t h = bh % p.H, b = bh / p.H;
+    float* Kw = sm + wv * PER;
+    float* AKs = Kw + CB * PK;
+    float* Ts = AKs + CB * PC;
+    const int n = (int)min((int64_t)CB, p.T - c * CB);
+    const int64_t tb = (b * p.T + c * CB) * p.H + h;
+    const int HDK = (int)(p.H * DK), HI = (int)p.H;
+    const int t = lane >> 2, c0 = CW * (lane & 3);
+    constexpr int SI = sizeof(TIn);
+    uint32_t kw[CW / packed<TIn>::PER_WORD];
+    bld(kw, rsrc(reinterpret_cast<const TIn*>(p.k) + tb * DK, n * HDK * SI), (t * HDK + c0) * SI);
+    const float a = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rsrc(p.alpha + tb, n * HI * 4), l16 * HI * 4, 0, 0));
+    const float bt = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rsrc(p.beta + tb, n * HI * 4), l16 * HI * 4, 0, 0));
+    float kn = 1.f;
+    if (p.l2norm) {
+        float ss = 0.f;
+#pragma unroll
+        for (int y = 0; y < CW; ++y) {
+            const float kk = packed<TIn>::at(kw, y);
+            ss += kk * kk;
+        }
+        kn = l2_inv(qsum(ss));
+    }
+#pragma unroll
+    for (int y0 = 0; y0 < CW; y0 += 4) {
+        f32x4 kv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kv[e] = packed<TIn>::at(kw, y0 + e) * kn;
+        *reinterpret_cast<f32x4*>(Kw + t * PK + c0 + y0) = kv;
+    }
+    const Gates g = chunk_gates(a, bt, n, lane);
+    wave_sync();
+    const f32x4 kk = mma16<NQK, true, true>(f32x4{0.f, 0.f, 0.f, 0.f}, Kw, PK, Kw, PK, lane);
+    const f32x4 gm = gamma_tile(g, true, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) AKs[(4 * lg + i) * PC + l16] = kk[i] * gm[i];
+    wave_sync();
+    solve_t<PC>(AKs, Ts, g, lane);
+    wave_sync();
+    const __amdgpu_buffer_rsrc_t ro = rsrc(p.ta + ci * 512, 512 * 4);
+    const int r = lane >> 2, c4 = 4 * (lane & 3);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ld4(Ts + r * PC + c4)), ro,
+                                           (r * 16 + c4) * 4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ld4(AKs + r * PC + c4)), ro,
+                                           (256 + r * 16 + c4) * 4, 0, 0);
+}
+
 template <int DK, int DV, typename TIn, typename TD>
 __global__ __launch_bounds__(NTB) __attribute__((amdgpu_waves_per_eu(2)))
 void gdn_bwd_kernel(BwdParams p) {
@@ -246,7 +375,7 @@ void gdn_bwd_kernel(BwdParams p) {
     const int row0 = rb * RBW;
     const int64_t nch = (T + CB - 1) / CB;
     float* ckb = p.ck + bh * nch * DV * DK;
-    float* tab = p.ta + wid * nch * 512;
+    const float* tab = p.ta + bh * nch * 512;
     auto tok = [&](int64_t t) { return (b * T + t) * H + h; };
     const int tr = tid >> 4;                   // this thread's token for the loads
     const int j0 = NC * (tid & 15);            // .. and its key channels
@@ -311,35 +440,8 @@ void gdn_bwd_kernel(BwdParams p) {
             if (bwd) DOs[o] = packed<TD>::at(x.d, e);
         }
     };
-    // the gate scalars of a chunk of n tokens (alpha = 1 past the end)
-    auto gates = [&](const PF& x, int n) {
-        Gates g;
-        g.be = x.b;
-        g.G = rscan16(l16 < n ? safe_log2(x.a) : 0.f);
-        const float GC = lane_value(g.G, 15);
-        g.lam = ex2(g.G);
-        g.rho = ex2(GC - g.G);
-        g.lamC = ex2(GC);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * lg + i;
-            g.br[i] = __shfl(g.be, r, 64);
-            g.Gr[i] = __shfl(g.G, r, 64);
-            g.lr[i] = __shfl(g.lam, r, 64);
-            g.rr[i] = __shfl(g.rho, r, 64);
-        }
-        return g;
-    };
-    // Gamma at the accumulator entries (r, s = l16), masked to s < r or s <= r
-    auto gamma = [&](const Gates& g, bool strict) {
-        f32x4 gm;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * lg + i;
-            gm[i] = (strict ? l16 < r : l16 <= r) ? ex2(g.Gr[i] - g.G) : 0.f;
-        }
-        return gm;
-    };
+    auto gates = [&](const PF& x, int n) { return chunk_gates(x.a, x.b, n, lane); };
+    auto gamma = [&](const Gates& g, bool strict) { return gamma_tile(g, strict, lane); };
     // sum over the pairs s < t <= r of W_rs (accumulator layout), for t = l16
     auto straddle = [&](const f32x4& w) {
         float acc = 0.f;
@@ -351,33 +453,6 @@ void gdn_bwd_kernel(BwdParams p) {
         acc += __shfl_xor(acc, 16, 64);
         acc += __shfl_xor(acc, 32, 64);
         return acc;
-    };
-    // A = diag(beta) AK, K K^T scaled by Gamma below the diagonal (wave 0)
-    auto ak_tile = [&](const Gates& g) {
-        const f32x4 kk = mma16<NQK, true, true>(zero4, Ks, L::PK, Ks, L::PK, lane);
-        const f32x4 gm = gamma(g, true);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) AKs[(4 * lg + i) * L::PC + l16] = kk[i] * gm[i];
-    };
-    // T = (I + A)^{-1} by one wave: lane 4 c + q owns column c, rows
-    // 4 q .. 4 q + 3; row r of the column is delta_rc - beta_r sum_{m < r}
-    // AK_rm T_mc (AK's upper part is zero), the four partial sums joined by
-    // a quad reduction.  The lane's AK entries are read before the first row.
-    auto tsolve = [&](const Gates& g) {
-        const int c = lane >> 2, q = lane & 3;
-        f32x4 ak[CB];
-#pragma unroll
-        for (int r = 0; r < CB; ++r) ak[r] = ld4(AKs + r * L::PC + 4 * q);
-        float tq[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < CB; ++r) {
-            float part = (ak[r][0] * tq[0] + ak[r][1] * tq[1]) + (ak[r][2] * tq[2] + ak[r][3] * tq[3]);
-            part = qsum(part);
-            const float t = r < c ? 0.f : (r == c ? 1.f : 0.f) - lane_value(g.be, r) * part;
-            if (q == (r >> 2)) tq[r & 3] = t;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Ts[(4 * q + j) * L::PC + c] = tq[j];
     };
     // K S^T (or K G'^T) for state-row tile t
     auto ks_tile = [&](const float* M, int t) {
@@ -396,54 +471,55 @@ void gdn_bwd_kernel(BwdParams p) {
             *reinterpret_cast<f32x4*>(Ss + i * L::PK + j) = sv[it];
         }
     }
+    // this thread's two entries of a chunk's T and AK (from gdn_bwd_solve)
+    u32x2w tv;
+    auto fetch_t = [&](int64_t c) {
+        tv = __builtin_amdgcn_raw_buffer_load_b64(rsrc(tab + c * 512, 512 * 4), 8 * tid, 0, 0);
+    };
+    auto commit_t = [&]() {
+        const int e = 2 * tid, r = (e & 255) >> 4, col = e & 15;
+        float* d = (e < 256 ? Ts : AKs) + r * L::PC + col;
+        d[0] = __uint_as_float(tv[0]);
+        d[1] = __uint_as_float(tv[1]);
+    };
     PF x;
     fetch(x, 0, false);
+    fetch_t(0);
     for (int64_t c = 0; c < nch; ++c) {
         renew_lane();
         __syncthreads();
         commit(x, c, false);
+        commit_t();
         const Gates g = gates(x, chunk_len(c));
-        if (c + 1 < nch) fetch(x, c + 1, false);
+        if (c + 1 < nch) {
+            fetch(x, c + 1, false);
+            fetch_t(c + 1);
+        }
         __syncthreads();
-        // wave 0: A and T (kept for the reverse sweep);  waves 1, 2: R;
-        // wave 3: S to the workspace
-        if (wv == 0) {
-            ak_tile(g);
-            wave_sync();
-            tsolve(g);
-            wave_sync();
-            const __amdgpu_buffer_rsrc_t rt = rsrc(tab + c * 512, 512 * 4);
-            const int r = lane >> 2, c4 = 4 * (lane & 3);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ld4(Ts + r * L::PC + c4)),
-                                                   rt, (r * 16 + c4) * 4, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ld4(AKs + r * L::PC + c4)),
-                                                   rt, (256 + r * 16 + c4) * 4, 0, 0);
-        } else if (wv <= 2) {
-            const int t = wv - 1;
+        // waves 0, 1: K S^T, R, then diag(rho) T R on row tile wv;
+        // waves 2, 3: S to the workspace, rows 16 (wv - 2) ..
+        if (wv < 2) {
+            const int t = wv;
             const f32x4 ks = ks_tile(Ss, t);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int o = (4 * lg + i) * L::PR + 16 * t + l16;
                 Rs[o] = g.br[i] * (Vs[o] - g.lr[i] * ks[i]);
             }
+            wave_sync();
+            const f32x4 u = mma16<1, true, false>(zero4, Ts, L::PC, Rs + 16 * t, L::PR, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) UTs[(4 * lg + i) * L::PR + 16 * t + l16] = g.rr[i] * u[i];
         } else {
             const __amdgpu_buffer_rsrc_t rc = rsrc(ckb + c * DV * DK, DV * DK * 4);
 #pragma unroll
-            for (int it = 0; it < NSW; ++it) {
-                const int e4 = lane + 64 * it;
+            for (int it = 0; it < NSW / 2; ++it) {
+                const int e4 = lane + 64 * it + (wv - 2) * (NSW / 2) * 64;
                 const int i = e4 / (DK / 4), j = 4 * (e4 % (DK / 4));
                 __builtin_amdgcn_raw_buffer_store_b128(
                     __builtin_bit_cast(u32x4, ld4(Ss + i * L::PK + j)), rc,
                     ((row0 + i) * DK + j) * 4, 0, 0);
             }
-        }
-        __syncthreads();
-        // diag(rho) T R (waves 0, 1)
-        if (wv < 2) {
-            const int t = wv;
-            const f32x4 u = mma16<1, true, false>(zero4, Ts, L::PC, Rs + 16 * t, L::PR, lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) UTs[(4 * lg + i) * L::PR + 16 * t + l16] = g.rr[i] * u[i];
         }
         __syncthreads();
         // S <- lambda_C S + (diag(rho) U)^T K on this wave's channel tiles
@@ -500,10 +576,6 @@ void gdn_bwd_kernel(BwdParams p) {
         bstore(db, rsrc(p.pb + o, bytes), t * HI * 4);
         bstore(dl, rsrc(p.pg + o, bytes), t * HI * 4);
     };
-    u32x2w tv;   // this thread's two entries of the chunk's T and AK
-    auto fetch_t = [&](int64_t c) {
-        tv = __builtin_amdgcn_raw_buffer_load_b64(rsrc(tab + c * 512, 512 * 4), 8 * tid, 0, 0);
-    };
     f32x4 sv[NSV];
     auto fetch_s = [&](int64_t c) {
         const __amdgpu_buffer_rsrc_t rc = rsrc(ckb + c * DV * DK, DV * DK * 4);
@@ -537,12 +609,7 @@ void gdn_bwd_kernel(BwdParams p) {
             *reinterpret_cast<f32x4*>(Ss + i * L::PK + j) = sv[it];
         }
         commit(x, c, true);
-        {
-            const int e = 2 * tid, r = (e & 255) >> 4, col = e & 15;
-            float* d = (e < 256 ? Ts : AKs) + r * L::PC + col;
-            d[0] = __uint_as_float(tv[0]);
-            d[1] = __uint_as_float(tv[1]);
-        }
+        commit_t();
         const Gates g = gates(x, n);
         if (c > 0) {
             fetch(x, c - 1, true);
@@ -550,7 +617,7 @@ void gdn_bwd_kernel(BwdParams p) {
             fetch_t(c - 1);
         }
         __syncthreads();
-        // ---- (T and AK come from the forward sweep)  waves 0, 3: X, R rows
+        // ---- (T and AK from gdn_bwd_solve)  waves 0, 3: X, R rows
         //      0..15, 16..31;  wave 1: P, K G'^T rows 0..15 and the later
         //      chunk's gate gradients;  wave 2: K G'^T rows 16..31;
         //      waves 2, 3: <G', S> over rows 0..15, 16..31
@@ -840,8 +907,9 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
     p.dv = a.dv;
     p.ds0 = a.ds0;
     p.ck = reinterpret_cast<float*>(a.workspace);
-    p.ta = p.ck + BH * nch * DV * DK;
-    float* wq = p.ta + BH * NRB * nch * 512;   // accumulators of the fused norm's input
+    float* ta = p.ck + BH * nch * DV * DK;
+    p.ta = ta;
+    float* wq = ta + BH * nch * 512;           // accumulators of the fused norm's input
     float* wk = wq + BTH * DK;
     p.pb = wk + BTH * DK;
     p.pg = p.pb + NRB * BTH;
@@ -855,6 +923,21 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
     if (e != hipSuccess) return e;
     const size_t lds = sizeof(float) * BL<DK>::TOTAL;
     auto fn = gdn_bwd_kernel<DK, DV, TIn, TD>;
+    // T and AK of every chunk first
+    SolveParams sp{};
+    sp.T = a.T;
+    sp.H = a.H;
+    sp.nch = nch;
+    sp.nchunks = BH * nch;
+    sp.k = a.k;
+    sp.alpha = a.alpha;
+    sp.beta = a.beta;
+    sp.ta = ta;
+    sp.l2norm = a.l2norm;
+    hipLaunchKernelGGL((gdn_bwd_solve<DK, TIn>), dim3((unsigned)((BH * nch + 3) / 4)), dim3(256), 0,
+                       a.stream, sp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     e = hipFuncSetAttribute((const void*)fn,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -889,7 +972,7 @@ size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t 
     const int64_t nrb = Dv / RBW;
     const int64_t BTH = B * T * H;
     return sizeof(float) *
-           (size_t)(B * H * nch * Dv * Dk + B * H * nrb * nch * 512 + 2 * BTH * Dk + 2 * nrb * BTH);
+           (size_t)(B * H * nch * Dv * Dk + B * H * nch * 512 + 2 * BTH * Dk + 2 * nrb * BTH);
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a) {

@@ -522,8 +522,8 @@ gdr_status_t gdr_output_gate_bwd_noalloc(int64_t N, int64_t H, int64_t Dv,
  *                  16-byte aligned, owned by the caller; its contents on
  *                  entry do not matter and on return are unspecified.
  *                  It holds the chunk-start states (B H ceil(T/16) Dv Dk
- *                  floats), each block of 32 state rows' copy of every
- *                  chunk's T and decayed Gram matrix (512 floats), dq and
+ *                  floats), every chunk's T and decayed Gram matrix
+ *                  (512 floats per (b, h, chunk)), dq and
  *                  dk accumulators for GDR_L2NORM_QK (2 B T H Dk floats) and
  *                  per-row-block partial sums of the gate gradients
  *                  (2 (Dv/32) B T H floats).  A smaller workspace_bytes is
