@@ -94,11 +94,11 @@ struct BL {
     static constexpr int V = Y + NN;
     static constexpr int X = V + NR;
     static constexpr int R = X + NR;
-    static constexpr int DO = R + NR;            // dL/do, then diag(lambda) dL/do
+    static constexpr int DO = R + NR;            // dL/do
     static constexpr int U = DO + NR;
     static constexpr int UT = U + NR;            // diag(rho) U
     static constexpr int DU = UT + NR;
-    static constexpr int KG = DU + NR;           // K G'^T
+    static constexpr int KG = DU + NR;           // K G'^T, then diag(lambda) dL/do
     static constexpr int DRB = KG + NR;          // diag(beta lambda) dR
     // per-token partial sums, two sets (chunk parity: a chunk's set is read
     // while the next chunk writes the other), offsets within a set:
@@ -349,6 +349,7 @@ void gdn_bwd_kernel(BwdParams p) {
     float* UTs = sm + L::UT;
     float* DUs = sm + L::DU;
     float* KGs = sm + L::KG;
+    float* DOLs = KGs;   // diag(lambda) dL/do from the third phase of a chunk on
     float* DRBs = sm + L::DRB;
 
     const int tid = threadIdx.x;
@@ -617,53 +618,48 @@ void gdn_bwd_kernel(BwdParams p) {
             fetch_t(c - 1);
         }
         __syncthreads();
-        // ---- (T and AK from gdn_bwd_solve)  waves 0, 3: X, R rows
-        //      0..15, 16..31;  wave 1: P, K G'^T rows 0..15 and the later
-        //      chunk's gate gradients;  wave 2: K G'^T rows 16..31;
-        //      waves 2, 3: <G', S> over rows 0..15, 16..31
-        if (wv == 1) {
-            const f32x4 qk = mma16<NQK, true, true>(zero4, Qs, L::PK, Ks, L::PK, lane);
-            const f32x4 kg = ks_tile(Gs, 0);
-            const f32x4 gm = gamma(g, false);
+        // ---- (T and AK from gdn_bwd_solve)  waves 0, 3: X, R rows 0..15,
+        //      16..31;  wave 0: P;  waves 1, 2: K G'^T rows 0..15, 16..31;
+        //      wave 1: the later chunk's gate gradients;  waves 2, 3:
+        //      <G', S> over rows 0..15, 16..31
+        if (wv == 0 || wv == 3) {
+            const int t = wv == 0 ? 0 : 1;
+            const f32x4 ks = ks_tile(Ss, t);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 4 * lg + i;
-                Ps[r * L::PC + l16] = qk[i] * gm[i];
-                KGs[r * L::PR + l16] = kg[i];
+                const int o = (4 * lg + i) * L::PR + 16 * t + l16;
+                const float xv = Vs[o] - g.lr[i] * ks[i];
+                Xs[o] = xv;
+                Rs[o] = g.br[i] * xv;
             }
+        } else {
+            const int t = wv - 1;
+            const f32x4 kg = ks_tile(Gs, t);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) KGs[(4 * lg + i) * L::PR + 16 * t + l16] = kg[i];
+        }
+        if (wv == 0) {
+            const f32x4 qk = mma16<NQK, true, true>(zero4, Qs, L::PK, Ks, L::PK, lane);
+            const f32x4 gm = gamma(g, false);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Ps[(4 * lg + i) * L::PC + l16] = qk[i] * gm[i];
+        } else if (wv == 1) {
             if (c + 1 < nch) finalize(c + 1, scr);
         } else {
-            if (wv == 2) {
-                const f32x4 kg = ks_tile(Gs, 1);
+            // lane: 4 channels (16-byte reads), CG / 4 of the 16 rows
+            const int t = wv - 2;
+            constexpr int CG = DK / 4;
+            const int c4 = 4 * (lane % CG), rg = lane / CG;
+            float sg = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) KGs[(4 * lg + i) * L::PR + 16 + l16] = kg[i];
-            } else {
-                const int t = wv == 0 ? 0 : 1;
-                const f32x4 ks = ks_tile(Ss, t);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int o = (4 * lg + i) * L::PR + 16 * t + l16;
-                    const float xv = Vs[o] - g.lr[i] * ks[i];
-                    Xs[o] = xv;
-                    Rs[o] = g.br[i] * xv;
-                }
+            for (int m = 0; m < CG / 4; ++m) {
+                const int i = 16 * t + (CG / 4) * rg + m;
+                const f32x4 gv = ld4(Gs + i * L::PK + c4), sv4 = ld4(Ss + i * L::PK + c4);
+                sg += (gv[0] * sv4[0] + gv[1] * sv4[1]) + (gv[2] * sv4[2] + gv[3] * sv4[3]);
             }
-            if (wv >= 2) {
-                // lane: 4 channels (16-byte reads), CG / 4 of the 16 rows
-                const int t = wv - 2;
-                constexpr int CG = DK / 4;
-                const int c4 = 4 * (lane % CG), rg = lane / CG;
-                float sg = 0.f;
 #pragma unroll
-                for (int m = 0; m < CG / 4; ++m) {
-                    const int i = 16 * t + (CG / 4) * rg + m;
-                    const f32x4 gv = ld4(Gs + i * L::PK + c4), sv4 = ld4(Ss + i * L::PK + c4);
-                    sg += (gv[0] * sv4[0] + gv[1] * sv4[1]) + (gv[2] * sv4[2] + gv[3] * sv4[3]);
-                }
-#pragma unroll
-                for (int m = 32; m >= 1; m >>= 1) sg += __shfl_xor(sg, m, 64);
-                if (lane == 0) scw[L::GSUM + t] = g.lamC * sg;
-            }
+            for (int m = 32; m >= 1; m >>= 1) sg += __shfl_xor(sg, m, 64);
+            if (lane == 0) scw[L::GSUM + t] = g.lamC * sg;
         }
         __syncthreads();
         // ---- U = T R and kappa (waves 0, 1);
@@ -694,8 +690,8 @@ void gdn_bwd_kernel(BwdParams p) {
             for (int i = 0; i < 4; ++i) DUs[(4 * lg + i) * L::PR + 16 * t + l16] = acc[i];
         }
         __syncthreads();
-        // ---- dR = T^T dU (waves 0, 1: dv to HBM, dbeta and tau row sums);
-        //      dP = dO U^T, D_P, pair sums, then dO -> diag(lambda) dO (wave 2);
+        // ---- dR = T^T dU (waves 0, 1: dv to HBM, dbeta and tau row sums,
+        //      then diag(lambda) dO);  dP = dO U^T, D_P, pair sums (wave 2);
         //      dA and M (wave 3)
         if (wv < 2) {
             const int t = wv;
@@ -718,6 +714,16 @@ void gdn_bwd_kernel(BwdParams p) {
                     scw[L::TAUR + 16 * t + 4 * lg + i] = -g.br[i] * st[i];
                 }
             }
+            // diag(lambda) dL/do, tokens 8 t .. 8 t + 7, into K G'^T's place
+            // (dead after the last phase): element lane + 64 e is token
+            // 8 t + 2 e + lane / 32, row lane % 32
+#pragma unroll
+            for (int e = 0; e < CB * RBW / 128; ++e) {
+                const int r = 8 * t + 2 * e;
+                const float lm = lane < 32 ? lane_value(g.lam, r) : lane_value(g.lam, r + 1);
+                const int o = (r + (lane >> 5)) * L::PR + (lane & 31);
+                DOLs[o] = DOs[o] * lm;
+            }
         } else if (wv == 2) {
             const f32x4 dp = mma16<2, true, true>(zero4, DOs, L::PR, Us, L::PR, lane);
             const f32x4 gm = gamma(g, false);
@@ -731,13 +737,6 @@ void gdn_bwd_kernel(BwdParams p) {
             }
             const float pr = straddle(w);
             if (lane < 16) scw[L::PRP + lane] = pr;
-            // only this wave reads dL/do in this phase: element lane + 64 e
-            // is token 2 e + lane / 32, row lane % 32
-#pragma unroll
-            for (int e = 0; e < CB * RBW / 64; ++e) {
-                const float lm = lane < 32 ? lane_value(g.lam, 2 * e) : lane_value(g.lam, 2 * e + 1);
-                DOs[(2 * e + (lane >> 5)) * L::PR + (lane & 31)] *= lm;
-            }
         } else {
             // dT = dU R^T, Y = dT T^T, dA = -T^T Y (strict), D_A, the A term
             // of dbeta, its pair sums and M
@@ -788,7 +787,7 @@ void gdn_bwd_kernel(BwdParams p) {
         float tq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct)
-            dq[ct] = mma16<2, true, false>(zero4, DOs, L::PR, Ss + 16 * (CTW * wv + ct), L::PK, lane);
+            dq[ct] = mma16<2, true, false>(zero4, DOLs, L::PR, Ss + 16 * (CTW * wv + ct), L::PK, lane);
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct)
             dk[ct] = mma16<2, true, false>(zero4, UTs, L::PR, Gs + 16 * (CTW * wv + ct), L::PK, lane);
@@ -832,7 +831,7 @@ void gdn_bwd_kernel(BwdParams p) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         gu[a2][ct][i] = Gs[(16 * a2 + 4 * lg + i) * L::PK + cc] * g.lamC;
-                    gu[a2][ct] = mma16<1, false, false>(gu[a2][ct], DOs + 16 * a2, L::PR,
+                    gu[a2][ct] = mma16<1, false, false>(gu[a2][ct], DOLs + 16 * a2, L::PR,
                                                         Qs + 16 * (CTW * wv + ct), L::PK, lane);
                 }
 #pragma unroll
