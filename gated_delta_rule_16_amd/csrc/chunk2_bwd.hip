@@ -469,7 +469,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         const bool wide = tables(true);
         // ---- wave 0: A, then T = (I + A)^{-1};  wave 1: P and K~ G'^T rows
         //      0..15 (into dU);  wave 2: R rows 0..15 and K~ G'^T rows 16..31;
-        //      wave 3: R rows 16..31 and sum_i G' (.) S per channel
+        //      wave 3: R rows 16..31
         //      (wide chunks: A and P entry by entry by all threads first)
         if (wide) {
             ap_entries(true);
@@ -493,17 +493,29 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             for (int i = 0; i < 4; ++i) dUs[(4 * lg + i) * L::PR + 16 * t + l16] = acc[i];
         } else {
             r_tile(1);
-#pragma unroll
-            for (int j = 0; j < DK / 64; ++j) {
-                const int cc = lane + 64 * j;
-                float sacc = 0.f;
-#pragma unroll 8
-                for (int i = 0; i < R2; ++i) sacc += Gs[i * L::PK + cc] * Ss[i * L::PK + cc];
-                GSc[cc] = sacc;
-            }
         }
         __syncthreads();
-        // ---- U = T R (waves 0, 1);  dU = K~ G'^T + P^T dO (waves 2, 3)
+        // ---- U = T R (waves 0, 1);  dU = K~ G'^T + P^T dO (waves 2, 3);
+        //      then sum_i G' (.) S per channel, DK / 4 channels per wave:
+        //      lane = channel group cg (4 channels, 16-byte reads) + NG x row
+        //      group, its rows summed, then the row groups by shuffles
+        {
+            constexpr int NG = DK / 16, RPL = NG / 2;
+            const int cg = lane % NG, rg = lane / NG, c0 = DK / 4 * wv + 4 * cg;
+            f32x4 sacc = zero4;
+#pragma unroll
+            for (int m = 0; m < RPL; ++m) {
+                const int i = RPL * rg + m;
+                const f32x4 gv = ld4(Gs + i * L::PK + c0), sv4 = ld4(Ss + i * L::PK + c0);
+#pragma unroll
+                for (int z = 0; z < 4; ++z) sacc[z] += gv[z] * sv4[z];
+            }
+#pragma unroll
+            for (int m = NG; m < 64; m *= 2)
+#pragma unroll
+                for (int z = 0; z < 4; ++z) sacc[z] += __shfl_xor(sacc[z], m, 64);
+            if (rg == 0) *reinterpret_cast<f32x4*>(GSc + c0) = sacc;
+        }
         if (wv < 2) {
             const int t = wv;
             const f32x4 acc = mma16<1, true, false>(zero4, Ts, L::PC, Rs + 16 * t, L::PR);
