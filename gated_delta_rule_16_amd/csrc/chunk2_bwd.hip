@@ -73,6 +73,7 @@ struct Bwd2Params {
     float* ck;                     // [BH][nch][Dv][Dk]
     float *pq, *pk, *pb, *pg;      // [BTH][Dk] accumulators of dq, dk, derase, d log alpha
                                    // (zero on entry)
+    const float* tt;               // [BH][nch][16][16]: T of each chunk (gdn2_bwd_solve)
     bool l2norm;                   // q, k normalised on load (GDR_L2NORM_QK)
 };
 
@@ -129,6 +130,149 @@ struct Pre2 {
     uint32_t k[WK], b[WK], a[WK], q[WK];
     uint32_t w[WP], v[WP], d[WD];
 };
+
+struct Solve2Params {
+    int64_t T, H, nch, nchunks;
+    const void *k, *alpha, *erase;
+    float* tt;                     // [B H nch][16][16]
+    bool l2norm;
+};
+
+// one element of a row of TIn at index i of a buffer, as fp32
+template <typename TIn>
+__device__ __forceinline__ float bload1(__amdgpu_buffer_rsrc_t r, int i) {
+    if constexpr (sizeof(TIn) == 2)
+        return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, 2 * i, 0, 0) << 16);
+    else
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 4 * i, 0, 0));
+}
+
+// T = (I + A)^{-1} of every chunk, A_rs = sum_c E_rc K_sc 2^{G_rc - G_sc}
+// (s < r), formed as the main kernel formed it (the factored decay, or entry
+// by entry in a wide chunk): it depends on the chunk's keys, erase and decay
+// only, so the chunks are solved side by side here and the sweeps read T.
+// One 64-thread workgroup per (b, h, chunk); lane l takes channels
+// l + 64 j of every token.
+template <int DK, typename TIn>
+__global__ __launch_bounds__(64) void gdn2_bwd_solve(Solve2Params p) {
+    constexpr int PK = DK + 4, PC = 20, NQK = DK / 16, CPL = DK / 64;
+    __shared__ __align__(16) float t1[C2 * PK], t2[C2 * PK], t3[C2 * PK], As[C2 * PC], Ts[C2 * PC];
+    const int lane = threadIdx.x, l16 = lane & 15, lg = lane >> 4;
+    const int64_t ci = blockIdx.x;
+    const int64_t bh = ci / p.nch, c = ci % p.nch;
+    const int64_t h = bh % p.H, b = bh / p.H;
+    const int n = (int)min((int64_t)C2, p.T - c * C2);
+    const int64_t tb = (b * p.T + c * C2) * p.H + h;
+    const int HDK = (int)(p.H * DK);
+    constexpr int SI = sizeof(TIn);
+    const __amdgpu_buffer_rsrc_t rk =
+        rsrc(reinterpret_cast<const TIn*>(p.k) + tb * DK, n * HDK * SI);
+    const __amdgpu_buffer_rsrc_t re =
+        rsrc(reinterpret_cast<const TIn*>(p.erase) + tb * DK, n * HDK * SI);
+    const __amdgpu_buffer_rsrc_t ra =
+        rsrc(reinterpret_cast<const TIn*>(p.alpha) + tb * DK, n * HDK * SI);
+    // rows past the chunk's end: zero keys and erase, alpha = 1
+    float kv[C2][CPL], ev[C2][CPL], gv[C2][CPL];
+#pragma unroll
+    for (int t = 0; t < C2; ++t)
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int i = t * HDK + lane + 64 * j;
+            kv[t][j] = bload1<TIn>(rk, i);
+            ev[t][j] = bload1<TIn>(re, i);
+            const float a = bload1<TIn>(ra, i);
+            gv[t][j] = t < n ? safe_log2(a) : 0.f;
+        }
+    if (p.l2norm) {
+#pragma unroll
+        for (int t = 0; t < C2; ++t) {
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) ss += kv[t][j] * kv[t][j];
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+            const float kn = l2_inv(ss);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) kv[t][j] *= kn;
+        }
+    }
+    bool wide_here = false;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        float g = 0.f;
+#pragma unroll
+        for (int t = 0; t < C2; ++t) {
+            g += gv[t][j];
+            gv[t][j] = g;            // within-chunk cumulative log2 alpha
+            ev[t][j] *= kv[t][j];    // E = erase (.) k
+        }
+        wide_here |= g < WIDE2;
+    }
+    const bool wide = __ballot(wide_here) != 0;
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    if (!wide) {
+        // A = E~ K^T, E~ = E (.) 2^G, K^ = K (.) 2^-G
+#pragma unroll
+        for (int t = 0; t < C2; ++t)
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                t1[t * PK + lane + 64 * j] = ev[t][j] * ex2(gv[t][j]);
+                t2[t * PK + lane + 64 * j] = kv[t][j] * ex2(fminf(-gv[t][j], 120.f));
+            }
+        wave_sync();
+        const f32x4 acc = mma16<NQK, true, true>(zero4, t1, PK, t2, PK, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * lg + i;
+            As[r * PC + l16] = l16 < r ? acc[i] : 0.f;
+        }
+    } else {
+        // entry by entry from the log decays: lane (r = 4 lg + i, s = l16)
+#pragma unroll
+        for (int t = 0; t < C2; ++t)
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                t1[t * PK + lane + 64 * j] = ev[t][j];
+                t2[t * PK + lane + 64 * j] = kv[t][j];
+                t3[t * PK + lane + 64 * j] = gv[t][j];
+            }
+        wave_sync();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * lg + i;
+            float av = 0.f;
+            if (l16 < r) {
+                for (int cc = 0; cc < DK; cc += 4) {
+                    const f32x4 er = ld4(t1 + r * PK + cc), ks = ld4(t2 + l16 * PK + cc);
+                    const f32x4 gr = ld4(t3 + r * PK + cc), gs = ld4(t3 + l16 * PK + cc);
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) av += er[z] * ks[z] * ex2(gr[z] - gs[z]);
+                }
+            }
+            As[r * PC + l16] = av;
+        }
+    }
+    wave_sync();
+    // T = (I + A)^{-1}: lane 4 c + q owns column c and the rows m = q (mod
+    // 4); row r is delta_rc - sum_{m < r} A_rm T_mc, joined by a quad sum
+    {
+        const int cl = lane >> 2, q = lane & 3;
+        float tq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < C2; ++r) {
+            float part = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) part += As[r * PC + 4 * j + q] * tq[j];
+            part = qsum(part);
+            const float t = r < cl ? 0.f : (r == cl ? 1.f : 0.f) - part;
+            if ((r & 3) == q) tq[r >> 2] = t;
+            if (q == 0) Ts[r * PC + cl] = t;
+        }
+    }
+    wave_sync();
+    const int r = lane >> 2, c4 = 4 * (lane & 3);
+    *reinterpret_cast<f32x4*>(p.tt + ci * 256 + r * 16 + c4) = ld4(Ts + r * PC + c4);
+}
 
 template <int DK, int DV, typename TIn, typename TD>
 __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
@@ -336,24 +480,6 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
             D[r * L::PC + l16] = (strict ? l16 < r : l16 <= r) ? acc[i] : 0.f;
         }
     };
-    // T = (I + A)^{-1} by wave 0: lane 4 c + q owns column c and the rows
-    // m = q (mod 4); row r of the column is delta_rc - sum_{m < r} A_rm T_mc
-    // (A's upper part is stored as zeros), the four partial sums joined by a
-    // quad reduction
-    auto tsolve = [&]() {
-        const int c = lane >> 2, q = lane & 3;
-        float tq[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < C2; ++r) {
-            float part = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) part += As[r * L::PC + 4 * j + q] * tq[j];
-            part = qsum(part);
-            const float t = r < c ? 0.f : (r == c ? 1.f : 0.f) - part;
-            if ((r & 3) == q) tq[r >> 2] = t;
-            if (q == 0) Ts[r * L::PC + c] = t;
-        }
-    };
     // R tile t (rows 16 t ..): R = w (.) v - E~ S^T
     auto r_tile = [&](int t) {
         f32x4 acc = mma16<NQK, true, true>(f32x4{0.f, 0.f, 0.f, 0.f}, Et, L::PK,
@@ -382,8 +508,13 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         }
         put_s(sv, Ss);
     }
+    // this thread's entry of a chunk's T (from gdn2_bwd_solve)
+    float tv;
+    auto fetch_t = [&](int64_t c) { tv = p.tt[(bh * nch + c) * 256 + tid]; };
+    auto commit_t = [&]() { Ts[(tid >> 4) * L::PC + (tid & 15)] = tv; };
     PF x;
     fetch(x, 0, false);
+    fetch_t(0);
     for (int64_t c = 0; c < nch; ++c) {
         __syncthreads();
 #pragma unroll
@@ -394,26 +525,18 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
                 ld4(Ss + i * L::PK + j);
         }
         commit(x, c, false);
-        if (c + 1 < nch) fetch(x, c + 1, false);
-        __syncthreads();
-        const bool wide = tables(false);
-        if (wide) {
-            ap_entries(false);
-            __syncthreads();
-        }
-        if (wv == 0) {
-            if (!wide) {
-                put_nn(mma16<NQK, true, true>(zero4, Et, L::PK, Kh, L::PK), As, true);
-                wave_sync();
-            }
-            tsolve();
-        } else if (wv <= 2) {
-            r_tile(wv - 1);
+        commit_t();
+        if (c + 1 < nch) {
+            fetch(x, c + 1, false);
+            fetch_t(c + 1);
         }
         __syncthreads();
-        // U = T R (waves 0, 1)
+        tables(false);
+        // R, then U = T R, on row tile wv (waves 0, 1)
         if (wv < 2) {
             const int t = wv;
+            r_tile(t);
+            wave_sync();
             const f32x4 acc = mma16<1, true, false>(zero4, Ts, L::PC, Rs + 16 * t, L::PR);
 #pragma unroll
             for (int i = 0; i < 4; ++i) Us[(4 * lg + i) * L::PR + 16 * t + l16] = acc[i];
@@ -452,6 +575,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
     f32x4 sv[NSV];
     fetch(x, nch - 1, true);
     fetch_s(sv, nch - 1);
+    fetch_t(nch - 1);
     // nothing in flight on entry: the compiler can then count the stores
     // each chunk issues after its prefetch instead of waiting for them all
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -461,38 +585,31 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         __syncthreads();
         put_s(sv, Ss);
         commit(x, c, true);
+        commit_t();
         if (c > 0) {
             fetch(x, c - 1, true);
             fetch_s(sv, c - 1);
+            fetch_t(c - 1);
         }
         __syncthreads();
         const bool wide = tables(true);
-        // ---- wave 0: A, then T = (I + A)^{-1};  wave 1: P and K~ G'^T rows
-        //      0..15 (into dU);  wave 2: R rows 0..15 and K~ G'^T rows 16..31;
-        //      wave 3: R rows 16..31
-        //      (wide chunks: A and P entry by entry by all threads first)
+        // ---- (T from gdn2_bwd_solve)  wave 0: P and K~ G'^T rows 16..31
+        //      (into dU);  wave 1: K~ G'^T rows 0..15;  waves 2, 3: R rows
+        //      0..15, 16..31  (wide chunks: P entry by entry by all threads
+        //      first)
         if (wide) {
             ap_entries(true);
             __syncthreads();
         }
-        if (wv == 0) {
-            if (!wide) {
-                put_nn(mma16<NQK, true, true>(zero4, Et, L::PK, Kh, L::PK), As, true);
-                wave_sync();
-            }
-            tsolve();
-        } else if (wv <= 2) {
-            if (wv == 1) {
-                if (!wide) put_nn(mma16<NQK, true, true>(zero4, Qt, L::PK, Kh, L::PK), Ps, false);
-            } else {
-                r_tile(0);
-            }
-            const int t = wv - 1;
+        if (wv < 2) {
+            if (wv == 0 && !wide)
+                put_nn(mma16<NQK, true, true>(zero4, Qt, L::PK, Kh, L::PK), Ps, false);
+            const int t = 1 - wv;
             const f32x4 acc = mma16<NQK, true, true>(zero4, Kt, L::PK, Gs + 16 * t * L::PK, L::PK);
 #pragma unroll
             for (int i = 0; i < 4; ++i) dUs[(4 * lg + i) * L::PR + 16 * t + l16] = acc[i];
         } else {
-            r_tile(1);
+            r_tile(wv - 2);
         }
         __syncthreads();
         // ---- U = T R (waves 0, 1);  dU = K~ G'^T + P^T dO (waves 2, 3);
@@ -753,9 +870,11 @@ hipError_t launch_bwd2_t(const Bwd2Args& a) {
     p.dw = a.dwrite;
     p.ds0 = a.ds0;
     p.ck = reinterpret_cast<float*>(a.workspace);
+    float* tt = p.ck + BH * nch * DV * DK;
+    p.tt = tt;
     // accumulators: dq, dk and derase go straight into the outputs unless the
     // fused norm's reverse mode follows; d log alpha always in the workspace
-    float* w = p.ck + BH * nch * DV * DK;
+    float* w = tt + BH * nch * 256;
     const int64_t nqk = BTH * DK;
     p.pq = a.l2norm ? w : a.dq;
     p.pk = a.l2norm ? w + nqk : a.dk;
@@ -765,6 +884,21 @@ hipError_t launch_bwd2_t(const Bwd2Args& a) {
     hipError_t e = hipSuccess;
     for (float* acc : {p.pq, p.pk, p.pb, p.pg})
         if (e == hipSuccess) e = launch_zero(acc, nqk * 4, a.stream);
+    if (e != hipSuccess) return e;
+    // T of every chunk first
+    Solve2Params sp{};
+    sp.T = a.T;
+    sp.H = a.H;
+    sp.nch = nch;
+    sp.nchunks = BH * nch;
+    sp.k = a.k;
+    sp.alpha = a.alpha;
+    sp.erase = a.erase;
+    sp.tt = tt;
+    sp.l2norm = a.l2norm;
+    hipLaunchKernelGGL((gdn2_bwd_solve<DK, TIn>), dim3((unsigned)(BH * nch)), dim3(64), 0, a.stream,
+                       sp);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_main<DK, DV, TIn, TD>(p, BH, a.stream);
     if (e != hipSuccess) return e;
@@ -794,7 +928,7 @@ size_t bwd2_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t
     const int64_t nch = (T + C2 - 1) / C2;
     const int64_t nrb = Dv / R2;
     (void)nrb;
-    return sizeof(float) * (size_t)(B * H * nch * Dv * Dk + 4 * B * T * H * Dk);
+    return sizeof(float) * (size_t)(B * H * nch * Dv * Dk + B * H * nch * 256 + 4 * B * T * H * Dk);
 }
 
 hipError_t launch_chunk2_bwd(const Bwd2Args& a) {

@@ -215,10 +215,11 @@ def bwd2(gdr, B=1, T=8, H=1, Dk=64, Dv=64, dt=1, q=A16, k=A16, v=A16, a=A16, e=A
 
 
 def test_bwd2_workspace_size(gdr):
-    """Chunk-start states (B H ceil(T/16) Dv Dk floats) plus accumulators of
-    dq, dk, derase and d log alpha (4 Dk floats per token-head)."""
+    """Chunk-start states (B H ceil(T/16) Dv Dk floats), each chunk's T
+    (16 x 16 floats) and accumulators of dq, dk, derase and d log alpha
+    (4 Dk floats per token-head)."""
     assert gdr.gdr2_chunk_bwd_workspace_size(2, 100, 3, 128, 64) == \
-        4 * (2 * 3 * 7 * 64 * 128 + 4 * 600 * 128)
+        4 * (2 * 3 * 7 * 64 * 128 + 2 * 3 * 7 * 256 + 4 * 600 * 128)
     assert gdr.gdr2_chunk_bwd_workspace_size(1, 8, 1, 64, 96) == 0
     assert gdr.gdr2_chunk_bwd_workspace_size(1, -8, 1, 64, 64) == 0
 
