@@ -573,7 +573,8 @@ gdr_status_t gdr_chunk_bwd(int64_t B, int64_t T, int64_t H, int64_t Dk,
  *                  gdr2_chunk_bwd_workspace_size(B, T, H, Dk, Dv) bytes,
  *                  16-byte aligned, owned by the caller, contents on entry
  *                  irrelevant and on return unspecified: the chunk-start
- *                  states (B H ceil(T/16) Dv Dk floats) and four
+ *                  states (B H ceil(T/16) Dv Dk floats), every chunk's
+ *                  T = (I + A)^{-1} (256 floats per (b, h, chunk)) and four
  *                  accumulators of B T H Dk floats.  A smaller
  *                  workspace_bytes is GDR_ERR_INVALID.
  *
