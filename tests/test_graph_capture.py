@@ -1,8 +1,11 @@
 """The C-ABI calls under HIP graph capture (torch.cuda.CUDAGraph on the
 capturing stream): every call enqueues kernels only (no memset nodes, no
 allocation, no host synchronisation), so a captured sequence replays to the
-same bits as the eager calls.  Each replay is separated by eager work and
-a synchronisation, and every replay is checked."""
+same bits as the eager calls -- but for the backwards' gradients that are
+summed over blocks of state rows by atomic adds (dq, dk, and GDN-2's dalpha
+and derase), whose order varies: those match to fp32 rounding.  Each replay
+is separated by eager work and a synchronisation, and every replay is
+checked."""
 import pytest
 import torch
 
@@ -11,7 +14,8 @@ from gdr_gen import make_decode, make_gdn, make_gdn2
 pytestmark = pytest.mark.gpu
 
 
-def _replays_match(fn, outs_eager, n=3):
+def _replays_match(fn, outs_eager, n=3, summed=()):
+    """summed: indices of outputs that atomic adds produce"""
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -28,8 +32,12 @@ def _replays_match(fn, outs_eager, n=3):
             o.zero_()
         g.replay()
         torch.cuda.synchronize()
-        for a, b in zip(outs, outs_eager):
-            assert torch.equal(a, b), f"replay {i} differs"
+        for j, (a, b) in enumerate(zip(outs, outs_eager)):
+            if j in summed:
+                assert ((a - b).abs().max() <= 1e-5 * b.abs().max()).item(), \
+                    f"replay {i} output {j} differs"
+            else:
+                assert torch.equal(a, b), f"replay {i} output {j} differs"
         del junk
 
 
@@ -75,7 +83,8 @@ def test_graph_gdr2_and_backward(gdr_lib):
     outs = fn()
     torch.cuda.synchronize()
     eager = [x.clone() for x in outs]
-    _replays_match(fn, eager)
+    # (o, sf, dq, dk, dv, dalpha, derase, dwrite, ds0)
+    _replays_match(fn, eager, summed=(2, 3, 5, 6))
 
 
 def test_graph_split_forward(gdr_lib):
@@ -126,4 +135,5 @@ def test_graph_split_backward_and_gate(gdr_lib):
     outs = fn()
     torch.cuda.synchronize()
     eager = [x.clone() for x in outs]
-    _replays_match(fn, eager)
+    # (dq, dk, dv, dalpha, dbeta, ds0, y, ...)
+    _replays_match(fn, eager, summed=(0, 1))
