@@ -649,7 +649,7 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         }
         __syncthreads();
         // ---- dR = T^T dU (waves 0, 1; dw, dv to HBM);  dP = dO U^T (wave 2);
-        //      dT = dU R^T (wave 3)
+        //      dT = dU R^T and dA (wave 3)
         if (wv < 2) {
             const int t = wv;
             const f32x4 acc = mma16<1, false, false>(zero4, Ts, L::PC, dUs + 16 * t, L::PR);
@@ -668,17 +668,16 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
         } else if (wv == 2) {
             put_nn(mma16<2, true, true>(zero4, dOs, L::PR, Us, L::PR), dPs, false);
         } else {
+            // dT = dU R^T, Y = dT T^T, then dA = -T^T Y (strict) over dT
             put_nn(mma16<2, true, true>(zero4, dUs, L::PR, Rs, L::PR), dTs, true);
-        }
-        __syncthreads();
-        // ---- wave 0 first: Y = dT T^T, then dA = -T^T Y (strict) over dT
-        if (wv == 0) {
+            wave_sync();
             const f32x4 y = mma16<1, true, true>(zero4, dTs, L::PC, Ts, L::PC);
 #pragma unroll
             for (int i = 0; i < 4; ++i) Ys[(4 * lg + i) * L::PC + l16] = y[i];
             wave_sync();
             put_nn(mma16<1, false, false, true>(zero4, Ts, L::PC, Ys, L::PC), dTs, true);
         }
+        __syncthreads();
         // ---- this wave's channel tiles: dE~ = -dR S, dQ~ = dO S, dK~ = U G';
         //      the dP parts of dQ_P and dK_AP
         f32x4 dEt[CTW], dQt[CTW], dKt[CTW], dEa[CTW], dQa[CTW], dKa[CTW];
@@ -693,7 +692,6 @@ __global__ __launch_bounds__(NT2) void chunk2_bwd_kernel(Bwd2Params p) {
                 dKa[ct] = mma16<1, false, false>(zero4, dPs, L::PC, Qt + 16 * t, L::PK);
             }
         }
-        __syncthreads();   // dA
         const float* dAs = dTs;
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
