@@ -694,9 +694,11 @@ def bench_gate_fused(gdr, torch, warmup, steps):
 
 def bench_bwd(gdr, torch, warmup, steps):
     """gdr_chunk_bwd on B8 H16 T4096 d128 (bf16 q/k/v and dL/do, dL/dS_T
-    given, zero S_0).  It runs the GDN-2 backward with broadcast gates, so
-    the flops are counted as for bench_bwd2: per token-head, chunk C = 16,
-    2 x (9 dk dv + 3 C dk + 3 C dv)."""
+    given, zero S_0).  Algorithmic flops per token-head, chunk C = 16, as
+    for bench_bwd2: 2 x (9 dk dv + 3 C dk + 3 C dv) -- nine state-sized
+    products (the forward sweep's K S^T and state update, K S^T again,
+    K G'^T, (lambda dO) S, (rho U) G', (beta lambda dR) S, the two terms of
+    the G' update) and the chunk-sized ones."""
     from gdr_gen import make_gdn
     inp = make_gdn(B=8, T=4096, H=16, Dk=128, Dv=128, dtype="bf16", seed=1001)
     dev = torch.device("cuda:0")
