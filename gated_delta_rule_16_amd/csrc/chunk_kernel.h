@@ -224,7 +224,7 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
     const int64_t tstride = H * DK;   // elements between tokens of q, k
     const bf16_t* kbase = p.k + (b * T * H + h) * DK;
     const bf16_t* qbase = p.q + (b * T * H + h) * DK;
-    const bf16_t* vbase = p.v + (b * T * H + h) * DV + row0;
+    const bf16_t* vbase = p.v ? p.v + (b * T * H + h) * DV + row0 : nullptr;
     const float* abase = p.alpha + b * T * H + h;
     const float* bbase = p.beta + b * T * H + h;
 
@@ -889,6 +889,12 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
         };
         auto load = [&](int64_t cn, Buf& f) {
             if constexpr (!NOO) load_k(cn, f.q, qbase);
+            if (!p.v) {
+                // no v: v = 0 (the sequence split's transition pass)
+#pragma unroll
+                for (int u = 0; u < VL; ++u) f.v[u] = u32x4{0u, 0u, 0u, 0u};
+                return;
+            }
             const int last = last_row(cn);
             const char* cb = reinterpret_cast<const char*>(vbase + cn * CH * H * DV);
 #pragma unroll

@@ -279,13 +279,16 @@ static gdr_status_t split_states(const ChunkArgs& a, const SplitLayout& l, char*
     r.out_bf16 = l.oP && !o ? true : a.out_bf16;
     r.s_final = R;
     if ((st = chunk_run(r)) != GDR_OK) return st;
-    // 2. each segment with v = 0 from the identity: P (d_k x d_k)
+    // 2. each segment with v = 0 from the identity: P (d_k x d_k).  The
+    // bf16 scalar-gate kernel given no v takes v = 0 without reading
+    // memory; the vector-ALU and channel-gate kernels read the zeroed buffer
+    const bool v_null = a.in_bf16 && !a.gated2;
     hipError_t e = launch_identity(P, a.B * a.H, (int)a.Dk, a.stream);
-    if (e == hipSuccess) e = launch_zero(vz, (int64_t)l.vz, a.stream);
+    if (e == hipSuccess && !v_null) e = launch_zero(vz, (int64_t)l.vz, a.stream);
     if (e != hipSuccess) return GDR_ERR_DEVICE;
     ChunkArgs pa = a;
     pa.Dv = a.Dk;
-    pa.v = vz;
+    pa.v = v_null ? nullptr : vz;
     if (a.gated2) pa.write = vz;   // w (.) v = 0 either way; w needs Dk columns here
     pa.s0 = P;
     pa.s_final = P;
