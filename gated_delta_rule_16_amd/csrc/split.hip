@@ -38,28 +38,43 @@ __global__ __launch_bounds__(256) void zero_kernel(u32x4* __restrict__ x, int64_
 }
 
 // For each (b, h) and rows row0 .. row0 + 15: S = s0 (or 0); for p < nseg,
-// Sin[b nseg + p] = S, then S = S P[b nseg + p] + R[b nseg + p].  P goes
-// through LDS; each thread keeps DK / 16 entries of its row.  The next
-// step's P and R are loaded into registers while the current step computes.
+// Sin[b nseg + p] = S, then S = S P[b nseg + p] + R[b nseg + p], on the
+// fp32 matrix cores (v_mfma_f32_16x16x4_f32: the same fp32 products and
+// sums as the recurrence, in blocks of four).  Wave w owns column tiles
+// TW w .. TW w + TW - 1 of S as accumulators (register r: row 4 (l / 16) +
+// r, column l mod 16 of the tile); P is staged once per step in LDS and
+// read as the B operand, S as the A operand from a row copy in LDS.  The
+// next step's P and R are loaded into registers while the current step
+// computes.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void split_scan_kernel(int64_t H, int nseg,
                                                          const float* __restrict__ s0,
                                                          const float* __restrict__ R,
                                                          const float* __restrict__ P,
                                                          float* __restrict__ Sin) {
-    constexpr int PK = DK + 4;
-    constexpr int NCOL = DK / 16;
-    constexpr int NP = DK * DK / 4 / 256;   // 16-byte pieces of P per thread
-    __shared__ __align__(16) float Ps[DK * PK];
-    __shared__ __align__(16) float Sr[SROWS * PK];
-    const int tid = threadIdx.x;
+    // P rows DK + 16 apart (the four rows one B read spans fall on four
+    // disjoint 16-bank groups), S rows DK + 4 (the 16 rows of one A read on
+    // distinct banks)
+    constexpr int PP = DK + 16;
+    constexpr int PS = DK + 4;
+    constexpr int TW = DK / 16 / 4;          // column tiles per wave
+    constexpr int NP = DK * DK / 4 / 256;    // 16-byte pieces of P per thread
+    static_assert(TW >= 1 && NP >= 1, "shape");
+    __shared__ __align__(16) float Ps[DK * PP];
+    __shared__ __align__(16) float Sr[SROWS * PS];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
     const int64_t unit = blockIdx.x / (DV / SROWS);
     const int row0 = (int)(blockIdx.x % (DV / SROWS)) * SROWS;
     const int64_t h = unit % H, b = unit / H;
-    const int i = tid >> 4, j0 = NCOL * (tid & 15);
     auto seg_of = [&](int p) { return (b * nseg + p) * H + h; };
+    // element (4 lg + r, column of tile t) of this lane within a d_v x d_k
+    // state of the workgroup's rows
+    auto at = [&](int t, int r) {
+        return (int64_t)(row0 + 4 * lg + r) * DK + 16 * (TW * wv + t) + l16;
+    };
     f32x4 pr[NP];
-    float rr[NCOL];
+    f32x4 rr[TW];
     auto fetch = [&](int p) {
         const int64_t seg = seg_of(p);
 #pragma unroll
@@ -69,40 +84,49 @@ __global__ __launch_bounds__(256) void split_scan_kernel(int64_t H, int nseg,
             pr[it] = *reinterpret_cast<const f32x4*>(P + (seg * DK + m) * DK + c);
         }
 #pragma unroll
-        for (int j = 0; j < NCOL; ++j) rr[j] = R[(seg * DV + row0 + i) * DK + j0 + j];
-    };
-    float s[NCOL];
+        for (int t = 0; t < TW; ++t)
 #pragma unroll
-    for (int j = 0; j < NCOL; ++j)
-        s[j] = s0 ? s0[((b * H + h) * DV + row0 + i) * DK + j0 + j] : 0.f;
+            for (int r = 0; r < 4; ++r) rr[t][r] = R[seg * DV * DK + at(t, r)];
+    };
+    f32x4 s[TW];
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[t][r] = s0 ? s0[(b * H + h) * DV * DK + at(t, r)] : 0.f;
     if (nseg > 1) fetch(0);
     for (int p = 0; p < nseg; ++p) {
         const int64_t seg = seg_of(p);
 #pragma unroll
-        for (int j = 0; j < NCOL; ++j) Sin[(seg * DV + row0 + i) * DK + j0 + j] = s[j];
+        for (int t = 0; t < TW; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sin[seg * DV * DK + at(t, r)] = s[t][r];
         if (p == nseg - 1) break;
         __syncthreads();   // the previous step's reads of Ps and Sr are done
 #pragma unroll
         for (int it = 0; it < NP; ++it) {
             const int e = tid + 256 * it;
             const int m = e / (DK / 4), c = 4 * (e % (DK / 4));
-            *reinterpret_cast<f32x4*>(Ps + m * PK + c) = pr[it];
+            *reinterpret_cast<f32x4*>(Ps + m * PP + c) = pr[it];
         }
 #pragma unroll
-        for (int j = 0; j < NCOL; ++j) Sr[i * PK + j0 + j] = s[j];
-        float acc[NCOL];
+        for (int t = 0; t < TW; ++t)
 #pragma unroll
-        for (int j = 0; j < NCOL; ++j) acc[j] = rr[j];
+            for (int r = 0; r < 4; ++r) Sr[(4 * lg + r) * PS + 16 * (TW * wv + t) + l16] = s[t][r];
+        f32x4 acc[TW];
+#pragma unroll
+        for (int t = 0; t < TW; ++t) acc[t] = rr[t];
         if (p + 1 < nseg - 1) fetch(p + 1);
         __syncthreads();
-#pragma unroll 4
-        for (int m = 0; m < DK; ++m) {
-            const float sm = Sr[i * PK + m];
 #pragma unroll
-            for (int j = 0; j < NCOL; ++j) acc[j] += sm * Ps[m * PK + j0 + j];
+        for (int kb = 0; kb < DK / 4; ++kb) {
+            const float av = Sr[l16 * PS + 4 * kb + lg];
+#pragma unroll
+            for (int t = 0; t < TW; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                    av, Ps[(4 * kb + lg) * PP + 16 * (TW * wv + t) + l16], acc[t], 0, 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < NCOL; ++j) s[j] = acc[j];
+        for (int t = 0; t < TW; ++t) s[t] = acc[t];
     }
 }
 
