@@ -612,6 +612,12 @@ __global__ __launch_bounds__(64 * NWAVE) void gdr2_bf16_kernel(Gdr2Params p) {
         };
         const int wt = lane >> 2, wr = 8 * (lane & 3);
         auto load = [&](int64_t cn, Buf& f) {
+            if (!p.v) {
+                // no v (nor w): v = 0 (the sequence split's transition pass)
+                f.v = u32x4{0u, 0u, 0u, 0u};
+                f.w = u32x4{0u, 0u, 0u, 0u};
+                return;
+            }
             const uint32_t off = (uint32_t)(min(wt, last_row(cn)) * (int)(H * DV) + wr) * 2u;
             const char* vb = reinterpret_cast<const char*>(p.v + vofs + cn * CH * H * DV);
             const char* wb = reinterpret_cast<const char*>(p.write + vofs + cn * CH * H * DV);

@@ -245,11 +245,16 @@ SplitLayout split_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv
     l.R = up256(bn * Dv * Dk * 4);
     l.P = up256(bn * Dk * Dk * 4);
     l.Sin = up256(bn * Dv * Dk * 4);
-    l.vz = up256((size_t)(B * T * H * Dk) * (in_dt == GDR_BF16 ? 2 : 4));
+    // a zero v for the P pass: fp32 inputs only (the bf16 kernels take a
+    // missing v as zero)
+    l.vz = in_dt == GDR_BF16 ? 0 : up256((size_t)(B * T * H * Dk) * 4);
     // the P pass's output (and, with `discard`, the R pass's) when it
-    // cannot go to o: bf16, max(Dk, Dv) columns
-    l.oP = discard ? up256((size_t)(B * T * H * (Dk > Dv ? Dk : Dv)) * 2)
-                   : Dk == Dv ? 0 : up256((size_t)(B * T * H * Dk) * 2);
+    // cannot go to o: bf16, max(Dk, Dv) columns; fp32 inputs only (the
+    // bf16 kernels' state passes write no o)
+    l.oP = in_dt == GDR_BF16 ? 0
+           : discard         ? up256((size_t)(B * T * H * (Dk > Dv ? Dk : Dv)) * 2)
+           : Dk == Dv        ? 0
+                             : up256((size_t)(B * T * H * Dk) * 2);
     l.total = l.R + l.P + l.Sin + l.vz + l.oP;
     return l;
 }
@@ -280,16 +285,16 @@ static gdr_status_t split_states(const ChunkArgs& a, const SplitLayout& l, char*
     r.s_final = R;
     if ((st = chunk_run(r)) != GDR_OK) return st;
     // 2. each segment with v = 0 from the identity: P (d_k x d_k).  The
-    // bf16 scalar-gate kernel given no v takes v = 0 without reading
-    // memory; the vector-ALU and channel-gate kernels read the zeroed buffer
-    const bool v_null = a.in_bf16 && !a.gated2;
+    // bf16 kernels given no v (GDN-2: nor w) take v = 0 without reading
+    // memory; the vector-ALU kernels read the zeroed buffer
+    const bool v_null = a.in_bf16;
     hipError_t e = launch_identity(P, a.B * a.H, (int)a.Dk, a.stream);
     if (e == hipSuccess && !v_null) e = launch_zero(vz, (int64_t)l.vz, a.stream);
     if (e != hipSuccess) return GDR_ERR_DEVICE;
     ChunkArgs pa = a;
     pa.Dv = a.Dk;
     pa.v = v_null ? nullptr : vz;
-    if (a.gated2) pa.write = vz;   // w (.) v = 0 either way; w needs Dk columns here
+    if (a.gated2) pa.write = pa.v;   // w (.) v = 0 either way; w needs Dk columns here
     pa.s0 = P;
     pa.s_final = P;
     pa.o = no_o ? nullptr : oP;

@@ -271,13 +271,13 @@ gdr_status_t gdr2_chunk_fwd_ex(int64_t B, int64_t T, int64_t H, int64_t Dk,
  *              nseg) bytes, 16-byte aligned, owned by the caller, contents
  *              irrelevant on entry and unspecified on return: R, P and the
  *              start states (fp32, B nseg H Dv Dk, B nseg H Dk Dk and
- *              B nseg H Dv Dk floats), a zero v for the P pass
- *              (B T H Dk in_dt elements) and, when Dk != Dv, that pass's
- *              discarded output (B T H Dk bf16)
+ *              B nseg H Dv Dk floats) and, for fp32 inputs only, a zero
+ *              v for the P pass (B T H Dk floats) and, when Dk != Dv, that
+ *              pass's discarded output (B T H Dk bf16)
  *
  * The results equal the plain call's up to rounding (the segments' states
- * are composed in fp32).  o is written three times (the first two are
- * overwritten).  The workspace size is 0 for arguments the call rejects
+ * are composed in fp32).  With fp32 inputs o is written three times (the
+ * first two are overwritten); with bf16 inputs once.  The workspace size is 0 for arguments the call rejects
  * and when no workspace is needed.  Calls on one workspace must not overlap.
  */
 size_t gdr_chunk_fwd_split_workspace_size(int64_t B, int64_t T, int64_t H,

@@ -250,11 +250,12 @@ def split(gdr, B=1, T=64, H=1, Dk=64, Dv=64, dt=1, q=A16, k=A16, v=A16, a=A16, b
 
 def test_split_workspace_size(gdr):
     """R, P and start states (fp32, 256-byte rounded), the zero v of the P pass
-    in the input dtype, and the P pass's output (bf16) only when Dk != Dv."""
+    (fp32 inputs only: the bf16 kernels take a missing v as zero), and the P
+    pass's output (bf16) only when Dk != Dv."""
     up = lambda x: (x + 255) // 256 * 256
     f = gdr.lib.gdr_chunk_fwd_split_workspace_size
     bn = 2 * 4 * 3
-    assert f(2, 96, 3, 128, 128, 1, 4) == (up(bn * 128 * 128 * 4) * 3 + up(2 * 96 * 3 * 128 * 2))
+    assert f(2, 96, 3, 128, 128, 1, 4) == up(bn * 128 * 128 * 4) * 3
     assert f(2, 96, 3, 128, 64, 0, 4) == (up(bn * 64 * 128 * 4) * 2 + up(bn * 128 * 128 * 4) +
                                           up(2 * 96 * 3 * 128 * 4) + up(2 * 96 * 3 * 128 * 2))
     assert f(2, 96, 3, 128, 128, 1, 1) == 0     # the plain call
@@ -381,16 +382,20 @@ def test_fwd_gate_validation(gdr, kw, code):
 
 def test_bwd_split_workspace_size(gdr):
     """nseg = 1: the plain backward's workspace; otherwise the split
-    forward's pieces (with a discard buffer for the passes' outputs), N and
-    the end gradients (fp32 per segment state), and the backward workspace
-    of the segment batch; 0 where the call would reject the sizes."""
+    forward's pieces (for fp32 inputs with the zero v and a discard buffer
+    for the passes' outputs; the bf16 kernels need neither), N and the end
+    gradients (fp32 per segment state), and the backward workspace of the
+    segment batch; 0 where the call would reject the sizes."""
     f = gdr.lib.gdr_chunk_bwd_split_workspace_size
     up = lambda x: (x + 255) // 256 * 256
     assert f(2, 96, 3, 128, 128, 1, 1) == gdr.gdr_chunk_bwd_workspace_size(2, 96, 3, 128, 128)
     bn = 2 * 4 * 3
-    fwd = up(bn * 128 * 128 * 4) * 3 + up(2 * 96 * 3 * 128 * 2) * 2
+    fwd = up(bn * 128 * 128 * 4) * 3
     bw = up(gdr.gdr_chunk_bwd_workspace_size(8, 24, 3, 128, 128))
     assert f(2, 96, 3, 128, 128, 1, 4) == fwd + up(bn * 128 * 128 * 4) * 2 + bw
+    fwd32 = fwd + up(2 * 96 * 3 * 128 * 4) + up(2 * 96 * 3 * 128 * 2)
+    bw32 = up(gdr.gdr_chunk_bwd_workspace_size(8, 24, 3, 128, 128))
+    assert f(2, 96, 3, 128, 128, 0, 4) == fwd32 + up(bn * 128 * 128 * 4) * 2 + bw32
     assert f(2, 96, 3, 128, 128, 1, 5) == 0
     assert f(2, 96, 3, 96, 128, 1, 4) == 0
 
