@@ -37,25 +37,33 @@ __global__ __launch_bounds__(256) void zero_kernel(u32x4* __restrict__ x, int64_
         x[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
-// For each (b, h) and rows row0 .. row0 + 15: S = s0 (or 0); for p < nseg,
-// Sin[b nseg + p] = S, then S = S P[b nseg + p] + R[b nseg + p], on the
-// fp32 matrix cores (v_mfma_f32_16x16x4_f32: the same fp32 products and
-// sums as the recurrence, in blocks of four).  Wave w owns column tiles
-// TW w .. TW w + TW - 1 of S as accumulators (register r: row 4 (l / 16) +
-// r, column l mod 16 of the tile); P is staged once per step in LDS and
-// read as the B operand, S as the A operand from a row copy in LDS.  The
-// next step's P and R are loaded into registers while the current step
-// computes.
-template <int DK, int DV>
+// For each (b, h) and rows row0 .. row0 + 15, a chain over the segments on
+// the fp32 matrix cores (v_mfma_f32_16x16x4_f32: the same fp32 products and
+// sums as the recurrence, in blocks of four):
+// - forward (REV false): S = s0 (or 0); for p = 0 .. nseg - 1,
+//   Sin[b nseg + p] = S, then S = S P[b nseg + p] + R[b nseg + p];
+// - reverse (REV true), the backward's carry dL/dS_in(p) = G_end(p) P_p^T +
+//   N_p with N_p the segment's own contribution (its backward from
+//   G_end = 0): G = dsf (or 0); for p = nseg - 1 .. 0, Gend[b nseg + p] = G,
+//   then G = G P[b nseg + p]^T + N[b nseg + p].
+// (init, X, out) are (s0, R, Sin) forward and (dsf, N, Gend) in reverse.
+// Wave w owns column tiles TW w .. TW w + TW - 1 of the state as
+// accumulators (register r: row 4 (l / 16) + r, column l mod 16 of the
+// tile); P is staged row-major in LDS once per step and read as the B
+// operand (P, or P^T by swapped indices), the state as the A operand from a
+// row copy in LDS.  The next step's P and X are loaded into registers while
+// the current step computes.
+template <int DK, int DV, bool REV>
 __global__ __launch_bounds__(256) void split_scan_kernel(int64_t H, int nseg,
-                                                         const float* __restrict__ s0,
-                                                         const float* __restrict__ R,
+                                                         const float* __restrict__ init,
+                                                         const float* __restrict__ X,
                                                          const float* __restrict__ P,
-                                                         float* __restrict__ Sin) {
-    // P rows DK + 16 apart (the four rows one B read spans fall on four
-    // disjoint 16-bank groups), S rows DK + 4 (the 16 rows of one A read on
-    // distinct banks)
-    constexpr int PP = DK + 16;
+                                                         float* __restrict__ out) {
+    // P rows DK + 16 apart forward (a B read spans four rows: four disjoint
+    // 16-bank groups) and DK + 4 in reverse (a B read spans 16 rows at four
+    // columns: rows four banks apart); state rows DK + 4 (the 16 rows of one
+    // A read on distinct banks)
+    constexpr int PP = REV ? DK + 4 : DK + 16;
     constexpr int PS = DK + 4;
     constexpr int TW = DK / 16 / 4;          // column tiles per wave
     constexpr int NP = DK * DK / 4 / 256;    // 16-byte pieces of P per thread
@@ -74,7 +82,7 @@ __global__ __launch_bounds__(256) void split_scan_kernel(int64_t H, int nseg,
         return (int64_t)(row0 + 4 * lg + r) * DK + 16 * (TW * wv + t) + l16;
     };
     f32x4 pr[NP];
-    f32x4 rr[TW];
+    f32x4 xr[TW];
     auto fetch = [&](int p) {
         const int64_t seg = seg_of(p);
 #pragma unroll
@@ -86,21 +94,22 @@ __global__ __launch_bounds__(256) void split_scan_kernel(int64_t H, int nseg,
 #pragma unroll
         for (int t = 0; t < TW; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) rr[t][r] = R[seg * DV * DK + at(t, r)];
+            for (int r = 0; r < 4; ++r) xr[t][r] = X[seg * DV * DK + at(t, r)];
     };
     f32x4 s[TW];
 #pragma unroll
     for (int t = 0; t < TW; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[t][r] = s0 ? s0[(b * H + h) * DV * DK + at(t, r)] : 0.f;
-    if (nseg > 1) fetch(0);
-    for (int p = 0; p < nseg; ++p) {
+        for (int r = 0; r < 4; ++r) s[t][r] = init ? init[(b * H + h) * DV * DK + at(t, r)] : 0.f;
+    if (nseg > 1) fetch(REV ? nseg - 1 : 0);
+    for (int q = 0; q < nseg; ++q) {
+        const int p = REV ? nseg - 1 - q : q;
         const int64_t seg = seg_of(p);
 #pragma unroll
         for (int t = 0; t < TW; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Sin[seg * DV * DK + at(t, r)] = s[t][r];
-        if (p == nseg - 1) break;
+            for (int r = 0; r < 4; ++r) out[seg * DV * DK + at(t, r)] = s[t][r];
+        if (q == nseg - 1) break;
         __syncthreads();   // the previous step's reads of Ps and Sr are done
 #pragma unroll
         for (int it = 0; it < NP; ++it) {
@@ -114,91 +123,21 @@ __global__ __launch_bounds__(256) void split_scan_kernel(int64_t H, int nseg,
             for (int r = 0; r < 4; ++r) Sr[(4 * lg + r) * PS + 16 * (TW * wv + t) + l16] = s[t][r];
         f32x4 acc[TW];
 #pragma unroll
-        for (int t = 0; t < TW; ++t) acc[t] = rr[t];
-        if (p + 1 < nseg - 1) fetch(p + 1);
+        for (int t = 0; t < TW; ++t) acc[t] = xr[t];
+        if (q + 1 < nseg - 1) fetch(REV ? p - 1 : p + 1);
         __syncthreads();
 #pragma unroll
         for (int kb = 0; kb < DK / 4; ++kb) {
             const float av = Sr[l16 * PS + 4 * kb + lg];
 #pragma unroll
-            for (int t = 0; t < TW; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                    av, Ps[(4 * kb + lg) * PP + 16 * (TW * wv + t) + l16], acc[t], 0, 0, 0);
+            for (int t = 0; t < TW; ++t) {
+                const int k = 4 * kb + lg, n = 16 * (TW * wv + t) + l16;
+                const float bv = REV ? Ps[n * PP + k] : Ps[k * PP + n];
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[t], 0, 0, 0);
+            }
         }
 #pragma unroll
         for (int t = 0; t < TW; ++t) s[t] = acc[t];
-    }
-}
-
-// The backward's carry composes the same way in reverse: dL/dS_in(p) =
-// G_end(p) P_p^T + N_p, with N_p the segment's own contribution (its
-// backward from G_end = 0).  For each (b, h) and rows row0 .. row0 + 15:
-// G = dsf (or 0) for the last segment; for p = nseg - 1 .. 1,
-// Gend[b nseg + p] = G, then G = G P[b nseg + p]^T + N[b nseg + p];
-// Gend[b nseg] = G.  P_p^T staged in LDS, as in split_scan_kernel.
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void split_rscan_kernel(int64_t H, int nseg,
-                                                          const float* __restrict__ dsf,
-                                                          const float* __restrict__ N,
-                                                          const float* __restrict__ P,
-                                                          float* __restrict__ Gend) {
-    constexpr int PK = DK + 4;
-    constexpr int NCOL = DK / 16;
-    constexpr int NP = DK * DK / 4 / 256;
-    __shared__ __align__(16) float Pt[DK * PK];   // Pt[m][j] = P[j][m]
-    __shared__ __align__(16) float Gr[SROWS * PK];
-    const int tid = threadIdx.x;
-    const int64_t unit = blockIdx.x / (DV / SROWS);
-    const int row0 = (int)(blockIdx.x % (DV / SROWS)) * SROWS;
-    const int64_t h = unit % H, b = unit / H;
-    const int i = tid >> 4, j0 = NCOL * (tid & 15);
-    auto seg_of = [&](int p) { return (b * nseg + p) * H + h; };
-    f32x4 pr[NP];
-    float nr[NCOL];
-    auto fetch = [&](int p) {
-        const int64_t seg = seg_of(p);
-#pragma unroll
-        for (int it = 0; it < NP; ++it) {
-            const int e = tid + 256 * it;
-            const int m = e / (DK / 4), c = 4 * (e % (DK / 4));
-            pr[it] = *reinterpret_cast<const f32x4*>(P + (seg * DK + m) * DK + c);
-        }
-#pragma unroll
-        for (int j = 0; j < NCOL; ++j) nr[j] = N[(seg * DV + row0 + i) * DK + j0 + j];
-    };
-    float gv[NCOL];
-#pragma unroll
-    for (int j = 0; j < NCOL; ++j)
-        gv[j] = dsf ? dsf[((b * H + h) * DV + row0 + i) * DK + j0 + j] : 0.f;
-    if (nseg > 1) fetch(nseg - 1);
-    for (int p = nseg - 1; p >= 0; --p) {
-        const int64_t seg = seg_of(p);
-#pragma unroll
-        for (int j = 0; j < NCOL; ++j) Gend[(seg * DV + row0 + i) * DK + j0 + j] = gv[j];
-        if (p == 0) break;
-        __syncthreads();   // the previous step's reads of Pt and Gr are done
-#pragma unroll
-        for (int it = 0; it < NP; ++it) {   // transposed into LDS
-            const int e = tid + 256 * it;
-            const int m = e / (DK / 4), c = 4 * (e % (DK / 4));
-#pragma unroll
-            for (int z = 0; z < 4; ++z) Pt[(c + z) * PK + m] = pr[it][z];
-        }
-#pragma unroll
-        for (int j = 0; j < NCOL; ++j) Gr[i * PK + j0 + j] = gv[j];
-        float acc[NCOL];
-#pragma unroll
-        for (int j = 0; j < NCOL; ++j) acc[j] = nr[j];
-        if (p - 1 > 0) fetch(p - 1);
-        __syncthreads();
-#pragma unroll 4
-        for (int m = 0; m < DK; ++m) {
-            const float gm = Gr[i * PK + m];
-#pragma unroll
-            for (int j = 0; j < NCOL; ++j) acc[j] += gm * Pt[m * PK + j0 + j];
-        }
-#pragma unroll
-        for (int j = 0; j < NCOL; ++j) gv[j] = acc[j];
     }
 }
 
@@ -217,7 +156,7 @@ __global__ __launch_bounds__(256) void seg_state_kernel(const float* __restrict_
 template <int DK, int DV>
 hipError_t rscan_t(const SplitScanArgs& a) {
     const int64_t blocks = a.B * a.H * (DV / SROWS);
-    hipLaunchKernelGGL((split_rscan_kernel<DK, DV>), dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((split_scan_kernel<DK, DV, true>), dim3((unsigned)blocks), dim3(256), 0,
                        a.stream, a.H, a.nseg, a.s0, a.R, a.P, a.Sin);
     return hipGetLastError();
 }
@@ -225,8 +164,8 @@ hipError_t rscan_t(const SplitScanArgs& a) {
 template <int DK, int DV>
 hipError_t scan_t(const SplitScanArgs& a) {
     const int64_t blocks = a.B * a.H * (DV / SROWS);
-    hipLaunchKernelGGL((split_scan_kernel<DK, DV>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
-                       a.H, a.nseg, a.s0, a.R, a.P, a.Sin);
+    hipLaunchKernelGGL((split_scan_kernel<DK, DV, false>), dim3((unsigned)blocks), dim3(256), 0,
+                       a.stream, a.H, a.nseg, a.s0, a.R, a.P, a.Sin);
     return hipGetLastError();
 }
 
