@@ -57,6 +57,15 @@ def test_bwd_split_dims(gdr_lib, dims):
                              seed=780 + dims[0], alpha_shift=-2.0, s0_std=0.1), 4, 20)
 
 
+@pytest.mark.parametrize("dims", [(128, 64), (64, 128), (64, 64)])
+def test_bwd_split_bf16_dims(gdr_lib, dims):
+    """bf16 inputs: the transition pass reads no v (d_v of that pass = d_k)
+    and the scans run at every head-dim pair."""
+    _check(gdr_lib, make_gdn(B=1, T=160, H=2, Dk=dims[0], Dv=dims[1], dtype="bf16",
+                             seed=785 + dims[0] + dims[1], alpha_shift=-2.0, s0_std=0.1), 5,
+           22, dout_dtype=torch.bfloat16)
+
+
 def test_bwd_split_bf16_norm_no_state(gdr_lib):
     """bf16 inputs and dL/do, q, k normalised on load, no S_0 or dL/dS_T."""
     _check(gdr_lib, make_gdn(B=1, T=192, H=2, Dk=128, Dv=128, dtype="bf16", seed=790,
