@@ -126,9 +126,9 @@ struct Lay {
     static constexpr int AF = GR + 3 * GRS;         // A fp32 [32][P36], two copies
     static constexpr int TF = AF + 2 * CH * P36 * 4;   // B1 private: T fp32 [32][P36]
     // output gate: team A's per-token partial sums of squares of o, three
-    // chunks [3][RB / 16][32], and the gate values of three chunks as
-    // loaded, token-major [32][GP] in the gate's dtype (GP = RB + 8
-    // elements: rows 16 or 32 bytes apart in banks)
+    // chunks [3][RB / 16][32], and w SiLU(gate) of three chunks as B0
+    // formed it, token-major fp32 [32][GP] (GP = RB + 8 elements: rows 32
+    // bytes apart in banks)
     static constexpr int GP = RB + 8;
     static constexpr int PSQ = TF + CH * P36 * 4;
     static constexpr int GGR = PSQ + (GATE ? 3 * (RB / 16) * CH * 4 : 0);
@@ -275,7 +275,6 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
         //   jt = 4 b3 + 2 b2 + b1 (bits of m) of the group's 8 tokens
         const int jt = 4 * ((m >> 3) & 1) + 2 * ((m >> 2) & 1) + ((m >> 1) & 1);
         const int tok = 16 * (jt >> 2) + 4 * g + (jt & 3);
-        const float wr = GATE && p.w ? p.w[row0 + i] : 1.f;
         float* psq = reinterpret_cast<float*>(smem + L::PSQ);   // [3][NA][CH]
         // chunk slots in 32-bit arithmetic (the call keeps T below 2^36)
         auto mod3 = [](int64_t cn) { return (int)((uint32_t)cn % 3u); };
@@ -319,31 +318,12 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
         // SiLU(x) = x / (1 + e^-x).  The lane's gate values (tokens 16 rt +
         // 4 g + r, channel i): bf16 by two transposed reads, fp32 one by one.
         auto gate_apply = [&](const f32x4 (&ov)[2], int64_t cn, f32x4 (&og)[2]) {
-            const unsigned char* gs = smem + L::GGR + mod3(cn) * L::GGS;
-            f32x4 gv[2];
-            if (p.gate_bf16) {
-                const bf16_t* gb = reinterpret_cast<const bf16_t*>(gs);
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    const s16x4 x = lds_tr16(gb + (16 * rt + 4 * g + (m >> 2)) * L::GP + 16 * a +
-                                             4 * (m & 3));
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) gv[rt][r] = bf2f((bf16_t)x[r]);
-                }
-            } else {
-                const float* gf = reinterpret_cast<const float*>(gs);
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) gv[rt][r] = gf[(16 * rt + 4 * g + r) * L::GP + i];
-            }
+            // w SiLU(g) of the chunk, formed by B0 when it staged the gate
+            const float* gf = reinterpret_cast<const float*>(smem + L::GGR + mod3(cn) * L::GGS);
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float x = gv[rt][r];
-                    og[rt][r] = ov[rt][r] * wr * (x * __builtin_amdgcn_rcpf(1.f + __expf(-x)));
-                }
+                for (int r = 0; r < 4; ++r) og[rt][r] = ov[rt][r] * gf[(16 * rt + 4 * g + r) * L::GP + i];
         };
         // the other row blocks' words for chunk cn, read once early in a
         // period (their round trip overlaps its work)
@@ -757,15 +737,24 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
             sigma = reset ? 1.f : s1;
         };
         if constexpr (GATE) {
-            // and the output gate's values of the chunk, for team A one period
-            // later: 32 tokens x RB channels, copied token-major into LDS in
-            // 16-byte pieces (VPC per token, GPL per lane)
+            // and the output gate's factor of the chunk, for team A one period
+            // later: w SiLU(g) over 32 tokens x RB channels, token-major fp32
+            // in LDS; the gate is read in 16-byte pieces (VPC per token, GPL
+            // per lane, EPC elements each), every piece of a lane at the same
+            // channels, so the lane's w values are loaded once.  B0 has the
+            // slack of the period; team A only multiplies.
             auto stage = [&](auto esz) {
                 constexpr int ES = decltype(esz)::value;   // gate element bytes
                 constexpr int VPC = RB * ES / 16, NPC = CH * VPC, GPL = (NPC + 63) / 64;
+                constexpr int EPC = 16 / ES;
+                static_assert(NPC % 64 == 0 && 64 % VPC == 0, "gate pieces");
                 struct GBuf {
                     u32x4 v[GPL];
                 };
+                const int c0 = (lane % VPC) * EPC;   // this lane's first channel
+                float wv[EPC];
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) wv[e] = p.w ? p.w[row0 + c0 + e] : 1.f;
                 const char* gbase = reinterpret_cast<const char*>(p.gate);
                 auto load = [&](int64_t cn, GBuf& f) {
                     const int last = last_row(cn);
@@ -782,13 +771,26 @@ __global__ __launch_bounds__(64 * (RB / 16 + NB)) void chunk_bf16_kernel(Bf16Par
                 };
                 auto prepare_g = [&](int64_t cn, const GBuf& f) {
                     prepare(cn);
-                    unsigned char* gs = smem + L::GGR + (int)(cn % 3) * L::GGS;
+                    float* gs = reinterpret_cast<float*>(smem + L::GGR + (int)(cn % 3) * L::GGS);
 #pragma unroll
                     for (int u = 0; u < GPL; ++u) {
-                        const int pc = lane + 64 * u;
-                        if (NPC % 64 == 0 || pc < NPC)
-                            *reinterpret_cast<u32x4*>(gs + ((pc / VPC) * L::GP * ES + 16 * (pc % VPC))) =
-                                f.v[u];
+                        const int t = (lane + 64 * u) / VPC;
+                        float sv[EPC];
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e) {
+                            float x;
+                            if constexpr (ES == 2) {
+                                const uint32_t wd = f.v[u][e >> 1];
+                                x = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
+                            } else {
+                                x = __uint_as_float(f.v[u][e]);
+                            }
+                            sv[e] = wv[e] * (x * __builtin_amdgcn_rcpf(1.f + __expf(-x)));
+                        }
+#pragma unroll
+                        for (int h4 = 0; h4 < EPC / 4; ++h4)
+                            *reinterpret_cast<f32x4*>(gs + t * L::GP + c0 + 4 * h4) =
+                                f32x4{sv[4 * h4], sv[4 * h4 + 1], sv[4 * h4 + 2], sv[4 * h4 + 3]};
                     }
                 };
                 GBuf fa, fb, fc;
